@@ -1,0 +1,579 @@
+/*
+ * cgo.c -- CPU oracle of the CacheGen-style KV-cache codec.
+ *
+ * TEST INFRASTRUCTURE.  Only tests/, the smoke check in __graft_entry__.py and the
+ * cpu_baseline leg of bench.py may load this library.  The product path (libcg, HIP)
+ * never calls it, and the two share no source, header, table or helper.
+ *
+ * Plain scalar C99, built with -O2 -ffp-contract=off and no fast-math, so every
+ * floating-point operation below is one IEEE binary32 operation in program order and
+ * fmaf() is the only fused operation.  Loops follow the steps of the method in the
+ * order the pages give them:
+ *
+ *   1. tokens are cut into chunks, and each chunk into groups of G tokens whose first
+ *      token is the anchor ("Guide to CacheGen", Solution pillar 2 and Implementation
+ *      Step 2: windows of W tokens, first token kept as the anchor, ceil(S/W) windows,
+ *      the last window may be short);
+ *   2. every other token is coded as a delta from its anchor (same passage: the delta
+ *      equation Delta_t = K_t - K_anchor);
+ *   3. deltas are quantized with a per-layer number of levels, finer for early layers
+ *      (Solution pillar 1; the gptget.net summary of CacheGen, Methodology), using a
+ *      min/max affine grid as in Implementation Step 1 (quantize_tensor /
+ *      dequantize_tensor) but taken per channel over the non-anchor deltas;
+ *   4. symbols are entropy-coded with an arithmetic (range) coder driven by empirical
+ *      frequency tables (Solution pillar 3; the summary's Deep Analysis, Methodology:
+ *      delta coding combined with arithmetic coding, per layer and channel), one
+ *      independent stream per (layer, K/V, channel, chunk) so chunks decode on their own
+ *      (summary, Methodology: the cache is cut into chunks that are streamed);
+ *   5. decoding inverts 4, then dequantizes and adds the anchor back (Implementation
+ *      Step 1 dequantize_tensor, computed in float32; Step 2 decode_sequence).
+ *
+ * Where the pages leave a step open (the coder, the table precision, the grid, the
+ * rounding, the stream layout) the readings written out in the comments below are
+ * the ones this project fixed; the same list is kept with the design notes.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define CGO_PROB_BITS 12u
+#define CGO_PROB_TOTAL (1u << CGO_PROB_BITS) /* frequencies sum to 4096 */
+#define CGO_MAX_BINS 32u
+#define CGO_LANES 64u                       /* channels per interleaved group */
+#define CGO_RANGE_INIT 0xFFFFFFFFu
+#define CGO_RENORM_BELOW 0x10000u           /* renormalise when range < 2^16 */
+
+/* ------------------------------------------------------------------------------ */
+/* IEEE-754 binary16 <-> binary32, written from the format definition.             */
+/* ------------------------------------------------------------------------------ */
+
+float cgo_half_to_float(uint16_t h)
+{
+    uint32_t sign = h >> 15, e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)m, -24);                 /* subnormal: m * 2^-24 (exact) */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(m | 0x400u), (int)e - 25); /* (1024 + m) * 2^(e-25) */
+    return sign ? -v : v;
+}
+
+/* Round-to-nearest-even conversion. */
+uint16_t cgo_float_to_half(float f)
+{
+    uint16_t sign = signbit(f) ? 0x8000u : 0;
+    float a = fabsf(f);
+    if (isnan(f))
+        return (uint16_t)(sign | 0x7E00u);
+    if (a >= 65520.0f)                              /* halfway to 2^16 rounds to even = inf */
+        return (uint16_t)(sign | 0x7C00u);
+    if (a < ldexpf(1.0f, -14)) {                    /* subnormal range: units of 2^-24 */
+        float q = rintf(ldexpf(a, 24));             /* default rounding mode: nearest-even */
+        return (uint16_t)(sign | (uint16_t)q);      /* q == 1024 encodes the smallest normal */
+    }
+    int e;
+    frexpf(a, &e);                                  /* a = frac * 2^e, frac in [0.5, 1) */
+    e -= 1;                                         /* a in [2^e, 2^(e+1)) */
+    float m = rintf(ldexpf(a, 10 - e));             /* in [1024, 2048] */
+    if (m >= 2048.0f) {
+        m = 1024.0f;
+        e += 1;
+    }
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)((uint32_t)m - 1024u));
+}
+
+void cgo_half_to_float_n(const uint16_t *h, float *f, size_t n)
+{
+    for (size_t i = 0; i < n; i++)
+        f[i] = cgo_half_to_float(h[i]);
+}
+
+void cgo_float_to_half_n(const float *f, uint16_t *h, size_t n)
+{
+    for (size_t i = 0; i < n; i++)
+        h[i] = cgo_float_to_half(f[i]);
+}
+
+static int half_is_finite(uint16_t h) { return ((h >> 10) & 0x1Fu) != 0x1Fu; }
+
+/* ------------------------------------------------------------------------------ */
+/* Segmentation: chunks of Tc tokens, groups of G tokens restarting at every chunk. */
+/* ------------------------------------------------------------------------------ */
+
+uint32_t cgo_num_chunks(uint32_t S, uint32_t Tc) { return (S + Tc - 1) / Tc; }
+
+uint32_t cgo_chunk_len(uint32_t S, uint32_t Tc, uint32_t k)
+{
+    uint32_t t0 = k * Tc;
+    return (S - t0 < Tc) ? S - t0 : Tc;
+}
+
+uint32_t cgo_groups_in(uint32_t len, uint32_t G) { return (len + G - 1) / G; }
+
+int cgo_is_anchor(uint32_t t, uint32_t G, uint32_t Tc) { return ((t % Tc) % G) == 0; }
+
+uint32_t cgo_anchor_of(uint32_t t, uint32_t G, uint32_t Tc)
+{
+    uint32_t k0 = (t / Tc) * Tc;
+    return k0 + ((t - k0) / G) * G;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Shapes.                                                                          */
+/* ------------------------------------------------------------------------------ */
+
+typedef struct {
+    uint32_t L, H, d, S, G, Tc;
+    const uint8_t *bins; /* [L], each in [2, 32] */
+} cgo_shape;
+
+static size_t kv_index(const cgo_shape *p, uint32_t l, uint32_t kv, uint32_t t, uint32_t c)
+{
+    size_t C = (size_t)p->H * p->d;
+    return (((size_t)l * 2 + kv) * p->S + t) * C + c;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Step 2-3a: per-channel range of the anchor deltas.                               */
+/*   Delta = f32(x_t) - f32(x_anchor)    (one binary32 subtraction)                 */
+/*   lo, hi = min / max over every non-anchor token of the channel (all chunks);    */
+/*   lo = hi = 0 when the channel has no non-anchor token;                          */
+/*   w = (hi - lo) / (N - 1);  r = 1 / w, or 0 when w == 0.                          */
+/* Returns -4 if any input element is Inf or NaN, else 0.                           */
+/* ------------------------------------------------------------------------------ */
+int cgo_range(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
+              const uint8_t *bins, const uint16_t *X, float *lo_out, float *w_out, float *r_out)
+{
+    cgo_shape p = {L, H, d, S, G, Tc, bins};
+    uint32_t C = H * d;
+    size_t total = (size_t)L * 2 * S * C;
+    for (size_t i = 0; i < total; i++)
+        if (!half_is_finite(X[i]))
+            return -4;
+    for (uint32_t l = 0; l < L; l++)
+        for (uint32_t kv = 0; kv < 2; kv++)
+            for (uint32_t c = 0; c < C; c++) {
+                int any = 0;
+                float lo = 0.0f, hi = 0.0f;
+                for (uint32_t t = 0; t < S; t++) {
+                    if (cgo_is_anchor(t, G, Tc))
+                        continue;
+                    uint32_t a = cgo_anchor_of(t, G, Tc);
+                    float delta = cgo_half_to_float(X[kv_index(&p, l, kv, t, c)]) -
+                                  cgo_half_to_float(X[kv_index(&p, l, kv, a, c)]);
+                    if (!any) {
+                        lo = hi = delta;
+                        any = 1;
+                    } else {
+                        if (delta < lo) lo = delta;
+                        if (delta > hi) hi = delta;
+                    }
+                }
+                size_t row = ((size_t)l * 2 + kv) * C + c;
+                float w = (hi - lo) / (float)(bins[l] - 1u);
+                lo_out[row] = lo;
+                w_out[row] = w;
+                r_out[row] = (w > 0.0f) ? 1.0f / w : 0.0f;
+            }
+    return 0;
+}
+
+/* Step 3b: q = clamp(floor(fma(Delta - lo, r, 0.5)), 0, N - 1): nearest grid point
+ * lo + q*w, ties upward.  Anchors carry no symbol (their slot is written as 0). */
+static uint8_t quantize_one(float delta, float lo, float r, uint32_t N)
+{
+    float v = floorf(fmaf(delta - lo, r, 0.5f));
+    if (!(v > 0.0f))
+        return 0;
+    if (v > (float)(N - 1u))
+        return (uint8_t)(N - 1u);
+    return (uint8_t)v;
+}
+
+void cgo_quantize(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
+                  const uint8_t *bins, const uint16_t *X, const float *lo, const float *r,
+                  uint32_t t_begin, uint32_t t_end, uint8_t *sym /* [L][2][S][C] */)
+{
+    cgo_shape p = {L, H, d, S, G, Tc, bins};
+    uint32_t C = H * d;
+    for (uint32_t l = 0; l < L; l++)
+        for (uint32_t kv = 0; kv < 2; kv++)
+            for (uint32_t t = t_begin; t < t_end; t++)
+                for (uint32_t c = 0; c < C; c++) {
+                    size_t i = kv_index(&p, l, kv, t, c);
+                    if (cgo_is_anchor(t, G, Tc)) {
+                        sym[i] = 0;
+                        continue;
+                    }
+                    size_t row = ((size_t)l * 2 + kv) * C + c;
+                    uint32_t a = cgo_anchor_of(t, G, Tc);
+                    float delta = cgo_half_to_float(X[i]) -
+                                  cgo_half_to_float(X[kv_index(&p, l, kv, a, c)]);
+                    sym[i] = quantize_one(delta, lo[row], r[row], bins[l]);
+                }
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Step 4a: empirical frequency table per (layer, K/V, channel), shared by all     */
+/* chunks of the channel.  Frequencies sum to T = 4096 and every symbol gets f >= 1: */
+/*   f[s] = 1 + floor(count[s] * (T - N) / n)     (n = sum of counts; 0 if n == 0)   */
+/* and the remainder T - sum(f) goes to the most frequent symbol (lowest index on    */
+/* ties).  freqs is [L][2][C][32], entries beyond N are 0.                           */
+/* ------------------------------------------------------------------------------ */
+void cgo_freqs_from_counts(const uint64_t *count, uint32_t N, uint16_t *f)
+{
+    uint64_t n = 0;
+    for (uint32_t s = 0; s < N; s++)
+        n += count[s];
+    uint32_t sum = 0, best = 0;
+    for (uint32_t s = 0; s < N; s++) {
+        uint64_t extra = n ? (count[s] * (uint64_t)(CGO_PROB_TOTAL - N)) / n : 0;
+        f[s] = (uint16_t)(1u + extra);
+        sum += f[s];
+        if (count[s] > count[best])
+            best = s;
+    }
+    f[best] = (uint16_t)(f[best] + (CGO_PROB_TOTAL - sum));
+}
+
+void cgo_histograms(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
+                    const uint8_t *bins, const uint8_t *sym, uint64_t *counts /* [L][2][C][32] */)
+{
+    cgo_shape p = {L, H, d, S, G, Tc, bins};
+    uint32_t C = H * d;
+    memset(counts, 0, sizeof(uint64_t) * (size_t)L * 2 * C * CGO_MAX_BINS);
+    for (uint32_t l = 0; l < L; l++)
+        for (uint32_t kv = 0; kv < 2; kv++)
+            for (uint32_t t = 0; t < S; t++) {
+                if (cgo_is_anchor(t, G, Tc))
+                    continue;
+                for (uint32_t c = 0; c < C; c++) {
+                    size_t row = ((size_t)l * 2 + kv) * C + c;
+                    counts[row * CGO_MAX_BINS + sym[kv_index(&p, l, kv, t, c)]] += 1;
+                }
+            }
+}
+
+void cgo_freqs(uint32_t L, uint32_t C, const uint8_t *bins, const uint64_t *counts,
+               uint16_t *freqs /* [L][2][C][32] */)
+{
+    memset(freqs, 0, sizeof(uint16_t) * (size_t)L * 2 * C * CGO_MAX_BINS);
+    for (uint32_t l = 0; l < L; l++)
+        for (uint32_t kv = 0; kv < 2; kv++)
+            for (uint32_t c = 0; c < C; c++) {
+                size_t row = ((size_t)l * 2 + kv) * C + c;
+                cgo_freqs_from_counts(counts + row * CGO_MAX_BINS, bins[l],
+                                      freqs + row * CGO_MAX_BINS);
+            }
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Step 4b: range coder (G. N. N. Martin, "Range encoding", 1979), multi-symbol,     */
+/* 32-bit range, 16-bit output words, probabilities in units of 1/4096.              */
+/*                                                                                    */
+/* Encoder, for symbols x_0 .. x_{m-1} with cumulative table cdf (cdf[N] = 4096):    */
+/*   low = 0, range = 2^32 - 1                                                        */
+/*   for each i: q = range >> 12; low += q * cdf[x_i]; range = q * f[x_i];            */
+/*               if i < m - 1 and range < 2^16: shift one 16-bit word out of low,     */
+/*               low <<= 16, range <<= 16   (a "renormalisation event" at step i)    */
+/*   the stream is the 2 + (number of events) base-65536 digits of the final low,    */
+/*   most significant first.  Carries out of the 32-bit window are added into the    */
+/*   words already written.  m == 0 gives an empty stream.                           */
+/* Word j is read by the decoder at step -1 (start) for j < 2, else at the step of    */
+/* event j - 2; steps_out receives that step for every word.                          */
+/* Returns the number of words.                                                       */
+/* ------------------------------------------------------------------------------ */
+uint32_t cgo_rc_encode(const uint8_t *x, uint32_t m, const uint16_t *f, uint32_t N,
+                       uint16_t *words, int32_t *steps_out)
+{
+    uint32_t cdf[CGO_MAX_BINS + 1];
+    cdf[0] = 0;
+    for (uint32_t s = 0; s < N; s++)
+        cdf[s + 1] = cdf[s] + f[s];
+    if (m == 0)
+        return 0;
+    uint64_t low = 0;
+    uint32_t range = CGO_RANGE_INIT;
+    uint32_t nw = 0, nev = 0;
+    int32_t *event_step = (int32_t *)malloc(sizeof(int32_t) * (m + 1));
+    for (uint32_t i = 0; i < m; i++) {
+        uint32_t s = x[i];
+        uint32_t q = range >> CGO_PROB_BITS;
+        low += (uint64_t)q * cdf[s];
+        range = q * f[s];
+        if (low >> 32) {                 /* carry into the words already written */
+            low &= 0xFFFFFFFFu;
+            uint32_t j = nw;
+            do {
+                j--;
+                words[j] = (uint16_t)(words[j] + 1u);
+            } while (words[j] == 0);
+        }
+        if (i + 1 < m && range < CGO_RENORM_BELOW) {
+            words[nw++] = (uint16_t)(low >> 16);
+            low = (low & 0xFFFFu) << 16;
+            range <<= 16;
+            event_step[nev++] = (int32_t)i;
+        }
+    }
+    words[nw++] = (uint16_t)(low >> 16);
+    words[nw++] = (uint16_t)(low & 0xFFFFu);
+    if (steps_out)
+        for (uint32_t j = 0; j < nw; j++)
+            steps_out[j] = (j < 2) ? -1 : event_step[j - 2];
+    free(event_step);
+    return nw;
+}
+
+/* Decoder: code = words 0..1; then for each step q = range >> 12, the symbol is the
+ * largest s with q * cdf[s] <= code; code -= q * cdf[s]; range = q * f[s]; and, except
+ * after the last symbol, range < 2^16 pulls in the next word.  Words past the end of
+ * the stream read as 0.  Returns the number of words consumed. */
+uint32_t cgo_rc_decode(const uint16_t *words, uint32_t nw, uint32_t m, const uint16_t *f,
+                       uint32_t N, uint8_t *x_out)
+{
+    uint32_t cdf[CGO_MAX_BINS + 1];
+    cdf[0] = 0;
+    for (uint32_t s = 0; s < N; s++)
+        cdf[s + 1] = cdf[s] + f[s];
+    if (m == 0)
+        return 0;
+    uint32_t pos = 0;
+#define NEXTW() (pos < nw ? words[pos++] : (pos++, 0u))
+    uint32_t code = NEXTW();
+    code = (code << 16) | NEXTW();
+    uint32_t range = CGO_RANGE_INIT;
+    for (uint32_t i = 0; i < m; i++) {
+        uint32_t q = range >> CGO_PROB_BITS;
+        uint32_t s = 0;
+        for (uint32_t j = 1; j < N; j++)
+            if (q * cdf[j] <= code)
+                s = j;
+        code -= q * cdf[s];
+        range = q * f[s];
+        x_out[i] = (uint8_t)s;
+        if (i + 1 < m && range < CGO_RENORM_BELOW) {
+            code = (code << 16) | NEXTW();
+            range <<= 16;
+        }
+    }
+#undef NEXTW
+    return pos;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Container pieces.                                                                */
+/*   group  = (chunk k, layer l, K/V kv, block b) with lanes 0..63 <-> channels      */
+/*            64b .. 64b+63 (channels >= C absent); groups are numbered in that      */
+/*            row-major order over chunks [k_begin, k_end).                          */
+/*   A group's word sequence holds the words of all its lanes' streams in the order  */
+/*   the 64 decoders read them when they run in lockstep: first words 0 and 1 of     */
+/*   lane 0, lane 1, ...; then, for step i = 0 .. m-2, the word each lane reads at   */
+/*   step i, lanes in ascending order.                                               */
+/*   offsets[g] = first word of group g in the payload, offsets[n_groups] = total.   */
+/*   anchors: fp16, for each chunk (ascending) [L][2][groups of the chunk][C].       */
+/* ------------------------------------------------------------------------------ */
+
+static uint32_t n_blocks(uint32_t C) { return (C + CGO_LANES - 1) / CGO_LANES; }
+
+uint64_t cgo_num_groups(uint32_t L, uint32_t C, uint32_t k_begin, uint32_t k_end)
+{
+    return (uint64_t)(k_end - k_begin) * L * 2 * n_blocks(C);
+}
+
+uint64_t cgo_anchor_rows(uint32_t L, uint32_t S, uint32_t G, uint32_t Tc, uint32_t k_begin,
+                         uint32_t k_end)
+{
+    uint64_t rows = 0;
+    for (uint32_t k = k_begin; k < k_end; k++)
+        rows += (uint64_t)L * 2 * cgo_groups_in(cgo_chunk_len(S, Tc, k), G);
+    return rows;
+}
+
+/* Copies anchors into anchors_out ([rows][C] fp16). */
+void cgo_anchors(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
+                 const uint16_t *X, uint32_t k_begin, uint32_t k_end, uint16_t *anchors_out)
+{
+    cgo_shape p = {L, H, d, S, G, Tc, NULL};
+    uint32_t C = H * d;
+    size_t row = 0;
+    for (uint32_t k = k_begin; k < k_end; k++) {
+        uint32_t len = cgo_chunk_len(S, Tc, k), ng = cgo_groups_in(len, G);
+        for (uint32_t l = 0; l < L; l++)
+            for (uint32_t kv = 0; kv < 2; kv++)
+                for (uint32_t g = 0; g < ng; g++, row++)
+                    for (uint32_t c = 0; c < C; c++)
+                        anchors_out[row * C + c] = X[kv_index(&p, l, kv, k * Tc + g * G, c)];
+    }
+}
+
+/* Encodes chunks [k_begin, k_end).  Writes offsets (n_groups + 1 entries) and the
+ * payload; returns the total number of words, or -1 if payload_cap is too small. */
+int64_t cgo_encode_payload(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G,
+                           uint32_t Tc, const uint8_t *bins, const uint8_t *sym,
+                           const uint16_t *freqs, uint32_t k_begin, uint32_t k_end,
+                           uint64_t *offsets, uint16_t *payload, uint64_t payload_cap)
+{
+    cgo_shape p = {L, H, d, S, G, Tc, bins};
+    uint32_t C = H * d, NB = n_blocks(C);
+    uint64_t total = 0, g = 0;
+    uint8_t *x = (uint8_t *)malloc(Tc + 1);
+    uint16_t *w[CGO_LANES];
+    int32_t *st[CGO_LANES];
+    uint32_t nw[CGO_LANES], rd[CGO_LANES];
+    for (uint32_t i = 0; i < CGO_LANES; i++) {
+        w[i] = (uint16_t *)malloc(sizeof(uint16_t) * (Tc + 2));
+        st[i] = (int32_t *)malloc(sizeof(int32_t) * (Tc + 2));
+    }
+    int64_t result = 0;
+    for (uint32_t k = k_begin; k < k_end && result == 0; k++) {
+        uint32_t t0 = k * Tc, len = cgo_chunk_len(S, Tc, k);
+        for (uint32_t l = 0; l < L; l++)
+            for (uint32_t kv = 0; kv < 2; kv++)
+                for (uint32_t b = 0; b < NB; b++, g++) {
+                    offsets[g] = total;
+                    uint32_t lanes = (C - b * CGO_LANES < CGO_LANES) ? C - b * CGO_LANES : CGO_LANES;
+                    uint32_t m = 0;
+                    for (uint32_t lane = 0; lane < lanes; lane++) {
+                        uint32_t c = b * CGO_LANES + lane;
+                        m = 0;
+                        for (uint32_t t = t0; t < t0 + len; t++)
+                            if (!cgo_is_anchor(t, G, Tc))
+                                x[m++] = sym[kv_index(&p, l, kv, t, c)];
+                        size_t row = ((size_t)l * 2 + kv) * C + c;
+                        nw[lane] = cgo_rc_encode(x, m, freqs + row * CGO_MAX_BINS, bins[l],
+                                                 w[lane], st[lane]);
+                        rd[lane] = 0;
+                    }
+                    /* merge in the order the lockstep decoders read the words */
+                    uint64_t need = 0;
+                    for (uint32_t lane = 0; lane < lanes; lane++)
+                        need += nw[lane];
+                    if (total + need > payload_cap) {
+                        result = -1;
+                        break;
+                    }
+                    for (int32_t step = -1; step < (int32_t)m; step++)
+                        for (uint32_t lane = 0; lane < lanes; lane++)
+                            while (rd[lane] < nw[lane] && st[lane][rd[lane]] == step)
+                                payload[total++] = w[lane][rd[lane]++];
+                }
+    }
+    if (result == 0) {
+        offsets[g] = total;
+        result = (int64_t)total;
+    }
+    for (uint32_t i = 0; i < CGO_LANES; i++) {
+        free(w[i]);
+        free(st[i]);
+    }
+    free(x);
+    return result;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Step 5: decode chunks [k_begin, k_end) into out ([L][2][S][C] fp16):             */
+/*   anchors are copied bit for bit;                                                 */
+/*   other tokens: y = fp16_rne(f32(anchor) + fma(f32(q), w, lo)).                   */
+/* Lanes of a group run in lockstep so that they read the interleaved words in the   */
+/* order they were written.  Reads past the group's end return 0.                    */
+/* Returns 0, or -5 when a group's declared extent is inconsistent.                  */
+/* ------------------------------------------------------------------------------ */
+int cgo_decode(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
+               const uint8_t *bins, const float *lo, const float *w, const uint16_t *freqs,
+               uint32_t k_begin, uint32_t k_end, const uint64_t *offsets,
+               const uint16_t *payload, uint64_t payload_words, const uint16_t *anchors,
+               uint16_t *out)
+{
+    cgo_shape p = {L, H, d, S, G, Tc, bins};
+    uint32_t C = H * d, NB = n_blocks(C);
+    uint64_t g = 0, arow_chunk = 0;
+    for (uint32_t k = k_begin; k < k_end; k++) {
+        uint32_t t0 = k * Tc, len = cgo_chunk_len(S, Tc, k), ng = cgo_groups_in(len, G);
+        uint32_t m = len - ng;
+        for (uint32_t l = 0; l < L; l++)
+            for (uint32_t kv = 0; kv < 2; kv++) {
+                const uint16_t *arows = anchors + (arow_chunk + ((uint64_t)l * 2 + kv) * ng) * C;
+                /* anchors, bit-exact */
+                for (uint32_t gi = 0; gi < ng; gi++)
+                    for (uint32_t c = 0; c < C; c++)
+                        out[kv_index(&p, l, kv, t0 + gi * G, c)] = arows[(size_t)gi * C + c];
+                for (uint32_t b = 0; b < NB; b++, g++) {
+                    uint64_t beg = offsets[g], end = offsets[g + 1];
+                    if (end < beg || end > payload_words)
+                        return -5;
+                    uint32_t lanes = (C - b * CGO_LANES < CGO_LANES) ? C - b * CGO_LANES : CGO_LANES;
+                    uint32_t code[CGO_LANES], range[CGO_LANES], cdf[CGO_LANES][CGO_MAX_BINS + 1];
+                    uint64_t cur = beg;
+                    if (m == 0)
+                        continue;
+#define GROUPW() (cur < end ? payload[cur++] : (cur++, 0u))
+                    for (uint32_t lane = 0; lane < lanes; lane++) {
+                        size_t row = ((size_t)l * 2 + kv) * C + b * CGO_LANES + lane;
+                        cdf[lane][0] = 0;
+                        for (uint32_t s = 0; s < bins[l]; s++)
+                            cdf[lane][s + 1] = cdf[lane][s] + freqs[row * CGO_MAX_BINS + s];
+                        uint32_t hi16 = GROUPW();
+                        code[lane] = (hi16 << 16) | GROUPW();
+                        range[lane] = CGO_RANGE_INIT;
+                    }
+                    uint32_t i = 0;
+                    for (uint32_t t = t0; t < t0 + len; t++) {
+                        if (cgo_is_anchor(t, G, Tc))
+                            continue;
+                        uint32_t a = cgo_anchor_of(t, G, Tc);
+                        for (uint32_t lane = 0; lane < lanes; lane++) {
+                            uint32_t c = b * CGO_LANES + lane;
+                            size_t row = ((size_t)l * 2 + kv) * C + c;
+                            uint32_t q = range[lane] >> CGO_PROB_BITS, s = 0;
+                            for (uint32_t j = 1; j < bins[l]; j++)
+                                if (q * cdf[lane][j] <= code[lane])
+                                    s = j;
+                            code[lane] -= q * cdf[lane][s];
+                            range[lane] = q * (cdf[lane][s + 1] - cdf[lane][s]);
+                            float anchor = cgo_half_to_float(out[kv_index(&p, l, kv, a, c)]);
+                            float y = anchor + fmaf((float)s, w[row], lo[row]);
+                            out[kv_index(&p, l, kv, t, c)] = cgo_float_to_half(y);
+                        }
+                        if (i + 1 < m)
+                            for (uint32_t lane = 0; lane < lanes; lane++)
+                                if (range[lane] < CGO_RENORM_BELOW) {
+                                    code[lane] = (code[lane] << 16) | GROUPW();
+                                    range[lane] <<= 16;
+                                }
+                        i++;
+                    }
+#undef GROUPW
+                }
+            }
+        arow_chunk += (uint64_t)L * 2 * ng;
+    }
+    return 0;
+}
+
+/* Dequantization of a symbol tensor (the unfused path): same formula as above. */
+void cgo_dequantize(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
+                    const float *lo, const float *w, const uint8_t *sym, const uint16_t *X_anchor_src,
+                    uint32_t t_begin, uint32_t t_end, uint16_t *out)
+{
+    cgo_shape p = {L, H, d, S, G, Tc, NULL};
+    uint32_t C = H * d;
+    for (uint32_t l = 0; l < L; l++)
+        for (uint32_t kv = 0; kv < 2; kv++)
+            for (uint32_t t = t_begin; t < t_end; t++)
+                for (uint32_t c = 0; c < C; c++) {
+                    size_t i = kv_index(&p, l, kv, t, c);
+                    uint32_t a = cgo_anchor_of(t, G, Tc);
+                    uint16_t ah = X_anchor_src[kv_index(&p, l, kv, a, c)];
+                    if (a == t) {
+                        out[i] = ah;
+                        continue;
+                    }
+                    size_t row = ((size_t)l * 2 + kv) * C + c;
+                    float y = cgo_half_to_float(ah) + fmaf((float)sym[i], w[row], lo[row]);
+                    out[i] = cgo_float_to_half(y);
+                }
+}

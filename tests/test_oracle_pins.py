@@ -1,0 +1,392 @@
+"""Pins of the CPU oracle to facts fixed by the pages or by mathematics.
+
+Every check here is independent of the oracle's own code: printed sizes from the pages,
+a by-hand transcription of the pages' windowing, numpy's IEEE fp16 conversion, exact
+rational arithmetic, exhaustive round trips, a big-integer model of the coder with no
+window or carry logic, and a sort-based model of the stream interleaving.
+"""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle as O
+from kv_cache_compression_cg_amd import configs, synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+T = O.PROB_TOTAL
+
+
+def _rows(name):
+    out = []
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            out.append(line.split())
+    return out
+
+
+# --------------------------------------------------------------------------- sizes
+def test_kv_size_formula_matches_printed_sizes():
+    for name, L, H, d, S, sz, printed, div, *_ in _rows("kv_sizes.txt"):
+        nbytes = 2 * int(L) * int(H) * int(d) * int(S) * int(sz)
+        v = nbytes / int(div)
+        p = float(printed)
+        step = 10 ** -(len(printed.split(".")[1]) if "." in printed else 0)
+        assert p <= v < p + step, (name, v, p)
+
+
+def test_workload_raw_bytes_are_the_formula():
+    for w in configs.ALL.values():
+        assert w.raw_bytes == 2 * w.L * w.H_kv * w.d * w.S * 2
+    assert configs.LLAMA3_70B.raw_bytes == 10_737_418_240
+    assert configs.LLAMA3_70B_131K.raw_bytes == 42_949_672_960
+    assert configs.LLAMA7B.raw_bytes == 637_534_208
+
+
+# --------------------------------------------------------------------------- segmentation
+def _page_windows(n_tokens, W):
+    """Transcription of the pages' windowing: windows start at 0, W, 2W, ...; the first
+    token of each window is its anchor; the last window may be short."""
+    anchors, owner = [], {}
+    for wi in range(math.ceil(n_tokens / W)):
+        start = wi * W
+        end = min(start + W, n_tokens)
+        anchors.append(start)
+        for t in range(start, end):
+            owner[t] = start
+    return anchors, owner
+
+
+def test_anchor_counts_golden():
+    lib = O.lib()
+    for S, G, Tc, _lens, expect in _rows("anchor_counts.txt"):
+        S, G, Tc, expect = int(S), int(G), int(Tc), int(expect)
+        shp = O.Shape.make(1, 1, 1, S, G, Tc, [8])
+        assert O.anchor_rows(shp, 0, shp.n_chunks) // 2 == expect
+        assert sum(1 for t in range(S) if lib.cgo_is_anchor(t, G, Tc)) == expect
+
+
+@settings(max_examples=60, deadline=None)
+@given(S=st.integers(1, 300), G=st.integers(1, 40), Tc=st.integers(1, 120))
+def test_segmentation_matches_page_windowing(S, G, Tc):
+    lib = O.lib()
+    for k in range(math.ceil(S / Tc)):
+        t0 = k * Tc
+        n = min(Tc, S - t0)
+        assert lib.cgo_chunk_len(S, Tc, k) == n
+        anchors, owner = _page_windows(n, G)
+        assert lib.cgo_groups_in(n, G) == len(anchors)
+        for u in range(n):
+            assert bool(lib.cgo_is_anchor(t0 + u, G, Tc)) == (u in anchors)
+            assert lib.cgo_anchor_of(t0 + u, G, Tc) == t0 + owner[u]
+
+
+# --------------------------------------------------------------------------- fp16
+def test_half_to_float_all_patterns():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float32)
+    got = O.half_to_float(h)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin].view(np.uint32), ref[fin].view(np.uint32))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[np.isinf(ref)], ref[np.isinf(ref)])
+
+
+def test_float_to_half_rne_against_numpy():
+    rng = np.random.default_rng(1)
+    halves = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    halves = halves[np.isfinite(halves)].astype(np.float32)
+    # exact values, every midpoint between neighbours (ties), and points near them
+    s = np.sort(np.unique(halves))
+    mids = ((s[:-1].astype(np.float64) + s[1:]) / 2).astype(np.float32)
+    cases = [halves, mids, np.nextafter(mids, np.float32(np.inf)),
+             np.nextafter(mids, np.float32(-np.inf)),
+             rng.standard_normal(200000).astype(np.float32) * np.float32(300),
+             (rng.standard_normal(200000) * 1e-6).astype(np.float32),
+             np.array([65504, 65519.99, 65520, 65536, 1e30, -65520, 2 ** -25, 2 ** -24,
+                       3 * 2 ** -26, 2 ** -14, 0.0, -0.0], np.float32)]
+    for f in cases:
+        with np.errstate(over="ignore"):
+            ref = f.astype(np.float16).view(np.uint16)
+        got = O.float_to_half(f)
+        assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------- tables
+def _small_data(L=2, S=70, C=6, G=5, Tc=33, bins=(4, 8), seed=3, heavy=True):
+    gen = configs.GenSpec(rho=0.85, heavy_tail=heavy, outlier_frac=0.2, outlier_mult=30.0,
+                          seed=seed)
+    X = synth.gen_custom(L, S, C, gen).view(torch.int16).numpy().view(np.uint16)
+    shp = O.Shape.make(L, 1, C, S, G, Tc, bins)
+    return shp, np.ascontiguousarray(X)
+
+
+def _deltas(shp, X, l, kv, c):
+    """(t, anchor, Delta) with Delta from numpy's float32 arithmetic."""
+    xs = X[l, kv, :, c].view(np.float16).astype(np.float32)
+    out = []
+    for t in range(shp.S):
+        u = t % shp.Tc
+        if u % shp.G == 0:
+            continue
+        a = t - u + (u // shp.G) * shp.G
+        out.append((t, a, np.float32(xs[t] - xs[a])))
+    return out
+
+
+def test_range_is_min_max_of_deltas():
+    shp, X = _small_data()
+    tab = O.build_tables(shp, X)
+    for l in range(shp.L):
+        for kv in range(2):
+            for c in range(shp.C):
+                d = np.array([x for _, _, x in _deltas(shp, X, l, kv, c)], np.float32)
+                lo, hi = d.min(), d.max()
+                assert tab.lo[l, kv, c] == lo
+                w = np.float32(np.float32(hi - lo) / np.float32(shp.bins[l] - 1))
+                assert tab.w[l, kv, c] == w
+                assert tab.r[l, kv, c] == (np.float32(1) / w if w > 0 else 0)
+
+
+def test_quantizer_picks_nearest_grid_point_exactly():
+    """q must minimise |Delta - (lo + q*w)| over the N grid points (exact rationals);
+    a different choice is only allowed within 2^-20 relative of a tie."""
+    shp, X = _small_data(L=2, S=90, C=5, bins=(3, 16))
+    tab = O.build_tables(shp, X)
+    sym = O.quantize(shp, X, tab.lo, tab.r, 0, shp.S)
+    checked = 0
+    for l in range(shp.L):
+        N = int(shp.bins[l])
+        for kv in range(2):
+            for c in range(shp.C):
+                lo, w = Fraction(float(tab.lo[l, kv, c])), Fraction(float(tab.w[l, kv, c]))
+                for t, _, dlt in _deltas(shp, X, l, kv, c):
+                    D = Fraction(float(dlt))
+                    q = int(sym[l, kv, t, c])
+                    err = abs(D - (lo + q * w))
+                    best = min(abs(D - (lo + j * w)) for j in range(N))
+                    assert err <= best + w * Fraction(1, 2 ** 20)
+                    assert err <= w / 2 * (1 + Fraction(1, 2 ** 20))
+                    checked += 1
+    assert checked > 1000
+
+
+def test_constant_channel_and_all_anchor_edge_cases():
+    S, C, G, Tc = 23, 3, 4, 10
+    X = np.zeros((1, 2, S, C), np.uint16)
+    X[0, 0, :, 0] = np.float16(1.5).view(np.uint16)           # constant channel
+    X[0, 0, :, 1] = np.arange(S).astype(np.float16).view(np.uint16)  # deltas 1, 2, 3
+    shp = O.Shape.make(1, 1, C, S, G, Tc, [3])                        # grid 1, 2, 3
+    tab = O.build_tables(shp, X)
+    assert tab.w[0, 0, 0] == 0 and tab.r[0, 0, 0] == 0 and tab.lo[0, 0, 0] == 0
+    enc = O.encode(shp, X, tab)
+    assert np.array_equal(O.decode(shp, tab, enc), X)         # exact for both channels
+    # G = 1: every token is an anchor, the payload is empty, decode is a copy
+    shp1 = O.Shape.make(1, 1, C, S, 1, Tc, [8])
+    tab1 = O.build_tables(shp1, X)
+    enc1 = O.encode(shp1, X, tab1)
+    assert enc1.payload.size == 0 and np.array_equal(O.decode(shp1, tab1, enc1), X)
+
+
+@settings(max_examples=200, deadline=None)
+@given(N=st.integers(2, 32), data=st.data())
+def test_frequency_table_invariants(N, data):
+    counts = data.draw(st.lists(st.one_of(st.integers(0, 3), st.integers(0, 10 ** 6)),
+                                min_size=N, max_size=N))
+    f = O.freqs_from_counts(counts, N).astype(np.int64)
+    assert f.sum() == T and (f >= 1).all()
+    n = sum(counts)
+    for a in range(N):
+        for b in range(N):
+            if counts[a] > counts[b]:
+                assert f[a] >= f[b]
+        if n:
+            assert abs(Fraction(int(f[a]), T) - Fraction(counts[a], n)) <= Fraction(N + 1, T)
+    if n == 0:
+        assert f[0] == T - N + 1 and (f[1:] == 1).all()
+
+
+# --------------------------------------------------------------------------- range coder
+def _big_model(x, f):
+    """Exact big-integer model of the coder (no 32-bit window, no carry handling)."""
+    cdf = np.concatenate([[0], np.cumsum(f)]).astype(int)
+    L, R, scale_words, events = 0, 2 ** 32 - 1, 0, []
+    for i, s in enumerate(x):
+        q = R // T
+        L += q * int(cdf[s])
+        R = q * int(f[s])
+        if i + 1 < len(x) and R < 2 ** 16:
+            L *= 2 ** 16
+            R *= 2 ** 16
+            scale_words += 1
+            events.append(i)
+    nw = 2 + scale_words
+    assert L + R <= (2 ** 32) * 2 ** (16 * scale_words)
+    words = [(L >> (16 * (nw - 1 - j))) & 0xFFFF for j in range(nw)]
+    steps = [-1, -1] + events
+    return words, steps
+
+
+FREQ_SETS = [[T // 2, T // 2], [1, T - 1], [T - 1, 1], [1, 1, T - 3, 1], [1000, 1000, 1000, 1096],
+             [1, 2, 3, T - 6], [7, 4081, 7, 1]]
+
+
+def test_coder_exhaustive_round_trip_and_big_integer_model():
+    n_cases = 0
+    for f in FREQ_SETS:
+        N = len(f)
+        for m in range(0, 7):
+            for x in itertools.product(range(N), repeat=m):
+                words, steps = O.rc_encode(x, f)
+                if m == 0:
+                    assert words.size == 0
+                    continue
+                bw, bs = _big_model(x, f)
+                assert list(words) == bw and list(steps) == bs
+                dec, used = O.rc_decode(words, m, f)
+                assert list(dec) == list(x) and used == len(words)
+                n_cases += 1
+    assert n_cases > 10000
+
+
+@settings(max_examples=150, deadline=None)
+@given(data=st.data())
+def test_coder_random_streams_against_big_model_and_length_bound(data):
+    N = data.draw(st.integers(2, 32))
+    counts = data.draw(st.lists(st.integers(0, 5000), min_size=N, max_size=N))
+    f = O.freqs_from_counts(counts, N)
+    p = f / f.sum()
+    m = data.draw(st.integers(1, 1500))
+    rng = np.random.default_rng(data.draw(st.integers(0, 2 ** 31)))
+    x = rng.choice(N, size=m, p=p)
+    words, steps = O.rc_encode(x, f)
+    bw, bs = _big_model(x, f)
+    assert list(words) == bw and list(steps) == bs
+    dec, used = O.rc_decode(words, m, f)
+    assert np.array_equal(dec, x) and used == len(words)
+    # each step loses at most log2(16/15) bits (range >= 2^16 before every step)
+    ideal = float(np.sum(np.log2(T / f[x].astype(np.float64))))
+    assert 16 * len(words) <= ideal + m * math.log2(16 / 15) + 32 + 1e-6
+
+
+def test_coded_size_close_to_empirical_entropy():
+    """Over realistic streams the coder spends within a few percent of the empirical
+    entropy of the channel's symbols (plus the two flushed words per stream)."""
+    shp, X = _small_data(L=2, S=1200, C=8, G=10, Tc=400, bins=(8, 32), seed=5)
+    tab = O.build_tables(shp, X)
+    enc = O.encode(shp, X, tab)
+    cnt = tab.counts.astype(np.float64)
+    n = cnt.sum(-1, keepdims=True)
+    p = np.where(cnt > 0, cnt / np.maximum(n, 1), 1.0)
+    h_emp_bits = float(-(cnt * np.log2(p)).sum())
+    n_streams = shp.L * 2 * shp.C * shp.n_chunks
+    coded = enc.payload.size * 16
+    assert coded <= 1.03 * h_emp_bits + 32 * n_streams
+    assert coded >= h_emp_bits * 0.99
+
+
+# --------------------------------------------------------------------------- interleaving
+def test_group_words_follow_lockstep_read_order():
+    """Sort-based model: every word of every lane, keyed by (read step, lane, index)."""
+    shp, X = _small_data(L=1, S=150, C=70, G=6, Tc=64, bins=(16,), seed=9)
+    tab = O.build_tables(shp, X)
+    enc = O.encode(shp, X, tab)
+    sym = O.quantize(shp, X, tab.lo, tab.r, 0, shp.S)
+    NB = -(-shp.C // O.LANES)
+    g = 0
+    for k in range(shp.n_chunks):
+        t0 = k * shp.Tc
+        toks = [t for t in range(t0, min(t0 + shp.Tc, shp.S)) if (t - t0) % shp.G]
+        for l in range(shp.L):
+            for kv in range(2):
+                for b in range(NB):
+                    keyed = []
+                    for lane in range(min(O.LANES, shp.C - b * O.LANES)):
+                        c = b * O.LANES + lane
+                        x = [int(sym[l, kv, t, c]) for t in toks]
+                        words, steps = O.rc_encode(x, tab.freqs[l, kv, c, :shp.bins[l]])
+                        keyed += [((int(s), lane, j), int(wd))
+                                  for j, (wd, s) in enumerate(zip(words, steps))]
+                    expect = [wd for _, wd in sorted(keyed)]
+                    got = enc.payload[enc.offsets[g]:enc.offsets[g + 1]]
+                    assert list(got) == expect
+                    g += 1
+    assert g == len(enc.offsets) - 1
+
+
+# --------------------------------------------------------------------------- reconstruction
+def _check_reconstruction(shp, X, tab, Y):
+    C = shp.C
+    xs = X.view(np.float16).astype(np.float64)
+    ys = Y.view(np.float16).astype(np.float64)
+    for t in range(shp.S):
+        u = t % shp.Tc
+        a = t - u + (u // shp.G) * shp.G
+        if a == t:
+            assert np.array_equal(Y[:, :, t], X[:, :, t])
+            continue
+        wv = tab.w.astype(np.float64)
+        ulp = np.spacing(np.abs(ys[:, :, t]).astype(np.float16)).astype(np.float64)
+        tol = (wv / 2 * (1 + 2 ** -20) + ulp / 2 +
+               2 ** -22 * (np.abs(xs[:, :, t]) + np.abs(xs[:, :, a]) + np.abs(tab.lo) + 32 * wv))
+        assert (np.abs(xs[:, :, t] - ys[:, :, t]) <= tol).all()
+    assert C > 0
+
+
+def test_round_trip_error_is_at_most_half_a_bin():
+    for heavy in (False, True):
+        shp, X = _small_data(L=3, S=333, C=16, G=10, Tc=128, bins=(2, 8, 32), heavy=heavy)
+        tab = O.build_tables(shp, X)
+        enc = O.encode(shp, X, tab)
+        Y = O.decode(shp, tab, enc)
+        _check_reconstruction(shp, X, tab, Y)
+        sym = O.quantize(shp, X, tab.lo, tab.r, 0, shp.S)
+        assert np.array_equal(O.dequantize(shp, tab, sym, X, 0, shp.S), Y)
+
+
+def test_brute_force_tiny_tensor_exact_rationals():
+    """L=1, S=12, C=2, G=4, N=4: grid, symbols and reconstruction from exact rationals."""
+    rng = np.random.default_rng(11)
+    X = (rng.standard_normal((1, 2, 12, 2)) * 3).astype(np.float16).view(np.uint16)
+    X = np.ascontiguousarray(X)
+    shp = O.Shape.make(1, 1, 2, 12, 4, 12, [4])
+    tab = O.build_tables(shp, X)
+    enc = O.encode(shp, X, tab)
+    Y = O.decode(shp, tab, enc)
+    xf = X.view(np.float16)
+    for kv in range(2):
+        for c in range(2):
+            D = {t: Fraction(float(np.float32(np.float32(xf[0, kv, t, c]) -
+                                              np.float32(xf[0, kv, t - t % 4, c]))))
+                 for t in range(12) if t % 4}
+            lo, hi = min(D.values()), max(D.values())
+            assert Fraction(float(tab.lo[0, kv, c])) == lo
+            w = (hi - lo) / 3
+            assert abs(Fraction(float(tab.w[0, kv, c])) - w) <= w * Fraction(1, 2 ** 23)
+            for t, d in D.items():
+                grid = [lo + j * w for j in range(4)]
+                j = min(range(4), key=lambda j: (abs(d - grid[j]), -j))
+                y = Fraction(float(xf[0, kv, t - t % 4, c])) + grid[j]
+                got = Fraction(float(Y[0, kv, t, c].view(np.float16)))
+                assert abs(got - y) <= abs(y) * Fraction(1, 2 ** 10) + Fraction(1, 2 ** 20)
+
+
+def test_decode_of_damaged_payload_stays_in_bounds():
+    shp, X = _small_data(L=1, S=200, C=64, G=10, Tc=100, bins=(16,), seed=2)
+    tab = O.build_tables(shp, X)
+    enc = O.encode(shp, X, tab)
+    rng = np.random.default_rng(0)
+    bad = enc.payload.copy()
+    bad[rng.integers(0, bad.size, 50)] ^= np.uint16(0x5A5A)
+    Y = O.decode(shp, tab, enc, payload=bad)
+    assert Y.shape == X.shape
+    trunc = enc.payload[: enc.payload.size // 2]
+    O.decode(shp, tab, O.Encoded(enc.k_begin, enc.k_end,
+                                 np.minimum(enc.offsets, trunc.size).astype(np.uint64),
+                                 trunc, enc.anchors))
