@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV-cache codec on one MI355X.
+
+One step = one pass of the whole hot path over the Llama-3-70B-shaped cache
+(L=80, H_kv=8, d=128, S=32768, fp16, 10.74 GB; anchor interval 10, 1536-token chunks,
+bins 32 / 16 / 8 for layers 0-19 / 20-39 / 40-79): cg_build_cdf (range, quantize,
+histogram, frequency tables), cg_encode (delta + quantize, range coding, interleaving)
+and cg_decode (range decode fused with dequantize + anchor-add) back to fp16.
+
+Reported `value`: cg_decode throughput in GB/s of raw fp16 KV reconstructed (the
+metric), from HIP events around each decode on the stream it runs on, averaged over
+the timed steps.  `ms_per_step` is the wall time of a whole step.  The input is
+resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, vendor figure
+METRIC = "cg_decode GB/s of raw fp16 KV reconstructed (% HBM peak); compression ratio"
+CPU_SAMPLE_LAYERS = (0, 10, 20, 30, 40, 50, 60, 70)   # bin tiers 32:16:8 in the ratio 2:2:4
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k3_decode_llama3_70b_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "kv_cache_compression_cg_amd", "csrc", "cg_kernels.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def table_bytes_read(tables) -> int:
+    """Decode-table bytes the decoder stages into LDS: per (layer, K/V, 64-channel
+    block), P = next power of two >= bins entries x 64 lanes x 8 bytes."""
+    nb = -(-tables.C // 64)
+    tot = 0
+    for b in tables.bins:
+        p = 1
+        while p < b:
+            p *= 2
+        tot += 2 * nb * p * 64 * 8
+    return tot
+
+
+def measured_traffic(alg_bytes: float):
+    """HBM bytes per decode launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counters, if they were taken on the current kernel source."""
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(w, X, max_threads: int) -> dict:
+    """The oracle (as it stands) decoding a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    cores = max(1, min(max_threads, os.cpu_count() or 1))
+    layers = CPU_SAMPLE_LAYERS
+    host = {l: np.ascontiguousarray(X[l:l + 1].cpu().view(torch.int16).numpy().view(np.uint16))
+            for l in layers}
+    shapes = {l: O.Shape.make(1, w.H_kv, w.d, w.S, w.group, w.chunk, [w.bins[l]]) for l in layers}
+    t = time.time()
+    with cf.ThreadPoolExecutor(cores) as ex:
+        tabs = dict(zip(layers, ex.map(lambda l: O.build_tables(shapes[l], host[l]), layers)))
+        # split each layer into chunk ranges so the decode spreads over every thread
+        per = max(1, -(-w.n_chunks * len(layers) // (2 * cores)))
+        items = [(l, k0, min(k0 + per, w.n_chunks)) for l in layers
+                 for k0 in range(0, w.n_chunks, per)]
+        encs = list(ex.map(lambda it: O.encode(shapes[it[0]], host[it[0]], tabs[it[0]],
+                                               it[1], it[2]), items))
+        log("[cpu] oracle prep (tables + encode of %d layers) %.1fs" % (len(layers),
+                                                                       time.time() - t))
+        outs = {l: np.zeros((1, 2, w.S, w.C), np.uint16) for l in layers}
+        t0 = time.perf_counter()
+        list(ex.map(lambda ie: O.decode(shapes[ie[0][0]], tabs[ie[0][0]], ie[1],
+                                        out=outs[ie[0][0]]), zip(items, encs)))
+        dt = time.perf_counter() - t0
+    for l in layers:
+        assert np.array_equal(outs[l][:, :, ::w.group][:, :, :w.chunk // w.group],
+                              host[l][:, :, ::w.group][:, :, :w.chunk // w.group])
+    raw = len(layers) * 2 * w.C * w.S * 2
+    return {"value": round(raw / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "oracle decode of layers %s (all 22 chunks, K and V; %.2f GB raw), "
+                      "%d threads over (layer, chunk-range) items, %.2fs wall"
+                      % (list(layers), raw / 1e9, cores, dt)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama3_70b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the codec runs on a single MI355X "
+              "(multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from kv_cache_compression_cg_amd import build, configs, synth
+    if not os.path.exists(build.LIB):
+        build.build()
+    from kv_cache_compression_cg_amd import cg
+
+    w = configs.ALL[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = time.time()
+    X = synth.gen_kv(w, device=dev)
+    out = torch.empty_like(X)
+    torch.cuda.synchronize()
+    log("[bench] %s: generated %.2f GB in %.1fs" % (w.name, w.raw_bytes / 1e9, time.time() - t))
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ts = time.perf_counter()
+        tab = cg.build_cdf(X, w.group, w.chunk, w.bins, H_kv=w.H_kv)
+        blob = cg.encode(tab, X)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cg.decode(tab, blob, out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        te = time.perf_counter()
+        return e0.elapsed_time(e1), (te - ts) * 1e3, tab, blob
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs, last = [], None
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        last = None                      # the previous step's handles are released here
+        dms, sms, tab, blob = step()
+        recs.append((dms, sms))
+        last = (tab, blob)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    tab, blob = last
+    dec_ms = [r[0] for r in recs]
+    step_ms = [r[1] for r in recs]
+    dec_mean = sum(dec_ms) / len(dec_ms)
+    value = w.raw_bytes / (dec_mean * 1e-3) / 1e9
+
+    # sanity: anchors bit-exact, first layer within half a bin
+    tt = torch.arange(w.S, device=dev)
+    anchor = ((tt % w.chunk) % w.group) == 0
+    assert torch.equal(out[:, :, anchor].view(torch.int16), X[:, :, anchor].view(torch.int16))
+    ex = tab.export()
+    wv = torch.from_numpy(ex["w"][0]).to(dev)[:, None, :]
+    err = (X[0].float() - out[0].float()).abs()
+    assert bool((err <= wv / 2 * 1.001 + 2 ** -10 * X[0].float().abs() + 1e-6).all())
+
+    comp = cg.compressed_bytes(tab, [blob])
+    alg = w.raw_bytes + blob.nbytes + table_bytes_read(tab)
+    achieved = alg / (dec_mean * 1e-3) / 1e9
+    roofline = {"kernel": "k3_decode", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(alg),
+                "algorithmic_bytes_per_launch": alg}
+    h = blob.header
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u32+f32", "data": "synthetic",
+        "config": {"workload": w.name, "L": w.L, "H_kv": w.H_kv, "d": w.d, "S": w.S,
+                   "group": w.group, "chunk": w.chunk,
+                   "bins": "32 (layers 0-19) / 16 (20-39) / 8 (40-79)",
+                   "raw_bytes": w.raw_bytes, "parallelism": "single GPU"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "compression_ratio": round(w.raw_bytes / comp, 4),
+        "compressed_bytes": {"total": comp, "payload": 2 * h["payload_words"],
+                             "anchors": h["anchors_bytes"],
+                             "offsets_and_header": h["payload_offset"] - h["anchors_bytes"],
+                             "tables": tab.stored_bytes},
+        "decode_ms": round(dec_mean, 4), "decode_ms_min": round(min(dec_ms), 4),
+        "encode_ms": round(sum(step_ms) / len(step_ms) - dec_mean, 3),
+        "roofline": roofline,
+    }
+    res["encode_GBps"] = round(w.raw_bytes / (res["encode_ms"] * 1e-3) / 1e9, 2)
+    log("[bench] decode %.3f ms (%.1f GB/s, %.1f%% of HBM peak), step %.1f ms, ratio %.3f"
+        % (dec_mean, value, res["pct_hbm_peak"], res["ms_per_step"], res["compression_ratio"]))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, X, args.cpu_threads)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

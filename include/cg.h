@@ -1,0 +1,176 @@
+/*
+ * cg.h -- C ABI of libcg, a CacheGen-style KV-cache codec for AMD MI355X (gfx950).
+ *
+ * The codec compresses an fp16 KV cache [L][2][S][C] (C = H_kv * d channels; index 1
+ * is K = 0 / V = 1) into independent bitstreams and decodes it back:
+ *   - tokens are cut into chunks of `chunk` tokens and each chunk into groups of
+ *     `group` tokens whose first token (the anchor) is kept in fp16 ("Guide to
+ *     CacheGen", Solution pillar 2 and Implementation Step 2);
+ *   - every other token is coded as its delta from the anchor, quantized to the
+ *     layer's number of levels, finer for early layers (same page, pillar 1; the
+ *     gptget.net summary of CacheGen, Methodology);
+ *   - the symbols are range-coded with empirical frequency tables per (layer, K/V,
+ *     channel), one stream per (layer, K/V, channel, chunk) (pillar 3; the summary's
+ *     Deep Analysis, Methodology);
+ *   - decoding inverts the coder, dequantizes in float32 and adds the anchor back
+ *     (Implementation Step 1 dequantize_tensor, Step 2 decode_sequence).
+ * The problem statement these calls follow is the pages' KV-size formula
+ * 2 * L * H_kv * d * S * sizeof(dtype) ("Guide to CacheGen", Problem) and the
+ * encode-into-compact-bitstreams / stream-chunks / GPU-decode pipeline (summary,
+ * Methodology).
+ *
+ * Conventions for every call:
+ *   - pointers named *_dev are device pointers on the current HIP device; the caller
+ *     owns them and the streams.  `hip_stream` is a hipStream_t (NULL = null stream).
+ *   - handles (cg_tables, cg_blob) are owned by the library, immutable after creation
+ *     and released with cg_free().  Concurrent cg_decode calls with the same handles on
+ *     different streams are allowed.
+ *   - return value: CG_OK or a negative CG_E_* code; cg_last_error() gives a message
+ *     (thread-local).  No call throws or aborts.
+ *   - limits: 1 <= L, H_kv, d, S; C = H_kv * d a multiple of 8; 1 <= group;
+ *     1 <= chunk <= 16384; 2 <= bins[l] <= 32; L * 2 * S * C < 2^40.
+ */
+#ifndef CG_H
+#define CG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CG_OK 0
+#define CG_E_INVAL (-1)     /* bad argument: null pointer, out-of-range size or chunk range */
+#define CG_E_NOMEM (-2)     /* device or host allocation failed */
+#define CG_E_HIP (-3)       /* HIP runtime error; cg_last_error() holds its text */
+#define CG_E_NONFINITE (-4) /* the KV input holds Inf or NaN */
+#define CG_E_CORRUPT (-5)   /* container and tables do not describe the same cache */
+
+#define CG_MAX_BINS 32
+#define CG_MAX_CHUNK 16384
+#define CG_LANES 64         /* channels per interleaved group of streams */
+#define CG_CONTAINER_MAGIC 0x31474B43u /* "CKG1" */
+
+/* Shape and coding parameters.  `bins` points to L bin counts (host memory, copied). */
+typedef struct cg_params {
+    uint32_t L, H_kv, d, S;
+    uint32_t group;          /* anchor interval G */
+    uint32_t chunk;          /* tokens per chunk (one stream per (layer, K/V, channel, chunk)) */
+    const uint8_t *bins;     /* [L], bins[l] = number of quantization levels of layer l */
+} cg_params;
+
+typedef struct cg_tables cg_tables; /* per-channel ranges and frequency tables (device) */
+typedef struct cg_blob cg_blob;     /* one encoded container (device) */
+
+/*
+ * Container layout (one device buffer, sections 256-byte aligned, little endian):
+ *   header     cg_container_header
+ *   offsets    uint64[n_groups + 1]: first payload word of every group, then the total.
+ *              Groups are (chunk, layer, K/V, block) in row-major order over chunks
+ *              [chunk_begin, chunk_end); block b holds channels 64b .. 64b+63.
+ *   anchors    fp16, for each chunk: [L][2][ceil(len_k / group)][C]
+ *   payload    uint16 words.  A group's words are the words of its (up to) 64 streams
+ *              in the order 64 decoders running in lockstep read them: words 0 and 1
+ *              of every lane in lane order, then at each symbol step the next word of
+ *              every lane that renormalises at that step, in lane order.
+ * Tables are stored separately; cg_tables_info.stored_bytes is their size.
+ */
+typedef struct cg_container_header {
+    uint32_t magic, version;
+    uint32_t L, H_kv, d, S, group, chunk;
+    uint32_t chunk_begin, chunk_end;
+    uint32_t n_blocks, reserved;
+    uint64_t n_groups;
+    uint64_t offsets_offset;  /* byte offset of the offsets section */
+    uint64_t anchors_offset, anchors_bytes;
+    uint64_t payload_offset, payload_words;
+    uint64_t total_bytes;
+} cg_container_header;
+
+typedef struct cg_blob_info {
+    const void *data;             /* device pointer to the container */
+    cg_container_header header;   /* host copy of its header */
+} cg_blob_info;
+
+typedef struct cg_tables_info {
+    uint32_t L, H_kv, d, S, group, chunk;
+    uint64_t stored_bytes;        /* lo, w (4 B each per row) + 2 B per frequency + bins */
+} cg_tables_info;
+
+/*
+ * Builds the per-(layer, K/V, channel) tables from the whole cache: the range of the
+ * anchor deltas, the bin width, and a frequency table of the quantized deltas over all
+ * chunks (T = 4096, every symbol >= 1).
+ *   kv_dev: fp16 [L][2][S][C], read only.
+ *   *out:   receives a new handle on success, untouched on error.
+ * Synchronises `hip_stream` once (to report CG_E_NONFINITE).
+ * Errors: CG_E_INVAL, CG_E_NOMEM, CG_E_HIP, CG_E_NONFINITE.
+ */
+int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream,
+                 cg_tables **out);
+
+/*
+ * Encodes chunks [chunk_begin, chunk_end) of kv_dev (the cache the tables were built
+ * from, or any cache of the same shape) into a new container.
+ * Synchronises `hip_stream` (the payload size is data dependent); the container is
+ * complete when the call returns.
+ * Errors: CG_E_INVAL (bad range), CG_E_NOMEM, CG_E_HIP.
+ */
+int cg_encode(const cg_tables *tables, const void *kv_dev, uint32_t chunk_begin,
+              uint32_t chunk_end, void *hip_stream, cg_blob **out);
+
+/*
+ * Decodes a container into kv_out_dev (fp16 [L][2][S][C]); writes exactly the tokens
+ * of chunks [chunk_begin, chunk_end), leaves every other token untouched.
+ *   container_dev: NULL to decode the blob's own copy, or a device buffer holding the
+ *                  same container bytes (e.g. staged from pinned host memory).  Its
+ *                  payload and offsets are not trusted: damaged bytes decode to wrong
+ *                  values but every read stays inside the container.
+ * Fully asynchronous on hip_stream.  Errors: CG_E_INVAL, CG_E_CORRUPT (blob and
+ * tables disagree on the shape), CG_E_HIP.
+ */
+int cg_decode(const cg_tables *tables, const cg_blob *blob, const void *container_dev,
+              void *kv_out_dev, void *hip_stream);
+
+/* Releases a cg_tables* or cg_blob* and its device memory.  NULL is a no-op. */
+void cg_free(void *handle);
+
+/* ----------------------------------------------------------------------------------
+ * Inspection and the unfused path.  Same conventions as above.
+ * ---------------------------------------------------------------------------------- */
+
+/* Thread-local text of the last error (empty string if none). */
+const char *cg_last_error(void);
+
+/* Host copies of the tables.  lo, w, r: float [L][2][C]; freqs: uint16 [L][2][C][32]
+ * (entries >= bins[l] are 0).  Any pointer may be NULL.  Synchronous. */
+int cg_tables_export(const cg_tables *tables, float *lo, float *w, float *r, uint16_t *freqs);
+int cg_tables_get_info(const cg_tables *tables, cg_tables_info *info);
+int cg_blob_get_info(const cg_blob *blob, cg_blob_info *info);
+
+/* Copies bytes [offset, offset + nbytes) of the container to host memory (synchronous).
+ * CG_E_INVAL if the range leaves the container. */
+int cg_blob_read(const cg_blob *blob, uint64_t offset, uint64_t nbytes, void *host_dst);
+
+/* The quantizer alone: uint8 symbols [L][2][S][C] for tokens of chunks
+ * [chunk_begin, chunk_end) (anchor slots are written 0, other tokens untouched).
+ * Asynchronous. */
+int cg_quantize(const cg_tables *tables, const void *kv_dev, uint32_t chunk_begin,
+                uint32_t chunk_end, void *sym_dev, void *hip_stream);
+
+/* The range decoder alone: writes uint8 symbols [L][2][S][C] for the container's
+ * tokens (anchor slots written 0).  Asynchronous. */
+int cg_decode_symbols(const cg_tables *tables, const cg_blob *blob, const void *container_dev,
+                      void *sym_dev, void *hip_stream);
+
+/* Dequantize + anchor-add alone: symbols [L][2][S][C] and the container's anchors to
+ * fp16 [L][2][S][C] for the container's tokens.  Asynchronous. */
+int cg_dequantize(const cg_tables *tables, const cg_blob *blob, const void *container_dev,
+                  const void *sym_dev, void *kv_out_dev, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CG_H */

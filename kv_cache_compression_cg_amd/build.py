@@ -1,0 +1,50 @@
+"""Builds libcg.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+    python -m kv_cache_compression_cg_amd.build
+
+Float rules for bit-exact parity with the CPU reference: no contraction of a*b+c into
+fma unless written (-ffp-contract=off), no fast-math, correctly rounded fp32 division
+and square root (HIP's default).  Packed fp32 instructions are disabled.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB_DIR = os.path.join(PKG, "_lib")
+LIB = os.path.join(LIB_DIR, "libcg.so")
+SOURCES = [os.path.join(CSRC, "cg_kernels.hip"), os.path.join(CSRC, "cg_api.cpp")]
+ARCH = os.environ.get("CG_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def flags() -> list:
+    return ["-O3", "-std=c++17", "--offload-arch=" + ARCH, "-fPIC", "-ffp-contract=off",
+            "-fno-fast-math", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(LIB_DIR, exist_ok=True)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + flags() + ["-shared", "-x", "hip"] + SOURCES + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,307 @@
+"""Python binding of libcg (include/cg.h): argument marshalling only.
+
+Every step of the codec runs in the library's HIP kernels; this module checks tensor
+shapes, passes device pointers and the current HIP stream, and wraps the handles.
+Torch tensors provide device memory and streams.  If libcg.so is not built the import
+fails: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from .build import LIB
+
+CG_OK = 0
+ERRORS = {-1: "CG_E_INVAL", -2: "CG_E_NOMEM", -3: "CG_E_HIP", -4: "CG_E_NONFINITE",
+          -5: "CG_E_CORRUPT"}
+MAX_BINS = 32
+LANES = 64
+
+
+class CgError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (%d): %s" % (ERRORS.get(code, "?"), code, msg))
+        self.code = code
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_uint32), ("H_kv", ctypes.c_uint32), ("d", ctypes.c_uint32),
+                ("S", ctypes.c_uint32), ("group", ctypes.c_uint32), ("chunk", ctypes.c_uint32),
+                ("bins", ctypes.POINTER(ctypes.c_uint8))]
+
+
+class ContainerHeader(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in
+                ("magic", "version", "L", "H_kv", "d", "S", "group", "chunk", "chunk_begin",
+                 "chunk_end", "n_blocks", "reserved")] + \
+               [(n, ctypes.c_uint64) for n in
+                ("n_groups", "offsets_offset", "anchors_offset", "anchors_bytes",
+                 "payload_offset", "payload_words", "total_bytes")]
+
+
+class BlobInfo(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("header", ContainerHeader)]
+
+
+class TablesInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in ("L", "H_kv", "d", "S", "group", "chunk")] + \
+               [("stored_bytes", ctypes.c_uint64)]
+
+
+EXPORTED = ["cg_build_cdf", "cg_encode", "cg_decode", "cg_free", "cg_last_error",
+            "cg_tables_export", "cg_tables_get_info", "cg_blob_get_info", "cg_blob_read",
+            "cg_quantize", "cg_decode_symbols", "cg_dequantize"]
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads the in-tree libcg.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB):
+        raise ImportError("libcg.so is not built (%s); run `python -m "
+                          "kv_cache_compression_cg_amd.build`" % LIB)
+    L = ctypes.CDLL(LIB)
+    vp, u32, u64 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "cg_build_cdf": [ctypes.POINTER(Params), vp, vp, pp],
+        "cg_encode": [vp, vp, u32, u32, vp, pp],
+        "cg_decode": [vp, vp, vp, vp, vp],
+        "cg_tables_export": [vp, vp, vp, vp, vp],
+        "cg_tables_get_info": [vp, ctypes.POINTER(TablesInfo)],
+        "cg_blob_get_info": [vp, ctypes.POINTER(BlobInfo)],
+        "cg_blob_read": [vp, u64, u64, vp],
+        "cg_quantize": [vp, vp, u32, u32, vp, vp],
+        "cg_decode_symbols": [vp, vp, vp, vp, vp],
+        "cg_dequantize": [vp, vp, vp, vp, vp, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.cg_free.argtypes = [vp]
+    L.cg_free.restype = None
+    L.cg_last_error.argtypes = []
+    L.cg_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != CG_OK:
+        raise CgError(rc, load().cg_last_error().decode(errors="replace"))
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _kv_check(kv: torch.Tensor, shape=None) -> None:
+    if not kv.is_cuda or kv.dtype != torch.float16 or not kv.is_contiguous() or kv.dim() != 4 \
+            or kv.shape[1] != 2:
+        raise ValueError("expected a contiguous fp16 CUDA tensor [L, 2, S, C]")
+    if shape is not None and tuple(kv.shape) != tuple(shape):
+        raise ValueError("KV shape %s does not match the tables %s" % (tuple(kv.shape), shape))
+
+
+class Tables:
+    """Per-(layer, K/V, channel) ranges and frequency tables, owned by libcg."""
+
+    def __init__(self, handle: ctypes.c_void_p, L, H_kv, d, S, group, chunk, bins, device):
+        self.handle = handle
+        self.L, self.H_kv, self.d, self.S = L, H_kv, d, S
+        self.group, self.chunk = group, chunk
+        self.bins = tuple(int(b) for b in bins)
+        self.device = device
+
+    @property
+    def C(self) -> int:
+        return self.H_kv * self.d
+
+    @property
+    def shape(self):
+        return (self.L, 2, self.S, self.C)
+
+    @property
+    def n_chunks(self) -> int:
+        return -(-self.S // self.chunk)
+
+    @property
+    def raw_bytes(self) -> int:
+        return 2 * self.L * self.C * self.S * 2
+
+    @property
+    def stored_bytes(self) -> int:
+        info = TablesInfo()
+        _check(load().cg_tables_get_info(self.handle, ctypes.byref(info)))
+        return int(info.stored_bytes)
+
+    def export(self) -> dict:
+        rows = (self.L, 2, self.C)
+        lo, w, r = (np.empty(rows, np.float32) for _ in range(3))
+        fr = np.empty(rows + (MAX_BINS,), np.uint16)
+        _check(load().cg_tables_export(self.handle, lo.ctypes.data, w.ctypes.data,
+                                       r.ctypes.data, fr.ctypes.data))
+        return {"lo": lo, "w": w, "r": r, "freqs": fr}
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.cg_free(self.handle)
+            self.handle = None
+
+
+class Blob:
+    """One encoded container (device memory owned by libcg)."""
+
+    def __init__(self, handle: ctypes.c_void_p, tables: Tables):
+        self.handle = handle
+        self.tables = tables
+        info = BlobInfo()
+        _check(load().cg_blob_get_info(handle, ctypes.byref(info)))
+        self.data_ptr = int(info.data)
+        h = info.header
+        self.header = {f: getattr(h, f) for f, _ in ContainerHeader._fields_}
+
+    @property
+    def nbytes(self) -> int:
+        return int(self.header["total_bytes"])
+
+    @property
+    def chunk_begin(self) -> int:
+        return int(self.header["chunk_begin"])
+
+    @property
+    def chunk_end(self) -> int:
+        return int(self.header["chunk_end"])
+
+    def read(self, offset: int = 0, nbytes: Optional[int] = None) -> np.ndarray:
+        nbytes = self.nbytes - offset if nbytes is None else nbytes
+        buf = np.empty(max(nbytes, 1), np.uint8)
+        _check(load().cg_blob_read(self.handle, offset, nbytes, buf.ctypes.data))
+        return buf[:nbytes]
+
+    def offsets(self) -> np.ndarray:
+        h = self.header
+        return self.read(h["offsets_offset"], (h["n_groups"] + 1) * 8).view(np.uint64)
+
+    def anchors(self) -> np.ndarray:
+        h = self.header
+        return self.read(h["anchors_offset"], h["anchors_bytes"]).view(np.uint16) \
+            .reshape(-1, self.tables.C)
+
+    def payload(self) -> np.ndarray:
+        h = self.header
+        return self.read(h["payload_offset"], h["payload_words"] * 2).view(np.uint16)
+
+    def raw_bytes(self) -> int:
+        t = self.tables
+        t0 = self.chunk_begin * t.chunk
+        t1 = min(self.chunk_end * t.chunk, t.S)
+        return 2 * t.L * t.C * (t1 - t0) * 2
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.cg_free(self.handle)
+            self.handle = None
+
+
+def build_cdf(kv: torch.Tensor, group: int, chunk: int, bins: Sequence[int],
+              H_kv: Optional[int] = None) -> Tables:
+    """kv: fp16 CUDA [L, 2, S, C].  H_kv only labels the channel split (C = H_kv * d)."""
+    _kv_check(kv)
+    L, _, S, C = kv.shape
+    H = H_kv if H_kv is not None else 1
+    if C % H:
+        raise ValueError("C must be a multiple of H_kv")
+    b = np.ascontiguousarray(np.asarray(bins, dtype=np.uint8))
+    if b.shape != (L,):
+        raise ValueError("need one bin count per layer")
+    p = Params(L, H, C // H, S, group, chunk, b.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    h = ctypes.c_void_p()
+    with torch.cuda.device(kv.device):
+        _check(load().cg_build_cdf(ctypes.byref(p), kv.data_ptr(), _stream(kv.device),
+                                   ctypes.byref(h)))
+    return Tables(h, L, H, C // H, S, group, chunk, b, kv.device)
+
+
+def encode(tables: Tables, kv: torch.Tensor, chunk_begin: int = 0,
+           chunk_end: Optional[int] = None) -> Blob:
+    _kv_check(kv, tables.shape)
+    chunk_end = tables.n_chunks if chunk_end is None else chunk_end
+    h = ctypes.c_void_p()
+    with torch.cuda.device(kv.device):
+        _check(load().cg_encode(tables.handle, kv.data_ptr(), chunk_begin, chunk_end,
+                                _stream(kv.device), ctypes.byref(h)))
+    return Blob(h, tables)
+
+
+def decode(tables: Tables, blob: Blob, out: Optional[torch.Tensor] = None,
+           container: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Writes the container's tokens into `out` (fp16 [L, 2, S, C]); asynchronous."""
+    if out is None:
+        out = torch.empty(tables.shape, dtype=torch.float16, device=tables.device)
+    _kv_check(out, tables.shape)
+    cptr = None
+    if container is not None:
+        if not container.is_cuda or container.numel() * container.element_size() < blob.nbytes:
+            raise ValueError("container buffer must be a CUDA tensor of at least blob.nbytes")
+        cptr = container.data_ptr()
+    with torch.cuda.device(out.device):
+        _check(load().cg_decode(tables.handle, blob.handle, cptr, out.data_ptr(),
+                                _stream(out.device)))
+    return out
+
+
+def quantize(tables: Tables, kv: torch.Tensor, chunk_begin: int = 0,
+             chunk_end: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _kv_check(kv, tables.shape)
+    chunk_end = tables.n_chunks if chunk_end is None else chunk_end
+    if out is None:
+        out = torch.zeros(tables.shape, dtype=torch.uint8, device=kv.device)
+    if out.dtype != torch.uint8 or tuple(out.shape) != tables.shape or not out.is_contiguous():
+        raise ValueError("symbols must be contiguous uint8 [L, 2, S, C]")
+    with torch.cuda.device(kv.device):
+        _check(load().cg_quantize(tables.handle, kv.data_ptr(), chunk_begin, chunk_end,
+                                  out.data_ptr(), _stream(kv.device)))
+    return out
+
+
+def decode_symbols(tables: Tables, blob: Blob, out: Optional[torch.Tensor] = None,
+                   container: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out is None:
+        out = torch.zeros(tables.shape, dtype=torch.uint8, device=tables.device)
+    if out.dtype != torch.uint8 or tuple(out.shape) != tables.shape or not out.is_contiguous():
+        raise ValueError("symbols must be contiguous uint8 [L, 2, S, C]")
+    cptr = container.data_ptr() if container is not None else None
+    with torch.cuda.device(out.device):
+        _check(load().cg_decode_symbols(tables.handle, blob.handle, cptr, out.data_ptr(),
+                                        _stream(out.device)))
+    return out
+
+
+def dequantize(tables: Tables, blob: Blob, sym: torch.Tensor,
+               out: Optional[torch.Tensor] = None,
+               container: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out is None:
+        out = torch.zeros(tables.shape, dtype=torch.float16, device=tables.device)
+    _kv_check(out, tables.shape)
+    if sym.dtype != torch.uint8 or tuple(sym.shape) != tables.shape or not sym.is_contiguous():
+        raise ValueError("symbols must be contiguous uint8 [L, 2, S, C]")
+    cptr = container.data_ptr() if container is not None else None
+    with torch.cuda.device(out.device):
+        _check(load().cg_dequantize(tables.handle, blob.handle, cptr, sym.data_ptr(),
+                                    out.data_ptr(), _stream(out.device)))
+    return out
+
+
+def compressed_bytes(tables: Tables, blobs: Sequence[Blob]) -> int:
+    """Everything needed to decode: the containers plus the stored tables."""
+    return sum(b.nbytes for b in blobs) + tables.stored_bytes

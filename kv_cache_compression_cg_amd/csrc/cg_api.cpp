@@ -1,0 +1,544 @@
+// cg_api.cpp -- host side of libcg: validation, handle ownership, allocation and the
+// launch sequence of every entry point declared in include/cg.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "cg.h"
+#include "cg_internal.h"
+
+using namespace cgk;
+
+namespace {
+
+constexpr uint32_t kTablesMagic = 0x54424743u;  // "CGBT"
+constexpr uint32_t kBlobMagic = 0x42424743u;    // "CGBB"
+
+thread_local std::string g_error;
+
+int fail(int code, const std::string &msg)
+{
+    g_error = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    if (e == hipErrorOutOfMemory)
+        return fail(CG_E_NOMEM, std::string(what) + ": out of device memory");
+    return fail(CG_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define CG_HIP(call, what)                       \
+    do {                                         \
+        hipError_t e_ = (call);                  \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+// Device buffer released on scope exit unless detached.
+struct DevBuf {
+    void *p = nullptr;
+    DevBuf() = default;
+    DevBuf(const DevBuf &) = delete;
+    DevBuf &operator=(const DevBuf &) = delete;
+    ~DevBuf()
+    {
+        if (p) (void)hipFree(p);
+    }
+    hipError_t alloc(size_t n)
+    {
+        return hipMalloc(&p, n ? n : 16);
+    }
+    void *detach()
+    {
+        void *q = p;
+        p = nullptr;
+        return q;
+    }
+    template <class T> T *as() const { return static_cast<T *>(p); }
+};
+
+// Makes `dev` current for the scope of a call and restores the caller's device.
+struct DeviceScope {
+    int prev = -1;
+    bool changed = false;
+    hipError_t enter(int dev)
+    {
+        hipError_t e = hipGetDevice(&prev);
+        if (e != hipSuccess) return e;
+        if (prev != dev) {
+            changed = true;
+            return hipSetDevice(dev);
+        }
+        return hipSuccess;
+    }
+    ~DeviceScope()
+    {
+        if (changed) (void)hipSetDevice(prev);
+    }
+};
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+uint32_t ceil_div(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+struct cg_tables {
+    uint32_t magic;
+    int device;
+    uint32_t L, H, d, S, G, Tc, C, NB;
+    uint32_t max_bins;
+    std::vector<uint8_t> bins;
+    uint8_t *d_bins;
+    float *d_lo, *d_w, *d_r;
+    uint16_t *d_freqs;
+    uint2 *d_dtab;
+};
+
+struct cg_blob {
+    uint32_t magic;
+    int device;
+    cg_container_header hdr;
+    uint8_t *d_data;
+};
+
+namespace {
+
+Geom make_geom(const cg_tables *t, uint32_t kb, uint32_t ke)
+{
+    Geom g;
+    g.L = t->L;
+    g.C = t->C;
+    g.S = t->S;
+    g.G = t->G;
+    g.Tc = t->Tc;
+    g.NB = t->NB;
+    g.ngF = ceil_div(t->Tc, t->G);
+    g.kb = kb;
+    g.ke = ke;
+    return g;
+}
+
+// Tokens per thread for the streaming kernels: about two million threads in flight.
+uint32_t pick_tpt(const cg_tables *t, uint64_t tokens)
+{
+    uint64_t work = (uint64_t)t->L * 2 * tokens * (t->C / 8);
+    uint64_t tpt = (work + (1u << 21) - 1) >> 21;
+    if (tpt < 8) tpt = 8;
+    if (tpt > 4096) tpt = 4096;
+    return (uint32_t)tpt;
+}
+
+int check_tables(const cg_tables *t)
+{
+    if (!t || t->magic != kTablesMagic) return fail(CG_E_INVAL, "invalid cg_tables handle");
+    return CG_OK;
+}
+
+int check_blob(const cg_tables *t, const cg_blob *b)
+{
+    if (!b || b->magic != kBlobMagic) return fail(CG_E_INVAL, "invalid cg_blob handle");
+    const cg_container_header &h = b->hdr;
+    if (h.L != t->L || h.H_kv != t->H || h.d != t->d || h.S != t->S || h.group != t->G ||
+        h.chunk != t->Tc)
+        return fail(CG_E_CORRUPT, "container and tables describe different caches");
+    return CG_OK;
+}
+
+ContainerView view_of(const cg_blob *b)
+{
+    ContainerView v;
+    v.offsets_off = b->hdr.offsets_offset;
+    v.anchors_off = b->hdr.anchors_offset;
+    v.payload_off = b->hdr.payload_offset;
+    v.payload_words = b->hdr.payload_words;
+    return v;
+}
+
+uint64_t anchor_rows(const cg_tables *t, uint32_t kb, uint32_t ke)
+{
+    uint64_t rows = 0;
+    for (uint32_t k = kb; k < ke; ++k) {
+        uint32_t t0 = k * t->Tc;
+        uint32_t len = (t->S - t0 < t->Tc) ? t->S - t0 : t->Tc;
+        rows += (uint64_t)t->L * 2 * ceil_div(len, t->G);
+    }
+    return rows;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *cg_last_error(void) { return g_error.c_str(); }
+
+int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, cg_tables **out)
+{
+    g_error.clear();
+    if (!params || !kv_dev || !out || !params->bins)
+        return fail(CG_E_INVAL, "null argument");
+    const cg_params &p = *params;
+    if (!p.L || !p.H_kv || !p.d || !p.S || !p.group || !p.chunk)
+        return fail(CG_E_INVAL, "zero dimension");
+    if (p.chunk > CG_MAX_CHUNK) return fail(CG_E_INVAL, "chunk > 16384");
+    uint64_t C = (uint64_t)p.H_kv * p.d;
+    if (C % 8 != 0) return fail(CG_E_INVAL, "H_kv * d must be a multiple of 8");
+    if (C >= (1u << 24) || p.S >= (1u << 31) || (uint64_t)p.L * 2 * C >= (1ull << 31) ||
+        (uint64_t)p.L * 2 * p.S * C >= (1ull << 40))
+        return fail(CG_E_INVAL, "cache too large");
+    uint32_t max_bins = 0;
+    for (uint32_t l = 0; l < p.L; ++l) {
+        if (p.bins[l] < 2 || p.bins[l] > CG_MAX_BINS) return fail(CG_E_INVAL, "bins outside [2, 32]");
+        if (p.bins[l] > max_bins) max_bins = p.bins[l];
+    }
+    hipStream_t st = (hipStream_t)hip_stream;
+
+    cg_tables *t = new (std::nothrow) cg_tables();
+    if (!t) return fail(CG_E_NOMEM, "host allocation");
+    t->magic = 0;
+    CG_HIP(hipGetDevice(&t->device), "hipGetDevice");
+    t->L = p.L;
+    t->H = p.H_kv;
+    t->d = p.d;
+    t->S = p.S;
+    t->G = p.group;
+    t->Tc = p.chunk;
+    t->C = (uint32_t)C;
+    t->NB = ceil_div(t->C, kLanes);
+    t->max_bins = max_bins;
+    t->bins.assign(p.bins, p.bins + p.L);
+
+    struct Owner {  // frees the half-built handle on every error path
+        cg_tables *t;
+        ~Owner()
+        {
+            if (t) cg_free(t);
+        }
+    } owner{t};
+    t->magic = kTablesMagic;  // cg_free may now release it
+
+    const uint64_t rows = (uint64_t)t->L * 2 * t->C;
+    DevBuf bins_d, lo_d, w_d, r_d, fr_d, dt_d;
+    CG_HIP(bins_d.alloc(t->L), "hipMalloc");
+    CG_HIP(lo_d.alloc(rows * 4), "hipMalloc");
+    CG_HIP(w_d.alloc(rows * 4), "hipMalloc");
+    CG_HIP(r_d.alloc(rows * 4), "hipMalloc");
+    CG_HIP(fr_d.alloc(rows * kMaxBins * 2), "hipMalloc");
+    const uint64_t dtab_bytes = (uint64_t)t->L * 2 * t->NB * kMaxBins * kLanes * sizeof(uint2);
+    CG_HIP(dt_d.alloc(dtab_bytes), "hipMalloc");
+    t->d_bins = bins_d.as<uint8_t>();
+    t->d_lo = lo_d.as<float>();
+    t->d_w = w_d.as<float>();
+    t->d_r = r_d.as<float>();
+    t->d_freqs = fr_d.as<uint16_t>();
+    t->d_dtab = dt_d.as<uint2>();
+    bins_d.detach();
+    lo_d.detach();
+    w_d.detach();
+    r_d.detach();
+    fr_d.detach();
+    dt_d.detach();
+
+    DevBuf ordlo, ordhi, counts, flag;
+    CG_HIP(ordlo.alloc(rows * 4), "hipMalloc");
+    CG_HIP(ordhi.alloc(rows * 4), "hipMalloc");
+    CG_HIP(counts.alloc(rows * kMaxBins * 4), "hipMalloc");
+    CG_HIP(flag.alloc(4), "hipMalloc");
+
+    CG_HIP(hipMemcpyAsync(t->d_bins, t->bins.data(), t->L, hipMemcpyHostToDevice, st), "copy bins");
+    CG_HIP(hipMemsetAsync(ordlo.p, 0xFF, rows * 4, st), "memset");
+    CG_HIP(hipMemsetAsync(ordhi.p, 0x00, rows * 4, st), "memset");
+    CG_HIP(hipMemsetAsync(counts.p, 0, rows * kMaxBins * 4, st), "memset");
+    CG_HIP(hipMemsetAsync(flag.p, 0, 4, st), "memset");
+    CG_HIP(hipMemsetAsync(t->d_dtab, 0, dtab_bytes, st), "memset");
+
+    Geom g = make_geom(t, 0, ceil_div(t->S, t->Tc));
+    CG_HIP(launch_k0(static_cast<const uint16_t *>(kv_dev), g, pick_tpt(t, t->S),
+                     ordlo.as<uint32_t>(), ordhi.as<uint32_t>(), flag.as<uint32_t>(), st),
+           "k0_minmax");
+    CG_HIP(launch_k0_finalize(g, t->d_bins, ordlo.as<uint32_t>(), ordhi.as<uint32_t>(), t->d_lo,
+                              t->d_w, t->d_r, st),
+           "k0_finalize");
+    CG_HIP(launch_k1(static_cast<const uint16_t *>(kv_dev), g, t->d_bins, max_bins, t->d_lo,
+                     t->d_r, counts.as<uint32_t>(), st),
+           "k1_hist");
+    CG_HIP(launch_k1_freqs(g, t->d_bins, counts.as<uint32_t>(), t->d_lo, t->d_w, t->d_freqs,
+                           t->d_dtab, st),
+           "k1_freqs");
+    uint32_t h_flag = 0;
+    CG_HIP(hipMemcpyAsync(&h_flag, flag.p, 4, hipMemcpyDeviceToHost, st), "copy flag");
+    CG_HIP(hipStreamSynchronize(st), "hipStreamSynchronize");
+    if (h_flag) return fail(CG_E_NONFINITE, "KV input holds Inf or NaN");
+    owner.t = nullptr;
+    *out = t;
+    return CG_OK;
+}
+
+int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, void *hip_stream,
+              cg_blob **out)
+{
+    g_error.clear();
+    if (int rc = check_tables(t)) return rc;
+    if (!kv_dev || !out) return fail(CG_E_INVAL, "null argument");
+    const uint32_t nchunks = ceil_div(t->S, t->Tc);
+    if (kb >= ke || ke > nchunks) return fail(CG_E_INVAL, "chunk range out of bounds");
+    DeviceScope ds;
+    CG_HIP(ds.enter(t->device), "hipSetDevice");
+    hipStream_t st = (hipStream_t)hip_stream;
+    Geom g = make_geom(t, kb, ke);
+    const uint32_t t_lo = kb * t->Tc;
+    const uint32_t t_hi = (ke * (uint64_t)t->Tc < t->S) ? ke * t->Tc : t->S;
+    const uint32_t T_r = t_hi - t_lo;
+    const uint64_t n_groups = (uint64_t)(ke - kb) * t->L * 2 * t->NB;
+    const uint64_t arows = anchor_rows(t, kb, ke);
+
+    DevBuf sym, anc, lane_words, group_words, group_off;
+    CG_HIP(sym.alloc((uint64_t)t->L * 2 * T_r * t->C), "hipMalloc symbols");
+    CG_HIP(anc.alloc(arows * t->C * 2), "hipMalloc anchors");
+    CG_HIP(lane_words.alloc(n_groups * kLanes * 4), "hipMalloc");
+    CG_HIP(group_words.alloc(n_groups * 8), "hipMalloc");
+    CG_HIP(group_off.alloc((n_groups + 1) * 8), "hipMalloc");
+
+    CG_HIP(launch_k2(static_cast<const uint16_t *>(kv_dev), g, t->d_bins, t->d_lo, t->d_r, t_lo,
+                     t_hi, pick_tpt(t, T_r), sym.as<uint8_t>(), t_lo, T_r, anc.as<uint16_t>(), st),
+           "k2_delta_quant");
+    CG_HIP(launch_k5_plan(sym.as<uint8_t>(), t_lo, T_r, g, t->d_dtab, lane_words.as<uint32_t>(),
+                          group_words.as<uint64_t>(), n_groups, st),
+           "k5_plan");
+    CG_HIP(launch_scan(group_words.as<uint64_t>(), group_off.as<uint64_t>(), n_groups, st),
+           "scan");
+    uint64_t total_words = 0;
+    CG_HIP(hipMemcpyAsync(&total_words, group_off.as<uint64_t>() + n_groups, 8,
+                          hipMemcpyDeviceToHost, st),
+           "copy size");
+    CG_HIP(hipStreamSynchronize(st), "hipStreamSynchronize");
+
+    cg_container_header h;
+    std::memset(&h, 0, sizeof h);
+    h.magic = CG_CONTAINER_MAGIC;
+    h.version = 1;
+    h.L = t->L;
+    h.H_kv = t->H;
+    h.d = t->d;
+    h.S = t->S;
+    h.group = t->G;
+    h.chunk = t->Tc;
+    h.chunk_begin = kb;
+    h.chunk_end = ke;
+    h.n_blocks = t->NB;
+    h.n_groups = n_groups;
+    h.offsets_offset = align256(sizeof(cg_container_header));
+    h.anchors_offset = align256(h.offsets_offset + (n_groups + 1) * 8);
+    h.anchors_bytes = arows * t->C * 2;
+    h.payload_offset = align256(h.anchors_offset + h.anchors_bytes);
+    h.payload_words = total_words;
+    h.total_bytes = h.payload_offset + total_words * 2;
+
+    cg_blob *b = new (std::nothrow) cg_blob();
+    if (!b) return fail(CG_E_NOMEM, "host allocation");
+    b->magic = 0;
+    b->device = t->device;
+    b->hdr = h;
+    DevBuf data, scratch;
+    hipError_t e = data.alloc(align256(h.total_bytes) + 256);
+    if (e != hipSuccess) {
+        delete b;
+        return hip_fail(e, "hipMalloc container");
+    }
+    e = scratch.alloc(total_words * 2);
+    if (e != hipSuccess) {
+        delete b;
+        return hip_fail(e, "hipMalloc scratch");
+    }
+    uint8_t *base = data.as<uint8_t>();
+#define CG_HIP_B(call, what)                 \
+    do {                                     \
+        hipError_t e2_ = (call);             \
+        if (e2_ != hipSuccess) {             \
+            delete b;                        \
+            return hip_fail(e2_, what);      \
+        }                                    \
+    } while (0)
+    CG_HIP_B(hipMemcpyAsync(base, &h, sizeof h, hipMemcpyHostToDevice, st), "copy header");
+    CG_HIP_B(hipMemcpyAsync(base + h.offsets_offset, group_off.p, (n_groups + 1) * 8,
+                            hipMemcpyDeviceToDevice, st),
+             "copy offsets");
+    CG_HIP_B(hipMemcpyAsync(base + h.anchors_offset, anc.p, h.anchors_bytes,
+                            hipMemcpyDeviceToDevice, st),
+             "copy anchors");
+    CG_HIP_B(launch_k5_encode(sym.as<uint8_t>(), t_lo, T_r, g, t->d_dtab,
+                              lane_words.as<uint32_t>(), group_off.as<uint64_t>(),
+                              scratch.as<uint16_t>(), n_groups, st),
+             "k5_encode");
+    CG_HIP_B(launch_k5_interleave(sym.as<uint8_t>(), t_lo, T_r, g, t->d_dtab,
+                                  lane_words.as<uint32_t>(), group_off.as<uint64_t>(),
+                                  scratch.as<uint16_t>(),
+                                  reinterpret_cast<uint16_t *>(base + h.payload_offset), n_groups,
+                                  st),
+             "k5_interleave");
+    CG_HIP_B(hipStreamSynchronize(st), "hipStreamSynchronize");
+#undef CG_HIP_B
+    b->d_data = static_cast<uint8_t *>(data.detach());
+    b->magic = kBlobMagic;
+    *out = b;
+    return CG_OK;
+}
+
+int cg_decode(const cg_tables *t, const cg_blob *b, const void *container_dev, void *kv_out_dev,
+              void *hip_stream)
+{
+    g_error.clear();
+    if (int rc = check_tables(t)) return rc;
+    if (int rc = check_blob(t, b)) return rc;
+    if (!kv_out_dev) return fail(CG_E_INVAL, "null output");
+    DeviceScope ds;
+    CG_HIP(ds.enter(t->device), "hipSetDevice");
+    const uint8_t *cont = container_dev ? static_cast<const uint8_t *>(container_dev) : b->d_data;
+    Geom g = make_geom(t, b->hdr.chunk_begin, b->hdr.chunk_end);
+    CG_HIP(launch_k3(g, t->d_bins, t->d_dtab, cont, view_of(b), static_cast<uint16_t *>(kv_out_dev),
+                     nullptr, (hipStream_t)hip_stream),
+           "k3_decode");
+    return CG_OK;
+}
+
+int cg_decode_symbols(const cg_tables *t, const cg_blob *b, const void *container_dev,
+                      void *sym_dev, void *hip_stream)
+{
+    g_error.clear();
+    if (int rc = check_tables(t)) return rc;
+    if (int rc = check_blob(t, b)) return rc;
+    if (!sym_dev) return fail(CG_E_INVAL, "null output");
+    DeviceScope ds;
+    CG_HIP(ds.enter(t->device), "hipSetDevice");
+    const uint8_t *cont = container_dev ? static_cast<const uint8_t *>(container_dev) : b->d_data;
+    Geom g = make_geom(t, b->hdr.chunk_begin, b->hdr.chunk_end);
+    CG_HIP(launch_k3(g, t->d_bins, t->d_dtab, cont, view_of(b), nullptr,
+                     static_cast<uint8_t *>(sym_dev), (hipStream_t)hip_stream),
+           "k3_decode_symbols");
+    return CG_OK;
+}
+
+int cg_dequantize(const cg_tables *t, const cg_blob *b, const void *container_dev,
+                  const void *sym_dev, void *kv_out_dev, void *hip_stream)
+{
+    g_error.clear();
+    if (int rc = check_tables(t)) return rc;
+    if (int rc = check_blob(t, b)) return rc;
+    if (!sym_dev || !kv_out_dev) return fail(CG_E_INVAL, "null argument");
+    DeviceScope ds;
+    CG_HIP(ds.enter(t->device), "hipSetDevice");
+    const uint8_t *cont = container_dev ? static_cast<const uint8_t *>(container_dev) : b->d_data;
+    Geom g = make_geom(t, b->hdr.chunk_begin, b->hdr.chunk_end);
+    const uint32_t t_lo = g.kb * t->Tc;
+    const uint32_t t_hi = (g.ke * (uint64_t)t->Tc < t->S) ? g.ke * t->Tc : t->S;
+    CG_HIP(launch_k4(g, t->d_lo, t->d_w, static_cast<const uint8_t *>(sym_dev), cont, view_of(b),
+                     t_lo, t_hi, pick_tpt(t, t_hi - t_lo), static_cast<uint16_t *>(kv_out_dev),
+                     (hipStream_t)hip_stream),
+           "k4_dequant");
+    return CG_OK;
+}
+
+int cg_quantize(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, void *sym_dev,
+                void *hip_stream)
+{
+    g_error.clear();
+    if (int rc = check_tables(t)) return rc;
+    if (!kv_dev || !sym_dev) return fail(CG_E_INVAL, "null argument");
+    const uint32_t nchunks = ceil_div(t->S, t->Tc);
+    if (kb >= ke || ke > nchunks) return fail(CG_E_INVAL, "chunk range out of bounds");
+    DeviceScope ds;
+    CG_HIP(ds.enter(t->device), "hipSetDevice");
+    Geom g = make_geom(t, kb, ke);
+    const uint32_t t_lo = kb * t->Tc;
+    const uint32_t t_hi = (ke * (uint64_t)t->Tc < t->S) ? ke * t->Tc : t->S;
+    CG_HIP(launch_k2(static_cast<const uint16_t *>(kv_dev), g, t->d_bins, t->d_lo, t->d_r, t_lo,
+                     t_hi, pick_tpt(t, t_hi - t_lo), static_cast<uint8_t *>(sym_dev), 0, t->S,
+                     nullptr, (hipStream_t)hip_stream),
+           "k2_delta_quant");
+    return CG_OK;
+}
+
+int cg_tables_export(const cg_tables *t, float *lo, float *w, float *r, uint16_t *freqs)
+{
+    g_error.clear();
+    if (int rc = check_tables(t)) return rc;
+    DeviceScope ds;
+    CG_HIP(ds.enter(t->device), "hipSetDevice");
+    const uint64_t rows = (uint64_t)t->L * 2 * t->C;
+    if (lo) CG_HIP(hipMemcpy(lo, t->d_lo, rows * 4, hipMemcpyDeviceToHost), "copy lo");
+    if (w) CG_HIP(hipMemcpy(w, t->d_w, rows * 4, hipMemcpyDeviceToHost), "copy w");
+    if (r) CG_HIP(hipMemcpy(r, t->d_r, rows * 4, hipMemcpyDeviceToHost), "copy r");
+    if (freqs)
+        CG_HIP(hipMemcpy(freqs, t->d_freqs, rows * kMaxBins * 2, hipMemcpyDeviceToHost),
+               "copy freqs");
+    return CG_OK;
+}
+
+int cg_tables_get_info(const cg_tables *t, cg_tables_info *info)
+{
+    g_error.clear();
+    if (int rc = check_tables(t)) return rc;
+    if (!info) return fail(CG_E_INVAL, "null argument");
+    info->L = t->L;
+    info->H_kv = t->H;
+    info->d = t->d;
+    info->S = t->S;
+    info->group = t->G;
+    info->chunk = t->Tc;
+    uint64_t bytes = (uint64_t)t->L * 2 * t->C * 8 + t->L;
+    for (uint32_t l = 0; l < t->L; ++l) bytes += (uint64_t)2 * t->C * t->bins[l] * 2;
+    info->stored_bytes = bytes;
+    return CG_OK;
+}
+
+int cg_blob_get_info(const cg_blob *b, cg_blob_info *info)
+{
+    g_error.clear();
+    if (!b || b->magic != kBlobMagic) return fail(CG_E_INVAL, "invalid cg_blob handle");
+    if (!info) return fail(CG_E_INVAL, "null argument");
+    info->data = b->d_data;
+    info->header = b->hdr;
+    return CG_OK;
+}
+
+int cg_blob_read(const cg_blob *b, uint64_t offset, uint64_t nbytes, void *host_dst)
+{
+    g_error.clear();
+    if (!b || b->magic != kBlobMagic) return fail(CG_E_INVAL, "invalid cg_blob handle");
+    if (!host_dst && nbytes) return fail(CG_E_INVAL, "null argument");
+    if (offset > b->hdr.total_bytes || nbytes > b->hdr.total_bytes - offset)
+        return fail(CG_E_INVAL, "range outside the container");
+    if (!nbytes) return CG_OK;
+    DeviceScope ds;
+    CG_HIP(ds.enter(b->device), "hipSetDevice");
+    CG_HIP(hipMemcpy(host_dst, b->d_data + offset, nbytes, hipMemcpyDeviceToHost), "copy container");
+    return CG_OK;
+}
+
+void cg_free(void *handle)
+{
+    if (!handle) return;
+    uint32_t magic;
+    std::memcpy(&magic, handle, sizeof magic);
+    if (magic == kTablesMagic) {
+        cg_tables *t = static_cast<cg_tables *>(handle);
+        t->magic = 0;
+        void *ptrs[] = {t->d_bins, t->d_lo, t->d_w, t->d_r, t->d_freqs, t->d_dtab};
+        for (void *p : ptrs)
+            if (p) (void)hipFree(p);
+        delete t;
+    } else if (magic == kBlobMagic) {
+        cg_blob *b = static_cast<cg_blob *>(handle);
+        b->magic = 0;
+        if (b->d_data) (void)hipFree(b->d_data);
+        delete b;
+    }
+}
+
+}  // extern "C"

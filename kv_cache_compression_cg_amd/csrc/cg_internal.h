@@ -1,0 +1,62 @@
+// cg_internal.h -- declarations shared by the kernels and the host side of libcg.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace cgk {
+
+constexpr uint32_t kProbBits = 12;                 // frequencies are in units of 1/4096
+constexpr uint32_t kProbTotal = 1u << kProbBits;
+constexpr uint32_t kMaxBins = 32;
+constexpr uint32_t kLanes = 64;                    // channels per group = wavefront width
+constexpr uint32_t kRenormBelow = 1u << 16;        // renormalise (one 16-bit word) below 2^16
+constexpr uint32_t kRangeInit = 0xFFFFFFFFu;
+
+// Geometry of one call.  kb, ke: chunk range being encoded / decoded.
+struct Geom {
+    uint32_t L, C, S, G, Tc;
+    uint32_t NB;   // blocks of 64 channels = ceil(C / 64)
+    uint32_t ngF;  // groups in a full chunk = ceil(Tc / G)
+    uint32_t kb, ke;
+};
+
+// Byte offsets of the container sections.
+struct ContainerView {
+    uint64_t offsets_off, anchors_off, payload_off, payload_words;
+};
+
+hipError_t launch_k0(const uint16_t *X, const Geom &g, uint32_t tpt, uint32_t *ord_lo,
+                     uint32_t *ord_hi, uint32_t *flag, hipStream_t st);
+hipError_t launch_k0_finalize(const Geom &g, const uint8_t *bins, const uint32_t *ord_lo,
+                              const uint32_t *ord_hi, float *lo, float *w, float *r,
+                              hipStream_t st);
+hipError_t launch_k1(const uint16_t *X, const Geom &g, const uint8_t *bins, uint32_t max_bins,
+                     const float *lo, const float *r, uint32_t *counts, hipStream_t st);
+hipError_t launch_k1_freqs(const Geom &g, const uint8_t *bins, const uint32_t *counts,
+                           const float *lo, const float *w, uint16_t *freqs, uint2 *dtab,
+                           hipStream_t st);
+hipError_t launch_k2(const uint16_t *X, const Geom &g, const uint8_t *bins, const float *lo,
+                     const float *r, uint32_t t_lo, uint32_t t_hi, uint32_t tpt, uint8_t *sym,
+                     uint32_t sym_t0, uint32_t sym_T, uint16_t *anchors, hipStream_t st);
+hipError_t launch_k5_plan(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
+                          const uint2 *dtab, uint32_t *lane_words, uint64_t *group_words,
+                          uint64_t n_groups, hipStream_t st);
+hipError_t launch_scan(const uint64_t *in, uint64_t *out, uint64_t n, hipStream_t st);
+hipError_t launch_k5_encode(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
+                            const uint2 *dtab, const uint32_t *lane_words,
+                            const uint64_t *group_off, uint16_t *scratch, uint64_t n_groups,
+                            hipStream_t st);
+hipError_t launch_k5_interleave(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T,
+                                const Geom &g, const uint2 *dtab, const uint32_t *lane_words,
+                                const uint64_t *group_off, const uint16_t *scratch,
+                                uint16_t *payload, uint64_t n_groups, hipStream_t st);
+hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint2 *dtab,
+                     const uint8_t *container, const ContainerView &cv, uint16_t *out,
+                     uint8_t *sym_out, hipStream_t st);
+hipError_t launch_k4(const Geom &g, const float *lo, const float *w, const uint8_t *sym,
+                     const uint8_t *container, const ContainerView &cv, uint32_t t_lo,
+                     uint32_t t_hi, uint32_t tpt, uint16_t *out, hipStream_t st);
+
+}  // namespace cgk

@@ -1,0 +1,884 @@
+// cg_kernels.hip -- gfx950 kernels of the KV-cache codec (see include/cg.h).
+//
+// Layout conventions shared by every kernel:
+//   * KV caches are fp16 [L][2][S][C]; "row" means (layer, K/V) = l * 2 + kv.
+//   * A "group" is (chunk, row, block b) with its 64 lanes = channels 64b .. 64b+63.
+//     One wavefront decodes one group: lane i owns the stream of channel 64b + i,
+//     all lanes step through the same token at the same time, so every output row
+//     is written as one contiguous 128-byte store and the interleaved words of the
+//     group are read from a contiguous, advancing window.
+//   * Decode table entry (8 bytes) of symbol s for a lane: {cdf[s] | f[s] << 16,
+//     dequantized delta lo + s * w as fp32 bits}, stored [row][block][32][64 lanes]
+//     so that all 64 lanes reading entry s of their own channel hit 64 different
+//     LDS banks whatever s each lane holds.
+//
+// Float rules (bit-exact with the CPU oracle): -ffp-contract=off, fp32 division and
+// reciprocal correctly rounded (HIP default), fmaf only where written, fp16 output
+// converted round-to-nearest-even.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cstdint>
+
+#include "cg_internal.h"
+
+namespace cgk {
+
+// ------------------------------------------------------------------------------ helpers
+__device__ __forceinline__ float h2f(uint32_t h) { return __half2float(__ushort_as_half((unsigned short)h)); }
+__device__ __forceinline__ uint32_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
+
+// unsigned image of a float that orders like the float (for atomic min / max)
+__device__ __forceinline__ uint32_t f2ord(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord2f(uint32_t o)
+{
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ bool any_nonfinite(uint4 v)
+{
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bad |= (w[i] & 0x7C00u) == 0x7C00u;
+        bad |= (w[i] & 0x7C000000u) == 0x7C000000u;
+    }
+    return bad;
+}
+
+__device__ __forceinline__ void unpack8(uint4 v, float f[8])
+{
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = h2f(w[i] & 0xFFFFu);
+        f[2 * i + 1] = h2f(w[i] >> 16);
+    }
+}
+
+// q = clamp(floor(fma(delta - lo, r, 0.5)), 0, N - 1)
+__device__ __forceinline__ uint32_t quantize1(float delta, float lo, float r, uint32_t N)
+{
+    float v = floorf(fmaf(delta - lo, r, 0.5f));
+    if (!(v > 0.0f)) return 0;
+    if (v > (float)(N - 1u)) return N - 1u;
+    return (uint32_t)v;
+}
+
+__device__ __forceinline__ uint32_t chunk_len(const Geom &g, uint32_t k)
+{
+    uint32_t t0 = k * g.Tc;
+    return (g.S - t0 < g.Tc) ? g.S - t0 : g.Tc;
+}
+
+// Walks tokens [t, t_end) keeping the chunk / group position without divisions.
+struct TokenWalk {
+    uint32_t t, u, gp, gi, k;  // token, offset in chunk, offset in group, group in chunk, chunk
+    __device__ void init(const Geom &g, uint32_t t_start)
+    {
+        t = t_start;
+        k = t / g.Tc;
+        u = t - k * g.Tc;
+        gi = u / g.G;
+        gp = u - gi * g.G;
+    }
+    __device__ void next(const Geom &g)
+    {
+        ++t;
+        ++u;
+        if (u == g.Tc) {
+            u = 0;
+            gp = 0;
+            gi = 0;
+            ++k;
+        } else if (++gp == g.G) {
+            gp = 0;
+            ++gi;
+        }
+    }
+};
+
+// Row of the anchors section holding (chunk k, row, group gi); chunks before k in the
+// range are full (only the last chunk of a cache can be short).
+__device__ __forceinline__ uint64_t anchor_row(const Geom &g, uint32_t k, uint32_t row, uint32_t gi)
+{
+    uint32_t len = chunk_len(g, k);
+    uint32_t ng = (len + g.G - 1) / g.G;
+    return (uint64_t)(k - g.kb) * g.L * 2 * g.ngF + (uint64_t)row * ng + gi;
+}
+
+// ------------------------------------------------------------------------------ K0
+// Per-channel min / max of the anchor deltas, and the non-finite flag.
+// Thread = (row, token block, 8 channels); 16-byte loads, one row of C channels is
+// read by C/8 consecutive threads.
+__global__ __launch_bounds__(256) void k0_minmax(const uint16_t *__restrict__ X, Geom g,
+                                                  uint32_t tpt, uint32_t ntb,
+                                                  uint32_t *__restrict__ ord_lo,
+                                                  uint32_t *__restrict__ ord_hi,
+                                                  uint32_t *__restrict__ flag)
+{
+    const uint32_t O = g.C / 8;
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (uint64_t)g.L * 2 * ntb * O) return;
+    uint32_t o = (uint32_t)(i % O);
+    uint64_t tmp = i / O;
+    uint32_t tb = (uint32_t)(tmp % ntb);
+    uint32_t row = (uint32_t)(tmp / ntb);
+    uint32_t t_begin = tb * tpt;
+    if (t_begin >= g.S) return;
+    uint32_t t_end = min(g.S, t_begin + tpt);
+    const uint16_t *base = X + (uint64_t)row * g.S * g.C + o * 8;
+
+    TokenWalk w;
+    w.init(g, t_begin);
+    float af[8], mn[8], mx[8];
+    bool any = false, bad = false;
+    if (w.gp != 0) {
+        uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
+        unpack8(a, af);
+    }
+    for (; w.t < t_end; w.next(g)) {
+        uint4 v = *reinterpret_cast<const uint4 *>(base + (uint64_t)w.t * g.C);
+        bad |= any_nonfinite(v);
+        float xf[8];
+        unpack8(v, xf);
+        if (w.gp == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) af[j] = xf[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float dl = xf[j] - af[j];
+                if (!any) {
+                    mn[j] = dl;
+                    mx[j] = dl;
+                } else {
+                    mn[j] = (dl < mn[j]) ? dl : mn[j];
+                    mx[j] = (dl > mx[j]) ? dl : mx[j];
+                }
+            }
+            any = true;
+        }
+    }
+    if (any) {
+        uint64_t r0 = (uint64_t)row * g.C + o * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            atomicMin(&ord_lo[r0 + j], f2ord(mn[j]));
+            atomicMax(&ord_hi[r0 + j], f2ord(mx[j]));
+        }
+    }
+    if (bad) atomicOr(flag, 1u);
+}
+
+// lo, w = (hi - lo) / (N - 1), r = 1 / w per (row, channel).
+__global__ __launch_bounds__(256) void k0_finalize(Geom g, const uint8_t *__restrict__ bins,
+                                                    const uint32_t *__restrict__ ord_lo,
+                                                    const uint32_t *__restrict__ ord_hi,
+                                                    float *__restrict__ lo, float *__restrict__ w,
+                                                    float *__restrict__ r)
+{
+    uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= g.L * 2 * g.C) return;
+    uint32_t l = i / (2 * g.C);
+    float a = 0.0f, b = 0.0f;
+    if (ord_lo[i] != 0xFFFFFFFFu) {
+        a = ord2f(ord_lo[i]);
+        b = ord2f(ord_hi[i]);
+    }
+    a = a + 0.0f;  // a zero bound is +0
+    b = b + 0.0f;
+    float ww = (b - a) / (float)(bins[l] - 1u);
+    lo[i] = a;
+    w[i] = ww;
+    r[i] = (ww > 0.0f) ? 1.0f / ww : 0.0f;
+}
+
+// ------------------------------------------------------------------------------ K1
+// Fused delta -> quantize -> histogram.  Block = (row, tile of 8*OCT channels, token
+// block); its SUB x OCT threads each own 8 channels of a token sub-range.  Counts go
+// to an LDS histogram [N][8][OCT] (consecutive lanes -> consecutive banks), then the
+// non-zero bins are added to the global u32 counts.
+__global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, Geom g,
+                                                const uint8_t *__restrict__ bins,
+                                                const float *__restrict__ lo,
+                                                const float *__restrict__ r, uint32_t OCT,
+                                                uint32_t SUB, uint32_t tpt, uint32_t ntiles,
+                                                uint32_t ntb, uint32_t *__restrict__ counts)
+{
+    extern __shared__ uint32_t hist[];
+    uint32_t tbb = blockIdx.x % ntb;
+    uint32_t tmp = blockIdx.x / ntb;
+    uint32_t ct = tmp % ntiles;
+    uint32_t row = tmp / ntiles;
+    uint32_t N = bins[row >> 1];
+    uint32_t nh = N * 8 * OCT;
+    for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) hist[j] = 0;
+    __syncthreads();
+
+    const uint32_t O = g.C / 8;
+    uint32_t ol = threadIdx.x % OCT, sub = threadIdx.x / OCT;
+    uint32_t o = ct * OCT + ol;
+    uint32_t t_begin = (tbb * SUB + sub) * tpt;
+    if (sub < SUB && o < O && t_begin < g.S) {
+        uint32_t t_end = min(g.S, t_begin + tpt);
+        const uint16_t *base = X + (uint64_t)row * g.S * g.C + o * 8;
+        float lo8[8], r8[8], af[8];
+        uint64_t r0 = (uint64_t)row * g.C + o * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            lo8[j] = lo[r0 + j];
+            r8[j] = r[r0 + j];
+        }
+        TokenWalk w;
+        w.init(g, t_begin);
+        if (w.gp != 0) {
+            uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
+            unpack8(a, af);
+        }
+        for (; w.t < t_end; w.next(g)) {
+            uint4 v = *reinterpret_cast<const uint4 *>(base + (uint64_t)w.t * g.C);
+            float xf[8];
+            unpack8(v, xf);
+            if (w.gp == 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) af[j] = xf[j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    uint32_t q = quantize1(xf[j] - af[j], lo8[j], r8[j], N);
+                    atomicAdd(&hist[(q * 8 + j) * OCT + ol], 1u);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) {
+        uint32_t v = hist[j];
+        if (!v) continue;
+        uint32_t s = j / (8 * OCT), rem = j - s * 8 * OCT;
+        uint32_t jj = rem / OCT, oo = ct * OCT + rem % OCT;
+        if (oo >= O) continue;
+        atomicAdd(&counts[((uint64_t)row * g.C + oo * 8 + jj) * kMaxBins + s], v);
+    }
+}
+
+// Frequencies (T = 4096, f >= 1, remainder to the most frequent symbol) and the decode
+// table of one (row, channel).
+__global__ __launch_bounds__(256) void k1_freqs(Geom g, const uint8_t *__restrict__ bins,
+                                                 const uint32_t *__restrict__ counts,
+                                                 const float *__restrict__ lo,
+                                                 const float *__restrict__ w,
+                                                 uint16_t *__restrict__ freqs,
+                                                 uint2 *__restrict__ dtab)
+{
+    uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= g.L * 2 * g.C) return;
+    uint32_t row = i / g.C, c = i - row * g.C;
+    uint32_t N = bins[row >> 1];
+    const uint32_t *cnt = counts + (uint64_t)i * kMaxBins;
+    uint64_t n = 0;
+    for (uint32_t s = 0; s < N; ++s) n += cnt[s];
+    uint32_t f[kMaxBins];
+    uint32_t sum = 0, best = 0;
+    for (uint32_t s = 0; s < N; ++s) {
+        uint64_t extra = n ? ((uint64_t)cnt[s] * (kProbTotal - N)) / n : 0;
+        f[s] = 1u + (uint32_t)extra;
+        sum += f[s];
+        if (cnt[s] > cnt[best]) best = s;
+    }
+    f[best] += kProbTotal - sum;
+    uint32_t P = 1;
+    while (P < N) P <<= 1;
+    float lo1 = lo[i], w1 = w[i];
+    uint2 *tb = dtab + ((uint64_t)(row * g.NB + c / kLanes) * kMaxBins) * kLanes + (c % kLanes);
+    uint32_t cdf = 0;
+    for (uint32_t s = 0; s < kMaxBins; ++s) {
+        uint32_t fs = (s < N) ? f[s] : 0;
+        freqs[(uint64_t)i * kMaxBins + s] = (uint16_t)fs;
+        uint2 e;
+        if (s < N) {
+            e.x = cdf | (fs << 16);
+            e.y = __float_as_uint(fmaf((float)s, w1, lo1));
+        } else {
+            // padding up to a power of two: cdf = T is never <= code for a valid stream
+            e.x = kProbTotal;
+            e.y = __float_as_uint(fmaf((float)(N - 1u), w1, lo1));
+        }
+        tb[(uint64_t)s * kLanes] = e;
+        cdf += fs;
+    }
+}
+
+// ------------------------------------------------------------------------------ K2
+// Fused anchor-delta + quantize over tokens [t_lo, t_hi): 16-byte fp16 loads, 8-byte
+// symbol stores, anchors copied to the container layout.  sym is [L][2][sym_T][C]
+// holding tokens from sym_t0.
+__global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict__ X, Geom g,
+                                                       const uint8_t *__restrict__ bins,
+                                                       const float *__restrict__ lo,
+                                                       const float *__restrict__ r,
+                                                       uint32_t t_lo, uint32_t t_hi,
+                                                       uint32_t tpt, uint32_t ntb,
+                                                       uint8_t *__restrict__ sym,
+                                                       uint32_t sym_t0, uint32_t sym_T,
+                                                       uint16_t *__restrict__ anchors)
+{
+    const uint32_t O = g.C / 8;
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (uint64_t)g.L * 2 * ntb * O) return;
+    uint32_t o = (uint32_t)(i % O);
+    uint64_t tmp = i / O;
+    uint32_t tb = (uint32_t)(tmp % ntb);
+    uint32_t row = (uint32_t)(tmp / ntb);
+    uint32_t t_begin = t_lo + tb * tpt;
+    if (t_begin >= t_hi) return;
+    uint32_t t_end = min(t_hi, t_begin + tpt);
+    uint32_t N = bins[row >> 1];
+    const uint16_t *base = X + (uint64_t)row * g.S * g.C + o * 8;
+    uint8_t *sbase = sym + (uint64_t)row * sym_T * g.C + o * 8;
+    float lo8[8], r8[8], af[8];
+    uint64_t r0 = (uint64_t)row * g.C + o * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        lo8[j] = lo[r0 + j];
+        r8[j] = r[r0 + j];
+    }
+    TokenWalk w;
+    w.init(g, t_begin);
+    if (w.gp != 0) {
+        uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
+        unpack8(a, af);
+    }
+    for (; w.t < t_end; w.next(g)) {
+        uint4 v = *reinterpret_cast<const uint4 *>(base + (uint64_t)w.t * g.C);
+        uint2 packed = make_uint2(0, 0);
+        float xf[8];
+        unpack8(v, xf);
+        if (w.gp == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) af[j] = xf[j];
+            if (anchors) {
+                uint64_t ar = anchor_row(g, w.k, row, w.gi);
+                *reinterpret_cast<uint4 *>(anchors + ar * g.C + o * 8) = v;
+            }
+        } else {
+            uint32_t q[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = quantize1(xf[j] - af[j], lo8[j], r8[j], N);
+            packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+            packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+        }
+        *reinterpret_cast<uint2 *>(sbase + (uint64_t)(w.t - sym_t0) * g.C) = packed;
+    }
+}
+
+// ------------------------------------------------------------------------------ K5
+// Range encoder, three wave-per-group passes:
+//   plan        replays the range evolution to count each lane's words;
+//   encode      codes each lane's stream into a lane-major scratch (exact size), carries
+//               rippled back into the words already written;
+//   interleave  replays the evolution again and moves every word to the position the
+//               lockstep decoders will read it from.
+struct GroupCtx {
+    uint32_t k, row, b, lane, c, nl, t0, len, ng, m;
+    bool present;
+};
+
+__device__ __forceinline__ GroupCtx group_ctx(const Geom &g, uint64_t gidx, uint32_t lane)
+{
+    GroupCtx x;
+    x.b = (uint32_t)(gidx % g.NB);
+    uint64_t tmp = gidx / g.NB;
+    x.row = (uint32_t)(tmp % (2 * g.L));
+    x.k = g.kb + (uint32_t)(tmp / (2 * g.L));
+    x.lane = lane;
+    x.c = x.b * kLanes + lane;
+    x.nl = min(kLanes, g.C - x.b * kLanes);
+    x.present = x.c < g.C;
+    x.t0 = x.k * g.Tc;
+    x.len = chunk_len(g, x.k);
+    x.ng = (x.len + g.G - 1) / g.G;
+    x.m = x.len - x.ng;
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t lane)
+{
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint32_t y = __shfl_up(x, d, 64);
+        if (lane >= (uint32_t)d) x += y;
+    }
+    return x - v;
+}
+
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__global__ __launch_bounds__(256) void k5_plan(const uint8_t *__restrict__ sym, uint32_t sym_t0,
+                                                uint32_t sym_T, Geom g,
+                                                const uint2 *__restrict__ dtab,
+                                                uint32_t *__restrict__ lane_words,
+                                                uint64_t *__restrict__ group_words,
+                                                uint64_t n_groups)
+{
+    uint64_t gidx = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) / kLanes;
+    uint32_t lane = threadIdx.x % kLanes;
+    if (gidx >= n_groups) return;
+    GroupCtx x = group_ctx(g, gidx, lane);
+    uint32_t words = 0;
+    if (x.present && x.m > 0) {
+        const uint8_t *sp = sym + (uint64_t)x.row * sym_T * g.C + x.c;
+        const uint2 *tab = dtab + ((uint64_t)(x.row * g.NB + x.b) * kMaxBins) * kLanes + lane;
+        uint32_t range = kRangeInit, ev = 0, i = 0;
+        for (uint32_t gi = 0; gi < x.ng; ++gi) {
+            uint32_t ulen = min(g.G, x.len - gi * g.G);
+            for (uint32_t u = 1; u < ulen; ++u) {
+                uint32_t t = x.t0 + gi * g.G + u;
+                uint32_t s = sp[(uint64_t)(t - sym_t0) * g.C];
+                uint32_t f = tab[(uint64_t)s * kLanes].x >> 16;
+                range = (range >> kProbBits) * f;
+                ++i;
+                if (i < x.m && range < kRenormBelow) {
+                    range <<= 16;
+                    ++ev;
+                }
+            }
+        }
+        words = 2 + ev;
+    }
+    lane_words[gidx * kLanes + lane] = words;
+    uint32_t tot = words;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) tot += __shfl_xor(tot, d, 64);
+    if (lane == 0) group_words[gidx] = tot;
+}
+
+// Exclusive prefix sum of n values in one block; out[n] = total.
+__global__ __launch_bounds__(1024) void k_scan(const uint64_t *__restrict__ in,
+                                                uint64_t *__restrict__ out, uint64_t n)
+{
+    __shared__ uint64_t part[1024];
+    uint32_t tid = threadIdx.x;
+    uint64_t per = (n + 1023) / 1024;
+    uint64_t beg = min(n, (uint64_t)tid * per), end = min(n, beg + per);
+    uint64_t s = 0;
+    for (uint64_t j = beg; j < end; ++j) s += in[j];
+    part[tid] = s;
+    __syncthreads();
+    for (uint32_t d = 1; d < 1024; d <<= 1) {
+        uint64_t y = (tid >= d) ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += y;
+        __syncthreads();
+    }
+    uint64_t run = part[tid] - s;
+    for (uint64_t j = beg; j < end; ++j) {
+        out[j] = run;
+        run += in[j];
+    }
+    if (tid == 1023) out[n] = part[1023];
+}
+
+__global__ __launch_bounds__(256) void k5_encode(const uint8_t *__restrict__ sym, uint32_t sym_t0,
+                                                  uint32_t sym_T, Geom g,
+                                                  const uint2 *__restrict__ dtab,
+                                                  const uint32_t *__restrict__ lane_words,
+                                                  const uint64_t *__restrict__ group_off,
+                                                  uint16_t *__restrict__ scratch, uint64_t n_groups)
+{
+    uint64_t gidx = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) / kLanes;
+    uint32_t lane = threadIdx.x % kLanes;
+    if (gidx >= n_groups) return;
+    GroupCtx x = group_ctx(g, gidx, lane);
+    uint32_t nwords = lane_words[gidx * kLanes + lane];
+    uint32_t lane_off = wave_excl_scan(nwords, lane);
+    if (!x.present || x.m == 0) return;
+    uint16_t *out = scratch + group_off[gidx] + lane_off;
+    const uint8_t *sp = sym + (uint64_t)x.row * sym_T * g.C + x.c;
+    const uint2 *tab = dtab + ((uint64_t)(x.row * g.NB + x.b) * kMaxBins) * kLanes + lane;
+    uint64_t low = 0;
+    uint32_t range = kRangeInit, nw = 0, i = 0;
+    for (uint32_t gi = 0; gi < x.ng; ++gi) {
+        uint32_t ulen = min(g.G, x.len - gi * g.G);
+        for (uint32_t u = 1; u < ulen; ++u) {
+            uint32_t t = x.t0 + gi * g.G + u;
+            uint32_t s = sp[(uint64_t)(t - sym_t0) * g.C];
+            uint32_t e = tab[(uint64_t)s * kLanes].x;
+            uint32_t q = range >> kProbBits;
+            low += (uint64_t)q * (e & 0xFFFFu);
+            range = q * (e >> 16);
+            if (low >> 32) {  // carry into the words already written
+                low &= 0xFFFFFFFFull;
+                uint32_t j = nw;
+                uint16_t v;
+                do {
+                    --j;
+                    v = (uint16_t)(out[j] + 1u);
+                    out[j] = v;
+                } while (v == 0 && j > 0);
+            }
+            ++i;
+            if (i < x.m && range < kRenormBelow) {
+                out[nw++] = (uint16_t)(low >> 16);
+                low = (low & 0xFFFFull) << 16;
+                range <<= 16;
+            }
+        }
+    }
+    out[nw++] = (uint16_t)(low >> 16);
+    out[nw++] = (uint16_t)(low & 0xFFFFu);
+}
+
+__global__ __launch_bounds__(256) void k5_interleave(const uint8_t *__restrict__ sym,
+                                                      uint32_t sym_t0, uint32_t sym_T, Geom g,
+                                                      const uint2 *__restrict__ dtab,
+                                                      const uint32_t *__restrict__ lane_words,
+                                                      const uint64_t *__restrict__ group_off,
+                                                      const uint16_t *__restrict__ scratch,
+                                                      uint16_t *__restrict__ payload,
+                                                      uint64_t n_groups)
+{
+    uint64_t gidx = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) / kLanes;
+    uint32_t lane = threadIdx.x % kLanes;
+    if (gidx >= n_groups) return;
+    GroupCtx x = group_ctx(g, gidx, lane);
+    uint32_t nwords = lane_words[gidx * kLanes + lane];
+    uint32_t lane_off = wave_excl_scan(nwords, lane);
+    if (x.m == 0) return;  // uniform over the wave
+    const uint16_t *src = scratch + group_off[gidx] + lane_off;
+    uint16_t *dst = payload + group_off[gidx];
+    if (x.present) {
+        dst[2 * lane] = src[0];
+        dst[2 * lane + 1] = src[1];
+    }
+    uint32_t cursor = 2 * x.nl, e = 2, range = kRangeInit, i = 0;
+    const uint8_t *sp = sym + (uint64_t)x.row * sym_T * g.C + (x.present ? x.c : 0);
+    const uint2 *tab = dtab + ((uint64_t)(x.row * g.NB + x.b) * kMaxBins) * kLanes + lane;
+    for (uint32_t gi = 0; gi < x.ng; ++gi) {
+        uint32_t ulen = min(g.G, x.len - gi * g.G);
+        for (uint32_t u = 1; u < ulen; ++u) {
+            uint32_t t = x.t0 + gi * g.G + u;
+            bool need = false;
+            ++i;
+            if (x.present) {
+                uint32_t s = sp[(uint64_t)(t - sym_t0) * g.C];
+                uint32_t f = tab[(uint64_t)s * kLanes].x >> 16;
+                range = (range >> kProbBits) * f;
+                need = (i < x.m) && (range < kRenormBelow);
+            }
+            uint64_t mask = __ballot(need);
+            if (need) {
+                dst[cursor + mbcnt64(mask)] = src[e++];
+                range <<= 16;
+            }
+            cursor += (uint32_t)__popcll(mask);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------ K3 (+K4)
+// Range decoder, one wavefront per group, fused with dequantize + anchor-add.
+// Block = 4 wavefronts = 4 consecutive chunks of the same (row, block), sharing the
+// block's decode table in LDS (P <= 32 entries x 64 lanes x 8 bytes).
+template <int LOGP, bool SYMBOLS>
+__device__ __forceinline__ void decode_wave(const Geom &g, const uint2 *__restrict__ tab_lds,
+                                            const uint8_t *__restrict__ container,
+                                            const ContainerView &cv, uint32_t k, uint32_t row,
+                                            uint32_t b, uint32_t lane, uint16_t *__restrict__ out,
+                                            uint8_t *__restrict__ sym_out)
+{
+    const uint32_t c = b * kLanes + lane;
+    const bool present = c < g.C;
+    const uint32_t nl = min(kLanes, g.C - b * kLanes);
+    const uint32_t t0 = k * g.Tc, len = chunk_len(g, k);
+    const uint32_t ng = (len + g.G - 1) / g.G, m = len - ng;
+
+    const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
+    const uint64_t *offs = reinterpret_cast<const uint64_t *>(container + cv.offsets_off);
+    uint64_t end = min(offs[gidx + 1], cv.payload_words);
+    uint64_t beg = min(offs[gidx], end);
+    const uint16_t *words = reinterpret_cast<const uint16_t *>(container + cv.payload_off);
+    const uint16_t *anc = reinterpret_cast<const uint16_t *>(container + cv.anchors_off) +
+                          anchor_row(g, k, row, 0) * g.C + c;
+    const uint64_t orow = ((uint64_t)row * g.S + t0) * g.C + c;
+
+    uint32_t code = 0, range = kRangeInit;
+    if (present && m > 0) {
+        uint64_t p0 = beg + 2 * lane;
+        uint32_t hi = p0 < end ? words[p0] : 0u;
+        uint32_t lo = p0 + 1 < end ? words[p0 + 1] : 0u;
+        code = (hi << 16) | lo;
+    }
+    uint64_t cursor = beg + 2 * nl;
+    const uint16_t *tab16 = reinterpret_cast<const uint16_t *>(tab_lds) + lane * 4;
+    const uint2 *tabe = tab_lds + lane;
+    uint32_t i = 0;
+    for (uint32_t gi = 0; gi < ng; ++gi) {
+        const uint32_t tr = gi * g.G;
+        uint32_t a16 = present ? anc[(uint64_t)gi * g.C] : 0u;
+        if (present) {
+            if (SYMBOLS)
+                sym_out[orow + (uint64_t)tr * g.C] = 0;
+            else
+                out[orow + (uint64_t)tr * g.C] = (uint16_t)a16;
+        }
+        const float af = h2f(a16);
+        const uint32_t ulen = min(g.G, len - tr);
+        for (uint32_t u = 1; u < ulen; ++u) {
+            const uint32_t q = range >> kProbBits;
+            uint32_t s = 0;
+#pragma unroll
+            for (int h = (1 << LOGP) >> 1; h >= 1; h >>= 1) {
+                uint32_t cdf = tab16[(s + h) * (kLanes * 4)];
+                if (__umul24(q, cdf) <= code) s += h;
+            }
+            const uint2 e = tabe[s * kLanes];
+            code -= __umul24(q, e.x & 0xFFFFu);
+            range = __umul24(q, e.x >> 16);
+            if (present) {
+                const uint64_t oi = orow + (uint64_t)(tr + u) * g.C;
+                if (SYMBOLS)
+                    sym_out[oi] = (uint8_t)s;
+                else
+                    out[oi] = (uint16_t)f2h(af + __uint_as_float(e.y));
+            }
+            ++i;
+            const bool need = present && (i < m) && (range < kRenormBelow);
+            const uint64_t mask = __ballot(need);
+            if (mask) {
+                if (need) {
+                    uint64_t pos = cursor + mbcnt64(mask);
+                    uint32_t wd = pos < end ? words[pos] : 0u;
+                    code = (code << 16) | wd;
+                    range <<= 16;
+                }
+                cursor += (uint32_t)__popcll(mask);
+            }
+        }
+    }
+}
+
+template <bool SYMBOLS>
+__global__ __launch_bounds__(256) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
+                                                  const uint2 *__restrict__ dtab,
+                                                  const uint8_t *__restrict__ container,
+                                                  ContainerView cv, uint32_t n_sets,
+                                                  uint16_t *__restrict__ out,
+                                                  uint8_t *__restrict__ sym_out)
+{
+    __shared__ uint2 tab[kMaxBins * kLanes];
+    const uint32_t set = blockIdx.x % n_sets;
+    const uint32_t tmp = blockIdx.x / n_sets;
+    const uint32_t b = tmp % g.NB;
+    const uint32_t row = tmp / g.NB;
+    const uint32_t N = bins[row >> 1];
+    uint32_t logp = 0;
+    while ((1u << logp) < N) ++logp;
+    const uint32_t n16 = ((1u << logp) * kLanes) / 2;  // 16-byte pieces of the table
+    const uint4 *src = reinterpret_cast<const uint4 *>(dtab + (uint64_t)(row * g.NB + b) * kMaxBins * kLanes);
+    uint4 *dst = reinterpret_cast<uint4 *>(tab);
+    for (uint32_t j = threadIdx.x; j < n16; j += blockDim.x) dst[j] = src[j];
+    __syncthreads();
+    const uint32_t wave = threadIdx.x / kLanes, lane = threadIdx.x % kLanes;
+    const uint32_t k = g.kb + set * 4 + wave;
+    if (k >= g.ke) return;
+    switch (logp) {
+    case 1: decode_wave<1, SYMBOLS>(g, tab, container, cv, k, row, b, lane, out, sym_out); break;
+    case 2: decode_wave<2, SYMBOLS>(g, tab, container, cv, k, row, b, lane, out, sym_out); break;
+    case 3: decode_wave<3, SYMBOLS>(g, tab, container, cv, k, row, b, lane, out, sym_out); break;
+    case 4: decode_wave<4, SYMBOLS>(g, tab, container, cv, k, row, b, lane, out, sym_out); break;
+    default: decode_wave<5, SYMBOLS>(g, tab, container, cv, k, row, b, lane, out, sym_out); break;
+    }
+}
+
+// ------------------------------------------------------------------------------ K4
+// Dequantize + anchor-add for a symbol tensor [L][2][S][C] (the unfused path):
+// y = fp16_rne(f32(anchor) + fma(f32(q), w, lo)); anchors copied from the container.
+__global__ __launch_bounds__(256) void k4_dequant(Geom g, const float *__restrict__ lo,
+                                                   const float *__restrict__ w,
+                                                   const uint8_t *__restrict__ sym,
+                                                   const uint8_t *__restrict__ container,
+                                                   ContainerView cv, uint32_t t_lo,
+                                                   uint32_t t_hi, uint32_t tpt, uint32_t ntb,
+                                                   uint16_t *__restrict__ out)
+{
+    const uint32_t O = g.C / 8;
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (uint64_t)g.L * 2 * ntb * O) return;
+    uint32_t o = (uint32_t)(i % O);
+    uint64_t tmp = i / O;
+    uint32_t tb = (uint32_t)(tmp % ntb);
+    uint32_t row = (uint32_t)(tmp / ntb);
+    uint32_t t_begin = t_lo + tb * tpt;
+    if (t_begin >= t_hi) return;
+    uint32_t t_end = min(t_hi, t_begin + tpt);
+    const uint16_t *anc = reinterpret_cast<const uint16_t *>(container + cv.anchors_off) + o * 8;
+    float lo8[8], w8[8], af[8];
+    uint64_t r0 = (uint64_t)row * g.C + o * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        lo8[j] = lo[r0 + j];
+        w8[j] = w[r0 + j];
+    }
+    TokenWalk tw;
+    tw.init(g, t_begin);
+    if (tw.gp != 0) {
+        uint4 a = *reinterpret_cast<const uint4 *>(anc + anchor_row(g, tw.k, row, tw.gi) * g.C);
+        unpack8(a, af);
+    }
+    const uint64_t ob = (uint64_t)row * g.S * g.C + o * 8;
+    for (; tw.t < t_end; tw.next(g)) {
+        uint4 res;
+        if (tw.gp == 0) {
+            res = *reinterpret_cast<const uint4 *>(anc + anchor_row(g, tw.k, row, tw.gi) * g.C);
+            unpack8(res, af);
+        } else {
+            uint2 s8 = *reinterpret_cast<const uint2 *>(sym + ob + (uint64_t)tw.t * g.C);
+            uint32_t h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                uint32_t q = ((j < 4 ? s8.x : s8.y) >> (8 * (j & 3))) & 0xFFu;
+                h[j] = f2h(af[j] + fmaf((float)q, w8[j], lo8[j]));
+            }
+            res = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                             h[6] | (h[7] << 16));
+        }
+        *reinterpret_cast<uint4 *>(out + ob + (uint64_t)tw.t * g.C) = res;
+    }
+}
+
+// ------------------------------------------------------------------------------ launchers
+hipError_t launch_k0(const uint16_t *X, const Geom &g, uint32_t tpt, uint32_t *ord_lo,
+                     uint32_t *ord_hi, uint32_t *flag, hipStream_t st)
+{
+    uint32_t ntb = (g.S + tpt - 1) / tpt;
+    uint64_t threads = (uint64_t)g.L * 2 * ntb * (g.C / 8);
+    hipLaunchKernelGGL(k0_minmax, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st, X, g,
+                       tpt, ntb, ord_lo, ord_hi, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_k0_finalize(const Geom &g, const uint8_t *bins, const uint32_t *ord_lo,
+                              const uint32_t *ord_hi, float *lo, float *w, float *r, hipStream_t st)
+{
+    uint32_t n = g.L * 2 * g.C;
+    hipLaunchKernelGGL(k0_finalize, dim3((n + 255) / 256), dim3(256), 0, st, g, bins, ord_lo,
+                       ord_hi, lo, w, r);
+    return hipGetLastError();
+}
+
+hipError_t launch_k1(const uint16_t *X, const Geom &g, const uint8_t *bins, uint32_t max_bins,
+                     const float *lo, const float *r, uint32_t *counts, hipStream_t st)
+{
+    const uint32_t O = g.C / 8;
+    const uint32_t OCT = O < 32 ? O : 32;
+    const uint32_t SUB = 256 / OCT;
+    const uint32_t ntiles = (O + OCT - 1) / OCT;
+    const uint64_t rows = (uint64_t)g.L * 2;
+    uint64_t ntb_target = (8192 + rows * ntiles - 1) / (rows * ntiles);
+    uint64_t tpt = (g.S + ntb_target * SUB - 1) / (ntb_target * SUB);
+    if (tpt < 16) tpt = 16;
+    uint32_t ntb = (uint32_t)((g.S + tpt * SUB - 1) / (tpt * SUB));
+    size_t lds = (size_t)max_bins * 8 * OCT * sizeof(uint32_t);
+    hipLaunchKernelGGL(k1_hist, dim3((uint32_t)(rows * ntiles * ntb)), dim3(256), lds, st, X, g,
+                       bins, lo, r, OCT, SUB, (uint32_t)tpt, ntiles, ntb, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_k1_freqs(const Geom &g, const uint8_t *bins, const uint32_t *counts,
+                           const float *lo, const float *w, uint16_t *freqs, uint2 *dtab,
+                           hipStream_t st)
+{
+    uint32_t n = g.L * 2 * g.C;
+    hipLaunchKernelGGL(k1_freqs, dim3((n + 255) / 256), dim3(256), 0, st, g, bins, counts, lo, w,
+                       freqs, dtab);
+    return hipGetLastError();
+}
+
+hipError_t launch_k2(const uint16_t *X, const Geom &g, const uint8_t *bins, const float *lo,
+                     const float *r, uint32_t t_lo, uint32_t t_hi, uint32_t tpt, uint8_t *sym,
+                     uint32_t sym_t0, uint32_t sym_T, uint16_t *anchors, hipStream_t st)
+{
+    uint32_t ntb = (t_hi - t_lo + tpt - 1) / tpt;
+    uint64_t threads = (uint64_t)g.L * 2 * ntb * (g.C / 8);
+    hipLaunchKernelGGL(k2_delta_quant, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st,
+                       X, g, bins, lo, r, t_lo, t_hi, tpt, ntb, sym, sym_t0, sym_T, anchors);
+    return hipGetLastError();
+}
+
+hipError_t launch_k5_plan(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
+                          const uint2 *dtab, uint32_t *lane_words, uint64_t *group_words,
+                          uint64_t n_groups, hipStream_t st)
+{
+    uint64_t blocks = (n_groups + 3) / 4;
+    hipLaunchKernelGGL(k5_plan, dim3((uint32_t)blocks), dim3(256), 0, st, sym, sym_t0, sym_T, g,
+                       dtab, lane_words, group_words, n_groups);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const uint64_t *in, uint64_t *out, uint64_t n, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, in, out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_k5_encode(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
+                            const uint2 *dtab, const uint32_t *lane_words,
+                            const uint64_t *group_off, uint16_t *scratch, uint64_t n_groups,
+                            hipStream_t st)
+{
+    uint64_t blocks = (n_groups + 3) / 4;
+    hipLaunchKernelGGL(k5_encode, dim3((uint32_t)blocks), dim3(256), 0, st, sym, sym_t0, sym_T, g,
+                       dtab, lane_words, group_off, scratch, n_groups);
+    return hipGetLastError();
+}
+
+hipError_t launch_k5_interleave(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T,
+                                const Geom &g, const uint2 *dtab, const uint32_t *lane_words,
+                                const uint64_t *group_off, const uint16_t *scratch,
+                                uint16_t *payload, uint64_t n_groups, hipStream_t st)
+{
+    uint64_t blocks = (n_groups + 3) / 4;
+    hipLaunchKernelGGL(k5_interleave, dim3((uint32_t)blocks), dim3(256), 0, st, sym, sym_t0,
+                       sym_T, g, dtab, lane_words, group_off, scratch, payload, n_groups);
+    return hipGetLastError();
+}
+
+hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint2 *dtab,
+                     const uint8_t *container, const ContainerView &cv, uint16_t *out,
+                     uint8_t *sym_out, hipStream_t st)
+{
+    uint32_t n_sets = (g.ke - g.kb + 3) / 4;
+    uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
+    if (sym_out)
+        hipLaunchKernelGGL(k3_decode<true>, dim3((uint32_t)blocks), dim3(256), 0, st, g, bins,
+                           dtab, container, cv, n_sets, out, sym_out);
+    else
+        hipLaunchKernelGGL(k3_decode<false>, dim3((uint32_t)blocks), dim3(256), 0, st, g, bins,
+                           dtab, container, cv, n_sets, out, sym_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_k4(const Geom &g, const float *lo, const float *w, const uint8_t *sym,
+                     const uint8_t *container, const ContainerView &cv, uint32_t t_lo,
+                     uint32_t t_hi, uint32_t tpt, uint16_t *out, hipStream_t st)
+{
+    uint32_t ntb = (t_hi - t_lo + tpt - 1) / tpt;
+    uint64_t threads = (uint64_t)g.L * 2 * ntb * (g.C / 8);
+    hipLaunchKernelGGL(k4_dequant, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st, g,
+                       lo, w, sym, container, cv, t_lo, t_hi, tpt, ntb, out);
+    return hipGetLastError();
+}
+
+}  // namespace cgk

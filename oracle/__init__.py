@@ -55,8 +55,7 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
-            build()
+        build(force=False)          # (re)compiles only when cgo.c is newer than the library
         L = ctypes.CDLL(LIB)
         L.cgo_half_to_float_n.argtypes = [_u16p, _f32p, ctypes.c_size_t]
         L.cgo_float_to_half_n.argtypes = [_f32p, _u16p, ctypes.c_size_t]

@@ -140,7 +140,7 @@ static size_t kv_index(const cgo_shape *p, uint32_t l, uint32_t kv, uint32_t t, 
 /* Step 2-3a: per-channel range of the anchor deltas.                               */
 /*   Delta = f32(x_t) - f32(x_anchor)    (one binary32 subtraction)                 */
 /*   lo, hi = min / max over every non-anchor token of the channel (all chunks);    */
-/*   lo = hi = 0 when the channel has no non-anchor token;                          */
+/*   lo = hi = 0 when the channel has no non-anchor token; a zero bound is +0;      */
 /*   w = (hi - lo) / (N - 1);  r = 1 / w, or 0 when w == 0.                          */
 /* Returns -4 if any input element is Inf or NaN, else 0.                           */
 /* ------------------------------------------------------------------------------ */
@@ -173,6 +173,9 @@ int cgo_range(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32
                     }
                 }
                 size_t row = ((size_t)l * 2 + kv) * C + c;
+                /* the sign of a zero bound is not meaningful: +0 + -0 = +0 fixes it */
+                lo = lo + 0.0f;
+                hi = hi + 0.0f;
                 float w = (hi - lo) / (float)(bins[l] - 1u);
                 lo_out[row] = lo;
                 w_out[row] = w;

@@ -1,0 +1,63 @@
+"""The C ABI library: it loads, exports every function include/cg.h declares, and its
+argument validation answers before touching a device (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cg.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cg_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from kv_cache_compression_cg_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    from kv_cache_compression_cg_amd import cg
+    return cg.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("cg_build_cdf", "cg_encode", "cg_decode", "cg_free"):
+        assert required in names
+
+
+def test_library_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    from kv_cache_compression_cg_amd import cg
+    assert sorted(cg.EXPORTED) == names
+
+
+def test_validation_without_device(lib):
+    from kv_cache_compression_cg_amd import cg
+    h = ctypes.c_void_p()
+    assert lib.cg_build_cdf(None, None, None, ctypes.byref(h)) == -1
+    assert b"null" in lib.cg_last_error()
+    bins = (ctypes.c_uint8 * 2)(8, 40)
+    p = cg.Params(2, 1, 8, 16, 4, 8, ctypes.cast(bins, ctypes.POINTER(ctypes.c_uint8)))
+    assert lib.cg_build_cdf(ctypes.byref(p), ctypes.c_void_p(16), None, ctypes.byref(h)) == -1
+    assert b"bins" in lib.cg_last_error()
+    p = cg.Params(2, 1, 6, 16, 4, 8, ctypes.cast(bins, ctypes.POINTER(ctypes.c_uint8)))
+    assert lib.cg_build_cdf(ctypes.byref(p), ctypes.c_void_p(16), None, ctypes.byref(h)) == -1
+    p = cg.Params(2, 1, 8, 16, 4, 20000, ctypes.cast(bins, ctypes.POINTER(ctypes.c_uint8)))
+    assert lib.cg_build_cdf(ctypes.byref(p), ctypes.c_void_p(16), None, ctypes.byref(h)) == -1
+    assert lib.cg_encode(None, None, 0, 1, None, ctypes.byref(h)) == -1
+    assert lib.cg_decode(None, None, None, None, None) == -1
+    assert lib.cg_quantize(None, None, 0, 1, None, None) == -1
+    assert lib.cg_blob_read(None, 0, 0, None) == -1
+    lib.cg_free(None)
+    # a handle that is neither tables nor blob is ignored
+    junk = ctypes.create_string_buffer(64)
+    lib.cg_free(junk)

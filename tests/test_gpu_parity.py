@@ -1,0 +1,190 @@
+"""GPU library (through the C ABI) against the CPU oracle, on the same seeded inputs.
+
+Bar: bit-exact tables (lo / w / r bits, frequencies), symbols, container (offsets,
+anchors, payload words) and decoded fp16 output, plus the unfused symbol path."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from kv_cache_compression_cg_amd import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def cg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_compression_cg_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    from kv_cache_compression_cg_amd import cg as _cg
+    _cg.load()
+    return _cg
+
+
+def _u16(t: torch.Tensor) -> np.ndarray:
+    return np.ascontiguousarray(t.detach().cpu().view(torch.int16).numpy().view(np.uint16))
+
+
+def _gen(L, S, C, gen, device="cuda"):
+    return synth.gen_custom(L, S, C, gen, device=device)
+
+
+GAUSS = configs.GenSpec(rho=0.9, heavy_tail=False, outlier_frac=0.02, outlier_mult=20.0, seed=0)
+HEAVY = configs.GenSpec(rho=0.85, heavy_tail=True, outlier_frac=0.05, outlier_mult=30.0, seed=1)
+
+
+def full_parity(cg, X, H, G, Tc, bins, chunk_range=None, label=""):
+    """Runs both sides on the same cache and compares every product of the path."""
+    L, _, S, C = X.shape
+    _say("[parity] %s L=%d S=%d C=%d G=%d Tc=%d bins=%s" % (label, L, S, C, G, Tc, list(bins)))
+    Xh = _u16(X)
+    shp = O.Shape.make(L, H, C // H, S, G, Tc, bins)
+    tab_o = O.build_tables(shp, Xh)
+    kb, ke = chunk_range if chunk_range else (0, shp.n_chunks)
+    enc_o = O.encode(shp, Xh, tab_o, kb, ke)
+
+    tab = cg.build_cdf(X, G, Tc, bins, H_kv=H)
+    ex = tab.export()
+    for name in ("lo", "w", "r"):
+        assert np.array_equal(ex[name].view(np.uint32), getattr(tab_o, name).view(np.uint32)), name
+    assert np.array_equal(ex["freqs"], tab_o.freqs)
+
+    sym = cg.quantize(tab, X, kb, ke)
+    t0, t1 = kb * Tc, min(ke * Tc, S)
+    sym_o = O.quantize(shp, Xh, tab_o.lo, tab_o.r, t0, t1)
+    assert np.array_equal(sym.cpu().numpy()[:, :, t0:t1], sym_o[:, :, t0:t1])
+
+    blob = cg.encode(tab, X, kb, ke)
+    assert np.array_equal(blob.offsets(), enc_o.offsets)
+    assert np.array_equal(blob.anchors(), enc_o.anchors)
+    assert np.array_equal(blob.payload(), enc_o.payload)
+
+    out = torch.full_like(X, float("nan"))
+    cg.decode(tab, blob, out)
+    ref = O.decode(shp, tab_o, enc_o, out=_u16(out))
+    torch.cuda.synchronize()
+    assert np.array_equal(_u16(out), ref)
+
+    dsym = cg.decode_symbols(tab, blob)
+    assert np.array_equal(dsym.cpu().numpy()[:, :, t0:t1], sym_o[:, :, t0:t1])
+    out2 = torch.full_like(X, float("nan"))
+    cg.dequantize(tab, blob, dsym, out2)
+    assert np.array_equal(_u16(out2), _u16(out))
+    return tab, blob, tab_o, enc_o
+
+
+def test_tiny_workload(cg):
+    w = configs.TINY
+    X = synth.gen_kv(w, device="cuda")
+    full_parity(cg, X, w.H_kv, w.group, w.chunk, w.bins, label="tiny")
+
+
+def test_several_tiles_ragged_tail_odd_bins(cg):
+    X = _gen(3, 1000, 192, HEAVY)
+    full_parity(cg, X, 3, 7, 300, (2, 13, 32), label="ragged")
+
+
+def test_partial_lane_block_and_chunk_range(cg):
+    X = _gen(2, 700, 72, GAUSS)
+    full_parity(cg, X, 9, 10, 256, (8, 5), label="C=72")
+    full_parity(cg, X, 9, 10, 256, (8, 5), chunk_range=(1, 3), label="C=72 chunks 1..3")
+
+
+def test_llama7b_shape_two_layers(cg):
+    w = configs.LLAMA7B
+    X = synth.gen_kv(w, device="cuda", layers=[0, 31])
+    full_parity(cg, X, w.H_kv, w.group, w.chunk, (w.bins[0], w.bins[31]), label="7B layers 0,31")
+
+
+@pytest.mark.parametrize("S,G,Tc", [(5, 10, 5), (37, 10, 37), (41, 4, 20), (64, 1, 16),
+                                    (130, 10, 16384)])
+def test_edge_shapes(cg, S, G, Tc):
+    X = _gen(2, S, 64, HEAVY)
+    full_parity(cg, X, 1, G, Tc, (2, 32), label="edge")
+
+
+def test_constant_and_signed_zero_channels(cg):
+    X = _gen(1, 300, 128, GAUSS)
+    X[0, 0, :, 0] = 1.5                     # constant channel
+    X[0, 1, :, 1] = 0.0                     # all +0
+    X[0, 1, 5::3, 2] = -0.0                 # mixes -0 and +0
+    X[0, 1, :, 2] = torch.where(torch.arange(300, device="cuda") % 3 == 0,
+                                torch.tensor(0.0, dtype=torch.float16, device="cuda"),
+                                torch.tensor(-0.0, dtype=torch.float16, device="cuda"))
+    tab, *_ = full_parity(cg, X, 2, 10, 128, (4,), label="constant/zero")
+    ex = tab.export()
+    assert ex["w"][0, 0, 0] == 0 and ex["lo"][0, 1, 2].view(np.uint32) == 0
+
+
+def test_nonfinite_input_is_rejected(cg):
+    X = _gen(1, 64, 64, GAUSS)
+    X[0, 1, 33, 7] = float("inf")
+    with pytest.raises(cg.CgError) as e:
+        cg.build_cdf(X, 10, 64, (8,), H_kv=1)
+    assert e.value.code == -4
+
+
+def test_mismatched_container_is_rejected(cg):
+    X = _gen(1, 64, 64, GAUSS)
+    t1 = cg.build_cdf(X, 10, 64, (8,), H_kv=1)
+    t2 = cg.build_cdf(X, 8, 64, (8,), H_kv=1)
+    b = cg.encode(t1, X)
+    with pytest.raises(cg.CgError) as e:
+        cg.decode(t2, b)
+    assert e.value.code == -5
+
+
+def test_damaged_container_decodes_without_fault(cg):
+    """Damaged payload words and offsets: reads stay inside the container."""
+    X = _gen(2, 500, 128, HEAVY)
+    tab = cg.build_cdf(X, 10, 128, (16, 4), H_kv=2)
+    blob = cg.encode(tab, X)
+    raw = torch.from_numpy(blob.read().copy()).cuda()
+    h = blob.header
+    g = torch.Generator().manual_seed(0)
+    pl0, pl1 = h["payload_offset"], h["payload_offset"] + 2 * h["payload_words"]
+    idx = torch.randint(pl0, pl1, (200,), generator=g)
+    raw[idx.cuda()] ^= 0x5A
+    offs = raw[h["offsets_offset"]:h["offsets_offset"] + 8 * (h["n_groups"] + 1)].view(torch.int64)
+    offs[3] = 1 << 40
+    offs[5] = 0
+    out = cg.decode(tab, blob, container=raw)
+    torch.cuda.synchronize()
+    assert out.shape == X.shape
+    # anchors are untouched by the damage
+    a = out[:, :, ::10][:, :, :13]
+    assert torch.equal(a.view(torch.int16), X[:, :, ::10][:, :, :13].view(torch.int16))
+
+
+def test_reconstruction_bound_at_scale(cg):
+    """8B-shaped slice, GPU only: anchors exact, every other element within half a bin
+    plus fp16 rounding (a property that holds at any size)."""
+    w = configs.LLAMA3_8B
+    X = synth.gen_kv(w, device="cuda", layers=[0, 20])
+    bins = (w.bins[0], w.bins[20])
+    tab = cg.build_cdf(X, w.group, w.chunk, bins, H_kv=w.H_kv)
+    blob = cg.encode(tab, X)
+    out = cg.decode(tab, blob)
+    wv = torch.from_numpy(tab.export()["w"]).cuda().double()
+    lo = torch.from_numpy(tab.export()["lo"]).cuda().double()
+    xs, ys = X.double(), out.double()
+    t = torch.arange(w.S, device="cuda")
+    anchor = ((t % w.chunk) % w.group) == 0
+    assert torch.equal(out[:, :, anchor].view(torch.int16), X[:, :, anchor].view(torch.int16))
+    err = (xs - ys).abs()[:, :, ~anchor]
+    ulp = torch.from_numpy(np.spacing(np.abs(out.cpu().numpy()).astype(np.float16))
+                           .astype(np.float64)).cuda()[:, :, ~anchor]
+    wb = wv[:, :, None, :]
+    tol = wb / 2 * (1 + 2 ** -20) + ulp / 2 + 2 ** -22 * (
+        xs.abs()[:, :, ~anchor] + ys.abs()[:, :, ~anchor] + 2 * lo.abs()[:, :, None, :] + 64 * wb)
+    assert bool((err <= tol).all())

@@ -390,3 +390,14 @@ def test_decode_of_damaged_payload_stays_in_bounds():
     O.decode(shp, tab, O.Encoded(enc.k_begin, enc.k_end,
                                  np.minimum(enc.offsets, trunc.size).astype(np.uint64),
                                  trunc, enc.anchors))
+
+
+def test_zero_bounds_are_positive_zero():
+    """Deltas of +0 and -0 compare equal; the stored bound is +0 either way."""
+    S, C = 30, 2
+    X = np.zeros((1, 2, S, C), np.uint16)
+    X[0, 0, 1::3, 0] = 0x8000                     # -0 at some tokens
+    X[0, 1, :, 1] = 0x8000                        # all -0: deltas are +0
+    shp = O.Shape.make(1, 1, C, S, 10, 30, [4])
+    tab = O.build_tables(shp, X)
+    assert (tab.lo.view(np.uint32) == 0).all() and (tab.w.view(np.uint32) == 0).all()
