@@ -338,7 +338,7 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     h.anchors_bytes = arows * t->C * 2;
     h.payload_offset = align256(h.anchors_offset + h.anchors_bytes);
     h.payload_words = total_words;
-    h.total_bytes = h.payload_offset + total_words * 2;
+    h.total_bytes = h.payload_offset + total_words * 2 + kPayloadPadBytes;
 
     cg_blob *b = new (std::nothrow) cg_blob();
     if (!b) return fail(CG_E_NOMEM, "host allocation");
@@ -346,7 +346,7 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     b->device = t->device;
     b->hdr = h;
     DevBuf data, scratch;
-    hipError_t e = data.alloc(align256(h.total_bytes) + 256);
+    hipError_t e = data.alloc(align256(h.total_bytes));
     if (e != hipSuccess) {
         delete b;
         return hip_fail(e, "hipMalloc container");
@@ -366,6 +366,8 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
         }                                    \
     } while (0)
     CG_HIP_B(hipMemcpyAsync(base, &h, sizeof h, hipMemcpyHostToDevice, st), "copy header");
+    CG_HIP_B(hipMemsetAsync(base + h.payload_offset + total_words * 2, 0, kPayloadPadBytes, st),
+             "clear padding");
     CG_HIP_B(hipMemcpyAsync(base + h.offsets_offset, group_off.p, (n_groups + 1) * 8,
                             hipMemcpyDeviceToDevice, st),
              "copy offsets");

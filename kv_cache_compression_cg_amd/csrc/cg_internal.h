@@ -11,8 +11,11 @@ constexpr uint32_t kProbBits = 12;                 // frequencies are in units o
 constexpr uint32_t kProbTotal = 1u << kProbBits;
 constexpr uint32_t kMaxBins = 32;
 constexpr uint32_t kLanes = 64;                    // channels per group = wavefront width
-constexpr uint32_t kRenormBelow = 1u << 16;        // renormalise (one 16-bit word) below 2^16
-constexpr uint32_t kRangeInit = 0xFFFFFFFFu;
+constexpr uint32_t kRenormBelow = 1u << 15;        // renormalise (one 16-bit word) below 2^15
+constexpr uint32_t kRangeInit = 0x7FFFFFFFu;       // 31-bit range
+constexpr uint32_t kPayloadPadBytes = 1024;        // zero bytes after the payload of a container
+// dword 3 of a raw (untyped) buffer resource on gfx9-family GPUs: 32-bit data format
+constexpr int kBufferFlags = 0x00020000;
 
 // Geometry of one call.  kb, ke: chunk range being encoded / decoded.
 struct Geom {

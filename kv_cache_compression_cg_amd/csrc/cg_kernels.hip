@@ -590,82 +590,175 @@ __global__ __launch_bounds__(256) void k5_interleave(const uint8_t *__restrict__
 // ------------------------------------------------------------------------------ K3 (+K4)
 // Range decoder, one wavefront per group, fused with dequantize + anchor-add.
 // Block = 4 wavefronts = 4 consecutive chunks of the same (row, block), sharing the
-// block's decode table in LDS (P <= 32 entries x 64 lanes x 8 bytes).
-template <int LOGP, bool SYMBOLS>
-__device__ __forceinline__ void decode_wave(const Geom &g, const uint2 *__restrict__ tab_lds,
+// block's decode table in LDS (P <= 32 entries x 64 lanes x 8 bytes).  Everything that
+// is the same for the 64 lanes (chunk, token, group, stream cursor, row addresses) is
+// kept in scalar registers; only the coder state and the table address are per lane.
+// Buffer resource over `bytes` bytes at p: loads at or past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             kBufferFlags);
+}
+
+// Per-wavefront LDS ring of payload words (stored inverted, see below), refilled with
+// 8-byte-per-lane loads one anchor group ahead of use.  Ring slots [0, 64) are mirrored
+// at [512, 576), so the up-to-64 words one step reads are contiguous in LDS.
+constexpr uint32_t kRingWords = 512;
+constexpr uint32_t kRingAlloc = kRingWords + 64;
+constexpr uint32_t kFetchWords = 256;
+constexpr uint32_t kWavesPerBlock = 4;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Stores the 4 words at stream position pos (a multiple of 4) into the ring.
+__device__ __forceinline__ void ring_put(uint16_t *ring, uint32_t pos, u32x2 v)
+{
+    const uint32_t slot = pos & (kRingWords - 1);
+    const uint2 iv = make_uint2(~v[0], ~v[1]);
+    *reinterpret_cast<uint2 *>(ring + slot) = iv;
+    if (slot < 64) *reinterpret_cast<uint2 *>(ring + slot + kRingWords) = iv;
+}
+
+// One wavefront decodes one group.  The coder state is kept as ncode = ~code, which
+// turns both the symbol search and the state update into one multiply-add each:
+//   q*cdf <= code  <=>  (int)(q*cdf + ncode) < 0    (all values < 2^31)
+//   ~(code - q*cdf) = q*cdf + ncode.
+// Renormalisation shifts in inverted words, which is why the ring holds ~word.
+template <int LOGP, bool SYMBOLS, bool FULL>
+__device__ __forceinline__ void decode_wave(const Geom &g, const uint8_t *__restrict__ tab,
+                                            uint16_t *__restrict__ ring,
                                             const uint8_t *__restrict__ container,
                                             const ContainerView &cv, uint32_t k, uint32_t row,
                                             uint32_t b, uint32_t lane, uint16_t *__restrict__ out,
                                             uint8_t *__restrict__ sym_out)
 {
-    const uint32_t c = b * kLanes + lane;
-    const bool present = c < g.C;
     const uint32_t nl = min(kLanes, g.C - b * kLanes);
+    const bool present = FULL || lane < nl;
     const uint32_t t0 = k * g.Tc, len = chunk_len(g, k);
     const uint32_t ng = (len + g.G - 1) / g.G, m = len - ng;
 
     const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
     const uint64_t *offs = reinterpret_cast<const uint64_t *>(container + cv.offsets_off);
-    uint64_t end = min(offs[gidx + 1], cv.payload_words);
-    uint64_t beg = min(offs[gidx], end);
-    const uint16_t *words = reinterpret_cast<const uint16_t *>(container + cv.payload_off);
+    const uint64_t end = min(offs[gidx + 1], cv.payload_words);
+    const uint64_t beg = min(offs[gidx], end);
+    // words from the group's first word to the end of the zero-padded payload; the
+    // hardware range check returns 0 for anything past it
+    const uint64_t avail = 2 * (cv.payload_words - beg) + kPayloadPadBytes;
+    const __amdgpu_buffer_rsrc_t wrs =
+        make_rsrc(container + cv.payload_off + 2 * beg, (uint32_t)min(avail, (uint64_t)0xFFFFFFFFu));
     const uint16_t *anc = reinterpret_cast<const uint16_t *>(container + cv.anchors_off) +
-                          anchor_row(g, k, row, 0) * g.C + c;
-    const uint64_t orow = ((uint64_t)row * g.S + t0) * g.C + c;
+                          anchor_row(g, k, row, 0) * g.C + b * kLanes;
+    const uint64_t obase = ((uint64_t)row * g.S + t0) * g.C + b * kLanes;
+    const __amdgpu_buffer_rsrc_t ors =
+        SYMBOLS ? make_rsrc(sym_out + obase, 0xFFFFFFFFu) : make_rsrc(out + obase, 0xFFFFFFFFu);
+    const uint32_t ostride = g.C * (SYMBOLS ? 1u : 2u);  // bytes between token rows
+    const uint32_t olane = lane * (SYMBOLS ? 1u : 2u);
 
-    uint32_t code = 0, range = kRangeInit;
-    if (present && m > 0) {
-        uint64_t p0 = beg + 2 * lane;
-        uint32_t hi = p0 < end ? words[p0] : 0u;
-        uint32_t lo = p0 + 1 < end ? words[p0 + 1] : 0u;
-        code = (hi << 16) | lo;
+    uint32_t ncode = 0xFFFFFFFFu, range = kRangeInit;
+    uint32_t re = 0;  // words [re - kRingWords, re) of the group are in the ring
+    if (m > 0) {
+        for (uint32_t j = 0; j < kRingWords; j += kFetchWords)
+            ring_put(ring, j + 4 * lane,
+                     __builtin_amdgcn_raw_buffer_load_b64(wrs, 2 * (j + 4 * lane), 0, 0));
+        re = kRingWords;
+        if (present) ncode = ((uint32_t)ring[2 * lane] << 16) | ring[2 * lane + 1];
     }
-    uint64_t cursor = beg + 2 * nl;
-    const uint16_t *tab16 = reinterpret_cast<const uint16_t *>(tab_lds) + lane * 4;
-    const uint2 *tabe = tab_lds + lane;
+    uint32_t cur = 2 * nl;  // next unread word of the group
+    u32x2 pf = {0u, 0u};
+    uint32_t pf_at = 0;
+    bool pending = false;
+    uint32_t a_next = present ? anc[lane] : 0u;
+    const uint32_t lb = lane * 8;  // byte offset of entry (symbol 0, this lane)
     uint32_t i = 0;
+    uint32_t orow = 0;             // byte offset of the current token row
     for (uint32_t gi = 0; gi < ng; ++gi) {
-        const uint32_t tr = gi * g.G;
-        uint32_t a16 = present ? anc[(uint64_t)gi * g.C] : 0u;
+        const uint32_t a16 = a_next;
         if (present) {
             if (SYMBOLS)
-                sym_out[orow + (uint64_t)tr * g.C] = 0;
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, ors, olane, orow, 0);
             else
-                out[orow + (uint64_t)tr * g.C] = (uint16_t)a16;
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)a16, ors, olane, orow, 0);
         }
+        orow += ostride;
+        // refill: commit the words fetched one group ago, fetch the next ones
+        if (pending) {
+            ring_put(ring, pf_at + 4 * lane, pf);
+            re = pf_at + kFetchWords;
+            pending = false;
+        }
+        if (m > 0 && re + kFetchWords - cur <= kRingWords) {
+            pf = __builtin_amdgcn_raw_buffer_load_b64(wrs, 2 * (re + 4 * lane), 0, 0);
+            pf_at = re;
+            pending = true;
+        }
+        if (present && gi + 1 < ng) a_next = anc[(uint64_t)(gi + 1) * g.C + lane];
         const float af = h2f(a16);
-        const uint32_t ulen = min(g.G, len - tr);
-        for (uint32_t u = 1; u < ulen; ++u) {
+        const uint32_t nsteps = __builtin_amdgcn_readfirstlane(min(g.G, len - gi * g.G) - 1);
+        for (uint32_t u = nsteps; u != 0; --u) {
             const uint32_t q = range >> kProbBits;
-            uint32_t s = 0;
+            uint32_t p = lb;
 #pragma unroll
             for (int h = (1 << LOGP) >> 1; h >= 1; h >>= 1) {
-                uint32_t cdf = tab16[(s + h) * (kLanes * 4)];
-                if (__umul24(q, cdf) <= code) s += h;
+                const uint32_t cdf = *reinterpret_cast<const uint16_t *>(tab + p + h * 512);
+                const int32_t d = (int32_t)(__umul24(q, cdf) + ncode);
+                p |= (uint32_t)(d >> 31) & ((uint32_t)h * 512u);
             }
-            const uint2 e = tabe[s * kLanes];
-            code -= __umul24(q, e.x & 0xFFFFu);
-            range = __umul24(q, e.x >> 16);
+            const uint32_t cdf_s = *reinterpret_cast<const uint16_t *>(tab + p);
+            const uint32_t f_s = *reinterpret_cast<const uint16_t *>(tab + p + 2);
+            ncode = __umul24(q, cdf_s) + ncode;
+            range = __umul24(q, f_s);
             if (present) {
-                const uint64_t oi = orow + (uint64_t)(tr + u) * g.C;
-                if (SYMBOLS)
-                    sym_out[oi] = (uint8_t)s;
-                else
-                    out[oi] = (uint16_t)f2h(af + __uint_as_float(e.y));
-            }
-            ++i;
-            const bool need = present && (i < m) && (range < kRenormBelow);
-            const uint64_t mask = __ballot(need);
-            if (mask) {
-                if (need) {
-                    uint64_t pos = cursor + mbcnt64(mask);
-                    uint32_t wd = pos < end ? words[pos] : 0u;
-                    code = (code << 16) | wd;
-                    range <<= 16;
+                if (SYMBOLS) {
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(p >> 9), ors, olane, orow, 0);
+                } else {
+                    const float dq = *reinterpret_cast<const float *>(tab + p + 4);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f2h(af + dq), ors, olane, orow, 0);
                 }
-                cursor += (uint32_t)__popcll(mask);
+            }
+            orow += ostride;
+            if (++i < m) {
+                const bool need = present && (range < kRenormBelow);
+                const uint64_t mask = __ballot(need);
+                if (mask) {
+                    const uint32_t cnt = (uint32_t)__popcll(mask);
+                    if (cur + cnt > re) {
+                        // the group outran the prefetch: commit it now, load more if needed
+                        if (pending) {
+                            ring_put(ring, pf_at + 4 * lane, pf);
+                            re = pf_at + kFetchWords;
+                            pending = false;
+                        }
+                        while (cur + cnt > re) {
+                            ring_put(ring, re + 4 * lane,
+                                     __builtin_amdgcn_raw_buffer_load_b64(wrs, 2 * (re + 4 * lane), 0, 0));
+                            re += kFetchWords;
+                        }
+                    }
+                    if (need) {
+                        const uint16_t *rp = ring + (cur & (kRingWords - 1));
+                        ncode = (ncode << 16) | rp[mbcnt64(mask)];
+                        range <<= 16;
+                    }
+                    cur += cnt;
+                }
             }
         }
+    }
+}
+
+template <bool SYMBOLS, bool FULL>
+__device__ __forceinline__ void decode_dispatch(uint32_t logp, const Geom &g, const uint8_t *tab,
+                                                uint16_t *ring, const uint8_t *container,
+                                                const ContainerView &cv, uint32_t k, uint32_t row,
+                                                uint32_t b, uint32_t lane, uint16_t *out,
+                                                uint8_t *sym_out)
+{
+    switch (logp) {
+    case 1: decode_wave<1, SYMBOLS, FULL>(g, tab, ring, container, cv, k, row, b, lane, out, sym_out); break;
+    case 2: decode_wave<2, SYMBOLS, FULL>(g, tab, ring, container, cv, k, row, b, lane, out, sym_out); break;
+    case 3: decode_wave<3, SYMBOLS, FULL>(g, tab, ring, container, cv, k, row, b, lane, out, sym_out); break;
+    case 4: decode_wave<4, SYMBOLS, FULL>(g, tab, ring, container, cv, k, row, b, lane, out, sym_out); break;
+    default: decode_wave<5, SYMBOLS, FULL>(g, tab, ring, container, cv, k, row, b, lane, out, sym_out); break;
     }
 }
 
@@ -678,6 +771,7 @@ __global__ __launch_bounds__(256) void k3_decode(Geom g, const uint8_t *__restri
                                                   uint8_t *__restrict__ sym_out)
 {
     __shared__ uint2 tab[kMaxBins * kLanes];
+    __shared__ uint16_t rings[kWavesPerBlock * kRingAlloc];
     const uint32_t set = blockIdx.x % n_sets;
     const uint32_t tmp = blockIdx.x / n_sets;
     const uint32_t b = tmp % g.NB;
@@ -690,16 +784,16 @@ __global__ __launch_bounds__(256) void k3_decode(Geom g, const uint8_t *__restri
     uint4 *dst = reinterpret_cast<uint4 *>(tab);
     for (uint32_t j = threadIdx.x; j < n16; j += blockDim.x) dst[j] = src[j];
     __syncthreads();
-    const uint32_t wave = threadIdx.x / kLanes, lane = threadIdx.x % kLanes;
-    const uint32_t k = g.kb + set * 4 + wave;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const uint32_t lane = threadIdx.x % kLanes;
+    const uint32_t k = g.kb + set * kWavesPerBlock + wave;
     if (k >= g.ke) return;
-    switch (logp) {
-    case 1: decode_wave<1, SYMBOLS>(g, tab, container, cv, k, row, b, lane, out, sym_out); break;
-    case 2: decode_wave<2, SYMBOLS>(g, tab, container, cv, k, row, b, lane, out, sym_out); break;
-    case 3: decode_wave<3, SYMBOLS>(g, tab, container, cv, k, row, b, lane, out, sym_out); break;
-    case 4: decode_wave<4, SYMBOLS>(g, tab, container, cv, k, row, b, lane, out, sym_out); break;
-    default: decode_wave<5, SYMBOLS>(g, tab, container, cv, k, row, b, lane, out, sym_out); break;
-    }
+    const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab);
+    uint16_t *ring = rings + wave * kRingAlloc;
+    if (g.C - b * kLanes >= kLanes)
+        decode_dispatch<SYMBOLS, true>(logp, g, tb, ring, container, cv, k, row, b, lane, out, sym_out);
+    else
+        decode_dispatch<SYMBOLS, false>(logp, g, tb, ring, container, cv, k, row, b, lane, out, sym_out);
 }
 
 // ------------------------------------------------------------------------------ K4
@@ -859,7 +953,7 @@ hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint2 *dtab,
                      const uint8_t *container, const ContainerView &cv, uint16_t *out,
                      uint8_t *sym_out, hipStream_t st)
 {
-    uint32_t n_sets = (g.ke - g.kb + 3) / 4;
+    uint32_t n_sets = (g.ke - g.kb + kWavesPerBlock - 1) / kWavesPerBlock;
     uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
     if (sym_out)
         hipLaunchKernelGGL(k3_decode<true>, dim3((uint32_t)blocks), dim3(256), 0, st, g, bins,

@@ -41,8 +41,8 @@
 #define CGO_PROB_TOTAL (1u << CGO_PROB_BITS) /* frequencies sum to 4096 */
 #define CGO_MAX_BINS 32u
 #define CGO_LANES 64u                       /* channels per interleaved group */
-#define CGO_RANGE_INIT 0xFFFFFFFFu
-#define CGO_RENORM_BELOW 0x10000u           /* renormalise when range < 2^16 */
+#define CGO_RANGE_INIT 0x7FFFFFFFu           /* 31-bit range: every product fits a signed int */
+#define CGO_RENORM_BELOW 0x8000u            /* renormalise when range < 2^15 */
 
 /* ------------------------------------------------------------------------------ */
 /* IEEE-754 binary16 <-> binary32, written from the format definition.             */
@@ -275,12 +275,12 @@ void cgo_freqs(uint32_t L, uint32_t C, const uint8_t *bins, const uint64_t *coun
 
 /* ------------------------------------------------------------------------------ */
 /* Step 4b: range coder (G. N. N. Martin, "Range encoding", 1979), multi-symbol,     */
-/* 32-bit range, 16-bit output words, probabilities in units of 1/4096.              */
+/* 31-bit range, 16-bit output words, probabilities in units of 1/4096.              */
 /*                                                                                    */
 /* Encoder, for symbols x_0 .. x_{m-1} with cumulative table cdf (cdf[N] = 4096):    */
-/*   low = 0, range = 2^32 - 1                                                        */
+/*   low = 0, range = 2^31 - 1                                                        */
 /*   for each i: q = range >> 12; low += q * cdf[x_i]; range = q * f[x_i];            */
-/*               if i < m - 1 and range < 2^16: shift one 16-bit word out of low,     */
+/*               if i < m - 1 and range < 2^15: shift one 16-bit word out of low,     */
 /*               low <<= 16, range <<= 16   (a "renormalisation event" at step i)    */
 /*   the stream is the 2 + (number of events) base-65536 digits of the final low,    */
 /*   most significant first.  Carries out of the 32-bit window are added into the    */
@@ -331,10 +331,10 @@ uint32_t cgo_rc_encode(const uint8_t *x, uint32_t m, const uint16_t *f, uint32_t
     return nw;
 }
 
-/* Decoder: code = words 0..1; then for each step q = range >> 12, the symbol is the
- * largest s with q * cdf[s] <= code; code -= q * cdf[s]; range = q * f[s]; and, except
- * after the last symbol, range < 2^16 pulls in the next word.  Words past the end of
- * the stream read as 0.  Returns the number of words consumed. */
+/* Decoder: code = words 0..1; range = 2^31 - 1; then for each step q = range >> 12, the
+ * symbol is the largest s with q * cdf[s] <= code; code -= q * cdf[s]; range = q * f[s];
+ * and, except after the last symbol, range < 2^15 pulls in the next word.  Words past
+ * the end of the stream read as 0.  Returns the number of words consumed. */
 uint32_t cgo_rc_decode(const uint16_t *words, uint32_t nw, uint32_t m, const uint16_t *f,
                        uint32_t N, uint8_t *x_out)
 {

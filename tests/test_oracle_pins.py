@@ -216,18 +216,18 @@ def test_frequency_table_invariants(N, data):
 def _big_model(x, f):
     """Exact big-integer model of the coder (no 32-bit window, no carry handling)."""
     cdf = np.concatenate([[0], np.cumsum(f)]).astype(int)
-    L, R, scale_words, events = 0, 2 ** 32 - 1, 0, []
+    L, R, scale_words, events = 0, 2 ** 31 - 1, 0, []
     for i, s in enumerate(x):
         q = R // T
         L += q * int(cdf[s])
         R = q * int(f[s])
-        if i + 1 < len(x) and R < 2 ** 16:
+        if i + 1 < len(x) and R < 2 ** 15:
             L *= 2 ** 16
             R *= 2 ** 16
             scale_words += 1
             events.append(i)
     nw = 2 + scale_words
-    assert L + R <= (2 ** 32) * 2 ** (16 * scale_words)
+    assert L + R <= (2 ** 31) * 2 ** (16 * scale_words)
     words = [(L >> (16 * (nw - 1 - j))) & 0xFFFF for j in range(nw)]
     steps = [-1, -1] + events
     return words, steps
@@ -270,9 +270,10 @@ def test_coder_random_streams_against_big_model_and_length_bound(data):
     assert list(words) == bw and list(steps) == bs
     dec, used = O.rc_decode(words, m, f)
     assert np.array_equal(dec, x) and used == len(words)
-    # each step loses at most log2(16/15) bits (range >= 2^16 before every step)
+    # each step loses at most log2(8/7) bits (range >= 2^15 before every step, so
+    # q * 4096 > range - 4096 >= range * 7/8)
     ideal = float(np.sum(np.log2(T / f[x].astype(np.float64))))
-    assert 16 * len(words) <= ideal + m * math.log2(16 / 15) + 32 + 1e-6
+    assert 16 * len(words) <= ideal + m * math.log2(8 / 7) + 32 + 1e-6
 
 
 def test_coded_size_close_to_empirical_entropy():
