@@ -156,6 +156,7 @@ ContainerView view_of(const cg_blob *b)
     ContainerView v;
     v.offsets_off = b->hdr.offsets_offset;
     v.anchors_off = b->hdr.anchors_offset;
+    v.anchors_bytes = b->hdr.anchors_bytes;
     v.payload_off = b->hdr.payload_offset;
     v.payload_words = b->hdr.payload_words;
     return v;

@@ -27,7 +27,7 @@ struct Geom {
 
 // Byte offsets of the container sections.
 struct ContainerView {
-    uint64_t offsets_off, anchors_off, payload_off, payload_words;
+    uint64_t offsets_off, anchors_off, anchors_bytes, payload_off, payload_words;
 };
 
 hipError_t launch_k0(const uint16_t *X, const Geom &g, uint32_t tpt, uint32_t *ord_lo,

@@ -601,29 +601,100 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 }
 
 // Per-wavefront LDS ring of payload words (stored inverted, see below), refilled with
-// 8-byte-per-lane loads one anchor group ahead of use.  Ring slots [0, 64) are mirrored
-// at [512, 576), so the up-to-64 words one step reads are contiguous in LDS.
-constexpr uint32_t kRingWords = 512;
+// 4-byte-per-lane loads.  Ring slots [0, 64) are mirrored at [R, R + 64), so the up-to-
+// 64 words one step reads are contiguous in LDS.
+constexpr uint32_t kRingWords = 256;
 constexpr uint32_t kRingAlloc = kRingWords + 64;
-constexpr uint32_t kFetchWords = 256;
+constexpr uint32_t kFetchWords = 128;
 constexpr uint32_t kWavesPerBlock = 4;
+// Groups of this many decode steps (anchor interval 10) run fully unrolled with their
+// outputs held in registers; any other group length takes the generic loop.
+constexpr int kUnrolledSteps = 9;
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// Stores the 4 words at stream position pos (a multiple of 4) into the ring.
-__device__ __forceinline__ void ring_put(uint16_t *ring, uint32_t pos, u32x2 v)
+// Stores the 2 words at stream position pos (even) into the ring, inverted.
+__device__ __forceinline__ void ring_put(uint16_t *ring, uint32_t pos, uint32_t v)
 {
     const uint32_t slot = pos & (kRingWords - 1);
-    const uint2 iv = make_uint2(~v[0], ~v[1]);
-    *reinterpret_cast<uint2 *>(ring + slot) = iv;
-    if (slot < 64) *reinterpret_cast<uint2 *>(ring + slot + kRingWords) = iv;
+    *reinterpret_cast<uint32_t *>(ring + slot) = ~v;
+    if (slot < 64) *reinterpret_cast<uint32_t *>(ring + slot + kRingWords) = ~v;
 }
 
-// One wavefront decodes one group.  The coder state is kept as ncode = ~code, which
+// State of one wavefront's decoder.  The coder state is kept as ncode = ~code, which
 // turns both the symbol search and the state update into one multiply-add each:
 //   q*cdf <= code  <=>  (int)(q*cdf + ncode) < 0    (all values < 2^31)
 //   ~(code - q*cdf) = q*cdf + ncode.
 // Renormalisation shifts in inverted words, which is why the ring holds ~word.
+struct WaveDecoder {
+    uint32_t ncode, range;
+    uint32_t cur, re;  // next unread word; words [re - R, re) are in the ring
+    uint32_t i, m;     // symbols decoded so far / in the chunk
+    uint16_t *ring;
+    __amdgpu_buffer_rsrc_t wrs;
+    bool present;
+
+    // Table entry of the decoded symbol (byte offset into the LDS table).
+    template <int LOGP>
+    __device__ __forceinline__ uint32_t symbol(const uint8_t *tab, uint32_t lb, float &dq)
+    {
+        const uint32_t q = range >> kProbBits;
+        uint32_t p = lb;
+#pragma unroll
+        for (int h = (1 << LOGP) >> 1; h >= 1; h >>= 1) {
+            const uint32_t cdf = *reinterpret_cast<const uint16_t *>(tab + p + h * 512);
+            const int32_t d = (int32_t)(__umul24(q, cdf) + ncode);
+            p |= (uint32_t)(d >> 31) & ((uint32_t)h * 512u);
+        }
+        const uint32_t cdf_s = *reinterpret_cast<const uint16_t *>(tab + p);
+        const uint32_t f_s = *reinterpret_cast<const uint16_t *>(tab + p + 2);
+        dq = *reinterpret_cast<const float *>(tab + p + 4);
+        ncode = __umul24(q, cdf_s) + ncode;
+        range = __umul24(q, f_s);
+        return p;
+    }
+
+    // Loads ring chunks until the words [cur, cur + cnt) are present (rare path).
+    __device__ __forceinline__ void refill_now(uint32_t cnt, uint32_t lane)
+    {
+        while (cur + cnt > re) {
+            ring_put(ring, re + 2 * lane, __builtin_amdgcn_raw_buffer_load_b32(wrs, 2 * (re + 2 * lane), 0, 0));
+            re += kFetchWords;
+        }
+    }
+
+    __device__ __forceinline__ void renorm(uint32_t lane)
+    {
+        if (++i < m) {
+            const bool need = present && (range < kRenormBelow);
+            const uint64_t mask = __ballot(need);
+            if (mask) {
+                const uint32_t cnt = (uint32_t)__popcll(mask);
+                if (cur + cnt > re) refill_now(cnt, lane);
+                if (need) {
+                    const uint16_t *rp = ring + (cur & (kRingWords - 1));
+                    ncode = (ncode << 16) | rp[mbcnt64(mask)];
+                    range <<= 16;
+                }
+                cur += cnt;
+            }
+        }
+    }
+};
+
+template <bool SYMBOLS>
+__device__ __forceinline__ void put_out(const __amdgpu_buffer_rsrc_t &ors, uint32_t olane,
+                                        uint32_t orow, uint32_t v)
+{
+    if (SYMBOLS)
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, ors, olane, orow, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, ors, olane, orow, 0);
+}
+
+// One wavefront decodes one group (chunk k, row, channel block b).  Vector memory is
+// only touched at anchor boundaries: there the next ring chunk and the next anchor row
+// are requested, then the previous group's outputs (held in registers) are written.
+// Waiting for the requested data at the following boundary therefore only waits for
+// operations issued a whole group earlier.
 template <int LOGP, bool SYMBOLS, bool FULL>
 __device__ __forceinline__ void decode_wave(const Geom &g, const uint8_t *__restrict__ tab,
                                             uint16_t *__restrict__ ring,
@@ -633,10 +704,14 @@ __device__ __forceinline__ void decode_wave(const Geom &g, const uint8_t *__rest
                                             uint8_t *__restrict__ sym_out)
 {
     const uint32_t nl = min(kLanes, g.C - b * kLanes);
-    const bool present = FULL || lane < nl;
     const uint32_t t0 = k * g.Tc, len = chunk_len(g, k);
-    const uint32_t ng = (len + g.G - 1) / g.G, m = len - ng;
+    const uint32_t ng = (len + g.G - 1) / g.G;
 
+    WaveDecoder dec;
+    dec.present = FULL || lane < nl;
+    dec.m = len - ng;
+    dec.i = 0;
+    dec.ring = ring;
     const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
     const uint64_t *offs = reinterpret_cast<const uint64_t *>(container + cv.offsets_off);
     const uint64_t end = min(offs[gidx + 1], cv.payload_words);
@@ -644,105 +719,98 @@ __device__ __forceinline__ void decode_wave(const Geom &g, const uint8_t *__rest
     // words from the group's first word to the end of the zero-padded payload; the
     // hardware range check returns 0 for anything past it
     const uint64_t avail = 2 * (cv.payload_words - beg) + kPayloadPadBytes;
-    const __amdgpu_buffer_rsrc_t wrs =
-        make_rsrc(container + cv.payload_off + 2 * beg, (uint32_t)min(avail, (uint64_t)0xFFFFFFFFu));
-    const uint16_t *anc = reinterpret_cast<const uint16_t *>(container + cv.anchors_off) +
-                          anchor_row(g, k, row, 0) * g.C + b * kLanes;
+    dec.wrs = make_rsrc(container + cv.payload_off + 2 * beg, (uint32_t)min(avail, (uint64_t)0xFFFFFFFFu));
+    // anchor rows of this group: row gi at byte 2 * (gi * C + lane); reads beyond the
+    // anchors section return 0
+    const uint64_t aoff = anchor_row(g, k, row, 0) * g.C + b * kLanes;
+    const __amdgpu_buffer_rsrc_t ars =
+        make_rsrc(container + cv.anchors_off + 2 * aoff,
+                  (uint32_t)min(cv.anchors_bytes - min(2 * aoff, cv.anchors_bytes), (uint64_t)0xFFFFFFFFu));
+    const uint32_t astride = 2 * g.C;
     const uint64_t obase = ((uint64_t)row * g.S + t0) * g.C + b * kLanes;
     const __amdgpu_buffer_rsrc_t ors =
         SYMBOLS ? make_rsrc(sym_out + obase, 0xFFFFFFFFu) : make_rsrc(out + obase, 0xFFFFFFFFu);
     const uint32_t ostride = g.C * (SYMBOLS ? 1u : 2u);  // bytes between token rows
     const uint32_t olane = lane * (SYMBOLS ? 1u : 2u);
+    const uint32_t lb = lane * 8;                         // entry (symbol 0, this lane)
 
-    uint32_t ncode = 0xFFFFFFFFu, range = kRangeInit;
-    uint32_t re = 0;  // words [re - kRingWords, re) of the group are in the ring
-    if (m > 0) {
-        for (uint32_t j = 0; j < kRingWords; j += kFetchWords)
-            ring_put(ring, j + 4 * lane,
-                     __builtin_amdgcn_raw_buffer_load_b64(wrs, 2 * (j + 4 * lane), 0, 0));
-        re = kRingWords;
-        if (present) ncode = ((uint32_t)ring[2 * lane] << 16) | ring[2 * lane + 1];
+    dec.ncode = 0xFFFFFFFFu;
+    dec.range = kRangeInit;
+    dec.re = 0;
+    if (dec.m > 0) {
+        dec.cur = 0;
+        dec.refill_now(kRingWords, lane);
+        if (dec.present) dec.ncode = ((uint32_t)ring[2 * lane] << 16) | ring[2 * lane + 1];
     }
-    uint32_t cur = 2 * nl;  // next unread word of the group
-    u32x2 pf = {0u, 0u};
-    uint32_t pf_at = 0;
-    bool pending = false;
-    uint32_t a_next = present ? anc[lane] : 0u;
-    const uint32_t lb = lane * 8;  // byte offset of entry (symbol 0, this lane)
-    uint32_t i = 0;
-    uint32_t orow = 0;             // byte offset of the current token row
+    dec.cur = 2 * nl;
+
+    uint32_t a16 = __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, 0, 0);
+    asm volatile("" : "+v"(a16));
+    float af = h2f(a16);
+    uint32_t y[kUnrolledSteps];
+    bool held = false;          // y holds the outputs of the previous group
+    uint32_t orow_held = 0;     // byte offset of its first decoded row
+    uint32_t orow = 0;          // byte offset of the current anchor row
     for (uint32_t gi = 0; gi < ng; ++gi) {
-        const uint32_t a16 = a_next;
-        if (present) {
-            if (SYMBOLS)
-                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, ors, olane, orow, 0);
-            else
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)a16, ors, olane, orow, 0);
-        }
-        orow += ostride;
-        // refill: commit the words fetched one group ago, fetch the next ones
-        if (pending) {
-            ring_put(ring, pf_at + 4 * lane, pf);
-            re = pf_at + kFetchWords;
-            pending = false;
-        }
-        if (m > 0 && re + kFetchWords - cur <= kRingWords) {
-            pf = __builtin_amdgcn_raw_buffer_load_b64(wrs, 2 * (re + 4 * lane), 0, 0);
-            pf_at = re;
-            pending = true;
-        }
-        if (present && gi + 1 < ng) a_next = anc[(uint64_t)(gi + 1) * g.C + lane];
-        const float af = h2f(a16);
-        const uint32_t nsteps = __builtin_amdgcn_readfirstlane(min(g.G, len - gi * g.G) - 1);
-        for (uint32_t u = nsteps; u != 0; --u) {
-            const uint32_t q = range >> kProbBits;
-            uint32_t p = lb;
+        // requests, consumed at the end of this group: the next anchor row and the next
+        // chunk of words (kept only if the ring has room for it)
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t a_next = __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, (gi + 1) * astride, 0);
+        const bool fetch = dec.m > 0 && dec.re + kFetchWords - dec.cur <= kRingWords;
+        const uint32_t pf_at = dec.re;
+        const uint32_t pf = __builtin_amdgcn_raw_buffer_load_b32(dec.wrs, 2 * (pf_at + 2 * lane), 0, 0);
+        // writes: the previous group's outputs, then this anchor row
+        if (held) {
+            if (dec.present) {
 #pragma unroll
-            for (int h = (1 << LOGP) >> 1; h >= 1; h >>= 1) {
-                const uint32_t cdf = *reinterpret_cast<const uint16_t *>(tab + p + h * 512);
-                const int32_t d = (int32_t)(__umul24(q, cdf) + ncode);
-                p |= (uint32_t)(d >> 31) & ((uint32_t)h * 512u);
+                for (int u = 0; u < kUnrolledSteps; ++u)
+                    put_out<SYMBOLS>(ors, olane, orow_held + u * ostride, y[u]);
             }
-            const uint32_t cdf_s = *reinterpret_cast<const uint16_t *>(tab + p);
-            const uint32_t f_s = *reinterpret_cast<const uint16_t *>(tab + p + 2);
-            ncode = __umul24(q, cdf_s) + ncode;
-            range = __umul24(q, f_s);
-            if (present) {
-                if (SYMBOLS) {
-                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(p >> 9), ors, olane, orow, 0);
-                } else {
-                    const float dq = *reinterpret_cast<const float *>(tab + p + 4);
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f2h(af + dq), ors, olane, orow, 0);
-                }
+            held = false;
+        }
+        if (dec.present) put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? 0u : a16);
+        orow += ostride;
+        __builtin_amdgcn_sched_barrier(0);
+
+        const uint32_t nsteps = __builtin_amdgcn_readfirstlane(min(g.G, len - gi * g.G) - 1);
+        if (nsteps == (uint32_t)kUnrolledSteps) {
+#pragma unroll
+            for (int u = 0; u < kUnrolledSteps; ++u) {
+                float dq;
+                const uint32_t p = dec.symbol<LOGP>(tab, lb, dq);
+                y[u] = SYMBOLS ? (p >> 9) : f2h(af + dq);
+                dec.renorm(lane);
             }
-            orow += ostride;
-            if (++i < m) {
-                const bool need = present && (range < kRenormBelow);
-                const uint64_t mask = __ballot(need);
-                if (mask) {
-                    const uint32_t cnt = (uint32_t)__popcll(mask);
-                    if (cur + cnt > re) {
-                        // the group outran the prefetch: commit it now, load more if needed
-                        if (pending) {
-                            ring_put(ring, pf_at + 4 * lane, pf);
-                            re = pf_at + kFetchWords;
-                            pending = false;
-                        }
-                        while (cur + cnt > re) {
-                            ring_put(ring, re + 4 * lane,
-                                     __builtin_amdgcn_raw_buffer_load_b64(wrs, 2 * (re + 4 * lane), 0, 0));
-                            re += kFetchWords;
-                        }
-                    }
-                    if (need) {
-                        const uint16_t *rp = ring + (cur & (kRingWords - 1));
-                        ncode = (ncode << 16) | rp[mbcnt64(mask)];
-                        range <<= 16;
-                    }
-                    cur += cnt;
-                }
+            held = true;
+            orow_held = orow;
+            orow += kUnrolledSteps * ostride;
+        } else {
+            for (uint32_t u = nsteps; u != 0; --u) {
+                float dq;
+                const uint32_t p = dec.symbol<LOGP>(tab, lb, dq);
+                if (dec.present) put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? (p >> 9) : f2h(af + dq));
+                orow += ostride;
+                dec.renorm(lane);
             }
         }
+        // consume this group's requests; the ring chunk is dropped if a refill inside the
+        // group already loaded those words
+        // (the empty asm pins where the loaded values are first needed, so the wait for
+        // them is placed here and not after the next group's requests)
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t an = a_next, pv = pf;
+        asm volatile("" : "+v"(an), "+v"(pv));
+        a16 = an;
+        af = h2f(a16);
+        if (fetch && dec.re == pf_at) {
+            ring_put(ring, pf_at + 2 * lane, pv);
+            dec.re = pf_at + kFetchWords;
+        }
+    }
+    if (held && dec.present) {
+#pragma unroll
+        for (int u = 0; u < kUnrolledSteps; ++u)
+            put_out<SYMBOLS>(ors, olane, orow_held + u * ostride, y[u]);
     }
 }
 
