@@ -98,7 +98,7 @@ struct cg_tables {
     uint8_t *d_bins;
     float *d_lo, *d_w, *d_r;
     uint16_t *d_freqs;
-    uint2 *d_dtab;
+    uint32_t *d_dtab;
 };
 
 struct cg_blob {
@@ -231,14 +231,14 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     CG_HIP(w_d.alloc(rows * 4), "hipMalloc");
     CG_HIP(r_d.alloc(rows * 4), "hipMalloc");
     CG_HIP(fr_d.alloc(rows * kMaxBins * 2), "hipMalloc");
-    const uint64_t dtab_bytes = (uint64_t)t->L * 2 * t->NB * kMaxBins * kLanes * sizeof(uint2);
+    const uint64_t dtab_bytes = (uint64_t)t->L * 2 * t->NB * kTabBlock * sizeof(uint32_t);
     CG_HIP(dt_d.alloc(dtab_bytes), "hipMalloc");
     t->d_bins = bins_d.as<uint8_t>();
     t->d_lo = lo_d.as<float>();
     t->d_w = w_d.as<float>();
     t->d_r = r_d.as<float>();
     t->d_freqs = fr_d.as<uint16_t>();
-    t->d_dtab = dt_d.as<uint2>();
+    t->d_dtab = dt_d.as<uint32_t>();
     bins_d.detach();
     lo_d.detach();
     w_d.detach();

@@ -14,6 +14,10 @@ constexpr uint32_t kLanes = 64;                    // channels per group = wavef
 constexpr uint32_t kRenormBelow = 1u << 15;        // renormalise (one 16-bit word) below 2^15
 constexpr uint32_t kRangeInit = 0x7FFFFFFFu;       // 31-bit range
 constexpr uint32_t kPayloadPadBytes = 1024;        // zero bytes after the payload of a container
+// Decode table of one (row, 64-channel block): two planes [32 symbols][64 lanes] of
+// 32-bit words, {cdf | f << 16} then the dequantized delta lo + s * w (fp32 bits).
+constexpr uint32_t kTabPlane = kMaxBins * kLanes;
+constexpr uint32_t kTabBlock = 2 * kTabPlane;
 // dword 3 of a raw (untyped) buffer resource on gfx9-family GPUs: 32-bit data format
 constexpr int kBufferFlags = 0x00020000;
 
@@ -38,24 +42,24 @@ hipError_t launch_k0_finalize(const Geom &g, const uint8_t *bins, const uint32_t
 hipError_t launch_k1(const uint16_t *X, const Geom &g, const uint8_t *bins, uint32_t max_bins,
                      const float *lo, const float *r, uint32_t *counts, hipStream_t st);
 hipError_t launch_k1_freqs(const Geom &g, const uint8_t *bins, const uint32_t *counts,
-                           const float *lo, const float *w, uint16_t *freqs, uint2 *dtab,
+                           const float *lo, const float *w, uint16_t *freqs, uint32_t *dtab,
                            hipStream_t st);
 hipError_t launch_k2(const uint16_t *X, const Geom &g, const uint8_t *bins, const float *lo,
                      const float *r, uint32_t t_lo, uint32_t t_hi, uint32_t tpt, uint8_t *sym,
                      uint32_t sym_t0, uint32_t sym_T, uint16_t *anchors, hipStream_t st);
 hipError_t launch_k5_plan(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
-                          const uint2 *dtab, uint32_t *lane_words, uint64_t *group_words,
+                          const uint32_t *dtab, uint32_t *lane_words, uint64_t *group_words,
                           uint64_t n_groups, hipStream_t st);
 hipError_t launch_scan(const uint64_t *in, uint64_t *out, uint64_t n, hipStream_t st);
 hipError_t launch_k5_encode(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
-                            const uint2 *dtab, const uint32_t *lane_words,
+                            const uint32_t *dtab, const uint32_t *lane_words,
                             const uint64_t *group_off, uint16_t *scratch, uint64_t n_groups,
                             hipStream_t st);
 hipError_t launch_k5_interleave(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T,
-                                const Geom &g, const uint2 *dtab, const uint32_t *lane_words,
+                                const Geom &g, const uint32_t *dtab, const uint32_t *lane_words,
                                 const uint64_t *group_off, const uint16_t *scratch,
                                 uint16_t *payload, uint64_t n_groups, hipStream_t st);
-hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint2 *dtab,
+hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
                      const uint8_t *container, const ContainerView &cv, uint16_t *out,
                      uint8_t *sym_out, hipStream_t st);
 hipError_t launch_k4(const Geom &g, const float *lo, const float *w, const uint8_t *sym,

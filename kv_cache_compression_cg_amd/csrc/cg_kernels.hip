@@ -276,7 +276,7 @@ __global__ __launch_bounds__(256) void k1_freqs(Geom g, const uint8_t *__restric
                                                  const float *__restrict__ lo,
                                                  const float *__restrict__ w,
                                                  uint16_t *__restrict__ freqs,
-                                                 uint2 *__restrict__ dtab)
+                                                 uint32_t *__restrict__ dtab)
 {
     uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= g.L * 2 * g.C) return;
@@ -297,21 +297,22 @@ __global__ __launch_bounds__(256) void k1_freqs(Geom g, const uint8_t *__restric
     uint32_t P = 1;
     while (P < N) P <<= 1;
     float lo1 = lo[i], w1 = w[i];
-    uint2 *tb = dtab + ((uint64_t)(row * g.NB + c / kLanes) * kMaxBins) * kLanes + (c % kLanes);
+    uint32_t *tb = dtab + (uint64_t)(row * g.NB + c / kLanes) * kTabBlock + (c % kLanes);
     uint32_t cdf = 0;
     for (uint32_t s = 0; s < kMaxBins; ++s) {
         uint32_t fs = (s < N) ? f[s] : 0;
         freqs[(uint64_t)i * kMaxBins + s] = (uint16_t)fs;
-        uint2 e;
+        uint32_t cf, dq;
         if (s < N) {
-            e.x = cdf | (fs << 16);
-            e.y = __float_as_uint(fmaf((float)s, w1, lo1));
+            cf = cdf | (fs << 16);
+            dq = __float_as_uint(fmaf((float)s, w1, lo1));
         } else {
             // padding up to a power of two: cdf = T is never <= code for a valid stream
-            e.x = kProbTotal;
-            e.y = __float_as_uint(fmaf((float)(N - 1u), w1, lo1));
+            cf = kProbTotal;
+            dq = __float_as_uint(fmaf((float)(N - 1u), w1, lo1));
         }
-        tb[(uint64_t)s * kLanes] = e;
+        tb[(uint64_t)s * kLanes] = cf;
+        tb[kTabPlane + (uint64_t)s * kLanes] = dq;
         cdf += fs;
     }
 }
@@ -427,7 +428,7 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t mask)
 
 __global__ __launch_bounds__(256) void k5_plan(const uint8_t *__restrict__ sym, uint32_t sym_t0,
                                                 uint32_t sym_T, Geom g,
-                                                const uint2 *__restrict__ dtab,
+                                                const uint32_t *__restrict__ dtab,
                                                 uint32_t *__restrict__ lane_words,
                                                 uint64_t *__restrict__ group_words,
                                                 uint64_t n_groups)
@@ -439,14 +440,14 @@ __global__ __launch_bounds__(256) void k5_plan(const uint8_t *__restrict__ sym, 
     uint32_t words = 0;
     if (x.present && x.m > 0) {
         const uint8_t *sp = sym + (uint64_t)x.row * sym_T * g.C + x.c;
-        const uint2 *tab = dtab + ((uint64_t)(x.row * g.NB + x.b) * kMaxBins) * kLanes + lane;
+        const uint32_t *tab = dtab + (uint64_t)(x.row * g.NB + x.b) * kTabBlock + lane;
         uint32_t range = kRangeInit, ev = 0, i = 0;
         for (uint32_t gi = 0; gi < x.ng; ++gi) {
             uint32_t ulen = min(g.G, x.len - gi * g.G);
             for (uint32_t u = 1; u < ulen; ++u) {
                 uint32_t t = x.t0 + gi * g.G + u;
                 uint32_t s = sp[(uint64_t)(t - sym_t0) * g.C];
-                uint32_t f = tab[(uint64_t)s * kLanes].x >> 16;
+                uint32_t f = tab[(uint64_t)s * kLanes] >> 16;
                 range = (range >> kProbBits) * f;
                 ++i;
                 if (i < x.m && range < kRenormBelow) {
@@ -492,7 +493,7 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *__restrict__ in,
 
 __global__ __launch_bounds__(256) void k5_encode(const uint8_t *__restrict__ sym, uint32_t sym_t0,
                                                   uint32_t sym_T, Geom g,
-                                                  const uint2 *__restrict__ dtab,
+                                                  const uint32_t *__restrict__ dtab,
                                                   const uint32_t *__restrict__ lane_words,
                                                   const uint64_t *__restrict__ group_off,
                                                   uint16_t *__restrict__ scratch, uint64_t n_groups)
@@ -506,7 +507,7 @@ __global__ __launch_bounds__(256) void k5_encode(const uint8_t *__restrict__ sym
     if (!x.present || x.m == 0) return;
     uint16_t *out = scratch + group_off[gidx] + lane_off;
     const uint8_t *sp = sym + (uint64_t)x.row * sym_T * g.C + x.c;
-    const uint2 *tab = dtab + ((uint64_t)(x.row * g.NB + x.b) * kMaxBins) * kLanes + lane;
+    const uint32_t *tab = dtab + (uint64_t)(x.row * g.NB + x.b) * kTabBlock + lane;
     uint64_t low = 0;
     uint32_t range = kRangeInit, nw = 0, i = 0;
     for (uint32_t gi = 0; gi < x.ng; ++gi) {
@@ -514,7 +515,7 @@ __global__ __launch_bounds__(256) void k5_encode(const uint8_t *__restrict__ sym
         for (uint32_t u = 1; u < ulen; ++u) {
             uint32_t t = x.t0 + gi * g.G + u;
             uint32_t s = sp[(uint64_t)(t - sym_t0) * g.C];
-            uint32_t e = tab[(uint64_t)s * kLanes].x;
+            uint32_t e = tab[(uint64_t)s * kLanes];
             uint32_t q = range >> kProbBits;
             low += (uint64_t)q * (e & 0xFFFFu);
             range = q * (e >> 16);
@@ -542,7 +543,7 @@ __global__ __launch_bounds__(256) void k5_encode(const uint8_t *__restrict__ sym
 
 __global__ __launch_bounds__(256) void k5_interleave(const uint8_t *__restrict__ sym,
                                                       uint32_t sym_t0, uint32_t sym_T, Geom g,
-                                                      const uint2 *__restrict__ dtab,
+                                                      const uint32_t *__restrict__ dtab,
                                                       const uint32_t *__restrict__ lane_words,
                                                       const uint64_t *__restrict__ group_off,
                                                       const uint16_t *__restrict__ scratch,
@@ -564,7 +565,7 @@ __global__ __launch_bounds__(256) void k5_interleave(const uint8_t *__restrict__
     }
     uint32_t cursor = 2 * x.nl, e = 2, range = kRangeInit, i = 0;
     const uint8_t *sp = sym + (uint64_t)x.row * sym_T * g.C + (x.present ? x.c : 0);
-    const uint2 *tab = dtab + ((uint64_t)(x.row * g.NB + x.b) * kMaxBins) * kLanes + lane;
+    const uint32_t *tab = dtab + (uint64_t)(x.row * g.NB + x.b) * kTabBlock + lane;
     for (uint32_t gi = 0; gi < x.ng; ++gi) {
         uint32_t ulen = min(g.G, x.len - gi * g.G);
         for (uint32_t u = 1; u < ulen; ++u) {
@@ -573,7 +574,7 @@ __global__ __launch_bounds__(256) void k5_interleave(const uint8_t *__restrict__
             ++i;
             if (x.present) {
                 uint32_t s = sp[(uint64_t)(t - sym_t0) * g.C];
-                uint32_t f = tab[(uint64_t)s * kLanes].x >> 16;
+                uint32_t f = tab[(uint64_t)s * kLanes] >> 16;
                 range = (range >> kProbBits) * f;
                 need = (i < x.m) && (range < kRenormBelow);
             }
@@ -624,6 +625,12 @@ __device__ __forceinline__ void ring_put(uint16_t *ring, uint32_t pos, uint32_t 
 //   q*cdf <= code  <=>  (int)(q*cdf + ncode) < 0    (all values < 2^31)
 //   ~(code - q*cdf) = q*cdf + ncode.
 // Renormalisation shifts in inverted words, which is why the ring holds ~word.
+// The LDS table holds, per symbol s and lane, {cdf | f << 16} at byte 256*s + 4*lane
+// and the dequantized delta 8 KiB further: a lane's probe never conflicts with
+// another lane's, whatever symbols the lanes are at.
+constexpr uint32_t kSymStride = kLanes * 4;              // bytes between symbols
+constexpr uint32_t kDqOffset = kTabPlane * 4;            // byte offset of the delta plane
+
 struct WaveDecoder {
     uint32_t ncode, range;
     uint32_t cur, re;  // next unread word; words [re - R, re) are in the ring
@@ -632,7 +639,7 @@ struct WaveDecoder {
     __amdgpu_buffer_rsrc_t wrs;
     bool present;
 
-    // Table entry of the decoded symbol (byte offset into the LDS table).
+    // Decodes one symbol; returns the byte offset of its table entry.
     template <int LOGP>
     __device__ __forceinline__ uint32_t symbol(const uint8_t *tab, uint32_t lb, float &dq)
     {
@@ -640,15 +647,14 @@ struct WaveDecoder {
         uint32_t p = lb;
 #pragma unroll
         for (int h = (1 << LOGP) >> 1; h >= 1; h >>= 1) {
-            const uint32_t cdf = *reinterpret_cast<const uint16_t *>(tab + p + h * 512);
+            const uint32_t cdf = *reinterpret_cast<const uint16_t *>(tab + p + h * kSymStride);
             const int32_t d = (int32_t)(__umul24(q, cdf) + ncode);
-            p |= (uint32_t)(d >> 31) & ((uint32_t)h * 512u);
+            p |= (uint32_t)(d >> 31) & ((uint32_t)h * kSymStride);
         }
-        const uint32_t cdf_s = *reinterpret_cast<const uint16_t *>(tab + p);
-        const uint32_t f_s = *reinterpret_cast<const uint16_t *>(tab + p + 2);
-        dq = *reinterpret_cast<const float *>(tab + p + 4);
-        ncode = __umul24(q, cdf_s) + ncode;
-        range = __umul24(q, f_s);
+        const uint32_t e = *reinterpret_cast<const uint32_t *>(tab + p);
+        dq = *reinterpret_cast<const float *>(tab + p + kDqOffset);
+        ncode = __umul24(q, e & 0xFFFFu) + ncode;
+        range = __umul24(q, e >> 16);
         return p;
     }
 
@@ -661,24 +667,26 @@ struct WaveDecoder {
         }
     }
 
+    // Renormalisation after a symbol that is not the chunk's last.
     __device__ __forceinline__ void renorm(uint32_t lane)
     {
-        if (++i < m) {
-            const bool need = present && (range < kRenormBelow);
-            const uint64_t mask = __ballot(need);
-            if (mask) {
-                const uint32_t cnt = (uint32_t)__popcll(mask);
-                if (cur + cnt > re) refill_now(cnt, lane);
-                if (need) {
-                    const uint16_t *rp = ring + (cur & (kRingWords - 1));
-                    ncode = (ncode << 16) | rp[mbcnt64(mask)];
-                    range <<= 16;
-                }
-                cur += cnt;
+        const bool need = present && (range < kRenormBelow);
+        const uint64_t mask = __ballot(need);
+        if (mask) {
+            const uint32_t cnt = (uint32_t)__popcll(mask);
+            if (cur + cnt > re) refill_now(cnt, lane);
+            if (need) {
+                const uint16_t *rp = ring + (cur & (kRingWords - 1));
+                ncode = (ncode << 16) | rp[mbcnt64(mask)];
+                range <<= 16;
             }
+            cur += cnt;
         }
     }
 };
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 template <bool SYMBOLS>
 __device__ __forceinline__ void put_out(const __amdgpu_buffer_rsrc_t &ors, uint32_t olane,
@@ -690,11 +698,34 @@ __device__ __forceinline__ void put_out(const __amdgpu_buffer_rsrc_t &ors, uint3
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, ors, olane, orow, 0);
 }
 
+// Writes the rows held for one unrolled group: fp16 values are converted two rows per
+// instruction (round to nearest even), symbols are stored as they are.
+template <bool SYMBOLS>
+__device__ __forceinline__ void flush_rows(const __amdgpu_buffer_rsrc_t &ors, uint32_t olane,
+                                           uint32_t orow, uint32_t ostride, const float *yf,
+                                           const uint32_t *ys)
+{
+#pragma unroll
+    for (int u = 0; u < kUnrolledSteps; u += 2) {
+        if (SYMBOLS) {
+            put_out<true>(ors, olane, orow + u * ostride, ys[u]);
+            if (u + 1 < kUnrolledSteps) put_out<true>(ors, olane, orow + (u + 1) * ostride, ys[u + 1]);
+        } else if (u + 1 < kUnrolledSteps) {
+            const f32x2 v = {yf[u], yf[u + 1]};
+            const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+            put_out<false>(ors, olane, orow + u * ostride, h & 0xFFFFu);
+            put_out<false>(ors, olane, orow + (u + 1) * ostride, h >> 16);
+        } else {
+            put_out<false>(ors, olane, orow + u * ostride, f2h(yf[u]));
+        }
+    }
+}
+
 // One wavefront decodes one group (chunk k, row, channel block b).  Vector memory is
-// only touched at anchor boundaries: there the next ring chunk and the next anchor row
-// are requested, then the previous group's outputs (held in registers) are written.
-// Waiting for the requested data at the following boundary therefore only waits for
-// operations issued a whole group earlier.
+// only touched at anchor boundaries: at a group's start the next anchor row and the
+// next chunk of words are requested and the previous group's outputs (held in
+// registers) are written; the requested data is consumed at the group's end.  Waits for
+// it therefore never wait for a store issued during the group.
 template <int LOGP, bool SYMBOLS, bool FULL>
 __device__ __forceinline__ void decode_wave(const Geom &g, const uint8_t *__restrict__ tab,
                                             uint16_t *__restrict__ ring,
@@ -732,7 +763,7 @@ __device__ __forceinline__ void decode_wave(const Geom &g, const uint8_t *__rest
         SYMBOLS ? make_rsrc(sym_out + obase, 0xFFFFFFFFu) : make_rsrc(out + obase, 0xFFFFFFFFu);
     const uint32_t ostride = g.C * (SYMBOLS ? 1u : 2u);  // bytes between token rows
     const uint32_t olane = lane * (SYMBOLS ? 1u : 2u);
-    const uint32_t lb = lane * 8;                         // entry (symbol 0, this lane)
+    const uint32_t lb = lane * 4;                         // entry (symbol 0, this lane)
 
     dec.ncode = 0xFFFFFFFFu;
     dec.range = kRangeInit;
@@ -747,8 +778,9 @@ __device__ __forceinline__ void decode_wave(const Geom &g, const uint8_t *__rest
     uint32_t a16 = __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, 0, 0);
     asm volatile("" : "+v"(a16));
     float af = h2f(a16);
-    uint32_t y[kUnrolledSteps];
-    bool held = false;          // y holds the outputs of the previous group
+    float yf[kUnrolledSteps];
+    uint32_t ys[kUnrolledSteps];
+    bool held = false;          // yf / ys hold the outputs of the previous group
     uint32_t orow_held = 0;     // byte offset of its first decoded row
     uint32_t orow = 0;          // byte offset of the current anchor row
     for (uint32_t gi = 0; gi < ng; ++gi) {
@@ -761,11 +793,7 @@ __device__ __forceinline__ void decode_wave(const Geom &g, const uint8_t *__rest
         const uint32_t pf = __builtin_amdgcn_raw_buffer_load_b32(dec.wrs, 2 * (pf_at + 2 * lane), 0, 0);
         // writes: the previous group's outputs, then this anchor row
         if (held) {
-            if (dec.present) {
-#pragma unroll
-                for (int u = 0; u < kUnrolledSteps; ++u)
-                    put_out<SYMBOLS>(ors, olane, orow_held + u * ostride, y[u]);
-            }
+            if (dec.present) flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
             held = false;
         }
         if (dec.present) put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? 0u : a16);
@@ -773,14 +801,19 @@ __device__ __forceinline__ void decode_wave(const Geom &g, const uint8_t *__rest
         __builtin_amdgcn_sched_barrier(0);
 
         const uint32_t nsteps = __builtin_amdgcn_readfirstlane(min(g.G, len - gi * g.G) - 1);
-        if (nsteps == (uint32_t)kUnrolledSteps) {
+        if (nsteps == (uint32_t)kUnrolledSteps && dec.i + kUnrolledSteps < dec.m) {
+            // a full group that does not hold the chunk's last symbol
 #pragma unroll
             for (int u = 0; u < kUnrolledSteps; ++u) {
                 float dq;
                 const uint32_t p = dec.symbol<LOGP>(tab, lb, dq);
-                y[u] = SYMBOLS ? (p >> 9) : f2h(af + dq);
+                if (SYMBOLS)
+                    ys[u] = p / kSymStride;
+                else
+                    yf[u] = af + dq;
                 dec.renorm(lane);
             }
+            dec.i += kUnrolledSteps;
             held = true;
             orow_held = orow;
             orow += kUnrolledSteps * ostride;
@@ -788,15 +821,14 @@ __device__ __forceinline__ void decode_wave(const Geom &g, const uint8_t *__rest
             for (uint32_t u = nsteps; u != 0; --u) {
                 float dq;
                 const uint32_t p = dec.symbol<LOGP>(tab, lb, dq);
-                if (dec.present) put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? (p >> 9) : f2h(af + dq));
+                if (dec.present) put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? p / kSymStride : f2h(af + dq));
                 orow += ostride;
-                dec.renorm(lane);
+                if (++dec.i < dec.m) dec.renorm(lane);
             }
         }
         // consume this group's requests; the ring chunk is dropped if a refill inside the
-        // group already loaded those words
-        // (the empty asm pins where the loaded values are first needed, so the wait for
-        // them is placed here and not after the next group's requests)
+        // group already loaded those words.  (The empty asm pins where the loaded values
+        // are first needed, so the wait for them is placed here.)
         __builtin_amdgcn_sched_barrier(0);
         uint32_t an = a_next, pv = pf;
         asm volatile("" : "+v"(an), "+v"(pv));
@@ -807,11 +839,7 @@ __device__ __forceinline__ void decode_wave(const Geom &g, const uint8_t *__rest
             dec.re = pf_at + kFetchWords;
         }
     }
-    if (held && dec.present) {
-#pragma unroll
-        for (int u = 0; u < kUnrolledSteps; ++u)
-            put_out<SYMBOLS>(ors, olane, orow_held + u * ostride, y[u]);
-    }
+    if (held && dec.present) flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
 }
 
 template <bool SYMBOLS, bool FULL>
@@ -832,13 +860,13 @@ __device__ __forceinline__ void decode_dispatch(uint32_t logp, const Geom &g, co
 
 template <bool SYMBOLS>
 __global__ __launch_bounds__(256) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
-                                                  const uint2 *__restrict__ dtab,
+                                                  const uint32_t *__restrict__ dtab,
                                                   const uint8_t *__restrict__ container,
                                                   ContainerView cv, uint32_t n_sets,
                                                   uint16_t *__restrict__ out,
                                                   uint8_t *__restrict__ sym_out)
 {
-    __shared__ uint2 tab[kMaxBins * kLanes];
+    __shared__ uint32_t tab[kTabBlock];
     __shared__ uint16_t rings[kWavesPerBlock * kRingAlloc];
     const uint32_t set = blockIdx.x % n_sets;
     const uint32_t tmp = blockIdx.x / n_sets;
@@ -847,10 +875,14 @@ __global__ __launch_bounds__(256) void k3_decode(Geom g, const uint8_t *__restri
     const uint32_t N = bins[row >> 1];
     uint32_t logp = 0;
     while ((1u << logp) < N) ++logp;
-    const uint32_t n16 = ((1u << logp) * kLanes) / 2;  // 16-byte pieces of the table
-    const uint4 *src = reinterpret_cast<const uint4 *>(dtab + (uint64_t)(row * g.NB + b) * kMaxBins * kLanes);
+    // stage the P = 2^logp used entries of both planes
+    const uint32_t n16 = ((1u << logp) * kLanes) / 4;  // 16-byte pieces per plane
+    const uint4 *src = reinterpret_cast<const uint4 *>(dtab + (uint64_t)(row * g.NB + b) * kTabBlock);
     uint4 *dst = reinterpret_cast<uint4 *>(tab);
-    for (uint32_t j = threadIdx.x; j < n16; j += blockDim.x) dst[j] = src[j];
+    for (uint32_t j = threadIdx.x; j < n16; j += blockDim.x) {
+        dst[j] = src[j];
+        dst[kTabPlane / 4 + j] = src[kTabPlane / 4 + j];
+    }
     __syncthreads();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     const uint32_t lane = threadIdx.x % kLanes;
@@ -959,7 +991,7 @@ hipError_t launch_k1(const uint16_t *X, const Geom &g, const uint8_t *bins, uint
 }
 
 hipError_t launch_k1_freqs(const Geom &g, const uint8_t *bins, const uint32_t *counts,
-                           const float *lo, const float *w, uint16_t *freqs, uint2 *dtab,
+                           const float *lo, const float *w, uint16_t *freqs, uint32_t *dtab,
                            hipStream_t st)
 {
     uint32_t n = g.L * 2 * g.C;
@@ -980,7 +1012,7 @@ hipError_t launch_k2(const uint16_t *X, const Geom &g, const uint8_t *bins, cons
 }
 
 hipError_t launch_k5_plan(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
-                          const uint2 *dtab, uint32_t *lane_words, uint64_t *group_words,
+                          const uint32_t *dtab, uint32_t *lane_words, uint64_t *group_words,
                           uint64_t n_groups, hipStream_t st)
 {
     uint64_t blocks = (n_groups + 3) / 4;
@@ -996,7 +1028,7 @@ hipError_t launch_scan(const uint64_t *in, uint64_t *out, uint64_t n, hipStream_
 }
 
 hipError_t launch_k5_encode(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
-                            const uint2 *dtab, const uint32_t *lane_words,
+                            const uint32_t *dtab, const uint32_t *lane_words,
                             const uint64_t *group_off, uint16_t *scratch, uint64_t n_groups,
                             hipStream_t st)
 {
@@ -1007,7 +1039,7 @@ hipError_t launch_k5_encode(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T,
 }
 
 hipError_t launch_k5_interleave(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T,
-                                const Geom &g, const uint2 *dtab, const uint32_t *lane_words,
+                                const Geom &g, const uint32_t *dtab, const uint32_t *lane_words,
                                 const uint64_t *group_off, const uint16_t *scratch,
                                 uint16_t *payload, uint64_t n_groups, hipStream_t st)
 {
@@ -1017,7 +1049,7 @@ hipError_t launch_k5_interleave(const uint8_t *sym, uint32_t sym_t0, uint32_t sy
     return hipGetLastError();
 }
 
-hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint2 *dtab,
+hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
                      const uint8_t *container, const ContainerView &cv, uint16_t *out,
                      uint8_t *sym_out, hipStream_t st)
 {
