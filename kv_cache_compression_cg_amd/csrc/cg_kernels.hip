@@ -670,18 +670,18 @@ struct WaveDecoder {
     // Renormalisation after a symbol that is not the chunk's last.
     __device__ __forceinline__ void renorm(uint32_t lane)
     {
+        // (the ballot takes the comparison itself, so the lane mask is not materialised
+        // in a vector register; with no lane renormalising the body does nothing)
         const bool need = present && (range < kRenormBelow);
-        const uint64_t mask = __ballot(need);
-        if (mask) {
-            const uint32_t cnt = (uint32_t)__popcll(mask);
-            if (cur + cnt > re) refill_now(cnt, lane);
-            if (need) {
-                const uint16_t *rp = ring + (cur & (kRingWords - 1));
-                ncode = (ncode << 16) | rp[mbcnt64(mask)];
-                range <<= 16;
-            }
-            cur += cnt;
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(need);
+        const uint32_t cnt = (uint32_t)__builtin_popcountll(mask);
+        if (__builtin_expect(cur + cnt > re, 0)) refill_now(cnt, lane);
+        if (need) {
+            const uint16_t *rp = ring + (cur & (kRingWords - 1));
+            ncode = (ncode << 16) | rp[mbcnt64(mask)];
+            range <<= 16;
         }
+        cur += cnt;
     }
 };
 
