@@ -15,7 +15,7 @@ constexpr uint32_t kRenormBelow = 1u << 15;        // renormalise (one 16-bit wo
 constexpr uint32_t kRangeInit = 0x7FFFFFFFu;       // 31-bit range
 constexpr uint32_t kPayloadPadBytes = 1024;        // zero bytes after the payload of a container
 // Decode table of one (row, 64-channel block): two planes [32 symbols][64 lanes] of
-// 32-bit words, {cdf | f << 16} then the dequantized delta lo + s * w (fp32 bits).
+// 32-bit words, {f | cdf << 16} then the dequantized delta lo + s * w (fp32 bits).
 constexpr uint32_t kTabPlane = kMaxBins * kLanes;
 constexpr uint32_t kTabBlock = 2 * kTabPlane;
 // dword 3 of a raw (untyped) buffer resource on gfx9-family GPUs: 32-bit data format

@@ -7,10 +7,10 @@
 //     all lanes step through the same token at the same time, so every output row
 //     is written as one contiguous 128-byte store and the interleaved words of the
 //     group are read from a contiguous, advancing window.
-//   * Decode table entry (8 bytes) of symbol s for a lane: {cdf[s] | f[s] << 16,
-//     dequantized delta lo + s * w as fp32 bits}, stored [row][block][32][64 lanes]
-//     so that all 64 lanes reading entry s of their own channel hit 64 different
-//     LDS banks whatever s each lane holds.
+//   * Decode table entry (8 bytes) of symbol s for a lane: {f[s] | cdf[s] << 16,
+//     dequantized delta lo + s * w as fp32 bits}, two planes [32][64 lanes] per
+//     (row, block), so that all 64 lanes reading entry s of their own channel hit
+//     64 different LDS banks whatever s each lane holds.
 //
 // Float rules (bit-exact with the CPU oracle): -ffp-contract=off, fp32 division and
 // reciprocal correctly rounded (HIP default), fmaf only where written, fp16 output
@@ -304,11 +304,11 @@ __global__ __launch_bounds__(256) void k1_freqs(Geom g, const uint8_t *__restric
         freqs[(uint64_t)i * kMaxBins + s] = (uint16_t)fs;
         uint32_t cf, dq;
         if (s < N) {
-            cf = cdf | (fs << 16);
+            cf = fs | (cdf << 16);
             dq = __float_as_uint(fmaf((float)s, w1, lo1));
         } else {
             // padding up to a power of two: cdf = T is never <= code for a valid stream
-            cf = kProbTotal;
+            cf = kProbTotal << 16;
             dq = __float_as_uint(fmaf((float)(N - 1u), w1, lo1));
         }
         tb[(uint64_t)s * kLanes] = cf;
@@ -447,7 +447,7 @@ __global__ __launch_bounds__(256) void k5_plan(const uint8_t *__restrict__ sym, 
             for (uint32_t u = 1; u < ulen; ++u) {
                 uint32_t t = x.t0 + gi * g.G + u;
                 uint32_t s = sp[(uint64_t)(t - sym_t0) * g.C];
-                uint32_t f = tab[(uint64_t)s * kLanes] >> 16;
+                uint32_t f = tab[(uint64_t)s * kLanes] & 0xFFFFu;
                 range = (range >> kProbBits) * f;
                 ++i;
                 if (i < x.m && range < kRenormBelow) {
@@ -517,8 +517,8 @@ __global__ __launch_bounds__(256) void k5_encode(const uint8_t *__restrict__ sym
             uint32_t s = sp[(uint64_t)(t - sym_t0) * g.C];
             uint32_t e = tab[(uint64_t)s * kLanes];
             uint32_t q = range >> kProbBits;
-            low += (uint64_t)q * (e & 0xFFFFu);
-            range = q * (e >> 16);
+            low += (uint64_t)q * (e >> 16);
+            range = q * (e & 0xFFFFu);
             if (low >> 32) {  // carry into the words already written
                 low &= 0xFFFFFFFFull;
                 uint32_t j = nw;
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(256) void k5_interleave(const uint8_t *__restrict__
             ++i;
             if (x.present) {
                 uint32_t s = sp[(uint64_t)(t - sym_t0) * g.C];
-                uint32_t f = tab[(uint64_t)s * kLanes] >> 16;
+                uint32_t f = tab[(uint64_t)s * kLanes] & 0xFFFFu;
                 range = (range >> kProbBits) * f;
                 need = (i < x.m) && (range < kRenormBelow);
             }
@@ -608,6 +608,7 @@ constexpr uint32_t kRingWords = 256;
 constexpr uint32_t kRingAlloc = kRingWords + 64;
 constexpr uint32_t kFetchWords = 128;
 constexpr uint32_t kWavesPerBlock = 4;
+constexpr uint32_t kStreamsPerWave = 2;   // chunks one wavefront decodes in lockstep
 // Groups of this many decode steps (anchor interval 10) run fully unrolled with their
 // outputs held in registers; any other group length takes the generic loop.
 constexpr int kUnrolledSteps = 9;
@@ -625,11 +626,26 @@ __device__ __forceinline__ void ring_put(uint16_t *ring, uint32_t pos, uint32_t 
 //   q*cdf <= code  <=>  (int)(q*cdf + ncode) < 0    (all values < 2^31)
 //   ~(code - q*cdf) = q*cdf + ncode.
 // Renormalisation shifts in inverted words, which is why the ring holds ~word.
-// The LDS table holds, per symbol s and lane, {cdf | f << 16} at byte 256*s + 4*lane
-// and the dequantized delta 8 KiB further: a lane's probe never conflicts with
+// The LDS table holds, per symbol s and lane, {f | cdf << 16} at byte 256*s + 4*lane
+// (cdf in the upper half, read zero-extended by the search) and the dequantized delta
+// 8 KiB further: a lane's probe never conflicts with
 // another lane's, whatever symbols the lanes are at.
 constexpr uint32_t kSymStride = kLanes * 4;              // bytes between symbols
 constexpr uint32_t kDqOffset = kTabPlane * 4;            // byte offset of the delta plane
+
+// p + (d < 0 ? STEP : 0) for a power-of-two STEP, as a shift and a shift-add.  (Written
+// out because the compiler otherwise folds the last level into an and + add pair.)
+template <uint32_t STEP>
+__device__ __forceinline__ uint32_t take_upper(uint32_t d, uint32_t p)
+{
+    static_assert((STEP & (STEP - 1)) == 0 && STEP >= 4 && STEP <= (1u << 15), "step");
+    constexpr uint32_t kShift = __builtin_ctz(STEP);
+    uint32_t r;
+    asm("v_lshrrev_b32 %0, 31, %1\n\tv_lshl_add_u32 %0, %0, %2, %3"
+        : "=&v"(r)
+        : "v"(d), "n"(kShift), "v"(p));
+    return r;
+}
 
 struct WaveDecoder {
     uint32_t ncode, range;
@@ -639,22 +655,36 @@ struct WaveDecoder {
     __amdgpu_buffer_rsrc_t wrs;
     bool present;
 
-    // Decodes one symbol; returns the byte offset of its table entry.
-    template <int LOGP>
-    __device__ __forceinline__ uint32_t symbol(const uint8_t *tab, uint32_t lb, float &dq)
+    // Binary search over the lane's cdf column, levels LEVEL .. 0: the largest symbol
+    // s with q*cdf[s] <= code, as the byte offset of its entry.
+    template <int LEVEL>
+    __device__ __forceinline__ uint32_t search(const uint8_t *tab, uint32_t p, uint32_t q) const
     {
-        const uint32_t q = range >> kProbBits;
-        uint32_t p = lb;
-#pragma unroll
-        for (int h = (1 << LOGP) >> 1; h >= 1; h >>= 1) {
-            const uint32_t cdf = *reinterpret_cast<const uint16_t *>(tab + p + h * kSymStride);
-            const int32_t d = (int32_t)(__umul24(q, cdf) + ncode);
-            p |= (uint32_t)(d >> 31) & ((uint32_t)h * kSymStride);
+        if constexpr (LEVEL < 0) {
+            return p;
+        } else {
+            constexpr uint32_t kStep = (1u << LEVEL) * kSymStride;
+            const uint32_t cdf = *reinterpret_cast<const uint16_t *>(tab + p + kStep + 2);
+            return search<LEVEL - 1>(tab, take_upper<kStep>(__umul24(q, cdf) + ncode, p), q);
         }
+    }
+
+    // Decodes one symbol; returns the byte offset of its table entry.  ctop is the
+    // lane's cdf at the first probe (symbol P/2), the same for every step.
+    template <int LOGP>
+    __device__ __forceinline__ uint32_t symbol(const uint8_t *tab, uint32_t lb, uint32_t ctop,
+                                               float &dq)
+    {
+        constexpr uint32_t kTop = (1u << (LOGP - 1)) * kSymStride;
+        const uint32_t q = range >> kProbBits;
+        const uint32_t p = search<LOGP - 2>(tab, take_upper<kTop>(__umul24(q, ctop) + ncode, lb), q);
+        // cdf as a zero-extending 16-bit read of the upper half, f from the low half of
+        // the whole entry (a word-select operand of the multiply): no masking needed
+        const uint32_t cdf = *reinterpret_cast<const uint16_t *>(tab + p + 2);
         const uint32_t e = *reinterpret_cast<const uint32_t *>(tab + p);
         dq = *reinterpret_cast<const float *>(tab + p + kDqOffset);
-        ncode = __umul24(q, e & 0xFFFFu) + ncode;
-        range = __umul24(q, e >> 16);
+        ncode = __umul24(q, cdf) + ncode;
+        range = __umul24(q, e & 0xFFFFu);
         return p;
     }
 
@@ -721,143 +751,294 @@ __device__ __forceinline__ void flush_rows(const __amdgpu_buffer_rsrc_t &ors, ui
     }
 }
 
-// One wavefront decodes one group (chunk k, row, channel block b).  Vector memory is
-// only touched at anchor boundaries: at a group's start the next anchor row and the
-// next chunk of words are requested and the previous group's outputs (held in
-// registers) are written; the requested data is consumed at the group's end.  Waits for
-// it therefore never wait for a store issued during the group.
-template <int LOGP, bool SYMBOLS, bool FULL>
-__device__ __forceinline__ void decode_wave(const Geom &g, const uint8_t *__restrict__ tab,
-                                            uint16_t *__restrict__ ring,
-                                            const uint8_t *__restrict__ container,
-                                            const ContainerView &cv, uint32_t k, uint32_t row,
-                                            uint32_t b, uint32_t lane, uint16_t *__restrict__ out,
-                                            uint8_t *__restrict__ sym_out)
-{
-    const uint32_t nl = min(kLanes, g.C - b * kLanes);
-    const uint32_t t0 = k * g.Tc, len = chunk_len(g, k);
-    const uint32_t ng = (len + g.G - 1) / g.G;
-
+// One decoder stream: chunk k of (row, channel block b), one channel per lane, with its
+// anchor rows, output rows and payload words.  Vector memory is only touched at anchor
+// boundaries: at a group's start the next anchor row and the next chunk of words are
+// requested and the previous group's outputs (held in registers) are written; the
+// requested data is consumed at the group's end.  Waits for it therefore never wait for
+// a store issued during the group.
+template <bool SYMBOLS>
+struct Stream {
     WaveDecoder dec;
-    dec.present = FULL || lane < nl;
-    dec.m = len - ng;
-    dec.i = 0;
-    dec.ring = ring;
-    const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
-    const uint64_t *offs = reinterpret_cast<const uint64_t *>(container + cv.offsets_off);
-    const uint64_t end = min(offs[gidx + 1], cv.payload_words);
-    const uint64_t beg = min(offs[gidx], end);
-    // words from the group's first word to the end of the zero-padded payload; the
-    // hardware range check returns 0 for anything past it
-    const uint64_t avail = 2 * (cv.payload_words - beg) + kPayloadPadBytes;
-    dec.wrs = make_rsrc(container + cv.payload_off + 2 * beg, (uint32_t)min(avail, (uint64_t)0xFFFFFFFFu));
-    // anchor rows of this group: row gi at byte 2 * (gi * C + lane); reads beyond the
-    // anchors section return 0
-    const uint64_t aoff = anchor_row(g, k, row, 0) * g.C + b * kLanes;
-    const __amdgpu_buffer_rsrc_t ars =
-        make_rsrc(container + cv.anchors_off + 2 * aoff,
-                  (uint32_t)min(cv.anchors_bytes - min(2 * aoff, cv.anchors_bytes), (uint64_t)0xFFFFFFFFu));
-    const uint32_t astride = 2 * g.C;
-    const uint64_t obase = ((uint64_t)row * g.S + t0) * g.C + b * kLanes;
-    const __amdgpu_buffer_rsrc_t ors =
-        SYMBOLS ? make_rsrc(sym_out + obase, 0xFFFFFFFFu) : make_rsrc(out + obase, 0xFFFFFFFFu);
-    const uint32_t ostride = g.C * (SYMBOLS ? 1u : 2u);  // bytes between token rows
-    const uint32_t olane = lane * (SYMBOLS ? 1u : 2u);
-    const uint32_t lb = lane * 4;                         // entry (symbol 0, this lane)
-
-    dec.ncode = 0xFFFFFFFFu;
-    dec.range = kRangeInit;
-    dec.re = 0;
-    if (dec.m > 0) {
-        dec.cur = 0;
-        dec.refill_now(kRingWords, lane);
-        if (dec.present) dec.ncode = ((uint32_t)ring[2 * lane] << 16) | ring[2 * lane + 1];
-    }
-    dec.cur = 2 * nl;
-
-    uint32_t a16 = __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, 0, 0);
-    asm volatile("" : "+v"(a16));
-    float af = h2f(a16);
+    __amdgpu_buffer_rsrc_t ars, ors;
+    uint32_t ng, len;           // groups / tokens in the chunk
+    uint32_t astride, ostride, olane;
+    uint32_t a16;               // anchor row of the current group (fp16 bits)
+    float af;
+    uint32_t orow;              // byte offset of the current anchor row
+    uint32_t orow_held;         // byte offset of the first row held in yf / ys
+    bool held;                  // yf / ys hold the outputs of the previous group
+    uint32_t a_next, pf, pf_at; // requests of the current group
+    bool fetch;
     float yf[kUnrolledSteps];
     uint32_t ys[kUnrolledSteps];
-    bool held = false;          // yf / ys hold the outputs of the previous group
-    uint32_t orow_held = 0;     // byte offset of its first decoded row
-    uint32_t orow = 0;          // byte offset of the current anchor row
-    for (uint32_t gi = 0; gi < ng; ++gi) {
-        // requests, consumed at the end of this group: the next anchor row and the next
-        // chunk of words (kept only if the ring has room for it)
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t a_next = __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, (gi + 1) * astride, 0);
-        const bool fetch = dec.m > 0 && dec.re + kFetchWords - dec.cur <= kRingWords;
-        const uint32_t pf_at = dec.re;
-        const uint32_t pf = __builtin_amdgcn_raw_buffer_load_b32(dec.wrs, 2 * (pf_at + 2 * lane), 0, 0);
-        // writes: the previous group's outputs, then this anchor row
+
+    __device__ __forceinline__ void init(const Geom &g, uint16_t *ring,
+                                         const uint8_t *__restrict__ container,
+                                         const ContainerView &cv, uint32_t k, uint32_t row,
+                                         uint32_t b, uint32_t lane, bool present,
+                                         uint16_t *__restrict__ out, uint8_t *__restrict__ sym_out)
+    {
+        const uint32_t nl = min(kLanes, g.C - b * kLanes);
+        const uint32_t t0 = k * g.Tc;
+        len = chunk_len(g, k);
+        ng = (len + g.G - 1) / g.G;
+        dec.present = present;
+        dec.m = len - ng;
+        dec.i = 0;
+        dec.ring = ring;
+        const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
+        const uint64_t *offs = reinterpret_cast<const uint64_t *>(container + cv.offsets_off);
+        const uint64_t end = min(offs[gidx + 1], cv.payload_words);
+        const uint64_t beg = min(offs[gidx], end);
+        // words from the group's first word to the end of the zero-padded payload; the
+        // hardware range check returns 0 for anything past it
+        const uint64_t avail = 2 * (cv.payload_words - beg) + kPayloadPadBytes;
+        dec.wrs = make_rsrc(container + cv.payload_off + 2 * beg,
+                            (uint32_t)min(avail, (uint64_t)0xFFFFFFFFu));
+        // anchor rows of this chunk: row gi at byte 2 * (gi * C + lane); reads beyond the
+        // anchors section return 0
+        const uint64_t aoff = anchor_row(g, k, row, 0) * g.C + b * kLanes;
+        ars = make_rsrc(container + cv.anchors_off + 2 * aoff,
+                        (uint32_t)min(cv.anchors_bytes - min(2 * aoff, cv.anchors_bytes),
+                                      (uint64_t)0xFFFFFFFFu));
+        astride = 2 * g.C;
+        const uint64_t obase = ((uint64_t)row * g.S + t0) * g.C + b * kLanes;
+        ors = SYMBOLS ? make_rsrc(sym_out + obase, 0xFFFFFFFFu) : make_rsrc(out + obase, 0xFFFFFFFFu);
+        ostride = g.C * (SYMBOLS ? 1u : 2u);  // bytes between token rows
+        olane = lane * (SYMBOLS ? 1u : 2u);
+
+        dec.ncode = 0xFFFFFFFFu;
+        dec.range = kRangeInit;
+        dec.re = 0;
+        if (dec.m > 0) {
+            dec.cur = 0;
+            dec.refill_now(kRingWords, lane);
+            if (present) dec.ncode = ((uint32_t)ring[2 * lane] << 16) | ring[2 * lane + 1];
+        }
+        dec.cur = 2 * nl;
+        held = false;
+        orow = 0;
+        orow_held = 0;
+    }
+
+    // first anchor row; the empty asm pins the wait for it here
+    __device__ __forceinline__ void first_anchor(uint32_t lane)
+    {
+        uint32_t v = __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, 0, 0);
+        asm volatile("" : "+v"(v));
+        a16 = v;
+        af = h2f(a16);
+    }
+
+    // decode steps in group gi (tokens less the anchor), wave-uniform
+    __device__ __forceinline__ uint32_t steps(const Geom &g, uint32_t gi) const
+    {
+        return __builtin_amdgcn_readfirstlane(min(g.G, len - gi * g.G) - 1);
+    }
+
+    // a full group that does not hold the chunk's last symbol
+    __device__ __forceinline__ bool unrollable(uint32_t nsteps) const
+    {
+        return nsteps == (uint32_t)kUnrolledSteps && dec.i + kUnrolledSteps < dec.m;
+    }
+
+    // the next anchor row and the next chunk of words (kept only if the ring has room)
+    __device__ __forceinline__ void request(uint32_t gi, uint32_t lane)
+    {
+        a_next = __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, (gi + 1) * astride, 0);
+        fetch = dec.m > 0 && dec.re + kFetchWords - dec.cur <= kRingWords;
+        pf_at = dec.re;
+        pf = __builtin_amdgcn_raw_buffer_load_b32(dec.wrs, 2 * (pf_at + 2 * lane), 0, 0);
+    }
+
+    // the previous group's outputs, then this group's anchor row
+    __device__ __forceinline__ void write_rows()
+    {
         if (held) {
             if (dec.present) flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
             held = false;
         }
         if (dec.present) put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? 0u : a16);
         orow += ostride;
-        __builtin_amdgcn_sched_barrier(0);
+    }
 
-        const uint32_t nsteps = __builtin_amdgcn_readfirstlane(min(g.G, len - gi * g.G) - 1);
-        if (nsteps == (uint32_t)kUnrolledSteps && dec.i + kUnrolledSteps < dec.m) {
-            // a full group that does not hold the chunk's last symbol
-#pragma unroll
-            for (int u = 0; u < kUnrolledSteps; ++u) {
-                float dq;
-                const uint32_t p = dec.symbol<LOGP>(tab, lb, dq);
-                if (SYMBOLS)
-                    ys[u] = p / kSymStride;
-                else
-                    yf[u] = af + dq;
-                dec.renorm(lane);
-            }
-            dec.i += kUnrolledSteps;
-            held = true;
-            orow_held = orow;
-            orow += kUnrolledSteps * ostride;
-        } else {
-            for (uint32_t u = nsteps; u != 0; --u) {
-                float dq;
-                const uint32_t p = dec.symbol<LOGP>(tab, lb, dq);
-                if (dec.present) put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? p / kSymStride : f2h(af + dq));
-                orow += ostride;
-                if (++dec.i < dec.m) dec.renorm(lane);
-            }
-        }
-        // consume this group's requests; the ring chunk is dropped if a refill inside the
-        // group already loaded those words.  (The empty asm pins where the loaded values
-        // are first needed, so the wait for them is placed here.)
-        __builtin_amdgcn_sched_barrier(0);
+    // takes in the requests; the ring chunk is dropped if a refill inside the group
+    // already loaded those words.  (The empty asm pins where the loaded values are first
+    // needed, so the wait for them is placed here.)
+    __device__ __forceinline__ void consume(uint32_t lane)
+    {
         uint32_t an = a_next, pv = pf;
         asm volatile("" : "+v"(an), "+v"(pv));
         a16 = an;
         af = h2f(a16);
         if (fetch && dec.re == pf_at) {
-            ring_put(ring, pf_at + 2 * lane, pv);
+            ring_put(dec.ring, pf_at + 2 * lane, pv);
             dec.re = pf_at + kFetchWords;
         }
     }
-    if (held && dec.present) flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
+
+    // step u of an unrolled group: the output stays in a register
+    template <int LOGP>
+    __device__ __forceinline__ void step_held(const uint8_t *tab, uint32_t lb, uint32_t ctop, int u)
+    {
+        float dq;
+        const uint32_t p = dec.template symbol<LOGP>(tab, lb, ctop, dq);
+        if (SYMBOLS)
+            ys[u] = p / kSymStride;
+        else
+            yf[u] = af + dq;
+    }
+
+    __device__ __forceinline__ void finish_unrolled()
+    {
+        dec.i += kUnrolledSteps;
+        held = true;
+        orow_held = orow;
+        orow += kUnrolledSteps * ostride;
+    }
+
+    template <int LOGP>
+    __device__ __forceinline__ void unrolled(const uint8_t *tab, uint32_t lb, uint32_t ctop,
+                                             uint32_t lane)
+    {
+#pragma unroll
+        for (int u = 0; u < kUnrolledSteps; ++u) {
+            step_held<LOGP>(tab, lb, ctop, u);
+            // the state update is computed here, next to its table read
+            asm volatile("" : "+v"(dec.ncode));
+            dec.renorm(lane);
+        }
+        finish_unrolled();
+    }
+
+    // any other group: one store per step
+    template <int LOGP>
+    __device__ __forceinline__ void generic(const uint8_t *tab, uint32_t lb, uint32_t ctop,
+                                            uint32_t nsteps, uint32_t lane)
+    {
+        for (uint32_t u = nsteps; u != 0; --u) {
+            float dq;
+            const uint32_t p = dec.template symbol<LOGP>(tab, lb, ctop, dq);
+            if (dec.present)
+                put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? p / kSymStride : f2h(af + dq));
+            orow += ostride;
+            if (++dec.i < dec.m) dec.renorm(lane);
+        }
+    }
+
+    __device__ __forceinline__ void final_flush()
+    {
+        if (held && dec.present) flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
+    }
+};
+
+// One wavefront decodes NS chunks of the same (row, channel block) in lockstep, sharing
+// the block's LDS table.  With two, the symbol searches of both streams sit in one
+// basic block, so the dependent LDS reads of one overlap the arithmetic of the other.
+template <int LOGP, bool SYMBOLS, bool FULL, int NS>
+__device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__restrict__ tab,
+                                              uint16_t *__restrict__ ring,
+                                              const uint8_t *__restrict__ container,
+                                              const ContainerView &cv, uint32_t k0, uint32_t k1,
+                                              uint32_t row, uint32_t b, uint32_t lane,
+                                              uint16_t *__restrict__ out,
+                                              uint8_t *__restrict__ sym_out)
+{
+    const bool present = FULL || lane < min(kLanes, g.C - b * kLanes);
+    const uint32_t lb = lane * 4;  // entry (symbol 0, this lane)
+    const uint32_t ctop =
+        *reinterpret_cast<const uint16_t *>(tab + lb + (1u << (LOGP - 1)) * kSymStride + 2);
+    Stream<SYMBOLS> st[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        st[s].init(g, ring + s * kRingAlloc, container, cv, s == 0 ? k0 : k1, row, b, lane,
+                   present, out, sym_out);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) st[s].first_anchor(lane);
+    uint32_t ngmax = st[0].ng;
+    if (NS == 2) ngmax = max(ngmax, st[NS - 1].ng);
+
+    for (uint32_t gi = 0; gi < ngmax; ++gi) {
+        bool act[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) act[s] = gi < st[s].ng;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            if (act[s]) st[s].request(gi, lane);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            if (act[s]) st[s].write_rows();
+        __builtin_amdgcn_sched_barrier(0);
+
+        uint32_t nsteps[NS];
+        bool unr[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            nsteps[s] = act[s] ? st[s].steps(g, gi) : 0u;
+            unr[s] = act[s] && st[s].unrollable(nsteps[s]);
+        }
+        if (NS == 2 && unr[0] && unr[NS - 1]) {
+#pragma unroll
+            for (int u = 0; u < kUnrolledSteps; ++u) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) st[s].template step_held<LOGP>(tab, lb, ctop, u);
+                // both state updates are computed here, next to their table reads
+                asm volatile("" : "+v"(st[0].dec.ncode), "+v"(st[NS - 1].dec.ncode));
+#pragma unroll
+                for (int s = 0; s < NS; ++s) st[s].dec.renorm(lane);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) st[s].finish_unrolled();
+        } else {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                if (unr[s])
+                    st[s].template unrolled<LOGP>(tab, lb, ctop, lane);
+                else if (act[s])
+                    st[s].template generic<LOGP>(tab, lb, ctop, nsteps[s], lane);
+            }
+        }
+
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            if (act[s]) st[s].consume(lane);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) st[s].final_flush();
 }
 
 template <bool SYMBOLS, bool FULL>
-__device__ __forceinline__ void decode_dispatch(uint32_t logp, const Geom &g, const uint8_t *tab,
-                                                uint16_t *ring, const uint8_t *container,
-                                                const ContainerView &cv, uint32_t k, uint32_t row,
-                                                uint32_t b, uint32_t lane, uint16_t *out,
-                                                uint8_t *sym_out)
+__device__ __forceinline__ void decode_dispatch(uint32_t logp, bool pair, const Geom &g,
+                                                const uint8_t *tab, uint16_t *ring,
+                                                const uint8_t *container, const ContainerView &cv,
+                                                uint32_t k0, uint32_t k1, uint32_t row, uint32_t b,
+                                                uint32_t lane, uint16_t *out, uint8_t *sym_out)
 {
+#define CG_DECODE_CASE(LP)                                                                        \
+    case LP:                                                                                      \
+        if (pair)                                                                                 \
+            decode_chunks<LP, SYMBOLS, FULL, 2>(g, tab, ring, container, cv, k0, k1, row, b,      \
+                                                lane, out, sym_out);                              \
+        else                                                                                      \
+            decode_chunks<LP, SYMBOLS, FULL, 1>(g, tab, ring, container, cv, k0, k1, row, b,      \
+                                                lane, out, sym_out);                              \
+        break;
     switch (logp) {
-    case 1: decode_wave<1, SYMBOLS, FULL>(g, tab, ring, container, cv, k, row, b, lane, out, sym_out); break;
-    case 2: decode_wave<2, SYMBOLS, FULL>(g, tab, ring, container, cv, k, row, b, lane, out, sym_out); break;
-    case 3: decode_wave<3, SYMBOLS, FULL>(g, tab, ring, container, cv, k, row, b, lane, out, sym_out); break;
-    case 4: decode_wave<4, SYMBOLS, FULL>(g, tab, ring, container, cv, k, row, b, lane, out, sym_out); break;
-    default: decode_wave<5, SYMBOLS, FULL>(g, tab, ring, container, cv, k, row, b, lane, out, sym_out); break;
+        CG_DECODE_CASE(1)
+        CG_DECODE_CASE(2)
+        CG_DECODE_CASE(3)
+        CG_DECODE_CASE(4)
+    default:
+        CG_DECODE_CASE(5)
     }
+#undef CG_DECODE_CASE
 }
 
+// Block = 4 wavefronts over the chunks [kb + 8 * set, kb + 8 * set + 8) of one (row,
+// channel block); wavefront w takes chunks base + w and base + w + 4.
 template <bool SYMBOLS>
 __global__ __launch_bounds__(256) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
                                                   const uint32_t *__restrict__ dtab,
@@ -867,7 +1048,7 @@ __global__ __launch_bounds__(256) void k3_decode(Geom g, const uint8_t *__restri
                                                   uint8_t *__restrict__ sym_out)
 {
     __shared__ uint32_t tab[kTabBlock];
-    __shared__ uint16_t rings[kWavesPerBlock * kRingAlloc];
+    __shared__ uint16_t rings[kWavesPerBlock * kStreamsPerWave * kRingAlloc];
     const uint32_t set = blockIdx.x % n_sets;
     const uint32_t tmp = blockIdx.x / n_sets;
     const uint32_t b = tmp % g.NB;
@@ -886,14 +1067,18 @@ __global__ __launch_bounds__(256) void k3_decode(Geom g, const uint8_t *__restri
     __syncthreads();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     const uint32_t lane = threadIdx.x % kLanes;
-    const uint32_t k = g.kb + set * kWavesPerBlock + wave;
-    if (k >= g.ke) return;
+    const uint32_t k0 = g.kb + set * kWavesPerBlock * kStreamsPerWave + wave;
+    const uint32_t k1 = k0 + kWavesPerBlock;
+    if (k0 >= g.ke) return;
     const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab);
-    uint16_t *ring = rings + wave * kRingAlloc;
+    uint16_t *ring = rings + wave * kStreamsPerWave * kRingAlloc;
+    const bool pair = k1 < g.ke;
     if (g.C - b * kLanes >= kLanes)
-        decode_dispatch<SYMBOLS, true>(logp, g, tb, ring, container, cv, k, row, b, lane, out, sym_out);
+        decode_dispatch<SYMBOLS, true>(logp, pair, g, tb, ring, container, cv, k0, k1, row, b,
+                                       lane, out, sym_out);
     else
-        decode_dispatch<SYMBOLS, false>(logp, g, tb, ring, container, cv, k, row, b, lane, out, sym_out);
+        decode_dispatch<SYMBOLS, false>(logp, pair, g, tb, ring, container, cv, k0, k1, row, b,
+                                        lane, out, sym_out);
 }
 
 // ------------------------------------------------------------------------------ K4
@@ -1053,7 +1238,8 @@ hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
                      const uint8_t *container, const ContainerView &cv, uint16_t *out,
                      uint8_t *sym_out, hipStream_t st)
 {
-    uint32_t n_sets = (g.ke - g.kb + kWavesPerBlock - 1) / kWavesPerBlock;
+    const uint32_t per_block = kWavesPerBlock * kStreamsPerWave;
+    uint32_t n_sets = (g.ke - g.kb + per_block - 1) / per_block;
     uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
     if (sym_out)
         hipLaunchKernelGGL(k3_decode<true>, dim3((uint32_t)blocks), dim3(256), 0, st, g, bins,

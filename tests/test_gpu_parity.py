@@ -106,6 +106,16 @@ def test_llama7b_shape_two_layers(cg):
     full_parity(cg, X, w.H_kv, w.group, w.chunk, (w.bins[0], w.bins[31]), label="7B layers 0,31")
 
 
+@pytest.mark.parametrize("G,Tc,rng", [(7, 150, None), (10, 90, None), (10, 90, (3, 12)),
+                                      (10, 240, None)])
+def test_paired_chunks(cg, G, Tc, rng):
+    """Many chunks per (row, channel block), so a wavefront decodes two chunks in
+    lockstep: equal and unequal chunk lengths, a partial lane block (C = 136), full and
+    partial anchor groups, and a chunk range that starts mid-cache."""
+    X = _gen(2, 2000, 136, HEAVY)
+    full_parity(cg, X, 17, G, Tc, (32, 8), chunk_range=rng, label="paired")
+
+
 @pytest.mark.parametrize("S,G,Tc", [(5, 10, 5), (37, 10, 37), (41, 4, 20), (64, 1, 16),
                                     (130, 10, 16384)])
 def test_edge_shapes(cg, S, G, Tc):
