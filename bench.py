@@ -12,7 +12,12 @@ metric), from HIP events around each decode on the stream it runs on, averaged o
 the timed steps.  `ms_per_step` is the wall time of a whole step.  The input is
 resident in HBM before timing starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+A second object, "streamed", covers the streamed decode of the 131K-token cache
+(L=80, S=131072, 42.95 GB): every chunk encoded at three levels, one level per chunk
+chosen from a seeded bandwidth trace, the chosen containers copied from pinned host
+memory on one HIP stream while earlier chunks decode on another.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-streamed]
 """
 from __future__ import annotations
 
@@ -106,6 +111,59 @@ def cpu_baseline(w, X, max_threads: int) -> dict:
                       % (list(layers), raw / 1e9, cores, dt)}
 
 
+def streamed_report(dev, n_slots: int = 3, reps: int = 3, seed: int = 0) -> dict:
+    """The 131K-token cache streamed chunk by chunk from pinned host memory, each chunk
+    at the level its bandwidth-trace entry allows, decoded while later chunks copy."""
+    import numpy as np
+    import torch
+
+    from kv_cache_compression_cg_amd import configs, streamed, synth
+
+    w = configs.LLAMA3_70B_131K
+    t = time.time()
+    X = synth.gen_kv(w, device=dev)
+    prep = streamed.prepare(X, w.group, w.chunk, w.levels, H_kv=w.H_kv, seed=seed)
+    log("[streamed] %s: %d chunks encoded at %d levels, chosen containers in pinned memory "
+        "(%.1fs)" % (w.name, w.n_chunks, len(w.levels), time.time() - t))
+    out = torch.empty_like(X)
+    runs = [streamed.run(prep, out, n_slots=n_slots) for _ in range(reps + 1)][1:]
+    tt = torch.arange(w.S, device=dev)
+    anchor = ((tt % w.chunk) % w.group) == 0
+    assert torch.equal(out[:, :, anchor].view(torch.int16), X[:, :, anchor].view(torch.int16))
+    mean = {k: sum(r[k] for r in runs) / len(runs) for k in ("total_ms", "copy_ms", "decode_ms")}
+    copied = runs[0]["copied_bytes"]
+    raw = w.raw_bytes
+    chunk_raw = np.array([2 * w.L * w.C * min(w.chunk, w.S - k * w.chunk) * 2
+                          for k in range(w.n_chunks)], dtype=np.float64)
+    lv, cnt = np.unique(prep.levels, return_counts=True)
+    res = {
+        "workload": w.name, "L": w.L, "H_kv": w.H_kv, "d": w.d, "S": w.S, "chunk": w.chunk,
+        "group": w.group, "raw_bytes": raw, "chunks": w.n_chunks,
+        "levels": "bins 32/16/8, 16/8/4, 8/4/2 for layers 0-19 / 20-39 / 40-79",
+        "chunks_per_level": {str(int(a)): int(b) for a, b in zip(lv, cnt)},
+        "streamed_bytes": copied, "table_bytes": prep.table_bytes,
+        "compression_ratio": round(raw / (copied + prep.table_bytes), 4),
+        "n_slots": n_slots, "reps": reps,
+        "total_ms": round(mean["total_ms"], 3), "copy_ms": round(mean["copy_ms"], 3),
+        "decode_ms": round(mean["decode_ms"], 3),
+        "end_to_end_GBps": round(raw / (mean["total_ms"] * 1e-3) / 1e9, 2),
+        "decode_only_GBps": round(raw / (mean["decode_ms"] * 1e-3) / 1e9, 2),
+        "h2d_GBps": round(copied / (mean["copy_ms"] * 1e-3) / 1e9, 2),
+        "overlap": round((mean["copy_ms"] + mean["decode_ms"] - mean["total_ms"])
+                         / min(mean["copy_ms"], mean["decode_ms"]), 4),
+        "network_s_trace": round(streamed.network_seconds(prep.sizes, prep.levels,
+                                                          prep.bw_gbps), 4),
+        "raw_fp16_network_s_trace": round(float(np.sum(chunk_raw * 8 / (prep.bw_gbps * 1e9))), 4),
+    }
+    log("[streamed] end-to-end %.1f GB/s raw-equivalent (copies %.1f GB/s, decode-only "
+        "%.1f GB/s, overlap %.2f), ratio %.3f"
+        % (res["end_to_end_GBps"], res["h2d_GBps"], res["decode_only_GBps"], res["overlap"],
+           res["compression_ratio"]))
+    del prep, out, X
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +171,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_70b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-streamed", action="store_true",
+                    help="skip the streamed decode of the 131K-token cache")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 4 GiB device-to-device copy (counter calibration)")
@@ -223,6 +283,10 @@ def main() -> int:
         % (dec_mean, value, res["pct_hbm_peak"], res["ms_per_step"], res["compression_ratio"]))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, X, args.cpu_threads)
+    if not args.no_streamed:
+        del X, out, tab, blob, last
+        torch.cuda.empty_cache()
+        res["streamed"] = streamed_report(dev)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -137,6 +137,52 @@ int cg_decode(const cg_tables *tables, const cg_blob *blob, const void *containe
 void cg_free(void *handle);
 
 /* ----------------------------------------------------------------------------------
+ * Streamed decode.  Chunk containers arrive from host memory while earlier chunks
+ * decode, and each chunk may come at its own compression level ("Guide to CacheGen",
+ * section 4, Overlapped Streaming Decoder Pipeline: chunk i decodes while chunk i+1 is
+ * in transit; gptget summary of arXiv 2310.07240, Methodology: the compression level
+ * follows the available bandwidth and GPU decoding keeps pace with transmission).
+ * ---------------------------------------------------------------------------------- */
+
+/* One container to stream: the tables of the level it was coded at, its handle (for
+ * the layout only; the handle's device copy is not read) and the same container bytes
+ * (cg_blob_read of the whole container) in host memory.  Pinned host memory (hipHostMalloc)
+ * lets the copy overlap decoding; pageable memory works but serialises. */
+typedef struct cg_stream_item {
+    const cg_tables *tables;
+    const cg_blob *blob;
+    const void *host_container;
+} cg_stream_item;
+
+/* Timings of a streamed decode from HIP events, milliseconds. */
+typedef struct cg_stream_stats {
+    float total_ms;        /* first copy started -> last decode finished */
+    float copy_ms;         /* sum over items of the host-to-device copy */
+    float decode_ms;       /* sum over items of the decode */
+    uint64_t copied_bytes; /* sum over items of the container size */
+} cg_stream_stats;
+
+/*
+ * Decodes items[0 .. n_items) in order into kv_out_dev (fp16 [L][2][S][C]).  Item i is
+ * copied into staging slot i % n_slots (slot j starts at staging_dev + j * slot_bytes)
+ * on copy_stream and decoded from there on decode_stream; a slot is refilled only after
+ * the decode that read it has finished.
+ *   staging_dev:   caller-owned device memory, n_slots * slot_bytes bytes; the address
+ *                  and slot_bytes are multiples of 256.
+ *   copy_stream, decode_stream: two different streams of the tables' device.
+ *   stats:         NULL to return once everything is queued (kv_out_dev, the staging
+ *                  memory and the host containers stay in use until decode_stream and
+ *                  copy_stream have drained); otherwise waits for both and fills *stats.
+ * Every item's tables must be on one device and describe the same cache shape, and its
+ * container must fit a slot; all of this is checked before anything is queued.
+ * Errors: CG_E_INVAL, CG_E_CORRUPT, CG_E_NOMEM, CG_E_HIP (after waiting for both
+ * streams if work had been queued).
+ */
+int cg_stream_decode(const cg_stream_item *items, uint32_t n_items, void *staging_dev,
+                     uint64_t slot_bytes, uint32_t n_slots, void *kv_out_dev,
+                     void *copy_stream, void *decode_stream, cg_stream_stats *stats);
+
+/* ----------------------------------------------------------------------------------
  * Inspection and the unfused path.  Same conventions as above.
  * ---------------------------------------------------------------------------------- */
 

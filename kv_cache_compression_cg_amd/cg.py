@@ -53,9 +53,19 @@ class TablesInfo(ctypes.Structure):
                [("stored_bytes", ctypes.c_uint64)]
 
 
+class StreamItem(ctypes.Structure):
+    _fields_ = [("tables", ctypes.c_void_p), ("blob", ctypes.c_void_p),
+                ("host_container", ctypes.c_void_p)]
+
+
+class StreamStats(ctypes.Structure):
+    _fields_ = [("total_ms", ctypes.c_float), ("copy_ms", ctypes.c_float),
+                ("decode_ms", ctypes.c_float), ("copied_bytes", ctypes.c_uint64)]
+
+
 EXPORTED = ["cg_build_cdf", "cg_encode", "cg_decode", "cg_free", "cg_last_error",
             "cg_tables_export", "cg_tables_get_info", "cg_blob_get_info", "cg_blob_read",
-            "cg_quantize", "cg_decode_symbols", "cg_dequantize"]
+            "cg_quantize", "cg_decode_symbols", "cg_dequantize", "cg_stream_decode"]
 
 _lib = None
 
@@ -82,6 +92,8 @@ def load() -> ctypes.CDLL:
         "cg_quantize": [vp, vp, u32, u32, vp, vp],
         "cg_decode_symbols": [vp, vp, vp, vp, vp],
         "cg_dequantize": [vp, vp, vp, vp, vp, vp],
+        "cg_stream_decode": [ctypes.POINTER(StreamItem), u32, vp, u64, u32, vp, vp, vp,
+                             ctypes.POINTER(StreamStats)],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -181,6 +193,15 @@ class Blob:
     @property
     def chunk_end(self) -> int:
         return int(self.header["chunk_end"])
+
+    def read_into(self, dst: torch.Tensor) -> torch.Tensor:
+        """Copies the whole container into a contiguous uint8 CPU tensor (e.g. pinned)."""
+        if dst.device.type != "cpu" or dst.dtype != torch.uint8 or not dst.is_contiguous() \
+                or dst.numel() < self.nbytes:
+            raise ValueError("destination must be a contiguous uint8 CPU tensor of the "
+                             "container's size")
+        _check(load().cg_blob_read(self.handle, 0, self.nbytes, dst.data_ptr()))
+        return dst
 
     def read(self, offset: int = 0, nbytes: Optional[int] = None) -> np.ndarray:
         nbytes = self.nbytes - offset if nbytes is None else nbytes
@@ -305,3 +326,38 @@ def dequantize(tables: Tables, blob: Blob, sym: torch.Tensor,
 def compressed_bytes(tables: Tables, blobs: Sequence[Blob]) -> int:
     """Everything needed to decode: the containers plus the stored tables."""
     return sum(b.nbytes for b in blobs) + tables.stored_bytes
+
+
+def stream_decode(items: Sequence[tuple], staging: torch.Tensor, n_slots: int,
+                  out: torch.Tensor, copy_stream: torch.cuda.Stream,
+                  decode_stream: torch.cuda.Stream, wait: bool = True) -> Optional[dict]:
+    """items: (Tables, Blob, host uint8 tensor holding Blob.read()) per container, decoded
+    in order into `out`; `staging` (uint8 CUDA) is split into n_slots equal slots.  With
+    wait=True returns the event timings, otherwise returns once the work is queued."""
+    if not items:
+        return {"total_ms": 0.0, "copy_ms": 0.0, "decode_ms": 0.0, "copied_bytes": 0}
+    t0 = items[0][0]
+    _kv_check(out, t0.shape)
+    if not staging.is_cuda or staging.dtype != torch.uint8 or not staging.is_contiguous():
+        raise ValueError("staging must be a contiguous uint8 CUDA tensor")
+    slot_bytes = staging.numel() // n_slots if n_slots > 0 else 0
+    arr = (StreamItem * len(items))()
+    for i, (t, b, host) in enumerate(items):
+        if host.device.type != "cpu" or host.dtype != torch.uint8 or host.numel() < b.nbytes \
+                or not host.is_contiguous():
+            raise ValueError("item %d: host container must be a contiguous uint8 CPU tensor "
+                             "of the container's size" % i)
+        arr[i] = StreamItem(t.handle.value if isinstance(t.handle, ctypes.c_void_p) else t.handle,
+                            b.handle.value if isinstance(b.handle, ctypes.c_void_p) else b.handle,
+                            host.data_ptr())
+    st = StreamStats()
+    with torch.cuda.device(out.device):
+        _check(load().cg_stream_decode(arr, len(items), staging.data_ptr(), slot_bytes,
+                                       max(n_slots, 0), out.data_ptr(),
+                                       ctypes.c_void_p(copy_stream.cuda_stream),
+                                       ctypes.c_void_p(decode_stream.cuda_stream),
+                                       ctypes.byref(st) if wait else None))
+    if not wait:
+        return None
+    return {"total_ms": st.total_ms, "copy_ms": st.copy_ms, "decode_ms": st.decode_ms,
+            "copied_bytes": int(st.copied_bytes)}

@@ -410,6 +410,139 @@ int cg_decode(const cg_tables *t, const cg_blob *b, const void *container_dev, v
     return CG_OK;
 }
 
+namespace {
+
+// Events of one streamed decode, destroyed on scope exit (HIP releases an event that is
+// still pending once it completes).
+struct EventSet {
+    std::vector<hipEvent_t> ev;
+    ~EventSet()
+    {
+        for (hipEvent_t e : ev)
+            if (e) (void)hipEventDestroy(e);
+    }
+    hipError_t make(size_t n, bool timing)
+    {
+        ev.assign(n, nullptr);
+        for (size_t i = 0; i < n; ++i) {
+            hipError_t e = timing ? hipEventCreate(&ev[i])
+                                  : hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+};
+
+bool same_shape(const cg_tables *a, const cg_tables *b)
+{
+    return a->L == b->L && a->H == b->H && a->d == b->d && a->S == b->S && a->G == b->G &&
+           a->Tc == b->Tc;
+}
+
+}  // namespace
+
+int cg_stream_decode(const cg_stream_item *items, uint32_t n_items, void *staging_dev,
+                     uint64_t slot_bytes, uint32_t n_slots, void *kv_out_dev,
+                     void *copy_stream, void *decode_stream, cg_stream_stats *stats)
+{
+    g_error.clear();
+    if (!items || !staging_dev || !kv_out_dev || !n_slots || !slot_bytes)
+        return fail(CG_E_INVAL, "null argument");
+    if (copy_stream == decode_stream)
+        return fail(CG_E_INVAL, "copy and decode streams must differ");
+    if (slot_bytes > UINT64_MAX / n_slots) return fail(CG_E_INVAL, "staging size overflows");
+    // container sections are 256-byte aligned relative to the container's first byte
+    if (reinterpret_cast<uintptr_t>(staging_dev) % 256 != 0 || slot_bytes % 256 != 0)
+        return fail(CG_E_INVAL, "staging memory and slot size must be 256-byte aligned");
+    if (n_items == 0) {
+        if (stats) *stats = cg_stream_stats{};
+        return CG_OK;
+    }
+    const cg_tables *t0 = items[0].tables;
+    if (int rc = check_tables(t0)) return rc;
+    for (uint32_t i = 0; i < n_items; ++i) {
+        const cg_stream_item &it = items[i];
+        if (int rc = check_tables(it.tables)) return rc;
+        if (int rc = check_blob(it.tables, it.blob)) return rc;
+        if (!it.host_container) return fail(CG_E_INVAL, "null host container");
+        if (it.tables->device != t0->device || !same_shape(it.tables, t0))
+            return fail(CG_E_INVAL, "items describe different caches or devices");
+        if (it.blob->hdr.total_bytes > slot_bytes)
+            return fail(CG_E_INVAL, "a container does not fit a staging slot");
+    }
+    DeviceScope ds;
+    CG_HIP(ds.enter(t0->device), "hipSetDevice");
+    hipStream_t cs = (hipStream_t)copy_stream, dec = (hipStream_t)decode_stream;
+
+    // per slot: copied (decode may start) and freed (the slot may be refilled); with
+    // stats, per item: copy start/end and decode start/end
+    EventSet slot_ev, item_ev;
+    CG_HIP(slot_ev.make(2 * (size_t)n_slots, false), "hipEventCreate");
+    if (stats) CG_HIP(item_ev.make(4 * (size_t)n_items, true), "hipEventCreate");
+    hipEvent_t *copied = slot_ev.ev.data(), *freed = copied + n_slots;
+
+    hipError_t err = hipSuccess;
+    const char *what = "";
+    uint64_t bytes = 0;
+    for (uint32_t i = 0; i < n_items && err == hipSuccess; ++i) {
+        const cg_stream_item &it = items[i];
+        const uint32_t j = i % n_slots;
+        uint8_t *slot = static_cast<uint8_t *>(staging_dev) + (uint64_t)j * slot_bytes;
+        const uint64_t nb = it.blob->hdr.total_bytes;
+        hipEvent_t *ie = stats ? item_ev.ev.data() + 4 * (size_t)i : nullptr;
+        if (i >= n_slots && (err = hipStreamWaitEvent(cs, freed[j], 0)) != hipSuccess) {
+            what = "hipStreamWaitEvent";
+            break;
+        }
+        if (ie && (err = hipEventRecord(ie[0], cs)) != hipSuccess) { what = "hipEventRecord"; break; }
+        if ((err = hipMemcpyAsync(slot, it.host_container, nb, hipMemcpyHostToDevice, cs)) !=
+            hipSuccess) {
+            what = "hipMemcpyAsync";
+            break;
+        }
+        if (ie && (err = hipEventRecord(ie[1], cs)) != hipSuccess) { what = "hipEventRecord"; break; }
+        if ((err = hipEventRecord(copied[j], cs)) != hipSuccess ||
+            (err = hipStreamWaitEvent(dec, copied[j], 0)) != hipSuccess) {
+            what = "copy -> decode event";
+            break;
+        }
+        if (ie && (err = hipEventRecord(ie[2], dec)) != hipSuccess) { what = "hipEventRecord"; break; }
+        const cg_blob *b = it.blob;
+        Geom g = make_geom(it.tables, b->hdr.chunk_begin, b->hdr.chunk_end);
+        if ((err = launch_k3(g, it.tables->d_bins, it.tables->d_dtab, slot, view_of(b),
+                             static_cast<uint16_t *>(kv_out_dev), nullptr, dec)) != hipSuccess) {
+            what = "k3_decode";
+            break;
+        }
+        if (ie && (err = hipEventRecord(ie[3], dec)) != hipSuccess) { what = "hipEventRecord"; break; }
+        if ((err = hipEventRecord(freed[j], dec)) != hipSuccess) { what = "hipEventRecord"; break; }
+        bytes += nb;
+    }
+    if (err != hipSuccess) {
+        (void)hipStreamSynchronize(cs);
+        (void)hipStreamSynchronize(dec);
+        return hip_fail(err, what);
+    }
+    if (!stats) return CG_OK;
+
+    CG_HIP(hipStreamSynchronize(cs), "hipStreamSynchronize");
+    CG_HIP(hipStreamSynchronize(dec), "hipStreamSynchronize");
+    cg_stream_stats st{};
+    const hipEvent_t *ie = item_ev.ev.data();
+    for (uint32_t i = 0; i < n_items; ++i) {
+        float c = 0.f, d = 0.f;
+        CG_HIP(hipEventElapsedTime(&c, ie[4 * i], ie[4 * i + 1]), "hipEventElapsedTime");
+        CG_HIP(hipEventElapsedTime(&d, ie[4 * i + 2], ie[4 * i + 3]), "hipEventElapsedTime");
+        st.copy_ms += c;
+        st.decode_ms += d;
+    }
+    CG_HIP(hipEventElapsedTime(&st.total_ms, ie[0], ie[4 * ((size_t)n_items - 1) + 3]),
+           "hipEventElapsedTime");
+    st.copied_bytes = bytes;
+    *stats = st;
+    return CG_OK;
+}
+
 int cg_decode_symbols(const cg_tables *t, const cg_blob *b, const void *container_dev,
                       void *sym_dev, void *hip_stream)
 {

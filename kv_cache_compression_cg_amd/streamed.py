@@ -1,0 +1,122 @@
+"""Streamed decode of a long cache, each chunk at a compression level picked for the
+bandwidth of the moment.
+
+The pages have the cache sent chunk by chunk, each chunk's compression level set by the
+available bandwidth, and GPU decoding running alongside the transfer: chunk i decodes
+while chunk i+1 is in transit ("Guide to CacheGen", section 4, Overlapped Streaming
+Decoder Pipeline; gptget summary of arXiv 2310.07240, Methodology).  They give no rule
+for the choice.  The rule used here: each chunk has a deadline, the time its container at
+the reference level would take at the trace's mean rate, and takes the finest level whose
+container meets that deadline at the chunk's own rate, else the coarsest level.
+
+Host logic only: the copies and decodes run in libcg (cg_stream_decode), on two HIP
+streams with 2-3 staging slots.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import cg
+
+TRACE_LO_GBPS = 1.0
+TRACE_HI_GBPS = 25.0
+REFERENCE_LEVEL = 1
+
+
+def bandwidth_trace(n_chunks: int, seed: int = 0) -> np.ndarray:
+    """Per-chunk link rate in Gbit/s, uniform on [1, 25], seeded."""
+    rng = np.random.default_rng([seed, 5])
+    return rng.uniform(TRACE_LO_GBPS, TRACE_HI_GBPS, size=n_chunks)
+
+
+def choose_levels(sizes: np.ndarray, bw_gbps: np.ndarray, ref_level: int = REFERENCE_LEVEL,
+                  ref_gbps: Optional[float] = None) -> np.ndarray:
+    """sizes: bytes [levels][chunks], level 0 the finest.  Returns the level per chunk."""
+    sizes = np.asarray(sizes, dtype=np.float64)
+    bw = np.asarray(bw_gbps, dtype=np.float64)
+    n_levels, n = sizes.shape
+    if bw.shape != (n,):
+        raise ValueError("one rate per chunk expected")
+    mean = 0.5 * (TRACE_LO_GBPS + TRACE_HI_GBPS) if ref_gbps is None else ref_gbps
+    deadline = sizes[ref_level] * 8.0 / (mean * 1e9)
+    out = np.full(n, n_levels - 1, dtype=np.int64)
+    for k in range(n):
+        for lv in range(n_levels):
+            if sizes[lv, k] * 8.0 / (bw[k] * 1e9) <= deadline[k]:
+                out[k] = lv
+                break
+    return out
+
+
+def network_seconds(sizes: np.ndarray, levels: np.ndarray, bw_gbps: np.ndarray) -> float:
+    """Time to send the chosen containers over the trace (no overlap with decoding)."""
+    sizes = np.asarray(sizes, dtype=np.float64)
+    chosen = sizes[np.asarray(levels), np.arange(sizes.shape[1])]
+    return float(np.sum(chosen * 8.0 / (np.asarray(bw_gbps, dtype=np.float64) * 1e9)))
+
+
+@dataclass
+class Prepared:
+    tables: List[cg.Tables]       # one per level
+    items: list                   # (Tables, Blob, pinned host tensor) per chunk, in order
+    levels: np.ndarray            # chosen level per chunk
+    sizes: np.ndarray             # container bytes [levels][chunks]
+    bw_gbps: np.ndarray
+    slot_bytes: int
+
+    @property
+    def streamed_bytes(self) -> int:
+        return int(sum(b.nbytes for _, b, _ in self.items))
+
+    @property
+    def table_bytes(self) -> int:
+        used = sorted(set(int(v) for v in self.levels))
+        return int(sum(self.tables[v].stored_bytes for v in used))
+
+
+def prepare(kv: torch.Tensor, group: int, chunk: int, level_bins: Sequence[Sequence[int]],
+            H_kv: int, seed: int = 0, force_levels: Optional[Sequence[int]] = None) -> Prepared:
+    """Builds the tables of every level, encodes every chunk at every level, picks one
+    level per chunk and keeps that container in pinned host memory."""
+    tables = [cg.build_cdf(kv, group, chunk, bins, H_kv=H_kv) for bins in level_bins]
+    n = tables[0].n_chunks
+    bw = bandwidth_trace(n, seed)
+    sizes = np.zeros((len(tables), n), dtype=np.int64)
+    levels = np.zeros(n, dtype=np.int64)
+    items = []
+    slot = 0
+    for k in range(n):
+        blobs = [cg.encode(t, kv, k, k + 1) for t in tables]
+        sizes[:, k] = [b.nbytes for b in blobs]
+        if force_levels is not None:
+            lv = int(force_levels[k])
+        else:
+            lv = int(choose_levels(sizes[:, k:k + 1], bw[k:k + 1])[0])
+        levels[k] = lv
+        host = torch.empty(blobs[lv].nbytes, dtype=torch.uint8, pin_memory=True)
+        blobs[lv].read_into(host)
+        items.append((tables[lv], blobs[lv], host))
+        slot = max(slot, blobs[lv].nbytes)
+        del blobs
+    slot = (slot + 255) // 256 * 256  # slots start on 256-byte boundaries
+    return Prepared(tables, items, levels, sizes, bw, slot)
+
+
+def run(prep: Prepared, out: torch.Tensor, n_slots: int = 3,
+        staging: Optional[torch.Tensor] = None) -> dict:
+    """Streams every chunk into `out` and returns the event timings."""
+    need = n_slots * prep.slot_bytes
+    if staging is None or staging.numel() < need:
+        staging = torch.empty(need, dtype=torch.uint8, device=out.device)
+    copy_stream = torch.cuda.Stream(device=out.device)
+    decode_stream = torch.cuda.Stream(device=out.device)
+    # the output and staging memory come from torch's current stream
+    copy_stream.wait_stream(torch.cuda.current_stream(out.device))
+    decode_stream.wait_stream(torch.cuda.current_stream(out.device))
+    stats = cg.stream_decode(prep.items, staging[:need], n_slots, out, copy_stream,
+                             decode_stream, wait=True)
+    return stats

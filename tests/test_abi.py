@@ -57,6 +57,23 @@ def test_validation_without_device(lib):
     assert lib.cg_decode(None, None, None, None, None) == -1
     assert lib.cg_quantize(None, None, 0, 1, None, None) == -1
     assert lib.cg_blob_read(None, 0, 0, None) == -1
+    # streamed decode: argument checks come before any device work
+    st = cg.StreamStats()
+    a, b = ctypes.c_void_p(1), ctypes.c_void_p(2)
+    buf = ctypes.c_void_p(16)
+    assert lib.cg_stream_decode(None, 1, buf, 64, 2, buf, a, b, ctypes.byref(st)) == -1
+    items = (cg.StreamItem * 1)(cg.StreamItem(None, None, None))
+    assert lib.cg_stream_decode(items, 1, buf, 64, 2, buf, a, a, ctypes.byref(st)) == -1
+    assert b"differ" in lib.cg_last_error()
+    assert lib.cg_stream_decode(items, 1, buf, 64, 0, buf, a, b, ctypes.byref(st)) == -1
+    assert lib.cg_stream_decode(items, 1, buf, 64, 2, buf, a, b, ctypes.byref(st)) == -1
+    assert b"aligned" in lib.cg_last_error()
+    buf = ctypes.c_void_p(4096)
+    assert lib.cg_stream_decode(items, 1, buf, 256, 2, buf, a, b, ctypes.byref(st)) == -1
+    assert b"cg_tables" in lib.cg_last_error()
+    st.total_ms = 5.0
+    assert lib.cg_stream_decode(items, 0, buf, 256, 2, buf, a, b, ctypes.byref(st)) == 0
+    assert st.total_ms == 0.0 and st.copied_bytes == 0
     lib.cg_free(None)
     # a handle that is neither tables nor blob is ignored
     junk = ctypes.create_string_buffer(64)

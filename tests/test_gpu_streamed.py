@@ -1,0 +1,139 @@
+"""Streamed decode (cg_stream_decode) against the CPU oracle.
+
+Every chunk is decoded from a container staged out of pinned host memory, at the
+compression level chosen for it; the result must equal the oracle's decode of that
+chunk at that level, bit for bit."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from kv_cache_compression_cg_amd import configs, streamed, synth
+
+pytestmark = pytest.mark.gpu
+
+LEVELS3 = [(32, 16, 8), (16, 8, 4), (8, 4, 2)]
+HEAVY = configs.GenSpec(rho=0.85, heavy_tail=True, outlier_frac=0.05, outlier_mult=30.0, seed=3)
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def cg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_compression_cg_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    from kv_cache_compression_cg_amd import cg as _cg
+    _cg.load()
+    return _cg
+
+
+def _u16(t: torch.Tensor) -> np.ndarray:
+    return np.ascontiguousarray(t.detach().cpu().view(torch.int16).numpy().view(np.uint16))
+
+
+def _oracle_stream(Xh, H, G, Tc, level_bins, levels):
+    """The oracle's decode of every chunk at its level (tokens of all chunks written)."""
+    L, _, S, C = Xh.shape
+    ref = np.zeros(Xh.shape, np.uint16)
+    encs = {}
+    for lv, bins in enumerate(level_bins):
+        ks = [k for k in range(len(levels)) if levels[k] == lv]
+        if not ks:
+            continue
+        shp = O.Shape.make(L, H, C // H, S, G, Tc, bins)
+        tab = O.build_tables(shp, Xh)
+        for k in ks:
+            enc = O.encode(shp, Xh, tab, k, k + 1)
+            encs[k] = enc
+            O.decode(shp, tab, enc, out=ref)
+    return ref, encs
+
+
+@pytest.mark.parametrize("n_slots", [1, 2, 3])
+def test_streamed_forced_levels(cg, n_slots):
+    L, S, H, d, G, Tc = 3, 4000, 2, 64, 10, 300
+    _say("[streamed] L=%d S=%d C=%d G=%d Tc=%d slots=%d" % (L, S, H * d, G, Tc, n_slots))
+    X = synth.gen_custom(L, S, H * d, HEAVY, device="cuda")
+    n = -(-S // Tc)
+    force = [0, 1, 2, 2, 1, 0, 0, 2, 1, 1, 2, 0, 1, 2][:n]
+    prep = streamed.prepare(X, G, Tc, LEVELS3, H_kv=H, force_levels=force)
+    assert list(prep.levels) == force
+    out = torch.full_like(X, float("nan"))
+    stats = streamed.run(prep, out, n_slots=n_slots)
+    torch.cuda.synchronize()
+    ref, encs = _oracle_stream(_u16(X), H, G, Tc, LEVELS3, force)
+    assert np.array_equal(_u16(out), ref)
+    # the staged containers are the oracle's, word for word
+    for k, (_, blob, host) in enumerate(prep.items):
+        assert np.array_equal(blob.payload(), encs[k].payload)
+        assert np.array_equal(blob.offsets(), encs[k].offsets)
+        assert np.array_equal(host.numpy()[:blob.nbytes], blob.read())
+    assert stats["copied_bytes"] == prep.streamed_bytes
+    assert stats["total_ms"] > 0 and stats["copy_ms"] > 0 and stats["decode_ms"] > 0
+
+
+def test_streamed_chosen_levels_and_ragged_shape(cg):
+    """Levels picked from the bandwidth trace; C = 72 (a partial lane block), G = 7."""
+    L, S, H, d, G, Tc = 3, 2500, 9, 8, 7, 200
+    _say("[streamed] chosen levels L=%d S=%d C=%d" % (L, S, H * d))
+    X = synth.gen_custom(L, S, H * d, HEAVY, device="cuda")
+    prep = streamed.prepare(X, G, Tc, LEVELS3, H_kv=H, seed=4)
+    exp = streamed.choose_levels(prep.sizes, prep.bw_gbps)
+    assert np.array_equal(prep.levels, exp)
+    out = torch.zeros_like(X)
+    streamed.run(prep, out, n_slots=2)
+    torch.cuda.synchronize()
+    ref, _ = _oracle_stream(_u16(X), H, G, Tc, LEVELS3, list(prep.levels))
+    assert np.array_equal(_u16(out), ref)
+
+
+@pytest.mark.timeout(900)
+def test_streamed_131k_sampled(cg):
+    """The 131K-token 70B-shaped cache streamed in full at the chosen levels.  Against
+    the oracle: layers 0, 30 and 79 (one per bin tier) on channel block 7, for eight
+    seeded chunks and the last one, at the chosen level and at both others."""
+    w = configs.LLAMA3_70B_131K
+    _say("[streamed] 131K: generating")
+    X = synth.gen_kv(w, device="cuda")
+    _say("[streamed] 131K: preparing %d chunks x %d levels" % (w.n_chunks, len(w.levels)))
+    prep = streamed.prepare(X, w.group, w.chunk, w.levels, H_kv=w.H_kv, seed=0)
+    out = torch.empty_like(X)
+    _say("[streamed] 131K: streaming")
+    stats = streamed.run(prep, out, n_slots=3)
+    torch.cuda.synchronize()
+    assert stats["copied_bytes"] == prep.streamed_bytes
+    layers, c0, c1 = [0, 30, 79], 7 * 64, 8 * 64
+    Xs = _u16(X[layers, :, :, c0:c1].contiguous())
+    outs = _u16(out[layers, :, :, c0:c1].contiguous())
+    rng = np.random.default_rng([0, 55])
+    ks = sorted(set(int(k) for k in rng.choice(w.n_chunks - 1, 8, replace=False)) | {w.n_chunks - 1})
+    Tc, S = w.chunk, w.S
+    for lv, bins in enumerate(w.levels):
+        _say("[streamed] 131K: oracle level %d" % lv)
+        shp = O.Shape.make(3, 1, 64, S, w.group, Tc, [bins[l] for l in layers])
+        tab = O.build_tables(shp, Xs)
+        ex = prep.tables[lv].export()
+        for name in ("lo", "w", "r"):
+            assert np.array_equal(ex[name][layers][:, :, c0:c1].view(np.uint32),
+                                  getattr(tab, name).view(np.uint32)), name
+        assert np.array_equal(ex["freqs"][layers][:, :, c0:c1], tab.freqs)
+        for k in ks:
+            enc = O.encode(shp, Xs, tab, k, k + 1)
+            ref = O.decode(shp, tab, enc)
+            t0, t1 = k * Tc, min((k + 1) * Tc, S)
+            if prep.levels[k] == lv:
+                got = outs[:, :, t0:t1]
+            else:
+                blob = cg.encode(prep.tables[lv], X, k, k + 1)
+                cg.decode(prep.tables[lv], blob, out)
+                got = _u16(out[layers, :, t0:t1, c0:c1].contiguous())
+                del blob
+            assert np.array_equal(got, ref[:, :, t0:t1]), (lv, k)
