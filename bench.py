@@ -111,7 +111,7 @@ def cpu_baseline(w, X, max_threads: int) -> dict:
                       % (list(layers), raw / 1e9, cores, dt)}
 
 
-def streamed_report(dev, n_slots: int = 3, reps: int = 3, seed: int = 0) -> dict:
+def streamed_report(dev, n_slots: int = 8, reps: int = 3, seed: int = 0) -> dict:
     """The 131K-token cache streamed chunk by chunk from pinned host memory, each chunk
     at the level its bandwidth-trace entry allows, decoded while later chunks copy."""
     import numpy as np

@@ -10,7 +10,9 @@ the reference level would take at the trace's mean rate, and takes the finest le
 container meets that deadline at the chunk's own rate, else the coarsest level.
 
 Host logic only: the copies and decodes run in libcg (cg_stream_decode), on two HIP
-streams with 2-3 staging slots.
+streams.  Eight staging slots by default: with only two or three, a copy that must wait
+for the decode freeing its slot leaves the copy engine idle for a while after that
+decode has finished, and the copies no longer run back to back.
 """
 from __future__ import annotations
 
@@ -106,7 +108,7 @@ def prepare(kv: torch.Tensor, group: int, chunk: int, level_bins: Sequence[Seque
     return Prepared(tables, items, levels, sizes, bw, slot)
 
 
-def run(prep: Prepared, out: torch.Tensor, n_slots: int = 3,
+def run(prep: Prepared, out: torch.Tensor, n_slots: int = 8,
         staging: Optional[torch.Tensor] = None) -> dict:
     """Streams every chunk into `out` and returns the event timings."""
     need = n_slots * prep.slot_bytes
