@@ -173,6 +173,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streamed", action="store_true",
                     help="skip the streamed decode of the 131K-token cache")
+    ap.add_argument("--only-streamed", action="store_true",
+                    help="run only the streamed decode of the 131K-token cache (profiling)")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 4 GiB device-to-device copy (counter calibration)")
@@ -202,6 +204,9 @@ def main() -> int:
     w = configs.ALL[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only_streamed:
+        print(json.dumps({"streamed": streamed_report(dev)}), flush=True)
+        return 0
     t = time.time()
     X = synth.gen_kv(w, device=dev)
     out = torch.empty_like(X)
