@@ -28,7 +28,8 @@
  *   - return value: CG_OK or a negative CG_E_* code; cg_last_error() gives a message
  *     (thread-local).  No call throws or aborts.
  *   - limits: 1 <= L, H_kv, d, S; C = H_kv * d a multiple of 8; 1 <= group;
- *     1 <= chunk <= 16384; 2 <= bins[l] <= 32; L * 2 * S * C < 2^40.
+ *     1 <= chunk <= 16384; 2 <= bins[l] <= 32; L * 2 * S * C < 2^40; S * C < 2^32;
+ *     chunk * C * 2 < 2^32 (32-bit offsets within one row of symbols and one chunk).
  */
 #ifndef CG_H
 #define CG_H

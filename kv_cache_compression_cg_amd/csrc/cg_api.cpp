@@ -190,8 +190,10 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     if (p.chunk > CG_MAX_CHUNK) return fail(CG_E_INVAL, "chunk > 16384");
     uint64_t C = (uint64_t)p.H_kv * p.d;
     if (C % 8 != 0) return fail(CG_E_INVAL, "H_kv * d must be a multiple of 8");
+    // 32-bit offsets inside one (layer, K/V) row of symbols and inside one chunk's rows
     if (C >= (1u << 24) || p.S >= (1u << 31) || (uint64_t)p.L * 2 * C >= (1ull << 31) ||
-        (uint64_t)p.L * 2 * p.S * C >= (1ull << 40))
+        (uint64_t)p.L * 2 * p.S * C >= (1ull << 40) || (uint64_t)p.S * C >= (1ull << 32) ||
+        (uint64_t)p.chunk * C * 2 >= (1ull << 32))
         return fail(CG_E_INVAL, "cache too large");
     uint32_t max_bins = 0;
     for (uint32_t l = 0; l < p.L; ++l) {
@@ -299,18 +301,23 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     const uint64_t n_groups = (uint64_t)(ke - kb) * t->L * 2 * t->NB;
     const uint64_t arows = anchor_rows(t, kb, ke);
 
-    DevBuf sym, anc, lane_words, group_words, group_off;
+    // renormalisation ballots of every step of every group, 64 steps per row chunk
+    const uint32_t full = t->Tc < t->S ? t->Tc : t->S;
+    const uint32_t mstride = (full - ceil_div(full, t->G) + 63) / 64 * 64;
+    DevBuf sym, anc, lane_words, group_words, group_off, masks;
     CG_HIP(sym.alloc((uint64_t)t->L * 2 * T_r * t->C), "hipMalloc symbols");
     CG_HIP(anc.alloc(arows * t->C * 2), "hipMalloc anchors");
     CG_HIP(lane_words.alloc(n_groups * kLanes * 4), "hipMalloc");
     CG_HIP(group_words.alloc(n_groups * 8), "hipMalloc");
     CG_HIP(group_off.alloc((n_groups + 1) * 8), "hipMalloc");
+    CG_HIP(masks.alloc(n_groups * (mstride ? mstride : 1) * 8), "hipMalloc ballots");
 
     CG_HIP(launch_k2(static_cast<const uint16_t *>(kv_dev), g, t->d_bins, t->d_lo, t->d_r, t_lo,
                      t_hi, pick_tpt(t, T_r), sym.as<uint8_t>(), t_lo, T_r, anc.as<uint16_t>(), st),
            "k2_delta_quant");
-    CG_HIP(launch_k5_plan(sym.as<uint8_t>(), t_lo, T_r, g, t->d_dtab, lane_words.as<uint32_t>(),
-                          group_words.as<uint64_t>(), n_groups, st),
+    CG_HIP(launch_k5_plan(sym.as<uint8_t>(), t_lo, T_r, g, t->d_bins, t->d_dtab,
+                          lane_words.as<uint32_t>(), group_words.as<uint64_t>(),
+                          masks.as<uint64_t>(), mstride, st),
            "k5_plan");
     CG_HIP(launch_scan(group_words.as<uint64_t>(), group_off.as<uint64_t>(), n_groups, st),
            "scan");
@@ -375,15 +382,13 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     CG_HIP_B(hipMemcpyAsync(base + h.anchors_offset, anc.p, h.anchors_bytes,
                             hipMemcpyDeviceToDevice, st),
              "copy anchors");
-    CG_HIP_B(launch_k5_encode(sym.as<uint8_t>(), t_lo, T_r, g, t->d_dtab,
+    CG_HIP_B(launch_k5_encode(sym.as<uint8_t>(), t_lo, T_r, g, t->d_bins, t->d_dtab,
                               lane_words.as<uint32_t>(), group_off.as<uint64_t>(),
-                              scratch.as<uint16_t>(), n_groups, st),
+                              scratch.as<uint16_t>(), st),
              "k5_encode");
-    CG_HIP_B(launch_k5_interleave(sym.as<uint8_t>(), t_lo, T_r, g, t->d_dtab,
-                                  lane_words.as<uint32_t>(), group_off.as<uint64_t>(),
-                                  scratch.as<uint16_t>(),
-                                  reinterpret_cast<uint16_t *>(base + h.payload_offset), n_groups,
-                                  st),
+    CG_HIP_B(launch_k5_interleave(g, lane_words.as<uint32_t>(), group_off.as<uint64_t>(),
+                                  masks.as<uint64_t>(), mstride, scratch.as<uint16_t>(),
+                                  reinterpret_cast<uint16_t *>(base + h.payload_offset), st),
              "k5_interleave");
     CG_HIP_B(hipStreamSynchronize(st), "hipStreamSynchronize");
 #undef CG_HIP_B

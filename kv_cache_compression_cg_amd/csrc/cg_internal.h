@@ -48,17 +48,18 @@ hipError_t launch_k2(const uint16_t *X, const Geom &g, const uint8_t *bins, cons
                      const float *r, uint32_t t_lo, uint32_t t_hi, uint32_t tpt, uint8_t *sym,
                      uint32_t sym_t0, uint32_t sym_T, uint16_t *anchors, hipStream_t st);
 hipError_t launch_k5_plan(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
-                          const uint32_t *dtab, uint32_t *lane_words, uint64_t *group_words,
-                          uint64_t n_groups, hipStream_t st);
+                          const uint8_t *bins, const uint32_t *dtab, uint32_t *lane_words,
+                          uint64_t *group_words, uint64_t *masks, uint32_t mstride,
+                          hipStream_t st);
 hipError_t launch_scan(const uint64_t *in, uint64_t *out, uint64_t n, hipStream_t st);
 hipError_t launch_k5_encode(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
-                            const uint32_t *dtab, const uint32_t *lane_words,
-                            const uint64_t *group_off, uint16_t *scratch, uint64_t n_groups,
-                            hipStream_t st);
-hipError_t launch_k5_interleave(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T,
-                                const Geom &g, const uint32_t *dtab, const uint32_t *lane_words,
-                                const uint64_t *group_off, const uint16_t *scratch,
-                                uint16_t *payload, uint64_t n_groups, hipStream_t st);
+                            const uint8_t *bins, const uint32_t *dtab,
+                            const uint32_t *lane_words, const uint64_t *group_off,
+                            uint16_t *scratch, hipStream_t st);
+hipError_t launch_k5_interleave(const Geom &g, const uint32_t *lane_words,
+                                const uint64_t *group_off, const uint64_t *masks,
+                                uint32_t mstride, const uint16_t *scratch, uint16_t *payload,
+                                hipStream_t st);
 hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
                      const uint8_t *container, const ContainerView &cv, uint16_t *out,
                      uint8_t *sym_out, hipStream_t st);

@@ -380,13 +380,40 @@ __global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict
     }
 }
 
+// ------------------------------------------------------------------------------ shared
+// Buffer resource over `bytes` bytes at p: loads at or past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             kBufferFlags);
+}
+
+// bytes between the table entries of consecutive symbols of one lane (32 symbols x 64
+// lanes x 4 bytes per plane)
+constexpr uint32_t kSymStride = kLanes * 4;              // bytes between symbols
+
+// v_writelane: lane j of `old` takes the wave-uniform value v (the lane select goes
+// through m0: one instruction may read only one scalar register)
+__device__ __forceinline__ uint32_t write_lane(uint32_t old, uint32_t v, uint32_t j)
+{
+    asm("s_mov_b32 m0, %2\n\tv_writelane_b32 %0, %1, m0" : "+v"(old) : "s"(v), "s"(j) : "m0");
+    return old;
+}
+
 // ------------------------------------------------------------------------------ K5
-// Range encoder, three wave-per-group passes:
-//   plan        replays the range evolution to count each lane's words;
+// Range encoder, three passes over the groups (chunk, row, channel block b); a block
+// holds 4 wavefronts = 4 chunks of one (row, b), sharing that pair's {f | cdf << 16}
+// table plane in LDS, and lane i codes the stream of channel 64b + i.  Symbols are loaded
+// eight steps ahead of their use.
+//   plan        replays the range evolution: counts each lane's words and records the
+//               wavefront's renormalisation ballot of every step;
 //   encode      codes each lane's stream into a lane-major scratch (exact size), carries
 //               rippled back into the words already written;
-//   interleave  replays the evolution again and moves every word to the position the
-//               lockstep decoders will read it from.
+//   interleave  moves every word to the position the lockstep decoders read it from,
+//               following the recorded ballots (no second replay of the coder).
+constexpr uint32_t kSymAhead = 8;
+constexpr uint32_t kEncWaves = 4;
+
 struct GroupCtx {
     uint32_t k, row, b, lane, c, nl, t0, len, ng, m;
     bool present;
@@ -426,37 +453,121 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t mask)
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Symbol i of a lane's stream sits at token t0 + 1 + i + i / (G - 1): anchors are
+// skipped.  Loads go through a buffer resource over the symbol rows of one (layer, K/V),
+// the lane's channel as vector offset and the token row as scalar offset; reads past
+// the rows return 0.
+struct SymFeed {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t voff, C, G1, rel, pos;
+
+    __device__ __forceinline__ void init(const uint8_t *rows, uint32_t bytes, uint32_t c,
+                                         uint32_t C_, uint32_t G, uint32_t t_rel)
+    {
+        rs = make_rsrc(rows, bytes);
+        voff = c;
+        C = C_;
+        G1 = G - 1;
+        rel = t_rel + 1;
+        pos = 0;
+    }
+    // issues the load of the next symbol
+    __device__ __forceinline__ uint32_t next()
+    {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b8(rs, voff, rel * C, 0);
+        rel += 1;
+        if (++pos == G1) {
+            pos = 0;
+            rel += 1;
+        }
+        return v;
+    }
+};
+
+// Block set-up shared by the encoder passes: (row, b, set) from the block index, the
+// P = 2^logp used entries of the table plane staged into LDS.  Returns the chunk of
+// this wavefront.
+__device__ __forceinline__ uint32_t enc_block(const Geom &g, const uint8_t *__restrict__ bins,
+                                              const uint32_t *__restrict__ dtab,
+                                              uint32_t n_sets, uint32_t *tab, uint32_t &row,
+                                              uint32_t &b)
+{
+    const uint32_t set = blockIdx.x % n_sets;
+    const uint32_t tmp = blockIdx.x / n_sets;
+    b = tmp % g.NB;
+    row = tmp / g.NB;
+    const uint32_t N = bins[row >> 1];
+    uint32_t P = 1;
+    while (P < N) P <<= 1;
+    const uint4 *src = reinterpret_cast<const uint4 *>(dtab + (uint64_t)(row * g.NB + b) * kTabBlock);
+    uint4 *dst = reinterpret_cast<uint4 *>(tab);
+    for (uint32_t j = threadIdx.x; j < P * kLanes / 4; j += blockDim.x) dst[j] = src[j];
+    __syncthreads();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    return g.kb + set * kEncWaves + wave;
+}
+
 __global__ __launch_bounds__(256) void k5_plan(const uint8_t *__restrict__ sym, uint32_t sym_t0,
                                                 uint32_t sym_T, Geom g,
+                                                const uint8_t *__restrict__ bins,
                                                 const uint32_t *__restrict__ dtab,
-                                                uint32_t *__restrict__ lane_words,
+                                                uint32_t n_sets, uint32_t *__restrict__ lane_words,
                                                 uint64_t *__restrict__ group_words,
-                                                uint64_t n_groups)
+                                                uint64_t *__restrict__ masks, uint32_t mstride)
 {
-    uint64_t gidx = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) / kLanes;
-    uint32_t lane = threadIdx.x % kLanes;
-    if (gidx >= n_groups) return;
-    GroupCtx x = group_ctx(g, gidx, lane);
+    __shared__ uint32_t tab[kTabPlane];
+    uint32_t row, b;
+    const uint32_t k = enc_block(g, bins, dtab, n_sets, tab, row, b);
+    if (k >= g.ke) return;
+    const uint32_t lane = threadIdx.x % kLanes;
+    const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
+    const GroupCtx x = group_ctx(g, gidx, lane);
     uint32_t words = 0;
-    if (x.present && x.m > 0) {
-        const uint8_t *sp = sym + (uint64_t)x.row * sym_T * g.C + x.c;
-        const uint32_t *tab = dtab + (uint64_t)(x.row * g.NB + x.b) * kTabBlock + lane;
-        uint32_t range = kRangeInit, ev = 0, i = 0;
-        for (uint32_t gi = 0; gi < x.ng; ++gi) {
-            uint32_t ulen = min(g.G, x.len - gi * g.G);
-            for (uint32_t u = 1; u < ulen; ++u) {
-                uint32_t t = x.t0 + gi * g.G + u;
-                uint32_t s = sp[(uint64_t)(t - sym_t0) * g.C];
-                uint32_t f = tab[(uint64_t)s * kLanes] & 0xFFFFu;
-                range = (range >> kProbBits) * f;
-                ++i;
-                if (i < x.m && range < kRenormBelow) {
-                    range <<= 16;
-                    ++ev;
+    if (x.m > 0) {  // uniform
+        SymFeed sf;
+        sf.init(sym + (uint64_t)row * sym_T * g.C, sym_T * g.C, x.present ? x.c : 0, g.C, g.G,
+                x.t0 - sym_t0);
+        const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab) + lane * 4;
+        uint64_t *mrow = masks + gidx * mstride;
+        uint32_t range = kRangeInit, ev = 0, mlo = 0, mhi = 0;
+        // one step: the ballot of step i is kept in lane i % 64 and written every 64 steps
+        auto step = [&](uint32_t i, uint32_t s) __attribute__((always_inline)) {
+            const uint32_t f = *reinterpret_cast<const uint16_t *>(tb + s * kSymStride);
+            range = (range >> kProbBits) * f;
+            const bool need = x.present && i + 1 < x.m && range < kRenormBelow;
+            const uint64_t mask = __builtin_amdgcn_ballot_w64(need);
+            if (need) {
+                range <<= 16;
+                ++ev;
+            }
+            const uint32_t j = i % kLanes;
+            mlo = write_lane(mlo, (uint32_t)mask, j);
+            mhi = write_lane(mhi, (uint32_t)(mask >> 32), j);
+            if (j == kLanes - 1 || i + 1 == x.m) {
+                if (lane <= j) {
+                    uint2 v;
+                    v.x = mlo;
+                    v.y = mhi;
+                    *reinterpret_cast<uint2 *>(mrow + (i - j) + lane) = v;
                 }
             }
+        };
+        uint32_t sr[kSymAhead];
+#pragma unroll
+        for (uint32_t r = 0; r < kSymAhead; ++r) sr[r] = sf.next();
+        uint32_t i = 0;
+        for (; i + kSymAhead <= x.m; i += kSymAhead) {
+#pragma unroll
+            for (uint32_t r = 0; r < kSymAhead; ++r) {
+                const uint32_t s_ = sr[r];
+                sr[r] = sf.next();
+                step(i + r, s_);
+            }
         }
-        words = 2 + ev;
+#pragma unroll
+        for (uint32_t r = 0; r < kSymAhead; ++r)
+            if (i + r < x.m) step(i + r, sr[r]);
+        if (x.present) words = 2 + ev;
     }
     lane_words[gidx * kLanes + lane] = words;
     uint32_t tot = words;
@@ -493,113 +604,132 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *__restrict__ in,
 
 __global__ __launch_bounds__(256) void k5_encode(const uint8_t *__restrict__ sym, uint32_t sym_t0,
                                                   uint32_t sym_T, Geom g,
+                                                  const uint8_t *__restrict__ bins,
                                                   const uint32_t *__restrict__ dtab,
+                                                  uint32_t n_sets,
                                                   const uint32_t *__restrict__ lane_words,
                                                   const uint64_t *__restrict__ group_off,
-                                                  uint16_t *__restrict__ scratch, uint64_t n_groups)
+                                                  uint16_t *__restrict__ scratch)
 {
-    uint64_t gidx = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) / kLanes;
-    uint32_t lane = threadIdx.x % kLanes;
-    if (gidx >= n_groups) return;
-    GroupCtx x = group_ctx(g, gidx, lane);
-    uint32_t nwords = lane_words[gidx * kLanes + lane];
-    uint32_t lane_off = wave_excl_scan(nwords, lane);
-    if (!x.present || x.m == 0) return;
+    __shared__ uint32_t tab[kTabPlane];
+    uint32_t row, b;
+    const uint32_t k = enc_block(g, bins, dtab, n_sets, tab, row, b);
+    if (k >= g.ke) return;
+    const uint32_t lane = threadIdx.x % kLanes;
+    const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
+    const GroupCtx x = group_ctx(g, gidx, lane);
+    const uint32_t nwords = lane_words[gidx * kLanes + lane];
+    const uint32_t lane_off = wave_excl_scan(nwords, lane);
+    if (x.m == 0) return;  // uniform
     uint16_t *out = scratch + group_off[gidx] + lane_off;
-    const uint8_t *sp = sym + (uint64_t)x.row * sym_T * g.C + x.c;
-    const uint32_t *tab = dtab + (uint64_t)(x.row * g.NB + x.b) * kTabBlock + lane;
+    SymFeed sf;
+    sf.init(sym + (uint64_t)row * sym_T * g.C, sym_T * g.C, x.present ? x.c : 0, g.C, g.G,
+            x.t0 - sym_t0);
+    const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab) + lane * 4;
     uint64_t low = 0;
-    uint32_t range = kRangeInit, nw = 0, i = 0;
-    for (uint32_t gi = 0; gi < x.ng; ++gi) {
-        uint32_t ulen = min(g.G, x.len - gi * g.G);
-        for (uint32_t u = 1; u < ulen; ++u) {
-            uint32_t t = x.t0 + gi * g.G + u;
-            uint32_t s = sp[(uint64_t)(t - sym_t0) * g.C];
-            uint32_t e = tab[(uint64_t)s * kLanes];
-            uint32_t q = range >> kProbBits;
-            low += (uint64_t)q * (e >> 16);
-            range = q * (e & 0xFFFFu);
-            if (low >> 32) {  // carry into the words already written
-                low &= 0xFFFFFFFFull;
-                uint32_t j = nw;
-                uint16_t v;
-                do {
-                    --j;
-                    v = (uint16_t)(out[j] + 1u);
-                    out[j] = v;
-                } while (v == 0 && j > 0);
-            }
-            ++i;
-            if (i < x.m && range < kRenormBelow) {
-                out[nw++] = (uint16_t)(low >> 16);
-                low = (low & 0xFFFFull) << 16;
-                range <<= 16;
+    uint32_t range = kRangeInit, nw = 0;
+    auto step = [&](uint32_t i, uint32_t s) __attribute__((always_inline)) {
+        const uint32_t e = *reinterpret_cast<const uint32_t *>(tb + s * kSymStride);
+        const uint32_t q = range >> kProbBits;
+        low += (uint64_t)q * (e >> 16);
+        range = q * (e & 0xFFFFu);
+        if (low >> 32) {  // carry into the words already written
+            low &= 0xFFFFFFFFull;
+            uint32_t j = nw;
+            uint16_t v;
+            do {
+                --j;
+                v = (uint16_t)(out[j] + 1u);
+                out[j] = v;
+            } while (v == 0 && j > 0);
+        }
+        if (i + 1 < x.m && range < kRenormBelow) {
+            out[nw++] = (uint16_t)(low >> 16);
+            low = (low & 0xFFFFull) << 16;
+            range <<= 16;
+        }
+    };
+    uint32_t sr[kSymAhead];
+#pragma unroll
+    for (uint32_t r = 0; r < kSymAhead; ++r) sr[r] = sf.next();
+    uint32_t i = 0;
+    if (x.present) {
+        for (; i + kSymAhead <= x.m; i += kSymAhead) {
+#pragma unroll
+            for (uint32_t r = 0; r < kSymAhead; ++r) {
+                const uint32_t s_ = sr[r];
+                sr[r] = sf.next();
+                step(i + r, s_);
             }
         }
+#pragma unroll
+        for (uint32_t r = 0; r < kSymAhead; ++r)
+            if (i + r < x.m) step(i + r, sr[r]);
+        out[nw++] = (uint16_t)(low >> 16);
+        out[nw++] = (uint16_t)(low & 0xFFFFu);
     }
-    out[nw++] = (uint16_t)(low >> 16);
-    out[nw++] = (uint16_t)(low & 0xFFFFu);
 }
 
-__global__ __launch_bounds__(256) void k5_interleave(const uint8_t *__restrict__ sym,
-                                                      uint32_t sym_t0, uint32_t sym_T, Geom g,
-                                                      const uint32_t *__restrict__ dtab,
+__global__ __launch_bounds__(256) void k5_interleave(Geom g, uint32_t n_sets,
                                                       const uint32_t *__restrict__ lane_words,
                                                       const uint64_t *__restrict__ group_off,
+                                                      const uint64_t *__restrict__ masks,
+                                                      uint32_t mstride,
                                                       const uint16_t *__restrict__ scratch,
-                                                      uint16_t *__restrict__ payload,
-                                                      uint64_t n_groups)
+                                                      uint16_t *__restrict__ payload)
 {
-    uint64_t gidx = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) / kLanes;
-    uint32_t lane = threadIdx.x % kLanes;
-    if (gidx >= n_groups) return;
-    GroupCtx x = group_ctx(g, gidx, lane);
-    uint32_t nwords = lane_words[gidx * kLanes + lane];
-    uint32_t lane_off = wave_excl_scan(nwords, lane);
-    if (x.m == 0) return;  // uniform over the wave
+    const uint32_t set = blockIdx.x % n_sets;
+    const uint32_t tmp = blockIdx.x / n_sets;
+    const uint32_t b = tmp % g.NB;
+    const uint32_t row = tmp / g.NB;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const uint32_t k = g.kb + set * kEncWaves + wave;
+    if (k >= g.ke) return;
+    const uint32_t lane = threadIdx.x % kLanes;
+    const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
+    const GroupCtx x = group_ctx(g, gidx, lane);
+    const uint32_t nwords = lane_words[gidx * kLanes + lane];
+    const uint32_t lane_off = wave_excl_scan(nwords, lane);
+    if (x.m == 0) return;  // uniform
     const uint16_t *src = scratch + group_off[gidx] + lane_off;
     uint16_t *dst = payload + group_off[gidx];
+    uint32_t e = 2, w_next = 0;
     if (x.present) {
         dst[2 * lane] = src[0];
         dst[2 * lane + 1] = src[1];
+        if (nwords > 2) w_next = src[2];
     }
-    uint32_t cursor = 2 * x.nl, e = 2, range = kRangeInit, i = 0;
-    const uint8_t *sp = sym + (uint64_t)x.row * sym_T * g.C + (x.present ? x.c : 0);
-    const uint32_t *tab = dtab + (uint64_t)(x.row * g.NB + x.b) * kTabBlock + lane;
-    for (uint32_t gi = 0; gi < x.ng; ++gi) {
-        uint32_t ulen = min(g.G, x.len - gi * g.G);
-        for (uint32_t u = 1; u < ulen; ++u) {
-            uint32_t t = x.t0 + gi * g.G + u;
-            bool need = false;
-            ++i;
-            if (x.present) {
-                uint32_t s = sp[(uint64_t)(t - sym_t0) * g.C];
-                uint32_t f = tab[(uint64_t)s * kLanes] & 0xFFFFu;
-                range = (range >> kProbBits) * f;
-                need = (i < x.m) && (range < kRenormBelow);
+    const uint64_t *mrow = masks + gidx * mstride;
+    uint32_t cursor = 2 * x.nl;
+    for (uint32_t base = 0; base < x.m; base += kLanes) {
+        // the ballots of steps base .. base + 63, one per lane
+        uint2 mm = make_uint2(0, 0);
+        if (base + lane < x.m) mm = *reinterpret_cast<const uint2 *>(mrow + base + lane);
+        const uint32_t n = min(kLanes, x.m - base);
+        for (uint32_t j = 0; j < n; ++j) {
+            // (readlane returns a signed int: go through uint32_t, no sign extension)
+            const uint32_t mlo = (uint32_t)__builtin_amdgcn_readlane(mm.x, j);
+            const uint32_t mhi = (uint32_t)__builtin_amdgcn_readlane(mm.y, j);
+            const uint64_t mask = ((uint64_t)mhi << 32) | mlo;
+            if (mask) {
+                if ((mask >> lane) & 1u) {
+                    dst[cursor + mbcnt64(mask)] = (uint16_t)w_next;
+                    ++e;
+                    if (e < nwords) w_next = src[e];
+                }
+                cursor += (uint32_t)__builtin_popcountll(mask);
             }
-            uint64_t mask = __ballot(need);
-            if (need) {
-                dst[cursor + mbcnt64(mask)] = src[e++];
-                range <<= 16;
-            }
-            cursor += (uint32_t)__popcll(mask);
         }
     }
 }
 
+
 // ------------------------------------------------------------------------------ K3 (+K4)
-// Range decoder, one wavefront per group, fused with dequantize + anchor-add.
-// Block = 4 wavefronts = 4 consecutive chunks of the same (row, block), sharing the
-// block's decode table in LDS (P <= 32 entries x 64 lanes x 8 bytes).  Everything that
-// is the same for the 64 lanes (chunk, token, group, stream cursor, row addresses) is
-// kept in scalar registers; only the coder state and the table address are per lane.
-// Buffer resource over `bytes` bytes at p: loads at or past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
-                                             kBufferFlags);
-}
+// Range decoder fused with dequantize + anchor-add.  Block = 4 wavefronts, each decoding
+// two chunks of the same (row, block) in lockstep, all sharing the block's decode table
+// in LDS (P <= 32 entries x 64 lanes x 8 bytes).  Everything that is the same for the
+// 64 lanes (chunk, token, group, stream cursor, row addresses) is kept in scalar
+// registers; only the coder state and the table address are per lane.
 
 // Per-wavefront LDS ring of payload words (stored inverted, see below), refilled with
 // 4-byte-per-lane loads.  Ring slots [0, 64) are mirrored at [R, R + 64), so the up-to-
@@ -630,7 +760,6 @@ __device__ __forceinline__ void ring_put(uint16_t *ring, uint32_t pos, uint32_t 
 // (cdf in the upper half, read zero-extended by the search) and the dequantized delta
 // 8 KiB further: a lane's probe never conflicts with
 // another lane's, whatever symbols the lanes are at.
-constexpr uint32_t kSymStride = kLanes * 4;              // bytes between symbols
 constexpr uint32_t kDqOffset = kTabPlane * 4;            // byte offset of the delta plane
 
 // p + (d < 0 ? STEP : 0) for a power-of-two STEP, as a shift and a shift-add.  (Written
@@ -1196,13 +1325,17 @@ hipError_t launch_k2(const uint16_t *X, const Geom &g, const uint8_t *bins, cons
     return hipGetLastError();
 }
 
+static uint32_t enc_sets(const Geom &g) { return (g.ke - g.kb + kEncWaves - 1) / kEncWaves; }
+
 hipError_t launch_k5_plan(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
-                          const uint32_t *dtab, uint32_t *lane_words, uint64_t *group_words,
-                          uint64_t n_groups, hipStream_t st)
+                          const uint8_t *bins, const uint32_t *dtab, uint32_t *lane_words,
+                          uint64_t *group_words, uint64_t *masks, uint32_t mstride,
+                          hipStream_t st)
 {
-    uint64_t blocks = (n_groups + 3) / 4;
+    const uint32_t n_sets = enc_sets(g);
+    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
     hipLaunchKernelGGL(k5_plan, dim3((uint32_t)blocks), dim3(256), 0, st, sym, sym_t0, sym_T, g,
-                       dtab, lane_words, group_words, n_groups);
+                       bins, dtab, n_sets, lane_words, group_words, masks, mstride);
     return hipGetLastError();
 }
 
@@ -1213,24 +1346,26 @@ hipError_t launch_scan(const uint64_t *in, uint64_t *out, uint64_t n, hipStream_
 }
 
 hipError_t launch_k5_encode(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
-                            const uint32_t *dtab, const uint32_t *lane_words,
-                            const uint64_t *group_off, uint16_t *scratch, uint64_t n_groups,
-                            hipStream_t st)
+                            const uint8_t *bins, const uint32_t *dtab,
+                            const uint32_t *lane_words, const uint64_t *group_off,
+                            uint16_t *scratch, hipStream_t st)
 {
-    uint64_t blocks = (n_groups + 3) / 4;
+    const uint32_t n_sets = enc_sets(g);
+    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
     hipLaunchKernelGGL(k5_encode, dim3((uint32_t)blocks), dim3(256), 0, st, sym, sym_t0, sym_T, g,
-                       dtab, lane_words, group_off, scratch, n_groups);
+                       bins, dtab, n_sets, lane_words, group_off, scratch);
     return hipGetLastError();
 }
 
-hipError_t launch_k5_interleave(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T,
-                                const Geom &g, const uint32_t *dtab, const uint32_t *lane_words,
-                                const uint64_t *group_off, const uint16_t *scratch,
-                                uint16_t *payload, uint64_t n_groups, hipStream_t st)
+hipError_t launch_k5_interleave(const Geom &g, const uint32_t *lane_words,
+                                const uint64_t *group_off, const uint64_t *masks,
+                                uint32_t mstride, const uint16_t *scratch, uint16_t *payload,
+                                hipStream_t st)
 {
-    uint64_t blocks = (n_groups + 3) / 4;
-    hipLaunchKernelGGL(k5_interleave, dim3((uint32_t)blocks), dim3(256), 0, st, sym, sym_t0,
-                       sym_T, g, dtab, lane_words, group_off, scratch, payload, n_groups);
+    const uint32_t n_sets = enc_sets(g);
+    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
+    hipLaunchKernelGGL(k5_interleave, dim3((uint32_t)blocks), dim3(256), 0, st, g, n_sets,
+                       lane_words, group_off, masks, mstride, scratch, payload);
     return hipGetLastError();
 }
 
