@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, vendor figure
 METRIC = "cg_decode GB/s of raw fp16 KV reconstructed (% HBM peak); compression ratio"
-CPU_SAMPLE_LAYERS = (0, 10, 20, 30, 40, 50, 60, 70)   # bin tiers 32:16:8 in the ratio 2:2:4
+CPU_SAMPLE_LAYERS = tuple(range(0, 80, 5))   # 16 layers; bin tiers 32:16:8 in the ratio 2:2:4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k3_decode_llama3_70b_traffic.json")
 
 

@@ -53,6 +53,14 @@ def test_validation_without_device(lib):
     assert lib.cg_build_cdf(ctypes.byref(p), ctypes.c_void_p(16), None, ctypes.byref(h)) == -1
     p = cg.Params(2, 1, 8, 16, 4, 20000, ctypes.cast(bins, ctypes.POINTER(ctypes.c_uint8)))
     assert lib.cg_build_cdf(ctypes.byref(p), ctypes.c_void_p(16), None, ctypes.byref(h)) == -1
+    # one (layer, K/V) row of symbols and one chunk's rows must fit 32-bit offsets
+    one = (ctypes.c_uint8 * 1)(8)
+    p = cg.Params(1, 1, 8192, 1 << 19, 10, 1024, ctypes.cast(one, ctypes.POINTER(ctypes.c_uint8)))
+    assert lib.cg_build_cdf(ctypes.byref(p), ctypes.c_void_p(16), None, ctypes.byref(h)) == -1
+    assert b"too large" in lib.cg_last_error()
+    p = cg.Params(1, 1, 1 << 17, 1 << 14, 10, 1 << 14, ctypes.cast(one, ctypes.POINTER(ctypes.c_uint8)))
+    assert lib.cg_build_cdf(ctypes.byref(p), ctypes.c_void_p(16), None, ctypes.byref(h)) == -1
+    assert b"too large" in lib.cg_last_error()
     assert lib.cg_encode(None, None, 0, 1, None, ctypes.byref(h)) == -1
     assert lib.cg_decode(None, None, None, None, None) == -1
     assert lib.cg_quantize(None, None, 0, 1, None, None) == -1
