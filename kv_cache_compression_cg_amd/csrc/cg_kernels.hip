@@ -1166,10 +1166,12 @@ __device__ __forceinline__ void decode_dispatch(uint32_t logp, bool pair, const 
 #undef CG_DECODE_CASE
 }
 
-// Block = 4 wavefronts over the chunks [kb + 8 * set, kb + 8 * set + 8) of one (row,
-// channel block); wavefront w takes chunks base + w and base + w + 4.
-template <bool SYMBOLS>
-__global__ __launch_bounds__(256) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
+// Block = WPB wavefronts over the chunks [kb + 2 WPB set, kb + 2 WPB (set + 1)) of one
+// (row, channel block); wavefront w takes chunks base + w and base + w + WPB.  Launches
+// over many chunks use 4 wavefronts per block, sharing the staged table; launches over
+// a few chunks (a streamed chunk) use 1, so that more blocks are resident.
+template <bool SYMBOLS, uint32_t WPB>
+__global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
                                                   const uint32_t *__restrict__ dtab,
                                                   const uint8_t *__restrict__ container,
                                                   ContainerView cv, uint32_t n_sets,
@@ -1177,7 +1179,7 @@ __global__ __launch_bounds__(256) void k3_decode(Geom g, const uint8_t *__restri
                                                   uint8_t *__restrict__ sym_out)
 {
     __shared__ uint32_t tab[kTabBlock];
-    __shared__ uint16_t rings[kWavesPerBlock * kStreamsPerWave * kRingAlloc];
+    __shared__ uint16_t rings[WPB * kStreamsPerWave * kRingAlloc];
     const uint32_t set = blockIdx.x % n_sets;
     const uint32_t tmp = blockIdx.x / n_sets;
     const uint32_t b = tmp % g.NB;
@@ -1196,8 +1198,8 @@ __global__ __launch_bounds__(256) void k3_decode(Geom g, const uint8_t *__restri
     __syncthreads();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     const uint32_t lane = threadIdx.x % kLanes;
-    const uint32_t k0 = g.kb + set * kWavesPerBlock * kStreamsPerWave + wave;
-    const uint32_t k1 = k0 + kWavesPerBlock;
+    const uint32_t k0 = g.kb + set * WPB * kStreamsPerWave + wave;
+    const uint32_t k1 = k0 + WPB;
     if (k0 >= g.ke) return;
     const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab);
     uint16_t *ring = rings + wave * kStreamsPerWave * kRingAlloc;
@@ -1373,15 +1375,28 @@ hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
                      const uint8_t *container, const ContainerView &cv, uint16_t *out,
                      uint8_t *sym_out, hipStream_t st)
 {
-    const uint32_t per_block = kWavesPerBlock * kStreamsPerWave;
-    uint32_t n_sets = (g.ke - g.kb + per_block - 1) / per_block;
-    uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
-    if (sym_out)
-        hipLaunchKernelGGL(k3_decode<true>, dim3((uint32_t)blocks), dim3(256), 0, st, g, bins,
-                           dtab, container, cv, n_sets, out, sym_out);
-    else
-        hipLaunchKernelGGL(k3_decode<false>, dim3((uint32_t)blocks), dim3(256), 0, st, g, bins,
-                           dtab, container, cv, n_sets, out, sym_out);
+    // fewer than 8 chunks: one wavefront per block (see k3_decode)
+    const bool wide = g.ke - g.kb >= kWavesPerBlock * kStreamsPerWave;
+    const uint32_t wpb = wide ? kWavesPerBlock : 1u;
+    const uint32_t per_block = wpb * kStreamsPerWave;
+    const uint32_t n_sets = (g.ke - g.kb + per_block - 1) / per_block;
+    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
+    const dim3 grid((uint32_t)blocks), block(wpb * kLanes);
+    if (sym_out) {
+        if (wide)
+            hipLaunchKernelGGL((k3_decode<true, kWavesPerBlock>), grid, block, 0, st, g, bins,
+                               dtab, container, cv, n_sets, out, sym_out);
+        else
+            hipLaunchKernelGGL((k3_decode<true, 1>), grid, block, 0, st, g, bins, dtab,
+                               container, cv, n_sets, out, sym_out);
+    } else {
+        if (wide)
+            hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock>), grid, block, 0, st, g, bins,
+                               dtab, container, cv, n_sets, out, sym_out);
+        else
+            hipLaunchKernelGGL((k3_decode<false, 1>), grid, block, 0, st, g, bins, dtab,
+                               container, cv, n_sets, out, sym_out);
+    }
     return hipGetLastError();
 }
 
