@@ -126,7 +126,8 @@ def streamed_report(dev, n_slots: int = 8, reps: int = 3, seed: int = 0) -> dict
     log("[streamed] %s: %d chunks encoded at %d levels, chosen containers in pinned memory "
         "(%.1fs)" % (w.name, w.n_chunks, len(w.levels), time.time() - t))
     out = torch.empty_like(X)
-    runs = [streamed.run(prep, out, n_slots=n_slots) for _ in range(reps + 1)][1:]
+    pipe = streamed.Pipeline(prep, dev, n_slots)
+    runs = [streamed.run(prep, out, n_slots=n_slots, pipe=pipe) for _ in range(reps + 1)][1:]
     tt = torch.arange(w.S, device=dev)
     anchor = ((tt % w.chunk) % w.group) == 0
     assert torch.equal(out[:, :, anchor].view(torch.int16), X[:, :, anchor].view(torch.int16))
@@ -159,7 +160,7 @@ def streamed_report(dev, n_slots: int = 8, reps: int = 3, seed: int = 0) -> dict
         "%.1f GB/s, overlap %.2f), ratio %.3f"
         % (res["end_to_end_GBps"], res["h2d_GBps"], res["decode_only_GBps"], res["overlap"],
            res["compression_ratio"]))
-    del prep, out, X
+    del prep, out, X, pipe
     torch.cuda.empty_cache()
     return res
 

@@ -489,15 +489,22 @@ int cg_stream_decode(const cg_stream_item *items, uint32_t n_items, void *stagin
     hipError_t err = hipSuccess;
     const char *what = "";
     uint64_t bytes = 0;
+    const uint32_t batch = n_slots > 1 ? n_slots / 2 : 1;
     for (uint32_t i = 0; i < n_items && err == hipSuccess; ++i) {
         const cg_stream_item &it = items[i];
         const uint32_t j = i % n_slots;
         uint8_t *slot = static_cast<uint8_t *>(staging_dev) + (uint64_t)j * slot_bytes;
         const uint64_t nb = it.blob->hdr.total_bytes;
         hipEvent_t *ie = stats ? item_ev.ev.data() + 4 * (size_t)i : nullptr;
-        if (i >= n_slots && (err = hipStreamWaitEvent(cs, freed[j], 0)) != hipSuccess) {
-            what = "hipStreamWaitEvent";
-            break;
+        // slot reuse: one wait per `batch` items, on the decode of the last item whose
+        // slot the next `batch` items take (decodes finish in order, so that event covers
+        // the earlier ones).  A wait per copy leaves the copy engine idle between copies.
+        if (i >= n_slots && (i - n_slots) % batch == 0) {
+            const uint32_t last = i - n_slots + batch - 1;
+            if ((err = hipStreamWaitEvent(cs, freed[last % n_slots], 0)) != hipSuccess) {
+                what = "hipStreamWaitEvent";
+                break;
+            }
         }
         if (ie && (err = hipEventRecord(ie[0], cs)) != hipSuccess) { what = "hipEventRecord"; break; }
         if ((err = hipMemcpyAsync(slot, it.host_container, nb, hipMemcpyHostToDevice, cs)) !=

@@ -108,17 +108,26 @@ def prepare(kv: torch.Tensor, group: int, chunk: int, level_bins: Sequence[Seque
     return Prepared(tables, items, levels, sizes, bw, slot)
 
 
+class Pipeline:
+    """Staging slots and the copy / decode streams, made once and reused: a stream's
+    first use and a fresh allocation would otherwise fall inside the timed run."""
+
+    def __init__(self, prep: Prepared, device, n_slots: int = 8):
+        self.n_slots = n_slots
+        self.staging = torch.empty(n_slots * prep.slot_bytes, dtype=torch.uint8, device=device)
+        self.copy_stream = torch.cuda.Stream(device=device)
+        self.decode_stream = torch.cuda.Stream(device=device)
+
+
 def run(prep: Prepared, out: torch.Tensor, n_slots: int = 8,
-        staging: Optional[torch.Tensor] = None) -> dict:
+        pipe: Optional[Pipeline] = None) -> dict:
     """Streams every chunk into `out` and returns the event timings."""
-    need = n_slots * prep.slot_bytes
-    if staging is None or staging.numel() < need:
-        staging = torch.empty(need, dtype=torch.uint8, device=out.device)
-    copy_stream = torch.cuda.Stream(device=out.device)
-    decode_stream = torch.cuda.Stream(device=out.device)
+    if pipe is None or pipe.staging.numel() < n_slots * prep.slot_bytes:
+        pipe = Pipeline(prep, out.device, n_slots)
     # the output and staging memory come from torch's current stream
-    copy_stream.wait_stream(torch.cuda.current_stream(out.device))
-    decode_stream.wait_stream(torch.cuda.current_stream(out.device))
-    stats = cg.stream_decode(prep.items, staging[:need], n_slots, out, copy_stream,
-                             decode_stream, wait=True)
+    cur = torch.cuda.current_stream(out.device)
+    pipe.copy_stream.wait_stream(cur)
+    pipe.decode_stream.wait_stream(cur)
+    stats = cg.stream_decode(prep.items, pipe.staging[:n_slots * prep.slot_bytes], n_slots, out,
+                             pipe.copy_stream, pipe.decode_stream, wait=True)
     return stats
