@@ -182,7 +182,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the codec runs on a single MI355X "
-              "(multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+              "(sharding across GPUs is not built)", file=sys.stderr)
         return 2
 
     import torch
