@@ -137,3 +137,35 @@ def test_streamed_131k_sampled(cg):
                 got = _u16(out[layers, :, t0:t1, c0:c1].contiguous())
                 del blob
             assert np.array_equal(got, ref[:, :, t0:t1]), (lv, k)
+
+
+def test_stream_decode_rejects_bad_items(cg):
+    """Checked before anything is queued: mixed shapes, a slot too small, misaligned
+    staging memory."""
+    X = synth.gen_custom(2, 600, 64, HEAVY, device="cuda")
+    Y = synth.gen_custom(2, 700, 64, HEAVY, device="cuda")
+    tx = cg.build_cdf(X, 10, 200, (8, 4), H_kv=1)
+    ty = cg.build_cdf(Y, 10, 200, (8, 4), H_kv=1)
+    bx = cg.encode(tx, X, 0, 1)
+    by = cg.encode(ty, Y, 0, 1)
+    hx = torch.from_numpy(bx.read().copy())
+    hy = torch.from_numpy(by.read().copy())
+    slot = (max(bx.nbytes, by.nbytes) + 255) // 256 * 256
+    staging = torch.empty(2 * slot + 256, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(X)
+    cs, ds = torch.cuda.Stream(), torch.cuda.Stream()
+    with pytest.raises(cg.CgError) as e:
+        cg.stream_decode([(tx, bx, hx), (ty, by, hy)], staging[:2 * slot], 2, out, cs, ds)
+    assert e.value.code == -1
+    with pytest.raises(cg.CgError) as e:
+        cg.stream_decode([(tx, bx, hx)], staging[:2 * 256], 2, out, cs, ds)
+    assert e.value.code == -1 and "slot" in str(e.value)
+    with pytest.raises(cg.CgError) as e:
+        cg.stream_decode([(tx, bx, hx)], staging[16:16 + 2 * slot], 2, out, cs, ds)
+    assert e.value.code == -1 and "aligned" in str(e.value)
+    # and the valid call decodes chunk 0 as cg_decode does
+    ref = cg.decode(tx, bx)
+    got = torch.zeros_like(X)
+    cg.stream_decode([(tx, bx, hx)], staging[:2 * slot], 2, got, cs, ds)
+    torch.cuda.synchronize()
+    assert torch.equal(got[:, :, :200].view(torch.int16), ref[:, :, :200].view(torch.int16))
