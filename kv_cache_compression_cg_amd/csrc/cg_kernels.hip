@@ -392,14 +392,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 // lanes x 4 bytes per plane)
 constexpr uint32_t kSymStride = kLanes * 4;              // bytes between symbols
 
-// v_writelane: lane j of `old` takes the wave-uniform value v (the lane select goes
-// through m0: one instruction may read only one scalar register)
-__device__ __forceinline__ uint32_t write_lane(uint32_t old, uint32_t v, uint32_t j)
-{
-    asm("s_mov_b32 m0, %2\n\tv_writelane_b32 %0, %1, m0" : "+v"(old) : "s"(v), "s"(j) : "m0");
-    return old;
-}
-
 // ------------------------------------------------------------------------------ K5
 // Range encoder, three passes over the groups (chunk, row, channel block b); a block
 // holds 4 wavefronts = 4 chunks of one (row, b), sharing that pair's {f | cdf << 16}
@@ -541,8 +533,10 @@ __global__ __launch_bounds__(256) void k5_plan(const uint8_t *__restrict__ sym, 
                 ++ev;
             }
             const uint32_t j = i % kLanes;
-            mlo = write_lane(mlo, (uint32_t)mask, j);
-            mhi = write_lane(mhi, (uint32_t)(mask >> 32), j);
+            if (lane == j) {
+                mlo = (uint32_t)mask;
+                mhi = (uint32_t)(mask >> 32);
+            }
             if (j == kLanes - 1 || i + 1 == x.m) {
                 if (lane <= j) {
                     uint2 v;
