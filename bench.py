@@ -44,8 +44,12 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "kv_cache_compression_cg_amd", "csrc", "cg_kernels.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the sources the decode kernel is built from."""
+    csrc = os.path.join(ROOT, "kv_cache_compression_cg_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ("cg_kernels_decode.hip", "cg_device.h", "cg_internal.h"):
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def table_bytes_read(tables) -> int:

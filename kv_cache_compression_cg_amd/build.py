@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIB_DIR, "libcg.so")
-SOURCES = [os.path.join(CSRC, "cg_kernels.hip"), os.path.join(CSRC, "cg_api.cpp")]
+SOURCES = [os.path.join(CSRC, "cg_kernels_encode.hip"), os.path.join(CSRC, "cg_kernels_decode.hip"),
+           os.path.join(CSRC, "cg_api.cpp")]
 ARCH = os.environ.get("CG_OFFLOAD_ARCH", "gfx950")
 
 

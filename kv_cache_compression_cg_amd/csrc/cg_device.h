@@ -1,0 +1,137 @@
+// cg_device.h -- device helpers and layout conventions shared by the encoder and decoder
+// kernels of the KV-cache codec (see include/cg.h).
+////
+// Layout conventions shared by every kernel:
+//   * KV caches are fp16 [L][2][S][C]; "row" means (layer, K/V) = l * 2 + kv.
+//   * A "group" is (chunk, row, block b) with its 64 lanes = channels 64b .. 64b+63.
+//     One wavefront decodes one group: lane i owns the stream of channel 64b + i,
+//     all lanes step through the same token at the same time, so every output row
+//     is written as one contiguous 128-byte store and the interleaved words of the
+//     group are read from a contiguous, advancing window.
+//   * Decode table entry (8 bytes) of symbol s for a lane: {f[s] | cdf[s] << 16,
+//     dequantized delta lo + s * w as fp32 bits}, two planes [32][64 lanes] per
+//     (row, block), so that all 64 lanes reading entry s of their own channel hit
+//     64 different LDS banks whatever s each lane holds.
+//
+// Float rules (bit-exact with the CPU oracle): -ffp-contract=off, fp32 division and
+// reciprocal correctly rounded (HIP default), fmaf only where written, fp16 output
+// converted round-to-nearest-even.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cstdint>
+
+#include "cg_internal.h"
+
+namespace cgk {
+
+// ------------------------------------------------------------------------------ helpers
+__device__ __forceinline__ float h2f(uint32_t h) { return __half2float(__ushort_as_half((unsigned short)h)); }
+__device__ __forceinline__ uint32_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
+
+// unsigned image of a float that orders like the float (for atomic min / max)
+__device__ __forceinline__ uint32_t f2ord(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord2f(uint32_t o)
+{
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ bool any_nonfinite(uint4 v)
+{
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bad |= (w[i] & 0x7C00u) == 0x7C00u;
+        bad |= (w[i] & 0x7C000000u) == 0x7C000000u;
+    }
+    return bad;
+}
+
+__device__ __forceinline__ void unpack8(uint4 v, float f[8])
+{
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = h2f(w[i] & 0xFFFFu);
+        f[2 * i + 1] = h2f(w[i] >> 16);
+    }
+}
+
+// q = clamp(floor(fma(delta - lo, r, 0.5)), 0, N - 1)
+__device__ __forceinline__ uint32_t quantize1(float delta, float lo, float r, uint32_t N)
+{
+    float v = floorf(fmaf(delta - lo, r, 0.5f));
+    if (!(v > 0.0f)) return 0;
+    if (v > (float)(N - 1u)) return N - 1u;
+    return (uint32_t)v;
+}
+
+__device__ __forceinline__ uint32_t chunk_len(const Geom &g, uint32_t k)
+{
+    uint32_t t0 = k * g.Tc;
+    return (g.S - t0 < g.Tc) ? g.S - t0 : g.Tc;
+}
+
+// Walks tokens [t, t_end) keeping the chunk / group position without divisions.
+struct TokenWalk {
+    uint32_t t, u, gp, gi, k;  // token, offset in chunk, offset in group, group in chunk, chunk
+    __device__ void init(const Geom &g, uint32_t t_start)
+    {
+        t = t_start;
+        k = t / g.Tc;
+        u = t - k * g.Tc;
+        gi = u / g.G;
+        gp = u - gi * g.G;
+    }
+    __device__ void next(const Geom &g)
+    {
+        ++t;
+        ++u;
+        if (u == g.Tc) {
+            u = 0;
+            gp = 0;
+            gi = 0;
+            ++k;
+        } else if (++gp == g.G) {
+            gp = 0;
+            ++gi;
+        }
+    }
+};
+
+// Row of the anchors section holding (chunk k, row, group gi); chunks before k in the
+// range are full (only the last chunk of a cache can be short).
+__device__ __forceinline__ uint64_t anchor_row(const Geom &g, uint32_t k, uint32_t row, uint32_t gi)
+{
+    uint32_t len = chunk_len(g, k);
+    uint32_t ng = (len + g.G - 1) / g.G;
+    return (uint64_t)(k - g.kb) * g.L * 2 * g.ngF + (uint64_t)row * ng + gi;
+}
+
+// ------------------------------------------------------------------------------ shared
+// Buffer resource over `bytes` bytes at p: loads at or past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             kBufferFlags);
+}
+
+// bytes between the table entries of consecutive symbols of one lane (32 symbols x 64
+// lanes x 4 bytes per plane)
+constexpr uint32_t kSymStride = kLanes * 4;              // bytes between symbols
+
+// rank of this lane among the set bits of a wave-wide mask
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+}  // namespace cgk

@@ -1,0 +1,593 @@
+// cg_kernels_decode.hip -- gfx950 kernels of cg_decode: the range decoder fused with
+// dequantize + anchor-add (K3), and the unfused dequantize + anchor-add (K4).
+
+#include "cg_device.h"
+
+namespace cgk {
+
+// ------------------------------------------------------------------------------ K3 (+K4)
+// Range decoder fused with dequantize + anchor-add.  Block = 4 wavefronts, each decoding
+// two chunks of the same (row, block) in lockstep, all sharing the block's decode table
+// in LDS (P <= 32 entries x 64 lanes x 8 bytes).  Everything that is the same for the
+// 64 lanes (chunk, token, group, stream cursor, row addresses) is kept in scalar
+// registers; only the coder state and the table address are per lane.
+
+// Per-wavefront LDS ring of payload words (stored inverted, see below), refilled with
+// 4-byte-per-lane loads.  Ring slots [0, 64) are mirrored at [R, R + 64), so the up-to-
+// 64 words one step reads are contiguous in LDS.
+constexpr uint32_t kRingWords = 256;
+constexpr uint32_t kRingAlloc = kRingWords + 64;
+constexpr uint32_t kFetchWords = 128;
+constexpr uint32_t kWavesPerBlock = 4;
+constexpr uint32_t kStreamsPerWave = 2;   // chunks one wavefront decodes in lockstep
+// Groups of this many decode steps (anchor interval 10) run fully unrolled with their
+// outputs held in registers; any other group length takes the generic loop.
+constexpr int kUnrolledSteps = 9;
+
+// Stores the 2 words at stream position pos (even) into the ring, inverted.
+__device__ __forceinline__ void ring_put(uint16_t *ring, uint32_t pos, uint32_t v)
+{
+    const uint32_t slot = pos & (kRingWords - 1);
+    *reinterpret_cast<uint32_t *>(ring + slot) = ~v;
+    if (slot < 64) *reinterpret_cast<uint32_t *>(ring + slot + kRingWords) = ~v;
+}
+
+// State of one wavefront's decoder.  The coder state is kept as ncode = ~code, which
+// turns both the symbol search and the state update into one multiply-add each:
+//   q*cdf <= code  <=>  (int)(q*cdf + ncode) < 0    (all values < 2^31)
+//   ~(code - q*cdf) = q*cdf + ncode.
+// Renormalisation shifts in inverted words, which is why the ring holds ~word.
+// The LDS table holds, per symbol s and lane, {f | cdf << 16} at byte 256*s + 4*lane
+// (cdf in the upper half, read zero-extended by the search) and the dequantized delta
+// 8 KiB further: a lane's probe never conflicts with
+// another lane's, whatever symbols the lanes are at.
+constexpr uint32_t kDqOffset = kTabPlane * 4;            // byte offset of the delta plane
+
+// p + (d < 0 ? STEP : 0) for a power-of-two STEP, as a shift and a shift-add.  (Written
+// out because the compiler otherwise folds the last level into an and + add pair.)
+template <uint32_t STEP>
+__device__ __forceinline__ uint32_t take_upper(uint32_t d, uint32_t p)
+{
+    static_assert((STEP & (STEP - 1)) == 0 && STEP >= 4 && STEP <= (1u << 15), "step");
+    constexpr uint32_t kShift = __builtin_ctz(STEP);
+    uint32_t r;
+    asm("v_lshrrev_b32 %0, 31, %1\n\tv_lshl_add_u32 %0, %0, %2, %3"
+        : "=&v"(r)
+        : "v"(d), "n"(kShift), "v"(p));
+    return r;
+}
+
+struct WaveDecoder {
+    uint32_t ncode, range;
+    uint32_t cur, re;  // next unread word; words [re - R, re) are in the ring
+    uint32_t i, m;     // symbols decoded so far / in the chunk
+    uint16_t *ring;
+    __amdgpu_buffer_rsrc_t wrs;
+    bool present;
+
+    // Binary search over the lane's cdf column, levels LEVEL .. 0: the largest symbol
+    // s with q*cdf[s] <= code, as the byte offset of its entry.
+    template <int LEVEL>
+    __device__ __forceinline__ uint32_t search(const uint8_t *tab, uint32_t p, uint32_t q) const
+    {
+        if constexpr (LEVEL < 0) {
+            return p;
+        } else {
+            constexpr uint32_t kStep = (1u << LEVEL) * kSymStride;
+            const uint32_t cdf = *reinterpret_cast<const uint16_t *>(tab + p + kStep + 2);
+            return search<LEVEL - 1>(tab, take_upper<kStep>(__umul24(q, cdf) + ncode, p), q);
+        }
+    }
+
+    // Decodes one symbol; returns the byte offset of its table entry.  ctop is the
+    // lane's cdf at the first probe (symbol P/2), the same for every step.
+    template <int LOGP>
+    __device__ __forceinline__ uint32_t symbol(const uint8_t *tab, uint32_t lb, uint32_t ctop,
+                                               float &dq)
+    {
+        constexpr uint32_t kTop = (1u << (LOGP - 1)) * kSymStride;
+        const uint32_t q = range >> kProbBits;
+        const uint32_t p = search<LOGP - 2>(tab, take_upper<kTop>(__umul24(q, ctop) + ncode, lb), q);
+        // cdf as a zero-extending 16-bit read of the upper half, f from the low half of
+        // the whole entry (a word-select operand of the multiply): no masking needed
+        const uint32_t cdf = *reinterpret_cast<const uint16_t *>(tab + p + 2);
+        const uint32_t e = *reinterpret_cast<const uint32_t *>(tab + p);
+        dq = *reinterpret_cast<const float *>(tab + p + kDqOffset);
+        ncode = __umul24(q, cdf) + ncode;
+        range = __umul24(q, e & 0xFFFFu);
+        return p;
+    }
+
+    // Loads ring chunks until the words [cur, cur + cnt) are present (rare path).
+    __device__ __forceinline__ void refill_now(uint32_t cnt, uint32_t lane)
+    {
+        while (cur + cnt > re) {
+            ring_put(ring, re + 2 * lane, __builtin_amdgcn_raw_buffer_load_b32(wrs, 2 * (re + 2 * lane), 0, 0));
+            re += kFetchWords;
+        }
+    }
+
+    // Renormalisation after a symbol that is not the chunk's last.
+    __device__ __forceinline__ void renorm(uint32_t lane)
+    {
+        // (the ballot takes the comparison itself, so the lane mask is not materialised
+        // in a vector register; with no lane renormalising the body does nothing)
+        const bool need = present && (range < kRenormBelow);
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(need);
+        const uint32_t cnt = (uint32_t)__builtin_popcountll(mask);
+        if (__builtin_expect(cur + cnt > re, 0)) refill_now(cnt, lane);
+        if (need) {
+            const uint16_t *rp = ring + (cur & (kRingWords - 1));
+            ncode = (ncode << 16) | rp[mbcnt64(mask)];
+            range <<= 16;
+        }
+        cur += cnt;
+    }
+};
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <bool SYMBOLS>
+__device__ __forceinline__ void put_out(const __amdgpu_buffer_rsrc_t &ors, uint32_t olane,
+                                        uint32_t orow, uint32_t v)
+{
+    if (SYMBOLS)
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, ors, olane, orow, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, ors, olane, orow, 0);
+}
+
+// Writes the rows held for one unrolled group: fp16 values are converted two rows per
+// instruction (round to nearest even), symbols are stored as they are.
+template <bool SYMBOLS>
+__device__ __forceinline__ void flush_rows(const __amdgpu_buffer_rsrc_t &ors, uint32_t olane,
+                                           uint32_t orow, uint32_t ostride, const float *yf,
+                                           const uint32_t *ys)
+{
+#pragma unroll
+    for (int u = 0; u < kUnrolledSteps; u += 2) {
+        if (SYMBOLS) {
+            put_out<true>(ors, olane, orow + u * ostride, ys[u]);
+            if (u + 1 < kUnrolledSteps) put_out<true>(ors, olane, orow + (u + 1) * ostride, ys[u + 1]);
+        } else if (u + 1 < kUnrolledSteps) {
+            const f32x2 v = {yf[u], yf[u + 1]};
+            const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+            put_out<false>(ors, olane, orow + u * ostride, h & 0xFFFFu);
+            put_out<false>(ors, olane, orow + (u + 1) * ostride, h >> 16);
+        } else {
+            put_out<false>(ors, olane, orow + u * ostride, f2h(yf[u]));
+        }
+    }
+}
+
+// One decoder stream: chunk k of (row, channel block b), one channel per lane, with its
+// anchor rows, output rows and payload words.  Vector memory is only touched at anchor
+// boundaries: at a group's start the next anchor row and the next chunk of words are
+// requested and the previous group's outputs (held in registers) are written; the
+// requested data is consumed at the group's end.  Waits for it therefore never wait for
+// a store issued during the group.
+template <bool SYMBOLS>
+struct Stream {
+    WaveDecoder dec;
+    __amdgpu_buffer_rsrc_t ars, ors;
+    uint32_t ng, len;           // groups / tokens in the chunk
+    uint32_t astride, ostride, olane;
+    uint32_t a16;               // anchor row of the current group (fp16 bits)
+    float af;
+    uint32_t orow;              // byte offset of the current anchor row
+    uint32_t orow_held;         // byte offset of the first row held in yf / ys
+    bool held;                  // yf / ys hold the outputs of the previous group
+    uint32_t a_next, pf, pf_at; // requests of the current group
+    bool fetch;
+    float yf[kUnrolledSteps];
+    uint32_t ys[kUnrolledSteps];
+
+    __device__ __forceinline__ void init(const Geom &g, uint16_t *ring,
+                                         const uint8_t *__restrict__ container,
+                                         const ContainerView &cv, uint32_t k, uint32_t row,
+                                         uint32_t b, uint32_t lane, bool present,
+                                         uint16_t *__restrict__ out, uint8_t *__restrict__ sym_out)
+    {
+        const uint32_t nl = min(kLanes, g.C - b * kLanes);
+        const uint32_t t0 = k * g.Tc;
+        len = chunk_len(g, k);
+        ng = (len + g.G - 1) / g.G;
+        dec.present = present;
+        dec.m = len - ng;
+        dec.i = 0;
+        dec.ring = ring;
+        const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
+        const uint64_t *offs = reinterpret_cast<const uint64_t *>(container + cv.offsets_off);
+        const uint64_t end = min(offs[gidx + 1], cv.payload_words);
+        const uint64_t beg = min(offs[gidx], end);
+        // words from the group's first word to the end of the zero-padded payload; the
+        // hardware range check returns 0 for anything past it
+        const uint64_t avail = 2 * (cv.payload_words - beg) + kPayloadPadBytes;
+        dec.wrs = make_rsrc(container + cv.payload_off + 2 * beg,
+                            (uint32_t)min(avail, (uint64_t)0xFFFFFFFFu));
+        // anchor rows of this chunk: row gi at byte 2 * (gi * C + lane); reads beyond the
+        // anchors section return 0
+        const uint64_t aoff = anchor_row(g, k, row, 0) * g.C + b * kLanes;
+        ars = make_rsrc(container + cv.anchors_off + 2 * aoff,
+                        (uint32_t)min(cv.anchors_bytes - min(2 * aoff, cv.anchors_bytes),
+                                      (uint64_t)0xFFFFFFFFu));
+        astride = 2 * g.C;
+        const uint64_t obase = ((uint64_t)row * g.S + t0) * g.C + b * kLanes;
+        ors = SYMBOLS ? make_rsrc(sym_out + obase, 0xFFFFFFFFu) : make_rsrc(out + obase, 0xFFFFFFFFu);
+        ostride = g.C * (SYMBOLS ? 1u : 2u);  // bytes between token rows
+        olane = lane * (SYMBOLS ? 1u : 2u);
+
+        dec.ncode = 0xFFFFFFFFu;
+        dec.range = kRangeInit;
+        dec.re = 0;
+        if (dec.m > 0) {
+            dec.cur = 0;
+            dec.refill_now(kRingWords, lane);
+            if (present) dec.ncode = ((uint32_t)ring[2 * lane] << 16) | ring[2 * lane + 1];
+        }
+        dec.cur = 2 * nl;
+        held = false;
+        orow = 0;
+        orow_held = 0;
+    }
+
+    // first anchor row; the empty asm pins the wait for it here
+    __device__ __forceinline__ void first_anchor(uint32_t lane)
+    {
+        uint32_t v = __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, 0, 0);
+        asm volatile("" : "+v"(v));
+        a16 = v;
+        af = h2f(a16);
+    }
+
+    // decode steps in group gi (tokens less the anchor), wave-uniform
+    __device__ __forceinline__ uint32_t steps(const Geom &g, uint32_t gi) const
+    {
+        return __builtin_amdgcn_readfirstlane(min(g.G, len - gi * g.G) - 1);
+    }
+
+    // a full group that does not hold the chunk's last symbol
+    __device__ __forceinline__ bool unrollable(uint32_t nsteps) const
+    {
+        return nsteps == (uint32_t)kUnrolledSteps && dec.i + kUnrolledSteps < dec.m;
+    }
+
+    // the next anchor row and the next chunk of words (kept only if the ring has room)
+    __device__ __forceinline__ void request(uint32_t gi, uint32_t lane)
+    {
+        a_next = __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, (gi + 1) * astride, 0);
+        fetch = dec.m > 0 && dec.re + kFetchWords - dec.cur <= kRingWords;
+        pf_at = dec.re;
+        pf = __builtin_amdgcn_raw_buffer_load_b32(dec.wrs, 2 * (pf_at + 2 * lane), 0, 0);
+    }
+
+    // the previous group's outputs, then this group's anchor row
+    __device__ __forceinline__ void write_rows()
+    {
+        if (held) {
+            if (dec.present) flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
+            held = false;
+        }
+        if (dec.present) put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? 0u : a16);
+        orow += ostride;
+    }
+
+    // takes in the requests; the ring chunk is dropped if a refill inside the group
+    // already loaded those words.  (The empty asm pins where the loaded values are first
+    // needed, so the wait for them is placed here.)
+    __device__ __forceinline__ void consume(uint32_t lane)
+    {
+        uint32_t an = a_next, pv = pf;
+        asm volatile("" : "+v"(an), "+v"(pv));
+        a16 = an;
+        af = h2f(a16);
+        if (fetch && dec.re == pf_at) {
+            ring_put(dec.ring, pf_at + 2 * lane, pv);
+            dec.re = pf_at + kFetchWords;
+        }
+    }
+
+    // step u of an unrolled group: the output stays in a register
+    template <int LOGP>
+    __device__ __forceinline__ void step_held(const uint8_t *tab, uint32_t lb, uint32_t ctop, int u)
+    {
+        float dq;
+        const uint32_t p = dec.template symbol<LOGP>(tab, lb, ctop, dq);
+        if (SYMBOLS)
+            ys[u] = p / kSymStride;
+        else
+            yf[u] = af + dq;
+    }
+
+    __device__ __forceinline__ void finish_unrolled()
+    {
+        dec.i += kUnrolledSteps;
+        held = true;
+        orow_held = orow;
+        orow += kUnrolledSteps * ostride;
+    }
+
+    template <int LOGP>
+    __device__ __forceinline__ void unrolled(const uint8_t *tab, uint32_t lb, uint32_t ctop,
+                                             uint32_t lane)
+    {
+#pragma unroll
+        for (int u = 0; u < kUnrolledSteps; ++u) {
+            step_held<LOGP>(tab, lb, ctop, u);
+            // the state update is computed here, next to its table read
+            asm volatile("" : "+v"(dec.ncode));
+            dec.renorm(lane);
+        }
+        finish_unrolled();
+    }
+
+    // any other group: one store per step
+    template <int LOGP>
+    __device__ __forceinline__ void generic(const uint8_t *tab, uint32_t lb, uint32_t ctop,
+                                            uint32_t nsteps, uint32_t lane)
+    {
+        for (uint32_t u = nsteps; u != 0; --u) {
+            float dq;
+            const uint32_t p = dec.template symbol<LOGP>(tab, lb, ctop, dq);
+            if (dec.present)
+                put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? p / kSymStride : f2h(af + dq));
+            orow += ostride;
+            if (++dec.i < dec.m) dec.renorm(lane);
+        }
+    }
+
+    __device__ __forceinline__ void final_flush()
+    {
+        if (held && dec.present) flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
+    }
+};
+
+// One wavefront decodes NS chunks of the same (row, channel block) in lockstep, sharing
+// the block's LDS table.  With two, the symbol searches of both streams sit in one
+// basic block, so the dependent LDS reads of one overlap the arithmetic of the other.
+template <int LOGP, bool SYMBOLS, bool FULL, int NS>
+__device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__restrict__ tab,
+                                              uint16_t *__restrict__ ring,
+                                              const uint8_t *__restrict__ container,
+                                              const ContainerView &cv, uint32_t k0, uint32_t k1,
+                                              uint32_t row, uint32_t b, uint32_t lane,
+                                              uint16_t *__restrict__ out,
+                                              uint8_t *__restrict__ sym_out)
+{
+    const bool present = FULL || lane < min(kLanes, g.C - b * kLanes);
+    const uint32_t lb = lane * 4;  // entry (symbol 0, this lane)
+    const uint32_t ctop =
+        *reinterpret_cast<const uint16_t *>(tab + lb + (1u << (LOGP - 1)) * kSymStride + 2);
+    Stream<SYMBOLS> st[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        st[s].init(g, ring + s * kRingAlloc, container, cv, s == 0 ? k0 : k1, row, b, lane,
+                   present, out, sym_out);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) st[s].first_anchor(lane);
+    uint32_t ngmax = st[0].ng;
+    if (NS == 2) ngmax = max(ngmax, st[NS - 1].ng);
+
+    for (uint32_t gi = 0; gi < ngmax; ++gi) {
+        bool act[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) act[s] = gi < st[s].ng;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            if (act[s]) st[s].request(gi, lane);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            if (act[s]) st[s].write_rows();
+        __builtin_amdgcn_sched_barrier(0);
+
+        uint32_t nsteps[NS];
+        bool unr[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            nsteps[s] = act[s] ? st[s].steps(g, gi) : 0u;
+            unr[s] = act[s] && st[s].unrollable(nsteps[s]);
+        }
+        if (NS == 2 && unr[0] && unr[NS - 1]) {
+#pragma unroll
+            for (int u = 0; u < kUnrolledSteps; ++u) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) st[s].template step_held<LOGP>(tab, lb, ctop, u);
+                // both state updates are computed here, next to their table reads
+                asm volatile("" : "+v"(st[0].dec.ncode), "+v"(st[NS - 1].dec.ncode));
+#pragma unroll
+                for (int s = 0; s < NS; ++s) st[s].dec.renorm(lane);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) st[s].finish_unrolled();
+        } else {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                if (unr[s])
+                    st[s].template unrolled<LOGP>(tab, lb, ctop, lane);
+                else if (act[s])
+                    st[s].template generic<LOGP>(tab, lb, ctop, nsteps[s], lane);
+            }
+        }
+
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            if (act[s]) st[s].consume(lane);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) st[s].final_flush();
+}
+
+template <bool SYMBOLS, bool FULL>
+__device__ __forceinline__ void decode_dispatch(uint32_t logp, bool pair, const Geom &g,
+                                                const uint8_t *tab, uint16_t *ring,
+                                                const uint8_t *container, const ContainerView &cv,
+                                                uint32_t k0, uint32_t k1, uint32_t row, uint32_t b,
+                                                uint32_t lane, uint16_t *out, uint8_t *sym_out)
+{
+#define CG_DECODE_CASE(LP)                                                                        \
+    case LP:                                                                                      \
+        if (pair)                                                                                 \
+            decode_chunks<LP, SYMBOLS, FULL, 2>(g, tab, ring, container, cv, k0, k1, row, b,      \
+                                                lane, out, sym_out);                              \
+        else                                                                                      \
+            decode_chunks<LP, SYMBOLS, FULL, 1>(g, tab, ring, container, cv, k0, k1, row, b,      \
+                                                lane, out, sym_out);                              \
+        break;
+    switch (logp) {
+        CG_DECODE_CASE(1)
+        CG_DECODE_CASE(2)
+        CG_DECODE_CASE(3)
+        CG_DECODE_CASE(4)
+    default:
+        CG_DECODE_CASE(5)
+    }
+#undef CG_DECODE_CASE
+}
+
+// Block = WPB wavefronts over the chunks [kb + 2 WPB set, kb + 2 WPB (set + 1)) of one
+// (row, channel block); wavefront w takes chunks base + w and base + w + WPB.  Launches
+// over many chunks use 4 wavefronts per block, sharing the staged table; launches over
+// a few chunks (a streamed chunk) use 1, so that more blocks are resident.
+template <bool SYMBOLS, uint32_t WPB>
+__global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
+                                                  const uint32_t *__restrict__ dtab,
+                                                  const uint8_t *__restrict__ container,
+                                                  ContainerView cv, uint32_t n_sets,
+                                                  uint16_t *__restrict__ out,
+                                                  uint8_t *__restrict__ sym_out)
+{
+    __shared__ uint32_t tab[kTabBlock];
+    __shared__ uint16_t rings[WPB * kStreamsPerWave * kRingAlloc];
+    const uint32_t set = blockIdx.x % n_sets;
+    const uint32_t tmp = blockIdx.x / n_sets;
+    const uint32_t b = tmp % g.NB;
+    const uint32_t row = tmp / g.NB;
+    const uint32_t N = bins[row >> 1];
+    uint32_t logp = 0;
+    while ((1u << logp) < N) ++logp;
+    // stage the P = 2^logp used entries of both planes
+    const uint32_t n16 = ((1u << logp) * kLanes) / 4;  // 16-byte pieces per plane
+    const uint4 *src = reinterpret_cast<const uint4 *>(dtab + (uint64_t)(row * g.NB + b) * kTabBlock);
+    uint4 *dst = reinterpret_cast<uint4 *>(tab);
+    for (uint32_t j = threadIdx.x; j < n16; j += blockDim.x) {
+        dst[j] = src[j];
+        dst[kTabPlane / 4 + j] = src[kTabPlane / 4 + j];
+    }
+    __syncthreads();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const uint32_t lane = threadIdx.x % kLanes;
+    const uint32_t k0 = g.kb + set * WPB * kStreamsPerWave + wave;
+    const uint32_t k1 = k0 + WPB;
+    if (k0 >= g.ke) return;
+    const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab);
+    uint16_t *ring = rings + wave * kStreamsPerWave * kRingAlloc;
+    const bool pair = k1 < g.ke;
+    if (g.C - b * kLanes >= kLanes)
+        decode_dispatch<SYMBOLS, true>(logp, pair, g, tb, ring, container, cv, k0, k1, row, b,
+                                       lane, out, sym_out);
+    else
+        decode_dispatch<SYMBOLS, false>(logp, pair, g, tb, ring, container, cv, k0, k1, row, b,
+                                        lane, out, sym_out);
+}
+
+// ------------------------------------------------------------------------------ K4
+// Dequantize + anchor-add for a symbol tensor [L][2][S][C] (the unfused path):
+// y = fp16_rne(f32(anchor) + fma(f32(q), w, lo)); anchors copied from the container.
+__global__ __launch_bounds__(256) void k4_dequant(Geom g, const float *__restrict__ lo,
+                                                   const float *__restrict__ w,
+                                                   const uint8_t *__restrict__ sym,
+                                                   const uint8_t *__restrict__ container,
+                                                   ContainerView cv, uint32_t t_lo,
+                                                   uint32_t t_hi, uint32_t tpt, uint32_t ntb,
+                                                   uint16_t *__restrict__ out)
+{
+    const uint32_t O = g.C / 8;
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (uint64_t)g.L * 2 * ntb * O) return;
+    uint32_t o = (uint32_t)(i % O);
+    uint64_t tmp = i / O;
+    uint32_t tb = (uint32_t)(tmp % ntb);
+    uint32_t row = (uint32_t)(tmp / ntb);
+    uint32_t t_begin = t_lo + tb * tpt;
+    if (t_begin >= t_hi) return;
+    uint32_t t_end = min(t_hi, t_begin + tpt);
+    const uint16_t *anc = reinterpret_cast<const uint16_t *>(container + cv.anchors_off) + o * 8;
+    float lo8[8], w8[8], af[8];
+    uint64_t r0 = (uint64_t)row * g.C + o * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        lo8[j] = lo[r0 + j];
+        w8[j] = w[r0 + j];
+    }
+    TokenWalk tw;
+    tw.init(g, t_begin);
+    if (tw.gp != 0) {
+        uint4 a = *reinterpret_cast<const uint4 *>(anc + anchor_row(g, tw.k, row, tw.gi) * g.C);
+        unpack8(a, af);
+    }
+    const uint64_t ob = (uint64_t)row * g.S * g.C + o * 8;
+    for (; tw.t < t_end; tw.next(g)) {
+        uint4 res;
+        if (tw.gp == 0) {
+            res = *reinterpret_cast<const uint4 *>(anc + anchor_row(g, tw.k, row, tw.gi) * g.C);
+            unpack8(res, af);
+        } else {
+            uint2 s8 = *reinterpret_cast<const uint2 *>(sym + ob + (uint64_t)tw.t * g.C);
+            uint32_t h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                uint32_t q = ((j < 4 ? s8.x : s8.y) >> (8 * (j & 3))) & 0xFFu;
+                h[j] = f2h(af[j] + fmaf((float)q, w8[j], lo8[j]));
+            }
+            res = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                             h[6] | (h[7] << 16));
+        }
+        *reinterpret_cast<uint4 *>(out + ob + (uint64_t)tw.t * g.C) = res;
+    }
+}
+
+// ------------------------------------------------------------------------------ launchers
+hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
+                     const uint8_t *container, const ContainerView &cv, uint16_t *out,
+                     uint8_t *sym_out, hipStream_t st)
+{
+    // fewer than 8 chunks: one wavefront per block (see k3_decode)
+    const bool wide = g.ke - g.kb >= kWavesPerBlock * kStreamsPerWave;
+    const uint32_t wpb = wide ? kWavesPerBlock : 1u;
+    const uint32_t per_block = wpb * kStreamsPerWave;
+    const uint32_t n_sets = (g.ke - g.kb + per_block - 1) / per_block;
+    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
+    const dim3 grid((uint32_t)blocks), block(wpb * kLanes);
+    if (sym_out) {
+        if (wide)
+            hipLaunchKernelGGL((k3_decode<true, kWavesPerBlock>), grid, block, 0, st, g, bins,
+                               dtab, container, cv, n_sets, out, sym_out);
+        else
+            hipLaunchKernelGGL((k3_decode<true, 1>), grid, block, 0, st, g, bins, dtab,
+                               container, cv, n_sets, out, sym_out);
+    } else {
+        if (wide)
+            hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock>), grid, block, 0, st, g, bins,
+                               dtab, container, cv, n_sets, out, sym_out);
+        else
+            hipLaunchKernelGGL((k3_decode<false, 1>), grid, block, 0, st, g, bins, dtab,
+                               container, cv, n_sets, out, sym_out);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_k4(const Geom &g, const float *lo, const float *w, const uint8_t *sym,
+                     const uint8_t *container, const ContainerView &cv, uint32_t t_lo,
+                     uint32_t t_hi, uint32_t tpt, uint16_t *out, hipStream_t st)
+{
+    uint32_t ntb = (t_hi - t_lo + tpt - 1) / tpt;
+    uint64_t threads = (uint64_t)g.L * 2 * ntb * (g.C / 8);
+    hipLaunchKernelGGL(k4_dequant, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st, g,
+                       lo, w, sym, container, cv, t_lo, t_hi, tpt, ntb, out);
+    return hipGetLastError();
+}
+
+}  // namespace cgk

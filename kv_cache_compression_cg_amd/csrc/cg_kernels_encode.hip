@@ -1,0 +1,702 @@
+// cg_kernels_encode.hip -- gfx950 kernels of cg_build_cdf and cg_encode: range and
+// non-finite check (K0), histogram and frequency / decode tables (K1), anchor delta +
+// quantize (K2) and the range encoder (K5).
+
+#include "cg_device.h"
+
+namespace cgk {
+
+// ------------------------------------------------------------------------------ K0
+// Per-channel min / max of the anchor deltas, and the non-finite flag.
+// Thread = (row, token block, 8 channels); 16-byte loads, one row of C channels is
+// read by C/8 consecutive threads.
+__global__ __launch_bounds__(256) void k0_minmax(const uint16_t *__restrict__ X, Geom g,
+                                                  uint32_t tpt, uint32_t ntb,
+                                                  uint32_t *__restrict__ ord_lo,
+                                                  uint32_t *__restrict__ ord_hi,
+                                                  uint32_t *__restrict__ flag)
+{
+    const uint32_t O = g.C / 8;
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (uint64_t)g.L * 2 * ntb * O) return;
+    uint32_t o = (uint32_t)(i % O);
+    uint64_t tmp = i / O;
+    uint32_t tb = (uint32_t)(tmp % ntb);
+    uint32_t row = (uint32_t)(tmp / ntb);
+    uint32_t t_begin = tb * tpt;
+    if (t_begin >= g.S) return;
+    uint32_t t_end = min(g.S, t_begin + tpt);
+    const uint16_t *base = X + (uint64_t)row * g.S * g.C + o * 8;
+
+    TokenWalk w;
+    w.init(g, t_begin);
+    float af[8], mn[8], mx[8];
+    bool any = false, bad = false;
+    if (w.gp != 0) {
+        uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
+        unpack8(a, af);
+    }
+    for (; w.t < t_end; w.next(g)) {
+        uint4 v = *reinterpret_cast<const uint4 *>(base + (uint64_t)w.t * g.C);
+        bad |= any_nonfinite(v);
+        float xf[8];
+        unpack8(v, xf);
+        if (w.gp == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) af[j] = xf[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float dl = xf[j] - af[j];
+                if (!any) {
+                    mn[j] = dl;
+                    mx[j] = dl;
+                } else {
+                    mn[j] = (dl < mn[j]) ? dl : mn[j];
+                    mx[j] = (dl > mx[j]) ? dl : mx[j];
+                }
+            }
+            any = true;
+        }
+    }
+    if (any) {
+        uint64_t r0 = (uint64_t)row * g.C + o * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            atomicMin(&ord_lo[r0 + j], f2ord(mn[j]));
+            atomicMax(&ord_hi[r0 + j], f2ord(mx[j]));
+        }
+    }
+    if (bad) atomicOr(flag, 1u);
+}
+
+// lo, w = (hi - lo) / (N - 1), r = 1 / w per (row, channel).
+__global__ __launch_bounds__(256) void k0_finalize(Geom g, const uint8_t *__restrict__ bins,
+                                                    const uint32_t *__restrict__ ord_lo,
+                                                    const uint32_t *__restrict__ ord_hi,
+                                                    float *__restrict__ lo, float *__restrict__ w,
+                                                    float *__restrict__ r)
+{
+    uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= g.L * 2 * g.C) return;
+    uint32_t l = i / (2 * g.C);
+    float a = 0.0f, b = 0.0f;
+    if (ord_lo[i] != 0xFFFFFFFFu) {
+        a = ord2f(ord_lo[i]);
+        b = ord2f(ord_hi[i]);
+    }
+    a = a + 0.0f;  // a zero bound is +0
+    b = b + 0.0f;
+    float ww = (b - a) / (float)(bins[l] - 1u);
+    lo[i] = a;
+    w[i] = ww;
+    r[i] = (ww > 0.0f) ? 1.0f / ww : 0.0f;
+}
+
+// ------------------------------------------------------------------------------ K1
+// Fused delta -> quantize -> histogram.  Block = (row, tile of 8*OCT channels, token
+// block); its SUB x OCT threads each own 8 channels of a token sub-range.  Counts go
+// to an LDS histogram [N][8][OCT] (consecutive lanes -> consecutive banks), then the
+// non-zero bins are added to the global u32 counts.
+__global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, Geom g,
+                                                const uint8_t *__restrict__ bins,
+                                                const float *__restrict__ lo,
+                                                const float *__restrict__ r, uint32_t OCT,
+                                                uint32_t SUB, uint32_t tpt, uint32_t ntiles,
+                                                uint32_t ntb, uint32_t *__restrict__ counts)
+{
+    extern __shared__ uint32_t hist[];
+    uint32_t tbb = blockIdx.x % ntb;
+    uint32_t tmp = blockIdx.x / ntb;
+    uint32_t ct = tmp % ntiles;
+    uint32_t row = tmp / ntiles;
+    uint32_t N = bins[row >> 1];
+    uint32_t nh = N * 8 * OCT;
+    for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) hist[j] = 0;
+    __syncthreads();
+
+    const uint32_t O = g.C / 8;
+    uint32_t ol = threadIdx.x % OCT, sub = threadIdx.x / OCT;
+    uint32_t o = ct * OCT + ol;
+    uint32_t t_begin = (tbb * SUB + sub) * tpt;
+    if (sub < SUB && o < O && t_begin < g.S) {
+        uint32_t t_end = min(g.S, t_begin + tpt);
+        const uint16_t *base = X + (uint64_t)row * g.S * g.C + o * 8;
+        float lo8[8], r8[8], af[8];
+        uint64_t r0 = (uint64_t)row * g.C + o * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            lo8[j] = lo[r0 + j];
+            r8[j] = r[r0 + j];
+        }
+        TokenWalk w;
+        w.init(g, t_begin);
+        if (w.gp != 0) {
+            uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
+            unpack8(a, af);
+        }
+        for (; w.t < t_end; w.next(g)) {
+            uint4 v = *reinterpret_cast<const uint4 *>(base + (uint64_t)w.t * g.C);
+            float xf[8];
+            unpack8(v, xf);
+            if (w.gp == 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) af[j] = xf[j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    uint32_t q = quantize1(xf[j] - af[j], lo8[j], r8[j], N);
+                    atomicAdd(&hist[(q * 8 + j) * OCT + ol], 1u);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) {
+        uint32_t v = hist[j];
+        if (!v) continue;
+        uint32_t s = j / (8 * OCT), rem = j - s * 8 * OCT;
+        uint32_t jj = rem / OCT, oo = ct * OCT + rem % OCT;
+        if (oo >= O) continue;
+        atomicAdd(&counts[((uint64_t)row * g.C + oo * 8 + jj) * kMaxBins + s], v);
+    }
+}
+
+// Frequencies (T = 4096, f >= 1, remainder to the most frequent symbol) and the decode
+// table of one (row, channel).
+__global__ __launch_bounds__(256) void k1_freqs(Geom g, const uint8_t *__restrict__ bins,
+                                                 const uint32_t *__restrict__ counts,
+                                                 const float *__restrict__ lo,
+                                                 const float *__restrict__ w,
+                                                 uint16_t *__restrict__ freqs,
+                                                 uint32_t *__restrict__ dtab)
+{
+    uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= g.L * 2 * g.C) return;
+    uint32_t row = i / g.C, c = i - row * g.C;
+    uint32_t N = bins[row >> 1];
+    const uint32_t *cnt = counts + (uint64_t)i * kMaxBins;
+    uint64_t n = 0;
+    for (uint32_t s = 0; s < N; ++s) n += cnt[s];
+    uint32_t f[kMaxBins];
+    uint32_t sum = 0, best = 0;
+    for (uint32_t s = 0; s < N; ++s) {
+        uint64_t extra = n ? ((uint64_t)cnt[s] * (kProbTotal - N)) / n : 0;
+        f[s] = 1u + (uint32_t)extra;
+        sum += f[s];
+        if (cnt[s] > cnt[best]) best = s;
+    }
+    f[best] += kProbTotal - sum;
+    uint32_t P = 1;
+    while (P < N) P <<= 1;
+    float lo1 = lo[i], w1 = w[i];
+    uint32_t *tb = dtab + (uint64_t)(row * g.NB + c / kLanes) * kTabBlock + (c % kLanes);
+    uint32_t cdf = 0;
+    for (uint32_t s = 0; s < kMaxBins; ++s) {
+        uint32_t fs = (s < N) ? f[s] : 0;
+        freqs[(uint64_t)i * kMaxBins + s] = (uint16_t)fs;
+        uint32_t cf, dq;
+        if (s < N) {
+            cf = fs | (cdf << 16);
+            dq = __float_as_uint(fmaf((float)s, w1, lo1));
+        } else {
+            // padding up to a power of two: cdf = T is never <= code for a valid stream
+            cf = kProbTotal << 16;
+            dq = __float_as_uint(fmaf((float)(N - 1u), w1, lo1));
+        }
+        tb[(uint64_t)s * kLanes] = cf;
+        tb[kTabPlane + (uint64_t)s * kLanes] = dq;
+        cdf += fs;
+    }
+}
+
+// ------------------------------------------------------------------------------ K2
+// Fused anchor-delta + quantize over tokens [t_lo, t_hi): 16-byte fp16 loads, 8-byte
+// symbol stores, anchors copied to the container layout.  sym is [L][2][sym_T][C]
+// holding tokens from sym_t0.
+__global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict__ X, Geom g,
+                                                       const uint8_t *__restrict__ bins,
+                                                       const float *__restrict__ lo,
+                                                       const float *__restrict__ r,
+                                                       uint32_t t_lo, uint32_t t_hi,
+                                                       uint32_t tpt, uint32_t ntb,
+                                                       uint8_t *__restrict__ sym,
+                                                       uint32_t sym_t0, uint32_t sym_T,
+                                                       uint16_t *__restrict__ anchors)
+{
+    const uint32_t O = g.C / 8;
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (uint64_t)g.L * 2 * ntb * O) return;
+    uint32_t o = (uint32_t)(i % O);
+    uint64_t tmp = i / O;
+    uint32_t tb = (uint32_t)(tmp % ntb);
+    uint32_t row = (uint32_t)(tmp / ntb);
+    uint32_t t_begin = t_lo + tb * tpt;
+    if (t_begin >= t_hi) return;
+    uint32_t t_end = min(t_hi, t_begin + tpt);
+    uint32_t N = bins[row >> 1];
+    const uint16_t *base = X + (uint64_t)row * g.S * g.C + o * 8;
+    uint8_t *sbase = sym + (uint64_t)row * sym_T * g.C + o * 8;
+    float lo8[8], r8[8], af[8];
+    uint64_t r0 = (uint64_t)row * g.C + o * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        lo8[j] = lo[r0 + j];
+        r8[j] = r[r0 + j];
+    }
+    TokenWalk w;
+    w.init(g, t_begin);
+    if (w.gp != 0) {
+        uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
+        unpack8(a, af);
+    }
+    for (; w.t < t_end; w.next(g)) {
+        uint4 v = *reinterpret_cast<const uint4 *>(base + (uint64_t)w.t * g.C);
+        uint2 packed = make_uint2(0, 0);
+        float xf[8];
+        unpack8(v, xf);
+        if (w.gp == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) af[j] = xf[j];
+            if (anchors) {
+                uint64_t ar = anchor_row(g, w.k, row, w.gi);
+                *reinterpret_cast<uint4 *>(anchors + ar * g.C + o * 8) = v;
+            }
+        } else {
+            uint32_t q[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q[j] = quantize1(xf[j] - af[j], lo8[j], r8[j], N);
+            packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+            packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+        }
+        *reinterpret_cast<uint2 *>(sbase + (uint64_t)(w.t - sym_t0) * g.C) = packed;
+    }
+}
+
+// ------------------------------------------------------------------------------ K5
+// Range encoder, three passes over the groups (chunk, row, channel block b); a block
+// holds 4 wavefronts = 4 chunks of one (row, b), sharing that pair's {f | cdf << 16}
+// table plane in LDS, and lane i codes the stream of channel 64b + i.  Symbols are loaded
+// eight steps ahead of their use.
+//   plan        replays the range evolution: counts each lane's words and records the
+//               wavefront's renormalisation ballot of every step;
+//   encode      codes each lane's stream into a lane-major scratch (exact size), carries
+//               rippled back into the words already written;
+//   interleave  moves every word to the position the lockstep decoders read it from,
+//               following the recorded ballots (no second replay of the coder).
+constexpr uint32_t kSymAhead = 8;
+constexpr uint32_t kEncWaves = 4;
+
+struct GroupCtx {
+    uint32_t k, row, b, lane, c, nl, t0, len, ng, m;
+    bool present;
+};
+
+__device__ __forceinline__ GroupCtx group_ctx(const Geom &g, uint64_t gidx, uint32_t lane)
+{
+    GroupCtx x;
+    x.b = (uint32_t)(gidx % g.NB);
+    uint64_t tmp = gidx / g.NB;
+    x.row = (uint32_t)(tmp % (2 * g.L));
+    x.k = g.kb + (uint32_t)(tmp / (2 * g.L));
+    x.lane = lane;
+    x.c = x.b * kLanes + lane;
+    x.nl = min(kLanes, g.C - x.b * kLanes);
+    x.present = x.c < g.C;
+    x.t0 = x.k * g.Tc;
+    x.len = chunk_len(g, x.k);
+    x.ng = (x.len + g.G - 1) / g.G;
+    x.m = x.len - x.ng;
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t lane)
+{
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint32_t y = __shfl_up(x, d, 64);
+        if (lane >= (uint32_t)d) x += y;
+    }
+    return x - v;
+}
+
+
+// Symbol i of a lane's stream sits at token t0 + 1 + i + i / (G - 1): anchors are
+// skipped.  Loads go through a buffer resource over the symbol rows of one (layer, K/V),
+// the lane's channel as vector offset and the token row as scalar offset; reads past
+// the rows return 0.
+struct SymFeed {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t voff, C, G1, rel, pos;
+
+    __device__ __forceinline__ void init(const uint8_t *rows, uint32_t bytes, uint32_t c,
+                                         uint32_t C_, uint32_t G, uint32_t t_rel)
+    {
+        rs = make_rsrc(rows, bytes);
+        voff = c;
+        C = C_;
+        G1 = G - 1;
+        rel = t_rel + 1;
+        pos = 0;
+    }
+    // issues the load of the next symbol
+    __device__ __forceinline__ uint32_t next()
+    {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b8(rs, voff, rel * C, 0);
+        rel += 1;
+        if (++pos == G1) {
+            pos = 0;
+            rel += 1;
+        }
+        return v;
+    }
+};
+
+// Block set-up shared by the encoder passes: (row, b, set) from the block index, the
+// P = 2^logp used entries of the table plane staged into LDS.  Returns the chunk of
+// this wavefront.
+__device__ __forceinline__ uint32_t enc_block(const Geom &g, const uint8_t *__restrict__ bins,
+                                              const uint32_t *__restrict__ dtab,
+                                              uint32_t n_sets, uint32_t *tab, uint32_t &row,
+                                              uint32_t &b)
+{
+    const uint32_t set = blockIdx.x % n_sets;
+    const uint32_t tmp = blockIdx.x / n_sets;
+    b = tmp % g.NB;
+    row = tmp / g.NB;
+    const uint32_t N = bins[row >> 1];
+    uint32_t P = 1;
+    while (P < N) P <<= 1;
+    const uint4 *src = reinterpret_cast<const uint4 *>(dtab + (uint64_t)(row * g.NB + b) * kTabBlock);
+    uint4 *dst = reinterpret_cast<uint4 *>(tab);
+    for (uint32_t j = threadIdx.x; j < P * kLanes / 4; j += blockDim.x) dst[j] = src[j];
+    __syncthreads();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    return g.kb + set * kEncWaves + wave;
+}
+
+__global__ __launch_bounds__(256) void k5_plan(const uint8_t *__restrict__ sym, uint32_t sym_t0,
+                                                uint32_t sym_T, Geom g,
+                                                const uint8_t *__restrict__ bins,
+                                                const uint32_t *__restrict__ dtab,
+                                                uint32_t n_sets, uint32_t *__restrict__ lane_words,
+                                                uint64_t *__restrict__ group_words,
+                                                uint64_t *__restrict__ masks, uint32_t mstride)
+{
+    __shared__ uint32_t tab[kTabPlane];
+    uint32_t row, b;
+    const uint32_t k = enc_block(g, bins, dtab, n_sets, tab, row, b);
+    if (k >= g.ke) return;
+    const uint32_t lane = threadIdx.x % kLanes;
+    const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
+    const GroupCtx x = group_ctx(g, gidx, lane);
+    uint32_t words = 0;
+    if (x.m > 0) {  // uniform
+        SymFeed sf;
+        sf.init(sym + (uint64_t)row * sym_T * g.C, sym_T * g.C, x.present ? x.c : 0, g.C, g.G,
+                x.t0 - sym_t0);
+        const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab) + lane * 4;
+        uint64_t *mrow = masks + gidx * mstride;
+        uint32_t range = kRangeInit, ev = 0, mlo = 0, mhi = 0;
+        // one step: the ballot of step i is kept in lane i % 64 and written every 64 steps
+        auto step = [&](uint32_t i, uint32_t s) __attribute__((always_inline)) {
+            const uint32_t f = *reinterpret_cast<const uint16_t *>(tb + s * kSymStride);
+            range = (range >> kProbBits) * f;
+            const bool need = x.present && i + 1 < x.m && range < kRenormBelow;
+            const uint64_t mask = __builtin_amdgcn_ballot_w64(need);
+            if (need) {
+                range <<= 16;
+                ++ev;
+            }
+            const uint32_t j = i % kLanes;
+            if (lane == j) {
+                mlo = (uint32_t)mask;
+                mhi = (uint32_t)(mask >> 32);
+            }
+            if (j == kLanes - 1 || i + 1 == x.m) {
+                if (lane <= j) {
+                    uint2 v;
+                    v.x = mlo;
+                    v.y = mhi;
+                    *reinterpret_cast<uint2 *>(mrow + (i - j) + lane) = v;
+                }
+            }
+        };
+        uint32_t sr[kSymAhead];
+#pragma unroll
+        for (uint32_t r = 0; r < kSymAhead; ++r) sr[r] = sf.next();
+        uint32_t i = 0;
+        for (; i + kSymAhead <= x.m; i += kSymAhead) {
+#pragma unroll
+            for (uint32_t r = 0; r < kSymAhead; ++r) {
+                const uint32_t s_ = sr[r];
+                sr[r] = sf.next();
+                step(i + r, s_);
+            }
+        }
+#pragma unroll
+        for (uint32_t r = 0; r < kSymAhead; ++r)
+            if (i + r < x.m) step(i + r, sr[r]);
+        if (x.present) words = 2 + ev;
+    }
+    lane_words[gidx * kLanes + lane] = words;
+    uint32_t tot = words;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) tot += __shfl_xor(tot, d, 64);
+    if (lane == 0) group_words[gidx] = tot;
+}
+
+// Exclusive prefix sum of n values in one block; out[n] = total.
+__global__ __launch_bounds__(1024) void k_scan(const uint64_t *__restrict__ in,
+                                                uint64_t *__restrict__ out, uint64_t n)
+{
+    __shared__ uint64_t part[1024];
+    uint32_t tid = threadIdx.x;
+    uint64_t per = (n + 1023) / 1024;
+    uint64_t beg = min(n, (uint64_t)tid * per), end = min(n, beg + per);
+    uint64_t s = 0;
+    for (uint64_t j = beg; j < end; ++j) s += in[j];
+    part[tid] = s;
+    __syncthreads();
+    for (uint32_t d = 1; d < 1024; d <<= 1) {
+        uint64_t y = (tid >= d) ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += y;
+        __syncthreads();
+    }
+    uint64_t run = part[tid] - s;
+    for (uint64_t j = beg; j < end; ++j) {
+        out[j] = run;
+        run += in[j];
+    }
+    if (tid == 1023) out[n] = part[1023];
+}
+
+__global__ __launch_bounds__(256) void k5_encode(const uint8_t *__restrict__ sym, uint32_t sym_t0,
+                                                  uint32_t sym_T, Geom g,
+                                                  const uint8_t *__restrict__ bins,
+                                                  const uint32_t *__restrict__ dtab,
+                                                  uint32_t n_sets,
+                                                  const uint32_t *__restrict__ lane_words,
+                                                  const uint64_t *__restrict__ group_off,
+                                                  uint16_t *__restrict__ scratch)
+{
+    __shared__ uint32_t tab[kTabPlane];
+    uint32_t row, b;
+    const uint32_t k = enc_block(g, bins, dtab, n_sets, tab, row, b);
+    if (k >= g.ke) return;
+    const uint32_t lane = threadIdx.x % kLanes;
+    const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
+    const GroupCtx x = group_ctx(g, gidx, lane);
+    const uint32_t nwords = lane_words[gidx * kLanes + lane];
+    const uint32_t lane_off = wave_excl_scan(nwords, lane);
+    if (x.m == 0) return;  // uniform
+    uint16_t *out = scratch + group_off[gidx] + lane_off;
+    SymFeed sf;
+    sf.init(sym + (uint64_t)row * sym_T * g.C, sym_T * g.C, x.present ? x.c : 0, g.C, g.G,
+            x.t0 - sym_t0);
+    const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab) + lane * 4;
+    uint64_t low = 0;
+    uint32_t range = kRangeInit, nw = 0;
+    auto step = [&](uint32_t i, uint32_t s) __attribute__((always_inline)) {
+        const uint32_t e = *reinterpret_cast<const uint32_t *>(tb + s * kSymStride);
+        const uint32_t q = range >> kProbBits;
+        low += (uint64_t)q * (e >> 16);
+        range = q * (e & 0xFFFFu);
+        if (low >> 32) {  // carry into the words already written
+            low &= 0xFFFFFFFFull;
+            uint32_t j = nw;
+            uint16_t v;
+            do {
+                --j;
+                v = (uint16_t)(out[j] + 1u);
+                out[j] = v;
+            } while (v == 0 && j > 0);
+        }
+        if (i + 1 < x.m && range < kRenormBelow) {
+            out[nw++] = (uint16_t)(low >> 16);
+            low = (low & 0xFFFFull) << 16;
+            range <<= 16;
+        }
+    };
+    uint32_t sr[kSymAhead];
+#pragma unroll
+    for (uint32_t r = 0; r < kSymAhead; ++r) sr[r] = sf.next();
+    uint32_t i = 0;
+    if (x.present) {
+        for (; i + kSymAhead <= x.m; i += kSymAhead) {
+#pragma unroll
+            for (uint32_t r = 0; r < kSymAhead; ++r) {
+                const uint32_t s_ = sr[r];
+                sr[r] = sf.next();
+                step(i + r, s_);
+            }
+        }
+#pragma unroll
+        for (uint32_t r = 0; r < kSymAhead; ++r)
+            if (i + r < x.m) step(i + r, sr[r]);
+        out[nw++] = (uint16_t)(low >> 16);
+        out[nw++] = (uint16_t)(low & 0xFFFFu);
+    }
+}
+
+__global__ __launch_bounds__(256) void k5_interleave(Geom g, uint32_t n_sets,
+                                                      const uint32_t *__restrict__ lane_words,
+                                                      const uint64_t *__restrict__ group_off,
+                                                      const uint64_t *__restrict__ masks,
+                                                      uint32_t mstride,
+                                                      const uint16_t *__restrict__ scratch,
+                                                      uint16_t *__restrict__ payload)
+{
+    const uint32_t set = blockIdx.x % n_sets;
+    const uint32_t tmp = blockIdx.x / n_sets;
+    const uint32_t b = tmp % g.NB;
+    const uint32_t row = tmp / g.NB;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const uint32_t k = g.kb + set * kEncWaves + wave;
+    if (k >= g.ke) return;
+    const uint32_t lane = threadIdx.x % kLanes;
+    const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
+    const GroupCtx x = group_ctx(g, gidx, lane);
+    const uint32_t nwords = lane_words[gidx * kLanes + lane];
+    const uint32_t lane_off = wave_excl_scan(nwords, lane);
+    if (x.m == 0) return;  // uniform
+    const uint16_t *src = scratch + group_off[gidx] + lane_off;
+    uint16_t *dst = payload + group_off[gidx];
+    uint32_t e = 2, w_next = 0;
+    if (x.present) {
+        dst[2 * lane] = src[0];
+        dst[2 * lane + 1] = src[1];
+        if (nwords > 2) w_next = src[2];
+    }
+    const uint64_t *mrow = masks + gidx * mstride;
+    uint32_t cursor = 2 * x.nl;
+    for (uint32_t base = 0; base < x.m; base += kLanes) {
+        // the ballots of steps base .. base + 63, one per lane
+        uint2 mm = make_uint2(0, 0);
+        if (base + lane < x.m) mm = *reinterpret_cast<const uint2 *>(mrow + base + lane);
+        const uint32_t n = min(kLanes, x.m - base);
+        for (uint32_t j = 0; j < n; ++j) {
+            // (readlane returns a signed int: go through uint32_t, no sign extension)
+            const uint32_t mlo = (uint32_t)__builtin_amdgcn_readlane(mm.x, j);
+            const uint32_t mhi = (uint32_t)__builtin_amdgcn_readlane(mm.y, j);
+            const uint64_t mask = ((uint64_t)mhi << 32) | mlo;
+            if (mask) {
+                if ((mask >> lane) & 1u) {
+                    dst[cursor + mbcnt64(mask)] = (uint16_t)w_next;
+                    ++e;
+                    if (e < nwords) w_next = src[e];
+                }
+                cursor += (uint32_t)__builtin_popcountll(mask);
+            }
+        }
+    }
+}
+
+
+// ------------------------------------------------------------------------------ launchers
+hipError_t launch_k0(const uint16_t *X, const Geom &g, uint32_t tpt, uint32_t *ord_lo,
+                     uint32_t *ord_hi, uint32_t *flag, hipStream_t st)
+{
+    uint32_t ntb = (g.S + tpt - 1) / tpt;
+    uint64_t threads = (uint64_t)g.L * 2 * ntb * (g.C / 8);
+    hipLaunchKernelGGL(k0_minmax, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st, X, g,
+                       tpt, ntb, ord_lo, ord_hi, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_k0_finalize(const Geom &g, const uint8_t *bins, const uint32_t *ord_lo,
+                              const uint32_t *ord_hi, float *lo, float *w, float *r, hipStream_t st)
+{
+    uint32_t n = g.L * 2 * g.C;
+    hipLaunchKernelGGL(k0_finalize, dim3((n + 255) / 256), dim3(256), 0, st, g, bins, ord_lo,
+                       ord_hi, lo, w, r);
+    return hipGetLastError();
+}
+
+hipError_t launch_k1(const uint16_t *X, const Geom &g, const uint8_t *bins, uint32_t max_bins,
+                     const float *lo, const float *r, uint32_t *counts, hipStream_t st)
+{
+    const uint32_t O = g.C / 8;
+    const uint32_t OCT = O < 32 ? O : 32;
+    const uint32_t SUB = 256 / OCT;
+    const uint32_t ntiles = (O + OCT - 1) / OCT;
+    const uint64_t rows = (uint64_t)g.L * 2;
+    uint64_t ntb_target = (8192 + rows * ntiles - 1) / (rows * ntiles);
+    uint64_t tpt = (g.S + ntb_target * SUB - 1) / (ntb_target * SUB);
+    if (tpt < 16) tpt = 16;
+    uint32_t ntb = (uint32_t)((g.S + tpt * SUB - 1) / (tpt * SUB));
+    size_t lds = (size_t)max_bins * 8 * OCT * sizeof(uint32_t);
+    hipLaunchKernelGGL(k1_hist, dim3((uint32_t)(rows * ntiles * ntb)), dim3(256), lds, st, X, g,
+                       bins, lo, r, OCT, SUB, (uint32_t)tpt, ntiles, ntb, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_k1_freqs(const Geom &g, const uint8_t *bins, const uint32_t *counts,
+                           const float *lo, const float *w, uint16_t *freqs, uint32_t *dtab,
+                           hipStream_t st)
+{
+    uint32_t n = g.L * 2 * g.C;
+    hipLaunchKernelGGL(k1_freqs, dim3((n + 255) / 256), dim3(256), 0, st, g, bins, counts, lo, w,
+                       freqs, dtab);
+    return hipGetLastError();
+}
+
+hipError_t launch_k2(const uint16_t *X, const Geom &g, const uint8_t *bins, const float *lo,
+                     const float *r, uint32_t t_lo, uint32_t t_hi, uint32_t tpt, uint8_t *sym,
+                     uint32_t sym_t0, uint32_t sym_T, uint16_t *anchors, hipStream_t st)
+{
+    uint32_t ntb = (t_hi - t_lo + tpt - 1) / tpt;
+    uint64_t threads = (uint64_t)g.L * 2 * ntb * (g.C / 8);
+    hipLaunchKernelGGL(k2_delta_quant, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st,
+                       X, g, bins, lo, r, t_lo, t_hi, tpt, ntb, sym, sym_t0, sym_T, anchors);
+    return hipGetLastError();
+}
+
+static uint32_t enc_sets(const Geom &g) { return (g.ke - g.kb + kEncWaves - 1) / kEncWaves; }
+
+hipError_t launch_k5_plan(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
+                          const uint8_t *bins, const uint32_t *dtab, uint32_t *lane_words,
+                          uint64_t *group_words, uint64_t *masks, uint32_t mstride,
+                          hipStream_t st)
+{
+    const uint32_t n_sets = enc_sets(g);
+    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
+    hipLaunchKernelGGL(k5_plan, dim3((uint32_t)blocks), dim3(256), 0, st, sym, sym_t0, sym_T, g,
+                       bins, dtab, n_sets, lane_words, group_words, masks, mstride);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const uint64_t *in, uint64_t *out, uint64_t n, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, in, out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_k5_encode(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
+                            const uint8_t *bins, const uint32_t *dtab,
+                            const uint32_t *lane_words, const uint64_t *group_off,
+                            uint16_t *scratch, hipStream_t st)
+{
+    const uint32_t n_sets = enc_sets(g);
+    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
+    hipLaunchKernelGGL(k5_encode, dim3((uint32_t)blocks), dim3(256), 0, st, sym, sym_t0, sym_T, g,
+                       bins, dtab, n_sets, lane_words, group_off, scratch);
+    return hipGetLastError();
+}
+
+hipError_t launch_k5_interleave(const Geom &g, const uint32_t *lane_words,
+                                const uint64_t *group_off, const uint64_t *masks,
+                                uint32_t mstride, const uint16_t *scratch, uint16_t *payload,
+                                hipStream_t st)
+{
+    const uint32_t n_sets = enc_sets(g);
+    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
+    hipLaunchKernelGGL(k5_interleave, dim3((uint32_t)blocks), dim3(256), 0, st, g, n_sets,
+                       lane_words, group_off, masks, mstride, scratch, payload);
+    return hipGetLastError();
+}
+
+
+}  // namespace cgk
