@@ -4,8 +4,8 @@
 One step = one pass of the whole hot path over the Llama-3-70B-shaped cache
 (L=80, H_kv=8, d=128, S=32768, fp16, 10.74 GB; anchor interval 10, 1536-token chunks,
 bins 32 / 16 / 8 for layers 0-19 / 20-39 / 40-79): cg_build_cdf (range, quantize,
-histogram, frequency tables), cg_encode (delta + quantize, range coding, interleaving)
-and cg_decode (range decode fused with dequantize + anchor-add) back to fp16.
+histogram, frequency tables), cg_encode (delta + quantize, rANS coding, interleaving)
+and cg_decode (rANS decode fused with dequantize + anchor-add) back to fp16.
 
 Reported `value`: cg_decode throughput in GB/s of raw fp16 KV reconstructed (the
 metric), from HIP events around each decode on the stream it runs on, averaged over
@@ -54,15 +54,9 @@ def kernel_source_hash() -> str:
 
 def table_bytes_read(tables) -> int:
     """Decode-table bytes the decoder stages into LDS: per (layer, K/V, 64-channel
-    block), P = next power of two >= bins entries x 64 lanes x 8 bytes."""
+    block), bins entries x 64 lanes x 4 bytes plus the 256-slot x 64-lane byte table."""
     nb = -(-tables.C // 64)
-    tot = 0
-    for b in tables.bins:
-        p = 1
-        while p < b:
-            p *= 2
-        tot += 2 * nb * p * 64 * 8
-    return tot
+    return sum(2 * nb * (b * 64 * 4 + 256 * 64) for b in tables.bins)
 
 
 def measured_traffic(alg_bytes: float):

@@ -9,9 +9,9 @@
  *   - every other token is coded as its delta from the anchor, quantized to the
  *     layer's number of levels, finer for early layers (same page, pillar 1; the
  *     gptget.net summary of CacheGen, Methodology);
- *   - the symbols are range-coded with empirical frequency tables per (layer, K/V,
- *     channel), one stream per (layer, K/V, channel, chunk) (pillar 3; the summary's
- *     Deep Analysis, Methodology);
+ *   - the symbols are entropy-coded (rANS, an arithmetic-type coder) with empirical
+ *     frequency tables per (layer, K/V, channel), one stream per (layer, K/V, channel,
+ *     chunk) (pillar 3; the summary's Deep Analysis, Methodology);
  *   - decoding inverts the coder, dequantizes in float32 and adds the anchor back
  *     (Implementation Step 1 dequantize_tensor, Step 2 decode_sequence).
  * The problem statement these calls follow is the pages' KV-size formula
@@ -102,7 +102,7 @@ typedef struct cg_tables_info {
 /*
  * Builds the per-(layer, K/V, channel) tables from the whole cache: the range of the
  * anchor deltas, the bin width, and a frequency table of the quantized deltas over all
- * chunks (T = 4096, every symbol >= 1).
+ * chunks (T = 256, every symbol >= 1).
  *   kv_dev: fp16 [L][2][S][C], read only.
  *   *out:   receives a new handle on success, untouched on error.
  * Synchronises `hip_stream` once (to report CG_E_NONFINITE).
@@ -206,7 +206,7 @@ int cg_blob_read(const cg_blob *blob, uint64_t offset, uint64_t nbytes, void *ho
 int cg_quantize(const cg_tables *tables, const void *kv_dev, uint32_t chunk_begin,
                 uint32_t chunk_end, void *sym_dev, void *hip_stream);
 
-/* The range decoder alone: writes uint8 symbols [L][2][S][C] for the container's
+/* The entropy decoder alone: writes uint8 symbols [L][2][S][C] for the container's
  * tokens (anchor slots written 0).  Asynchronous. */
 int cg_decode_symbols(const cg_tables *tables, const cg_blob *blob, const void *container_dev,
                       void *sym_dev, void *hip_stream);

@@ -409,7 +409,7 @@ int cg_decode(const cg_tables *t, const cg_blob *b, const void *container_dev, v
     CG_HIP(ds.enter(t->device), "hipSetDevice");
     const uint8_t *cont = container_dev ? static_cast<const uint8_t *>(container_dev) : b->d_data;
     Geom g = make_geom(t, b->hdr.chunk_begin, b->hdr.chunk_end);
-    CG_HIP(launch_k3(g, t->d_bins, t->d_dtab, cont, view_of(b), static_cast<uint16_t *>(kv_out_dev),
+    CG_HIP(launch_k3(g, t->d_bins, t->d_dtab, t->d_lo, t->d_w, cont, view_of(b), static_cast<uint16_t *>(kv_out_dev),
                      nullptr, (hipStream_t)hip_stream),
            "k3_decode");
     return CG_OK;
@@ -521,7 +521,7 @@ int cg_stream_decode(const cg_stream_item *items, uint32_t n_items, void *stagin
         if (ie && (err = hipEventRecord(ie[2], dec)) != hipSuccess) { what = "hipEventRecord"; break; }
         const cg_blob *b = it.blob;
         Geom g = make_geom(it.tables, b->hdr.chunk_begin, b->hdr.chunk_end);
-        if ((err = launch_k3(g, it.tables->d_bins, it.tables->d_dtab, slot, view_of(b),
+        if ((err = launch_k3(g, it.tables->d_bins, it.tables->d_dtab, it.tables->d_lo, it.tables->d_w, slot, view_of(b),
                              static_cast<uint16_t *>(kv_out_dev), nullptr, dec)) != hipSuccess) {
             what = "k3_decode";
             break;
@@ -566,7 +566,7 @@ int cg_decode_symbols(const cg_tables *t, const cg_blob *b, const void *containe
     CG_HIP(ds.enter(t->device), "hipSetDevice");
     const uint8_t *cont = container_dev ? static_cast<const uint8_t *>(container_dev) : b->d_data;
     Geom g = make_geom(t, b->hdr.chunk_begin, b->hdr.chunk_end);
-    CG_HIP(launch_k3(g, t->d_bins, t->d_dtab, cont, view_of(b), nullptr,
+    CG_HIP(launch_k3(g, t->d_bins, t->d_dtab, t->d_lo, t->d_w, cont, view_of(b), nullptr,
                      static_cast<uint8_t *>(sym_dev), (hipStream_t)hip_stream),
            "k3_decode_symbols");
     return CG_OK;

@@ -7,17 +7,19 @@
 
 namespace cgk {
 
-constexpr uint32_t kProbBits = 12;                 // frequencies are in units of 1/4096
+constexpr uint32_t kProbBits = 8;                  // frequencies are in units of 1/256
 constexpr uint32_t kProbTotal = 1u << kProbBits;
 constexpr uint32_t kMaxBins = 32;
 constexpr uint32_t kLanes = 64;                    // channels per group = wavefront width
-constexpr uint32_t kRenormBelow = 1u << 15;        // renormalise (one 16-bit word) below 2^15
-constexpr uint32_t kRangeInit = 0x7FFFFFFFu;       // 31-bit range
+constexpr uint32_t kStateLow = 1u << 16;           // rANS state in [2^16, 2^32), 16-bit words
 constexpr uint32_t kPayloadPadBytes = 1024;        // zero bytes after the payload of a container
-// Decode table of one (row, 64-channel block): two planes [32 symbols][64 lanes] of
-// 32-bit words, {f | cdf << 16} then the dequantized delta lo + s * w (fp32 bits).
+// Decode table of one (row, 64-channel block), in 32-bit words: two planes [32 symbols]
+// [64 lanes], {f | cdf << 24} then the dequantized delta lo + s * w (fp32 bits), then
+// the slot table [256 slots][64 lanes] of bytes: the symbol whose interval [cdf, cdf + f)
+// holds the slot.
 constexpr uint32_t kTabPlane = kMaxBins * kLanes;
-constexpr uint32_t kTabBlock = 2 * kTabPlane;
+constexpr uint32_t kTabLut = 2 * kTabPlane;
+constexpr uint32_t kTabBlock = kTabLut + kProbTotal * kLanes / 4;
 // dword 3 of a raw (untyped) buffer resource on gfx9-family GPUs: 32-bit data format
 constexpr int kBufferFlags = 0x00020000;
 
@@ -60,9 +62,9 @@ hipError_t launch_k5_interleave(const Geom &g, const uint32_t *lane_words,
                                 const uint64_t *group_off, const uint64_t *masks,
                                 uint32_t mstride, const uint16_t *scratch, uint16_t *payload,
                                 hipStream_t st);
-hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
-                     const uint8_t *container, const ContainerView &cv, uint16_t *out,
-                     uint8_t *sym_out, hipStream_t st);
+hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, const float *lo,
+                     const float *w, const uint8_t *container, const ContainerView &cv,
+                     uint16_t *out, uint8_t *sym_out, hipStream_t st);
 hipError_t launch_k4(const Geom &g, const float *lo, const float *w, const uint8_t *sym,
                      const uint8_t *container, const ContainerView &cv, uint32_t t_lo,
                      uint32_t t_hi, uint32_t tpt, uint16_t *out, hipStream_t st);

@@ -1,4 +1,4 @@
-// cg_kernels_decode.hip -- gfx950 kernels of cg_decode: the range decoder fused with
+// cg_kernels_decode.hip -- gfx950 kernels of cg_decode: the rANS decoder fused with
 // dequantize + anchor-add (K3), and the unfused dequantize + anchor-add (K4).
 
 #include "cg_device.h"
@@ -6,13 +6,13 @@
 namespace cgk {
 
 // ------------------------------------------------------------------------------ K3 (+K4)
-// Range decoder fused with dequantize + anchor-add.  Block = 4 wavefronts, each decoding
+// rANS decoder fused with dequantize + anchor-add.  Block = 4 wavefronts, each decoding
 // two chunks of the same (row, block) in lockstep, all sharing the block's decode table
-// in LDS (P <= 32 entries x 64 lanes x 8 bytes).  Everything that is the same for the
-// 64 lanes (chunk, token, group, stream cursor, row addresses) is kept in scalar
-// registers; only the coder state and the table address are per lane.
+// in LDS (N <= 32 entries x 64 lanes x 4 bytes, slot table 256 x 64 bytes).  Everything
+// that is the same for the 64 lanes (chunk, token, group, stream cursor, row addresses)
+// is kept in scalar registers; only the coder state and the table address are per lane.
 
-// Per-wavefront LDS ring of payload words (stored inverted, see below), refilled with
+// Per-wavefront LDS ring of payload words, refilled with
 // 4-byte-per-lane loads.  Ring slots [0, 64) are mirrored at [R, R + 64), so the up-to-
 // 64 words one step reads are contiguous in LDS.
 constexpr uint32_t kRingWords = 256;
@@ -24,77 +24,42 @@ constexpr uint32_t kStreamsPerWave = 2;   // chunks one wavefront decodes in loc
 // outputs held in registers; any other group length takes the generic loop.
 constexpr int kUnrolledSteps = 9;
 
-// Stores the 2 words at stream position pos (even) into the ring, inverted.
+// Stores the 2 words at stream position pos (even) into the ring.
 __device__ __forceinline__ void ring_put(uint16_t *ring, uint32_t pos, uint32_t v)
 {
     const uint32_t slot = pos & (kRingWords - 1);
-    *reinterpret_cast<uint32_t *>(ring + slot) = ~v;
-    if (slot < 64) *reinterpret_cast<uint32_t *>(ring + slot + kRingWords) = ~v;
+    *reinterpret_cast<uint32_t *>(ring + slot) = v;
+    if (slot < 64) *reinterpret_cast<uint32_t *>(ring + slot + kRingWords) = v;
 }
 
-// State of one wavefront's decoder.  The coder state is kept as ncode = ~code, which
-// turns both the symbol search and the state update into one multiply-add each:
-//   q*cdf <= code  <=>  (int)(q*cdf + ncode) < 0    (all values < 2^31)
-//   ~(code - q*cdf) = q*cdf + ncode.
-// Renormalisation shifts in inverted words, which is why the ring holds ~word.
-// The LDS table holds, per symbol s and lane, {f | cdf << 16} at byte 256*s + 4*lane
-// (cdf in the upper half, read zero-extended by the search) and the dequantized delta
-// 8 KiB further: a lane's probe never conflicts with
-// another lane's, whatever symbols the lanes are at.
-constexpr uint32_t kDqOffset = kTabPlane * 4;            // byte offset of the delta plane
-
-// p + (d < 0 ? STEP : 0) for a power-of-two STEP, as a shift and a shift-add.  (Written
-// out because the compiler otherwise folds the last level into an and + add pair.)
-template <uint32_t STEP>
-__device__ __forceinline__ uint32_t take_upper(uint32_t d, uint32_t p)
-{
-    static_assert((STEP & (STEP - 1)) == 0 && STEP >= 4 && STEP <= (1u << 15), "step");
-    constexpr uint32_t kShift = __builtin_ctz(STEP);
-    uint32_t r;
-    asm("v_lshrrev_b32 %0, 31, %1\n\tv_lshl_add_u32 %0, %0, %2, %3"
-        : "=&v"(r)
-        : "v"(d), "n"(kShift), "v"(p));
-    return r;
-}
+// The block's table in LDS: the entry of symbol s for this lane {f | cdf << 24} at byte
+// 256 s + 4 lane (lanes never conflict, whatever symbols they are at), then the slot
+// table, byte 64 slot + lane.  The dequantized delta lo + s * w is recomputed (one
+// conversion and one fma, as the table builder does) rather than staged.
+constexpr uint32_t kLdsLut = kTabPlane * 4;
+constexpr uint32_t kLdsWords = kTabPlane + kProbTotal * kLanes / 4;
 
 struct WaveDecoder {
-    uint32_t ncode, range;
+    uint32_t x;        // rANS state, in [2^16, 2^32) between symbols
+    float dlo, dw;     // the lane's channel: lo and bin width
     uint32_t cur, re;  // next unread word; words [re - R, re) are in the ring
     uint32_t i, m;     // symbols decoded so far / in the chunk
     uint16_t *ring;
     __amdgpu_buffer_rsrc_t wrs;
     bool present;
 
-    // Binary search over the lane's cdf column, levels LEVEL .. 0: the largest symbol
-    // s with q*cdf[s] <= code, as the byte offset of its entry.
-    template <int LEVEL>
-    __device__ __forceinline__ uint32_t search(const uint8_t *tab, uint32_t p, uint32_t q) const
-    {
-        if constexpr (LEVEL < 0) {
-            return p;
-        } else {
-            constexpr uint32_t kStep = (1u << LEVEL) * kSymStride;
-            const uint32_t cdf = *reinterpret_cast<const uint16_t *>(tab + p + kStep + 2);
-            return search<LEVEL - 1>(tab, take_upper<kStep>(__umul24(q, cdf) + ncode, p), q);
-        }
-    }
-
-    // Decodes one symbol; returns the byte offset of its table entry.  ctop is the
-    // lane's cdf at the first probe (symbol P/2), the same for every step.
-    template <int LOGP>
-    __device__ __forceinline__ uint32_t symbol(const uint8_t *tab, uint32_t lb, uint32_t ctop,
+    // Decodes one symbol: the low 8 bits of the state name a slot, the slot table names
+    // the symbol, and x = f * (x >> 8) + slot - cdf (f in the low byte of the entry, so
+    // the 24-bit multiply sees f alone).  Returns the byte offset of the symbol's entry.
+    __device__ __forceinline__ uint32_t symbol(const uint8_t *tab, uint32_t lane, uint32_t lb,
                                                float &dq)
     {
-        constexpr uint32_t kTop = (1u << (LOGP - 1)) * kSymStride;
-        const uint32_t q = range >> kProbBits;
-        const uint32_t p = search<LOGP - 2>(tab, take_upper<kTop>(__umul24(q, ctop) + ncode, lb), q);
-        // cdf as a zero-extending 16-bit read of the upper half, f from the low half of
-        // the whole entry (a word-select operand of the multiply): no masking needed
-        const uint32_t cdf = *reinterpret_cast<const uint16_t *>(tab + p + 2);
+        const uint32_t slot = x & (kProbTotal - 1u);
+        const uint32_t s = tab[kLdsLut + slot * kLanes + lane];
+        const uint32_t p = s * kSymStride + lb;
         const uint32_t e = *reinterpret_cast<const uint32_t *>(tab + p);
-        dq = *reinterpret_cast<const float *>(tab + p + kDqOffset);
-        ncode = __umul24(q, cdf) + ncode;
-        range = __umul24(q, e & 0xFFFFu);
+        dq = fmaf((float)s, dw, dlo);
+        x = __umul24(e, x >> kProbBits) + slot - (e >> 24);
         return p;
     }
 
@@ -112,14 +77,13 @@ struct WaveDecoder {
     {
         // (the ballot takes the comparison itself, so the lane mask is not materialised
         // in a vector register; with no lane renormalising the body does nothing)
-        const bool need = present && (range < kRenormBelow);
+        const bool need = present && (x < kStateLow);
         const uint64_t mask = __builtin_amdgcn_ballot_w64(need);
         const uint32_t cnt = (uint32_t)__builtin_popcountll(mask);
         if (__builtin_expect(cur + cnt > re, 0)) refill_now(cnt, lane);
         if (need) {
             const uint16_t *rp = ring + (cur & (kRingWords - 1));
-            ncode = (ncode << 16) | rp[mbcnt64(mask)];
-            range <<= 16;
+            x = (x << 16) | rp[mbcnt64(mask)];
         }
         cur += cnt;
     }
@@ -184,6 +148,8 @@ struct Stream {
     uint32_t ys[kUnrolledSteps];
 
     __device__ __forceinline__ void init(const Geom &g, uint16_t *ring,
+                                         const float *__restrict__ lo,
+                                         const float *__restrict__ w,
                                          const uint8_t *__restrict__ container,
                                          const ContainerView &cv, uint32_t k, uint32_t row,
                                          uint32_t b, uint32_t lane, bool present,
@@ -218,13 +184,14 @@ struct Stream {
         ostride = g.C * (SYMBOLS ? 1u : 2u);  // bytes between token rows
         olane = lane * (SYMBOLS ? 1u : 2u);
 
-        dec.ncode = 0xFFFFFFFFu;
-        dec.range = kRangeInit;
+        dec.x = kStateLow;
+        dec.dlo = present ? lo[(uint64_t)row * g.C + b * kLanes + lane] : 0.0f;
+        dec.dw = present ? w[(uint64_t)row * g.C + b * kLanes + lane] : 0.0f;
         dec.re = 0;
         if (dec.m > 0) {
             dec.cur = 0;
             dec.refill_now(kRingWords, lane);
-            if (present) dec.ncode = ((uint32_t)ring[2 * lane] << 16) | ring[2 * lane + 1];
+            if (present) dec.x = ((uint32_t)ring[2 * lane] << 16) | ring[2 * lane + 1];
         }
         dec.cur = 2 * nl;
         held = false;
@@ -262,6 +229,15 @@ struct Stream {
         pf = __builtin_amdgcn_raw_buffer_load_b32(dec.wrs, 2 * (pf_at + 2 * lane), 0, 0);
     }
 
+    // write_rows for a stream holding rows with every lane present
+    __device__ __forceinline__ void write_held_rows()
+    {
+        flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
+        held = false;
+        put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? 0u : a16);
+        orow += ostride;
+    }
+
     // the previous group's outputs, then this group's anchor row
     __device__ __forceinline__ void write_rows()
     {
@@ -289,11 +265,10 @@ struct Stream {
     }
 
     // step u of an unrolled group: the output stays in a register
-    template <int LOGP>
-    __device__ __forceinline__ void step_held(const uint8_t *tab, uint32_t lb, uint32_t ctop, int u)
+    __device__ __forceinline__ void step_held(const uint8_t *tab, uint32_t lane, uint32_t lb, int u)
     {
         float dq;
-        const uint32_t p = dec.template symbol<LOGP>(tab, lb, ctop, dq);
+        const uint32_t p = dec.symbol(tab, lane, lb, dq);
         if (SYMBOLS)
             ys[u] = p / kSymStride;
         else
@@ -308,28 +283,25 @@ struct Stream {
         orow += kUnrolledSteps * ostride;
     }
 
-    template <int LOGP>
-    __device__ __forceinline__ void unrolled(const uint8_t *tab, uint32_t lb, uint32_t ctop,
-                                             uint32_t lane)
+    __device__ __forceinline__ void unrolled(const uint8_t *tab, uint32_t lane, uint32_t lb)
     {
 #pragma unroll
         for (int u = 0; u < kUnrolledSteps; ++u) {
-            step_held<LOGP>(tab, lb, ctop, u);
-            // the state update is computed here, next to its table read
-            asm volatile("" : "+v"(dec.ncode));
+            step_held(tab, lane, lb, u);
+            // the state update is computed here, next to its table reads
+            asm volatile("" : "+v"(dec.x));
             dec.renorm(lane);
         }
         finish_unrolled();
     }
 
     // any other group: one store per step
-    template <int LOGP>
-    __device__ __forceinline__ void generic(const uint8_t *tab, uint32_t lb, uint32_t ctop,
-                                            uint32_t nsteps, uint32_t lane)
+    __device__ __forceinline__ void generic(const uint8_t *tab, uint32_t lane, uint32_t lb,
+                                            uint32_t nsteps)
     {
         for (uint32_t u = nsteps; u != 0; --u) {
             float dq;
-            const uint32_t p = dec.template symbol<LOGP>(tab, lb, ctop, dq);
+            const uint32_t p = dec.symbol(tab, lane, lb, dq);
             if (dec.present)
                 put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? p / kSymStride : f2h(af + dq));
             orow += ostride;
@@ -343,12 +315,32 @@ struct Stream {
     }
 };
 
+// An unrolled group of both streams of a wavefront in lockstep.
+template <bool SYMBOLS, int NS>
+__device__ __forceinline__ void paired_steps(Stream<SYMBOLS> (&st)[NS], const uint8_t *tab,
+                                             uint32_t lane, uint32_t lb)
+{
+#pragma unroll
+    for (int u = 0; u < kUnrolledSteps; ++u) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) st[s].step_held(tab, lane, lb, u);
+        // both state updates are computed here, next to their table reads
+        asm volatile("" : "+v"(st[0].dec.x), "+v"(st[NS - 1].dec.x));
+#pragma unroll
+        for (int s = 0; s < NS; ++s) st[s].dec.renorm(lane);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) st[s].finish_unrolled();
+}
+
 // One wavefront decodes NS chunks of the same (row, channel block) in lockstep, sharing
 // the block's LDS table.  With two, the symbol searches of both streams sit in one
 // basic block, so the dependent LDS reads of one overlap the arithmetic of the other.
-template <int LOGP, bool SYMBOLS, bool FULL, int NS>
+template <bool SYMBOLS, bool FULL, int NS>
 __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__restrict__ tab,
                                               uint16_t *__restrict__ ring,
+                                              const float *__restrict__ lo,
+                                              const float *__restrict__ w,
                                               const uint8_t *__restrict__ container,
                                               const ContainerView &cv, uint32_t k0, uint32_t k1,
                                               uint32_t row, uint32_t b, uint32_t lane,
@@ -357,12 +349,10 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
 {
     const bool present = FULL || lane < min(kLanes, g.C - b * kLanes);
     const uint32_t lb = lane * 4;  // entry (symbol 0, this lane)
-    const uint32_t ctop =
-        *reinterpret_cast<const uint16_t *>(tab + lb + (1u << (LOGP - 1)) * kSymStride + 2);
     Stream<SYMBOLS> st[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-        st[s].init(g, ring + s * kRingAlloc, container, cv, s == 0 ? k0 : k1, row, b, lane,
+        st[s].init(g, ring + s * kRingAlloc, lo, w, container, cv, s == 0 ? k0 : k1, row, b, lane,
                    present, out, sym_out);
 #pragma unroll
     for (int s = 0; s < NS; ++s) st[s].first_anchor(lane);
@@ -371,8 +361,30 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
 
     for (uint32_t gi = 0; gi < ngmax; ++gi) {
         bool act[NS];
+        uint32_t nsteps[NS];
+        bool unr[NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) act[s] = gi < st[s].ng;
+        for (int s = 0; s < NS; ++s) {
+            act[s] = gi < st[s].ng;
+            nsteps[s] = act[s] ? st[s].steps(g, gi) : 0u;
+            unr[s] = act[s] && st[s].unrollable(nsteps[s]);
+        }
+        if (FULL && NS == 2 && unr[0] && unr[NS - 1] && st[0].held && st[NS - 1].held) {
+            // The common group.  Every memory operation in it is unconditional, so the
+            // wait at its end (the counter retires in issue order) covers the requests
+            // but not the 20 row stores issued after them.
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) st[s].request(gi, lane);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) st[s].write_held_rows();
+            __builtin_amdgcn_sched_barrier(0);
+            paired_steps(st, tab, lane, lb);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) st[s].consume(lane);
+            continue;
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < NS; ++s)
@@ -381,33 +393,15 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
         for (int s = 0; s < NS; ++s)
             if (act[s]) st[s].write_rows();
         __builtin_amdgcn_sched_barrier(0);
-
-        uint32_t nsteps[NS];
-        bool unr[NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            nsteps[s] = act[s] ? st[s].steps(g, gi) : 0u;
-            unr[s] = act[s] && st[s].unrollable(nsteps[s]);
-        }
         if (NS == 2 && unr[0] && unr[NS - 1]) {
-#pragma unroll
-            for (int u = 0; u < kUnrolledSteps; ++u) {
-#pragma unroll
-                for (int s = 0; s < NS; ++s) st[s].template step_held<LOGP>(tab, lb, ctop, u);
-                // both state updates are computed here, next to their table reads
-                asm volatile("" : "+v"(st[0].dec.ncode), "+v"(st[NS - 1].dec.ncode));
-#pragma unroll
-                for (int s = 0; s < NS; ++s) st[s].dec.renorm(lane);
-            }
-#pragma unroll
-            for (int s = 0; s < NS; ++s) st[s].finish_unrolled();
+            paired_steps(st, tab, lane, lb);
         } else {
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 if (unr[s])
-                    st[s].template unrolled<LOGP>(tab, lb, ctop, lane);
+                    st[s].unrolled(tab, lane, lb);
                 else if (act[s])
-                    st[s].template generic<LOGP>(tab, lb, ctop, nsteps[s], lane);
+                    st[s].generic(tab, lane, lb, nsteps[s]);
             }
         }
 
@@ -420,33 +414,6 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
     for (int s = 0; s < NS; ++s) st[s].final_flush();
 }
 
-template <bool SYMBOLS, bool FULL>
-__device__ __forceinline__ void decode_dispatch(uint32_t logp, bool pair, const Geom &g,
-                                                const uint8_t *tab, uint16_t *ring,
-                                                const uint8_t *container, const ContainerView &cv,
-                                                uint32_t k0, uint32_t k1, uint32_t row, uint32_t b,
-                                                uint32_t lane, uint16_t *out, uint8_t *sym_out)
-{
-#define CG_DECODE_CASE(LP)                                                                        \
-    case LP:                                                                                      \
-        if (pair)                                                                                 \
-            decode_chunks<LP, SYMBOLS, FULL, 2>(g, tab, ring, container, cv, k0, k1, row, b,      \
-                                                lane, out, sym_out);                              \
-        else                                                                                      \
-            decode_chunks<LP, SYMBOLS, FULL, 1>(g, tab, ring, container, cv, k0, k1, row, b,      \
-                                                lane, out, sym_out);                              \
-        break;
-    switch (logp) {
-        CG_DECODE_CASE(1)
-        CG_DECODE_CASE(2)
-        CG_DECODE_CASE(3)
-        CG_DECODE_CASE(4)
-    default:
-        CG_DECODE_CASE(5)
-    }
-#undef CG_DECODE_CASE
-}
-
 // Block = WPB wavefronts over the chunks [kb + 2 WPB set, kb + 2 WPB (set + 1)) of one
 // (row, channel block); wavefront w takes chunks base + w and base + w + WPB.  Launches
 // over many chunks use 4 wavefronts per block, sharing the staged table; launches over
@@ -454,28 +421,27 @@ __device__ __forceinline__ void decode_dispatch(uint32_t logp, bool pair, const 
 template <bool SYMBOLS, uint32_t WPB>
 __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
                                                   const uint32_t *__restrict__ dtab,
+                                                  const float *__restrict__ lo,
+                                                  const float *__restrict__ w,
                                                   const uint8_t *__restrict__ container,
                                                   ContainerView cv, uint32_t n_sets,
                                                   uint16_t *__restrict__ out,
                                                   uint8_t *__restrict__ sym_out)
 {
-    __shared__ uint32_t tab[kTabBlock];
+    __shared__ uint32_t tab[kLdsWords];
     __shared__ uint16_t rings[WPB * kStreamsPerWave * kRingAlloc];
     const uint32_t set = blockIdx.x % n_sets;
     const uint32_t tmp = blockIdx.x / n_sets;
     const uint32_t b = tmp % g.NB;
     const uint32_t row = tmp / g.NB;
     const uint32_t N = bins[row >> 1];
-    uint32_t logp = 0;
-    while ((1u << logp) < N) ++logp;
-    // stage the P = 2^logp used entries of both planes
-    const uint32_t n16 = ((1u << logp) * kLanes) / 4;  // 16-byte pieces per plane
+    // stage the N used entries and the slot table
+    const uint32_t n16 = (N * kLanes) / 4;  // 16-byte pieces of entries
     const uint4 *src = reinterpret_cast<const uint4 *>(dtab + (uint64_t)(row * g.NB + b) * kTabBlock);
     uint4 *dst = reinterpret_cast<uint4 *>(tab);
-    for (uint32_t j = threadIdx.x; j < n16; j += blockDim.x) {
-        dst[j] = src[j];
-        dst[kTabPlane / 4 + j] = src[kTabPlane / 4 + j];
-    }
+    for (uint32_t j = threadIdx.x; j < n16; j += blockDim.x) dst[j] = src[j];
+    for (uint32_t j = threadIdx.x; j < kProbTotal * kLanes / 16; j += blockDim.x)
+        dst[kTabPlane / 4 + j] = src[kTabLut / 4 + j];
     __syncthreads();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     const uint32_t lane = threadIdx.x % kLanes;
@@ -485,12 +451,17 @@ __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__r
     const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab);
     uint16_t *ring = rings + wave * kStreamsPerWave * kRingAlloc;
     const bool pair = k1 < g.ke;
-    if (g.C - b * kLanes >= kLanes)
-        decode_dispatch<SYMBOLS, true>(logp, pair, g, tb, ring, container, cv, k0, k1, row, b,
-                                       lane, out, sym_out);
-    else
-        decode_dispatch<SYMBOLS, false>(logp, pair, g, tb, ring, container, cv, k0, k1, row, b,
-                                        lane, out, sym_out);
+    if (g.C - b * kLanes >= kLanes) {
+        if (pair)
+            decode_chunks<SYMBOLS, true, 2>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out);
+        else
+            decode_chunks<SYMBOLS, true, 1>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out);
+    } else {
+        if (pair)
+            decode_chunks<SYMBOLS, false, 2>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out);
+        else
+            decode_chunks<SYMBOLS, false, 1>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out);
+    }
 }
 
 // ------------------------------------------------------------------------------ K4
@@ -550,9 +521,9 @@ __global__ __launch_bounds__(256) void k4_dequant(Geom g, const float *__restric
 }
 
 // ------------------------------------------------------------------------------ launchers
-hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
-                     const uint8_t *container, const ContainerView &cv, uint16_t *out,
-                     uint8_t *sym_out, hipStream_t st)
+hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, const float *lo,
+                     const float *w, const uint8_t *container, const ContainerView &cv,
+                     uint16_t *out, uint8_t *sym_out, hipStream_t st)
 {
     // fewer than 8 chunks: one wavefront per block (see k3_decode)
     const bool wide = g.ke - g.kb >= kWavesPerBlock * kStreamsPerWave;
@@ -564,17 +535,17 @@ hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
     if (sym_out) {
         if (wide)
             hipLaunchKernelGGL((k3_decode<true, kWavesPerBlock>), grid, block, 0, st, g, bins,
-                               dtab, container, cv, n_sets, out, sym_out);
+                               dtab, lo, w, container, cv, n_sets, out, sym_out);
         else
             hipLaunchKernelGGL((k3_decode<true, 1>), grid, block, 0, st, g, bins, dtab,
-                               container, cv, n_sets, out, sym_out);
+                               lo, w, container, cv, n_sets, out, sym_out);
     } else {
         if (wide)
             hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock>), grid, block, 0, st, g, bins,
-                               dtab, container, cv, n_sets, out, sym_out);
+                               dtab, lo, w, container, cv, n_sets, out, sym_out);
         else
             hipLaunchKernelGGL((k3_decode<false, 1>), grid, block, 0, st, g, bins, dtab,
-                               container, cv, n_sets, out, sym_out);
+                               lo, w, container, cv, n_sets, out, sym_out);
     }
     return hipGetLastError();
 }

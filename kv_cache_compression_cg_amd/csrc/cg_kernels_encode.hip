@@ -187,26 +187,25 @@ __global__ __launch_bounds__(256) void k1_freqs(Geom g, const uint8_t *__restric
         if (cnt[s] > cnt[best]) best = s;
     }
     f[best] += kProbTotal - sum;
-    uint32_t P = 1;
-    while (P < N) P <<= 1;
     float lo1 = lo[i], w1 = w[i];
     uint32_t *tb = dtab + (uint64_t)(row * g.NB + c / kLanes) * kTabBlock + (c % kLanes);
     uint32_t cdf = 0;
     for (uint32_t s = 0; s < kMaxBins; ++s) {
         uint32_t fs = (s < N) ? f[s] : 0;
         freqs[(uint64_t)i * kMaxBins + s] = (uint16_t)fs;
-        uint32_t cf, dq;
-        if (s < N) {
-            cf = fs | (cdf << 16);
-            dq = __float_as_uint(fmaf((float)s, w1, lo1));
-        } else {
-            // padding up to a power of two: cdf = T is never <= code for a valid stream
-            cf = kProbTotal << 16;
-            dq = __float_as_uint(fmaf((float)(N - 1u), w1, lo1));
-        }
-        tb[(uint64_t)s * kLanes] = cf;
-        tb[kTabPlane + (uint64_t)s * kLanes] = dq;
+        // (f <= 255 and cdf <= 255 since N >= 2; symbols >= N are never looked up)
+        tb[(uint64_t)s * kLanes] = (s < N) ? fs | (cdf << 24) : 0u;
+        tb[kTabPlane + (uint64_t)s * kLanes] =
+            __float_as_uint(fmaf((float)min(s, N - 1u), w1, lo1));
         cdf += fs;
+    }
+    // slot table: every slot in [cdf[s], cdf[s] + f[s]) names s
+    uint8_t *lut = reinterpret_cast<uint8_t *>(dtab + (uint64_t)(row * g.NB + c / kLanes) * kTabBlock +
+                                               kTabLut) + (c % kLanes);
+    uint32_t s = 0, end = f[0];
+    for (uint32_t slot = 0; slot < kProbTotal; ++slot) {
+        while (slot >= end) end += f[++s];
+        lut[(uint64_t)slot * kLanes] = (uint8_t)s;
     }
 }
 
@@ -274,14 +273,17 @@ __global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict
 }
 
 // ------------------------------------------------------------------------------ K5
-// Range encoder, three passes over the groups (chunk, row, channel block b); a block
-// holds 4 wavefronts = 4 chunks of one (row, b), sharing that pair's {f | cdf << 16}
-// table plane in LDS, and lane i codes the stream of channel 64b + i.  Symbols are loaded
-// eight steps ahead of their use.
-//   plan        replays the range evolution: counts each lane's words and records the
-//               wavefront's renormalisation ballot of every step;
-//   encode      codes each lane's stream into a lane-major scratch (exact size), carries
-//               rippled back into the words already written;
+// rANS encoder, three passes over the groups (chunk, row, channel block b); a block
+// holds 4 wavefronts = 4 chunks of one (row, b), sharing that pair's {f | cdf << 24}
+// table plane in LDS, and lane i codes the stream of channel 64b + i.  The coder runs
+// from the chunk's last symbol to its first; symbols are loaded eight steps ahead.
+//   plan        replays the state evolution: counts each lane's words and records, for
+//               every step, the wavefront's ballot of lanes that shift a word out before
+//               coding that step's symbol -- the lanes whose decoders read a word after
+//               decoding it;
+//   encode      codes each lane's stream into a lane-major scratch of exact size, in
+//               decoder read order (state words first, then the shifted-out words from
+//               the first step to the last, i.e. filled from the end);
 //   interleave  moves every word to the position the lockstep decoders read it from,
 //               following the recorded ballots (no second replay of the coder).
 constexpr uint32_t kSymAhead = 8;
@@ -323,35 +325,52 @@ __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t lane)
 
 
 // Symbol i of a lane's stream sits at token t0 + 1 + i + i / (G - 1): anchors are
-// skipped.  Loads go through a buffer resource over the symbol rows of one (layer, K/V),
-// the lane's channel as vector offset and the token row as scalar offset; reads past
-// the rows return 0.
+// skipped.  The feed walks i = m - 1 down to 0.  Loads go through a buffer resource over
+// the symbol rows of one (layer, K/V), the lane's channel as vector offset and the token
+// row as scalar offset; reads outside the rows return 0 (the look-ahead past i = 0 reads
+// such rows, and is never used).
 struct SymFeed {
     __amdgpu_buffer_rsrc_t rs;
     uint32_t voff, C, G1, rel, pos;
 
+    // m >= 1 and G >= 2
     __device__ __forceinline__ void init(const uint8_t *rows, uint32_t bytes, uint32_t c,
-                                         uint32_t C_, uint32_t G, uint32_t t_rel)
+                                         uint32_t C_, uint32_t G, uint32_t t_rel, uint32_t m)
     {
         rs = make_rsrc(rows, bytes);
         voff = c;
         C = C_;
         G1 = G - 1;
-        rel = t_rel + 1;
-        pos = 0;
+        pos = (m - 1) % G1;
+        rel = t_rel + 1 + (m - 1) + (m - 1) / G1;
     }
-    // issues the load of the next symbol
+    // issues the load of the next symbol (downwards)
     __device__ __forceinline__ uint32_t next()
     {
         const uint32_t v = __builtin_amdgcn_raw_buffer_load_b8(rs, voff, rel * C, 0);
-        rel += 1;
-        if (++pos == G1) {
-            pos = 0;
-            rel += 1;
+        if (pos == 0) {
+            pos = G1 - 1;
+            rel -= 2;
+        } else {
+            --pos;
+            rel -= 1;
         }
         return v;
     }
 };
+
+// One rANS coding step on a table entry {f | cdf << 24}; returns whether the low 16
+// bits of the state were shifted out first (into *word).
+__device__ __forceinline__ bool rans_step(uint32_t &state, uint32_t e, uint32_t &word)
+{
+    const uint32_t f = max(e & 0xFFu, 1u);  // (absent lanes read an unset entry)
+    const bool shift = state >= (f << 24);
+    word = state & 0xFFFFu;
+    if (shift) state >>= 16;
+    const uint32_t q = state / f;
+    state = q * kProbTotal + (state - q * f) + (e >> 24);
+    return shift;
+}
 
 // Block set-up shared by the encoder passes: (row, b, set) from the block index, the
 // P = 2^logp used entries of the table plane staged into LDS.  Returns the chunk of
@@ -395,49 +414,47 @@ __global__ __launch_bounds__(256) void k5_plan(const uint8_t *__restrict__ sym, 
     if (x.m > 0) {  // uniform
         SymFeed sf;
         sf.init(sym + (uint64_t)row * sym_T * g.C, sym_T * g.C, x.present ? x.c : 0, g.C, g.G,
-                x.t0 - sym_t0);
+                x.t0 - sym_t0, x.m);
         const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab) + lane * 4;
         uint64_t *mrow = masks + gidx * mstride;
-        uint32_t range = kRangeInit, ev = 0, mlo = 0, mhi = 0;
-        // one step: the ballot of step i is kept in lane i % 64 and written every 64 steps
+        uint32_t state = kStateLow, ev = 0, mlo = 0, mhi = 0;
+        // one step: the ballot of step i is kept in lane i % 64 and written when i
+        // reaches a multiple of 64 (steps run downwards)
         auto step = [&](uint32_t i, uint32_t s) __attribute__((always_inline)) {
-            const uint32_t f = *reinterpret_cast<const uint16_t *>(tb + s * kSymStride);
-            range = (range >> kProbBits) * f;
-            const bool need = x.present && i + 1 < x.m && range < kRenormBelow;
+            const uint32_t e = *reinterpret_cast<const uint32_t *>(tb + s * kSymStride);
+            uint32_t word;
+            const bool need = rans_step(state, e, word) && x.present;
             const uint64_t mask = __builtin_amdgcn_ballot_w64(need);
-            if (need) {
-                range <<= 16;
-                ++ev;
-            }
+            ev += need ? 1u : 0u;
             const uint32_t j = i % kLanes;
             if (lane == j) {
                 mlo = (uint32_t)mask;
                 mhi = (uint32_t)(mask >> 32);
             }
-            if (j == kLanes - 1 || i + 1 == x.m) {
-                if (lane <= j) {
+            if (j == 0) {
+                if (lane <= min(kLanes - 1, x.m - 1 - i)) {
                     uint2 v;
                     v.x = mlo;
                     v.y = mhi;
-                    *reinterpret_cast<uint2 *>(mrow + (i - j) + lane) = v;
+                    *reinterpret_cast<uint2 *>(mrow + i + lane) = v;
                 }
             }
         };
         uint32_t sr[kSymAhead];
 #pragma unroll
         for (uint32_t r = 0; r < kSymAhead; ++r) sr[r] = sf.next();
-        uint32_t i = 0;
-        for (; i + kSymAhead <= x.m; i += kSymAhead) {
+        uint32_t done = 0;
+        for (; done + kSymAhead <= x.m; done += kSymAhead) {
 #pragma unroll
             for (uint32_t r = 0; r < kSymAhead; ++r) {
                 const uint32_t s_ = sr[r];
                 sr[r] = sf.next();
-                step(i + r, s_);
+                step(x.m - 1 - (done + r), s_);
             }
         }
 #pragma unroll
         for (uint32_t r = 0; r < kSymAhead; ++r)
-            if (i + r < x.m) step(i + r, sr[r]);
+            if (done + r < x.m) step(x.m - 1 - (done + r), sr[r]);
         if (x.present) words = 2 + ev;
     }
     lane_words[gidx * kLanes + lane] = words;
@@ -493,52 +510,34 @@ __global__ __launch_bounds__(256) void k5_encode(const uint8_t *__restrict__ sym
     const uint32_t lane_off = wave_excl_scan(nwords, lane);
     if (x.m == 0) return;  // uniform
     uint16_t *out = scratch + group_off[gidx] + lane_off;
+    if (!x.present) return;
     SymFeed sf;
-    sf.init(sym + (uint64_t)row * sym_T * g.C, sym_T * g.C, x.present ? x.c : 0, g.C, g.G,
-            x.t0 - sym_t0);
+    sf.init(sym + (uint64_t)row * sym_T * g.C, sym_T * g.C, x.c, g.C, g.G, x.t0 - sym_t0, x.m);
     const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab) + lane * 4;
-    uint64_t low = 0;
-    uint32_t range = kRangeInit, nw = 0;
-    auto step = [&](uint32_t i, uint32_t s) __attribute__((always_inline)) {
+    // words shifted out at steps m-1, m-2, ... fill the scratch from its end
+    uint32_t state = kStateLow, pos = nwords - 1;
+    auto step = [&](uint32_t s) __attribute__((always_inline)) {
         const uint32_t e = *reinterpret_cast<const uint32_t *>(tb + s * kSymStride);
-        const uint32_t q = range >> kProbBits;
-        low += (uint64_t)q * (e >> 16);
-        range = q * (e & 0xFFFFu);
-        if (low >> 32) {  // carry into the words already written
-            low &= 0xFFFFFFFFull;
-            uint32_t j = nw;
-            uint16_t v;
-            do {
-                --j;
-                v = (uint16_t)(out[j] + 1u);
-                out[j] = v;
-            } while (v == 0 && j > 0);
-        }
-        if (i + 1 < x.m && range < kRenormBelow) {
-            out[nw++] = (uint16_t)(low >> 16);
-            low = (low & 0xFFFFull) << 16;
-            range <<= 16;
-        }
+        uint32_t word;
+        if (rans_step(state, e, word)) out[pos--] = (uint16_t)word;
     };
     uint32_t sr[kSymAhead];
 #pragma unroll
     for (uint32_t r = 0; r < kSymAhead; ++r) sr[r] = sf.next();
-    uint32_t i = 0;
-    if (x.present) {
-        for (; i + kSymAhead <= x.m; i += kSymAhead) {
+    uint32_t done = 0;
+    for (; done + kSymAhead <= x.m; done += kSymAhead) {
 #pragma unroll
-            for (uint32_t r = 0; r < kSymAhead; ++r) {
-                const uint32_t s_ = sr[r];
-                sr[r] = sf.next();
-                step(i + r, s_);
-            }
+        for (uint32_t r = 0; r < kSymAhead; ++r) {
+            const uint32_t s_ = sr[r];
+            sr[r] = sf.next();
+            step(s_);
         }
-#pragma unroll
-        for (uint32_t r = 0; r < kSymAhead; ++r)
-            if (i + r < x.m) step(i + r, sr[r]);
-        out[nw++] = (uint16_t)(low >> 16);
-        out[nw++] = (uint16_t)(low & 0xFFFFu);
     }
+#pragma unroll
+    for (uint32_t r = 0; r < kSymAhead; ++r)
+        if (done + r < x.m) step(sr[r]);
+    out[0] = (uint16_t)(state >> 16);
+    out[1] = (uint16_t)(state & 0xFFFFu);
 }
 
 __global__ __launch_bounds__(256) void k5_interleave(Geom g, uint32_t n_sets,

@@ -7,7 +7,7 @@ and numpy; it shares no code with the GPU library and never imports it.
 Parity status of each function is listed in its docstring; every function here is
 pinned by the CPU tests in tests/test_oracle_pins.py against properties fixed by the
 pages or by mathematics (closed-form sizes, exhaustive round trips, a big-integer
-model of the coder, exact rational bounds, brute force on tiny tensors).
+closed form of the coder on uniform tables, exact rational bounds, brute force on tiny tensors).
 """
 from __future__ import annotations
 
@@ -24,7 +24,7 @@ SRC = os.path.join(HERE, "cgo.c")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(BUILD_DIR, "libcgo.so")
 
-PROB_BITS = 12
+PROB_BITS = 8
 PROB_TOTAL = 1 << PROB_BITS
 MAX_BINS = 32
 LANES = 64
@@ -65,10 +65,11 @@ def lib() -> ctypes.CDLL:
         L.cgo_histograms.argtypes = [_u32] * 6 + [_u8p, _u8p, _u64p]
         L.cgo_freqs.argtypes = [_u32, _u32, _u8p, _u64p, _u16p]
         L.cgo_freqs_from_counts.argtypes = [_u64p, _u32, _u16p]
-        L.cgo_rc_encode.argtypes = [_u8p, _u32, _u16p, _u32, _u16p, _i32p]
-        L.cgo_rc_encode.restype = _u32
-        L.cgo_rc_decode.argtypes = [_u16p, _u32, _u32, _u16p, _u32, _u8p]
-        L.cgo_rc_decode.restype = _u32
+        L.cgo_rans_encode.argtypes = [_u8p, _u32, _u16p, _u32, _u16p, _i32p]
+        L.cgo_rans_encode.restype = _u32
+        L.cgo_rans_decode.argtypes = [_u16p, _u32, _u32, _u16p, _u32, _u8p,
+                                      ctypes.POINTER(ctypes.c_uint32)]
+        L.cgo_rans_decode.restype = _u32
         L.cgo_num_groups.argtypes = [_u32, _u32, _u32, _u32]
         L.cgo_num_groups.restype = ctypes.c_uint64
         L.cgo_anchor_rows.argtypes = [_u32] * 6
@@ -195,28 +196,30 @@ def quantize(shp: Shape, X: np.ndarray, lo: np.ndarray, r: np.ndarray,
     return sym
 
 
-# ------------------------------------------------------------------ range coder
-def rc_encode(x: Sequence[int], f: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
-    """Single stream: returns (words uint16, read step of every word int32)."""
+# ------------------------------------------------------------------ rANS coder
+def rans_encode(x: Sequence[int], f: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """Single stream: returns (words uint16 in read order, read step of every word int32)."""
     x = np.ascontiguousarray(np.asarray(x, dtype=np.uint8))
     f = np.ascontiguousarray(np.asarray(f, dtype=np.uint16))
     words = np.zeros(len(x) + 2, np.uint16)
     steps = np.zeros(len(x) + 2, np.int32)
-    n = lib().cgo_rc_encode(_p(x, _u8p), len(x), _p(f, _u16p), len(f), _p(words, _u16p),
-                            _p(steps, _i32p))
+    n = lib().cgo_rans_encode(_p(x, _u8p), len(x), _p(f, _u16p), len(f), _p(words, _u16p),
+                              _p(steps, _i32p))
     return words[:n].copy(), steps[:n].copy()
 
 
-def rc_decode(words: Sequence[int], m: int, f: Sequence[int]) -> Tuple[np.ndarray, int]:
+def rans_decode(words: Sequence[int], m: int, f: Sequence[int]) -> Tuple[np.ndarray, int, int]:
+    """Returns (symbols, words consumed, final decoder state)."""
     words = np.ascontiguousarray(np.asarray(words, dtype=np.uint16))
     if words.size == 0:
         words = np.zeros(1, np.uint16)[:0]
     f = np.ascontiguousarray(np.asarray(f, dtype=np.uint16))
     out = np.zeros(max(m, 1), np.uint8)
     buf = np.ascontiguousarray(np.concatenate([words, np.zeros(1, np.uint16)]))
-    used = lib().cgo_rc_decode(_p(buf, _u16p), len(words), m, _p(f, _u16p), len(f),
-                               _p(out, _u8p))
-    return out[:m].copy(), int(used)
+    fin = ctypes.c_uint32(0)
+    used = lib().cgo_rans_decode(_p(buf, _u16p), len(words), m, _p(f, _u16p), len(f),
+                                 _p(out, _u8p), ctypes.byref(fin))
+    return out[:m].copy(), int(used), int(fin.value)
 
 
 # ------------------------------------------------------------------ container

@@ -20,11 +20,12 @@
  *      (Solution pillar 1; the gptget.net summary of CacheGen, Methodology), using a
  *      min/max affine grid as in Implementation Step 1 (quantize_tensor /
  *      dequantize_tensor) but taken per channel over the non-anchor deltas;
- *   4. symbols are entropy-coded with an arithmetic (range) coder driven by empirical
+ *   4. symbols are entropy-coded with an arithmetic-type coder driven by empirical
  *      frequency tables (Solution pillar 3; the summary's Deep Analysis, Methodology:
- *      delta coding combined with arithmetic coding, per layer and channel), one
- *      independent stream per (layer, K/V, channel, chunk) so chunks decode on their own
- *      (summary, Methodology: the cache is cut into chunks that are streamed);
+ *      delta coding combined with arithmetic coding, per layer and channel), here range
+ *      asymmetric numeral systems (rANS), one independent stream per (layer, K/V,
+ *      channel, chunk) so chunks decode on their own (summary, Methodology: the cache is
+ *      cut into chunks that are streamed);
  *   5. decoding inverts 4, then dequantizes and adds the anchor back (Implementation
  *      Step 1 dequantize_tensor, computed in float32; Step 2 decode_sequence).
  *
@@ -37,12 +38,11 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define CGO_PROB_BITS 12u
-#define CGO_PROB_TOTAL (1u << CGO_PROB_BITS) /* frequencies sum to 4096 */
+#define CGO_PROB_BITS 8u
+#define CGO_PROB_TOTAL (1u << CGO_PROB_BITS) /* frequencies sum to 256 */
 #define CGO_MAX_BINS 32u
 #define CGO_LANES 64u                       /* channels per interleaved group */
-#define CGO_RANGE_INIT 0x7FFFFFFFu           /* 31-bit range: every product fits a signed int */
-#define CGO_RENORM_BELOW 0x8000u            /* renormalise when range < 2^15 */
+#define CGO_STATE_LOW 0x10000u              /* coder state lives in [2^16, 2^32) */
 
 /* ------------------------------------------------------------------------------ */
 /* IEEE-754 binary16 <-> binary32, written from the format definition.             */
@@ -221,7 +221,7 @@ void cgo_quantize(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, ui
 
 /* ------------------------------------------------------------------------------ */
 /* Step 4a: empirical frequency table per (layer, K/V, channel), shared by all     */
-/* chunks of the channel.  Frequencies sum to T = 4096 and every symbol gets f >= 1: */
+/* chunks of the channel.  Frequencies sum to T = 256 and every symbol gets f >= 1:  */
 /*   f[s] = 1 + floor(count[s] * (T - N) / n)     (n = sum of counts; 0 if n == 0)   */
 /* and the remainder T - sum(f) goes to the most frequent symbol (lowest index on    */
 /* ties).  freqs is [L][2][C][32], entries beyond N are 0.                           */
@@ -274,96 +274,95 @@ void cgo_freqs(uint32_t L, uint32_t C, const uint8_t *bins, const uint64_t *coun
 }
 
 /* ------------------------------------------------------------------------------ */
-/* Step 4b: range coder (G. N. N. Martin, "Range encoding", 1979), multi-symbol,     */
-/* 31-bit range, 16-bit output words, probabilities in units of 1/4096.              */
-/*                                                                                    */
-/* Encoder, for symbols x_0 .. x_{m-1} with cumulative table cdf (cdf[N] = 4096):    */
-/*   low = 0, range = 2^31 - 1                                                        */
-/*   for each i: q = range >> 12; low += q * cdf[x_i]; range = q * f[x_i];            */
-/*               if i < m - 1 and range < 2^15: shift one 16-bit word out of low,     */
-/*               low <<= 16, range <<= 16   (a "renormalisation event" at step i)    */
-/*   the stream is the 2 + (number of events) base-65536 digits of the final low,    */
-/*   most significant first.  Carries out of the 32-bit window are added into the    */
-/*   words already written.  m == 0 gives an empty stream.                           */
-/* Word j is read by the decoder at step -1 (start) for j < 2, else at the step of    */
-/* event j - 2; steps_out receives that step for every word.                          */
-/* Returns the number of words.                                                       */
+/* Step 4b: rANS (J. Duda, "Asymmetric numeral systems", 2009/2013), probabilities   */
+/* in units of 1/256, a 32-bit state kept in [2^16, 2^32) and 16-bit output words.    */
+/* With cdf[s] = f[0] + ... + f[s-1]:                                                  */
+/*   coding step   C(s, x) = floor(x / f[s]) * 256 + (x mod f[s]) + cdf[s]            */
+/*   decoding step slot = x mod 256; s = the symbol with cdf[s] <= slot < cdf[s+1];  */
+/*                 x = f[s] * floor(x / 256) + slot - cdf[s]     (inverts C exactly)  */
+/* The encoder runs over x_{m-1} .. x_0 from x = 2^16; before coding x_i it shifts    */
+/* out the low 16 bits of x when x >= f[s] * 2^24, which keeps C(s, x) below 2^32.    */
+/* The decoder runs forward from the final encoder state (the stream's first two     */
+/* words, high half first) and, after decoding x_i, pulls in a word exactly when x    */
+/* fell below 2^16 -- the word the encoder shifted out before coding x_i -- so it     */
+/* reads the words in the reverse of the order they were produced and ends in state   */
+/* 2^16.  The encoder never shifts before x_{m-1} (x = 2^16 < f * 2^24), so no word   */
+/* follows the last symbol.  m == 0 gives an empty stream.                            */
+/* Words are returned in read order; steps_out receives the decoder step reading each */
+/* word: -1 for the two state words, else i.  Returns the number of words.            */
 /* ------------------------------------------------------------------------------ */
-uint32_t cgo_rc_encode(const uint8_t *x, uint32_t m, const uint16_t *f, uint32_t N,
-                       uint16_t *words, int32_t *steps_out)
+static void make_cdf(const uint16_t *f, uint32_t N, uint32_t *cdf)
 {
-    uint32_t cdf[CGO_MAX_BINS + 1];
     cdf[0] = 0;
     for (uint32_t s = 0; s < N; s++)
         cdf[s + 1] = cdf[s] + f[s];
+}
+
+uint32_t cgo_rans_encode(const uint8_t *x, uint32_t m, const uint16_t *f, uint32_t N,
+                         uint16_t *words, int32_t *steps_out)
+{
+    uint32_t cdf[CGO_MAX_BINS + 1];
+    make_cdf(f, N, cdf);
     if (m == 0)
         return 0;
-    uint64_t low = 0;
-    uint32_t range = CGO_RANGE_INIT;
-    uint32_t nw = 0, nev = 0;
-    int32_t *event_step = (int32_t *)malloc(sizeof(int32_t) * (m + 1));
-    for (uint32_t i = 0; i < m; i++) {
-        uint32_t s = x[i];
-        uint32_t q = range >> CGO_PROB_BITS;
-        low += (uint64_t)q * cdf[s];
-        range = q * f[s];
-        if (low >> 32) {                 /* carry into the words already written */
-            low &= 0xFFFFFFFFu;
-            uint32_t j = nw;
-            do {
-                j--;
-                words[j] = (uint16_t)(words[j] + 1u);
-            } while (words[j] == 0);
+    /* produced[j] / step[j]: words in production order (highest step first) */
+    uint16_t *produced = (uint16_t *)malloc(sizeof(uint16_t) * (m + 1));
+    int32_t *step = (int32_t *)malloc(sizeof(int32_t) * (m + 1));
+    uint32_t np = 0;
+    uint32_t state = CGO_STATE_LOW;
+    for (uint32_t i = m; i-- > 0;) {
+        uint32_t s = x[i], fs = f[s];
+        if ((uint64_t)state >= ((uint64_t)fs << 24)) {
+            produced[np] = (uint16_t)(state & 0xFFFFu);
+            step[np++] = (int32_t)i;
+            state >>= 16;
         }
-        if (i + 1 < m && range < CGO_RENORM_BELOW) {
-            words[nw++] = (uint16_t)(low >> 16);
-            low = (low & 0xFFFFu) << 16;
-            range <<= 16;
-            event_step[nev++] = (int32_t)i;
-        }
+        state = (state / fs) * CGO_PROB_TOTAL + state % fs + cdf[s];
     }
-    words[nw++] = (uint16_t)(low >> 16);
-    words[nw++] = (uint16_t)(low & 0xFFFFu);
-    if (steps_out)
-        for (uint32_t j = 0; j < nw; j++)
-            steps_out[j] = (j < 2) ? -1 : event_step[j - 2];
-    free(event_step);
+    uint32_t nw = 0;
+    words[nw] = (uint16_t)(state >> 16);
+    if (steps_out) steps_out[nw] = -1;
+    nw++;
+    words[nw] = (uint16_t)(state & 0xFFFFu);
+    if (steps_out) steps_out[nw] = -1;
+    nw++;
+    for (uint32_t j = np; j-- > 0;) {
+        words[nw] = produced[j];
+        if (steps_out) steps_out[nw] = step[j];
+        nw++;
+    }
+    free(produced);
+    free(step);
     return nw;
 }
 
-/* Decoder: code = words 0..1; range = 2^31 - 1; then for each step q = range >> 12, the
- * symbol is the largest s with q * cdf[s] <= code; code -= q * cdf[s]; range = q * f[s];
- * and, except after the last symbol, range < 2^15 pulls in the next word.  Words past
- * the end of the stream read as 0.  Returns the number of words consumed. */
-uint32_t cgo_rc_decode(const uint16_t *words, uint32_t nw, uint32_t m, const uint16_t *f,
-                       uint32_t N, uint8_t *x_out)
+/* Decodes m symbols; words past the end of the stream read as 0.  Returns the number
+ * of words consumed; *final_state (if given) receives the state after the last symbol
+ * (2^16 for an intact stream). */
+uint32_t cgo_rans_decode(const uint16_t *words, uint32_t nw, uint32_t m, const uint16_t *f,
+                         uint32_t N, uint8_t *x_out, uint32_t *final_state)
 {
     uint32_t cdf[CGO_MAX_BINS + 1];
-    cdf[0] = 0;
-    for (uint32_t s = 0; s < N; s++)
-        cdf[s + 1] = cdf[s] + f[s];
+    make_cdf(f, N, cdf);
+    if (final_state) *final_state = CGO_STATE_LOW;
     if (m == 0)
         return 0;
     uint32_t pos = 0;
 #define NEXTW() (pos < nw ? words[pos++] : (pos++, 0u))
-    uint32_t code = NEXTW();
-    code = (code << 16) | NEXTW();
-    uint32_t range = CGO_RANGE_INIT;
+    uint32_t state = NEXTW();
+    state = (state << 16) | NEXTW();
     for (uint32_t i = 0; i < m; i++) {
-        uint32_t q = range >> CGO_PROB_BITS;
-        uint32_t s = 0;
+        uint32_t slot = state % CGO_PROB_TOTAL, s = 0;
         for (uint32_t j = 1; j < N; j++)
-            if (q * cdf[j] <= code)
+            if (cdf[j] <= slot)
                 s = j;
-        code -= q * cdf[s];
-        range = q * f[s];
+        state = f[s] * (state / CGO_PROB_TOTAL) + slot - cdf[s];
         x_out[i] = (uint8_t)s;
-        if (i + 1 < m && range < CGO_RENORM_BELOW) {
-            code = (code << 16) | NEXTW();
-            range <<= 16;
-        }
+        if (i + 1 < m && state < CGO_STATE_LOW)
+            state = (state << 16) | NEXTW();
     }
 #undef NEXTW
+    if (final_state) *final_state = state;
     return pos;
 }
 
@@ -447,8 +446,8 @@ int64_t cgo_encode_payload(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint3
                             if (!cgo_is_anchor(t, G, Tc))
                                 x[m++] = sym[kv_index(&p, l, kv, t, c)];
                         size_t row = ((size_t)l * 2 + kv) * C + c;
-                        nw[lane] = cgo_rc_encode(x, m, freqs + row * CGO_MAX_BINS, bins[l],
-                                                 w[lane], st[lane]);
+                        nw[lane] = cgo_rans_encode(x, m, freqs + row * CGO_MAX_BINS, bins[l],
+                                                   w[lane], st[lane]);
                         rd[lane] = 0;
                     }
                     /* merge in the order the lockstep decoders read the words */
@@ -509,7 +508,7 @@ int cgo_decode(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint3
                     if (end < beg || end > payload_words)
                         return -5;
                     uint32_t lanes = (C - b * CGO_LANES < CGO_LANES) ? C - b * CGO_LANES : CGO_LANES;
-                    uint32_t code[CGO_LANES], range[CGO_LANES], cdf[CGO_LANES][CGO_MAX_BINS + 1];
+                    uint32_t state[CGO_LANES], cdf[CGO_LANES][CGO_MAX_BINS + 1];
                     uint64_t cur = beg;
                     if (m == 0)
                         continue;
@@ -520,8 +519,7 @@ int cgo_decode(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint3
                         for (uint32_t s = 0; s < bins[l]; s++)
                             cdf[lane][s + 1] = cdf[lane][s] + freqs[row * CGO_MAX_BINS + s];
                         uint32_t hi16 = GROUPW();
-                        code[lane] = (hi16 << 16) | GROUPW();
-                        range[lane] = CGO_RANGE_INIT;
+                        state[lane] = (hi16 << 16) | GROUPW();
                     }
                     uint32_t i = 0;
                     for (uint32_t t = t0; t < t0 + len; t++) {
@@ -531,22 +529,20 @@ int cgo_decode(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint3
                         for (uint32_t lane = 0; lane < lanes; lane++) {
                             uint32_t c = b * CGO_LANES + lane;
                             size_t row = ((size_t)l * 2 + kv) * C + c;
-                            uint32_t q = range[lane] >> CGO_PROB_BITS, s = 0;
+                            uint32_t slot = state[lane] % CGO_PROB_TOTAL, s = 0;
                             for (uint32_t j = 1; j < bins[l]; j++)
-                                if (q * cdf[lane][j] <= code[lane])
+                                if (cdf[lane][j] <= slot)
                                     s = j;
-                            code[lane] -= q * cdf[lane][s];
-                            range[lane] = q * (cdf[lane][s + 1] - cdf[lane][s]);
+                            state[lane] = (cdf[lane][s + 1] - cdf[lane][s]) *
+                                              (state[lane] / CGO_PROB_TOTAL) + slot - cdf[lane][s];
                             float anchor = cgo_half_to_float(out[kv_index(&p, l, kv, a, c)]);
                             float y = anchor + fmaf((float)s, w[row], lo[row]);
                             out[kv_index(&p, l, kv, t, c)] = cgo_float_to_half(y);
                         }
                         if (i + 1 < m)
                             for (uint32_t lane = 0; lane < lanes; lane++)
-                                if (range[lane] < CGO_RENORM_BELOW) {
-                                    code[lane] = (code[lane] << 16) | GROUPW();
-                                    range[lane] <<= 16;
-                                }
+                                if (state[lane] < CGO_STATE_LOW)
+                                    state[lane] = (state[lane] << 16) | GROUPW();
                         i++;
                     }
 #undef GROUPW

@@ -2,8 +2,8 @@
 
 Every check here is independent of the oracle's own code: printed sizes from the pages,
 a by-hand transcription of the pages' windowing, numpy's IEEE fp16 conversion, exact
-rational arithmetic, exhaustive round trips, a big-integer model of the coder with no
-window or carry logic, and a sort-based model of the stream interleaving.
+rational arithmetic, exhaustive round trips, the coder's closed form on uniform tables
+and its information bound, and a sort-based model of the stream interleaving.
 """
 import itertools
 import math
@@ -212,52 +212,59 @@ def test_frequency_table_invariants(N, data):
         assert f[0] == T - N + 1 and (f[1:] == 1).all()
 
 
-# --------------------------------------------------------------------------- range coder
-def _big_model(x, f):
-    """Exact big-integer model of the coder (no 32-bit window, no carry handling)."""
-    cdf = np.concatenate([[0], np.cumsum(f)]).astype(int)
-    L, R, scale_words, events = 0, 2 ** 31 - 1, 0, []
-    for i, s in enumerate(x):
-        q = R // T
-        L += q * int(cdf[s])
-        R = q * int(f[s])
-        if i + 1 < len(x) and R < 2 ** 15:
-            L *= 2 ** 16
-            R *= 2 ** 16
-            scale_words += 1
-            events.append(i)
-    nw = 2 + scale_words
-    assert L + R <= (2 ** 31) * 2 ** (16 * scale_words)
-    words = [(L >> (16 * (nw - 1 - j))) & 0xFFFF for j in range(nw)]
-    steps = [-1, -1] + events
-    return words, steps
+# --------------------------------------------------------------------------- rANS coder
+FREQ_SETS = [[T // 2, T // 2], [1, T - 1], [T - 1, 1], [1, 1, T - 3, 1], [60, 60, 60, 76],
+             [1, 2, 3, T - 6], [7, 241, 7, 1]]
+STATE_LOW = 2 ** 16
 
 
-FREQ_SETS = [[T // 2, T // 2], [1, T - 1], [T - 1, 1], [1, 1, T - 3, 1], [1000, 1000, 1000, 1096],
-             [1, 2, 3, T - 6], [7, 4081, 7, 1]]
+def _check_steps(steps, m):
+    """Two state words read before step 0, then at most one word per step, never after
+    the last symbol, in increasing step order."""
+    assert list(steps[:2]) == [-1, -1]
+    rest = [int(v) for v in steps[2:]]
+    assert rest == sorted(set(rest)) and all(0 <= v <= m - 2 for v in rest)
 
 
-def test_coder_exhaustive_round_trip_and_big_integer_model():
+def test_coder_exhaustive_round_trip_and_final_state():
     n_cases = 0
     for f in FREQ_SETS:
         N = len(f)
         for m in range(0, 7):
             for x in itertools.product(range(N), repeat=m):
-                words, steps = O.rc_encode(x, f)
+                words, steps = O.rans_encode(x, f)
                 if m == 0:
                     assert words.size == 0
                     continue
-                bw, bs = _big_model(x, f)
-                assert list(words) == bw and list(steps) == bs
-                dec, used = O.rc_decode(words, m, f)
+                _check_steps(steps, m)
+                dec, used, fin = O.rans_decode(words, m, f)
                 assert list(dec) == list(x) and used == len(words)
+                assert fin == STATE_LOW  # the decoder retraces the encoder to its start
                 n_cases += 1
     assert n_cases > 10000
 
 
+@pytest.mark.parametrize("bits", [1, 2, 3, 5])
+def test_coder_uniform_tables_insert_symbol_bits(bits):
+    """With N = 2^b equal frequencies f = 256 / N, one coding step writes the symbol's b
+    bits into the state at bit 8 - b and moves the bits above up (floor(x / f) * 256 +
+    x mod f + s * f).  From x = 2^16 and while no word is shifted out (b * m <= 15) the
+    stream is the two halves of 2^(16 + b m) + sum_i x_i 2^(8 - b + b i)."""
+    N = 2 ** bits
+    f = [T // N] * N
+    rng = np.random.default_rng(bits)
+    for m in range(1, 15 // bits + 1):
+        for _ in range(20):
+            x = [int(v) for v in rng.integers(0, N, m)]
+            state = 2 ** (16 + bits * m) + sum(s << (8 - bits + bits * i) for i, s in enumerate(x))
+            words, steps = O.rans_encode(x, f)
+            assert list(words) == [state >> 16, state & 0xFFFF]
+            assert list(steps) == [-1, -1]
+
+
 @settings(max_examples=150, deadline=None)
 @given(data=st.data())
-def test_coder_random_streams_against_big_model_and_length_bound(data):
+def test_coder_random_streams_round_trip_and_length_bound(data):
     N = data.draw(st.integers(2, 32))
     counts = data.draw(st.lists(st.integers(0, 5000), min_size=N, max_size=N))
     f = O.freqs_from_counts(counts, N)
@@ -265,20 +272,21 @@ def test_coder_random_streams_against_big_model_and_length_bound(data):
     m = data.draw(st.integers(1, 1500))
     rng = np.random.default_rng(data.draw(st.integers(0, 2 ** 31)))
     x = rng.choice(N, size=m, p=p)
-    words, steps = O.rc_encode(x, f)
-    bw, bs = _big_model(x, f)
-    assert list(words) == bw and list(steps) == bs
-    dec, used = O.rc_decode(words, m, f)
-    assert np.array_equal(dec, x) and used == len(words)
-    # each step loses at most log2(8/7) bits (range >= 2^15 before every step, so
-    # q * 4096 > range - 4096 >= range * 7/8)
+    words, steps = O.rans_encode(x, f)
+    _check_steps(steps, m)
+    dec, used, fin = O.rans_decode(words, m, f)
+    assert np.array_equal(dec, x) and used == len(words) and fin == STATE_LOW
+    # log2 of the state plus 16 per word shifted out grows by at most log2(256 / f) +
+    # log2(1 + 2^-8) per step (the state is >= 2^8 f when coded), starts at 16 and ends
+    # at >= 16 + 16 * (words - 2)
     ideal = float(np.sum(np.log2(T / f[x].astype(np.float64))))
-    assert 16 * len(words) <= ideal + m * math.log2(8 / 7) + 32 + 1e-6
+    assert 16 * len(words) <= ideal + m * math.log2(1 + 2 ** -8) + 32 + 1e-6
 
 
 def test_coded_size_close_to_empirical_entropy():
-    """Over realistic streams the coder spends within a few percent of the empirical
-    entropy of the channel's symbols (plus the two flushed words per stream)."""
+    """Over realistic streams the coder spends what the frequency tables imply (their
+    cross-entropy against the counts, within the per-step bound, plus the two state
+    words per stream), and that is within a few percent of the empirical entropy."""
     shp, X = _small_data(L=2, S=1200, C=8, G=10, Tc=400, bins=(8, 32), seed=5)
     tab = O.build_tables(shp, X)
     enc = O.encode(shp, X, tab)
@@ -287,8 +295,11 @@ def test_coded_size_close_to_empirical_entropy():
     p = np.where(cnt > 0, cnt / np.maximum(n, 1), 1.0)
     h_emp_bits = float(-(cnt * np.log2(p)).sum())
     n_streams = shp.L * 2 * shp.C * shp.n_chunks
+    f = np.maximum(tab.freqs.astype(np.float64), 1.0)
+    cross_bits = float((cnt * np.log2(T / f)).sum())
     coded = enc.payload.size * 16
-    assert coded <= 1.03 * h_emp_bits + 32 * n_streams
+    assert coded <= cross_bits + cnt.sum() * math.log2(1 + 2 ** -8) + 32 * n_streams + 1e-6
+    assert cross_bits <= 1.05 * h_emp_bits
     assert coded >= h_emp_bits * 0.99
 
 
@@ -311,7 +322,7 @@ def test_group_words_follow_lockstep_read_order():
                     for lane in range(min(O.LANES, shp.C - b * O.LANES)):
                         c = b * O.LANES + lane
                         x = [int(sym[l, kv, t, c]) for t in toks]
-                        words, steps = O.rc_encode(x, tab.freqs[l, kv, c, :shp.bins[l]])
+                        words, steps = O.rans_encode(x, tab.freqs[l, kv, c, :shp.bins[l]])
                         keyed += [((int(s), lane, j), int(wd))
                                   for j, (wd, s) in enumerate(zip(words, steps))]
                     expect = [wd for _, wd in sorted(keyed)]
