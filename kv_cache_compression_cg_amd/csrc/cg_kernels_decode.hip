@@ -32,12 +32,13 @@ __device__ __forceinline__ void ring_put(uint16_t *ring, uint32_t pos, uint32_t 
     if (slot < 64) *reinterpret_cast<uint32_t *>(ring + slot + kRingWords) = v;
 }
 
-// The block's table in LDS: the entry of symbol s for this lane {f | cdf << 24} at byte
-// 256 s + 4 lane (lanes never conflict, whatever symbols they are at), then the slot
-// table, byte 64 slot + lane.  The dequantized delta lo + s * w is recomputed (one
-// conversion and one fma, as the table builder does) rather than staged.
-constexpr uint32_t kLdsLut = kTabPlane * 4;
-constexpr uint32_t kLdsWords = kTabPlane + kProbTotal * kLanes / 4;
+// The block's table in LDS, all bytes: f of symbol s for this lane at 64 s + lane, cdf of
+// s 2 KiB further, then the slot table at 64 slot + lane (20 KiB in all).  The
+// dequantized delta lo + s * w is recomputed (one conversion and one fma, as the table
+// builder does) rather than staged.
+constexpr uint32_t kLdsCdf = kMaxBins * kLanes;
+constexpr uint32_t kLdsLut = 2 * kMaxBins * kLanes;
+constexpr uint32_t kLdsWords = (kLdsLut + kProbTotal * kLanes) / 4;
 
 struct WaveDecoder {
     uint32_t x;        // rANS state, in [2^16, 2^32) between symbols
@@ -49,18 +50,17 @@ struct WaveDecoder {
     bool present;
 
     // Decodes one symbol: the low 8 bits of the state name a slot, the slot table names
-    // the symbol, and x = f * (x >> 8) + slot - cdf (f in the low byte of the entry, so
-    // the 24-bit multiply sees f alone).  Returns the byte offset of the symbol's entry.
+    // the symbol, and x = f * (x >> 8) + slot - cdf.  Returns the symbol.
     __device__ __forceinline__ uint32_t symbol(const uint8_t *tab, uint32_t lane, uint32_t lb,
                                                float &dq)
     {
         const uint32_t slot = x & (kProbTotal - 1u);
         const uint32_t s = tab[kLdsLut + slot * kLanes + lane];
-        const uint32_t p = s * kSymStride + lb;
-        const uint32_t e = *reinterpret_cast<const uint32_t *>(tab + p);
+        const uint32_t p = s * kLanes + lane;
+        const uint32_t f = tab[p], cdf = tab[kLdsCdf + p];
         dq = fmaf((float)s, dw, dlo);
-        x = __umul24(e, x >> kProbBits) + slot - (e >> 24);
-        return p;
+        x = __umul24(f, x >> kProbBits) + slot - cdf;
+        return s;
     }
 
     // Loads ring chunks until the words [cur, cur + cnt) are present (rare path).
@@ -270,7 +270,7 @@ struct Stream {
         float dq;
         const uint32_t p = dec.symbol(tab, lane, lb, dq);
         if (SYMBOLS)
-            ys[u] = p / kSymStride;
+            ys[u] = p;
         else
             yf[u] = af + dq;
     }
@@ -303,7 +303,7 @@ struct Stream {
             float dq;
             const uint32_t p = dec.symbol(tab, lane, lb, dq);
             if (dec.present)
-                put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? p / kSymStride : f2h(af + dq));
+                put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? p : f2h(af + dq));
             orow += ostride;
             if (++dec.i < dec.m) dec.renorm(lane);
         }
@@ -435,13 +435,18 @@ __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__r
     const uint32_t b = tmp % g.NB;
     const uint32_t row = tmp / g.NB;
     const uint32_t N = bins[row >> 1];
-    // stage the N used entries and the slot table
-    const uint32_t n16 = (N * kLanes) / 4;  // 16-byte pieces of entries
-    const uint4 *src = reinterpret_cast<const uint4 *>(dtab + (uint64_t)(row * g.NB + b) * kTabBlock);
-    uint4 *dst = reinterpret_cast<uint4 *>(tab);
-    for (uint32_t j = threadIdx.x; j < n16; j += blockDim.x) dst[j] = src[j];
+    // stage f and cdf of the N used entries as bytes, and the slot table
+    const uint32_t *src = dtab + (uint64_t)(row * g.NB + b) * kTabBlock;
+    uint8_t *tb8 = reinterpret_cast<uint8_t *>(tab);
+    for (uint32_t j = threadIdx.x; j < N * kLanes; j += blockDim.x) {
+        const uint32_t e = src[j];
+        tb8[j] = (uint8_t)e;
+        tb8[kLdsCdf + j] = (uint8_t)(e >> 24);
+    }
+    const uint4 *lsrc = reinterpret_cast<const uint4 *>(src + kTabLut);
+    uint4 *ldst = reinterpret_cast<uint4 *>(tb8 + kLdsLut);
     for (uint32_t j = threadIdx.x; j < kProbTotal * kLanes / 16; j += blockDim.x)
-        dst[kTabPlane / 4 + j] = src[kTabLut / 4 + j];
+        ldst[j] = lsrc[j];
     __syncthreads();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     const uint32_t lane = threadIdx.x % kLanes;
