@@ -72,20 +72,33 @@ struct WaveDecoder {
         }
     }
 
-    // Renormalisation after a symbol that is not the chunk's last.
+    // Renormalisation after a symbol that is not the chunk's last, in two halves so that
+    // the two streams of a wavefront can share one refill branch and overlap their ring
+    // reads.  First: which lanes read a word, and how many words that takes.
+    __device__ __forceinline__ uint64_t renorm_mask() const
+    {
+        return __builtin_amdgcn_ballot_w64(present && (x < kStateLow));
+    }
+
+    // Then: every lane reads the ring at its rank among the reading lanes (lanes that do
+    // not read take a neighbour's word, in bounds), and the reading lanes shift it in.
+    // No branch: some lane reads at almost every step.
+    __device__ __forceinline__ void renorm_take(uint64_t mask)
+    {
+        const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, cur & (kRingWords - 1)));
+        const uint32_t w = ring[at];
+        const bool need = present && (x < kStateLow);
+        x = need ? (x << 16) | w : x;
+        cur += (uint32_t)__builtin_popcountll(mask);
+    }
+
     __device__ __forceinline__ void renorm(uint32_t lane)
     {
-        // (the ballot takes the comparison itself, so the lane mask is not materialised
-        // in a vector register; with no lane renormalising the body does nothing)
-        const bool need = present && (x < kStateLow);
-        const uint64_t mask = __builtin_amdgcn_ballot_w64(need);
+        const uint64_t mask = renorm_mask();
         const uint32_t cnt = (uint32_t)__builtin_popcountll(mask);
         if (__builtin_expect(cur + cnt > re, 0)) refill_now(cnt, lane);
-        if (need) {
-            const uint16_t *rp = ring + (cur & (kRingWords - 1));
-            x = (x << 16) | rp[mbcnt64(mask)];
-        }
-        cur += cnt;
+        renorm_take(mask);
     }
 };
 
@@ -326,8 +339,20 @@ __device__ __forceinline__ void paired_steps(Stream<SYMBOLS> (&st)[NS], const ui
         for (int s = 0; s < NS; ++s) st[s].step_held(tab, lane, lb, u);
         // both state updates are computed here, next to their table reads
         asm volatile("" : "+v"(st[0].dec.x), "+v"(st[NS - 1].dec.x));
+        uint64_t mask[NS];
+        bool short_ring = false;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) st[s].dec.renorm(lane);
+        for (int s = 0; s < NS; ++s) {
+            mask[s] = st[s].dec.renorm_mask();
+            short_ring |= st[s].dec.cur + (uint32_t)__builtin_popcountll(mask[s]) > st[s].dec.re;
+        }
+        if (__builtin_expect(short_ring, 0)) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                st[s].dec.refill_now((uint32_t)__builtin_popcountll(mask[s]), lane);
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) st[s].dec.renorm_take(mask[s]);
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) st[s].finish_unrolled();
