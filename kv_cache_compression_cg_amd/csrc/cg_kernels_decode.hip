@@ -49,17 +49,34 @@ struct WaveDecoder {
     __amdgpu_buffer_rsrc_t wrs;
     bool present;
 
-    // Decodes one symbol: the low 8 bits of the state name a slot, the slot table names
-    // the symbol, and x = f * (x >> 8) + slot - cdf.  Returns the symbol.
-    __device__ __forceinline__ uint32_t symbol(const uint8_t *tab, uint32_t lane, uint32_t lb,
-                                               float &dq)
+    // Decoding a symbol: the low 8 bits of the state name a slot, the slot table names
+    // the symbol, and x = f * (x >> 8) + slot - cdf.  In two halves, so that the slot
+    // table reads of a wavefront's two streams are both in flight before either is used.
+    __device__ __forceinline__ uint32_t slot_symbol(const uint8_t *tab, uint32_t lane,
+                                                    uint32_t &slot) const
     {
-        const uint32_t slot = x & (kProbTotal - 1u);
-        const uint32_t s = tab[kLdsLut + slot * kLanes + lane];
+        slot = x & (kProbTotal - 1u);
+        return tab[kLdsLut + slot * kLanes + lane];
+    }
+
+    __device__ __forceinline__ void update(const uint8_t *tab, uint32_t lane, uint32_t slot,
+                                           uint32_t s, float &dq)
+    {
         const uint32_t p = s * kLanes + lane;
         const uint32_t f = tab[p], cdf = tab[kLdsCdf + p];
         dq = fmaf((float)s, dw, dlo);
         x = __umul24(f, x >> kProbBits) + slot - cdf;
+    }
+
+    // Returns the symbol.
+    __device__ __forceinline__ uint32_t symbol(const uint8_t *tab, uint32_t lane, float &dq)
+    {
+        uint32_t slot;
+        uint32_t s = slot_symbol(tab, lane, slot);
+        // (an opaque 32-bit value from here: the byte read already zero-extends, and
+        // without this the compiler masks it again)
+        asm volatile("" : "+v"(s));
+        update(tab, lane, slot, s, dq);
         return s;
     }
 
@@ -278,14 +295,19 @@ struct Stream {
     }
 
     // step u of an unrolled group: the output stays in a register
-    __device__ __forceinline__ void step_held(const uint8_t *tab, uint32_t lane, uint32_t lb, int u)
+    __device__ __forceinline__ void hold(int u, uint32_t s, float dq)
     {
-        float dq;
-        const uint32_t p = dec.symbol(tab, lane, lb, dq);
         if (SYMBOLS)
-            ys[u] = p;
+            ys[u] = s;
         else
             yf[u] = af + dq;
+    }
+
+    __device__ __forceinline__ void step_held(const uint8_t *tab, uint32_t lane, int u)
+    {
+        float dq;
+        const uint32_t s = dec.symbol(tab, lane, dq);
+        hold(u, s, dq);
     }
 
     __device__ __forceinline__ void finish_unrolled()
@@ -296,11 +318,11 @@ struct Stream {
         orow += kUnrolledSteps * ostride;
     }
 
-    __device__ __forceinline__ void unrolled(const uint8_t *tab, uint32_t lane, uint32_t lb)
+    __device__ __forceinline__ void unrolled(const uint8_t *tab, uint32_t lane)
     {
 #pragma unroll
         for (int u = 0; u < kUnrolledSteps; ++u) {
-            step_held(tab, lane, lb, u);
+            step_held(tab, lane, u);
             // the state update is computed here, next to its table reads
             asm volatile("" : "+v"(dec.x));
             dec.renorm(lane);
@@ -309,14 +331,13 @@ struct Stream {
     }
 
     // any other group: one store per step
-    __device__ __forceinline__ void generic(const uint8_t *tab, uint32_t lane, uint32_t lb,
-                                            uint32_t nsteps)
+    __device__ __forceinline__ void generic(const uint8_t *tab, uint32_t lane, uint32_t nsteps)
     {
         for (uint32_t u = nsteps; u != 0; --u) {
             float dq;
-            const uint32_t p = dec.symbol(tab, lane, lb, dq);
+            const uint32_t sym = dec.symbol(tab, lane, dq);
             if (dec.present)
-                put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? p : f2h(af + dq));
+                put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? sym : f2h(af + dq));
             orow += ostride;
             if (++dec.i < dec.m) dec.renorm(lane);
         }
@@ -331,12 +352,21 @@ struct Stream {
 // An unrolled group of both streams of a wavefront in lockstep.
 template <bool SYMBOLS, int NS>
 __device__ __forceinline__ void paired_steps(Stream<SYMBOLS> (&st)[NS], const uint8_t *tab,
-                                             uint32_t lane, uint32_t lb)
+                                             uint32_t lane)
 {
 #pragma unroll
     for (int u = 0; u < kUnrolledSteps; ++u) {
+        uint32_t slot[NS], sym[NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) st[s].step_held(tab, lane, lb, u);
+        for (int s = 0; s < NS; ++s) sym[s] = st[s].dec.slot_symbol(tab, lane, slot[s]);
+        // (opaque 32-bit values: see WaveDecoder::symbol)
+        asm volatile("" : "+v"(sym[0]), "+v"(sym[NS - 1]));
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            float dq;
+            st[s].dec.update(tab, lane, slot[s], sym[s], dq);
+            st[s].hold(u, sym[s], dq);
+        }
         // both state updates are computed here, next to their table reads
         asm volatile("" : "+v"(st[0].dec.x), "+v"(st[NS - 1].dec.x));
         uint64_t mask[NS];
@@ -373,7 +403,6 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
                                               uint8_t *__restrict__ sym_out)
 {
     const bool present = FULL || lane < min(kLanes, g.C - b * kLanes);
-    const uint32_t lb = lane * 4;  // entry (symbol 0, this lane)
     Stream<SYMBOLS> st[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
@@ -404,7 +433,7 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
 #pragma unroll
             for (int s = 0; s < NS; ++s) st[s].write_held_rows();
             __builtin_amdgcn_sched_barrier(0);
-            paired_steps(st, tab, lane, lb);
+            paired_steps(st, tab, lane);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < NS; ++s) st[s].consume(lane);
@@ -419,14 +448,14 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
             if (act[s]) st[s].write_rows();
         __builtin_amdgcn_sched_barrier(0);
         if (NS == 2 && unr[0] && unr[NS - 1]) {
-            paired_steps(st, tab, lane, lb);
+            paired_steps(st, tab, lane);
         } else {
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 if (unr[s])
-                    st[s].unrolled(tab, lane, lb);
+                    st[s].unrolled(tab, lane);
                 else if (act[s])
-                    st[s].generic(tab, lane, lb, nsteps[s]);
+                    st[s].generic(tab, lane, nsteps[s]);
             }
         }
 
