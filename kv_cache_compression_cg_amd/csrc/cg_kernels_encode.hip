@@ -1,6 +1,6 @@
 // cg_kernels_encode.hip -- gfx950 kernels of cg_build_cdf and cg_encode: range and
 // non-finite check (K0), histogram and frequency / decode tables (K1), anchor delta +
-// quantize (K2) and the range encoder (K5).
+// quantize (K2) and the rANS encoder (K5).
 
 #include "cg_device.h"
 
