@@ -71,10 +71,11 @@ typedef struct cg_blob cg_blob;     /* one encoded container (device) */
  *              Groups are (chunk, layer, K/V, block) in row-major order over chunks
  *              [chunk_begin, chunk_end); block b holds channels 64b .. 64b+63.
  *   anchors    fp16, for each chunk: [L][2][ceil(len_k / group)][C]
- *   payload    uint16 words.  A group's words are the words of its (up to) 64 streams
- *              in the order 64 decoders running in lockstep read them: words 0 and 1
- *              of every lane in lane order, then at each symbol step the next word of
- *              every lane that renormalises at that step, in lane order.
+ *   payload    uint16 words.  A group's words are the words of its (up to) 64 rANS
+ *              streams in the order 64 decoders running in lockstep read them: the two
+ *              state words of every lane in lane order, then after each symbol step the
+ *              next word of every lane whose state fell below 2^16, in lane order.
+ * Header version 2 (rANS, 8-bit frequencies); version 1 containers are not readable.
  * Tables are stored separately; cg_tables_info.stored_bytes is their size.
  */
 typedef struct cg_container_header {

@@ -301,7 +301,7 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     const uint64_t n_groups = (uint64_t)(ke - kb) * t->L * 2 * t->NB;
     const uint64_t arows = anchor_rows(t, kb, ke);
 
-    // renormalisation ballots of every step of every group, 64 steps per row chunk
+    // word-read ballots of every step of every group, 64 steps per row chunk
     const uint32_t full = t->Tc < t->S ? t->Tc : t->S;
     const uint32_t mstride = (full - ceil_div(full, t->G) + 63) / 64 * 64;
     DevBuf sym, anc, lane_words, group_words, group_off, masks;
@@ -330,7 +330,7 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     cg_container_header h;
     std::memset(&h, 0, sizeof h);
     h.magic = CG_CONTAINER_MAGIC;
-    h.version = 1;
+    h.version = 2;  // rANS with 8-bit frequencies
     h.L = t->L;
     h.H_kv = t->H;
     h.d = t->d;
