@@ -349,6 +349,37 @@ struct Stream {
     }
 };
 
+// renorm_take for the two streams of a wavefront at once: each stream's reading lanes
+// read their word and shift it in under an exec mask of just those lanes, so the other
+// lanes need no select, and both reads are in flight before the one wait.  (Written as
+// one asm block because the compiler would branch around each masked region; the block
+// waits for its own reads and restores exec, so the compiler's counters and exec are
+// as before.)
+__device__ __forceinline__ void take_words_pair(WaveDecoder &d0, WaveDecoder &d1, uint64_t m0,
+                                                uint64_t m1)
+{
+    typedef __attribute__((address_space(3))) uint16_t lds_u16;
+    const uint32_t a0 = (uint32_t)(size_t)(lds_u16 *)(d0.ring + (d0.cur & (kRingWords - 1))) + 2 * mbcnt64(m0);
+    const uint32_t a1 = (uint32_t)(size_t)(lds_u16 *)(d1.ring + (d1.cur & (kRingWords - 1))) + 2 * mbcnt64(m1);
+    uint32_t w0, w1;
+    uint64_t save;
+    asm volatile(
+        "s_and_saveexec_b64 %[sv], %[m0]\n\t"
+        "ds_read_u16 %[w0], %[a0]\n\t"
+        "s_mov_b64 exec, %[m1]\n\t"
+        "ds_read_u16 %[w1], %[a1]\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "v_lshl_or_b32 %[x1], %[x1], 16, %[w1]\n\t"
+        "s_mov_b64 exec, %[m0]\n\t"
+        "v_lshl_or_b32 %[x0], %[x0], 16, %[w0]\n\t"
+        "s_mov_b64 exec, %[sv]"
+        : [x0] "+v"(d0.x), [x1] "+v"(d1.x), [w0] "=&v"(w0), [w1] "=&v"(w1), [sv] "=&s"(save)
+        : [m0] "s"(m0), [m1] "s"(m1), [a0] "v"(a0), [a1] "v"(a1)
+        : "memory", "scc");
+    d0.cur += (uint32_t)__builtin_popcountll(m0);
+    d1.cur += (uint32_t)__builtin_popcountll(m1);
+}
+
 // An unrolled group of both streams of a wavefront in lockstep.
 template <bool SYMBOLS, int NS>
 __device__ __forceinline__ void paired_steps(Stream<SYMBOLS> (&st)[NS], const uint8_t *tab,
@@ -381,15 +412,19 @@ __device__ __forceinline__ void paired_steps(Stream<SYMBOLS> (&st)[NS], const ui
             for (int s = 0; s < NS; ++s)
                 st[s].dec.refill_now((uint32_t)__builtin_popcountll(mask[s]), lane);
         }
+        if constexpr (NS == 2) {
+            take_words_pair(st[0].dec, st[1].dec, mask[0], mask[1]);
+        } else {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) st[s].dec.renorm_take(mask[s]);
+            for (int s = 0; s < NS; ++s) st[s].dec.renorm_take(mask[s]);
+        }
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) st[s].finish_unrolled();
 }
 
 // One wavefront decodes NS chunks of the same (row, channel block) in lockstep, sharing
-// the block's LDS table.  With two, the symbol searches of both streams sit in one
+// the block's LDS table.  With two, the symbol decodes of both streams sit in one
 // basic block, so the dependent LDS reads of one overlap the arithmetic of the other.
 template <bool SYMBOLS, bool FULL, int NS>
 __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__restrict__ tab,
