@@ -24,12 +24,16 @@ constexpr uint32_t kStreamsPerWave = 2;   // chunks one wavefront decodes in loc
 // outputs held in registers; any other group length takes the generic loop.
 constexpr int kUnrolledSteps = 9;
 
+// A 32-bit view of ring words that the compiler must treat as aliasing the 16-bit
+// reads (a word read back after a refill is reloaded, not forwarded from before it).
+typedef uint32_t __attribute__((may_alias)) ring_pair_t;
+
 // Stores the 2 words at stream position pos (even) into the ring.
 __device__ __forceinline__ void ring_put(uint16_t *ring, uint32_t pos, uint32_t v)
 {
     const uint32_t slot = pos & (kRingWords - 1);
-    *reinterpret_cast<uint32_t *>(ring + slot) = v;
-    if (slot < 64) *reinterpret_cast<uint32_t *>(ring + slot + kRingWords) = v;
+    *reinterpret_cast<ring_pair_t *>(ring + slot) = v;
+    if (slot < 64) *reinterpret_cast<ring_pair_t *>(ring + slot + kRingWords) = v;
 }
 
 // The block's table in LDS, all bytes: f of symbol s for this lane at 64 s + lane, cdf of
@@ -42,7 +46,8 @@ constexpr uint32_t kLdsWords = (kLdsLut + kProbTotal * kLanes) / 4;
 
 struct WaveDecoder {
     uint32_t x;        // rANS state, in [2^16, 2^32) between symbols
-    float dlo, dw;     // the lane's channel: lo and bin width
+    float dlo, dw24;   // the lane's channel: lo, and the bin width times 2^24
+    uint64_t pmask;    // lanes with a channel (wave-uniform)
     uint32_t cur, re;  // next unread word; words [re - R, re) are in the ring
     uint32_t i, m;     // symbols decoded so far / in the chunk
     uint16_t *ring;
@@ -56,7 +61,11 @@ struct WaveDecoder {
                                                     uint32_t &slot) const
     {
         slot = x & (kProbTotal - 1u);
-        return tab[kLdsLut + slot * kLanes + lane];
+        // byte of (slot, lane): 256 (slot / 4) + 4 lane + slot mod 4 (one bank per lane),
+        // formed as ((x & 0xFC) << 6) | ((x & 3) | 4 lane) in one shift-or
+        uint32_t a;
+        asm("v_lshl_or_b32 %0, %1, 6, %2" : "=v"(a) : "v"(x & 0xFCu), "v"((x & 3u) | (lane << 2)));
+        return tab[kLdsLut + a];
     }
 
     __device__ __forceinline__ void update(const uint8_t *tab, uint32_t lane, uint32_t slot,
@@ -64,7 +73,11 @@ struct WaveDecoder {
     {
         const uint32_t p = s * kLanes + lane;
         const uint32_t f = tab[p], cdf = tab[kLdsCdf + p];
-        dq = fmaf((float)s, dw, dlo);
+        // fma(s, w, lo) with s taken as the fp16 subnormal s * 2^-24 and w pre-scaled by
+        // 2^24: both scalings are exact and the fma's product is the same real number,
+        // so the result is bit-identical, and the hardware reads s straight from the
+        // byte without a conversion instruction
+        dq = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)s), dw24, dlo);
         x = __umul24(f, x >> kProbBits) + slot - cdf;
     }
 
@@ -94,7 +107,9 @@ struct WaveDecoder {
     // reads.  First: which lanes read a word, and how many words that takes.
     __device__ __forceinline__ uint64_t renorm_mask() const
     {
-        return __builtin_amdgcn_ballot_w64(present && (x < kStateLow));
+        // the compare's own lane mask (a ballot of a combined condition would first be
+        // materialised as a 0/1 vector and compared again)
+        return __builtin_amdgcn_uicmp(x, kStateLow, 36 /* unsigned less-than */) & pmask;
     }
 
     // Then: every lane reads the ring at its rank among the reading lanes (lanes that do
@@ -216,7 +231,8 @@ struct Stream {
 
         dec.x = kStateLow;
         dec.dlo = present ? lo[(uint64_t)row * g.C + b * kLanes + lane] : 0.0f;
-        dec.dw = present ? w[(uint64_t)row * g.C + b * kLanes + lane] : 0.0f;
+        dec.dw24 = present ? w[(uint64_t)row * g.C + b * kLanes + lane] * 16777216.0f : 0.0f;
+        dec.pmask = __builtin_amdgcn_ballot_w64(present);
         dec.re = 0;
         if (dec.m > 0) {
             dec.cur = 0;
@@ -349,37 +365,6 @@ struct Stream {
     }
 };
 
-// renorm_take for the two streams of a wavefront at once: each stream's reading lanes
-// read their word and shift it in under an exec mask of just those lanes, so the other
-// lanes need no select, and both reads are in flight before the one wait.  (Written as
-// one asm block because the compiler would branch around each masked region; the block
-// waits for its own reads and restores exec, so the compiler's counters and exec are
-// as before.)
-__device__ __forceinline__ void take_words_pair(WaveDecoder &d0, WaveDecoder &d1, uint64_t m0,
-                                                uint64_t m1)
-{
-    typedef __attribute__((address_space(3))) uint16_t lds_u16;
-    const uint32_t a0 = (uint32_t)(size_t)(lds_u16 *)(d0.ring + (d0.cur & (kRingWords - 1))) + 2 * mbcnt64(m0);
-    const uint32_t a1 = (uint32_t)(size_t)(lds_u16 *)(d1.ring + (d1.cur & (kRingWords - 1))) + 2 * mbcnt64(m1);
-    uint32_t w0, w1;
-    uint64_t save;
-    asm volatile(
-        "s_and_saveexec_b64 %[sv], %[m0]\n\t"
-        "ds_read_u16 %[w0], %[a0]\n\t"
-        "s_mov_b64 exec, %[m1]\n\t"
-        "ds_read_u16 %[w1], %[a1]\n\t"
-        "s_waitcnt lgkmcnt(0)\n\t"
-        "v_lshl_or_b32 %[x1], %[x1], 16, %[w1]\n\t"
-        "s_mov_b64 exec, %[m0]\n\t"
-        "v_lshl_or_b32 %[x0], %[x0], 16, %[w0]\n\t"
-        "s_mov_b64 exec, %[sv]"
-        : [x0] "+v"(d0.x), [x1] "+v"(d1.x), [w0] "=&v"(w0), [w1] "=&v"(w1), [sv] "=&s"(save)
-        : [m0] "s"(m0), [m1] "s"(m1), [a0] "v"(a0), [a1] "v"(a1)
-        : "memory", "scc");
-    d0.cur += (uint32_t)__builtin_popcountll(m0);
-    d1.cur += (uint32_t)__builtin_popcountll(m1);
-}
-
 // An unrolled group of both streams of a wavefront in lockstep.
 template <bool SYMBOLS, int NS>
 __device__ __forceinline__ void paired_steps(Stream<SYMBOLS> (&st)[NS], const uint8_t *tab,
@@ -400,23 +385,36 @@ __device__ __forceinline__ void paired_steps(Stream<SYMBOLS> (&st)[NS], const ui
         }
         // both state updates are computed here, next to their table reads
         asm volatile("" : "+v"(st[0].dec.x), "+v"(st[NS - 1].dec.x));
-        uint64_t mask[NS];
-        bool short_ring = false;
+        // Renormalisation.  Each lane reads the ring at its rank among the reading lanes
+        // (lanes that do not read take a neighbour's word, in bounds) before the check
+        // that the ring holds those words, so the reads do not wait for the check; in
+        // the rare case that a refill is due they are repeated after it.
+        bool need[NS];
+        uint32_t at[NS], wv[NS], curn[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            mask[s] = st[s].dec.renorm_mask();
-            short_ring |= st[s].dec.cur + (uint32_t)__builtin_popcountll(mask[s]) > st[s].dec.re;
+            WaveDecoder &d = st[s].dec;
+            need[s] = d.present && d.x < kStateLow;
+            const uint64_t mask = __builtin_amdgcn_ballot_w64(need[s]);
+            at[s] = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mask, d.cur & (kRingWords - 1)));
+            wv[s] = d.ring[at[s]];
+            curn[s] = d.cur + (uint32_t)__builtin_popcountll(mask);
         }
-        if (__builtin_expect(short_ring, 0)) {
+        int32_t room = (int32_t)(st[0].dec.re - curn[0]);
+        if (NS == 2) room |= (int32_t)(st[NS - 1].dec.re - curn[NS - 1]);
+        if (__builtin_expect(room < 0, 0)) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-                st[s].dec.refill_now((uint32_t)__builtin_popcountll(mask[s]), lane);
+            for (int s = 0; s < NS; ++s) {
+                st[s].dec.refill_now(curn[s] - st[s].dec.cur, lane);
+                wv[s] = st[s].dec.ring[at[s]];
+            }
         }
-        if constexpr (NS == 2) {
-            take_words_pair(st[0].dec, st[1].dec, mask[0], mask[1]);
-        } else {
 #pragma unroll
-            for (int s = 0; s < NS; ++s) st[s].dec.renorm_take(mask[s]);
+        for (int s = 0; s < NS; ++s) {
+            WaveDecoder &d = st[s].dec;
+            d.x = need[s] ? (d.x << 16) | wv[s] : d.x;
+            d.cur = curn[s];
         }
     }
 #pragma unroll
@@ -619,8 +617,9 @@ hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, c
                      const float *w, const uint8_t *container, const ContainerView &cv,
                      uint16_t *out, uint8_t *sym_out, hipStream_t st)
 {
+    const uint32_t nk = g.ke - g.kb;
     // fewer than 8 chunks: one wavefront per block (see k3_decode)
-    const bool wide = g.ke - g.kb >= kWavesPerBlock * kStreamsPerWave;
+    const bool wide = nk >= kWavesPerBlock * kStreamsPerWave;
     const uint32_t wpb = wide ? kWavesPerBlock : 1u;
     const uint32_t per_block = wpb * kStreamsPerWave;
     const uint32_t n_sets = (g.ke - g.kb + per_block - 1) / per_block;

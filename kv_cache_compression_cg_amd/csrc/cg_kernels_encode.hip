@@ -199,13 +199,16 @@ __global__ __launch_bounds__(256) void k1_freqs(Geom g, const uint8_t *__restric
             __float_as_uint(fmaf((float)min(s, N - 1u), w1, lo1));
         cdf += fs;
     }
-    // slot table: every slot in [cdf[s], cdf[s] + f[s]) names s
+    // slot table: every slot in [cdf[s], cdf[s] + f[s]) names s; the byte of (slot, lane)
+    // is at 256 (slot / 4) + 4 lane + slot mod 4, so each lane's slots share its own
+    // 4-byte column and 64 lanes reading any slots hit 64 different dwords of one row
+    // each in its own bank
     uint8_t *lut = reinterpret_cast<uint8_t *>(dtab + (uint64_t)(row * g.NB + c / kLanes) * kTabBlock +
-                                               kTabLut) + (c % kLanes);
+                                               kTabLut) + 4 * (c % kLanes);
     uint32_t s = 0, end = f[0];
     for (uint32_t slot = 0; slot < kProbTotal; ++slot) {
         while (slot >= end) end += f[++s];
-        lut[(uint64_t)slot * kLanes] = (uint8_t)s;
+        lut[(slot >> 2) * (4 * kLanes) + (slot & 3u)] = (uint8_t)s;
     }
 }
 

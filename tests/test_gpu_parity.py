@@ -107,11 +107,14 @@ def test_llama7b_shape_two_layers(cg):
 
 
 @pytest.mark.parametrize("G,Tc,rng", [(7, 150, None), (10, 90, None), (10, 90, (3, 12)),
-                                      (10, 240, None)])
+                                      (10, 240, None), (10, 60, None), (7, 70, None),
+                                      (10, 60, (2, 30)), (10, 125, None)])
 def test_paired_chunks(cg, G, Tc, rng):
     """Many chunks per (row, channel block), so a wavefront decodes two chunks in
     lockstep: equal and unequal chunk lengths, a partial lane block (C = 136), full and
-    partial anchor groups, and a chunk range that starts mid-cache."""
+    partial anchor groups, and a chunk range that starts mid-cache.  Chunk counts 9 to
+    34 per (row, block) give blocks of 8 chunks with a partial last set, G = 7 (no
+    unrolled groups) and a wavefront left with one chunk."""
     X = _gen(2, 2000, 136, HEAVY)
     full_parity(cg, X, 17, G, Tc, (32, 8), chunk_range=rng, label="paired")
 
@@ -154,10 +157,13 @@ def test_mismatched_container_is_rejected(cg):
     assert e.value.code == -5
 
 
-def test_damaged_container_decodes_without_fault(cg):
-    """Damaged payload words and offsets: reads stay inside the container."""
-    X = _gen(2, 500, 128, HEAVY)
-    tab = cg.build_cdf(X, 10, 128, (16, 4), H_kv=2)
+@pytest.mark.parametrize("S,Tc", [(500, 128), (2000, 100)])
+def test_damaged_container_decodes_without_fault(cg, S, Tc):
+    """Damaged payload words and offsets: reads stay inside the container, with one
+    wavefront per block (4 chunks) and four (20 chunks)."""
+    _say("[damaged] S=%d Tc=%d" % (S, Tc))
+    X = _gen(2, S, 128, HEAVY)
+    tab = cg.build_cdf(X, 10, Tc, (16, 4), H_kv=2)
     blob = cg.encode(tab, X)
     raw = torch.from_numpy(blob.read().copy()).cuda()
     h = blob.header
