@@ -163,6 +163,35 @@ def streamed_report(dev, n_slots: int = 8, reps: int = 3, seed: int = 0) -> dict
     return res
 
 
+def decode_loop(w, dev, n: int) -> dict:
+    """One encode of the workload, then n decodes back to back on one stream, each timed
+    with HIP events; the rest of the step is left out, so that a counter run or a power
+    reading taken meanwhile sees the decoder alone."""
+    import torch
+
+    from kv_cache_compression_cg_amd import cg, synth
+    X = synth.gen_kv(w, device=dev)
+    tab = cg.build_cdf(X, w.group, w.chunk, w.bins, H_kv=w.H_kv)
+    blob = cg.encode(tab, X)
+    out = torch.empty_like(X)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    log("[decode-loop] %d decodes of %s" % (n, w.name))
+    t0 = time.time()
+    for e0, e1 in ev:
+        e0.record(stream)
+        cg.decode(tab, blob, out)
+        e1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.time() - t0
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return {"decode_loop": n, "workload": w.name, "raw_bytes": w.raw_bytes,
+            "decode_ms_mean": round(sum(ms) / n, 4), "decode_ms_median": round(ms[n // 2], 4),
+            "decode_ms_min": round(ms[0], 4), "wall_s": round(wall, 3),
+            "GBps_mean": round(w.raw_bytes / (sum(ms) / n) / 1e6, 1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +206,9 @@ def main() -> int:
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 4 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--decode-loop", type=int, default=0, metavar="N",
+                    help="only encode the workload once and decode it N times back to back "
+                         "(for counters and for sampling board power during the decode)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the codec runs on a single MI355X "
@@ -203,6 +235,9 @@ def main() -> int:
     w = configs.ALL[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.decode_loop:
+        print(json.dumps(decode_loop(w, dev, args.decode_loop)), flush=True)
+        return 0
     if args.only_streamed:
         print(json.dumps({"streamed": streamed_report(dev)}), flush=True)
         return 0
