@@ -8,7 +8,8 @@ namespace cgk {
 // ------------------------------------------------------------------------------ K3 (+K4)
 // rANS decoder fused with dequantize + anchor-add.  Block = 4 wavefronts, each decoding
 // two chunks of the same (row, block) in lockstep, all sharing the block's decode table
-// in LDS (N <= 32 entries x 64 lanes x 4 bytes, slot table 256 x 64 bytes).  Everything
+// in LDS (f and cdf of up to 32 symbols per lane as bytes, and the 256-slot table of
+// symbol bytes laid out one LDS bank per lane).  Everything
 // that is the same for the 64 lanes (chunk, token, group, stream cursor, row addresses)
 // is kept in scalar registers; only the coder state and the table address are per lane.
 
@@ -505,6 +506,12 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
 // (row, channel block); wavefront w takes chunks base + w and base + w + WPB.  Launches
 // over many chunks use 4 wavefronts per block, sharing the staged table; launches over
 // a few chunks (a streamed chunk) use 1, so that more blocks are resident.
+//
+// Blocks are dealt to the 8 XCDs in turn (block index mod 8).  The channel block of a
+// row is rotated by the row index, so that the blocks each XCD holds at a time write all
+// 16 (for C = 1024) 128-byte columns of the 2 KiB token rows evenly; without it an XCD
+// writes only a few of them (those b with a fixed residue), and its writes and anchor
+// reads queue on the few L2 / memory channels that these addresses map to.
 template <bool SYMBOLS, uint32_t WPB>
 __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
                                                   const uint32_t *__restrict__ dtab,
@@ -519,8 +526,8 @@ __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__r
     __shared__ uint16_t rings[WPB * kStreamsPerWave * kRingAlloc];
     const uint32_t set = blockIdx.x % n_sets;
     const uint32_t tmp = blockIdx.x / n_sets;
-    const uint32_t b = tmp % g.NB;
     const uint32_t row = tmp / g.NB;
+    const uint32_t b = (tmp % g.NB + row) % g.NB;
     const uint32_t N = bins[row >> 1];
     // stage f and cdf of the N used entries as bytes, and the slot table
     const uint32_t *src = dtab + (uint64_t)(row * g.NB + b) * kTabBlock;
