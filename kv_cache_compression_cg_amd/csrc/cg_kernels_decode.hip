@@ -507,11 +507,13 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
 // over many chunks use 4 wavefronts per block, sharing the staged table; launches over
 // a few chunks (a streamed chunk) use 1, so that more blocks are resident.
 //
-// Blocks are dealt to the 8 XCDs in turn (block index mod 8).  The channel block of a
-// row is rotated by the row index, so that the blocks each XCD holds at a time write all
-// 16 (for C = 1024) 128-byte columns of the 2 KiB token rows evenly; without it an XCD
-// writes only a few of them (those b with a fixed residue), and its writes and anchor
-// reads queue on the few L2 / memory channels that these addresses map to.
+// Block order: the channel block varies fastest, then the chunk set, then the row, so
+// that the blocks dispatched together cover every 128-byte column of the same token rows
+// (whole 2 KiB rows for C = 1024 are written at about the same time).  Blocks are dealt
+// to the 8 XCDs in turn (block index mod 8), so the channel block is also rotated by the
+// row: otherwise an XCD would hold only the columns b with one residue mod 8, and its
+// writes and anchor reads would queue on the few L2 / memory channels those addresses
+// map to.
 template <bool SYMBOLS, uint32_t WPB>
 __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
                                                   const uint32_t *__restrict__ dtab,
@@ -524,10 +526,10 @@ __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__r
 {
     __shared__ uint32_t tab[kLdsWords];
     __shared__ uint16_t rings[WPB * kStreamsPerWave * kRingAlloc];
-    const uint32_t set = blockIdx.x % n_sets;
-    const uint32_t tmp = blockIdx.x / n_sets;
-    const uint32_t row = tmp / g.NB;
-    const uint32_t b = (tmp % g.NB + row) % g.NB;
+    const uint32_t tmp = blockIdx.x / g.NB;
+    const uint32_t set = tmp % n_sets;
+    const uint32_t row = tmp / n_sets;
+    const uint32_t b = (blockIdx.x % g.NB + row) % g.NB;
     const uint32_t N = bins[row >> 1];
     // stage f and cdf of the N used entries as bytes, and the slot table
     const uint32_t *src = dtab + (uint64_t)(row * g.NB + b) * kTabBlock;
