@@ -383,10 +383,12 @@ __device__ __forceinline__ uint32_t enc_block(const Geom &g, const uint8_t *__re
                                               uint32_t n_sets, uint32_t *tab, uint32_t &row,
                                               uint32_t &b)
 {
-    const uint32_t set = blockIdx.x % n_sets;
-    const uint32_t tmp = blockIdx.x / n_sets;
-    b = tmp % g.NB;
-    row = tmp / g.NB;
+    // block order as in the decoder: channel block fastest, rotated by the row, so that
+    // the blocks each XCD holds at a time cover all columns of the token rows
+    const uint32_t tmp = blockIdx.x / g.NB;
+    const uint32_t set = tmp % n_sets;
+    row = tmp / n_sets;
+    b = (blockIdx.x % g.NB + row) % g.NB;
     const uint32_t N = bins[row >> 1];
     uint32_t P = 1;
     while (P < N) P <<= 1;
@@ -551,10 +553,10 @@ __global__ __launch_bounds__(256) void k5_interleave(Geom g, uint32_t n_sets,
                                                       const uint16_t *__restrict__ scratch,
                                                       uint16_t *__restrict__ payload)
 {
-    const uint32_t set = blockIdx.x % n_sets;
-    const uint32_t tmp = blockIdx.x / n_sets;
-    const uint32_t b = tmp % g.NB;
-    const uint32_t row = tmp / g.NB;
+    const uint32_t tmp = blockIdx.x / g.NB;
+    const uint32_t set = tmp % n_sets;
+    const uint32_t row = tmp / n_sets;
+    const uint32_t b = (blockIdx.x % g.NB + row) % g.NB;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     const uint32_t k = g.kb + set * kEncWaves + wave;
     if (k >= g.ke) return;
