@@ -13,7 +13,9 @@ metric), from HIP events around each decode on the stream it runs on, averaged o
 (the container resident in HBM).  `decode_ms_in_step` is the decode inside the steps,
 right after each step's encode.  `ms_per_step` is the wall time of a whole step.
 
-A second object, "streamed", covers the streamed decode of the 131K-token cache
+An object "kv_asymmetric" covers the same cache with the V rows one step coarser than
+the K rows (decode throughput and ratio).  An object "streamed" covers the streamed
+decode of the 131K-token cache
 (L=80, S=131072, 42.95 GB): every chunk encoded at three levels, one level per chunk
 chosen from a seeded bandwidth trace, the chosen containers copied from pinned host
 memory on one HIP stream while earlier chunks decode on another.
@@ -57,7 +59,7 @@ def table_bytes_read(tables) -> int:
     """Decode-table bytes the decoder stages into LDS: per (layer, K/V, 64-channel
     block), bins entries x 64 lanes x 4 bytes plus the 256-slot x 64-lane byte table."""
     nb = -(-tables.C // 64)
-    return sum(2 * nb * (b * 64 * 4 + 256 * 64) for b in tables.bins)
+    return sum(nb * (b * 64 * 4 + 256 * 64) for b in tables.row_bins)
 
 
 def measured_traffic(alg_bytes: float):
@@ -164,6 +166,44 @@ def streamed_report(dev, n_slots: int = 8, reps: int = 3, seed: int = 0) -> dict
     return res
 
 
+def kv_asymmetric_report(w, X, out, reps: int) -> dict:
+    """Keys finer than values ("Guide to CacheGen", Solution pillar 1): the V rows take one
+    step coarser bin counts than the K rows (K 32 / 16 / 8, V 16 / 8 / 4 by layer tier).
+    Decode throughput over back-to-back decodes of the resident container, and the ratio."""
+    import torch
+
+    from kv_cache_compression_cg_amd import cg
+    bins_v = [max(2, b // 2) for b in w.bins]
+    tab = cg.build_cdf(X, w.group, w.chunk, w.bins, H_kv=w.H_kv, bins_v=bins_v)
+    blob = cg.encode(tab, X)
+    stream = torch.cuda.current_stream(X.device)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps + 2)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        cg.decode(tab, blob, out)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev[2:]]
+    dec = sum(ms) / len(ms)
+    tt = torch.arange(w.S, device=X.device)
+    anchor = ((tt % w.chunk) % w.group) == 0
+    assert torch.equal(out[:, :, anchor].view(torch.int16), X[:, :, anchor].view(torch.int16))
+    wv = torch.from_numpy(tab.export()["w"][0]).to(X.device)[:, None, :]
+    err = (X[0].float() - out[0].float()).abs()
+    assert bool((err <= wv / 2 * 1.001 + 2 ** -10 * X[0].float().abs() + 1e-6).all())
+    comp = cg.compressed_bytes(tab, [blob])
+    res = {"workload": w.name, "bins_k": "32 / 16 / 8 (layers 0-19 / 20-39 / 40-79)",
+           "bins_v": "16 / 8 / 4", "decode_ms": round(dec, 4), "decode_reps": len(ms),
+           "value_GBps": round(w.raw_bytes / (dec * 1e-3) / 1e9, 2),
+           "pct_hbm_peak": round(100 * w.raw_bytes / (dec * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+           "compression_ratio": round(w.raw_bytes / comp, 4), "compressed_bytes": comp}
+    log("[kv-asymmetric] decode %.3f ms (%.1f GB/s), ratio %.3f"
+        % (dec, res["value_GBps"], res["compression_ratio"]))
+    del blob, tab
+    return res
+
+
 def decode_loop(w, dev, n: int) -> dict:
     """One encode of the workload, then n decodes back to back on one stream, each timed
     with HIP events; the rest of the step is left out, so that a counter run or a power
@@ -207,6 +247,8 @@ def main() -> int:
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 4 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--no-kv-asymmetric", action="store_true",
+                    help="skip the keys-finer-than-values variant (V rows one step coarser)")
     ap.add_argument("--decode-reps", type=int, default=20,
                     help="back-to-back decodes after the timed steps that give `value`")
     ap.add_argument("--decode-loop", type=int, default=0, metavar="N",
@@ -340,6 +382,8 @@ def main() -> int:
         "step %.1f ms, ratio %.3f" % (dec_mean, value, res["pct_hbm_peak"],
                                      res["decode_ms_in_step"], res["ms_per_step"],
                                      res["compression_ratio"]))
+    if not args.no_kv_asymmetric:
+        res["kv_asymmetric"] = kv_asymmetric_report(w, X, out, args.decode_reps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, X, args.cpu_threads)
     if not args.no_streamed:

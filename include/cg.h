@@ -28,7 +28,7 @@
  *   - return value: CG_OK or a negative CG_E_* code; cg_last_error() gives a message
  *     (thread-local).  No call throws or aborts.
  *   - limits: 1 <= L, H_kv, d, S; C = H_kv * d a multiple of 8; 1 <= group;
- *     1 <= chunk <= 16384; 2 <= bins[l] <= 32; L * 2 * S * C < 2^40; S * C < 2^32;
+ *     1 <= chunk <= 16384; 2 <= bins[l] <= 32 (and bins_v[l]); L * 2 * S * C < 2^40; S * C < 2^32;
  *     chunk * C * 2 < 2^32 (32-bit offsets within one row of symbols and one chunk).
  */
 #ifndef CG_H
@@ -53,12 +53,15 @@ extern "C" {
 #define CG_LANES 64         /* channels per interleaved group of streams */
 #define CG_CONTAINER_MAGIC 0x31474B43u /* "CKG1" */
 
-/* Shape and coding parameters.  `bins` points to L bin counts (host memory, copied). */
+/* Shape and coding parameters.  `bins` points to L bin counts (host memory, copied);
+ * `bins_v`, if not NULL, to L bin counts for the V rows, `bins` then giving those of the
+ * K rows (keys kept finer than values: "Guide to CacheGen", Solution pillar 1). */
 typedef struct cg_params {
     uint32_t L, H_kv, d, S;
     uint32_t group;          /* anchor interval G */
     uint32_t chunk;          /* tokens per chunk (one stream per (layer, K/V, channel, chunk)) */
     const uint8_t *bins;     /* [L], bins[l] = number of quantization levels of layer l */
+    const uint8_t *bins_v;   /* [L] or NULL: levels of the V rows of layer l (NULL: bins[l]) */
 } cg_params;
 
 typedef struct cg_tables cg_tables; /* per-channel ranges and frequency tables (device) */
@@ -192,7 +195,8 @@ int cg_stream_decode(const cg_stream_item *items, uint32_t n_items, void *stagin
 const char *cg_last_error(void);
 
 /* Host copies of the tables.  lo, w, r: float [L][2][C]; freqs: uint16 [L][2][C][32]
- * (entries >= bins[l] are 0).  Any pointer may be NULL.  Synchronous. */
+ * (entries >= the bin count of the (layer, K/V) row are 0).  Any pointer may be NULL.
+ * Synchronous. */
 int cg_tables_export(const cg_tables *tables, float *lo, float *w, float *r, uint16_t *freqs);
 int cg_tables_get_info(const cg_tables *tables, cg_tables_info *info);
 int cg_blob_get_info(const cg_blob *blob, cg_blob_info *info);

@@ -32,7 +32,7 @@ class CgError(RuntimeError):
 class Params(ctypes.Structure):
     _fields_ = [("L", ctypes.c_uint32), ("H_kv", ctypes.c_uint32), ("d", ctypes.c_uint32),
                 ("S", ctypes.c_uint32), ("group", ctypes.c_uint32), ("chunk", ctypes.c_uint32),
-                ("bins", ctypes.POINTER(ctypes.c_uint8))]
+                ("bins", ctypes.POINTER(ctypes.c_uint8)), ("bins_v", ctypes.POINTER(ctypes.c_uint8))]
 
 
 class ContainerHeader(ctypes.Structure):
@@ -127,12 +127,19 @@ def _kv_check(kv: torch.Tensor, shape=None) -> None:
 class Tables:
     """Per-(layer, K/V, channel) ranges and frequency tables, owned by libcg."""
 
-    def __init__(self, handle: ctypes.c_void_p, L, H_kv, d, S, group, chunk, bins, device):
+    def __init__(self, handle: ctypes.c_void_p, L, H_kv, d, S, group, chunk, bins, device,
+                 bins_v=None):
         self.handle = handle
         self.L, self.H_kv, self.d, self.S = L, H_kv, d, S
         self.group, self.chunk = group, chunk
-        self.bins = tuple(int(b) for b in bins)
+        self.bins = tuple(int(b) for b in bins)             # K rows (and V rows without bins_v)
+        self.bins_v = self.bins if bins_v is None else tuple(int(b) for b in bins_v)
         self.device = device
+
+    @property
+    def row_bins(self):
+        """Bin count of every (layer, K/V) row, in row order l * 2 + kv."""
+        return tuple(n for kv_pair in zip(self.bins, self.bins_v) for n in kv_pair)
 
     @property
     def C(self) -> int:
@@ -235,8 +242,10 @@ class Blob:
 
 
 def build_cdf(kv: torch.Tensor, group: int, chunk: int, bins: Sequence[int],
-              H_kv: Optional[int] = None) -> Tables:
-    """kv: fp16 CUDA [L, 2, S, C].  H_kv only labels the channel split (C = H_kv * d)."""
+              H_kv: Optional[int] = None, bins_v: Optional[Sequence[int]] = None) -> Tables:
+    """kv: fp16 CUDA [L, 2, S, C].  H_kv only labels the channel split (C = H_kv * d).
+    bins: bin count per layer; with bins_v, those of the K rows, and bins_v those of the
+    V rows."""
     _kv_check(kv)
     L, _, S, C = kv.shape
     H = H_kv if H_kv is not None else 1
@@ -245,12 +254,17 @@ def build_cdf(kv: torch.Tensor, group: int, chunk: int, bins: Sequence[int],
     b = np.ascontiguousarray(np.asarray(bins, dtype=np.uint8))
     if b.shape != (L,):
         raise ValueError("need one bin count per layer")
-    p = Params(L, H, C // H, S, group, chunk, b.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    bv = None if bins_v is None else np.ascontiguousarray(np.asarray(bins_v, dtype=np.uint8))
+    if bv is not None and bv.shape != (L,):
+        raise ValueError("need one V bin count per layer")
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    p = Params(L, H, C // H, S, group, chunk, b.ctypes.data_as(u8p),
+               bv.ctypes.data_as(u8p) if bv is not None else None)
     h = ctypes.c_void_p()
     with torch.cuda.device(kv.device):
         _check(load().cg_build_cdf(ctypes.byref(p), kv.data_ptr(), _stream(kv.device),
                                    ctypes.byref(h)))
-    return Tables(h, L, H, C // H, S, group, chunk, b, kv.device)
+    return Tables(h, L, H, C // H, S, group, chunk, b, kv.device, bins_v=bv)
 
 
 def encode(tables: Tables, kv: torch.Tensor, chunk_begin: int = 0,

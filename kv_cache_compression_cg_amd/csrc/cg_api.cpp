@@ -94,7 +94,7 @@ struct cg_tables {
     int device;
     uint32_t L, H, d, S, G, Tc, C, NB;
     uint32_t max_bins;
-    std::vector<uint8_t> bins;
+    std::vector<uint8_t> bins;    // per (layer, K/V) row, l * 2 + kv
     uint8_t *d_bins;
     float *d_lo, *d_w, *d_r;
     uint16_t *d_freqs;
@@ -196,10 +196,12 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
         (uint64_t)p.chunk * C * 2 >= (1ull << 32))
         return fail(CG_E_INVAL, "cache too large");
     uint32_t max_bins = 0;
-    for (uint32_t l = 0; l < p.L; ++l) {
-        if (p.bins[l] < 2 || p.bins[l] > CG_MAX_BINS) return fail(CG_E_INVAL, "bins outside [2, 32]");
-        if (p.bins[l] > max_bins) max_bins = p.bins[l];
-    }
+    for (uint32_t l = 0; l < p.L; ++l)
+        for (uint32_t kv = 0; kv < 2; ++kv) {
+            const uint8_t n = (kv && p.bins_v) ? p.bins_v[l] : p.bins[l];
+            if (n < 2 || n > CG_MAX_BINS) return fail(CG_E_INVAL, "bins outside [2, 32]");
+            if (n > max_bins) max_bins = n;
+        }
     hipStream_t st = (hipStream_t)hip_stream;
 
     cg_tables *t = new (std::nothrow) cg_tables();
@@ -215,7 +217,11 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     t->C = (uint32_t)C;
     t->NB = ceil_div(t->C, kLanes);
     t->max_bins = max_bins;
-    t->bins.assign(p.bins, p.bins + p.L);
+    t->bins.resize((size_t)2 * p.L);  // per (layer, K/V) row: l * 2 + kv
+    for (uint32_t l = 0; l < p.L; ++l) {
+        t->bins[2 * l] = p.bins[l];
+        t->bins[2 * l + 1] = p.bins_v ? p.bins_v[l] : p.bins[l];
+    }
 
     struct Owner {  // frees the half-built handle on every error path
         cg_tables *t;
@@ -228,7 +234,7 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
 
     const uint64_t rows = (uint64_t)t->L * 2 * t->C;
     DevBuf bins_d, lo_d, w_d, r_d, fr_d, dt_d;
-    CG_HIP(bins_d.alloc(t->L), "hipMalloc");
+    CG_HIP(bins_d.alloc((uint64_t)2 * t->L), "hipMalloc");
     CG_HIP(lo_d.alloc(rows * 4), "hipMalloc");
     CG_HIP(w_d.alloc(rows * 4), "hipMalloc");
     CG_HIP(r_d.alloc(rows * 4), "hipMalloc");
@@ -254,7 +260,8 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     CG_HIP(counts.alloc(rows * kMaxBins * 4), "hipMalloc");
     CG_HIP(flag.alloc(4), "hipMalloc");
 
-    CG_HIP(hipMemcpyAsync(t->d_bins, t->bins.data(), t->L, hipMemcpyHostToDevice, st), "copy bins");
+    CG_HIP(hipMemcpyAsync(t->d_bins, t->bins.data(), (size_t)2 * t->L, hipMemcpyHostToDevice, st),
+           "copy bins");
     CG_HIP(hipMemsetAsync(ordlo.p, 0xFF, rows * 4, st), "memset");
     CG_HIP(hipMemsetAsync(ordhi.p, 0x00, rows * 4, st), "memset");
     CG_HIP(hipMemsetAsync(counts.p, 0, rows * kMaxBins * 4, st), "memset");
@@ -639,8 +646,8 @@ int cg_tables_get_info(const cg_tables *t, cg_tables_info *info)
     info->S = t->S;
     info->group = t->G;
     info->chunk = t->Tc;
-    uint64_t bytes = (uint64_t)t->L * 2 * t->C * 8 + t->L;
-    for (uint32_t l = 0; l < t->L; ++l) bytes += (uint64_t)2 * t->C * t->bins[l] * 2;
+    uint64_t bytes = (uint64_t)t->L * 2 * t->C * 8 + (uint64_t)2 * t->L;
+    for (uint32_t r = 0; r < 2 * t->L; ++r) bytes += (uint64_t)t->C * t->bins[r] * 2;
     info->stored_bytes = bytes;
     return CG_OK;
 }

@@ -538,7 +538,7 @@ __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__r
     const uint32_t set = tmp % n_sets;
     const uint32_t row = tmp / n_sets;
     const uint32_t b = (blockIdx.x % g.NB + row) % g.NB;
-    const uint32_t N = bins[row >> 1];
+    const uint32_t N = bins[row];
     // stage f and cdf of the N used entries as bytes, and the slot table
     const uint32_t *src = dtab + (uint64_t)(row * g.NB + b) * kTabBlock;
     uint8_t *tb8 = reinterpret_cast<uint8_t *>(tab);

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void k0_finalize(Geom g, const uint8_t *__rest
 {
     uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= g.L * 2 * g.C) return;
-    uint32_t l = i / (2 * g.C);
+    uint32_t row = i / g.C;   // (layer, K/V) row
     float a = 0.0f, b = 0.0f;
     if (ord_lo[i] != 0xFFFFFFFFu) {
         a = ord2f(ord_lo[i]);
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void k0_finalize(Geom g, const uint8_t *__rest
     }
     a = a + 0.0f;  // a zero bound is +0
     b = b + 0.0f;
-    float ww = (b - a) / (float)(bins[l] - 1u);
+    float ww = (b - a) / (float)(bins[row] - 1u);
     lo[i] = a;
     w[i] = ww;
     r[i] = (ww > 0.0f) ? 1.0f / ww : 0.0f;
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
     uint32_t tmp = blockIdx.x / ntb;
     uint32_t ct = tmp % ntiles;
     uint32_t row = tmp / ntiles;
-    uint32_t N = bins[row >> 1];
+    uint32_t N = bins[row];
     uint32_t nh = N * 8 * OCT;
     for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) hist[j] = 0;
     __syncthreads();
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void k1_freqs(Geom g, const uint8_t *__restric
     uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= g.L * 2 * g.C) return;
     uint32_t row = i / g.C, c = i - row * g.C;
-    uint32_t N = bins[row >> 1];
+    uint32_t N = bins[row];
     const uint32_t *cnt = counts + (uint64_t)i * kMaxBins;
     uint64_t n = 0;
     for (uint32_t s = 0; s < N; ++s) n += cnt[s];
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict
     uint32_t t_begin = t_lo + tb * tpt;
     if (t_begin >= t_hi) return;
     uint32_t t_end = min(t_hi, t_begin + tpt);
-    uint32_t N = bins[row >> 1];
+    uint32_t N = bins[row];
     const uint16_t *base = X + (uint64_t)row * g.S * g.C + o * 8;
     uint8_t *sbase = sym + (uint64_t)row * sym_T * g.C + o * 8;
     float lo8[8], r8[8], af[8];
@@ -410,7 +410,7 @@ __device__ __forceinline__ uint32_t enc_block(const Geom &g, const uint8_t *__re
     const uint32_t set = tmp % n_sets;
     row = tmp / n_sets;
     b = (blockIdx.x % g.NB + row) % g.NB;
-    const uint32_t N = bins[row >> 1];
+    const uint32_t N = bins[row];
     uint32_t P = 1;
     while (P < N) P <<= 1;
     const uint4 *src = reinterpret_cast<const uint4 *>(dtab + (uint64_t)(row * g.NB + b) * kTabBlock);

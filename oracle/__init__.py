@@ -108,7 +108,7 @@ class Shape:
     S: int
     G: int
     Tc: int
-    bins: np.ndarray  # uint8 [L]
+    bins: np.ndarray  # uint8 [L][2] flattened: bin count of (layer l, K/V kv) at l * 2 + kv
 
     @property
     def C(self) -> int:
@@ -122,10 +122,14 @@ class Shape:
         return (self.L, self.H, self.d, self.S, self.G, self.Tc)
 
     @staticmethod
-    def make(L, H, d, S, G, Tc, bins: Sequence[int]) -> "Shape":
-        b = np.ascontiguousarray(np.asarray(bins, dtype=np.uint8))
-        assert b.shape == (L,)
-        return Shape(L, H, d, S, G, Tc, b)
+    def make(L, H, d, S, G, Tc, bins: Sequence[int], bins_v: Optional[Sequence[int]] = None) -> "Shape":
+        """bins: the bin count of each layer (K and V rows alike), or of its K rows when
+        bins_v gives those of the V rows (the keys-finer-than-values variant of the
+        Guide's Solution pillar 1)."""
+        k = np.asarray(bins, dtype=np.uint8)
+        v = k if bins_v is None else np.asarray(bins_v, dtype=np.uint8)
+        assert k.shape == (L,) and v.shape == (L,)
+        return Shape(L, H, d, S, G, Tc, np.ascontiguousarray(np.stack([k, v], axis=1).reshape(-1)))
 
 
 # ------------------------------------------------------------------ fp16 conversions
@@ -298,8 +302,6 @@ def dequantize(shp: Shape, tab: Tables, sym: np.ndarray, X_anchor_src: np.ndarra
 
 
 def table_bytes(shp: Shape) -> int:
-    """Stored side information: lo and w (4 B each) per row, one 2-byte frequency per
-    symbol per row, one byte per layer for the bin count."""
-    rows_per_layer = 2 * shp.C
-    return int(rows_per_layer * shp.L * 8 + sum(int(b) * rows_per_layer * 2 for b in shp.bins)
-               + shp.L)
+    """Stored side information: lo and w (4 B each) per channel row, one 2-byte frequency
+    per symbol per channel row, one byte per (layer, K/V) for the bin count."""
+    return int(2 * shp.C * shp.L * 8 + sum(int(b) * shp.C * 2 for b in shp.bins) + 2 * shp.L)

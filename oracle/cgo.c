@@ -127,7 +127,7 @@ uint32_t cgo_anchor_of(uint32_t t, uint32_t G, uint32_t Tc)
 
 typedef struct {
     uint32_t L, H, d, S, G, Tc;
-    const uint8_t *bins; /* [L], each in [2, 32] */
+    const uint8_t *bins; /* [L][2]: bin count of (layer l, K/V kv) at l * 2 + kv, each in [2, 32] */
 } cgo_shape;
 
 static size_t kv_index(const cgo_shape *p, uint32_t l, uint32_t kv, uint32_t t, uint32_t c)
@@ -176,7 +176,7 @@ int cgo_range(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32
                 /* the sign of a zero bound is not meaningful: +0 + -0 = +0 fixes it */
                 lo = lo + 0.0f;
                 hi = hi + 0.0f;
-                float w = (hi - lo) / (float)(bins[l] - 1u);
+                float w = (hi - lo) / (float)(bins[l * 2 + kv] - 1u);
                 lo_out[row] = lo;
                 w_out[row] = w;
                 r_out[row] = (w > 0.0f) ? 1.0f / w : 0.0f;
@@ -215,7 +215,7 @@ void cgo_quantize(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, ui
                     uint32_t a = cgo_anchor_of(t, G, Tc);
                     float delta = cgo_half_to_float(X[i]) -
                                   cgo_half_to_float(X[kv_index(&p, l, kv, a, c)]);
-                    sym[i] = quantize_one(delta, lo[row], r[row], bins[l]);
+                    sym[i] = quantize_one(delta, lo[row], r[row], bins[l * 2 + kv]);
                 }
 }
 
@@ -268,7 +268,7 @@ void cgo_freqs(uint32_t L, uint32_t C, const uint8_t *bins, const uint64_t *coun
         for (uint32_t kv = 0; kv < 2; kv++)
             for (uint32_t c = 0; c < C; c++) {
                 size_t row = ((size_t)l * 2 + kv) * C + c;
-                cgo_freqs_from_counts(counts + row * CGO_MAX_BINS, bins[l],
+                cgo_freqs_from_counts(counts + row * CGO_MAX_BINS, bins[l * 2 + kv],
                                       freqs + row * CGO_MAX_BINS);
             }
 }
@@ -446,7 +446,7 @@ int64_t cgo_encode_payload(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint3
                             if (!cgo_is_anchor(t, G, Tc))
                                 x[m++] = sym[kv_index(&p, l, kv, t, c)];
                         size_t row = ((size_t)l * 2 + kv) * C + c;
-                        nw[lane] = cgo_rans_encode(x, m, freqs + row * CGO_MAX_BINS, bins[l],
+                        nw[lane] = cgo_rans_encode(x, m, freqs + row * CGO_MAX_BINS, bins[l * 2 + kv],
                                                    w[lane], st[lane]);
                         rd[lane] = 0;
                     }
@@ -516,7 +516,7 @@ int cgo_decode(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint3
                     for (uint32_t lane = 0; lane < lanes; lane++) {
                         size_t row = ((size_t)l * 2 + kv) * C + b * CGO_LANES + lane;
                         cdf[lane][0] = 0;
-                        for (uint32_t s = 0; s < bins[l]; s++)
+                        for (uint32_t s = 0; s < bins[l * 2 + kv]; s++)
                             cdf[lane][s + 1] = cdf[lane][s] + freqs[row * CGO_MAX_BINS + s];
                         uint32_t hi16 = GROUPW();
                         state[lane] = (hi16 << 16) | GROUPW();
@@ -530,7 +530,7 @@ int cgo_decode(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint3
                             uint32_t c = b * CGO_LANES + lane;
                             size_t row = ((size_t)l * 2 + kv) * C + c;
                             uint32_t slot = state[lane] % CGO_PROB_TOTAL, s = 0;
-                            for (uint32_t j = 1; j < bins[l]; j++)
+                            for (uint32_t j = 1; j < bins[l * 2 + kv]; j++)
                                 if (cdf[lane][j] <= slot)
                                     s = j;
                             state[lane] = (cdf[lane][s + 1] - cdf[lane][s]) *

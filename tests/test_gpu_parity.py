@@ -43,17 +43,18 @@ GAUSS = configs.GenSpec(rho=0.9, heavy_tail=False, outlier_frac=0.02, outlier_mu
 HEAVY = configs.GenSpec(rho=0.85, heavy_tail=True, outlier_frac=0.05, outlier_mult=30.0, seed=1)
 
 
-def full_parity(cg, X, H, G, Tc, bins, chunk_range=None, label=""):
+def full_parity(cg, X, H, G, Tc, bins, chunk_range=None, label="", bins_v=None):
     """Runs both sides on the same cache and compares every product of the path."""
     L, _, S, C = X.shape
-    _say("[parity] %s L=%d S=%d C=%d G=%d Tc=%d bins=%s" % (label, L, S, C, G, Tc, list(bins)))
+    _say("[parity] %s L=%d S=%d C=%d G=%d Tc=%d bins=%s bins_v=%s"
+         % (label, L, S, C, G, Tc, list(bins), None if bins_v is None else list(bins_v)))
     Xh = _u16(X)
-    shp = O.Shape.make(L, H, C // H, S, G, Tc, bins)
+    shp = O.Shape.make(L, H, C // H, S, G, Tc, bins, bins_v=bins_v)
     tab_o = O.build_tables(shp, Xh)
     kb, ke = chunk_range if chunk_range else (0, shp.n_chunks)
     enc_o = O.encode(shp, Xh, tab_o, kb, ke)
 
-    tab = cg.build_cdf(X, G, Tc, bins, H_kv=H)
+    tab = cg.build_cdf(X, G, Tc, bins, H_kv=H, bins_v=bins_v)
     ex = tab.export()
     for name in ("lo", "w", "r"):
         assert np.array_equal(ex[name].view(np.uint32), getattr(tab_o, name).view(np.uint32)), name
@@ -117,6 +118,14 @@ def test_paired_chunks(cg, G, Tc, rng):
     unrolled groups) and a wavefront left with one chunk."""
     X = _gen(2, 2000, 136, HEAVY)
     full_parity(cg, X, 17, G, Tc, (32, 8), chunk_range=rng, label="paired")
+
+
+def test_keys_finer_than_values(cg):
+    """Separate bin counts for the V rows (keys kept finer than values): K 32 / 16 / 8,
+    V 16 / 4 / 2 over three layers, a ragged last chunk, G = 7, a partial lane block."""
+    X = _gen(3, 1000, 136, HEAVY)
+    tab, *_ = full_parity(cg, X, 17, 7, 300, (32, 16, 8), label="K/V bins", bins_v=(16, 4, 2))
+    assert tab.row_bins == (32, 16, 16, 4, 8, 2)
 
 
 @pytest.mark.parametrize("S,G,Tc", [(5, 10, 5), (37, 10, 37), (41, 4, 20), (64, 1, 16),

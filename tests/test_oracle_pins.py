@@ -149,7 +149,7 @@ def test_range_is_min_max_of_deltas():
                 d = np.array([x for _, _, x in _deltas(shp, X, l, kv, c)], np.float32)
                 lo, hi = d.min(), d.max()
                 assert tab.lo[l, kv, c] == lo
-                w = np.float32(np.float32(hi - lo) / np.float32(shp.bins[l] - 1))
+                w = np.float32(np.float32(hi - lo) / np.float32(shp.bins[l * 2 + kv] - 1))
                 assert tab.w[l, kv, c] == w
                 assert tab.r[l, kv, c] == (np.float32(1) / w if w > 0 else 0)
 
@@ -162,8 +162,8 @@ def test_quantizer_picks_nearest_grid_point_exactly():
     sym = O.quantize(shp, X, tab.lo, tab.r, 0, shp.S)
     checked = 0
     for l in range(shp.L):
-        N = int(shp.bins[l])
         for kv in range(2):
+            N = int(shp.bins[l * 2 + kv])
             for c in range(shp.C):
                 lo, w = Fraction(float(tab.lo[l, kv, c])), Fraction(float(tab.w[l, kv, c]))
                 for t, _, dlt in _deltas(shp, X, l, kv, c):
@@ -322,7 +322,7 @@ def test_group_words_follow_lockstep_read_order():
                     for lane in range(min(O.LANES, shp.C - b * O.LANES)):
                         c = b * O.LANES + lane
                         x = [int(sym[l, kv, t, c]) for t in toks]
-                        words, steps = O.rans_encode(x, tab.freqs[l, kv, c, :shp.bins[l]])
+                        words, steps = O.rans_encode(x, tab.freqs[l, kv, c, :shp.bins[l * 2 + kv]])
                         keyed += [((int(s), lane, j), int(wd))
                                   for j, (wd, s) in enumerate(zip(words, steps))]
                     expect = [wd for _, wd in sorted(keyed)]
@@ -413,3 +413,42 @@ def test_zero_bounds_are_positive_zero():
     shp = O.Shape.make(1, 1, C, S, 10, 30, [4])
     tab = O.build_tables(shp, X)
     assert (tab.lo.view(np.uint32) == 0).all() and (tab.w.view(np.uint32) == 0).all()
+
+
+def test_key_and_value_rows_take_their_own_bin_counts():
+    """Keys finer than values ("Guide to CacheGen", Solution pillar 1): with separate bin
+    counts for the V rows, every K row is coded exactly as in a run where all rows use the
+    K counts, and every V row as in a run with the V counts, since ranges, widths, tables
+    and streams all belong to one (layer, K/V, channel).  Checked on tables, symbols,
+    every group's payload words and the decoded rows (a partial channel block, C = 70)."""
+    L, C, S, G, Tc = 2, 70, 90, 5, 40
+    bk, bv = (16, 5), (4, 9)
+    _, X = _small_data(L=L, S=S, C=C, G=G, Tc=Tc, bins=bk)
+    shp = O.Shape.make(L, 1, C, S, G, Tc, bk, bins_v=bv)
+    assert list(shp.bins) == [16, 4, 5, 9]
+    ref = {0: O.Shape.make(L, 1, C, S, G, Tc, bk), 1: O.Shape.make(L, 1, C, S, G, Tc, bv)}
+    tab = O.build_tables(shp, X)
+    tabs = {kv: O.build_tables(s, X) for kv, s in ref.items()}
+    for kv in range(2):
+        for name in ("lo", "w", "r", "freqs"):
+            assert np.array_equal(getattr(tab, name)[:, kv], getattr(tabs[kv], name)[:, kv]), name
+    sym = O.quantize(shp, X, tab.lo, tab.r, 0, S)
+    for kv in range(2):
+        sref = O.quantize(ref[kv], X, tabs[kv].lo, tabs[kv].r, 0, S)
+        assert np.array_equal(sym[:, kv], sref[:, kv])
+        assert int(sym[:, kv].max()) < max(bk if kv == 0 else bv)
+    enc = O.encode(shp, X, tab)
+    encs = {kv: O.encode(ref[kv], X, tabs[kv]) for kv in range(2)}
+    NB = -(-C // O.LANES)
+    for k in range(shp.n_chunks):
+        for l in range(L):
+            for kv in range(2):
+                for b in range(NB):
+                    g = ((k * 2 * L) + l * 2 + kv) * NB + b
+                    mine = enc.payload[int(enc.offsets[g]):int(enc.offsets[g + 1])]
+                    e = encs[kv]
+                    theirs = e.payload[int(e.offsets[g]):int(e.offsets[g + 1])]
+                    assert np.array_equal(mine, theirs), (k, l, kv, b)
+    out = O.decode(shp, tab, enc)
+    for kv in range(2):
+        assert np.array_equal(out[:, kv], O.decode(ref[kv], tabs[kv], encs[kv])[:, kv])
