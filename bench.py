@@ -161,8 +161,46 @@ def streamed_report(dev, n_slots: int = 8, reps: int = 3, seed: int = 0) -> dict
         "%.1f GB/s, overlap %.2f), ratio %.3f"
         % (res["end_to_end_GBps"], res["h2d_GBps"], res["decode_only_GBps"], res["overlap"],
            res["compression_ratio"]))
-    del prep, out, X, pipe
+    del prep, pipe
+    res["controller"] = controller_report(w, X, out, n_slots, seed, res["network_s_trace"])
+    del out, X
     torch.cuda.empty_cache()
+    return res
+
+
+CONTROLLER_PREFILL_TOK_S = 4000.0  # modelled recompute rate of the text fallback
+
+
+def controller_report(w, X, out, n_slots: int, seed: int, slo_s: float) -> dict:
+    """The same cache and trace with the closed-loop controller choosing the levels: the
+    rate is estimated from the chunks already sent, and the SLO is the fetch time of the
+    open-loop choice above (which knows every chunk's rate in advance).  A chunk that
+    cannot meet it even at the coarsest level falls back to text when recomputing it (at a
+    modelled 4000 tokens/s) is predicted to be faster.  The chosen containers are streamed
+    and decoded once; text chunks are not."""
+    import numpy as np
+    import torch
+
+    from kv_cache_compression_cg_amd import streamed
+    ctl = streamed.ControllerConfig(slo_s=slo_s, prior_gbps=13.0,
+                                    prefill_tok_per_s=CONTROLLER_PREFILL_TOK_S)
+    prep = streamed.prepare(X, w.group, w.chunk, w.levels, H_kv=w.H_kv, seed=seed,
+                            controller=ctl)
+    tokens = [min(w.chunk, w.S - k * w.chunk) for k in range(w.n_chunks)]
+    levels, _, fetch_s = streamed.control_levels(prep.sizes, prep.bw_gbps, tokens, ctl)
+    stats = streamed.run(prep, out, n_slots=n_slots)
+    torch.cuda.synchronize()
+    lv, cnt = np.unique(levels, return_counts=True)
+    names = {streamed.TEXT: "text"}
+    res = {"slo_s": round(slo_s, 4), "prefill_tok_per_s_model": CONTROLLER_PREFILL_TOK_S,
+           "alpha": ctl.alpha, "prior_gbps": ctl.prior_gbps,
+           "chunks_per_level": {names.get(int(a), str(int(a))): int(b) for a, b in zip(lv, cnt)},
+           "fetch_s_trace": round(fetch_s, 4), "slo_met": bool(fetch_s <= slo_s),
+           "streamed_bytes": prep.streamed_bytes,
+           "total_ms": round(stats["total_ms"], 3), "decode_ms": round(stats["decode_ms"], 3)}
+    log("[controller] levels %s, fetch %.2f s over the trace (SLO %.1f s), streamed %.2f GB"
+        % (res["chunks_per_level"], fetch_s, slo_s, prep.streamed_bytes / 1e9))
+    del prep
     return res
 
 

@@ -54,6 +54,67 @@ def choose_levels(sizes: np.ndarray, bw_gbps: np.ndarray, ref_level: int = REFER
     return out
 
 
+TEXT = -1   # level of a chunk sent as text and recomputed instead of as KV
+
+
+@dataclass
+class ControllerConfig:
+    """Closed-loop level choice under a fetch-time SLO.
+
+    The pages have the compression level of each part of the context follow the bandwidth
+    so that the fetch meets its delay objective, and fall back to sending text for the
+    model to recompute when the bandwidth is too low (gptget summary of arXiv 2310.07240,
+    Methodology and abstract; phantomic12 notes).  They give no estimator or rule; the
+    ones here: the rate is estimated from the chunks already sent (an exponentially
+    weighted mean, `alpha` on the newest).  The time left in the SLO first covers every
+    remaining chunk at its coarsest level (at the estimate); what is left over, the
+    slack, is shared equally, so chunk k may spend its coarsest time plus slack / (chunks
+    left) and takes the finest level predicted to fit.  With a right estimate a feasible
+    SLO is then always met.  When the slack is negative (the SLO cannot be met even at
+    the coarsest level) and sending the chunk's tokens as text and recomputing them
+    (`prefill_tok_per_s`, a modelled rate; 0 disables the fallback) is predicted to be
+    faster than its coarsest container, the chunk falls back to text."""
+    slo_s: float
+    alpha: float = 0.5
+    prior_gbps: float = 10.0
+    prefill_tok_per_s: float = 0.0
+    text_bytes_per_token: int = 4
+
+
+def control_levels(sizes: np.ndarray, bw_gbps: np.ndarray, chunk_tokens: Sequence[int],
+                   cfg: ControllerConfig):
+    """sizes: container bytes [levels][chunks], level 0 the finest; bw_gbps: the link
+    rate each chunk actually meets (unknown to the controller until it has been sent).
+    Returns (level per chunk, TEXT for a fallback chunk; the rate estimate each choice
+    used; the simulated fetch time: transfers at the actual rates plus recomputation)."""
+    sizes = np.asarray(sizes, dtype=np.float64)
+    bw = np.asarray(bw_gbps, dtype=np.float64)
+    n_levels, n = sizes.shape
+    if bw.shape != (n,) or len(chunk_tokens) != n:
+        raise ValueError("one rate and one token count per chunk expected")
+    est = float(cfg.prior_gbps)
+    elapsed = 0.0
+    levels = np.zeros(n, dtype=np.int64)
+    estimates = np.zeros(n, dtype=np.float64)
+    for k in range(n):
+        estimates[k] = est
+        pred = sizes[:, k] * 8.0 / (est * 1e9)
+        slack = cfg.slo_s - elapsed - float(np.sum(sizes[-1, k:])) * 8.0 / (est * 1e9)
+        allowed = pred[-1] + max(slack, 0.0) / (n - k)
+        choice = int(np.nonzero(pred <= allowed)[0][0])   # the coarsest level always fits
+        text_bytes = float(chunk_tokens[k]) * cfg.text_bytes_per_token
+        recompute = (float(chunk_tokens[k]) / cfg.prefill_tok_per_s
+                     if cfg.prefill_tok_per_s > 0 else float("inf"))
+        if slack < 0.0 and text_bytes * 8.0 / (est * 1e9) + recompute < pred[-1]:
+            choice = TEXT
+        sent = text_bytes if choice == TEXT else sizes[choice, k]
+        elapsed += sent * 8.0 / (bw[k] * 1e9) + (recompute if choice == TEXT else 0.0)
+        # the transfer just made measures the link rate of this chunk
+        est = cfg.alpha * bw[k] + (1.0 - cfg.alpha) * est
+        levels[k] = choice
+    return levels, estimates, elapsed
+
+
 def network_seconds(sizes: np.ndarray, levels: np.ndarray, bw_gbps: np.ndarray) -> float:
     """Time to send the chosen containers over the trace (no overlap with decoding)."""
     sizes = np.asarray(sizes, dtype=np.float64)
@@ -76,17 +137,26 @@ class Prepared:
 
     @property
     def table_bytes(self) -> int:
-        used = sorted(set(int(v) for v in self.levels))
+        used = sorted(set(int(v) for v in self.levels if v != TEXT))
         return int(sum(self.tables[v].stored_bytes for v in used))
 
 
 def prepare(kv: torch.Tensor, group: int, chunk: int, level_bins: Sequence[Sequence[int]],
-            H_kv: int, seed: int = 0, force_levels: Optional[Sequence[int]] = None) -> Prepared:
+            H_kv: int, seed: int = 0, force_levels: Optional[Sequence[int]] = None,
+            controller: Optional[ControllerConfig] = None) -> Prepared:
     """Builds the tables of every level, encodes every chunk at every level, picks one
-    level per chunk and keeps that container in pinned host memory."""
+    level per chunk and keeps that container in pinned host memory.  A chunk at level
+    TEXT (recomputed from text) is not kept.  With `controller`, the levels come from
+    control_levels over the trace: the container sizes of every chunk at every level are
+    taken first (a sender has them: the containers are encoded ahead of time)."""
     tables = [cg.build_cdf(kv, group, chunk, bins, H_kv=H_kv) for bins in level_bins]
     n = tables[0].n_chunks
     bw = bandwidth_trace(n, seed)
+    if controller is not None:
+        all_sizes = np.array([[cg.encode(t, kv, k, k + 1).nbytes for k in range(n)]
+                              for t in tables], dtype=np.int64)
+        tokens = [min(chunk, kv.shape[2] - k * chunk) for k in range(n)]
+        force_levels = list(control_levels(all_sizes, bw, tokens, controller)[0])
     sizes = np.zeros((len(tables), n), dtype=np.int64)
     levels = np.zeros(n, dtype=np.int64)
     items = []
@@ -99,6 +169,9 @@ def prepare(kv: torch.Tensor, group: int, chunk: int, level_bins: Sequence[Seque
         else:
             lv = int(choose_levels(sizes[:, k:k + 1], bw[k:k + 1])[0])
         levels[k] = lv
+        if lv == TEXT:   # recomputed from text: nothing to stream or decode
+            del blobs
+            continue
         host = torch.empty(blobs[lv].nbytes, dtype=torch.uint8, pin_memory=True)
         blobs[lv].read_into(host)
         items.append((tables[lv], blobs[lv], host))

@@ -80,6 +80,51 @@ def test_streamed_forced_levels(cg, n_slots):
     assert stats["total_ms"] > 0 and stats["copy_ms"] > 0 and stats["decode_ms"] > 0
 
 
+def test_streamed_with_text_fallback_chunks(cg):
+    """Chunks at level TEXT (recomputed from text) are neither streamed nor decoded: their
+    rows keep what the output held; every other chunk equals the oracle's decode."""
+    L, S, H, d, G, Tc = 3, 2600, 2, 64, 10, 300
+    _say("[streamed] text fallback L=%d S=%d" % (L, S))
+    X = synth.gen_custom(L, S, H * d, HEAVY, device="cuda")
+    n = -(-S // Tc)
+    T = streamed.TEXT
+    force = [0, T, 2, T, T, 1, 0, 2, T][:n]
+    prep = streamed.prepare(X, G, Tc, LEVELS3, H_kv=H, force_levels=force)
+    assert list(prep.levels) == force and len(prep.items) == sum(v != T for v in force)
+    out = torch.full_like(X, float("nan"))
+    streamed.run(prep, out, n_slots=3)
+    torch.cuda.synchronize()
+    got = _u16(out)
+    ref, _ = _oracle_stream(_u16(X), H, G, Tc, LEVELS3, force)
+    nan16 = _u16(torch.full((1,), float("nan"), dtype=torch.float16))[0]
+    for k, lv in enumerate(force):
+        rows = slice(k * Tc, min((k + 1) * Tc, S))
+        if lv == T:
+            assert (got[:, :, rows] == nan16).all(), k
+        else:
+            assert np.array_equal(got[:, :, rows], ref[:, :, rows]), k
+
+
+def test_streamed_controller_levels(cg):
+    """Levels from the closed-loop controller (with text fallback), streamed and decoded:
+    the levels are control_levels' over the container sizes and the trace."""
+    L, S, H, d, G, Tc = 3, 3000, 2, 64, 10, 250
+    X = synth.gen_custom(L, S, H * d, HEAVY, device="cuda")
+    ctl = streamed.ControllerConfig(slo_s=2e-4, prior_gbps=13.0, prefill_tok_per_s=2e6)
+    prep = streamed.prepare(X, G, Tc, LEVELS3, H_kv=H, seed=6, controller=ctl)
+    n = prep.sizes.shape[1]
+    tokens = [min(Tc, S - k * Tc) for k in range(n)]
+    exp = streamed.control_levels(prep.sizes, prep.bw_gbps, tokens, ctl)[0]
+    assert np.array_equal(prep.levels, exp)
+    _say("[streamed] controller levels %s" % list(prep.levels))
+    out = torch.zeros_like(X)
+    streamed.run(prep, out, n_slots=2)
+    torch.cuda.synchronize()
+    keep = [int(v) for v in prep.levels]
+    ref, _ = _oracle_stream(_u16(X), H, G, Tc, LEVELS3, keep)
+    assert np.array_equal(_u16(out), ref)
+
+
 def test_streamed_chosen_levels_and_ragged_shape(cg):
     """Levels picked from the bandwidth trace; C = 72 (a partial lane block), G = 7."""
     L, S, H, d, G, Tc = 3, 2500, 9, 8, 7, 200

@@ -44,3 +44,66 @@ def test_more_bandwidth_never_picks_a_coarser_level(rows, b1, b2):
     a = streamed.choose_levels(sizes, np.full(n, lo))
     b = streamed.choose_levels(sizes, np.full(n, hi))
     assert np.all(b <= a)
+
+
+def test_controller_hand_worked():
+    """Three chunks, two levels (bytes [[100, 200, 150], [50, 100, 80]] x 1e6), actual
+    rates 8, 4, 16 Gbit/s, prior 8 Gbit/s, alpha 0.5, SLO 0.33 s.
+    Chunk 0 (estimate 8): coarsest times 0.05, 0.1, 0.08 s, slack 0.33 - 0.23 = 0.1,
+    allowed 0.05 + 0.1 / 3 = 0.0833 s; level 0 needs 0.1 -> level 1, sent in 0.05 s.
+    Chunk 1 (estimate 8): slack 0.33 - 0.05 - 0.18 = 0.1, allowed 0.1 + 0.05 = 0.15 s;
+    level 0 needs 0.2 -> level 1, sent at 4 Gbit/s in 0.2 s (elapsed 0.25); estimate 6.
+    Chunk 2 (estimate 6): coarsest 80e6 * 8 / 6e9 = 0.1067 s, slack 0.33 - 0.25 - 0.1067
+    < 0 -> level 1, sent at 16 in 0.04 s: 0.29 s, within the SLO.  With text fallback at
+    1e5 tokens/s (1536 tokens: 0.01536 s to recompute, 6144 B of text) and the slack
+    negative, chunk 2 falls back: 0.25 + 6144 * 8 / 16e9 + 0.01536 s."""
+    sizes = np.array([[100e6, 200e6, 150e6], [50e6, 100e6, 80e6]])
+    bw = [8.0, 4.0, 16.0]
+    cfg = streamed.ControllerConfig(slo_s=0.33, alpha=0.5, prior_gbps=8.0)
+    lv, est, t = streamed.control_levels(sizes, bw, [1536] * 3, cfg)
+    assert lv.tolist() == [1, 1, 1]
+    assert est.tolist() == [8.0, 8.0, 6.0]
+    assert abs(t - 0.29) < 1e-12
+    cfg.prefill_tok_per_s = 1e5
+    lv, est, t = streamed.control_levels(sizes, bw, [1536] * 3, cfg)
+    assert lv.tolist() == [1, 1, streamed.TEXT]
+    assert abs(t - (0.25 + 6144 * 8 / 16e9 + 0.01536)) < 1e-12
+
+
+def test_controller_generous_slo_takes_finest_levels():
+    rng = np.random.default_rng(1)
+    sizes = np.sort(rng.uniform(1e6, 5e7, size=(3, 40)), axis=0)[::-1]
+    bw = rng.uniform(1.0, 25.0, size=40)
+    cfg = streamed.ControllerConfig(slo_s=1e6, prefill_tok_per_s=1e4)
+    lv, _, _ = streamed.control_levels(sizes, bw, [1536] * 40, cfg)
+    assert (lv == 0).all()
+
+
+def test_controller_meets_a_feasible_slo_at_a_known_rate():
+    """With the rate constant and known (the prior equals it), the plan is exact: any SLO
+    at least the coarsest fetch time is met without falling back to text, and a looser
+    SLO never gives a coarser mix (more bytes are sent)."""
+    rng = np.random.default_rng(2)
+    sizes = np.sort(rng.uniform(1e6, 5e7, size=(3, 30)), axis=0)[::-1]
+    rate = 7.0
+    times = sizes * 8.0 / (rate * 1e9)
+    sent = []
+    for frac in (0.0, 0.3, 0.7, 1.0):
+        slo = times[-1].sum() + frac * (times[0].sum() - times[-1].sum())
+        cfg = streamed.ControllerConfig(slo_s=slo * (1 + 1e-9), prior_gbps=rate)
+        lv, _, t = streamed.control_levels(sizes, [rate] * 30, [1536] * 30, cfg)
+        assert t <= slo * (1 + 1e-9) + 1e-12
+        assert (lv != streamed.TEXT).all()
+        sent.append(float(sizes[lv, np.arange(30)].sum()))
+    assert sent == sorted(sent)
+
+
+def test_controller_without_fallback_never_sends_text():
+    rng = np.random.default_rng(3)
+    sizes = np.sort(rng.uniform(1e6, 5e7, size=(3, 30)), axis=0)[::-1]
+    cfg = streamed.ControllerConfig(slo_s=1e-3, prefill_tok_per_s=0.0)
+    lv, _, _ = streamed.control_levels(sizes, rng.uniform(0.1, 1.0, size=30), [1536] * 30, cfg)
+    assert (lv == 2).all()
+    cfg.prefill_tok_per_s = 1e6
+    lv, _, _ = streamed.control_levels(sizes, rng.uniform(0.1, 1.0, size=30), [1536] * 30, cfg)
+    assert (lv == streamed.TEXT).all()
