@@ -13,8 +13,9 @@ metric), from HIP events around each decode on the stream it runs on, averaged o
 (the container resident in HBM).  `decode_ms_in_step` is the decode inside the steps,
 right after each step's encode.  `ms_per_step` is the wall time of a whole step.
 
-An object "kv_asymmetric" covers the same cache with the V rows one step coarser than
-the K rows (decode throughput and ratio).  An object "streamed" covers the streamed
+An object "paged" decodes the same container into a paged cache (16-token pages, a
+shuffled block table); "kv_asymmetric" covers the same cache with the V rows one step
+coarser than the K rows (decode throughput and ratio).  An object "streamed" covers the streamed
 decode of the 131K-token cache
 (L=80, S=131072, 42.95 GB): every chunk encoded at three levels, one level per chunk
 chosen from a seeded bandwidth trace, the chosen containers copied from pinned host
@@ -204,6 +205,45 @@ def controller_report(w, X, out, n_slots: int, seed: int, slo_s: float) -> dict:
     return res
 
 
+PAGE_TOKENS = 16
+
+
+def paged_report(w, tab, blob, out, reps: int) -> dict:
+    """The same container decoded into a paged cache (the Guide's Best Practices: write
+    straight into the serving engine's KV blocks): 16-token pages, a seeded shuffled
+    block table, back-to-back decodes; checked against the contiguous decode in `out`
+    on the first and last layer."""
+    import torch
+
+    from kv_cache_compression_cg_amd import cg
+    nb = -(-w.S // PAGE_TOKENS)
+    gen = torch.Generator().manual_seed(0)
+    bt = torch.randperm(nb, generator=gen).to(torch.int32).to(out.device)
+    pages = torch.empty((w.L, 2, nb, PAGE_TOKENS, w.C), dtype=torch.float16, device=out.device)
+    stream = torch.cuda.current_stream(out.device)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps + 2)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        cg.decode_paged(tab, blob, pages, bt)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev[2:]]
+    dec = sum(ms) / len(ms)
+    for l in (0, w.L - 1):
+        got = pages[l][:, bt.long()].reshape(2, nb * PAGE_TOKENS, w.C)[:, :w.S]
+        assert torch.equal(got.view(torch.int16), out[l].view(torch.int16))
+    res = {"workload": w.name, "page_tokens": PAGE_TOKENS, "pages": nb,
+           "block_table": "seeded permutation", "decode_ms": round(dec, 4),
+           "decode_reps": len(ms), "value_GBps": round(w.raw_bytes / (dec * 1e-3) / 1e9, 2),
+           "pct_hbm_peak": round(100 * w.raw_bytes / (dec * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+    log("[paged] decode into %d-token pages %.3f ms (%.1f GB/s)"
+        % (PAGE_TOKENS, dec, res["value_GBps"]))
+    del pages
+    torch.cuda.empty_cache()
+    return res
+
+
 def kv_asymmetric_report(w, X, out, reps: int) -> dict:
     """Keys finer than values ("Guide to CacheGen", Solution pillar 1): the V rows take one
     step coarser bin counts than the K rows (K 32 / 16 / 8, V 16 / 8 / 4 by layer tier).
@@ -286,7 +326,7 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 4 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--no-kv-asymmetric", action="store_true",
-                    help="skip the keys-finer-than-values variant (V rows one step coarser)")
+                    help="skip the paged-output and keys-finer-than-values objects")
     ap.add_argument("--decode-reps", type=int, default=20,
                     help="back-to-back decodes after the timed steps that give `value`")
     ap.add_argument("--decode-loop", type=int, default=0, metavar="N",
@@ -421,6 +461,7 @@ def main() -> int:
                                      res["decode_ms_in_step"], res["ms_per_step"],
                                      res["compression_ratio"]))
     if not args.no_kv_asymmetric:
+        res["paged"] = paged_report(w, tab, blob, out, args.decode_reps)
         res["kv_asymmetric"] = kv_asymmetric_report(w, X, out, args.decode_reps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, X, args.cpu_threads)

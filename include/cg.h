@@ -138,6 +138,24 @@ int cg_encode(const cg_tables *tables, const void *kv_dev, uint32_t chunk_begin,
 int cg_decode(const cg_tables *tables, const cg_blob *blob, const void *container_dev,
               void *kv_out_dev, void *hip_stream);
 
+/*
+ * Decodes into a paged KV cache (vLLM-style block table) instead of a contiguous one:
+ * the decompressor writes straight into the serving engine's KV blocks ("Guide to
+ * CacheGen", Best Practices: inject into paged buffers).
+ *   pages_dev:       fp16 [L][2][num_pages][page_tokens][H_kv * d], device, caller-owned;
+ *                    one pool of num_pages pages per (layer, K/V).
+ *   block_table_dev: int32 [ceil(S / page_tokens)], device: token t of every (layer, K/V)
+ *                    goes to page block_table[t / page_tokens], row t % page_tokens.
+ *   page_tokens:     a power of two; num_pages * page_tokens * H_kv * d * 2 < 2^32.
+ * Writes the tokens of the blob's chunks; a block whose page id is negative or
+ * >= num_pages is skipped (none of its rows is written), other pages are untouched.
+ * container_dev as in cg_decode.  Fully asynchronous on hip_stream.  Errors:
+ * CG_E_INVAL, CG_E_CORRUPT, CG_E_HIP.
+ */
+int cg_decode_paged(const cg_tables *tables, const cg_blob *blob, const void *container_dev,
+                    void *pages_dev, const int32_t *block_table_dev, uint32_t page_tokens,
+                    uint32_t num_pages, void *hip_stream);
+
 /* Releases a cg_tables* or cg_blob* and its device memory.  NULL is a no-op. */
 void cg_free(void *handle);
 

@@ -65,7 +65,8 @@ class StreamStats(ctypes.Structure):
 
 EXPORTED = ["cg_build_cdf", "cg_encode", "cg_decode", "cg_free", "cg_last_error",
             "cg_tables_export", "cg_tables_get_info", "cg_blob_get_info", "cg_blob_read",
-            "cg_quantize", "cg_decode_symbols", "cg_dequantize", "cg_stream_decode"]
+            "cg_quantize", "cg_decode_symbols", "cg_dequantize", "cg_stream_decode",
+            "cg_decode_paged"]
 
 _lib = None
 
@@ -85,6 +86,7 @@ def load() -> ctypes.CDLL:
         "cg_build_cdf": [ctypes.POINTER(Params), vp, vp, pp],
         "cg_encode": [vp, vp, u32, u32, vp, pp],
         "cg_decode": [vp, vp, vp, vp, vp],
+        "cg_decode_paged": [vp, vp, vp, vp, vp, u32, u32, vp],
         "cg_tables_export": [vp, vp, vp, vp, vp],
         "cg_tables_get_info": [vp, ctypes.POINTER(TablesInfo)],
         "cg_blob_get_info": [vp, ctypes.POINTER(BlobInfo)],
@@ -276,6 +278,26 @@ def encode(tables: Tables, kv: torch.Tensor, chunk_begin: int = 0,
         _check(load().cg_encode(tables.handle, kv.data_ptr(), chunk_begin, chunk_end,
                                 _stream(kv.device), ctypes.byref(h)))
     return Blob(h, tables)
+
+
+def decode_paged(tables: Tables, blob: Blob, pages: torch.Tensor, block_table: torch.Tensor,
+                 container: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decodes into a paged cache: pages fp16 CUDA [L, 2, num_pages, page_tokens, C],
+    block_table int32 CUDA [ceil(S / page_tokens)] (logical token block -> page)."""
+    L, two, num_pages, P, C = pages.shape
+    if (pages.dtype != torch.float16 or not pages.is_cuda or not pages.is_contiguous()
+            or (L, two, C) != (tables.L, 2, tables.C)):
+        raise ValueError("pages must be contiguous fp16 CUDA [L, 2, num_pages, page_tokens, C]")
+    nb = -(-tables.S // P)
+    if (block_table.dtype != torch.int32 or not block_table.is_cuda
+            or not block_table.is_contiguous() or block_table.numel() < nb):
+        raise ValueError("block_table must be contiguous int32 CUDA with ceil(S / page_tokens) entries")
+    with torch.cuda.device(pages.device):
+        _check(load().cg_decode_paged(tables.handle, blob.handle,
+                                      container.data_ptr() if container is not None else None,
+                                      pages.data_ptr(), block_table.data_ptr(), P, num_pages,
+                                      _stream(pages.device)))
+    return pages
 
 
 def decode(tables: Tables, blob: Blob, out: Optional[torch.Tensor] = None,

@@ -405,6 +405,36 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     return CG_OK;
 }
 
+int cg_decode_paged(const cg_tables *t, const cg_blob *b, const void *container_dev,
+                    void *pages_dev, const int32_t *block_table_dev, uint32_t page_tokens,
+                    uint32_t num_pages, void *hip_stream)
+{
+    g_error.clear();
+    if (int rc = check_tables(t)) return rc;
+    if (int rc = check_blob(t, b)) return rc;
+    if (!pages_dev || !block_table_dev) return fail(CG_E_INVAL, "null pages or block table");
+    if (!page_tokens || (page_tokens & (page_tokens - 1)))
+        return fail(CG_E_INVAL, "page_tokens must be a power of two");
+    if (!num_pages) return fail(CG_E_INVAL, "no pages");
+    if ((uint64_t)num_pages * page_tokens * t->C * 2 >= (1ull << 32))
+        return fail(CG_E_INVAL, "page pool too large for 32-bit offsets");
+    DeviceScope ds;
+    CG_HIP(ds.enter(t->device), "hipSetDevice");
+    const uint8_t *cont = container_dev ? static_cast<const uint8_t *>(container_dev) : b->d_data;
+    Geom g = make_geom(t, b->hdr.chunk_begin, b->hdr.chunk_end);
+    Paged pg;
+    pg.pages = static_cast<uint16_t *>(pages_dev);
+    pg.bt = block_table_dev;
+    pg.lp = 0;
+    while ((1u << pg.lp) < page_tokens) ++pg.lp;
+    pg.num_pages = num_pages;
+    pg.n_blocks = ceil_div(t->S, page_tokens);
+    CG_HIP(launch_k3_paged(g, t->d_bins, t->d_dtab, t->d_lo, t->d_w, cont, view_of(b), pg,
+                           (hipStream_t)hip_stream),
+           "k3_decode (paged)");
+    return CG_OK;
+}
+
 int cg_decode(const cg_tables *t, const cg_blob *b, const void *container_dev, void *kv_out_dev,
               void *hip_stream)
 {

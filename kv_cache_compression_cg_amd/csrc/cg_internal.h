@@ -31,6 +31,14 @@ struct Geom {
     uint32_t kb, ke;
 };
 
+// Paged output (vLLM-style block table): pages fp16 [L][2][num_pages][1 << lp][C]; token t
+// of a (layer, K/V) row goes to page bt[t >> lp], row t & ((1 << lp) - 1).
+struct Paged {
+    uint16_t *pages;
+    const int32_t *bt;
+    uint32_t lp, num_pages, n_blocks;
+};
+
 // Byte offsets of the container sections.
 struct ContainerView {
     uint64_t offsets_off, anchors_off, anchors_bytes, payload_off, payload_words;
@@ -65,6 +73,9 @@ hipError_t launch_k5_interleave(const Geom &g, const uint32_t *lane_words,
 hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, const float *lo,
                      const float *w, const uint8_t *container, const ContainerView &cv,
                      uint16_t *out, uint8_t *sym_out, hipStream_t st);
+hipError_t launch_k3_paged(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
+                           const float *lo, const float *w, const uint8_t *container,
+                           const ContainerView &cv, const Paged &pg, hipStream_t st);
 hipError_t launch_k4(const Geom &g, const float *lo, const float *w, const uint8_t *sym,
                      const uint8_t *container, const ContainerView &cv, uint32_t t_lo,
                      uint32_t t_hi, uint32_t tpt, uint16_t *out, hipStream_t st);

@@ -182,7 +182,7 @@ __device__ __forceinline__ void flush_rows(const __amdgpu_buffer_rsrc_t &ors, ui
 // requested and the previous group's outputs (held in registers) are written; the
 // requested data is consumed at the group's end.  Waits for it therefore never wait for
 // a store issued during the group.
-template <bool SYMBOLS>
+template <bool SYMBOLS, bool PAGED = false>
 struct Stream {
     WaveDecoder dec;
     __amdgpu_buffer_rsrc_t ars, ors;
@@ -197,6 +197,71 @@ struct Stream {
     bool fetch;
     float yf[kUnrolledSteps];
     uint32_t ys[kUnrolledSteps];
+    // paged output only: chunk rows of orow / orow_held, the chunk's first token, the
+    // block whose page is cached, that page's byte offset in the row's page pool and the
+    // resource its rows are stored through (a zero-size one for an invalid page id)
+    uint32_t trow, trow_held, t0;
+    uint32_t pblk, poff;
+    const int32_t *bt;
+    uint32_t lp, n_blocks, num_pages;
+    __amdgpu_buffer_rsrc_t pool_rs, null_rs, prs;
+
+    static constexpr uint32_t kNoBlock = 0xFFFFFFFFu;
+
+    // Byte offset of chunk row tr in the row's page pool, and the resource to store it
+    // through.  A page id that is not a page of the pool selects the zero-size resource:
+    // the store is still issued (so every row store of a group stays unconditional) and
+    // the buffer range check discards it.
+    __device__ __forceinline__ uint32_t page_row(uint32_t tr)
+    {
+        const uint32_t t = t0 + tr, blk = t >> lp;
+        if (blk != pblk) {
+            pblk = blk;
+            // a scalar load (the table is read-only and the same for the whole wavefront),
+            // waited for in the same block
+            uint32_t pg = kNoBlock;
+            if (blk < n_blocks) {
+                const int32_t *p = bt + blk;
+                asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                             : "=s"(pg) : "s"(p) : "memory");
+            }
+            const bool ok = pg < num_pages;
+            poff = ok ? (pg << lp) * ostride : 0u;
+            prs = ok ? pool_rs : null_rs;
+        }
+        return poff + (t & ((1u << lp) - 1u)) * ostride;
+    }
+
+    // stores value v as chunk row tr (byte offset orow_lin in the linear output)
+    __device__ __forceinline__ void store_row(uint32_t orow_lin, uint32_t tr, uint32_t v)
+    {
+        if constexpr (PAGED) {
+            const uint32_t o = page_row(tr);
+            put_out<SYMBOLS>(prs, olane, o, v);
+        } else {
+            put_out<SYMBOLS>(ors, olane, orow_lin, v);
+        }
+    }
+
+    // the rows held for one unrolled group
+    __device__ __forceinline__ void flush()
+    {
+        if constexpr (!PAGED) {
+            flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUnrolledSteps; u += 2) {
+                if (u + 1 < kUnrolledSteps) {
+                    const f32x2 v = {yf[u], yf[u + 1]};
+                    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+                    store_row(0, trow_held + u, h & 0xFFFFu);
+                    store_row(0, trow_held + u + 1, h >> 16);
+                } else {
+                    store_row(0, trow_held + u, f2h(yf[u]));
+                }
+            }
+        }
+    }
 
     __device__ __forceinline__ void init(const Geom &g, uint16_t *ring,
                                          const float *__restrict__ lo,
@@ -204,10 +269,11 @@ struct Stream {
                                          const uint8_t *__restrict__ container,
                                          const ContainerView &cv, uint32_t k, uint32_t row,
                                          uint32_t b, uint32_t lane, bool present,
-                                         uint16_t *__restrict__ out, uint8_t *__restrict__ sym_out)
+                                         uint16_t *__restrict__ out, uint8_t *__restrict__ sym_out,
+                                         const Paged &pg)
     {
         const uint32_t nl = min(kLanes, g.C - b * kLanes);
-        const uint32_t t0 = k * g.Tc;
+        const uint32_t t0_chunk = k * g.Tc;
         len = chunk_len(g, k);
         ng = (len + g.G - 1) / g.G;
         dec.present = present;
@@ -230,10 +296,27 @@ struct Stream {
                         (uint32_t)min(cv.anchors_bytes - min(2 * aoff, cv.anchors_bytes),
                                       (uint64_t)0xFFFFFFFFu));
         astride = 2 * g.C;
-        const uint64_t obase = ((uint64_t)row * g.S + t0) * g.C + b * kLanes;
+        const uint64_t obase = ((uint64_t)row * g.S + t0_chunk) * g.C + b * kLanes;
         ors = SYMBOLS ? make_rsrc(sym_out + obase, 0xFFFFFFFFu) : make_rsrc(out + obase, 0xFFFFFFFFu);
         ostride = g.C * (SYMBOLS ? 1u : 2u);  // bytes between token rows
         olane = lane * (SYMBOLS ? 1u : 2u);
+        if constexpr (PAGED) {
+            // this row's page pool: num_pages pages of 2^lp token rows
+            const uint64_t pool = ((uint64_t)pg.num_pages << pg.lp) * g.C;
+            uint16_t *base = pg.pages + (uint64_t)row * pool + b * kLanes;
+            pool_rs = make_rsrc(base, (uint32_t)(2 * pool - 2 * (uint64_t)b * kLanes));
+            null_rs = make_rsrc(base, 0u);
+            prs = null_rs;
+            bt = pg.bt;
+            lp = pg.lp;
+            n_blocks = pg.n_blocks;
+            num_pages = pg.num_pages;
+            t0 = t0_chunk;
+            pblk = kNoBlock;
+            poff = 0;
+        }
+        trow = 0;
+        trow_held = 0;
 
         dec.x = kStateLow;
         dec.dlo = present ? lo[(uint64_t)row * g.C + b * kLanes + lane] : 0.0f;
@@ -287,21 +370,23 @@ struct Stream {
     // write_rows for a stream holding rows with every lane present
     __device__ __forceinline__ void write_held_rows()
     {
-        flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
+        flush();
         held = false;
-        put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? 0u : a16);
+        store_row(orow, trow, SYMBOLS ? 0u : a16);
         orow += ostride;
+        ++trow;
     }
 
     // the previous group's outputs, then this group's anchor row
     __device__ __forceinline__ void write_rows()
     {
         if (held) {
-            if (dec.present) flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
+            if (dec.present) flush();
             held = false;
         }
-        if (dec.present) put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? 0u : a16);
+        if (dec.present) store_row(orow, trow, SYMBOLS ? 0u : a16);
         orow += ostride;
+        ++trow;
     }
 
     // takes in the requests; the ring chunk is dropped if a refill inside the group
@@ -341,6 +426,8 @@ struct Stream {
         held = true;
         orow_held = orow;
         orow += kUnrolledSteps * ostride;
+        trow_held = trow;
+        trow += kUnrolledSteps;
     }
 
     __device__ __forceinline__ void unrolled(const uint8_t *tab, uint32_t lane)
@@ -362,21 +449,22 @@ struct Stream {
             float dq;
             const uint32_t sym = dec.symbol(tab, lane, dq);
             if (dec.present)
-                put_out<SYMBOLS>(ors, olane, orow, SYMBOLS ? sym : f2h(af + dq));
+                store_row(orow, trow, SYMBOLS ? sym : f2h(af + dq));
             orow += ostride;
+            ++trow;
             if (++dec.i < dec.m) dec.renorm(lane);
         }
     }
 
     __device__ __forceinline__ void final_flush()
     {
-        if (held && dec.present) flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
+        if (held && dec.present) flush();
     }
 };
 
 // An unrolled group of both streams of a wavefront in lockstep.
-template <bool SYMBOLS, int NS>
-__device__ __forceinline__ void paired_steps(Stream<SYMBOLS> (&st)[NS], const uint8_t *tab,
+template <bool SYMBOLS, bool PAGED, int NS>
+__device__ __forceinline__ void paired_steps(Stream<SYMBOLS, PAGED> (&st)[NS], const uint8_t *tab,
                                              uint32_t lane)
 {
 #pragma unroll
@@ -433,7 +521,7 @@ __device__ __forceinline__ void paired_steps(Stream<SYMBOLS> (&st)[NS], const ui
 // One wavefront decodes NS chunks of the same (row, channel block) in lockstep, sharing
 // the block's LDS table.  With two, the symbol decodes of both streams sit in one
 // basic block, so the dependent LDS reads of one overlap the arithmetic of the other.
-template <bool SYMBOLS, bool FULL, int NS>
+template <bool SYMBOLS, bool FULL, int NS, bool PAGED>
 __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__restrict__ tab,
                                               uint16_t *__restrict__ ring,
                                               const float *__restrict__ lo,
@@ -442,14 +530,14 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
                                               const ContainerView &cv, uint32_t k0, uint32_t k1,
                                               uint32_t row, uint32_t b, uint32_t lane,
                                               uint16_t *__restrict__ out,
-                                              uint8_t *__restrict__ sym_out)
+                                              uint8_t *__restrict__ sym_out, const Paged &pg)
 {
     const bool present = FULL || lane < min(kLanes, g.C - b * kLanes);
-    Stream<SYMBOLS> st[NS];
+    Stream<SYMBOLS, PAGED> st[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
         st[s].init(g, ring + s * kRingAlloc, lo, w, container, cv, s == 0 ? k0 : k1, row, b, lane,
-                   present, out, sym_out);
+                   present, out, sym_out, pg);
 #pragma unroll
     for (int s = 0; s < NS; ++s) st[s].first_anchor(lane);
     uint32_t ngmax = st[0].ng;
@@ -522,7 +610,7 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
 // row: otherwise an XCD would hold only the columns b with one residue mod 8, and its
 // writes and anchor reads would queue on the few L2 / memory channels those addresses
 // map to.
-template <bool SYMBOLS, uint32_t WPB>
+template <bool SYMBOLS, uint32_t WPB, bool PAGED = false>
 __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
                                                   const uint32_t *__restrict__ dtab,
                                                   const float *__restrict__ lo,
@@ -530,7 +618,7 @@ __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__r
                                                   const uint8_t *__restrict__ container,
                                                   ContainerView cv, uint32_t n_sets,
                                                   uint16_t *__restrict__ out,
-                                                  uint8_t *__restrict__ sym_out)
+                                                  uint8_t *__restrict__ sym_out, Paged pg)
 {
     __shared__ uint32_t tab[kLdsWords];
     __shared__ uint16_t rings[WPB * kStreamsPerWave * kRingAlloc];
@@ -562,14 +650,14 @@ __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__r
     const bool pair = k1 < g.ke;
     if (g.C - b * kLanes >= kLanes) {
         if (pair)
-            decode_chunks<SYMBOLS, true, 2>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out);
+            decode_chunks<SYMBOLS, true, 2, PAGED>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
         else
-            decode_chunks<SYMBOLS, true, 1>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out);
+            decode_chunks<SYMBOLS, true, 1, PAGED>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
     } else {
         if (pair)
-            decode_chunks<SYMBOLS, false, 2>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out);
+            decode_chunks<SYMBOLS, false, 2, PAGED>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
         else
-            decode_chunks<SYMBOLS, false, 1>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out);
+            decode_chunks<SYMBOLS, false, 1, PAGED>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
     }
 }
 
@@ -642,21 +730,42 @@ hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, c
     const uint32_t n_sets = (g.ke - g.kb + per_block - 1) / per_block;
     const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
     const dim3 grid((uint32_t)blocks), block(wpb * kLanes);
+    const Paged none{};
     if (sym_out) {
         if (wide)
             hipLaunchKernelGGL((k3_decode<true, kWavesPerBlock>), grid, block, 0, st, g, bins,
-                               dtab, lo, w, container, cv, n_sets, out, sym_out);
+                               dtab, lo, w, container, cv, n_sets, out, sym_out, none);
         else
             hipLaunchKernelGGL((k3_decode<true, 1>), grid, block, 0, st, g, bins, dtab,
-                               lo, w, container, cv, n_sets, out, sym_out);
+                               lo, w, container, cv, n_sets, out, sym_out, none);
     } else {
         if (wide)
             hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock>), grid, block, 0, st, g, bins,
-                               dtab, lo, w, container, cv, n_sets, out, sym_out);
+                               dtab, lo, w, container, cv, n_sets, out, sym_out, none);
         else
             hipLaunchKernelGGL((k3_decode<false, 1>), grid, block, 0, st, g, bins, dtab,
-                               lo, w, container, cv, n_sets, out, sym_out);
+                               lo, w, container, cv, n_sets, out, sym_out, none);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_k3_paged(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
+                           const float *lo, const float *w, const uint8_t *container,
+                           const ContainerView &cv, const Paged &pg, hipStream_t st)
+{
+    const uint32_t nk = g.ke - g.kb;
+    const bool wide = nk >= kWavesPerBlock * kStreamsPerWave;
+    const uint32_t wpb = wide ? kWavesPerBlock : 1u;
+    const uint32_t per_block = wpb * kStreamsPerWave;
+    const uint32_t n_sets = (g.ke - g.kb + per_block - 1) / per_block;
+    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
+    const dim3 grid((uint32_t)blocks), block(wpb * kLanes);
+    if (wide)
+        hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock, true>), grid, block, 0, st, g, bins,
+                           dtab, lo, w, container, cv, n_sets, nullptr, nullptr, pg);
+    else
+        hipLaunchKernelGGL((k3_decode<false, 1, true>), grid, block, 0, st, g, bins, dtab, lo, w,
+                           container, cv, n_sets, nullptr, nullptr, pg);
     return hipGetLastError();
 }
 

@@ -213,3 +213,71 @@ def test_reconstruction_bound_at_scale(cg):
     tol = wb / 2 * (1 + 2 ** -20) + ulp / 2 + 2 ** -22 * (
         xs.abs()[:, :, ~anchor] + ys.abs()[:, :, ~anchor] + 2 * lo.abs()[:, :, None, :] + 64 * wb)
     assert bool((err <= tol).all())
+
+
+def _gather_pages(pages, bt, S):
+    """[L, 2, num_pages, P, C] pages read through the block table back to [L, 2, S, C]."""
+    L, _, _, P, C = pages.shape
+    nb = -(-S // P)
+    return pages[:, :, bt[:nb].long()].reshape(L, 2, nb * P, C)[:, :, :S]
+
+
+@pytest.mark.parametrize("S,Tc,P,rng", [(1000, 300, 16, None), (2000, 90, 64, None),
+                                        (700, 256, 1, None), (2000, 60, 16, (2, 30))])
+def test_paged_output_matches_oracle(cg, S, Tc, P, rng):
+    """cg_decode_paged through a shuffled block table equals the oracle's decode bit for
+    bit; pages no block maps to, and rows of the blob's other chunks, stay untouched."""
+    _say("[paged] S=%d Tc=%d P=%d chunks=%s" % (S, Tc, P, rng))
+    L, C, H, G, bins = 2, 136, 17, 10, (32, 8)
+    X = _gen(L, S, C, HEAVY)
+    n_chunks = -(-S // Tc)
+    kb, ke = rng if rng else (0, n_chunks)
+    tab = cg.build_cdf(X, G, Tc, bins, H_kv=H)
+    blob = cg.encode(tab, X, kb, ke)
+    nb = -(-S // P)
+    n_pages = nb + 5
+    gen = torch.Generator().manual_seed(S + P)
+    bt = torch.randperm(n_pages, generator=gen)[:nb].to(torch.int32).cuda()
+    pages = torch.full((L, 2, n_pages, P, C), float("nan"), dtype=torch.float16, device="cuda")
+    cg.decode_paged(tab, blob, pages, bt)
+    torch.cuda.synchronize()
+    Xh = _u16(X)
+    shp = O.Shape.make(L, H, C // H, S, G, Tc, bins)
+    tab_o = O.build_tables(shp, Xh)
+    enc_o = O.encode(shp, Xh, tab_o, kb, ke)
+    nan16 = _u16(torch.full((1,), float("nan"), dtype=torch.float16))[0]
+    ref = O.decode(shp, tab_o, enc_o, out=np.full(Xh.shape, nan16, np.uint16))
+    got = _u16(_gather_pages(pages, bt, S))
+    assert np.array_equal(got, ref)
+    unused = sorted(set(range(n_pages)) - set(bt.cpu().tolist()))
+    assert (_u16(pages[:, :, unused]) == nan16).all()
+
+
+def test_paged_output_skips_invalid_page_ids(cg):
+    """Blocks mapped to a negative page id or one past the pool write nothing."""
+    L, S, C, Tc, P = 2, 600, 64, 200, 16
+    X = _gen(L, S, C, GAUSS)
+    tab = cg.build_cdf(X, 10, Tc, (8, 8), H_kv=1)
+    blob = cg.encode(tab, X)
+    nb = -(-S // P)
+    bt = torch.arange(nb, dtype=torch.int32)
+    bad = [3, 17, 30]
+    bt[3], bt[17], bt[30] = -1, nb, 1 << 30
+    bt = bt.cuda()
+    pages = torch.full((L, 2, nb, P, C), float("nan"), dtype=torch.float16, device="cuda")
+    cg.decode_paged(tab, blob, pages, bt)
+    ref = cg.decode(tab, blob)
+    torch.cuda.synchronize()
+    nan16 = _u16(torch.full((1,), float("nan"), dtype=torch.float16))[0]
+    got = _u16(pages)
+    want = _u16(ref)
+    for j in range(nb):
+        rows = slice(j * P, min((j + 1) * P, S))
+        if j in bad:
+            assert (got[:, :, j] == nan16).all(), j    # page j belongs to no valid block
+        else:
+            n = rows.stop - rows.start
+            assert np.array_equal(got[:, :, j, :n], want[:, :, rows]), j
+    bt12 = torch.zeros(-(-S // 12), dtype=torch.int32, device="cuda")
+    with pytest.raises(cg.CgError):        # 12 tokens per page: not a power of two
+        cg.decode_paged(tab, blob, pages[:, :, :, :12].contiguous(), bt12)
