@@ -190,31 +190,30 @@ struct Stream {
     uint32_t astride, ostride, olane;
     uint32_t a16;               // anchor row of the current group (fp16 bits)
     float af;
-    uint32_t orow;              // byte offset of the current anchor row
-    uint32_t orow_held;         // byte offset of the first row held in yf / ys
+    uint32_t orow;              // byte offset of the current anchor row (paged: its token)
+    uint32_t orow_held;         // byte offset of the first row held in yf / ys (paged: token)
     bool held;                  // yf / ys hold the outputs of the previous group
     uint32_t a_next, pf, pf_at; // requests of the current group
     bool fetch;
     float yf[kUnrolledSteps];
     uint32_t ys[kUnrolledSteps];
-    // paged output only: chunk rows of orow / orow_held, the chunk's first token, the
-    // block whose page is cached, that page's byte offset in the row's page pool and the
-    // resource its rows are stored through (a zero-size one for an invalid page id)
-    uint32_t trow, trow_held, t0;
+    // paged output only (ors is then the row's page pool): the block whose page is
+    // cached, that page's byte offset in the pool and the resource its rows are stored
+    // through (a zero-size one for an invalid page id)
     uint32_t pblk, poff;
     const int32_t *bt;
     uint32_t lp, n_blocks, num_pages;
-    __amdgpu_buffer_rsrc_t pool_rs, null_rs, prs;
+    __amdgpu_buffer_rsrc_t prs;
 
     static constexpr uint32_t kNoBlock = 0xFFFFFFFFu;
 
-    // Byte offset of chunk row tr in the row's page pool, and the resource to store it
-    // through.  A page id that is not a page of the pool selects the zero-size resource:
-    // the store is still issued (so every row store of a group stays unconditional) and
-    // the buffer range check discards it.
-    __device__ __forceinline__ uint32_t page_row(uint32_t tr)
+    // Byte offset of token t in the row's page pool, and the resource to store it
+    // through.  A page id that is not a page of the pool selects a resource of zero size
+    // and address: the store is still issued (so every row store of a group stays
+    // unconditional) and the buffer range check discards it.
+    __device__ __forceinline__ uint32_t page_row(uint32_t t)
     {
-        const uint32_t t = t0 + tr, blk = t >> lp;
+        const uint32_t blk = t >> lp;
         if (blk != pblk) {
             pblk = blk;
             // a scalar load (the table is read-only and the same for the whole wavefront),
@@ -227,38 +226,51 @@ struct Stream {
             }
             const bool ok = pg < num_pages;
             poff = ok ? (pg << lp) * ostride : 0u;
-            prs = ok ? pool_rs : null_rs;
+            prs = ok ? ors : make_rsrc(nullptr, 0u);
         }
         return poff + (t & ((1u << lp) - 1u)) * ostride;
     }
 
-    // stores value v as chunk row tr (byte offset orow_lin in the linear output)
-    __device__ __forceinline__ void store_row(uint32_t orow_lin, uint32_t tr, uint32_t v)
+    // stores value v as the row at orow value r (paged: token r)
+    __device__ __forceinline__ void store_row(uint32_t r, uint32_t v)
     {
         if constexpr (PAGED) {
-            const uint32_t o = page_row(tr);
+            const uint32_t o = page_row(r);
             put_out<SYMBOLS>(prs, olane, o, v);
         } else {
-            put_out<SYMBOLS>(ors, olane, orow_lin, v);
+            put_out<SYMBOLS>(ors, olane, r, v);
         }
     }
+
+    // step of orow per token row: bytes in the linear output, one token when paged
+    __device__ __forceinline__ uint32_t rstep() const { return PAGED ? 1u : ostride; }
 
     // the rows held for one unrolled group
     __device__ __forceinline__ void flush()
     {
         if constexpr (!PAGED) {
             flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
+        } else if ((1u << lp) - (orow_held & ((1u << lp) - 1u)) >= (uint32_t)kUnrolledSteps) {
+            // the group's rows lie in one page: stored as the linear output stores them
+            const uint32_t o = page_row(orow_held);
+            flush_rows<SYMBOLS>(prs, olane, o, ostride, yf, ys);
         } else {
+            flush_paged_rows();
+        }
+    }
+
+    // the held rows one by one, each through its own page
+    __device__ __forceinline__ void flush_paged_rows()
+    {
 #pragma unroll
-            for (int u = 0; u < kUnrolledSteps; u += 2) {
-                if (u + 1 < kUnrolledSteps) {
-                    const f32x2 v = {yf[u], yf[u + 1]};
-                    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-                    store_row(0, trow_held + u, h & 0xFFFFu);
-                    store_row(0, trow_held + u + 1, h >> 16);
-                } else {
-                    store_row(0, trow_held + u, f2h(yf[u]));
-                }
+        for (int u = 0; u < kUnrolledSteps; u += 2) {
+            if (u + 1 < kUnrolledSteps) {
+                const f32x2 v = {yf[u], yf[u + 1]};
+                const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+                store_row(orow_held + u, h & 0xFFFFu);
+                store_row(orow_held + u + 1, h >> 16);
+            } else {
+                store_row(orow_held + u, f2h(yf[u]));
             }
         }
     }
@@ -303,20 +315,16 @@ struct Stream {
         if constexpr (PAGED) {
             // this row's page pool: num_pages pages of 2^lp token rows
             const uint64_t pool = ((uint64_t)pg.num_pages << pg.lp) * g.C;
-            uint16_t *base = pg.pages + (uint64_t)row * pool + b * kLanes;
-            pool_rs = make_rsrc(base, (uint32_t)(2 * pool - 2 * (uint64_t)b * kLanes));
-            null_rs = make_rsrc(base, 0u);
-            prs = null_rs;
+            ors = make_rsrc(pg.pages + (uint64_t)row * pool + b * kLanes,
+                            (uint32_t)(2 * pool - 2 * (uint64_t)b * kLanes));
+            prs = make_rsrc(nullptr, 0u);
             bt = pg.bt;
             lp = pg.lp;
             n_blocks = pg.n_blocks;
             num_pages = pg.num_pages;
-            t0 = t0_chunk;
             pblk = kNoBlock;
             poff = 0;
         }
-        trow = 0;
-        trow_held = 0;
 
         dec.x = kStateLow;
         dec.dlo = present ? lo[(uint64_t)row * g.C + b * kLanes + lane] : 0.0f;
@@ -330,8 +338,8 @@ struct Stream {
         }
         dec.cur = 2 * nl;
         held = false;
-        orow = 0;
-        orow_held = 0;
+        orow = PAGED ? t0_chunk : 0u;
+        orow_held = orow;
     }
 
     // first anchor row; the empty asm pins the wait for it here
@@ -372,9 +380,8 @@ struct Stream {
     {
         flush();
         held = false;
-        store_row(orow, trow, SYMBOLS ? 0u : a16);
-        orow += ostride;
-        ++trow;
+        store_row(orow, SYMBOLS ? 0u : a16);
+        orow += rstep();
     }
 
     // the previous group's outputs, then this group's anchor row
@@ -384,9 +391,8 @@ struct Stream {
             if (dec.present) flush();
             held = false;
         }
-        if (dec.present) store_row(orow, trow, SYMBOLS ? 0u : a16);
-        orow += ostride;
-        ++trow;
+        if (dec.present) store_row(orow, SYMBOLS ? 0u : a16);
+        orow += rstep();
     }
 
     // takes in the requests; the ring chunk is dropped if a refill inside the group
@@ -425,9 +431,7 @@ struct Stream {
         dec.i += kUnrolledSteps;
         held = true;
         orow_held = orow;
-        orow += kUnrolledSteps * ostride;
-        trow_held = trow;
-        trow += kUnrolledSteps;
+        orow += kUnrolledSteps * rstep();
     }
 
     __device__ __forceinline__ void unrolled(const uint8_t *tab, uint32_t lane)
@@ -449,9 +453,8 @@ struct Stream {
             float dq;
             const uint32_t sym = dec.symbol(tab, lane, dq);
             if (dec.present)
-                store_row(orow, trow, SYMBOLS ? sym : f2h(af + dq));
-            orow += ostride;
-            ++trow;
+                store_row(orow, SYMBOLS ? sym : f2h(af + dq));
+            orow += rstep();
             if (++dec.i < dec.m) dec.renorm(lane);
         }
     }
