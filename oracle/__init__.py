@@ -59,10 +59,10 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB)
         L.cgo_half_to_float_n.argtypes = [_u16p, _f32p, ctypes.c_size_t]
         L.cgo_float_to_half_n.argtypes = [_f32p, _u16p, ctypes.c_size_t]
-        L.cgo_range.argtypes = [_u32] * 6 + [_u8p, _u16p, _f32p, _f32p, _f32p]
+        L.cgo_range.argtypes = [_u32] * 6 + [_u8p, _u16p, _f32p, _f32p, _f32p, _u32]
         L.cgo_range.restype = ctypes.c_int
         L.cgo_quantize.argtypes = [_u32] * 6 + [_u8p, _u16p, _f32p, _f32p, _u32, _u32, _u8p]
-        L.cgo_histograms.argtypes = [_u32] * 6 + [_u8p, _u8p, _u64p]
+        L.cgo_histograms.argtypes = [_u32] * 6 + [_u8p, _u8p, _u64p, _u32]
         L.cgo_freqs.argtypes = [_u32, _u32, _u8p, _u64p, _u16p]
         L.cgo_freqs_from_counts.argtypes = [_u64p, _u32, _u16p]
         L.cgo_rans_encode.argtypes = [_u8p, _u32, _u16p, _u32, _u16p, _i32p]
@@ -109,6 +109,7 @@ class Shape:
     G: int
     Tc: int
     bins: np.ndarray  # uint8 [L][2] flattened: bin count of (layer l, K/V kv) at l * 2 + kv
+    n_sink: int = 0   # first tokens of the sequence kept in fp16 (attention sinks)
 
     @property
     def C(self) -> int:
@@ -122,14 +123,18 @@ class Shape:
         return (self.L, self.H, self.d, self.S, self.G, self.Tc)
 
     @staticmethod
-    def make(L, H, d, S, G, Tc, bins: Sequence[int], bins_v: Optional[Sequence[int]] = None) -> "Shape":
+    def make(L, H, d, S, G, Tc, bins: Sequence[int], bins_v: Optional[Sequence[int]] = None,
+             n_sink: int = 0) -> "Shape":
         """bins: the bin count of each layer (K and V rows alike), or of its K rows when
         bins_v gives those of the V rows (the keys-finer-than-values variant of the
-        Guide's Solution pillar 1)."""
+        Guide's Solution pillar 1).  n_sink: the first n_sink tokens of the sequence are
+        reproduced exactly from an fp16 copy and left out of the ranges and histograms
+        (the Guide's Best Practices: protect the attention sinks)."""
         k = np.asarray(bins, dtype=np.uint8)
         v = k if bins_v is None else np.asarray(bins_v, dtype=np.uint8)
         assert k.shape == (L,) and v.shape == (L,)
-        return Shape(L, H, d, S, G, Tc, np.ascontiguousarray(np.stack([k, v], axis=1).reshape(-1)))
+        return Shape(L, H, d, S, G, Tc, np.ascontiguousarray(np.stack([k, v], axis=1).reshape(-1)),
+                     int(n_sink))
 
 
 # ------------------------------------------------------------------ fp16 conversions
@@ -155,6 +160,7 @@ class Tables:
     r: np.ndarray       # float32 [L, 2, C]
     counts: np.ndarray  # uint64 [L, 2, C, 32]
     freqs: np.ndarray   # uint16 [L, 2, C, 32]
+    sinks: Optional[np.ndarray] = None  # uint16 [L, 2, min(n_sink, S), C]: fp16 copy
 
 
 class NonFinite(ValueError):
@@ -169,15 +175,17 @@ def build_tables(shp: Shape, X: np.ndarray) -> Tables:
     w = np.empty_like(lo)
     r = np.empty_like(lo)
     rc = lib().cgo_range(*shp.args(), _p(shp.bins, _u8p), _p(X, _u16p), _p(lo, _f32p),
-                         _p(w, _f32p), _p(r, _f32p))
+                         _p(w, _f32p), _p(r, _f32p), shp.n_sink)
     if rc == -4:
         raise NonFinite("input holds Inf or NaN")
     sym = quantize(shp, X, lo, r, 0, shp.S)
     counts = np.empty((shp.L, 2, shp.C, MAX_BINS), np.uint64)
-    lib().cgo_histograms(*shp.args(), _p(shp.bins, _u8p), _p(sym, _u8p), _p(counts, _u64p))
+    lib().cgo_histograms(*shp.args(), _p(shp.bins, _u8p), _p(sym, _u8p), _p(counts, _u64p),
+                         shp.n_sink)
     freqs = np.empty((shp.L, 2, shp.C, MAX_BINS), np.uint16)
     lib().cgo_freqs(shp.L, shp.C, _p(shp.bins, _u8p), _p(counts, _u64p), _p(freqs, _u16p))
-    return Tables(lo, w, r, counts, freqs)
+    sinks = X[:, :, :min(shp.n_sink, shp.S)].copy()
+    return Tables(lo, w, r, counts, freqs, sinks)
 
 
 def freqs_from_counts(counts: Sequence[int], N: int) -> np.ndarray:
@@ -287,7 +295,14 @@ def decode(shp: Shape, tab: Tables, enc: Encoded, out: Optional[np.ndarray] = No
                           payload.size, _p(anchors, _u16p), _p(out, _u16p))
     if rc != 0:
         raise ValueError("inconsistent container (code %d)" % rc)
+    _put_sinks(shp, tab, out, enc.k_begin * shp.Tc, min(enc.k_end * shp.Tc, shp.S))
     return out
+
+
+def _put_sinks(shp: Shape, tab: Tables, out: np.ndarray, t_begin: int, t_end: int) -> None:
+    """The sink tokens in [t_begin, t_end) take their stored fp16 values."""
+    for t in range(t_begin, min(t_end, shp.n_sink, shp.S)):
+        out[:, :, t] = tab.sinks[:, :, t]
 
 
 def dequantize(shp: Shape, tab: Tables, sym: np.ndarray, X_anchor_src: np.ndarray,
@@ -298,10 +313,13 @@ def dequantize(shp: Shape, tab: Tables, sym: np.ndarray, X_anchor_src: np.ndarra
                          _p(np.ascontiguousarray(sym, np.uint8), _u8p),
                          _p(np.ascontiguousarray(X_anchor_src, np.uint16), _u16p),
                          t_begin, t_end, _p(out, _u16p))
+    _put_sinks(shp, tab, out, t_begin, t_end)
     return out
 
 
 def table_bytes(shp: Shape) -> int:
     """Stored side information: lo and w (4 B each) per channel row, one 2-byte frequency
-    per symbol per channel row, one byte per (layer, K/V) for the bin count."""
-    return int(2 * shp.C * shp.L * 8 + sum(int(b) * shp.C * 2 for b in shp.bins) + 2 * shp.L)
+    per symbol per channel row, one byte per (layer, K/V) for the bin count, and the fp16
+    copy of the sink tokens."""
+    return int(2 * shp.C * shp.L * 8 + sum(int(b) * shp.C * 2 for b in shp.bins) + 2 * shp.L
+               + 2 * shp.L * min(shp.n_sink, shp.S) * shp.C * 2)

@@ -139,13 +139,16 @@ static size_t kv_index(const cgo_shape *p, uint32_t l, uint32_t kv, uint32_t t, 
 /* ------------------------------------------------------------------------------ */
 /* Step 2-3a: per-channel range of the anchor deltas.                               */
 /*   Delta = f32(x_t) - f32(x_anchor)    (one binary32 subtraction)                 */
-/*   lo, hi = min / max over every non-anchor token of the channel (all chunks);    */
+/*   lo, hi = min / max over every non-anchor token of the channel (all chunks)     */
+/*   except the first n_sink tokens of the sequence, which are kept in fp16         */
+/*   ("Guide to CacheGen", Best Practices: protect the attention sinks);            */
 /*   lo = hi = 0 when the channel has no non-anchor token; a zero bound is +0;      */
 /*   w = (hi - lo) / (N - 1);  r = 1 / w, or 0 when w == 0.                          */
 /* Returns -4 if any input element is Inf or NaN, else 0.                           */
 /* ------------------------------------------------------------------------------ */
 int cgo_range(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
-              const uint8_t *bins, const uint16_t *X, float *lo_out, float *w_out, float *r_out)
+              const uint8_t *bins, const uint16_t *X, float *lo_out, float *w_out, float *r_out,
+              uint32_t n_sink)
 {
     cgo_shape p = {L, H, d, S, G, Tc, bins};
     uint32_t C = H * d;
@@ -158,7 +161,7 @@ int cgo_range(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32
             for (uint32_t c = 0; c < C; c++) {
                 int any = 0;
                 float lo = 0.0f, hi = 0.0f;
-                for (uint32_t t = 0; t < S; t++) {
+                for (uint32_t t = n_sink; t < S; t++) {
                     if (cgo_is_anchor(t, G, Tc))
                         continue;
                     uint32_t a = cgo_anchor_of(t, G, Tc);
@@ -242,15 +245,18 @@ void cgo_freqs_from_counts(const uint64_t *count, uint32_t N, uint16_t *f)
     f[best] = (uint16_t)(f[best] + (CGO_PROB_TOTAL - sum));
 }
 
+/* Symbol counts per channel row over the tokens the range covers (non-anchor tokens
+ * from n_sink on). */
 void cgo_histograms(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
-                    const uint8_t *bins, const uint8_t *sym, uint64_t *counts /* [L][2][C][32] */)
+                    const uint8_t *bins, const uint8_t *sym, uint64_t *counts /* [L][2][C][32] */,
+                    uint32_t n_sink)
 {
     cgo_shape p = {L, H, d, S, G, Tc, bins};
     uint32_t C = H * d;
     memset(counts, 0, sizeof(uint64_t) * (size_t)L * 2 * C * CGO_MAX_BINS);
     for (uint32_t l = 0; l < L; l++)
         for (uint32_t kv = 0; kv < 2; kv++)
-            for (uint32_t t = 0; t < S; t++) {
+            for (uint32_t t = n_sink; t < S; t++) {
                 if (cgo_is_anchor(t, G, Tc))
                     continue;
                 for (uint32_t c = 0; c < C; c++) {

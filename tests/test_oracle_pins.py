@@ -452,3 +452,40 @@ def test_key_and_value_rows_take_their_own_bin_counts():
     out = O.decode(shp, tab, enc)
     for kv in range(2):
         assert np.array_equal(out[:, kv], O.decode(ref[kv], tabs[kv], encs[kv])[:, kv])
+
+
+@pytest.mark.parametrize("G", [4, 3])
+def test_sink_tokens_are_kept_in_fp16_and_left_out_of_the_tables(G):
+    """Attention sinks ("Guide to CacheGen", Best Practices): the first four tokens come
+    back exactly, and their values reach neither the ranges nor the frequency tables.
+    Planting huge values on the sinks that are not anchors (tokens 1-3 at G = 4, 1-2 at
+    G = 3, where token 3 anchors the next group and so still feeds its deltas) changes no
+    table and no decoded token from 4 on.  Without sinks the plant widens the range; the
+    ranges with sinks are the brute-force min / max of the deltas of tokens >= 4."""
+    L, C, S, Tc, n_sink = 2, 9, 70, 30, 4
+    shp0, X = _small_data(L=L, S=S, C=C, G=G, Tc=Tc, bins=(8, 4))
+    shp = O.Shape.make(L, 1, C, S, G, Tc, (8, 4), n_sink=n_sink)
+    P = X.copy()
+    for t in range(1, n_sink):
+        if t % G:
+            P[:, :, t] = np.float16(30000.0).view(np.uint16)
+    tx, tp = O.build_tables(shp, X), O.build_tables(shp, P)
+    for name in ("lo", "w", "r", "counts", "freqs"):
+        assert np.array_equal(getattr(tx, name), getattr(tp, name)), name
+    assert (O.build_tables(shp0, P).w > tx.w).any()
+    for l in range(L):
+        for kv in range(2):
+            for c in range(C):
+                ds = [d for t, _, d in _deltas(shp, X, l, kv, c) if t >= n_sink]
+                assert tx.lo[l, kv, c] == np.float32(min(ds)) + np.float32(0.0)
+                assert tx.lo[l, kv, c] + tx.w[l, kv, c] * (shp.bins[l * 2 + kv] - 1) >= max(ds) - 1e-3
+    enc = O.encode(shp, P, tp)
+    out = O.decode(shp, tp, enc)
+    assert np.array_equal(out[:, :, :n_sink], P[:, :, :n_sink])
+    assert np.array_equal(tp.sinks, P[:, :, :n_sink])
+    ref = O.decode(shp, tx, O.encode(shp, X, tx))
+    assert np.array_equal(out[:, :, n_sink:], ref[:, :, n_sink:])
+    # a decode of chunk 1 alone writes no sink row
+    part = O.decode(shp, tp, O.encode(shp, P, tp, 1, 2))
+    assert (part[:, :, :Tc] == 0).all()
+    assert O.table_bytes(shp) == O.table_bytes(shp0) + 2 * L * n_sink * C * 2
