@@ -15,7 +15,8 @@ right after each step's encode.  `ms_per_step` is the wall time of a whole step.
 
 An object "paged" decodes the same container into a paged cache (16-token pages, a
 shuffled block table); "kv_asymmetric" covers the same cache with the V rows one step
-coarser than the K rows (decode throughput and ratio).  An object "streamed" covers the streamed
+coarser than the K rows, and "sinks" with the first four tokens kept in fp16 (decode
+throughput and ratio).  An object "streamed" covers the streamed
 decode of the 131K-token cache
 (L=80, S=131072, 42.95 GB): every chunk encoded at three levels, one level per chunk
 chosen from a seeded bandwidth trace, the chosen containers copied from pinned host
@@ -244,15 +245,13 @@ def paged_report(w, tab, blob, out, reps: int) -> dict:
     return res
 
 
-def kv_asymmetric_report(w, X, out, reps: int) -> dict:
-    """Keys finer than values ("Guide to CacheGen", Solution pillar 1): the V rows take one
-    step coarser bin counts than the K rows (K 32 / 16 / 8, V 16 / 8 / 4 by layer tier).
-    Decode throughput over back-to-back decodes of the resident container, and the ratio."""
+def _variant_decode(w, X, out, reps: int, **build_kw):
+    """Tables and container of a format variant of the cache, then back-to-back decodes
+    of the resident container; checks anchors exact and the half-bin bound on layer 0."""
     import torch
 
     from kv_cache_compression_cg_amd import cg
-    bins_v = [max(2, b // 2) for b in w.bins]
-    tab = cg.build_cdf(X, w.group, w.chunk, w.bins, H_kv=w.H_kv, bins_v=bins_v)
+    tab = cg.build_cdf(X, w.group, w.chunk, w.bins, H_kv=w.H_kv, **build_kw)
     blob = cg.encode(tab, X)
     stream = torch.cuda.current_stream(X.device)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -267,18 +266,39 @@ def kv_asymmetric_report(w, X, out, reps: int) -> dict:
     tt = torch.arange(w.S, device=X.device)
     anchor = ((tt % w.chunk) % w.group) == 0
     assert torch.equal(out[:, :, anchor].view(torch.int16), X[:, :, anchor].view(torch.int16))
+    n_sink = build_kw.get("n_sink", 0)
     wv = torch.from_numpy(tab.export()["w"][0]).to(X.device)[:, None, :]
-    err = (X[0].float() - out[0].float()).abs()
-    assert bool((err <= wv / 2 * 1.001 + 2 ** -10 * X[0].float().abs() + 1e-6).all())
+    err = (X[0, :, n_sink:].float() - out[0, :, n_sink:].float()).abs()
+    assert bool((err <= wv / 2 * 1.001 + 2 ** -10 * X[0, :, n_sink:].float().abs() + 1e-6).all())
     comp = cg.compressed_bytes(tab, [blob])
-    res = {"workload": w.name, "bins_k": "32 / 16 / 8 (layers 0-19 / 20-39 / 40-79)",
-           "bins_v": "16 / 8 / 4", "decode_ms": round(dec, 4), "decode_reps": len(ms),
+    res = {"workload": w.name, "decode_ms": round(dec, 4), "decode_reps": len(ms),
            "value_GBps": round(w.raw_bytes / (dec * 1e-3) / 1e9, 2),
            "pct_hbm_peak": round(100 * w.raw_bytes / (dec * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
            "compression_ratio": round(w.raw_bytes / comp, 4), "compressed_bytes": comp}
-    log("[kv-asymmetric] decode %.3f ms (%.1f GB/s), ratio %.3f"
-        % (dec, res["value_GBps"], res["compression_ratio"]))
     del blob, tab
+    return res
+
+
+def kv_asymmetric_report(w, X, out, reps: int) -> dict:
+    """Keys finer than values ("Guide to CacheGen", Solution pillar 1): the V rows take one
+    step coarser bin counts than the K rows (K 32 / 16 / 8, V 16 / 8 / 4 by layer tier).
+    Decode throughput over back-to-back decodes of the resident container, and the ratio."""
+    res = {"bins_k": "32 / 16 / 8 (layers 0-19 / 20-39 / 40-79)", "bins_v": "16 / 8 / 4"}
+    res.update(_variant_decode(w, X, out, reps, bins_v=[max(2, b // 2) for b in w.bins]))
+    log("[kv-asymmetric] decode %.3f ms (%.1f GB/s), ratio %.3f"
+        % (res["decode_ms"], res["value_GBps"], res["compression_ratio"]))
+    return res
+
+
+def sinks_report(w, X, out, reps: int, n_sink: int = 4) -> dict:
+    """Attention sinks ("Guide to CacheGen", Best Practices): the first four tokens kept
+    in fp16 and out of the tables; the decode writes them back exactly (checked)."""
+    import torch
+    res = {"n_sink": n_sink}
+    res.update(_variant_decode(w, X, out, reps, n_sink=n_sink))
+    assert torch.equal(out[:, :, :n_sink].view(torch.int16), X[:, :, :n_sink].view(torch.int16))
+    log("[sinks] decode %.3f ms (%.1f GB/s), ratio %.3f"
+        % (res["decode_ms"], res["value_GBps"], res["compression_ratio"]))
     return res
 
 
@@ -326,7 +346,7 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 4 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--no-kv-asymmetric", action="store_true",
-                    help="skip the paged-output and keys-finer-than-values objects")
+                    help="skip the paged-output, keys-finer-than-values and sink objects")
     ap.add_argument("--decode-reps", type=int, default=20,
                     help="back-to-back decodes after the timed steps that give `value`")
     ap.add_argument("--decode-loop", type=int, default=0, metavar="N",
@@ -463,6 +483,7 @@ def main() -> int:
     if not args.no_kv_asymmetric:
         res["paged"] = paged_report(w, tab, blob, out, args.decode_reps)
         res["kv_asymmetric"] = kv_asymmetric_report(w, X, out, args.decode_reps)
+        res["sinks"] = sinks_report(w, X, out, args.decode_reps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, X, args.cpu_threads)
     if not args.no_streamed:

@@ -62,6 +62,10 @@ typedef struct cg_params {
     uint32_t chunk;          /* tokens per chunk (one stream per (layer, K/V, channel, chunk)) */
     const uint8_t *bins;     /* [L], bins[l] = number of quantization levels of layer l */
     const uint8_t *bins_v;   /* [L] or NULL: levels of the V rows of layer l (NULL: bins[l]) */
+    uint32_t n_sink;         /* first n_sink tokens of the sequence (attention sinks, "Guide to
+                                CacheGen", Best Practices) kept as an fp16 copy in the tables:
+                                left out of ranges and histograms, written back exactly by
+                                every decode; 0 = none; values above S act as S */
 } cg_params;
 
 typedef struct cg_tables cg_tables; /* per-channel ranges and frequency tables (device) */

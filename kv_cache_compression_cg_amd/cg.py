@@ -32,7 +32,8 @@ class CgError(RuntimeError):
 class Params(ctypes.Structure):
     _fields_ = [("L", ctypes.c_uint32), ("H_kv", ctypes.c_uint32), ("d", ctypes.c_uint32),
                 ("S", ctypes.c_uint32), ("group", ctypes.c_uint32), ("chunk", ctypes.c_uint32),
-                ("bins", ctypes.POINTER(ctypes.c_uint8)), ("bins_v", ctypes.POINTER(ctypes.c_uint8))]
+                ("bins", ctypes.POINTER(ctypes.c_uint8)), ("bins_v", ctypes.POINTER(ctypes.c_uint8)),
+                ("n_sink", ctypes.c_uint32)]
 
 
 class ContainerHeader(ctypes.Structure):
@@ -130,8 +131,9 @@ class Tables:
     """Per-(layer, K/V, channel) ranges and frequency tables, owned by libcg."""
 
     def __init__(self, handle: ctypes.c_void_p, L, H_kv, d, S, group, chunk, bins, device,
-                 bins_v=None):
+                 bins_v=None, n_sink=0):
         self.handle = handle
+        self.n_sink = min(int(n_sink), S)
         self.L, self.H_kv, self.d, self.S = L, H_kv, d, S
         self.group, self.chunk = group, chunk
         self.bins = tuple(int(b) for b in bins)             # K rows (and V rows without bins_v)
@@ -244,11 +246,14 @@ class Blob:
 
 
 def build_cdf(kv: torch.Tensor, group: int, chunk: int, bins: Sequence[int],
-              H_kv: Optional[int] = None, bins_v: Optional[Sequence[int]] = None) -> Tables:
+              H_kv: Optional[int] = None, bins_v: Optional[Sequence[int]] = None,
+              n_sink: int = 0) -> Tables:
     """kv: fp16 CUDA [L, 2, S, C].  H_kv only labels the channel split (C = H_kv * d).
     bins: bin count per layer; with bins_v, those of the K rows, and bins_v those of the
-    V rows."""
+    V rows.  n_sink: the first n_sink tokens are kept as an fp16 copy (attention sinks)."""
     _kv_check(kv)
+    if n_sink < 0:
+        raise ValueError("n_sink must be >= 0")
     L, _, S, C = kv.shape
     H = H_kv if H_kv is not None else 1
     if C % H:
@@ -261,12 +266,12 @@ def build_cdf(kv: torch.Tensor, group: int, chunk: int, bins: Sequence[int],
         raise ValueError("need one V bin count per layer")
     u8p = ctypes.POINTER(ctypes.c_uint8)
     p = Params(L, H, C // H, S, group, chunk, b.ctypes.data_as(u8p),
-               bv.ctypes.data_as(u8p) if bv is not None else None)
+               bv.ctypes.data_as(u8p) if bv is not None else None, int(n_sink))
     h = ctypes.c_void_p()
     with torch.cuda.device(kv.device):
         _check(load().cg_build_cdf(ctypes.byref(p), kv.data_ptr(), _stream(kv.device),
                                    ctypes.byref(h)))
-    return Tables(h, L, H, C // H, S, group, chunk, b, kv.device, bins_v=bv)
+    return Tables(h, L, H, C // H, S, group, chunk, b, kv.device, bins_v=bv, n_sink=n_sink)
 
 
 def encode(tables: Tables, kv: torch.Tensor, chunk_begin: int = 0,

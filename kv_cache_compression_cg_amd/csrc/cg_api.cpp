@@ -2,6 +2,7 @@
 // launch sequence of every entry point declared in include/cg.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -99,6 +100,8 @@ struct cg_tables {
     float *d_lo, *d_w, *d_r;
     uint16_t *d_freqs;
     uint32_t *d_dtab;
+    uint32_t n_sink;              // min(params n_sink, S)
+    uint16_t *d_sinks;            // fp16 [L][2][n_sink][C], or null
 };
 
 struct cg_blob {
@@ -122,7 +125,19 @@ Geom make_geom(const cg_tables *t, uint32_t kb, uint32_t ke)
     g.ngF = ceil_div(t->Tc, t->G);
     g.kb = kb;
     g.ke = ke;
+    g.n_sink = t->n_sink;
     return g;
+}
+
+// Writes the sink rows among the tokens of chunks [kb, ke) into a contiguous output or,
+// when pg.pages is set, into pages.
+hipError_t put_sinks(const cg_tables *t, uint32_t kb, uint32_t ke, uint16_t *out, const Paged &pg,
+                     hipStream_t st)
+{
+    if (!t->n_sink) return hipSuccess;
+    const uint64_t a = (uint64_t)kb * t->Tc, b = std::min<uint64_t>((uint64_t)ke * t->Tc, t->n_sink);
+    if (a >= b) return hipSuccess;
+    return launch_sinks(make_geom(t, kb, ke), t->d_sinks, t->n_sink, (uint32_t)a, (uint32_t)b, out, pg, st);
 }
 
 // Tokens per thread for the streaming kernels: about two million threads in flight.
@@ -217,6 +232,8 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     t->C = (uint32_t)C;
     t->NB = ceil_div(t->C, kLanes);
     t->max_bins = max_bins;
+    t->n_sink = std::min(p.n_sink, p.S);
+    t->d_sinks = nullptr;
     t->bins.resize((size_t)2 * p.L);  // per (layer, K/V) row: l * 2 + kv
     for (uint32_t l = 0; l < p.L; ++l) {
         t->bins[2 * l] = p.bins[l];
@@ -247,6 +264,16 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     t->d_r = r_d.as<float>();
     t->d_freqs = fr_d.as<uint16_t>();
     t->d_dtab = dt_d.as<uint32_t>();
+    const uint64_t sink_row = (uint64_t)t->n_sink * t->C * 2;  // bytes per (layer, K/V)
+    if (sink_row) {
+        DevBuf sk_d;
+        CG_HIP(sk_d.alloc(2 * t->L * sink_row), "hipMalloc");
+        t->d_sinks = sk_d.as<uint16_t>();
+        sk_d.detach();
+        CG_HIP(hipMemcpy2DAsync(t->d_sinks, sink_row, kv_dev, (uint64_t)t->S * t->C * 2, sink_row,
+                                2 * t->L, hipMemcpyDeviceToDevice, st),
+               "copy sink rows");
+    }
     bins_d.detach();
     lo_d.detach();
     w_d.detach();
@@ -432,6 +459,7 @@ int cg_decode_paged(const cg_tables *t, const cg_blob *b, const void *container_
     CG_HIP(launch_k3_paged(g, t->d_bins, t->d_dtab, t->d_lo, t->d_w, cont, view_of(b), pg,
                            (hipStream_t)hip_stream),
            "k3_decode (paged)");
+    CG_HIP(put_sinks(t, g.kb, g.ke, nullptr, pg, (hipStream_t)hip_stream), "k_sinks (paged)");
     return CG_OK;
 }
 
@@ -449,6 +477,8 @@ int cg_decode(const cg_tables *t, const cg_blob *b, const void *container_dev, v
     CG_HIP(launch_k3(g, t->d_bins, t->d_dtab, t->d_lo, t->d_w, cont, view_of(b), static_cast<uint16_t *>(kv_out_dev),
                      nullptr, (hipStream_t)hip_stream),
            "k3_decode");
+    CG_HIP(put_sinks(t, g.kb, g.ke, static_cast<uint16_t *>(kv_out_dev), Paged{}, (hipStream_t)hip_stream),
+           "k_sinks");
     return CG_OK;
 }
 
@@ -563,6 +593,11 @@ int cg_stream_decode(const cg_stream_item *items, uint32_t n_items, void *stagin
             what = "k3_decode";
             break;
         }
+        if ((err = put_sinks(it.tables, g.kb, g.ke, static_cast<uint16_t *>(kv_out_dev), Paged{}, dec)) !=
+            hipSuccess) {
+            what = "k_sinks";
+            break;
+        }
         if (ie && (err = hipEventRecord(ie[3], dec)) != hipSuccess) { what = "hipEventRecord"; break; }
         if ((err = hipEventRecord(freed[j], dec)) != hipSuccess) { what = "hipEventRecord"; break; }
         bytes += nb;
@@ -626,6 +661,8 @@ int cg_dequantize(const cg_tables *t, const cg_blob *b, const void *container_de
                      t_lo, t_hi, pick_tpt(t, t_hi - t_lo), static_cast<uint16_t *>(kv_out_dev),
                      (hipStream_t)hip_stream),
            "k4_dequant");
+    CG_HIP(put_sinks(t, g.kb, g.ke, static_cast<uint16_t *>(kv_out_dev), Paged{}, (hipStream_t)hip_stream),
+           "k_sinks");
     return CG_OK;
 }
 
@@ -678,6 +715,7 @@ int cg_tables_get_info(const cg_tables *t, cg_tables_info *info)
     info->chunk = t->Tc;
     uint64_t bytes = (uint64_t)t->L * 2 * t->C * 8 + (uint64_t)2 * t->L;
     for (uint32_t r = 0; r < 2 * t->L; ++r) bytes += (uint64_t)t->C * t->bins[r] * 2;
+    bytes += (uint64_t)2 * t->L * t->n_sink * t->C * 2;
     info->stored_bytes = bytes;
     return CG_OK;
 }
@@ -714,7 +752,7 @@ void cg_free(void *handle)
     if (magic == kTablesMagic) {
         cg_tables *t = static_cast<cg_tables *>(handle);
         t->magic = 0;
-        void *ptrs[] = {t->d_bins, t->d_lo, t->d_w, t->d_r, t->d_freqs, t->d_dtab};
+        void *ptrs[] = {t->d_bins, t->d_lo, t->d_w, t->d_r, t->d_freqs, t->d_dtab, t->d_sinks};
         for (void *p : ptrs)
             if (p) (void)hipFree(p);
         delete t;

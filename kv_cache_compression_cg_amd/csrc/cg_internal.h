@@ -29,6 +29,7 @@ struct Geom {
     uint32_t NB;   // blocks of 64 channels = ceil(C / 64)
     uint32_t ngF;  // groups in a full chunk = ceil(Tc / G)
     uint32_t kb, ke;
+    uint32_t n_sink = 0;  // first tokens of the sequence kept in fp16 (left out of the tables)
 };
 
 // Paged output (vLLM-style block table): pages fp16 [L][2][num_pages][1 << lp][C]; token t
@@ -76,6 +77,10 @@ hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, c
 hipError_t launch_k3_paged(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
                            const float *lo, const float *w, const uint8_t *container,
                            const ContainerView &cv, const Paged &pg, hipStream_t st);
+// Writes the stored fp16 sink rows of tokens [t_a, t_b) into the output: the contiguous
+// [L][2][S][C] out, or the pages of pg when pg.pages is set.
+hipError_t launch_sinks(const Geom &g, const uint16_t *sinks, uint32_t n_sink, uint32_t t_a,
+                        uint32_t t_b, uint16_t *out, const Paged &pg, hipStream_t st);
 hipError_t launch_k4(const Geom &g, const float *lo, const float *w, const uint8_t *sym,
                      const uint8_t *container, const ContainerView &cv, uint32_t t_lo,
                      uint32_t t_hi, uint32_t tpt, uint16_t *out, hipStream_t st);

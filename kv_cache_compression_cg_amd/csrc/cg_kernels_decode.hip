@@ -752,6 +752,45 @@ hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, c
     return hipGetLastError();
 }
 
+// Attention sinks ("Guide to CacheGen", Best Practices): the first n_sink tokens of the
+// sequence are written from their fp16 copy, [L][2][n_sink][C], one thread per 8 channels
+// of one token of one (layer, K/V) row.
+__global__ __launch_bounds__(256) void k_sinks(Geom g, const uint16_t *__restrict__ sinks,
+                                               uint32_t n_sink, uint32_t t_a, uint32_t nt,
+                                               uint16_t *__restrict__ out, Paged pg)
+{
+    const uint32_t O = g.C / 8;
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (uint64_t)g.L * 2 * nt * O) return;
+    const uint32_t o = (uint32_t)(i % O);
+    const uint64_t tmp = i / O;
+    const uint32_t t = t_a + (uint32_t)(tmp % nt);
+    const uint32_t row = (uint32_t)(tmp / nt);
+    const uint4 v = *reinterpret_cast<const uint4 *>(sinks + ((uint64_t)row * n_sink + t) * g.C + o * 8);
+    uint16_t *dst;
+    if (pg.pages) {
+        const uint32_t blk = t >> pg.lp;
+        if (blk >= pg.n_blocks) return;
+        const uint32_t id = (uint32_t)pg.bt[blk];
+        if (id >= pg.num_pages) return;  // negative ids too
+        const uint64_t pool = ((uint64_t)pg.num_pages << pg.lp) * g.C;
+        dst = pg.pages + row * pool + (((uint64_t)id << pg.lp) + (t & ((1u << pg.lp) - 1u))) * g.C;
+    } else {
+        dst = out + ((uint64_t)row * g.S + t) * g.C;
+    }
+    *reinterpret_cast<uint4 *>(dst + o * 8) = v;
+}
+
+hipError_t launch_sinks(const Geom &g, const uint16_t *sinks, uint32_t n_sink, uint32_t t_a,
+                        uint32_t t_b, uint16_t *out, const Paged &pg, hipStream_t st)
+{
+    if (t_b <= t_a) return hipSuccess;
+    const uint64_t n = (uint64_t)g.L * 2 * (t_b - t_a) * (g.C / 8);
+    hipLaunchKernelGGL(k_sinks, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, g, sinks,
+                       n_sink, t_a, t_b - t_a, out, pg);
+    return hipGetLastError();
+}
+
 hipError_t launch_k3_paged(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
                            const float *lo, const float *w, const uint8_t *container,
                            const ContainerView &cv, const Paged &pg, hipStream_t st)

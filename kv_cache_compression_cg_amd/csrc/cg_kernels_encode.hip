@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void k0_minmax(const uint16_t *__restrict__ X,
         if (w.gp == 0) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) af[j] = xf[j];
-        } else {
+        } else if (w.t >= g.n_sink) {  // sink tokens stay out of the range
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 float dl = xf[j] - af[j];
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
             if (w.gp == 0) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) af[j] = xf[j];
-            } else {
+            } else if (w.t >= g.n_sink) {  // and out of the histograms
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     uint32_t q = quantize1(xf[j] - af[j], lo8[j], r8[j], N);

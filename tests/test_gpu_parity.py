@@ -43,18 +43,19 @@ GAUSS = configs.GenSpec(rho=0.9, heavy_tail=False, outlier_frac=0.02, outlier_mu
 HEAVY = configs.GenSpec(rho=0.85, heavy_tail=True, outlier_frac=0.05, outlier_mult=30.0, seed=1)
 
 
-def full_parity(cg, X, H, G, Tc, bins, chunk_range=None, label="", bins_v=None):
+def full_parity(cg, X, H, G, Tc, bins, chunk_range=None, label="", bins_v=None, n_sink=0):
     """Runs both sides on the same cache and compares every product of the path."""
     L, _, S, C = X.shape
     _say("[parity] %s L=%d S=%d C=%d G=%d Tc=%d bins=%s bins_v=%s"
          % (label, L, S, C, G, Tc, list(bins), None if bins_v is None else list(bins_v)))
     Xh = _u16(X)
-    shp = O.Shape.make(L, H, C // H, S, G, Tc, bins, bins_v=bins_v)
+    shp = O.Shape.make(L, H, C // H, S, G, Tc, bins, bins_v=bins_v, n_sink=n_sink)
     tab_o = O.build_tables(shp, Xh)
     kb, ke = chunk_range if chunk_range else (0, shp.n_chunks)
     enc_o = O.encode(shp, Xh, tab_o, kb, ke)
 
-    tab = cg.build_cdf(X, G, Tc, bins, H_kv=H, bins_v=bins_v)
+    tab = cg.build_cdf(X, G, Tc, bins, H_kv=H, bins_v=bins_v, n_sink=n_sink)
+    assert tab.stored_bytes == O.table_bytes(shp)
     ex = tab.export()
     for name in ("lo", "w", "r"):
         assert np.array_equal(ex[name].view(np.uint32), getattr(tab_o, name).view(np.uint32)), name
@@ -281,3 +282,32 @@ def test_paged_output_skips_invalid_page_ids(cg):
     bt12 = torch.zeros(-(-S // 12), dtype=torch.int32, device="cuda")
     with pytest.raises(cg.CgError):        # 12 tokens per page: not a power of two
         cg.decode_paged(tab, blob, pages[:, :, :, :12].contiguous(), bt12)
+
+
+@pytest.mark.parametrize("n_sink,G,Tc,rng", [(4, 10, 300, None), (40, 5, 32, None),
+                                             (40, 5, 32, (1, 5)), (4, 10, 300, (1, 3))])
+def test_attention_sinks(cg, n_sink, G, Tc, rng):
+    """Sink tokens ("Guide to CacheGen", Best Practices) planted with large values: tables,
+    container and decode equal the oracle's (the sinks out of ranges and histograms, and
+    written back exactly); sinks spread over two chunks (Tc = 32), chunk ranges that
+    start after the sinks or among them; a partial lane block (C = 72).  Also through
+    the paged output."""
+    L, S, C, H, bins = 2, 1000, 72, 9, (16, 4)
+    X = _gen(L, S, C, HEAVY)
+    X[:, :, 1:n_sink:3] = 3000.0
+    tab, blob, tab_o, enc_o = full_parity(cg, X, H, G, Tc, bins, chunk_range=rng,
+                                          label="sinks %d" % n_sink, n_sink=n_sink)
+    kb, ke = rng if rng else (0, -(-S // Tc))
+    P = 16
+    nb = -(-S // P)
+    bt = torch.randperm(nb, generator=torch.Generator().manual_seed(n_sink)).to(torch.int32).cuda()
+    pages = torch.full((L, 2, nb, P, C), float("nan"), dtype=torch.float16, device="cuda")
+    cg.decode_paged(tab, blob, pages, bt)
+    torch.cuda.synchronize()
+    shp = O.Shape.make(L, H, C // H, S, G, Tc, bins, n_sink=n_sink)
+    nan16 = _u16(torch.full((1,), float("nan"), dtype=torch.float16))[0]
+    ref = O.decode(shp, tab_o, enc_o, out=np.full((L, 2, S, C), nan16, np.uint16))
+    assert np.array_equal(_u16(_gather_pages(pages, bt, S)), ref)
+    t_end = min(ke * Tc, n_sink)
+    if kb * Tc < t_end:
+        assert np.array_equal(ref[:, :, kb * Tc:t_end], _u16(X)[:, :, kb * Tc:t_end])

@@ -214,3 +214,25 @@ def test_stream_decode_rejects_bad_items(cg):
     cg.stream_decode([(tx, bx, hx)], staging[:2 * slot], 2, got, cs, ds)
     torch.cuda.synchronize()
     assert torch.equal(got[:, :, :200].view(torch.int16), ref[:, :, :200].view(torch.int16))
+
+
+def test_stream_decode_writes_sink_tokens(cg):
+    """Tables with attention sinks: the streamed decode of chunks 0 and 1 (the sinks span
+    both) equals cg_decode's, which the parity tests hold to the oracle."""
+    X = synth.gen_custom(2, 600, 64, HEAVY, device="cuda")
+    X[:, :, 1:12] = 2000.0
+    tab = cg.build_cdf(X, 5, 8, (8, 4), H_kv=1, n_sink=12)
+    blobs = [cg.encode(tab, X, k, k + 1) for k in range(3)]
+    hosts = [torch.from_numpy(b.read().copy()) for b in blobs]
+    slot = (max(b.nbytes for b in blobs) + 255) // 256 * 256
+    staging = torch.empty(2 * slot, dtype=torch.uint8, device="cuda")
+    got = torch.zeros_like(X)
+    cs, ds = torch.cuda.Stream(), torch.cuda.Stream()
+    cg.stream_decode([(tab, b, h) for b, h in zip(blobs, hosts)], staging, 2, got, cs, ds)
+    torch.cuda.synchronize()
+    ref = torch.zeros_like(X)
+    for b in blobs:
+        cg.decode(tab, b, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(got[:, :, :24].view(torch.int16), ref[:, :, :24].view(torch.int16))
+    assert torch.equal(got[:, :, :12].view(torch.int16), X[:, :, :12].view(torch.int16))
