@@ -104,7 +104,8 @@ typedef struct cg_blob_info {
 
 typedef struct cg_tables_info {
     uint32_t L, H_kv, d, S, group, chunk;
-    uint64_t stored_bytes;        /* lo, w (4 B each per row) + 2 B per frequency + bins */
+    uint64_t stored_bytes;        /* lo, w (4 B each per row) + 2 B per frequency + bins
+                                     + the fp16 sink rows (2 B per sink token per channel row) */
 } cg_tables_info;
 
 /*
