@@ -132,7 +132,9 @@ int cg_encode(const cg_tables *tables, const void *kv_dev, uint32_t chunk_begin,
 
 /*
  * Decodes a container into kv_out_dev (fp16 [L][2][S][C]); writes exactly the tokens
- * of chunks [chunk_begin, chunk_end), leaves every other token untouched.
+ * of chunks [chunk_begin, chunk_end), leaves every other token untouched.  Sink tokens
+ * (cg_params.n_sink) among them are written from the tables' fp16 copy, after the
+ * decoded rows, on the same stream.
  *   container_dev: NULL to decode the blob's own copy, or a device buffer holding the
  *                  same container bytes (e.g. staged from pinned host memory).  Its
  *                  payload and offsets are not trusted: damaged bytes decode to wrong
@@ -152,8 +154,9 @@ int cg_decode(const cg_tables *tables, const cg_blob *blob, const void *containe
  *   block_table_dev: int32 [ceil(S / page_tokens)], device: token t of every (layer, K/V)
  *                    goes to page block_table[t / page_tokens], row t % page_tokens.
  *   page_tokens:     a power of two; num_pages * page_tokens * H_kv * d * 2 < 2^32.
- * Writes the tokens of the blob's chunks; a block whose page id is negative or
- * >= num_pages is skipped (none of its rows is written), other pages are untouched.
+ * Writes the tokens of the blob's chunks (sink tokens as in cg_decode); a block whose
+ * page id is negative or >= num_pages is skipped (none of its rows is written), other
+ * pages are untouched.
  * container_dev as in cg_decode.  Fully asynchronous on hip_stream.  Errors:
  * CG_E_INVAL, CG_E_CORRUPT, CG_E_HIP.
  */
@@ -193,8 +196,8 @@ typedef struct cg_stream_stats {
 /*
  * Decodes items[0 .. n_items) in order into kv_out_dev (fp16 [L][2][S][C]).  Item i is
  * copied into staging slot i % n_slots (slot j starts at staging_dev + j * slot_bytes)
- * on copy_stream and decoded from there on decode_stream; a slot is refilled only after
- * the decode that read it has finished.
+ * on copy_stream and decoded from there on decode_stream (sink tokens as in cg_decode);
+ * a slot is refilled only after the decode that read it has finished.
  *   staging_dev:   caller-owned device memory, n_slots * slot_bytes bytes; the address
  *                  and slot_bytes are multiples of 256.
  *   copy_stream, decode_stream: two different streams of the tables' device.
@@ -240,7 +243,8 @@ int cg_decode_symbols(const cg_tables *tables, const cg_blob *blob, const void *
                       void *sym_dev, void *hip_stream);
 
 /* Dequantize + anchor-add alone: symbols [L][2][S][C] and the container's anchors to
- * fp16 [L][2][S][C] for the container's tokens.  Asynchronous. */
+ * fp16 [L][2][S][C] for the container's tokens, sink tokens as in cg_decode.
+ * Asynchronous. */
 int cg_dequantize(const cg_tables *tables, const cg_blob *blob, const void *container_dev,
                   const void *sym_dev, void *kv_out_dev, void *hip_stream);
 
