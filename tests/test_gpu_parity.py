@@ -285,13 +285,15 @@ def test_paged_output_skips_invalid_page_ids(cg):
 
 
 @pytest.mark.parametrize("n_sink,G,Tc,rng", [(4, 10, 300, None), (40, 5, 32, None),
-                                             (40, 5, 32, (1, 5)), (4, 10, 300, (1, 3))])
+                                             (40, 5, 32, (1, 5)), (4, 10, 300, (1, 3)),
+                                             (2000, 10, 300, None)])
 def test_attention_sinks(cg, n_sink, G, Tc, rng):
     """Sink tokens ("Guide to CacheGen", Best Practices) planted with large values: tables,
     container and decode equal the oracle's (the sinks out of ranges and histograms, and
     written back exactly); sinks spread over two chunks (Tc = 32), chunk ranges that
-    start after the sinks or among them; a partial lane block (C = 72).  Also through
-    the paged output."""
+    start after the sinks or among them; a partial lane block (C = 72); n_sink above S
+    (every token a sink: the tables see no token at all).  Also through the paged
+    output."""
     L, S, C, H, bins = 2, 1000, 72, 9, (16, 4)
     X = _gen(L, S, C, HEAVY)
     X[:, :, 1:n_sink:3] = 3000.0
