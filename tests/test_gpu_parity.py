@@ -313,3 +313,11 @@ def test_attention_sinks(cg, n_sink, G, Tc, rng):
     t_end = min(ke * Tc, n_sink)
     if kb * Tc < t_end:
         assert np.array_equal(ref[:, :, kb * Tc:t_end], _u16(X)[:, :, kb * Tc:t_end])
+
+
+def test_extreme_outlier_channel(cg):
+    """One channel scaled by 500 (clamped to the fp16 range) next to regular ones, in a
+    partial lane block: tables, container and decode equal the oracle's."""
+    X = _gen(2, 900, 72, HEAVY)
+    X[..., 37] = (X[..., 37].float() * 500.0).clamp(-65504, 65504).half()
+    full_parity(cg, X, 9, 10, 300, (16, 4), label="outlier x500")

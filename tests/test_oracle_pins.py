@@ -489,3 +489,29 @@ def test_sink_tokens_are_kept_in_fp16_and_left_out_of_the_tables(G):
     part = O.decode(shp, tp, O.encode(shp, P, tp, 1, 2))
     assert (part[:, :, :Tc] == 0).all()
     assert O.table_bytes(shp) == O.table_bytes(shp0) + 2 * L * n_sink * C * 2
+
+
+def test_outlier_channel_leaves_the_other_channels_alone():
+    """Outlier channels ("Guide to CacheGen", Solution pillar 3: kept apart so that they do
+    not distort the distribution of regular channels).  Tables are per (layer, K/V,
+    channel), so scaling one channel by 500 changes that channel's range and frequencies
+    only: every other channel keeps its tables, symbols and decoded values bit for bit,
+    and the outlier channel still meets the half-bin bound."""
+    L, C, S, G, Tc = 1, 70, 90, 5, 40
+    shp, X = _small_data(L=L, S=S, C=C, G=G, Tc=Tc, bins=(8,))
+    Y = X.copy()
+    oc = 37
+    v = Y[:, :, :, oc].view(np.float16).astype(np.float32) * 500.0
+    Y[:, :, :, oc] = np.clip(v, -65504, 65504).astype(np.float16).view(np.uint16)
+    tx, ty = O.build_tables(shp, X), O.build_tables(shp, Y)
+    keep = [c for c in range(C) if c != oc]
+    for name in ("lo", "w", "r", "freqs"):
+        assert np.array_equal(getattr(tx, name)[:, :, keep], getattr(ty, name)[:, :, keep]), name
+    assert ty.w[0, 0, oc] > 100 * tx.w[0, 0, oc]
+    ox = O.decode(shp, tx, O.encode(shp, X, tx))
+    oy = O.decode(shp, ty, O.encode(shp, Y, ty))
+    assert np.array_equal(ox[..., keep], oy[..., keep])
+    y = Y[..., oc].view(np.float16).astype(np.float64)
+    d = oy[..., oc].view(np.float16).astype(np.float64)
+    wv = ty.w[:, :, oc].astype(np.float64)[:, :, None]
+    assert (np.abs(y - d) <= wv / 2 * (1 + 2 ** -20) + np.abs(d) * 2 ** -11 + 1e-30).all()
