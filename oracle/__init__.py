@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.cgo_range.restype = ctypes.c_int
         L.cgo_quantize.argtypes = [_u32] * 6 + [_u8p, _u16p, _f32p, _f32p, _u32, _u32, _u8p]
         L.cgo_histograms.argtypes = [_u32] * 6 + [_u8p, _u8p, _u64p, _u32]
+        L.cgo_anchor_grid.argtypes = [_u32] * 6 + [_u16p, _f32p, _f32p, _f32p]
+        L.cgo_snap_anchors.argtypes = [_u32] * 6 + [_u16p, _f32p, _f32p, _f32p, _u16p]
+        L.cgo_anchor_codes.argtypes = [_u32] * 6 + [_u16p, _f32p, _f32p, _u32, _u32, _u8p]
+        L.cgo_anchors_from_codes.argtypes = [_u32] * 5 + [_u8p, _f32p, _f32p, _u32, _u32, _u16p]
         L.cgo_freqs.argtypes = [_u32, _u32, _u8p, _u64p, _u16p]
         L.cgo_freqs_from_counts.argtypes = [_u64p, _u32, _u16p]
         L.cgo_rans_encode.argtypes = [_u8p, _u32, _u16p, _u32, _u16p, _i32p]
@@ -110,6 +114,7 @@ class Shape:
     Tc: int
     bins: np.ndarray  # uint8 [L][2] flattened: bin count of (layer l, K/V kv) at l * 2 + kv
     n_sink: int = 0   # first tokens of the sequence kept in fp16 (attention sinks)
+    anchor_bits: int = 16  # 16: anchors stored as fp16; 8: as codes on a 256-level grid
 
     @property
     def C(self) -> int:
@@ -124,17 +129,21 @@ class Shape:
 
     @staticmethod
     def make(L, H, d, S, G, Tc, bins: Sequence[int], bins_v: Optional[Sequence[int]] = None,
-             n_sink: int = 0) -> "Shape":
+             n_sink: int = 0, anchor_bits: int = 16) -> "Shape":
         """bins: the bin count of each layer (K and V rows alike), or of its K rows when
         bins_v gives those of the V rows (the keys-finer-than-values variant of the
         Guide's Solution pillar 1).  n_sink: the first n_sink tokens of the sequence are
         reproduced exactly from an fp16 copy and left out of the ranges and histograms
-        (the Guide's Best Practices: protect the attention sinks)."""
+        (the Guide's Best Practices: protect the attention sinks).  anchor_bits = 8 stores
+        each anchor as a code on a 256-level grid of its channel (the Guide's Solution
+        pillar 2: anchors quantized with high precision); the deltas are taken against
+        the anchor's grid value."""
+        assert anchor_bits in (8, 16)
         k = np.asarray(bins, dtype=np.uint8)
         v = k if bins_v is None else np.asarray(bins_v, dtype=np.uint8)
         assert k.shape == (L,) and v.shape == (L,)
         return Shape(L, H, d, S, G, Tc, np.ascontiguousarray(np.stack([k, v], axis=1).reshape(-1)),
-                     int(n_sink))
+                     int(n_sink), int(anchor_bits))
 
 
 # ------------------------------------------------------------------ fp16 conversions
@@ -161,16 +170,41 @@ class Tables:
     counts: np.ndarray  # uint64 [L, 2, C, 32]
     freqs: np.ndarray   # uint16 [L, 2, C, 32]
     sinks: Optional[np.ndarray] = None  # uint16 [L, 2, min(n_sink, S), C]: fp16 copy
+    alo: Optional[np.ndarray] = None    # float32 [L, 2, C]: anchor grid (8-bit anchors)
+    aw: Optional[np.ndarray] = None
+    ar: Optional[np.ndarray] = None
 
 
 class NonFinite(ValueError):
     pass
 
 
+def anchor_grid(shp: Shape, X: np.ndarray):
+    """alo, aw, ar (float32 [L, 2, C]) of the 8-bit anchor grid."""
+    alo = np.empty((shp.L, 2, shp.C), np.float32)
+    aw, ar = np.empty_like(alo), np.empty_like(alo)
+    lib().cgo_anchor_grid(*shp.args(), _p(X, _u16p), _p(alo, _f32p), _p(aw, _f32p), _p(ar, _f32p))
+    return alo, aw, ar
+
+
+def snap_anchors(shp: Shape, X: np.ndarray, tab: "Tables") -> np.ndarray:
+    """X with its anchor tokens replaced by their 8-bit grid values (X itself for fp16
+    anchors): the cache the encoder codes the deltas of."""
+    if shp.anchor_bits == 16:
+        return X
+    Y = np.empty_like(X)
+    lib().cgo_snap_anchors(*shp.args(), _p(X, _u16p), _p(tab.alo, _f32p), _p(tab.aw, _f32p),
+                           _p(tab.ar, _f32p), _p(Y, _u16p))
+    return Y
+
+
 def build_tables(shp: Shape, X: np.ndarray) -> Tables:
     """X: uint16 view of fp16 [L, 2, S, C].  Range, quantize, histogram, frequencies."""
     X = np.ascontiguousarray(X, dtype=np.uint16)
     assert X.shape == (shp.L, 2, shp.S, shp.C)
+    grid = anchor_grid(shp, X) if shp.anchor_bits == 8 else (None, None, None)
+    X0 = X
+    X = snap_anchors(shp, X, Tables(None, None, None, None, None, None, *grid))
     lo = np.empty((shp.L, 2, shp.C), np.float32)
     w = np.empty_like(lo)
     r = np.empty_like(lo)
@@ -184,8 +218,8 @@ def build_tables(shp: Shape, X: np.ndarray) -> Tables:
                          shp.n_sink)
     freqs = np.empty((shp.L, 2, shp.C, MAX_BINS), np.uint16)
     lib().cgo_freqs(shp.L, shp.C, _p(shp.bins, _u8p), _p(counts, _u64p), _p(freqs, _u16p))
-    sinks = X[:, :, :min(shp.n_sink, shp.S)].copy()
-    return Tables(lo, w, r, counts, freqs, sinks)
+    sinks = X0[:, :, :min(shp.n_sink, shp.S)].copy()
+    return Tables(lo, w, r, counts, freqs, sinks, *grid)
 
 
 def freqs_from_counts(counts: Sequence[int], N: int) -> np.ndarray:
@@ -241,7 +275,7 @@ class Encoded:
     k_end: int
     offsets: np.ndarray  # uint64 [n_groups + 1] (word offsets)
     payload: np.ndarray  # uint16 [offsets[-1]]
-    anchors: np.ndarray  # uint16 (fp16 bits) [rows, C]
+    anchors: np.ndarray  # uint16 (fp16 bits) [rows, C], or uint8 codes with 8-bit anchors
 
     @property
     def payload_bytes(self) -> int:
@@ -261,7 +295,7 @@ def encode(shp: Shape, X: np.ndarray, tab: Tables, k_begin: int = 0,
     k_end = shp.n_chunks if k_end is None else k_end
     X = np.ascontiguousarray(X, dtype=np.uint16)
     t0, t1 = k_begin * shp.Tc, min(k_end * shp.Tc, shp.S)
-    sym = quantize(shp, X, tab.lo, tab.r, t0, t1)
+    sym = quantize(shp, snap_anchors(shp, X, tab), tab.lo, tab.r, t0, t1)
     ng = n_groups(shp, k_begin, k_end)
     offsets = np.zeros(ng + 1, np.uint64)
     cap = 0
@@ -274,9 +308,27 @@ def encode(shp: Shape, X: np.ndarray, tab: Tables, k_begin: int = 0,
                                  _p(offsets, _u64p), _p(payload, _u16p), cap)
     assert n >= 0
     rows = anchor_rows(shp, k_begin, k_end)
-    anchors = np.zeros((max(rows, 1), shp.C), np.uint16)
-    lib().cgo_anchors(*shp.args(), _p(X, _u16p), k_begin, k_end, _p(anchors, _u16p))
+    if shp.anchor_bits == 8:
+        anchors = np.zeros((max(rows, 1), shp.C), np.uint8)
+        lib().cgo_anchor_codes(*shp.args(), _p(X, _u16p), _p(tab.alo, _f32p), _p(tab.ar, _f32p),
+                               k_begin, k_end, _p(anchors, _u8p))
+    else:
+        anchors = np.zeros((max(rows, 1), shp.C), np.uint16)
+        lib().cgo_anchors(*shp.args(), _p(X, _u16p), k_begin, k_end, _p(anchors, _u16p))
     return Encoded(k_begin, k_end, offsets, payload[:n].copy(), anchors[:rows].copy())
+
+
+def anchor_values(shp: Shape, tab: Tables, enc: "Encoded") -> np.ndarray:
+    """The fp16 anchor rows a container stands for (its codes mapped back for 8-bit
+    anchors)."""
+    if shp.anchor_bits == 16:
+        return enc.anchors
+    out = np.zeros(enc.anchors.shape, np.uint16)
+    codes = np.ascontiguousarray(enc.anchors)
+    lib().cgo_anchors_from_codes(shp.L, shp.C, shp.S, shp.G, shp.Tc, _p(codes, _u8p),
+                                 _p(tab.alo, _f32p), _p(tab.aw, _f32p), enc.k_begin, enc.k_end,
+                                 _p(out, _u16p))
+    return out
 
 
 def decode(shp: Shape, tab: Tables, enc: Encoded, out: Optional[np.ndarray] = None,
@@ -286,7 +338,8 @@ def decode(shp: Shape, tab: Tables, enc: Encoded, out: Optional[np.ndarray] = No
         out = np.zeros((shp.L, 2, shp.S, shp.C), np.uint16)
     payload = enc.payload if payload is None else payload
     pl = np.ascontiguousarray(np.concatenate([payload.astype(np.uint16), np.zeros(1, np.uint16)]))
-    anchors = np.ascontiguousarray(enc.anchors if enc.anchors.size else np.zeros((1, shp.C), np.uint16))
+    av = anchor_values(shp, tab, enc)
+    anchors = np.ascontiguousarray(av if av.size else np.zeros((1, shp.C), np.uint16))
     rc = lib().cgo_decode(*shp.args(), _p(shp.bins, _u8p),
                           _p(np.ascontiguousarray(tab.lo), _f32p),
                           _p(np.ascontiguousarray(tab.w), _f32p),
@@ -308,10 +361,11 @@ def _put_sinks(shp: Shape, tab: Tables, out: np.ndarray, t_begin: int, t_end: in
 def dequantize(shp: Shape, tab: Tables, sym: np.ndarray, X_anchor_src: np.ndarray,
                t_begin: int, t_end: int) -> np.ndarray:
     out = np.zeros((shp.L, 2, shp.S, shp.C), np.uint16)
+    src = snap_anchors(shp, np.ascontiguousarray(X_anchor_src, np.uint16), tab)
     lib().cgo_dequantize(*shp.args(), _p(np.ascontiguousarray(tab.lo), _f32p),
                          _p(np.ascontiguousarray(tab.w), _f32p),
                          _p(np.ascontiguousarray(sym, np.uint8), _u8p),
-                         _p(np.ascontiguousarray(X_anchor_src, np.uint16), _u16p),
+                         _p(src, _u16p),
                          t_begin, t_end, _p(out, _u16p))
     _put_sinks(shp, tab, out, t_begin, t_end)
     return out
@@ -319,7 +373,8 @@ def dequantize(shp: Shape, tab: Tables, sym: np.ndarray, X_anchor_src: np.ndarra
 
 def table_bytes(shp: Shape) -> int:
     """Stored side information: lo and w (4 B each) per channel row, one 2-byte frequency
-    per symbol per channel row, one byte per (layer, K/V) for the bin count, and the fp16
-    copy of the sink tokens."""
+    per symbol per channel row, one byte per (layer, K/V) for the bin count, the fp16
+    copy of the sink tokens, and alo and aw (4 B each) per channel row with 8-bit anchors."""
     return int(2 * shp.C * shp.L * 8 + sum(int(b) * shp.C * 2 for b in shp.bins) + 2 * shp.L
-               + 2 * shp.L * min(shp.n_sink, shp.S) * shp.C * 2)
+               + 2 * shp.L * min(shp.n_sink, shp.S) * shp.C * 2
+               + (2 * shp.C * shp.L * 8 if shp.anchor_bits == 8 else 0))

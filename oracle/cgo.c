@@ -401,6 +401,115 @@ uint64_t cgo_anchor_rows(uint32_t L, uint32_t S, uint32_t G, uint32_t Tc, uint32
     return rows;
 }
 
+/* ------------------------------------------------------------------------------ */
+/* 8-bit anchors (optional): the anchor token is "quantized and stored with high    */
+/* precision" ("Guide to CacheGen", Solution pillar 2), read here as 256 levels on  */
+/* a min-offset grid per (layer, K/V, channel) over its anchor tokens (all chunks), */
+/* the same grid form as the deltas':                                              */
+/*   alo, ahi = min / max of f32(x) over the anchor tokens (+0 for a zero bound);   */
+/*   aw = (ahi - alo) / 255; ar = 1 / aw, or 0 when aw == 0;                        */
+/*   code = clamp(floor(fma(x - alo, ar, 0.5)), 0, 255);                            */
+/*   anchor value = fp16_rne(fma(code, aw, alo)).                                   */
+/* The deltas are then taken against the anchor value, so the encoder and decoder   */
+/* agree on it and the delta grid's bound is unchanged.                             */
+/* ------------------------------------------------------------------------------ */
+void cgo_anchor_grid(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
+                     const uint16_t *X, float *alo, float *aw, float *ar)
+{
+    cgo_shape p = {L, H, d, S, G, Tc, NULL};
+    uint32_t C = H * d;
+    for (uint32_t l = 0; l < L; l++)
+        for (uint32_t kv = 0; kv < 2; kv++)
+            for (uint32_t c = 0; c < C; c++) {
+                float lo = 0.0f, hi = 0.0f;
+                int any = 0;
+                for (uint32_t t = 0; t < S; t++) {
+                    if (!cgo_is_anchor(t, G, Tc))
+                        continue;
+                    float x = cgo_half_to_float(X[kv_index(&p, l, kv, t, c)]);
+                    if (!any || x < lo) lo = x;
+                    if (!any || x > hi) hi = x;
+                    any = 1;
+                }
+                lo = lo + 0.0f;
+                hi = hi + 0.0f;
+                size_t row = ((size_t)l * 2 + kv) * C + c;
+                float w = (hi - lo) / 255.0f;
+                alo[row] = lo;
+                aw[row] = w;
+                ar[row] = (w > 0.0f) ? 1.0f / w : 0.0f;
+            }
+}
+
+static uint8_t anchor_code(uint16_t x, float alo, float ar)
+{
+    return quantize_one(cgo_half_to_float(x), alo, ar, 256u);
+}
+
+static uint16_t anchor_value(uint8_t code, float alo, float aw)
+{
+    return cgo_float_to_half(fmaf((float)code, aw, alo));
+}
+
+/* X_out = X with every anchor token replaced by its anchor value. */
+void cgo_snap_anchors(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
+                      const uint16_t *X, const float *alo, const float *aw, const float *ar,
+                      uint16_t *X_out)
+{
+    cgo_shape p = {L, H, d, S, G, Tc, NULL};
+    uint32_t C = H * d;
+    memcpy(X_out, X, sizeof(uint16_t) * (size_t)L * 2 * S * C);
+    for (uint32_t l = 0; l < L; l++)
+        for (uint32_t kv = 0; kv < 2; kv++)
+            for (uint32_t t = 0; t < S; t++) {
+                if (!cgo_is_anchor(t, G, Tc))
+                    continue;
+                for (uint32_t c = 0; c < C; c++) {
+                    size_t row = ((size_t)l * 2 + kv) * C + c, i = kv_index(&p, l, kv, t, c);
+                    X_out[i] = anchor_value(anchor_code(X[i], alo[row], ar[row]), alo[row], aw[row]);
+                }
+            }
+}
+
+/* Anchor codes of chunks [k_begin, k_end) in the anchors section's row order. */
+void cgo_anchor_codes(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
+                      const uint16_t *X, const float *alo, const float *ar, uint32_t k_begin,
+                      uint32_t k_end, uint8_t *codes_out)
+{
+    cgo_shape p = {L, H, d, S, G, Tc, NULL};
+    uint32_t C = H * d;
+    size_t r = 0;
+    for (uint32_t k = k_begin; k < k_end; k++) {
+        uint32_t ng = cgo_groups_in(cgo_chunk_len(S, Tc, k), G);
+        for (uint32_t l = 0; l < L; l++)
+            for (uint32_t kv = 0; kv < 2; kv++)
+                for (uint32_t g = 0; g < ng; g++, r++)
+                    for (uint32_t c = 0; c < C; c++) {
+                        size_t row = ((size_t)l * 2 + kv) * C + c;
+                        codes_out[r * C + c] =
+                            anchor_code(X[kv_index(&p, l, kv, k * Tc + g * G, c)], alo[row], ar[row]);
+                    }
+    }
+}
+
+/* The fp16 anchor values of an anchors section of codes (same row order). */
+void cgo_anchors_from_codes(uint32_t L, uint32_t C, uint32_t S, uint32_t G, uint32_t Tc,
+                            const uint8_t *codes, const float *alo, const float *aw,
+                            uint32_t k_begin, uint32_t k_end, uint16_t *anchors_out)
+{
+    size_t r = 0;
+    for (uint32_t k = k_begin; k < k_end; k++) {
+        uint32_t ng = cgo_groups_in(cgo_chunk_len(S, Tc, k), G);
+        for (uint32_t l = 0; l < L; l++)
+            for (uint32_t kv = 0; kv < 2; kv++)
+                for (uint32_t g = 0; g < ng; g++, r++)
+                    for (uint32_t c = 0; c < C; c++) {
+                        size_t row = ((size_t)l * 2 + kv) * C + c;
+                        anchors_out[r * C + c] = anchor_value(codes[r * C + c], alo[row], aw[row]);
+                    }
+    }
+}
+
 /* Copies anchors into anchors_out ([rows][C] fp16). */
 void cgo_anchors(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
                  const uint16_t *X, uint32_t k_begin, uint32_t k_end, uint16_t *anchors_out)

@@ -515,3 +515,57 @@ def test_outlier_channel_leaves_the_other_channels_alone():
     d = oy[..., oc].view(np.float16).astype(np.float64)
     wv = ty.w[:, :, oc].astype(np.float64)[:, :, None]
     assert (np.abs(y - d) <= wv / 2 * (1 + 2 ** -20) + np.abs(d) * 2 ** -11 + 1e-30).all()
+
+
+@pytest.mark.parametrize("G,Tc", [(5, 40), (10, 90)])
+def test_8bit_anchors(G, Tc):
+    """Anchors quantized to 8 bits ("Guide to CacheGen", Solution pillar 2): the grid of
+    a channel spans its anchor tokens (brute-force min / max, width / 255); each code is
+    the nearest grid point (checked against all 256); decoded anchors are the grid values,
+    within half a grid step of the input; every other token still meets the delta grid's
+    half-bin bound, since its delta is taken against the decoded anchor.  The container's
+    payload equals an fp16-anchor encode of the cache whose anchors hold their grid
+    values, and its anchors section is half the size."""
+    L, C, S = 2, 70, 200
+    shp16, X = _small_data(L=L, S=S, C=C, G=G, Tc=Tc, bins=(16, 4))
+    shp = O.Shape.make(L, 1, C, S, G, Tc, (16, 4), anchor_bits=8)
+    tab = O.build_tables(shp, X)
+    xf = X.view(np.float16).astype(np.float64)
+    anc = [t for t in range(S) if (t % Tc) % G == 0]
+    amin, amax = xf[:, :, anc].min(axis=2), xf[:, :, anc].max(axis=2)
+    assert np.array_equal(tab.alo, (amin.astype(np.float32) + np.float32(0)))
+    assert np.array_equal(tab.aw, ((amax - amin).astype(np.float32) / np.float32(255)).astype(np.float32))
+    enc = O.encode(shp, X, tab)
+    assert enc.anchors.dtype == np.uint8
+    # codes against brute force, anchor rows in container order (chunk, l, kv, group)
+    r = 0
+    grid = tab.alo.astype(np.float64)[..., None] + np.arange(256) * tab.aw.astype(np.float64)[..., None]
+    for k in range(shp.n_chunks):
+        for l in range(L):
+            for kv in range(2):
+                for t in range(k * Tc, min((k + 1) * Tc, S), G):
+                    dist = np.abs(xf[l, kv, t][:, None] - grid[l, kv])
+                    code = enc.anchors[r].astype(np.int64)
+                    best = dist.min(axis=1)
+                    got = dist[np.arange(C), code]
+                    assert (got <= best + 1e-6 * (1 + np.abs(xf[l, kv, t]))).all(), (k, l, kv, t)
+                    r += 1
+    assert r == enc.anchors.shape[0]
+    out = O.decode(shp, tab, enc)
+    of = out.view(np.float16).astype(np.float64)
+    aw = tab.aw.astype(np.float64)[:, :, None, :]
+    ea = np.abs(of[:, :, anc] - xf[:, :, anc])
+    assert (ea <= aw / 2 * (1 + 2 ** -20) + np.abs(of[:, :, anc]) * 2 ** -11 + 1e-30).all()
+    non = [t for t in range(S) if (t % Tc) % G]
+    wv = tab.w.astype(np.float64)[:, :, None, :]
+    en = np.abs(of[:, :, non] - xf[:, :, non])
+    assert (en <= wv / 2 * (1 + 2 ** -20) + np.abs(of[:, :, non]) * 2 ** -11 + 1e-30).all()
+    Xs = O.snap_anchors(shp, X, tab)
+    t16 = O.build_tables(shp16, Xs)
+    for name in ("lo", "w", "r", "freqs"):
+        assert np.array_equal(getattr(t16, name), getattr(tab, name)), name
+    e16 = O.encode(shp16, Xs, t16)
+    assert np.array_equal(e16.payload, enc.payload) and np.array_equal(e16.offsets, enc.offsets)
+    assert np.array_equal(O.decode(shp16, t16, e16), out)
+    assert enc.anchors.nbytes * 2 == e16.anchors.nbytes
+    assert O.table_bytes(shp) == O.table_bytes(shp16) + 2 * L * C * 8
