@@ -66,6 +66,12 @@ typedef struct cg_params {
                                 CacheGen", Best Practices) kept as an fp16 copy in the tables:
                                 left out of ranges and histograms, written back exactly by
                                 every decode; 0 = none; values above S act as S */
+    uint32_t anchor_bits;    /* 0 or 16: anchors stored as fp16.  8: each anchor stored as a
+                                code on a 256-level grid of its (layer, K/V, channel) row
+                                ("Guide to CacheGen", Solution pillar 2: anchors quantized
+                                with high precision), min to max of the row's anchor tokens;
+                                the decoded anchor is the fp16 grid value and the deltas are
+                                taken against it */
 } cg_params;
 
 typedef struct cg_tables cg_tables; /* per-channel ranges and frequency tables (device) */
@@ -77,7 +83,8 @@ typedef struct cg_blob cg_blob;     /* one encoded container (device) */
  *   offsets    uint64[n_groups + 1]: first payload word of every group, then the total.
  *              Groups are (chunk, layer, K/V, block) in row-major order over chunks
  *              [chunk_begin, chunk_end); block b holds channels 64b .. 64b+63.
- *   anchors    fp16, for each chunk: [L][2][ceil(len_k / group)][C]
+ *   anchors    fp16 (uint8 grid codes with 8-bit anchors), for each chunk:
+ *              [L][2][ceil(len_k / group)][C]
  *   payload    uint16 words.  A group's words are the words of its (up to) 64 rANS
  *              streams in the order 64 decoders running in lockstep read them: the two
  *              state words of every lane in lane order, then after each symbol step the
@@ -89,7 +96,8 @@ typedef struct cg_container_header {
     uint32_t magic, version;
     uint32_t L, H_kv, d, S, group, chunk;
     uint32_t chunk_begin, chunk_end;
-    uint32_t n_blocks, reserved;
+    uint32_t n_blocks;
+    uint32_t reserved;        /* bits per stored anchor element: 0 = fp16, 8 = grid codes */
     uint64_t n_groups;
     uint64_t offsets_offset;  /* byte offset of the offsets section */
     uint64_t anchors_offset, anchors_bytes;

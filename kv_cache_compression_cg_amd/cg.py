@@ -33,7 +33,7 @@ class Params(ctypes.Structure):
     _fields_ = [("L", ctypes.c_uint32), ("H_kv", ctypes.c_uint32), ("d", ctypes.c_uint32),
                 ("S", ctypes.c_uint32), ("group", ctypes.c_uint32), ("chunk", ctypes.c_uint32),
                 ("bins", ctypes.POINTER(ctypes.c_uint8)), ("bins_v", ctypes.POINTER(ctypes.c_uint8)),
-                ("n_sink", ctypes.c_uint32)]
+                ("n_sink", ctypes.c_uint32), ("anchor_bits", ctypes.c_uint32)]
 
 
 class ContainerHeader(ctypes.Structure):
@@ -131,9 +131,10 @@ class Tables:
     """Per-(layer, K/V, channel) ranges and frequency tables, owned by libcg."""
 
     def __init__(self, handle: ctypes.c_void_p, L, H_kv, d, S, group, chunk, bins, device,
-                 bins_v=None, n_sink=0):
+                 bins_v=None, n_sink=0, anchor_bits=16):
         self.handle = handle
         self.n_sink = min(int(n_sink), S)
+        self.anchor_bits = int(anchor_bits)
         self.L, self.H_kv, self.d, self.S = L, H_kv, d, S
         self.group, self.chunk = group, chunk
         self.bins = tuple(int(b) for b in bins)             # K rows (and V rows without bins_v)
@@ -225,9 +226,10 @@ class Blob:
         return self.read(h["offsets_offset"], (h["n_groups"] + 1) * 8).view(np.uint64)
 
     def anchors(self) -> np.ndarray:
+        """fp16 bits [rows, C], or uint8 grid codes [rows, C] with 8-bit anchors."""
         h = self.header
-        return self.read(h["anchors_offset"], h["anchors_bytes"]).view(np.uint16) \
-            .reshape(-1, self.tables.C)
+        raw = self.read(h["anchors_offset"], h["anchors_bytes"])
+        return (raw if h["reserved"] == 8 else raw.view(np.uint16)).reshape(-1, self.tables.C)
 
     def payload(self) -> np.ndarray:
         h = self.header
@@ -247,13 +249,16 @@ class Blob:
 
 def build_cdf(kv: torch.Tensor, group: int, chunk: int, bins: Sequence[int],
               H_kv: Optional[int] = None, bins_v: Optional[Sequence[int]] = None,
-              n_sink: int = 0) -> Tables:
+              n_sink: int = 0, anchor_bits: int = 16) -> Tables:
     """kv: fp16 CUDA [L, 2, S, C].  H_kv only labels the channel split (C = H_kv * d).
     bins: bin count per layer; with bins_v, those of the K rows, and bins_v those of the
-    V rows.  n_sink: the first n_sink tokens are kept as an fp16 copy (attention sinks)."""
+    V rows.  n_sink: the first n_sink tokens are kept as an fp16 copy (attention sinks).
+    anchor_bits: 16 (fp16 anchors) or 8 (anchors as codes on a per-channel grid)."""
     _kv_check(kv)
     if n_sink < 0:
         raise ValueError("n_sink must be >= 0")
+    if anchor_bits not in (8, 16):
+        raise ValueError("anchor_bits must be 8 or 16")
     L, _, S, C = kv.shape
     H = H_kv if H_kv is not None else 1
     if C % H:
@@ -266,12 +271,14 @@ def build_cdf(kv: torch.Tensor, group: int, chunk: int, bins: Sequence[int],
         raise ValueError("need one V bin count per layer")
     u8p = ctypes.POINTER(ctypes.c_uint8)
     p = Params(L, H, C // H, S, group, chunk, b.ctypes.data_as(u8p),
-               bv.ctypes.data_as(u8p) if bv is not None else None, int(n_sink))
+               bv.ctypes.data_as(u8p) if bv is not None else None, int(n_sink),
+               int(anchor_bits))
     h = ctypes.c_void_p()
     with torch.cuda.device(kv.device):
         _check(load().cg_build_cdf(ctypes.byref(p), kv.data_ptr(), _stream(kv.device),
                                    ctypes.byref(h)))
-    return Tables(h, L, H, C // H, S, group, chunk, b, kv.device, bins_v=bv, n_sink=n_sink)
+    return Tables(h, L, H, C // H, S, group, chunk, b, kv.device, bins_v=bv, n_sink=n_sink,
+                  anchor_bits=anchor_bits)
 
 
 def encode(tables: Tables, kv: torch.Tensor, chunk_begin: int = 0,

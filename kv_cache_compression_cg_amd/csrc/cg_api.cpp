@@ -102,6 +102,7 @@ struct cg_tables {
     uint32_t *d_dtab;
     uint32_t n_sink;              // min(params n_sink, S)
     uint16_t *d_sinks;            // fp16 [L][2][n_sink][C], or null
+    float *d_alo, *d_aw, *d_ar;   // 8-bit anchor grid [L][2][C], or null (fp16 anchors)
 };
 
 struct cg_blob {
@@ -126,6 +127,9 @@ Geom make_geom(const cg_tables *t, uint32_t kb, uint32_t ke)
     g.kb = kb;
     g.ke = ke;
     g.n_sink = t->n_sink;
+    g.alo = t->d_alo;
+    g.aw = t->d_aw;
+    g.ar = t->d_ar;
     return g;
 }
 
@@ -161,7 +165,7 @@ int check_blob(const cg_tables *t, const cg_blob *b)
     if (!b || b->magic != kBlobMagic) return fail(CG_E_INVAL, "invalid cg_blob handle");
     const cg_container_header &h = b->hdr;
     if (h.L != t->L || h.H_kv != t->H || h.d != t->d || h.S != t->S || h.group != t->G ||
-        h.chunk != t->Tc)
+        h.chunk != t->Tc || h.reserved != (t->d_alo ? 8u : 0u))
         return fail(CG_E_CORRUPT, "container and tables describe different caches");
     return CG_OK;
 }
@@ -203,6 +207,8 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     if (!p.L || !p.H_kv || !p.d || !p.S || !p.group || !p.chunk)
         return fail(CG_E_INVAL, "zero dimension");
     if (p.chunk > CG_MAX_CHUNK) return fail(CG_E_INVAL, "chunk > 16384");
+    if (p.anchor_bits != 0 && p.anchor_bits != 8 && p.anchor_bits != 16)
+        return fail(CG_E_INVAL, "anchor_bits must be 0, 8 or 16");
     uint64_t C = (uint64_t)p.H_kv * p.d;
     if (C % 8 != 0) return fail(CG_E_INVAL, "H_kv * d must be a multiple of 8");
     // 32-bit offsets inside one (layer, K/V) row of symbols and inside one chunk's rows
@@ -234,6 +240,7 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     t->max_bins = max_bins;
     t->n_sink = std::min(p.n_sink, p.S);
     t->d_sinks = nullptr;
+    t->d_alo = t->d_aw = t->d_ar = nullptr;
     t->bins.resize((size_t)2 * p.L);  // per (layer, K/V) row: l * 2 + kv
     for (uint32_t l = 0; l < p.L; ++l) {
         t->bins[2 * l] = p.bins[l];
@@ -264,6 +271,18 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     t->d_r = r_d.as<float>();
     t->d_freqs = fr_d.as<uint16_t>();
     t->d_dtab = dt_d.as<uint32_t>();
+    if (p.anchor_bits == 8) {
+        DevBuf alo_d, aw_d, ar_d;
+        CG_HIP(alo_d.alloc(rows * 4), "hipMalloc");
+        CG_HIP(aw_d.alloc(rows * 4), "hipMalloc");
+        CG_HIP(ar_d.alloc(rows * 4), "hipMalloc");
+        t->d_alo = alo_d.as<float>();
+        t->d_aw = aw_d.as<float>();
+        t->d_ar = ar_d.as<float>();
+        alo_d.detach();
+        aw_d.detach();
+        ar_d.detach();
+    }
     const uint64_t sink_row = (uint64_t)t->n_sink * t->C * 2;  // bytes per (layer, K/V)
     if (sink_row) {
         DevBuf sk_d;
@@ -296,6 +315,10 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     CG_HIP(hipMemsetAsync(t->d_dtab, 0, dtab_bytes, st), "memset");
 
     Geom g = make_geom(t, 0, ceil_div(t->S, t->Tc));
+    if (t->d_alo)
+        CG_HIP(launch_anchor_grid(static_cast<const uint16_t *>(kv_dev), g, t->d_alo, t->d_aw,
+                                  t->d_ar, st),
+               "k_anchor_grid");
     CG_HIP(launch_k0(static_cast<const uint16_t *>(kv_dev), g, pick_tpt(t, t->S),
                      ordlo.as<uint32_t>(), ordhi.as<uint32_t>(), flag.as<uint32_t>(), st),
            "k0_minmax");
@@ -377,7 +400,8 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     h.n_groups = n_groups;
     h.offsets_offset = align256(sizeof(cg_container_header));
     h.anchors_offset = align256(h.offsets_offset + (n_groups + 1) * 8);
-    h.anchors_bytes = arows * t->C * 2;
+    h.anchors_bytes = arows * t->C * (t->d_alo ? 1 : 2);
+    h.reserved = t->d_alo ? 8u : 0u;  // bits per stored anchor element (0: fp16)
     h.payload_offset = align256(h.anchors_offset + h.anchors_bytes);
     h.payload_words = total_words;
     h.total_bytes = h.payload_offset + total_words * 2 + kPayloadPadBytes;
@@ -716,6 +740,7 @@ int cg_tables_get_info(const cg_tables *t, cg_tables_info *info)
     uint64_t bytes = (uint64_t)t->L * 2 * t->C * 8 + (uint64_t)2 * t->L;
     for (uint32_t r = 0; r < 2 * t->L; ++r) bytes += (uint64_t)t->C * t->bins[r] * 2;
     bytes += (uint64_t)2 * t->L * t->n_sink * t->C * 2;
+    if (t->d_alo) bytes += (uint64_t)t->L * 2 * t->C * 8;
     info->stored_bytes = bytes;
     return CG_OK;
 }
@@ -752,7 +777,8 @@ void cg_free(void *handle)
     if (magic == kTablesMagic) {
         cg_tables *t = static_cast<cg_tables *>(handle);
         t->magic = 0;
-        void *ptrs[] = {t->d_bins, t->d_lo, t->d_w, t->d_r, t->d_freqs, t->d_dtab, t->d_sinks};
+        void *ptrs[] = {t->d_bins, t->d_lo, t->d_w, t->d_r, t->d_freqs, t->d_dtab, t->d_sinks,
+                        t->d_alo, t->d_aw, t->d_ar};
         for (void *p : ptrs)
             if (p) (void)hipFree(p);
         delete t;

@@ -74,6 +74,32 @@ __device__ __forceinline__ uint32_t quantize1(float delta, float lo, float r, ui
     return (uint32_t)v;
 }
 
+// fp16_rne of fp32 fma(a, b, c), the fma rounded to fp32 first.  (The empty asm keeps
+// the compiler from fusing the fma and the conversion into one mixed-precision fma,
+// which rounds once and differs from the two roundings in rare cases.)
+__device__ __forceinline__ uint32_t f2h_fma(float a, float b, float c)
+{
+    float v = fmaf(a, b, c);
+    asm volatile("" : "+v"(v));
+    return f2h(v);
+}
+
+// 8-bit anchors: the anchor value of x on its row's grid, fp16_rne(fma(code, aw, alo))
+// with code = quantize1(x, alo, ar, 256), as a float.
+__device__ __forceinline__ float anchor_snap(float x, float alo, float aw, float ar)
+{
+    return h2f(f2h_fma((float)quantize1(x, alo, ar, 256u), aw, alo));
+}
+
+// Applies anchor_snap to the 8 channels of an anchor read by an encoder thread whose
+// channels start at row element r0 (no-op for fp16 anchors).
+__device__ __forceinline__ void snap8(const Geom &g, uint64_t r0, float af[8])
+{
+    if (!g.alo) return;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) af[j] = anchor_snap(af[j], g.alo[r0 + j], g.aw[r0 + j], g.ar[r0 + j]);
+}
+
 __device__ __forceinline__ uint32_t chunk_len(const Geom &g, uint32_t k)
 {
     uint32_t t0 = k * g.Tc;

@@ -30,6 +30,9 @@ struct Geom {
     uint32_t ngF;  // groups in a full chunk = ceil(Tc / G)
     uint32_t kb, ke;
     uint32_t n_sink = 0;  // first tokens of the sequence kept in fp16 (left out of the tables)
+    // 8-bit anchors: the anchor grid of every (layer, K/V, channel) row, [L][2][C]; null
+    // alo means fp16 anchors
+    const float *alo = nullptr, *aw = nullptr, *ar = nullptr;
 };
 
 // Paged output (vLLM-style block table): pages fp16 [L][2][num_pages][1 << lp][C]; token t
@@ -79,6 +82,10 @@ hipError_t launch_k3_paged(const Geom &g, const uint8_t *bins, const uint32_t *d
                            const ContainerView &cv, const Paged &pg, hipStream_t st);
 // Writes the stored fp16 sink rows of tokens [t_a, t_b) into the output: the contiguous
 // [L][2][S][C] out, or the pages of pg when pg.pages is set.
+// The 8-bit anchor grid of every (layer, K/V, channel) row over its anchor tokens.
+hipError_t launch_anchor_grid(const uint16_t *X, const Geom &g, float *alo, float *aw, float *ar,
+                              hipStream_t st);
+
 hipError_t launch_sinks(const Geom &g, const uint16_t *sinks, uint32_t n_sink, uint32_t t_a,
                         uint32_t t_b, uint16_t *out, const Paged &pg, hipStream_t st);
 hipError_t launch_k4(const Geom &g, const float *lo, const float *w, const uint8_t *sym,

@@ -182,13 +182,14 @@ __device__ __forceinline__ void flush_rows(const __amdgpu_buffer_rsrc_t &ors, ui
 // requested and the previous group's outputs (held in registers) are written; the
 // requested data is consumed at the group's end.  Waits for it therefore never wait for
 // a store issued during the group.
-template <bool SYMBOLS, bool PAGED = false>
+template <bool SYMBOLS, bool PAGED = false, bool A8 = false>
 struct Stream {
     WaveDecoder dec;
     __amdgpu_buffer_rsrc_t ars, ors;
     uint32_t ng, len;           // groups / tokens in the chunk
     uint32_t astride, ostride, olane;
     uint32_t a16;               // anchor row of the current group (fp16 bits)
+    float galo, gaw;            // 8-bit anchors (A8): ars holds codes on this lane's grid
     float af;
     uint32_t orow;              // byte offset of the current anchor row (paged: its token)
     uint32_t orow_held;         // byte offset of the first row held in yf / ys (paged: token)
@@ -304,10 +305,17 @@ struct Stream {
         // anchor rows of this chunk: row gi at byte 2 * (gi * C + lane); reads beyond the
         // anchors section return 0
         const uint64_t aoff = anchor_row(g, k, row, 0) * g.C + b * kLanes;
-        ars = make_rsrc(container + cv.anchors_off + 2 * aoff,
-                        (uint32_t)min(cv.anchors_bytes - min(2 * aoff, cv.anchors_bytes),
+        const uint64_t aesz = A8 ? 1u : 2u;  // bytes per anchor element
+        ars = make_rsrc(container + cv.anchors_off + aesz * aoff,
+                        (uint32_t)min(cv.anchors_bytes - min(aesz * aoff, cv.anchors_bytes),
                                       (uint64_t)0xFFFFFFFFu));
-        astride = 2 * g.C;
+        astride = (uint32_t)aesz * g.C;
+        galo = 0.0f;
+        gaw = 0.0f;
+        if (A8 && present) {
+            galo = g.alo[(uint64_t)row * g.C + b * kLanes + lane];
+            gaw = g.aw[(uint64_t)row * g.C + b * kLanes + lane];
+        }
         const uint64_t obase = ((uint64_t)row * g.S + t0_chunk) * g.C + b * kLanes;
         ors = SYMBOLS ? make_rsrc(sym_out + obase, 0xFFFFFFFFu) : make_rsrc(out + obase, 0xFFFFFFFFu);
         ostride = g.C * (SYMBOLS ? 1u : 2u);  // bytes between token rows
@@ -345,9 +353,16 @@ struct Stream {
     // first anchor row; the empty asm pins the wait for it here
     __device__ __forceinline__ void first_anchor(uint32_t lane)
     {
-        uint32_t v = __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, 0, kNT);
+        uint32_t v = A8 ? __builtin_amdgcn_raw_buffer_load_b8(ars, lane, 0, kNT)
+                        : __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, 0, kNT);
         asm volatile("" : "+v"(v));
-        a16 = v;
+        set_anchor(v);
+    }
+
+    // the anchor row from its loaded value: fp16 bits, or an 8-bit code on the grid
+    __device__ __forceinline__ void set_anchor(uint32_t v)
+    {
+        a16 = A8 ? f2h_fma((float)v, gaw, galo) : v;
         af = h2f(a16);
     }
 
@@ -368,7 +383,8 @@ struct Stream {
     // would be fetched again, not found in the cache)
     __device__ __forceinline__ void request(uint32_t gi, uint32_t lane)
     {
-        a_next = __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, (gi + 1) * astride, kNT);
+        a_next = A8 ? __builtin_amdgcn_raw_buffer_load_b8(ars, lane, (gi + 1) * astride, kNT)
+                    : __builtin_amdgcn_raw_buffer_load_b16(ars, 2 * lane, (gi + 1) * astride, kNT);
         fetch = dec.m > 0 && dec.re + kFetchWords - dec.cur <= kRingWords;
         pf_at = dec.re;
         pf = 0;
@@ -402,8 +418,7 @@ struct Stream {
     {
         uint32_t an = a_next, pv = pf;
         asm volatile("" : "+v"(an), "+v"(pv));
-        a16 = an;
-        af = h2f(a16);
+        set_anchor(an);
         if (fetch && dec.re == pf_at) {
             ring_put(dec.ring, pf_at + 2 * lane, pv);
             dec.re = pf_at + kFetchWords;
@@ -466,8 +481,8 @@ struct Stream {
 };
 
 // An unrolled group of both streams of a wavefront in lockstep.
-template <bool SYMBOLS, bool PAGED, int NS>
-__device__ __forceinline__ void paired_steps(Stream<SYMBOLS, PAGED> (&st)[NS], const uint8_t *tab,
+template <bool SYMBOLS, bool PAGED, bool A8, int NS>
+__device__ __forceinline__ void paired_steps(Stream<SYMBOLS, PAGED, A8> (&st)[NS], const uint8_t *tab,
                                              uint32_t lane)
 {
 #pragma unroll
@@ -524,7 +539,7 @@ __device__ __forceinline__ void paired_steps(Stream<SYMBOLS, PAGED> (&st)[NS], c
 // One wavefront decodes NS chunks of the same (row, channel block) in lockstep, sharing
 // the block's LDS table.  With two, the symbol decodes of both streams sit in one
 // basic block, so the dependent LDS reads of one overlap the arithmetic of the other.
-template <bool SYMBOLS, bool FULL, int NS, bool PAGED>
+template <bool SYMBOLS, bool FULL, int NS, bool PAGED, bool A8>
 __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__restrict__ tab,
                                               uint16_t *__restrict__ ring,
                                               const float *__restrict__ lo,
@@ -536,7 +551,7 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
                                               uint8_t *__restrict__ sym_out, const Paged &pg)
 {
     const bool present = FULL || lane < min(kLanes, g.C - b * kLanes);
-    Stream<SYMBOLS, PAGED> st[NS];
+    Stream<SYMBOLS, PAGED, A8> st[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
         st[s].init(g, ring + s * kRingAlloc, lo, w, container, cv, s == 0 ? k0 : k1, row, b, lane,
@@ -613,7 +628,7 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
 // row: otherwise an XCD would hold only the columns b with one residue mod 8, and its
 // writes and anchor reads would queue on the few L2 / memory channels those addresses
 // map to.
-template <bool SYMBOLS, uint32_t WPB, bool PAGED = false>
+template <bool SYMBOLS, uint32_t WPB, bool PAGED = false, bool A8 = false>
 __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
                                                   const uint32_t *__restrict__ dtab,
                                                   const float *__restrict__ lo,
@@ -653,14 +668,14 @@ __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__r
     const bool pair = k1 < g.ke;
     if (g.C - b * kLanes >= kLanes) {
         if (pair)
-            decode_chunks<SYMBOLS, true, 2, PAGED>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
+            decode_chunks<SYMBOLS, true, 2, PAGED, A8>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
         else
-            decode_chunks<SYMBOLS, true, 1, PAGED>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
+            decode_chunks<SYMBOLS, true, 1, PAGED, A8>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
     } else {
         if (pair)
-            decode_chunks<SYMBOLS, false, 2, PAGED>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
+            decode_chunks<SYMBOLS, false, 2, PAGED, A8>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
         else
-            decode_chunks<SYMBOLS, false, 1, PAGED>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
+            decode_chunks<SYMBOLS, false, 1, PAGED, A8>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
     }
 }
 
@@ -686,6 +701,7 @@ __global__ __launch_bounds__(256) void k4_dequant(Geom g, const float *__restric
     if (t_begin >= t_hi) return;
     uint32_t t_end = min(t_hi, t_begin + tpt);
     const uint16_t *anc = reinterpret_cast<const uint16_t *>(container + cv.anchors_off) + o * 8;
+    const uint8_t *anc8 = container + cv.anchors_off + o * 8;
     float lo8[8], w8[8], af[8];
     uint64_t r0 = (uint64_t)row * g.C + o * 8;
 #pragma unroll
@@ -693,17 +709,29 @@ __global__ __launch_bounds__(256) void k4_dequant(Geom g, const float *__restric
         lo8[j] = lo[r0 + j];
         w8[j] = w[r0 + j];
     }
+    // an anchor row: fp16 bits, or 8-bit codes mapped to their grid values
+    auto load_anchor = [&](uint64_t arow) -> uint4 {
+        if (!g.alo) return *reinterpret_cast<const uint4 *>(anc + arow * g.C);
+        const uint2 c = *reinterpret_cast<const uint2 *>(anc8 + arow * g.C);
+        uint32_t h[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            h[j] = f2h_fma((float)(((j < 4 ? c.x : c.y) >> (8 * (j & 3))) & 0xFFu), g.aw[r0 + j],
+                           g.alo[r0 + j]);
+        return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                          h[6] | (h[7] << 16));
+    };
     TokenWalk tw;
     tw.init(g, t_begin);
     if (tw.gp != 0) {
-        uint4 a = *reinterpret_cast<const uint4 *>(anc + anchor_row(g, tw.k, row, tw.gi) * g.C);
+        uint4 a = load_anchor(anchor_row(g, tw.k, row, tw.gi));
         unpack8(a, af);
     }
     const uint64_t ob = (uint64_t)row * g.S * g.C + o * 8;
     for (; tw.t < t_end; tw.next(g)) {
         uint4 res;
         if (tw.gp == 0) {
-            res = *reinterpret_cast<const uint4 *>(anc + anchor_row(g, tw.k, row, tw.gi) * g.C);
+            res = load_anchor(anchor_row(g, tw.k, row, tw.gi));
             unpack8(res, af);
         } else {
             uint2 s8 = *reinterpret_cast<const uint2 *>(sym + ob + (uint64_t)tw.t * g.C);
@@ -734,12 +762,21 @@ hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, c
     const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
     const dim3 grid((uint32_t)blocks), block(wpb * kLanes);
     const Paged none{};
+    // symbols do not depend on the anchors: the symbol decoder reads an 8-bit anchors
+    // section as fp16 rows, in bounds (the resource ends with the section), and ignores it
     if (sym_out) {
         if (wide)
             hipLaunchKernelGGL((k3_decode<true, kWavesPerBlock>), grid, block, 0, st, g, bins,
                                dtab, lo, w, container, cv, n_sets, out, sym_out, none);
         else
             hipLaunchKernelGGL((k3_decode<true, 1>), grid, block, 0, st, g, bins, dtab,
+                               lo, w, container, cv, n_sets, out, sym_out, none);
+    } else if (g.alo) {
+        if (wide)
+            hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock, false, true>), grid, block, 0, st, g,
+                               bins, dtab, lo, w, container, cv, n_sets, out, sym_out, none);
+        else
+            hipLaunchKernelGGL((k3_decode<false, 1, false, true>), grid, block, 0, st, g, bins, dtab,
                                lo, w, container, cv, n_sets, out, sym_out, none);
     } else {
         if (wide)
@@ -802,7 +839,13 @@ hipError_t launch_k3_paged(const Geom &g, const uint8_t *bins, const uint32_t *d
     const uint32_t n_sets = (g.ke - g.kb + per_block - 1) / per_block;
     const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
     const dim3 grid((uint32_t)blocks), block(wpb * kLanes);
-    if (wide)
+    if (g.alo && wide)
+        hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock, true, true>), grid, block, 0, st, g,
+                           bins, dtab, lo, w, container, cv, n_sets, nullptr, nullptr, pg);
+    else if (g.alo)
+        hipLaunchKernelGGL((k3_decode<false, 1, true, true>), grid, block, 0, st, g, bins, dtab, lo,
+                           w, container, cv, n_sets, nullptr, nullptr, pg);
+    else if (wide)
         hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock, true>), grid, block, 0, st, g, bins,
                            dtab, lo, w, container, cv, n_sets, nullptr, nullptr, pg);
     else

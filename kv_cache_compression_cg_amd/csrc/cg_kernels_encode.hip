@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256) void k0_minmax(const uint16_t *__restrict__ X,
     if (w.gp != 0) {
         uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
         unpack8(a, af);
+        snap8(g, (uint64_t)row * g.C + o * 8, af);
     }
     for (; w.t < t_end; w.next(g)) {
         uint4 v = ntload16(base + (uint64_t)w.t * g.C);
@@ -65,6 +66,7 @@ __global__ __launch_bounds__(256) void k0_minmax(const uint16_t *__restrict__ X,
         if (w.gp == 0) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) af[j] = xf[j];
+            snap8(g, (uint64_t)row * g.C + o * 8, af);
         } else if (w.t >= g.n_sink) {  // sink tokens stay out of the range
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -155,6 +157,7 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
         if (w.gp != 0) {
             uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
             unpack8(a, af);
+            snap8(g, (uint64_t)row * g.C + o * 8, af);
         }
         for (; w.t < t_end; w.next(g)) {
             uint4 v = ntload16(base + (uint64_t)w.t * g.C);
@@ -163,6 +166,7 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
             if (w.gp == 0) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) af[j] = xf[j];
+                snap8(g, (uint64_t)row * g.C + o * 8, af);
             } else if (w.t >= g.n_sink) {  // and out of the histograms
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -272,6 +276,7 @@ __global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict
     if (w.gp != 0) {
         uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
         unpack8(a, af);
+        snap8(g, (uint64_t)row * g.C + o * 8, af);
     }
     for (; w.t < t_end; w.next(g)) {
         uint4 v = ntload16(base + (uint64_t)w.t * g.C);
@@ -281,7 +286,23 @@ __global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict
         if (w.gp == 0) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) af[j] = xf[j];
-            if (anchors) {
+            if (g.alo) {
+                // 8-bit anchors: the codes go to the container, their grid values anchor
+                // the deltas
+                const uint64_t r0 = (uint64_t)row * g.C + o * 8;
+                uint32_t cd[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    cd[j] = quantize1(af[j], g.alo[r0 + j], g.ar[r0 + j], 256u);
+                    af[j] = h2f(f2h_fma((float)cd[j], g.aw[r0 + j], g.alo[r0 + j]));
+                }
+                if (anchors) {
+                    uint8_t *a8 = reinterpret_cast<uint8_t *>(anchors);
+                    const uint2 pk = make_uint2(cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24),
+                                                cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24));
+                    ntstore8(a8 + anchor_row(g, w.k, row, w.gi) * g.C + o * 8, pk);
+                }
+            } else if (anchors) {
                 uint64_t ar = anchor_row(g, w.k, row, w.gi);
                 ntstore16(anchors + ar * g.C + o * 8, v);
             }
@@ -294,6 +315,47 @@ __global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict
         }
         ntstore8(sbase + (uint64_t)(w.t - sym_t0) * g.C, packed);
     }
+}
+
+// 8-bit anchor grid ("Guide to CacheGen", Solution pillar 2: the anchor is quantized with
+// high precision): per (layer, K/V, channel) row, min / max of its anchor tokens over all
+// chunks, width (max - min) / 255, zero bounds as +0.  One thread per row element; a
+// wavefront reads 64 consecutive channels of one anchor token.
+__global__ __launch_bounds__(256) void k_anchor_grid(const uint16_t *__restrict__ X, Geom g,
+                                                      float *__restrict__ alo,
+                                                      float *__restrict__ aw,
+                                                      float *__restrict__ ar)
+{
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (uint64_t)g.L * 2 * g.C) return;
+    const uint32_t c = (uint32_t)(i % g.C), row = (uint32_t)(i / g.C);
+    const uint16_t *base = X + (uint64_t)row * g.S * g.C + c;
+    float lo = 0.0f, hi = 0.0f;
+    bool any = false;
+    for (uint32_t t0 = 0; t0 < g.S; t0 += g.Tc) {
+        const uint32_t t1 = min(g.S, t0 + g.Tc);
+        for (uint32_t t = t0; t < t1; t += g.G) {
+            const float x = h2f(base[(uint64_t)t * g.C]);
+            if (!any || x < lo) lo = x;
+            if (!any || x > hi) hi = x;
+            any = true;
+        }
+    }
+    lo = lo + 0.0f;
+    hi = hi + 0.0f;
+    const float w = (hi - lo) / 255.0f;
+    alo[i] = lo;
+    aw[i] = w;
+    ar[i] = (w > 0.0f) ? 1.0f / w : 0.0f;
+}
+
+hipError_t launch_anchor_grid(const uint16_t *X, const Geom &g, float *alo, float *aw, float *ar,
+                              hipStream_t st)
+{
+    const uint64_t n = (uint64_t)g.L * 2 * g.C;
+    hipLaunchKernelGGL(k_anchor_grid, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, X, g,
+                       alo, aw, ar);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------ K5

@@ -43,18 +43,21 @@ GAUSS = configs.GenSpec(rho=0.9, heavy_tail=False, outlier_frac=0.02, outlier_mu
 HEAVY = configs.GenSpec(rho=0.85, heavy_tail=True, outlier_frac=0.05, outlier_mult=30.0, seed=1)
 
 
-def full_parity(cg, X, H, G, Tc, bins, chunk_range=None, label="", bins_v=None, n_sink=0):
+def full_parity(cg, X, H, G, Tc, bins, chunk_range=None, label="", bins_v=None, n_sink=0,
+                anchor_bits=16):
     """Runs both sides on the same cache and compares every product of the path."""
     L, _, S, C = X.shape
     _say("[parity] %s L=%d S=%d C=%d G=%d Tc=%d bins=%s bins_v=%s"
          % (label, L, S, C, G, Tc, list(bins), None if bins_v is None else list(bins_v)))
     Xh = _u16(X)
-    shp = O.Shape.make(L, H, C // H, S, G, Tc, bins, bins_v=bins_v, n_sink=n_sink)
+    shp = O.Shape.make(L, H, C // H, S, G, Tc, bins, bins_v=bins_v, n_sink=n_sink,
+                       anchor_bits=anchor_bits)
     tab_o = O.build_tables(shp, Xh)
     kb, ke = chunk_range if chunk_range else (0, shp.n_chunks)
     enc_o = O.encode(shp, Xh, tab_o, kb, ke)
 
-    tab = cg.build_cdf(X, G, Tc, bins, H_kv=H, bins_v=bins_v, n_sink=n_sink)
+    tab = cg.build_cdf(X, G, Tc, bins, H_kv=H, bins_v=bins_v, n_sink=n_sink,
+                       anchor_bits=anchor_bits)
     assert tab.stored_bytes == O.table_bytes(shp)
     ex = tab.export()
     for name in ("lo", "w", "r"):
@@ -63,7 +66,7 @@ def full_parity(cg, X, H, G, Tc, bins, chunk_range=None, label="", bins_v=None, 
 
     sym = cg.quantize(tab, X, kb, ke)
     t0, t1 = kb * Tc, min(ke * Tc, S)
-    sym_o = O.quantize(shp, Xh, tab_o.lo, tab_o.r, t0, t1)
+    sym_o = O.quantize(shp, O.snap_anchors(shp, Xh, tab_o), tab_o.lo, tab_o.r, t0, t1)
     assert np.array_equal(sym.cpu().numpy()[:, :, t0:t1], sym_o[:, :, t0:t1])
 
     blob = cg.encode(tab, X, kb, ke)
@@ -321,3 +324,29 @@ def test_extreme_outlier_channel(cg):
     X = _gen(2, 900, 72, HEAVY)
     X[..., 37] = (X[..., 37].float() * 500.0).clamp(-65504, 65504).half()
     full_parity(cg, X, 9, 10, 300, (16, 4), label="outlier x500")
+
+
+@pytest.mark.parametrize("S,C,G,Tc,rng,n_sink", [(1000, 192, 10, 300, None, 0),
+                                                (700, 72, 7, 256, (1, 3), 0),
+                                                (2000, 136, 10, 90, None, 4),
+                                                (2000, 136, 10, 60, (2, 30), 0)])
+def test_8bit_anchors(cg, S, C, G, Tc, rng, n_sink):
+    """Anchors stored as 8-bit codes on a per-channel grid ("Guide to CacheGen", Solution
+    pillar 2): tables, codes, payload, decode (fused and unfused) and paged decode equal
+    the oracle's; several tiles, a partial lane block, paired chunks, chunk ranges and
+    sinks."""
+    L, H, bins = 2, (3 if C == 192 else 9 if C == 72 else 17), (32, 8)
+    X = _gen(L, S, C, HEAVY)
+    tab, blob, tab_o, enc_o = full_parity(cg, X, H, G, Tc, bins, chunk_range=rng,
+                                          label="8-bit anchors", n_sink=n_sink, anchor_bits=8)
+    assert blob.anchors().dtype == np.uint8
+    P = 16
+    nb = -(-S // P)
+    bt = torch.randperm(nb, generator=torch.Generator().manual_seed(S)).to(torch.int32).cuda()
+    pages = torch.full((L, 2, nb, P, C), float("nan"), dtype=torch.float16, device="cuda")
+    cg.decode_paged(tab, blob, pages, bt)
+    torch.cuda.synchronize()
+    shp = O.Shape.make(L, H, C // H, S, G, Tc, bins, n_sink=n_sink, anchor_bits=8)
+    nan16 = _u16(torch.full((1,), float("nan"), dtype=torch.float16))[0]
+    ref = O.decode(shp, tab_o, enc_o, out=np.full((L, 2, S, C), nan16, np.uint16))
+    assert np.array_equal(_u16(_gather_pages(pages, bt, S)), ref)
