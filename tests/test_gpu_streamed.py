@@ -216,12 +216,14 @@ def test_stream_decode_rejects_bad_items(cg):
     assert torch.equal(got[:, :, :200].view(torch.int16), ref[:, :, :200].view(torch.int16))
 
 
-def test_stream_decode_writes_sink_tokens(cg):
-    """Tables with attention sinks: the streamed decode of chunks 0 and 1 (the sinks span
-    both) equals cg_decode's, which the parity tests hold to the oracle."""
+@pytest.mark.parametrize("anchor_bits", [16, 8])
+def test_stream_decode_writes_sink_tokens(cg, anchor_bits):
+    """Tables with attention sinks (and fp16 or 8-bit anchors): the streamed decode of
+    chunks 0 to 2 (the sinks span 0 and 1) equals cg_decode's, which the parity tests
+    hold to the oracle."""
     X = synth.gen_custom(2, 600, 64, HEAVY, device="cuda")
     X[:, :, 1:12] = 2000.0
-    tab = cg.build_cdf(X, 5, 8, (8, 4), H_kv=1, n_sink=12)
+    tab = cg.build_cdf(X, 5, 8, (8, 4), H_kv=1, n_sink=12, anchor_bits=anchor_bits)
     blobs = [cg.encode(tab, X, k, k + 1) for k in range(3)]
     hosts = [torch.from_numpy(b.read().copy()) for b in blobs]
     slot = (max(b.nbytes for b in blobs) + 255) // 256 * 256
