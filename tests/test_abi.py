@@ -86,3 +86,27 @@ def test_validation_without_device(lib):
     # a handle that is neither tables nor blob is ignored
     junk = ctypes.create_string_buffer(64)
     lib.cg_free(junk)
+
+
+def _struct_fields(name):
+    """Field names of a `typedef struct name { ... } name;` in cg.h, in order."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (name, name), text, flags=re.S).group(1)
+    fields = []
+    for decl in body.split(";"):
+        for part in decl.split(","):
+            ids = re.findall(r"[A-Za-z_]\w*", re.sub(r"\[.*?\]", "", part))
+            if ids:
+                fields.append(ids[-1])
+    return fields
+
+
+@pytest.mark.parametrize("cname,pyname", [("cg_params", "Params"),
+                                          ("cg_container_header", "ContainerHeader"),
+                                          ("cg_tables_info", "TablesInfo"),
+                                          ("cg_stream_stats", "StreamStats")])
+def test_binding_structs_follow_the_header(cname, pyname):
+    """The ctypes structures carry the header's fields in the header's order."""
+    from kv_cache_compression_cg_amd import cg
+    ours = [f for f, _ in getattr(cg, pyname)._fields_]
+    assert ours == _struct_fields(cname)
