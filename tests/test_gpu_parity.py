@@ -350,3 +350,12 @@ def test_8bit_anchors(cg, S, C, G, Tc, rng, n_sink):
     nan16 = _u16(torch.full((1,), float("nan"), dtype=torch.float16))[0]
     ref = O.decode(shp, tab_o, enc_o, out=np.full((L, 2, S, C), nan16, np.uint16))
     assert np.array_equal(_u16(_gather_pages(pages, bt, S)), ref)
+
+
+def test_format_variants_together(cg):
+    """Keys finer than values, attention sinks and 8-bit anchors at once, on paired
+    chunks and a partial lane block: everything equals the oracle's."""
+    X = _gen(3, 1500, 136, HEAVY)
+    X[:, :, 1:4] = 1500.0
+    full_parity(cg, X, 17, 10, 100, (32, 16, 8), bins_v=(16, 8, 4), n_sink=4,
+                anchor_bits=8, label="bins_v + sinks + 8-bit anchors")
