@@ -61,6 +61,12 @@ def test_validation_without_device(lib):
     p = cg.Params(1, 1, 1 << 17, 1 << 14, 10, 1 << 14, ctypes.cast(one, ctypes.POINTER(ctypes.c_uint8)))
     assert lib.cg_build_cdf(ctypes.byref(p), ctypes.c_void_p(16), None, ctypes.byref(h)) == -1
     assert b"too large" in lib.cg_last_error()
+    # 8-bit or fp16 anchors only
+    two = (ctypes.c_uint8 * 2)(8, 8)
+    p = cg.Params(2, 1, 8, 16, 4, 8, ctypes.cast(two, ctypes.POINTER(ctypes.c_uint8)), None, 0, 4)
+    assert lib.cg_build_cdf(ctypes.byref(p), ctypes.c_void_p(16), None, ctypes.byref(h)) == -1
+    assert b"anchor_bits" in lib.cg_last_error()
+    assert lib.cg_decode_paged(None, None, None, None, None, 16, 1, None) == -1
     assert lib.cg_encode(None, None, 0, 1, None, ctypes.byref(h)) == -1
     assert lib.cg_decode(None, None, None, None, None) == -1
     assert lib.cg_quantize(None, None, 0, 1, None, None) == -1
