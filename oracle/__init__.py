@@ -33,6 +33,7 @@ _u8p = ctypes.POINTER(ctypes.c_uint8)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _u64p = ctypes.POINTER(ctypes.c_uint64)
 _i32p = ctypes.POINTER(ctypes.c_int32)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
 _f32p = ctypes.POINTER(ctypes.c_float)
 _u32 = ctypes.c_uint32
 
@@ -59,7 +60,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB)
         L.cgo_half_to_float_n.argtypes = [_u16p, _f32p, ctypes.c_size_t]
         L.cgo_float_to_half_n.argtypes = [_f32p, _u16p, ctypes.c_size_t]
-        L.cgo_range.argtypes = [_u32] * 6 + [_u8p, _u16p, _f32p, _f32p, _f32p, _u32]
+        L.cgo_range.argtypes = [_u32] * 6 + [_u8p, _u16p, _f32p, _f32p, _f32p, _u32, _u32]
         L.cgo_range.restype = ctypes.c_int
         L.cgo_quantize.argtypes = [_u32] * 6 + [_u8p, _u16p, _f32p, _f32p, _u32, _u32, _u8p]
         L.cgo_histograms.argtypes = [_u32] * 6 + [_u8p, _u8p, _u64p, _u32]
@@ -87,6 +88,12 @@ def lib() -> ctypes.CDLL:
         L.cgo_decode.restype = ctypes.c_int
         L.cgo_dequantize.argtypes = ([_u32] * 6 + [_f32p, _f32p, _u8p, _u16p, _u32, _u32,
                                                    _u16p])
+        L.cgo_outliers.argtypes = ([_u32] * 6 + [_u8p, _u16p, _u16p, _f32p, _f32p, _f32p, _f32p,
+                                               _u32, _u32, _u32, _u64p, _u32p, _u16p])
+        L.cgo_outliers.restype = ctypes.c_uint64
+        L.cgo_apply_outliers.argtypes = ([_u32] * 5 + [_u32, _u32, _u64p, _u32p, _u16p,
+                                                     ctypes.c_uint64, _u16p])
+        L.cgo_apply_outliers.restype = ctypes.c_int
         for name in ("cgo_num_chunks", "cgo_chunk_len", "cgo_groups_in", "cgo_anchor_of"):
             getattr(L, name).restype = _u32
         L.cgo_num_chunks.argtypes = [_u32, _u32]
@@ -115,6 +122,7 @@ class Shape:
     bins: np.ndarray  # uint8 [L][2] flattened: bin count of (layer l, K/V kv) at l * 2 + kv
     n_sink: int = 0   # first tokens of the sequence kept in fp16 (attention sinks)
     anchor_bits: int = 16  # 16: anchors stored as fp16; 8: as codes on a 256-level grid
+    outlier_ppm: int = 0   # 0: no outlier table; else the clip budget per end, parts per million
 
     @property
     def C(self) -> int:
@@ -129,7 +137,7 @@ class Shape:
 
     @staticmethod
     def make(L, H, d, S, G, Tc, bins: Sequence[int], bins_v: Optional[Sequence[int]] = None,
-             n_sink: int = 0, anchor_bits: int = 16) -> "Shape":
+             n_sink: int = 0, anchor_bits: int = 16, outlier_ppm: int = 0) -> "Shape":
         """bins: the bin count of each layer (K and V rows alike), or of its K rows when
         bins_v gives those of the V rows (the keys-finer-than-values variant of the
         Guide's Solution pillar 1).  n_sink: the first n_sink tokens of the sequence are
@@ -137,13 +145,17 @@ class Shape:
         (the Guide's Best Practices: protect the attention sinks).  anchor_bits = 8 stores
         each anchor as a code on a 256-level grid of its channel (the Guide's Solution
         pillar 2: anchors quantized with high precision); the deltas are taken against
-        the anchor's grid value."""
+        the anchor's grid value.  outlier_ppm > 0 turns on the sparse outlier table (the
+        Guide's Solution pillar 3): each channel's grid spans a central range that leaves
+        at most outlier_ppm / 10^6 of its deltas out at each end, and every element off
+        its grid is stored exactly in fp16 in the container."""
         assert anchor_bits in (8, 16)
+        assert 0 <= outlier_ppm <= 250000
         k = np.asarray(bins, dtype=np.uint8)
         v = k if bins_v is None else np.asarray(bins_v, dtype=np.uint8)
         assert k.shape == (L,) and v.shape == (L,)
         return Shape(L, H, d, S, G, Tc, np.ascontiguousarray(np.stack([k, v], axis=1).reshape(-1)),
-                     int(n_sink), int(anchor_bits))
+                     int(n_sink), int(anchor_bits), int(outlier_ppm))
 
 
 # ------------------------------------------------------------------ fp16 conversions
@@ -169,7 +181,6 @@ class Tables:
     r: np.ndarray       # float32 [L, 2, C]
     counts: np.ndarray  # uint64 [L, 2, C, 32]
     freqs: np.ndarray   # uint16 [L, 2, C, 32]
-    sinks: Optional[np.ndarray] = None  # uint16 [L, 2, min(n_sink, S), C]: fp16 copy
     alo: Optional[np.ndarray] = None    # float32 [L, 2, C]: anchor grid (8-bit anchors)
     aw: Optional[np.ndarray] = None
     ar: Optional[np.ndarray] = None
@@ -204,12 +215,12 @@ def build_tables(shp: Shape, X: np.ndarray) -> Tables:
     assert X.shape == (shp.L, 2, shp.S, shp.C)
     grid = anchor_grid(shp, X) if shp.anchor_bits == 8 else (None, None, None)
     X0 = X
-    X = snap_anchors(shp, X, Tables(None, None, None, None, None, None, *grid))
+    X = snap_anchors(shp, X, Tables(None, None, None, None, None, *grid))
     lo = np.empty((shp.L, 2, shp.C), np.float32)
     w = np.empty_like(lo)
     r = np.empty_like(lo)
     rc = lib().cgo_range(*shp.args(), _p(shp.bins, _u8p), _p(X, _u16p), _p(lo, _f32p),
-                         _p(w, _f32p), _p(r, _f32p), shp.n_sink)
+                         _p(w, _f32p), _p(r, _f32p), shp.n_sink, shp.outlier_ppm)
     if rc == -4:
         raise NonFinite("input holds Inf or NaN")
     sym = quantize(shp, X, lo, r, 0, shp.S)
@@ -218,8 +229,8 @@ def build_tables(shp: Shape, X: np.ndarray) -> Tables:
                          shp.n_sink)
     freqs = np.empty((shp.L, 2, shp.C, MAX_BINS), np.uint16)
     lib().cgo_freqs(shp.L, shp.C, _p(shp.bins, _u8p), _p(counts, _u64p), _p(freqs, _u16p))
-    sinks = X0[:, :, :min(shp.n_sink, shp.S)].copy()
-    return Tables(lo, w, r, counts, freqs, sinks, *grid)
+    del X0
+    return Tables(lo, w, r, counts, freqs, *grid)
 
 
 def freqs_from_counts(counts: Sequence[int], N: int) -> np.ndarray:
@@ -276,10 +287,19 @@ class Encoded:
     offsets: np.ndarray  # uint64 [n_groups + 1] (word offsets)
     payload: np.ndarray  # uint16 [offsets[-1]]
     anchors: np.ndarray  # uint16 (fp16 bits) [rows, C], or uint8 codes with 8-bit anchors
+    sinks: np.ndarray = None        # uint16 [L, 2, n, C]: the sink tokens among the chunks
+    out_offsets: np.ndarray = None  # uint64 [n_groups + 1]: outlier entries per group
+    out_keys: np.ndarray = None     # uint32 [n_out]: (token within the chunk) << 6 | lane
+    out_values: np.ndarray = None   # uint16 [n_out]: fp16 bits
+    clamped: int = 0                # off-grid elements coded clamped (no outlier table)
 
     @property
     def payload_bytes(self) -> int:
         return int(self.payload.size) * 2
+
+    @property
+    def n_outliers(self) -> int:
+        return 0 if self.out_keys is None else int(self.out_keys.size)
 
 
 def n_groups(shp: Shape, k_begin: int, k_end: int) -> int:
@@ -288,6 +308,34 @@ def n_groups(shp: Shape, k_begin: int, k_end: int) -> int:
 
 def anchor_rows(shp: Shape, k_begin: int, k_end: int) -> int:
     return int(lib().cgo_anchor_rows(shp.L, shp.S, shp.G, shp.Tc, k_begin, k_end))
+
+
+def sink_tokens(shp: Shape, k_begin: int, k_end: int) -> Tuple[int, int]:
+    """Token range [a, b) of the sink tokens among chunks [k_begin, k_end)."""
+    a = k_begin * shp.Tc
+    b = min(k_end * shp.Tc, shp.S, shp.n_sink)
+    return a, max(a, b)
+
+
+def outliers(shp: Shape, X: np.ndarray, tab: Tables, k_begin: int, k_end: int, store: bool):
+    """(offsets, keys, values, count) of the outlier table of chunks [k_begin, k_end);
+    with store=False only the count of off-grid elements."""
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    Xs = np.ascontiguousarray(snap_anchors(shp, X, tab))
+    ng = n_groups(shp, k_begin, k_end)
+    a8 = shp.anchor_bits == 8
+    f32 = lambda a: _p(np.ascontiguousarray(a, np.float32), _f32p) if a is not None else None
+    args = (*shp.args(), _p(shp.bins, _u8p), _p(X, _u16p), _p(Xs, _u16p), f32(tab.lo), f32(tab.r),
+            f32(tab.alo) if a8 else None, f32(tab.ar) if a8 else None, shp.n_sink, k_begin, k_end)
+    n = int(lib().cgo_outliers(*args, None, None, None))
+    if not store:
+        return None, None, None, n
+    offsets = np.zeros(ng + 1, np.uint64)
+    keys = np.zeros(max(n, 1), np.uint32)
+    values = np.zeros(max(n, 1), np.uint16)
+    n2 = int(lib().cgo_outliers(*args, _p(offsets, _u64p), _p(keys, _u32p), _p(values, _u16p)))
+    assert n2 == n
+    return offsets, keys[:n].copy(), values[:n].copy(), n
 
 
 def encode(shp: Shape, X: np.ndarray, tab: Tables, k_begin: int = 0,
@@ -315,7 +363,14 @@ def encode(shp: Shape, X: np.ndarray, tab: Tables, k_begin: int = 0,
     else:
         anchors = np.zeros((max(rows, 1), shp.C), np.uint16)
         lib().cgo_anchors(*shp.args(), _p(X, _u16p), k_begin, k_end, _p(anchors, _u16p))
-    return Encoded(k_begin, k_end, offsets, payload[:n].copy(), anchors[:rows].copy())
+    sa, sb = sink_tokens(shp, k_begin, k_end)
+    enc = Encoded(k_begin, k_end, offsets, payload[:n].copy(), anchors[:rows].copy(),
+                  sinks=X[:, :, sa:sb].copy())
+    if shp.outlier_ppm:
+        enc.out_offsets, enc.out_keys, enc.out_values, _ = outliers(shp, X, tab, k_begin, k_end, True)
+    else:
+        enc.clamped = outliers(shp, X, tab, k_begin, k_end, False)[3]
+    return enc
 
 
 def anchor_values(shp: Shape, tab: Tables, enc: "Encoded") -> np.ndarray:
@@ -333,7 +388,8 @@ def anchor_values(shp: Shape, tab: Tables, enc: "Encoded") -> np.ndarray:
 
 def decode(shp: Shape, tab: Tables, enc: Encoded, out: Optional[np.ndarray] = None,
            payload: Optional[np.ndarray] = None) -> np.ndarray:
-    """fp16 bits [L, 2, S, C]; tokens outside the encoded chunks are left as in `out`."""
+    """fp16 bits [L, 2, S, C]; tokens outside the encoded chunks are left as in `out`.
+    The decoded rows first, then the container's sink rows and outlier entries."""
     if out is None:
         out = np.zeros((shp.L, 2, shp.S, shp.C), np.uint16)
     payload = enc.payload if payload is None else payload
@@ -348,18 +404,29 @@ def decode(shp: Shape, tab: Tables, enc: Encoded, out: Optional[np.ndarray] = No
                           payload.size, _p(anchors, _u16p), _p(out, _u16p))
     if rc != 0:
         raise ValueError("inconsistent container (code %d)" % rc)
-    _put_sinks(shp, tab, out, enc.k_begin * shp.Tc, min(enc.k_end * shp.Tc, shp.S))
+    _put_extras(shp, enc, out)
     return out
 
 
-def _put_sinks(shp: Shape, tab: Tables, out: np.ndarray, t_begin: int, t_end: int) -> None:
-    """The sink tokens in [t_begin, t_end) take their stored fp16 values."""
-    for t in range(t_begin, min(t_end, shp.n_sink, shp.S)):
-        out[:, :, t] = tab.sinks[:, :, t]
+def _put_extras(shp: Shape, enc: Encoded, out: np.ndarray) -> None:
+    """The container's sink rows, then its outlier entries, written over `out`."""
+    sa, sb = sink_tokens(shp, enc.k_begin, enc.k_end)
+    if sb > sa:
+        out[:, :, sa:sb] = enc.sinks
+    if enc.out_keys is not None and enc.out_keys.size:
+        rc = lib().cgo_apply_outliers(shp.L, shp.H, shp.d, shp.S, shp.Tc, enc.k_begin, enc.k_end,
+                                      _p(np.ascontiguousarray(enc.out_offsets), _u64p),
+                                      _p(np.ascontiguousarray(enc.out_keys), _u32p),
+                                      _p(np.ascontiguousarray(enc.out_values), _u16p),
+                                      enc.out_keys.size, _p(out, _u16p))
+        if rc != 0:
+            raise ValueError("inconsistent outlier table (code %d)" % rc)
 
 
 def dequantize(shp: Shape, tab: Tables, sym: np.ndarray, X_anchor_src: np.ndarray,
-               t_begin: int, t_end: int) -> np.ndarray:
+               t_begin: int, t_end: int, enc: Optional[Encoded] = None) -> np.ndarray:
+    """The unfused path: symbols and anchors to fp16, then (given a container) its sink
+    rows and outlier entries."""
     out = np.zeros((shp.L, 2, shp.S, shp.C), np.uint16)
     src = snap_anchors(shp, np.ascontiguousarray(X_anchor_src, np.uint16), tab)
     lib().cgo_dequantize(*shp.args(), _p(np.ascontiguousarray(tab.lo), _f32p),
@@ -367,14 +434,111 @@ def dequantize(shp: Shape, tab: Tables, sym: np.ndarray, X_anchor_src: np.ndarra
                          _p(np.ascontiguousarray(sym, np.uint8), _u8p),
                          _p(src, _u16p),
                          t_begin, t_end, _p(out, _u16p))
-    _put_sinks(shp, tab, out, t_begin, t_end)
+    if enc is not None:
+        _put_extras(shp, enc, out)
     return out
 
 
+# ------------------------------------------------------------------ stored bytes
+# Byte layouts of the two stored objects, written from their specification in
+# include/cg.h (cg_tables_header, cg_container_header): little endian, fixed-width.
+TABLES_MAGIC = 0x31544743      # "CGT1"
+TABLES_VERSION = 1
+CONTAINER_MAGIC = 0x31474B43   # "CKG1"
+CONTAINER_VERSION = 3
+PAYLOAD_PAD = 1024
+
+
+def _a256(x: int) -> int:
+    return (x + 255) & ~255
+
+
 def table_bytes(shp: Shape) -> int:
-    """Stored side information: lo and w (4 B each) per channel row, one 2-byte frequency
-    per symbol per channel row, one byte per (layer, K/V) for the bin count, the fp16
-    copy of the sink tokens, and alo and aw (4 B each) per channel row with 8-bit anchors."""
-    return int(2 * shp.C * shp.L * 8 + sum(int(b) * shp.C * 2 for b in shp.bins) + 2 * shp.L
-               + 2 * shp.L * min(shp.n_sink, shp.S) * shp.C * 2
-               + (2 * shp.C * shp.L * 8 if shp.anchor_bits == 8 else 0))
+    """Size of the stored tables (tables_bytes): a 56-byte header, the bin count of every
+    (layer, K/V) row (padded to 4 bytes), lo and w (4 B each) per channel row, alo and aw
+    too with 8-bit anchors, and N 2-byte frequencies per channel row."""
+    rows = 2 * shp.L * shp.C
+    return int(56 + ((2 * shp.L + 3) & ~3) + rows * 8 * (2 if shp.anchor_bits == 8 else 1)
+               + sum(int(b) * shp.C * 2 for b in shp.bins))
+
+
+def tables_bytes(shp: Shape, tab: Tables) -> bytes:
+    head = np.array([TABLES_MAGIC, TABLES_VERSION, shp.L, shp.H, shp.d, shp.S, shp.G, shp.Tc,
+                     shp.n_sink, shp.anchor_bits, shp.outlier_ppm, 0], np.uint32).tobytes()
+    parts = [head, np.array([table_bytes(shp)], np.uint64).tobytes()]
+    bins = np.zeros((2 * shp.L + 3) & ~3, np.uint8)
+    bins[:2 * shp.L] = shp.bins
+    parts += [bins.tobytes(), tab.lo.astype(np.float32).tobytes(), tab.w.astype(np.float32).tobytes()]
+    if shp.anchor_bits == 8:
+        parts += [tab.alo.astype(np.float32).tobytes(), tab.aw.astype(np.float32).tobytes()]
+    for l in range(shp.L):
+        for kv in range(2):
+            N = int(shp.bins[l * 2 + kv])
+            parts.append(np.ascontiguousarray(tab.freqs[l, kv, :, :N]).astype(np.uint16).tobytes())
+    out = b"".join(parts)
+    assert len(out) == table_bytes(shp)
+    return out
+
+
+def container_layout(shp: Shape, enc: Encoded) -> dict:
+    """Header fields of the container (version 3): every section 256-byte aligned."""
+    ng = n_groups(shp, enc.k_begin, enc.k_end)
+    sa, sb = sink_tokens(shp, enc.k_begin, enc.k_end)
+    h = dict(magic=CONTAINER_MAGIC, version=CONTAINER_VERSION, L=shp.L, H_kv=shp.H, d=shp.d,
+             S=shp.S, group=shp.G, chunk=shp.Tc, chunk_begin=enc.k_begin, chunk_end=enc.k_end,
+             n_blocks=-(-shp.C // LANES), anchor_bits=shp.anchor_bits, n_sink=sb - sa,
+             outlier_ppm=shp.outlier_ppm, n_groups=ng)
+    h["offsets_offset"] = _a256(160)
+    h["anchors_offset"] = _a256(h["offsets_offset"] + (ng + 1) * 8)
+    h["anchors_bytes"] = anchor_rows(shp, enc.k_begin, enc.k_end) * shp.C * (1 if shp.anchor_bits == 8 else 2)
+    h["sinks_offset"] = _a256(h["anchors_offset"] + h["anchors_bytes"])
+    end = h["sinks_offset"] + 2 * shp.L * (sb - sa) * shp.C * 2
+    n_out = enc.n_outliers
+    h["outliers_offset"] = _a256(end)
+    if shp.outlier_ppm:
+        h["outlier_keys_offset"] = _a256(h["outliers_offset"] + (ng + 1) * 8)
+        h["outlier_values_offset"] = _a256(h["outlier_keys_offset"] + n_out * 4)
+        end = h["outlier_values_offset"] + n_out * 2
+    else:
+        h["outlier_keys_offset"] = h["outlier_values_offset"] = h["outliers_offset"]
+    h["n_outliers"] = n_out
+    h["clamped"] = enc.clamped
+    h["payload_offset"] = _a256(end)
+    h["payload_words"] = int(enc.payload.size)
+    h["total_bytes"] = h["payload_offset"] + 2 * h["payload_words"] + PAYLOAD_PAD
+    return h
+
+
+HEADER_U32 = ("magic", "version", "L", "H_kv", "d", "S", "group", "chunk", "chunk_begin",
+              "chunk_end", "n_blocks", "anchor_bits", "n_sink", "outlier_ppm")
+HEADER_U64 = ("n_groups", "offsets_offset", "anchors_offset", "anchors_bytes", "sinks_offset",
+              "outliers_offset", "outlier_keys_offset", "outlier_values_offset", "n_outliers",
+              "clamped", "payload_offset", "payload_words", "total_bytes")
+
+
+def container_bytes(shp: Shape, enc: Encoded) -> bytes:
+    """The whole container (version 3), zero bytes between sections and 1 KiB of zeros
+    after the payload."""
+    h = container_layout(shp, enc)
+    buf = np.zeros(h["total_bytes"], np.uint8)
+    head = (np.array([h[k] for k in HEADER_U32], np.uint32).tobytes() +
+            np.array([h[k] for k in HEADER_U64], np.uint64).tobytes())
+    assert len(head) == 160
+
+    def put(off, arr):
+        b = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+        buf[off:off + b.size] = b
+
+    put(0, np.frombuffer(head, np.uint8))
+    put(h["offsets_offset"], enc.offsets.astype(np.uint64))
+    put(h["anchors_offset"], enc.anchors)
+    if h["n_sink"]:
+        put(h["sinks_offset"], enc.sinks.astype(np.uint16))
+    if shp.outlier_ppm:
+        put(h["outliers_offset"], enc.out_offsets.astype(np.uint64))
+        if enc.n_outliers:
+            put(h["outlier_keys_offset"], enc.out_keys.astype(np.uint32))
+            put(h["outlier_values_offset"], enc.out_values.astype(np.uint16))
+    if enc.payload.size:
+        put(h["payload_offset"], enc.payload.astype(np.uint16))
+    return buf.tobytes()

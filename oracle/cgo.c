@@ -143,12 +143,81 @@ static size_t kv_index(const cgo_shape *p, uint32_t l, uint32_t kv, uint32_t t, 
 /*   except the first n_sink tokens of the sequence, which are kept in fp16         */
 /*   ("Guide to CacheGen", Best Practices: protect the attention sinks);            */
 /*   lo = hi = 0 when the channel has no non-anchor token; a zero bound is +0;      */
+/*   with the outlier table on (outlier_ppm > 0), [lo, hi] is narrowed to a central */
+/*   range first (clip_range below);                                                */
 /*   w = (hi - lo) / (N - 1);  r = 1 / w, or 0 when w == 0.                          */
 /* Returns -4 if any input element is Inf or NaN, else 0.                           */
 /* ------------------------------------------------------------------------------ */
+
+#define CGO_FINE_BINS 256u
+
+/* Grid point j of the fine grid over [lo, hi]: fma(j, wf, lo), wf = (hi - lo) / 256. */
+static float fine_point(uint32_t j, float wf, float lo) { return fmaf((float)j, wf, lo); }
+
+/* Fine-grid interval of a delta: the largest j in [0, 255] with fine_point(j) <= delta
+ * (0 if none).  The points do not decrease with j, so a binary search finds it. */
+static uint32_t fine_index(float delta, float wf, float lo)
+{
+    uint32_t a = 0, b = CGO_FINE_BINS - 1u;
+    while (a < b) {
+        uint32_t mid = (a + b + 1u) / 2u;
+        if (fine_point(mid, wf, lo) <= delta)
+            a = mid;
+        else
+            b = mid - 1u;
+    }
+    return a;
+}
+
+/* Central range for the sparse outlier table ("Guide to CacheGen", Solution pillar 3:
+ * outliers go to a compact sparse table so that they do not distort the regular
+ * distribution).  The pages give no rule; the reading taken here: count the row's n
+ * deltas in the 256 intervals [p_j, p_j+1) of the fine grid p_j = fma(j, wf, lo) over
+ * [lo, hi] (the last interval open above); with the budget b = floor(n * ppm / 10^6),
+ * drop whole intervals from the bottom while the dropped count stays <= b, and from the
+ * top likewise:
+ *   j_lo = the largest j with count(intervals < j) <= b,
+ *   j_hi = the smallest j with count(intervals > j) <= b,
+ *   lo' = p_{j_lo}, hi' = p_{j_hi + 1} (hi when j_hi = 255), at most hi.
+ * Every delta below lo' lies in a dropped interval, and so does every delta above hi',
+ * so at most b deltas fall outside each end.  Nothing is narrowed when w is 0 or n is 0. */
+static void clip_range(const float *d, size_t n, uint32_t ppm, float *lo_io, float *hi_io)
+{
+    float lo = *lo_io, hi = *hi_io;
+    float wf = (hi - lo) / (float)CGO_FINE_BINS;
+    if (n == 0 || ppm == 0 || !(wf > 0.0f))
+        return;
+    uint64_t cnt[CGO_FINE_BINS];
+    memset(cnt, 0, sizeof cnt);
+    for (size_t i = 0; i < n; i++)
+        cnt[fine_index(d[i], wf, lo)] += 1;
+    uint64_t budget = ((uint64_t)n * ppm) / 1000000u;
+    uint32_t j_lo = 0, j_hi = CGO_FINE_BINS - 1u;
+    uint64_t below = 0;
+    for (uint32_t j = 1; j < CGO_FINE_BINS; j++) {
+        below += cnt[j - 1];
+        if (below > budget)
+            break;
+        j_lo = j;
+    }
+    uint64_t above = 0;
+    for (uint32_t j = CGO_FINE_BINS - 1u; j > 0; j--) {
+        above += cnt[j];
+        if (above > budget)
+            break;
+        j_hi = j - 1u;
+    }
+    float lo_c = fine_point(j_lo, wf, lo);
+    float hi_c = (j_hi == CGO_FINE_BINS - 1u) ? hi : fine_point(j_hi + 1u, wf, lo);
+    if (hi_c > hi)
+        hi_c = hi;
+    *lo_io = lo_c + 0.0f;
+    *hi_io = hi_c + 0.0f;
+}
+
 int cgo_range(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
               const uint8_t *bins, const uint16_t *X, float *lo_out, float *w_out, float *r_out,
-              uint32_t n_sink)
+              uint32_t n_sink, uint32_t outlier_ppm)
 {
     cgo_shape p = {L, H, d, S, G, Tc, bins};
     uint32_t C = H * d;
@@ -156,10 +225,11 @@ int cgo_range(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32
     for (size_t i = 0; i < total; i++)
         if (!half_is_finite(X[i]))
             return -4;
+    float *dl = (float *)malloc(sizeof(float) * (S ? S : 1));
     for (uint32_t l = 0; l < L; l++)
         for (uint32_t kv = 0; kv < 2; kv++)
             for (uint32_t c = 0; c < C; c++) {
-                int any = 0;
+                size_t n = 0;
                 float lo = 0.0f, hi = 0.0f;
                 for (uint32_t t = n_sink; t < S; t++) {
                     if (cgo_is_anchor(t, G, Tc))
@@ -167,23 +237,25 @@ int cgo_range(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32
                     uint32_t a = cgo_anchor_of(t, G, Tc);
                     float delta = cgo_half_to_float(X[kv_index(&p, l, kv, t, c)]) -
                                   cgo_half_to_float(X[kv_index(&p, l, kv, a, c)]);
-                    if (!any) {
+                    if (n == 0) {
                         lo = hi = delta;
-                        any = 1;
                     } else {
                         if (delta < lo) lo = delta;
                         if (delta > hi) hi = delta;
                     }
+                    dl[n++] = delta;
                 }
                 size_t row = ((size_t)l * 2 + kv) * C + c;
                 /* the sign of a zero bound is not meaningful: +0 + -0 = +0 fixes it */
                 lo = lo + 0.0f;
                 hi = hi + 0.0f;
+                clip_range(dl, n, outlier_ppm, &lo, &hi);
                 float w = (hi - lo) / (float)(bins[l * 2 + kv] - 1u);
                 lo_out[row] = lo;
                 w_out[row] = w;
                 r_out[row] = (w > 0.0f) ? 1.0f / w : 0.0f;
             }
+    free(dl);
     return 0;
 }
 
@@ -197,6 +269,19 @@ static uint8_t quantize_one(float delta, float lo, float r, uint32_t N)
     if (v > (float)(N - 1u))
         return (uint8_t)(N - 1u);
     return (uint8_t)v;
+}
+
+/* An element is off its grid when the clamp above changes its code: its nearest grid
+ * point is more than half a step away (floor(fma(Delta - lo, r, 0.5)) outside [0, N-1]),
+ * or the grid has zero width (r = 0: the single point lo) and does not hold it.  The
+ * tables' own cache has no off-grid element except outside a clipped central range; a
+ * cache coded with another cache's tables may have more. */
+static int off_grid(float delta, float lo, float r, uint32_t N)
+{
+    if (r == 0.0f)
+        return delta != lo;
+    float v = floorf(fmaf(delta - lo, r, 0.5f));
+    return v < 0.0f || v > (float)(N - 1u);
 }
 
 void cgo_quantize(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
@@ -525,6 +610,100 @@ void cgo_anchors(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uin
                     for (uint32_t c = 0; c < C; c++)
                         anchors_out[row * C + c] = X[kv_index(&p, l, kv, k * Tc + g * G, c)];
     }
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Sparse outlier table ("Guide to CacheGen", Solution pillar 3).  An entry holds     */
+/* one element exactly, in fp16, and is written over the decoded value.  Elements    */
+/* taken: every element of the chunks [k_begin, k_end) from token n_sink on that is   */
+/* off its grid (off_grid above): a non-anchor token whose delta (against its        */
+/* anchor's decoded value) is off the delta grid, or, with 8-bit anchors, an anchor   */
+/* token whose code is off the anchor grid.  The stream still codes the clamped       */
+/* symbol of such an element, so the streams do not change.                            */
+/* Entries are grouped like the payload: for each group (chunk, layer, K/V, block) in */
+/* container order, ascending token, then ascending lane, with                        */
+/*   key   = (t - k * Tc) << 6 | lane      (token within the chunk, lane in the block) */
+/*   value = the element's fp16 bits;                                                  */
+/* offsets[g] = first entry of group g, offsets[n_groups] = the total.                 */
+/* X is the cache, Xs the same cache with anchor tokens replaced by their decoded     */
+/* values (X itself for fp16 anchors); alo / ar are NULL for fp16 anchors.  With      */
+/* keys == NULL nothing is stored and the elements are only counted (this is the      */
+/* count of clamped elements of a container coded without the table).                 */
+/* Returns the number of elements taken.                                               */
+/* ------------------------------------------------------------------------------ */
+uint64_t cgo_outliers(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
+                      const uint8_t *bins, const uint16_t *X, const uint16_t *Xs,
+                      const float *lo, const float *r, const float *alo, const float *ar,
+                      uint32_t n_sink, uint32_t k_begin, uint32_t k_end, uint64_t *offsets,
+                      uint32_t *keys, uint16_t *values)
+{
+    cgo_shape p = {L, H, d, S, G, Tc, bins};
+    uint32_t C = H * d, NB = n_blocks(C);
+    uint64_t n = 0, g = 0;
+    for (uint32_t k = k_begin; k < k_end; k++) {
+        uint32_t t0 = k * Tc, len = cgo_chunk_len(S, Tc, k);
+        for (uint32_t l = 0; l < L; l++)
+            for (uint32_t kv = 0; kv < 2; kv++)
+                for (uint32_t b = 0; b < NB; b++, g++) {
+                    if (offsets) offsets[g] = n;
+                    uint32_t lanes = (C - b * CGO_LANES < CGO_LANES) ? C - b * CGO_LANES : CGO_LANES;
+                    for (uint32_t t = t0; t < t0 + len; t++) {
+                        if (t < n_sink)
+                            continue;
+                        for (uint32_t lane = 0; lane < lanes; lane++) {
+                            uint32_t c = b * CGO_LANES + lane;
+                            size_t row = ((size_t)l * 2 + kv) * C + c, i = kv_index(&p, l, kv, t, c);
+                            int off;
+                            if (cgo_is_anchor(t, G, Tc)) {
+                                off = alo ? off_grid(cgo_half_to_float(X[i]), alo[row], ar[row], 256u) : 0;
+                            } else {
+                                uint32_t a = cgo_anchor_of(t, G, Tc);
+                                float delta = cgo_half_to_float(Xs[i]) -
+                                              cgo_half_to_float(Xs[kv_index(&p, l, kv, a, c)]);
+                                off = off_grid(delta, lo[row], r[row], bins[l * 2 + kv]);
+                            }
+                            if (!off)
+                                continue;
+                            if (keys) {
+                                keys[n] = ((t - t0) << 6) | lane;
+                                values[n] = X[i];
+                            }
+                            n++;
+                        }
+                    }
+                }
+    }
+    if (offsets) offsets[g] = n;
+    return n;
+}
+
+/* Writes the outlier entries of chunks [k_begin, k_end) into out ([L][2][S][C] fp16).
+ * Returns 0, or -5 when the offsets or a key do not fit the container's groups. */
+int cgo_apply_outliers(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t Tc,
+                       uint32_t k_begin, uint32_t k_end, const uint64_t *offsets,
+                       const uint32_t *keys, const uint16_t *values, uint64_t n_entries,
+                       uint16_t *out)
+{
+    cgo_shape p = {L, H, d, S, 1, Tc, NULL};
+    uint32_t C = H * d, NB = n_blocks(C);
+    uint64_t g = 0;
+    for (uint32_t k = k_begin; k < k_end; k++) {
+        uint32_t t0 = k * Tc, len = cgo_chunk_len(S, Tc, k);
+        for (uint32_t l = 0; l < L; l++)
+            for (uint32_t kv = 0; kv < 2; kv++)
+                for (uint32_t b = 0; b < NB; b++, g++) {
+                    uint64_t beg = offsets[g], end = offsets[g + 1];
+                    if (end < beg || end > n_entries)
+                        return -5;
+                    for (uint64_t e = beg; e < end; e++) {
+                        uint32_t u = keys[e] >> 6, lane = keys[e] & 63u;
+                        if (u >= len || b * CGO_LANES + lane >= C)
+                            return -5;
+                        out[kv_index(&p, l, kv, t0 + u, b * CGO_LANES + lane)] = values[e];
+                    }
+                }
+    }
+    return 0;
 }
 
 /* Encodes chunks [k_begin, k_end).  Writes offsets (n_groups + 1 entries) and the

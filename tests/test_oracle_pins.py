@@ -212,6 +212,85 @@ def test_frequency_table_invariants(N, data):
         assert f[0] == T - N + 1 and (f[1:] == 1).all()
 
 
+def _freqs_by_rule(counts, N):
+    """The frequency rule written out from its statement, in Python integers: every
+    symbol gets 1 plus its share of the other T - N units, floor(c * (T - N) / n), and
+    the units left over go to the most frequent symbol, the lowest index among equals.
+    With no counts every share is 0."""
+    n = sum(counts)
+    f = [1 + (c * (T - N) // n if n else 0) for c in counts]
+    top = max(counts)
+    best = counts.index(top)
+    f[best] += T - sum(f)
+    return f
+
+
+# hand-worked cases (T = 256): counts -> frequencies, with the arithmetic
+FREQ_CASES = [
+    # n = 9, shares floor(3 * 253 / 9) = 84 -> f = 85 each, sum 255, the 1 left over
+    # goes to index 0 (three-way tie, lowest index)
+    ([3, 3, 3], [86, 85, 85]),
+    # n = 5, shares 252/5 = 50.4 -> 50, 100.8 -> 100 twice, 0 -> 0; f = 51, 101, 101, 1
+    # (sum 254); the 2 left over go to index 1 (tie between 1 and 2, lowest index)
+    ([1, 2, 2, 0], [51, 103, 101, 1]),
+    # n = 15, shares 0, 252/15 = 16.8 -> 16, 7 * 252/15 = 117.6 -> 117 twice;
+    # f = 1, 17, 118, 118 (sum 254); the 2 left over go to index 2 (tie of 2 and 3)
+    ([0, 1, 7, 7], [1, 17, 120, 118]),
+    # n = 0: every f = 1 and the 254 left over go to index 0 (all counts tie at 0)
+    ([0, 0], [255, 1]),
+    ([0, 0, 0, 0, 0], [252, 1, 1, 1, 1]),
+    # exact shares: 128 * 254 / 256 = 127, no remainder
+    ([128, 128], [128, 128]),
+    # one symbol takes everything: f = 1 + 254 = 255 and 1 for the other
+    ([0, 1000], [1, 255]),
+]
+
+
+@pytest.mark.parametrize("counts,expect", FREQ_CASES)
+def test_frequency_rule_hand_worked(counts, expect):
+    assert sum(expect) == T
+    assert _freqs_by_rule(counts, len(counts)) == expect
+    assert list(O.freqs_from_counts(counts, len(counts))) == expect
+
+
+@settings(max_examples=400, deadline=None)
+@given(N=st.integers(2, 32), data=st.data())
+def test_frequency_rule_recomputed_independently(N, data):
+    """The oracle's frequencies equal the rule recomputed in Python integers, on drawn
+    counts that include many ties (small values), zeros and large values."""
+    counts = data.draw(st.lists(st.one_of(st.integers(0, 2), st.integers(0, 50),
+                                          st.integers(0, 2 ** 40)), min_size=N, max_size=N))
+    assert list(O.freqs_from_counts(counts, N)) == _freqs_by_rule(counts, N)
+
+
+@pytest.mark.parametrize("L,S,C,G,Tc,n_sink", [(2, 70, 6, 5, 33, 0), (2, 97, 9, 4, 30, 4),
+                                                (1, 50, 3, 7, 50, 9), (2, 41, 5, 10, 16, 13),
+                                                (1, 12, 2, 1, 5, 0)])
+def test_histogram_counts_are_a_direct_count(L, S, C, G, Tc, n_sink):
+    """counts[l, kv, c, s] is the number of tokens t >= n_sink that are not anchors (by
+    the pages' windowing, restarted at every chunk) whose symbol is s, over all chunks:
+    recounted here with numpy's bincount.  Ragged last chunks, sinks that reach past the
+    first chunk's groups, and G = 1 (no symbol at all) are included."""
+    _, X = _small_data(L=L, S=S, C=C, G=G, Tc=Tc, bins=(8,) * L)
+    shp = O.Shape.make(L, 1, C, S, G, Tc, [5 + 3 * l for l in range(L)], n_sink=n_sink)
+    tab = O.build_tables(shp, X)
+    sym = O.quantize(shp, X, tab.lo, tab.r, 0, S)
+    coded = []
+    for k in range(math.ceil(S / Tc)):
+        n = min(Tc, S - k * Tc)
+        anchors, _ = _page_windows(n, G)
+        coded += [k * Tc + u for u in range(n) if u not in anchors and k * Tc + u >= n_sink]
+    for l in range(L):
+        for kv in range(2):
+            N = int(shp.bins[l * 2 + kv])
+            for c in range(C):
+                ref = np.bincount(sym[l, kv, coded, c].astype(np.int64), minlength=O.MAX_BINS)
+                assert ref.size == O.MAX_BINS
+                assert np.array_equal(tab.counts[l, kv, c], ref.astype(np.uint64)), (l, kv, c)
+                assert ref[N:].sum() == 0
+    assert tab.counts.sum() == len(coded) * 2 * L * C
+
+
 # --------------------------------------------------------------------------- rANS coder
 FREQ_SETS = [[T // 2, T // 2], [1, T - 1], [T - 1, 1], [1, 1, T - 3, 1], [60, 60, 60, 76],
              [1, 2, 3, T - 6], [7, 241, 7, 1]]
@@ -482,13 +561,15 @@ def test_sink_tokens_are_kept_in_fp16_and_left_out_of_the_tables(G):
     enc = O.encode(shp, P, tp)
     out = O.decode(shp, tp, enc)
     assert np.array_equal(out[:, :, :n_sink], P[:, :, :n_sink])
-    assert np.array_equal(tp.sinks, P[:, :, :n_sink])
+    assert np.array_equal(enc.sinks, P[:, :, :n_sink])
     ref = O.decode(shp, tx, O.encode(shp, X, tx))
     assert np.array_equal(out[:, :, n_sink:], ref[:, :, n_sink:])
+    # the sink rows belong to the container: tables built from X code P's sinks exactly
+    assert np.array_equal(O.decode(shp, tx, O.encode(shp, P, tx))[:, :, :n_sink], P[:, :, :n_sink])
     # a decode of chunk 1 alone writes no sink row
     part = O.decode(shp, tp, O.encode(shp, P, tp, 1, 2))
     assert (part[:, :, :Tc] == 0).all()
-    assert O.table_bytes(shp) == O.table_bytes(shp0) + 2 * L * n_sink * C * 2
+    assert O.table_bytes(shp) == O.table_bytes(shp0)
 
 
 def test_outlier_channel_leaves_the_other_channels_alone():
@@ -569,3 +650,276 @@ def test_8bit_anchors(G, Tc):
     assert np.array_equal(O.decode(shp16, t16, e16), out)
     assert enc.anchors.nbytes * 2 == e16.anchors.nbytes
     assert O.table_bytes(shp) == O.table_bytes(shp16) + 2 * L * C * 8
+    assert enc.clamped == 0 and e16.clamped == 0
+
+
+# --------------------------------------------------------------------------- outlier table
+def _grid_dist(D, lo, w, N):
+    """Exact distance from a delta to the nearest of the N points lo + j*w."""
+    D, lo, w = Fraction(float(D)), Fraction(float(lo)), Fraction(float(w))
+    return min(abs(D - (lo + j * w)) for j in range(N))
+
+
+def _coded_deltas(shp, Xs, l, kv, c):
+    """(t, Delta) of the coded tokens (not anchors, t >= n_sink) of one channel row."""
+    return [(t, d) for t, _, d in _deltas(shp, Xs, l, kv, c) if t >= shp.n_sink]
+
+
+@pytest.mark.parametrize("ppm", [20000, 100000, 250000])
+def test_outlier_clip_leaves_at_most_the_budget_out_at_each_end(ppm):
+    """The clipped range [lo', hi'] of every channel row lies inside the deltas' range,
+    leaves at most b = floor(n * ppm / 10^6) deltas below lo' and at most b above hi',
+    and is not narrower than the fine grid needs: one more fine interval (width
+    (hi - lo) / 256) dropped at an end would leave more than b out there."""
+    L, S, C, G, Tc = 2, 400, 7, 5, 130
+    _, X = _small_data(L=L, S=S, C=C, G=G, Tc=Tc, bins=(8, 8), seed=5)
+    shp = O.Shape.make(L, 1, C, S, G, Tc, (16, 4), n_sink=3, outlier_ppm=ppm)
+    tab = O.build_tables(shp, X)
+    narrowed = 0
+    for l in range(L):
+        for kv in range(2):
+            N = int(shp.bins[l * 2 + kv])
+            for c in range(C):
+                d = np.array([x for _, x in _coded_deltas(shp, X, l, kv, c)], np.float64)
+                n, b = d.size, d.size * ppm // 10 ** 6
+                lo, hi = d.min(), d.max()
+                lo_c = float(tab.lo[l, kv, c])
+                hi_c = lo_c + float(tab.w[l, kv, c]) * (N - 1)
+                assert lo <= lo_c <= hi and lo_c <= hi_c <= hi * (1 + 2 ** -20) + 2 ** -30
+                assert (d < lo_c).sum() <= b
+                assert (d > hi_c * (1 + 2 ** -20) + 2 ** -30).sum() <= b
+                wf = (hi - lo) / 256
+                if lo_c + 2.01 * wf < hi_c:
+                    assert (d < lo_c + 1.001 * wf).sum() > b
+                if hi_c - 2.01 * wf > lo_c:
+                    assert (d > hi_c - 1.001 * wf).sum() > b
+                narrowed += (hi_c - lo_c) < 0.9 * (hi - lo)
+    assert narrowed > 0
+
+
+def test_outlier_table_off_or_empty_budget_changes_nothing():
+    """ppm = 0, or a budget that rounds down to 0 deltas, keeps the full range: tables,
+    streams and decoded values are those of the plain codec."""
+    shp0, X = _small_data(L=2, S=120, C=6, G=5, Tc=60, bins=(8, 4))
+    t0 = O.build_tables(shp0, X)
+    e0 = O.encode(shp0, X, t0)
+    shp = O.Shape.make(2, 1, 6, 120, 5, 60, (8, 4), outlier_ppm=1000)  # n ~ 96: b = 0
+    t1 = O.build_tables(shp, X)
+    for name in ("lo", "w", "r", "freqs"):
+        assert np.array_equal(getattr(t0, name), getattr(t1, name)), name
+    e1 = O.encode(shp, X, t1)
+    assert np.array_equal(e0.payload, e1.payload) and e1.n_outliers == 0 and e0.clamped == 0
+    assert np.array_equal(O.decode(shp0, t0, e0), O.decode(shp, t1, e1))
+
+
+@pytest.mark.parametrize("anchor_bits", [16, 8])
+def test_outlier_entries_are_exactly_the_off_grid_elements(anchor_bits):
+    """Every element whose nearest grid point is more than half a step away (exact
+    rationals, up to 2^-20 relative at the boundary) has an entry, and no other element
+    has one; entries are grouped like the payload (chunk, layer, K/V, 64-channel block),
+    in ascending token then lane, and hold the element's fp16 bits; the decode returns
+    them exactly and every other element within half a step of the clipped grid."""
+    L, S, C, G, Tc, ppm = 2, 300, 70, 10, 128, 30000
+    _, X = _small_data(L=L, S=S, C=C, G=G, Tc=Tc, bins=(8, 8), seed=7)
+    shp = O.Shape.make(L, 1, C, S, G, Tc, (8, 32), n_sink=2, anchor_bits=anchor_bits,
+                       outlier_ppm=ppm)
+    tab = O.build_tables(shp, X)
+    enc = O.encode(shp, X, tab)
+    Xs = O.snap_anchors(shp, X, tab)
+    expect = set()
+    for l in range(L):
+        for kv in range(2):
+            N = int(shp.bins[l * 2 + kv])
+            for c in range(C):
+                w = Fraction(float(tab.w[l, kv, c]))
+                for t, D in _coded_deltas(shp, Xs, l, kv, c):
+                    dist = _grid_dist(D, tab.lo[l, kv, c], tab.w[l, kv, c], N)
+                    if dist > w / 2 * (1 + Fraction(1, 2 ** 20)) or (w == 0 and dist > 0):
+                        expect.add((l, kv, t, c))
+                    elif dist >= w / 2 * (1 - Fraction(1, 2 ** 20)) and w > 0:
+                        expect.add((l, kv, t, c, "edge"))
+    got = []
+    NB = -(-C // O.LANES)
+    g = 0
+    for k in range(shp.n_chunks):
+        for l in range(L):
+            for kv in range(2):
+                for b in range(NB):
+                    beg, end = int(enc.out_offsets[g]), int(enc.out_offsets[g + 1])
+                    keys = [int(v) for v in enc.out_keys[beg:end]]
+                    assert keys == sorted(keys)
+                    for e in range(beg, end):
+                        t = k * Tc + (int(enc.out_keys[e]) >> 6)
+                        c = b * O.LANES + (int(enc.out_keys[e]) & 63)
+                        assert enc.out_values[e] == X[l, kv, t, c]
+                        got.append((l, kv, t, c))
+                    g += 1
+    assert g == len(enc.out_offsets) - 1 and int(enc.out_offsets[-1]) == len(got)
+    hard = {e for e in expect if len(e) == 4}
+    edge = {e[:4] for e in expect if len(e) == 5}
+    assert hard <= set(got) and set(got) <= hard | edge
+    assert len(got) > 0
+    out = O.decode(shp, tab, enc)
+    for (l, kv, t, c) in got:
+        assert out[l, kv, t, c] == X[l, kv, t, c]
+    # the rest within half a step of the clipped grid (anchors exact with fp16 anchors)
+    xs, ys = X.view(np.float16).astype(np.float64), out.view(np.float16).astype(np.float64)
+    wv = tab.w.astype(np.float64)[:, :, None, :]
+    err = np.abs(xs - ys)
+    if anchor_bits == 8:
+        err[:, :, [t for t in range(S) if (t % Tc) % G == 0]] = 0
+    assert (err <= wv / 2 * (1 + 2 ** -20) + np.abs(ys) * 2 ** -11 + 1e-30).all()
+    # without the table the same elements are coded clamped and only counted
+    shp_off = O.Shape.make(L, 1, C, S, G, Tc, (8, 32), n_sink=2, anchor_bits=anchor_bits)
+    tab_off = O.Tables(tab.lo, tab.w, tab.r, tab.counts, tab.freqs, tab.alo, tab.aw, tab.ar)
+    e_off = O.encode(shp_off, X, tab_off)
+    assert e_off.clamped == len(got) and e_off.n_outliers == 0
+    assert np.array_equal(e_off.payload, enc.payload)
+
+
+@pytest.mark.parametrize("anchor_bits", [16, 8])
+def test_another_cache_is_coded_within_the_bound_with_the_table(anchor_bits):
+    """Tables profiled on one cache ("Guide to CacheGen", Solution pillar 3: calibration
+    tables) coding another: with the outlier table, every element the tables' grids
+    cannot hold within half a step -- including, with 8-bit anchors, anchors beyond
+    their grid -- is stored exactly; without it those elements are counted as clamped.
+    Both counts equal a brute-force count over the new cache."""
+    L, S, C, G, Tc = 1, 200, 9, 5, 100
+    _, X = _small_data(L=L, S=S, C=C, G=G, Tc=Tc, bins=(8,), seed=1)
+    _, Y = _small_data(L=L, S=S, C=C, G=G, Tc=Tc, bins=(8,), seed=2)
+    Y = Y.copy()
+    Y[0, 0, 50, 3] = np.float16(2000.0).view(np.uint16)     # an anchor (t = 50) far out
+    Y[0, 1, 57, 4] = np.float16(-3000.0).view(np.uint16)    # a non-anchor far out
+    on = O.Shape.make(L, 1, C, S, G, Tc, (8,), anchor_bits=anchor_bits, outlier_ppm=5000)
+    off = O.Shape.make(L, 1, C, S, G, Tc, (8,), anchor_bits=anchor_bits)
+    t_on, t_off = O.build_tables(on, X), O.build_tables(off, X)
+    e_on, e_off = O.encode(on, Y, t_on), O.encode(off, Y, t_off)
+    Ys_on, Ys_off = O.snap_anchors(on, Y, t_on), O.snap_anchors(off, Y, t_off)
+
+    def brute(shp, tab, Ys):
+        n = 0
+        for kv in range(2):
+            for c in range(C):
+                w = Fraction(float(tab.w[0, kv, c]))
+                for t, D in _coded_deltas(shp, Ys, 0, kv, c):
+                    dist = _grid_dist(D, tab.lo[0, kv, c], tab.w[0, kv, c], 8)
+                    n += dist > w / 2 * (1 + Fraction(1, 2 ** 20)) or (w == 0 and dist > 0)
+                if anchor_bits == 8:
+                    aw = Fraction(float(tab.aw[0, kv, c]))
+                    for t in range(0, S, G):
+                        x = Fraction(float(Y[0, kv, t, c].view(np.float16)))
+                        a = _grid_dist(x, tab.alo[0, kv, c], tab.aw[0, kv, c], 256)
+                        n += a > aw / 2 * (1 + Fraction(1, 2 ** 20))
+        return n
+
+    assert e_on.n_outliers == brute(on, t_on, Ys_on) and e_on.n_outliers >= 2
+    assert e_off.clamped == brute(off, t_off, Ys_off) and e_off.clamped >= 2
+    out = O.decode(on, t_on, e_on)
+    assert out[0, 1, 57, 4] == Y[0, 1, 57, 4] and out[0, 0, 50, 3] == Y[0, 0, 50, 3]
+    ys, xs = out.view(np.float16).astype(np.float64), Y.view(np.float16).astype(np.float64)
+    tol = t_on.w.astype(np.float64)[:, :, None, :] / 2 * (1 + 2 ** -20) + np.abs(ys) * 2 ** -11
+    if anchor_bits == 8:
+        tol[:, :, ::G] = t_on.aw.astype(np.float64)[:, :, None, :] / 2 * (1 + 2 ** -20) + np.abs(ys[:, :, ::G]) * 2 ** -11
+    assert (np.abs(xs - ys) <= tol + 1e-30).all()
+
+
+def test_outlier_brute_force_tiny():
+    """L=1, S=30, C=2, G=3, N=4, 10% budget: the clipped range, the entries and the
+    decode worked out from exact rationals and a sort."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_t(2, size=(1, 2, 30, 2)) * 2
+    X = np.ascontiguousarray(x.astype(np.float16).view(np.uint16))
+    shp = O.Shape.make(1, 1, 2, 30, 3, 30, [4], outlier_ppm=100000)
+    tab = O.build_tables(shp, X)
+    enc = O.encode(shp, X, tab)
+    out = O.decode(shp, tab, enc)
+    xf = X.view(np.float16)
+    n_entries = 0
+    for kv in range(2):
+        for c in range(2):
+            D = {t: Fraction(float(np.float32(np.float32(xf[0, kv, t, c]) -
+                                              np.float32(xf[0, kv, t - t % 3, c]))))
+                 for t in range(30) if t % 3}
+            vals = sorted(D.values())
+            n, b = len(vals), len(vals) // 10
+            lo_c, w = Fraction(float(tab.lo[0, kv, c])), Fraction(float(tab.w[0, kv, c]))
+            hi_c = lo_c + 3 * w
+            assert sum(v < lo_c for v in vals) <= b and sum(v > hi_c * (1 + Fraction(1, 2 ** 20)) for v in vals) <= b
+            for t, d in D.items():
+                dist = min(abs(d - (lo_c + j * w)) for j in range(4))
+                if dist > w / 2 * (1 + Fraction(1, 2 ** 20)):
+                    n_entries += 1
+                    assert out[0, kv, t, c] == X[0, kv, t, c]
+                else:
+                    y = Fraction(float(xf[0, kv, t - t % 3, c])) + lo_c + \
+                        min(range(4), key=lambda j: (abs(d - (lo_c + j * w)), -j)) * w
+                    got = Fraction(float(out[0, kv, t, c].view(np.float16)))
+                    assert abs(got - y) <= abs(y) * Fraction(1, 2 ** 10) + Fraction(1, 2 ** 20)
+    assert n_entries == enc.n_outliers and n_entries > 0
+
+
+# --------------------------------------------------------------------------- stored bytes
+def _parse_header(buf):
+    import struct
+    u32 = struct.unpack_from("<14I", buf, 0)
+    u64 = struct.unpack_from("<13Q", buf, 56)
+    return dict(zip(O.HEADER_U32, u32)) | dict(zip(O.HEADER_U64, u64))
+
+
+@pytest.mark.parametrize("ppm,anchor_bits,n_sink,rng", [(0, 16, 0, None), (30000, 16, 5, None),
+                                                         (30000, 8, 5, (1, 3)), (0, 8, 200, (0, 2))])
+def test_container_and_table_bytes_follow_their_layout(ppm, anchor_bits, n_sink, rng):
+    """The stored bytes: every section 256-byte aligned after a 160-byte header, in the
+    order offsets, anchors, sinks, outlier offsets / keys / values, payload, with the
+    sizes their arrays give, zero bytes between sections and 1 KiB of zeros after the
+    payload; the tables' 56-byte header, bins, lo, w (alo, aw), then N frequencies per
+    channel row."""
+    L, S, C, G, Tc = 2, 260, 70, 10, 64
+    _, X = _small_data(L=L, S=S, C=C, G=G, Tc=Tc, bins=(8, 8), seed=9)
+    shp = O.Shape.make(L, 1, C, S, G, Tc, (8, 5), n_sink=n_sink, anchor_bits=anchor_bits,
+                       outlier_ppm=ppm)
+    tab = O.build_tables(shp, X)
+    kb, ke = rng if rng else (0, shp.n_chunks)
+    enc = O.encode(shp, X, tab, kb, ke)
+    buf = O.container_bytes(shp, enc)
+    h = _parse_header(buf)
+    assert h["magic"] == 0x31474B43 and h["version"] == 3 and h["total_bytes"] == len(buf)
+    assert (h["L"], h["H_kv"], h["d"], h["S"], h["group"], h["chunk"]) == (L, 1, C, S, G, Tc)
+    assert (h["chunk_begin"], h["chunk_end"], h["n_blocks"]) == (kb, ke, 2)
+    ng = (ke - kb) * L * 2 * 2
+    sa, sb = kb * Tc, max(kb * Tc, min(ke * Tc, S, n_sink))
+    secs = [("offsets_offset", (ng + 1) * 8),
+            ("anchors_offset", enc.anchors.nbytes),
+            ("sinks_offset", 2 * L * (sb - sa) * C * 2),
+            ("outliers_offset", (ng + 1) * 8 if ppm else 0),
+            ("outlier_keys_offset", enc.n_outliers * 4),
+            ("outlier_values_offset", enc.n_outliers * 2),
+            ("payload_offset", enc.payload.size * 2)]
+    end = 160
+    for name, size in secs:
+        off = h[name]
+        assert off % 256 == 0 and off >= end and off - end < 256 and not any(buf[end:off])
+        end = off + size
+    assert h["anchors_bytes"] == enc.anchors.nbytes and h["n_sink"] == sb - sa
+    assert h["payload_words"] == enc.payload.size and h["n_outliers"] == enc.n_outliers
+    assert len(buf) == end + 1024 and not any(buf[end:])
+    p = h["payload_offset"]
+    assert np.array_equal(np.frombuffer(buf, np.uint16, enc.payload.size, p), enc.payload)
+    assert np.array_equal(np.frombuffer(buf, np.uint64, ng + 1, h["offsets_offset"]), enc.offsets)
+    if sb > sa:
+        got = np.frombuffer(buf, np.uint16, 2 * L * (sb - sa) * C, h["sinks_offset"])
+        assert np.array_equal(got.reshape(L, 2, sb - sa, C), X[:, :, sa:sb])
+    tb = O.tables_bytes(shp, tab)
+    assert len(tb) == O.table_bytes(shp)
+    import struct
+    t32 = struct.unpack_from("<12I", tb, 0)
+    assert t32[:2] == (0x31544743, 1) and t32[2:11] == (L, 1, C, S, G, Tc, n_sink, anchor_bits, ppm)
+    assert struct.unpack_from("<Q", tb, 48)[0] == len(tb)
+    off = 56 + 4
+    assert list(tb[56:56 + 2 * L]) == list(shp.bins)
+    lo = np.frombuffer(tb, np.float32, 2 * L * C, off)
+    assert np.array_equal(lo, tab.lo.reshape(-1))
+    off += 2 * L * C * 4 * (4 if anchor_bits == 8 else 2)
+    fr = np.frombuffer(tb, np.uint16, (len(tb) - off) // 2, off)
+    assert fr.size == C * sum(int(b) for b in shp.bins)
+    assert int(fr[:8].astype(np.int64).sum()) == T   # the first channel row's table
