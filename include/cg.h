@@ -63,47 +63,94 @@ typedef struct cg_params {
     const uint8_t *bins;     /* [L], bins[l] = number of quantization levels of layer l */
     const uint8_t *bins_v;   /* [L] or NULL: levels of the V rows of layer l (NULL: bins[l]) */
     uint32_t n_sink;         /* first n_sink tokens of the sequence (attention sinks, "Guide to
-                                CacheGen", Best Practices) kept as an fp16 copy in the tables:
-                                left out of ranges and histograms, written back exactly by
-                                every decode; 0 = none; values above S act as S */
+                                CacheGen", Best Practices) kept in fp16: left out of ranges
+                                and histograms, stored by cg_encode in every container that
+                                holds them and written back exactly by every decode; 0 = none;
+                                values above S act as S */
     uint32_t anchor_bits;    /* 0 or 16: anchors stored as fp16.  8: each anchor stored as a
                                 code on a 256-level grid of its (layer, K/V, channel) row
                                 ("Guide to CacheGen", Solution pillar 2: anchors quantized
                                 with high precision), min to max of the row's anchor tokens;
                                 the decoded anchor is the fp16 grid value and the deltas are
                                 taken against it */
+    uint32_t outlier_ppm;    /* 0: no outlier table.  1 .. 250000: sparse outlier table
+                                ("Guide to CacheGen", Solution pillar 3: outliers kept in a
+                                compact sparse table so that they do not distort the regular
+                                distribution).  Each channel row's grid spans a central range
+                                that leaves at most floor(n * outlier_ppm / 10^6) of its n
+                                deltas out at each end (chosen on 256 equal intervals of the
+                                full range), and every element off its grid is stored
+                                exactly in fp16 in the container */
 } cg_params;
 
 typedef struct cg_tables cg_tables; /* per-channel ranges and frequency tables (device) */
 typedef struct cg_blob cg_blob;     /* one encoded container (device) */
 
 /*
- * Container layout (one device buffer, sections 256-byte aligned, little endian):
- *   header     cg_container_header
+ * Container (version 3): one buffer, little endian, every section 256-byte aligned
+ * relative to the first byte, the bytes between sections zero:
+ *   header     cg_container_header (160 bytes)
  *   offsets    uint64[n_groups + 1]: first payload word of every group, then the total.
  *              Groups are (chunk, layer, K/V, block) in row-major order over chunks
  *              [chunk_begin, chunk_end); block b holds channels 64b .. 64b+63.
  *   anchors    fp16 (uint8 grid codes with 8-bit anchors), for each chunk:
  *              [L][2][ceil(len_k / group)][C]
- *   payload    uint16 words.  A group's words are the words of its (up to) 64 rANS
- *              streams in the order 64 decoders running in lockstep read them: the two
- *              state words of every lane in lane order, then after each symbol step the
- *              next word of every lane whose state fell below 2^16, in lane order.
- * Header version 2 (rANS, 8-bit frequencies); version 1 containers are not readable.
- * Tables are stored separately; cg_tables_info.stored_bytes is their size.
+ *   sinks      fp16 [L][2][n_sink][C]: tokens chunk_begin * chunk .. + n_sink, the
+ *              attention sinks among the container's tokens, copied from the encoded cache
+ *   outliers   (outlier_ppm > 0 only) uint64[n_groups + 1] first entry of every group,
+ *              then the total; then uint32 keys [n_outliers] (token within the chunk << 6
+ *              | lane), then uint16 fp16 values [n_outliers] (each its own section).
+ *              A group's entries are in ascending key order.
+ *   payload    uint16 words, then 1 KiB of zeros.  A group's words are the words of its
+ *              (up to) 64 rANS streams in the order 64 decoders running in lockstep read
+ *              them: the two state words of every lane in lane order, then after each
+ *              symbol step the next word of every lane whose state fell below 2^16, in
+ *              lane order.
+ * Every section offset follows from the fields before it: offsets at 256, then each
+ * section at the next multiple of 256 after the previous one's end; the outlier sections
+ * are empty (all three offsets equal) when outlier_ppm is 0.  total_bytes =
+ * payload_offset + 2 * payload_words + 1024.
+ * Tables are stored separately (cg_tables_serialize); the compression ratio counts both.
  */
 typedef struct cg_container_header {
-    uint32_t magic, version;
+    uint32_t magic, version;          /* CG_CONTAINER_MAGIC, CG_CONTAINER_VERSION */
     uint32_t L, H_kv, d, S, group, chunk;
     uint32_t chunk_begin, chunk_end;
-    uint32_t n_blocks;
-    uint32_t reserved;        /* bits per stored anchor element: 0 = fp16, 8 = grid codes */
+    uint32_t n_blocks;                /* ceil(H_kv * d / 64) */
+    uint32_t anchor_bits;             /* 16: fp16 anchors, 8: grid codes */
+    uint32_t n_sink;                  /* sink tokens stored in this container */
+    uint32_t outlier_ppm;             /* the tables' setting; 0: no outlier sections */
     uint64_t n_groups;
-    uint64_t offsets_offset;  /* byte offset of the offsets section */
+    uint64_t offsets_offset;
     uint64_t anchors_offset, anchors_bytes;
+    uint64_t sinks_offset;
+    uint64_t outliers_offset, outlier_keys_offset, outlier_values_offset, n_outliers;
+    uint64_t clamped;                 /* elements off their grid coded clamped (no outlier
+                                         table): 0 for the cache the tables were built from */
     uint64_t payload_offset, payload_words;
     uint64_t total_bytes;
 } cg_container_header;
+
+#define CG_CONTAINER_VERSION 3u
+#define CG_TABLES_MAGIC 0x31544743u  /* "CGT1" */
+#define CG_TABLES_VERSION 1u
+
+/*
+ * Stored tables (cg_tables_serialize / cg_tables_import), little endian, no padding
+ * except after bins:
+ *   header   cg_tables_header (56 bytes)
+ *   bins     uint8 [L][2] (level count of every (layer, K/V) row), zero-padded to 4 bytes
+ *   lo, w    float [L][2][C] each: the grid of every channel row
+ *   alo, aw  float [L][2][C] each, with 8-bit anchors only: the anchor grid
+ *   freqs    uint16: for each (layer, K/V) row and channel, its N frequencies (sum 256)
+ * The reciprocals r = 1/w (and 1/aw) are recomputed on import, 0 where the width is 0.
+ */
+typedef struct cg_tables_header {
+    uint32_t magic, version;          /* CG_TABLES_MAGIC, CG_TABLES_VERSION */
+    uint32_t L, H_kv, d, S, group, chunk;
+    uint32_t n_sink, anchor_bits, outlier_ppm, reserved;
+    uint64_t total_bytes;
+} cg_tables_header;
 
 typedef struct cg_blob_info {
     const void *data;             /* device pointer to the container */
@@ -112,43 +159,57 @@ typedef struct cg_blob_info {
 
 typedef struct cg_tables_info {
     uint32_t L, H_kv, d, S, group, chunk;
-    uint64_t stored_bytes;        /* lo, w (4 B each per row) + 2 B per frequency + bins
-                                     + the fp16 sink rows (2 B per sink token per channel row) */
+    uint64_t stored_bytes;        /* size of the stored tables (cg_tables_serialize) */
 } cg_tables_info;
 
 /*
- * Builds the per-(layer, K/V, channel) tables from the whole cache: the range of the
- * anchor deltas, the bin width, and a frequency table of the quantized deltas over all
- * chunks (T = 256, every symbol >= 1).
- *   kv_dev: fp16 [L][2][S][C], read only.
+ * Builds the per-(layer, K/V, channel) tables from the whole cache ("Guide to CacheGen",
+ * Solution pillar 3: tables of empirical symbol frequencies from calibration profiling,
+ * kept per layer and channel as in the gptget.net summary's Deep Analysis): the range of
+ * the anchor deltas (narrowed to a central range with the outlier table), the bin width
+ * from the layer's level count (pillar 1), and a frequency table of the quantized deltas
+ * over all chunks (T = 256, every symbol >= 1).
+ *   params: shape and coding parameters, read during the call only.
+ *   kv_dev: fp16 [L][2][S][C] on the current device, read only.
  *   *out:   receives a new handle on success, untouched on error.
  * Synchronises `hip_stream` once (to report CG_E_NONFINITE).
- * Errors: CG_E_INVAL, CG_E_NOMEM, CG_E_HIP, CG_E_NONFINITE.
+ * Errors: CG_E_INVAL (null pointer, a zero dimension, a limit exceeded, bins outside
+ * [2, 32], anchor_bits not 0 / 8 / 16, outlier_ppm > 250000), CG_E_NOMEM, CG_E_HIP,
+ * CG_E_NONFINITE.
  */
 int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream,
                  cg_tables **out);
 
 /*
- * Encodes chunks [chunk_begin, chunk_end) of kv_dev (the cache the tables were built
- * from, or any cache of the same shape) into a new container.
+ * Encodes chunks [chunk_begin, chunk_end) of kv_dev into a new container: the anchors,
+ * the sink rows among those tokens, the entropy-coded delta symbols ("Guide to CacheGen",
+ * Solution pillars 2-3 and Implementation Step 2; the summary's Methodology: the cache is
+ * encoded into compact bitstreams, chunk by chunk) and, with the outlier table, the
+ * entries of every element off its grid.
+ *   kv_dev: fp16 [L][2][S][C], read only: the cache the tables were built from, or
+ *           another cache of the same shape coded with these tables (calibration
+ *           tables).  Elements of another cache that the tables' grids do not hold
+ *           within half a step are stored exactly with the outlier table; without it
+ *           they are coded clamped and counted in the header's `clamped`.
  * Synchronises `hip_stream` (the payload size is data dependent); the container is
  * complete when the call returns.
- * Errors: CG_E_INVAL (bad range), CG_E_NOMEM, CG_E_HIP.
+ * Errors: CG_E_INVAL (null pointer, bad chunk range), CG_E_NOMEM, CG_E_HIP.
  */
 int cg_encode(const cg_tables *tables, const void *kv_dev, uint32_t chunk_begin,
               uint32_t chunk_end, void *hip_stream, cg_blob **out);
 
 /*
- * Decodes a container into kv_out_dev (fp16 [L][2][S][C]); writes exactly the tokens
- * of chunks [chunk_begin, chunk_end), leaves every other token untouched.  Sink tokens
- * (cg_params.n_sink) among them are written from the tables' fp16 copy, after the
- * decoded rows, on the same stream.
+ * Decodes a container into kv_out_dev (fp16 [L][2][S][C]) ("Guide to CacheGen",
+ * Implementation Step 1 dequantize_tensor and Step 2 decode_sequence; the summary's
+ * Methodology: GPU decoding of the received bitstreams).  Writes exactly the tokens of
+ * chunks [chunk_begin, chunk_end) and leaves every other token untouched: the decoded
+ * rows, then, on the same stream, the container's sink rows and outlier entries.
  *   container_dev: NULL to decode the blob's own copy, or a device buffer holding the
  *                  same container bytes (e.g. staged from pinned host memory).  Its
- *                  payload and offsets are not trusted: damaged bytes decode to wrong
- *                  values but every read stays inside the container.
+ *                  payload, offsets and outlier entries are not trusted: damaged bytes
+ *                  decode to wrong values but every read and write stays in bounds.
  * Fully asynchronous on hip_stream.  Errors: CG_E_INVAL, CG_E_CORRUPT (blob and
- * tables disagree on the shape), CG_E_HIP.
+ * tables disagree on the shape or settings), CG_E_HIP.
  */
 int cg_decode(const cg_tables *tables, const cg_blob *blob, const void *container_dev,
               void *kv_out_dev, void *hip_stream);
@@ -162,9 +223,9 @@ int cg_decode(const cg_tables *tables, const cg_blob *blob, const void *containe
  *   block_table_dev: int32 [ceil(S / page_tokens)], device: token t of every (layer, K/V)
  *                    goes to page block_table[t / page_tokens], row t % page_tokens.
  *   page_tokens:     a power of two; num_pages * page_tokens * H_kv * d * 2 < 2^32.
- * Writes the tokens of the blob's chunks (sink tokens as in cg_decode); a block whose
- * page id is negative or >= num_pages is skipped (none of its rows is written), other
- * pages are untouched.
+ * Writes the tokens of the blob's chunks (sink rows and outlier entries as in
+ * cg_decode); a block whose page id is negative or >= num_pages is skipped (none of its
+ * rows is written), other pages are untouched.
  * container_dev as in cg_decode.  Fully asynchronous on hip_stream.  Errors:
  * CG_E_INVAL, CG_E_CORRUPT, CG_E_HIP.
  */
@@ -172,8 +233,48 @@ int cg_decode_paged(const cg_tables *tables, const cg_blob *blob, const void *co
                     void *pages_dev, const int32_t *block_table_dev, uint32_t page_tokens,
                     uint32_t num_pages, void *hip_stream);
 
-/* Releases a cg_tables* or cg_blob* and its device memory.  NULL is a no-op. */
+/* Releases a cg_tables* or cg_blob* and its device memory ("Guide to CacheGen",
+ * Implementation: the compressor / decompressor objects own their buffers).  NULL is a
+ * no-op; any other pointer must be a live handle of this library. */
 void cg_free(void *handle);
+
+/* ----------------------------------------------------------------------------------
+ * Stored form.  Tables and containers are written to host memory, kept or sent
+ * elsewhere, and imported by a receiver that decodes them ("Guide to CacheGen", Problem:
+ * caches offloaded to RAM, SSD or remote storage; the gptget.net summary, Methodology:
+ * encoded bitstreams streamed over the network to the serving GPU).
+ * ---------------------------------------------------------------------------------- */
+
+/* Writes the stored tables (layout above) to host_dst if capacity allows; *size_out
+ * (if not NULL) receives their size either way.  Synchronous.
+ * Errors: CG_E_INVAL (null tables, host_dst NULL or capacity too small with a non-NULL
+ * host_dst), CG_E_HIP. */
+int cg_tables_serialize(const cg_tables *tables, void *host_dst, uint64_t capacity,
+                        uint64_t *size_out);
+
+/* Checks stored tables in host memory without touching a device: header, sizes, level
+ * counts, finite grids with widths >= 0, every frequency table >= 1 per symbol and
+ * summing to 256.  *header_out (if not NULL) receives the header.  Returns CG_OK or
+ * CG_E_CORRUPT (CG_E_INVAL for null bytes). */
+int cg_tables_check(const void *host_bytes, uint64_t nbytes, cg_tables_header *header_out);
+
+/* Checks, then builds a tables handle on the current device from stored tables.
+ * Synchronous.  Errors: CG_E_INVAL, CG_E_CORRUPT, CG_E_NOMEM, CG_E_HIP. */
+int cg_tables_import(const void *host_bytes, uint64_t nbytes, cg_tables **out);
+
+/* Checks a container in host memory without touching a device: magic, version, shape
+ * limits, every section offset against the layout, group offsets starting at 0,
+ * non-decreasing and ending at payload_words, outlier offsets likewise and every key
+ * inside its group's chunk and block.  *header_out (if not NULL) receives the header.
+ * Returns CG_OK or CG_E_CORRUPT (CG_E_INVAL for null bytes). */
+int cg_container_check(const void *host_bytes, uint64_t nbytes, cg_container_header *header_out);
+
+/* Checks a container against itself (cg_container_check) and against the tables (shape,
+ * anchor width, outlier setting, sink count), then copies it to the tables' device as a
+ * new blob.  Synchronous on hip_stream.  Errors: CG_E_INVAL, CG_E_CORRUPT, CG_E_NOMEM,
+ * CG_E_HIP. */
+int cg_blob_import(const cg_tables *tables, const void *host_bytes, uint64_t nbytes,
+                   void *hip_stream, cg_blob **out);
 
 /* ----------------------------------------------------------------------------------
  * Streamed decode.  Chunk containers arrive from host memory while earlier chunks
@@ -251,8 +352,8 @@ int cg_decode_symbols(const cg_tables *tables, const cg_blob *blob, const void *
                       void *sym_dev, void *hip_stream);
 
 /* Dequantize + anchor-add alone: symbols [L][2][S][C] and the container's anchors to
- * fp16 [L][2][S][C] for the container's tokens, sink tokens as in cg_decode.
- * Asynchronous. */
+ * fp16 [L][2][S][C] for the container's tokens, then its sink rows and outlier entries
+ * as in cg_decode.  Asynchronous. */
 int cg_dequantize(const cg_tables *tables, const cg_blob *blob, const void *container_dev,
                   const void *sym_dev, void *kv_out_dev, void *hip_stream);
 

@@ -33,16 +33,24 @@ class Params(ctypes.Structure):
     _fields_ = [("L", ctypes.c_uint32), ("H_kv", ctypes.c_uint32), ("d", ctypes.c_uint32),
                 ("S", ctypes.c_uint32), ("group", ctypes.c_uint32), ("chunk", ctypes.c_uint32),
                 ("bins", ctypes.POINTER(ctypes.c_uint8)), ("bins_v", ctypes.POINTER(ctypes.c_uint8)),
-                ("n_sink", ctypes.c_uint32), ("anchor_bits", ctypes.c_uint32)]
+                ("n_sink", ctypes.c_uint32), ("anchor_bits", ctypes.c_uint32),
+                ("outlier_ppm", ctypes.c_uint32)]
 
 
 class ContainerHeader(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint32) for n in
                 ("magic", "version", "L", "H_kv", "d", "S", "group", "chunk", "chunk_begin",
-                 "chunk_end", "n_blocks", "reserved")] + \
+                 "chunk_end", "n_blocks", "anchor_bits", "n_sink", "outlier_ppm")] + \
                [(n, ctypes.c_uint64) for n in
-                ("n_groups", "offsets_offset", "anchors_offset", "anchors_bytes",
-                 "payload_offset", "payload_words", "total_bytes")]
+                ("n_groups", "offsets_offset", "anchors_offset", "anchors_bytes", "sinks_offset",
+                 "outliers_offset", "outlier_keys_offset", "outlier_values_offset",
+                 "n_outliers", "clamped", "payload_offset", "payload_words", "total_bytes")]
+
+
+class TablesHeader(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in
+                ("magic", "version", "L", "H_kv", "d", "S", "group", "chunk", "n_sink",
+                 "anchor_bits", "outlier_ppm", "reserved")] + [("total_bytes", ctypes.c_uint64)]
 
 
 class BlobInfo(ctypes.Structure):
@@ -67,7 +75,8 @@ class StreamStats(ctypes.Structure):
 EXPORTED = ["cg_build_cdf", "cg_encode", "cg_decode", "cg_free", "cg_last_error",
             "cg_tables_export", "cg_tables_get_info", "cg_blob_get_info", "cg_blob_read",
             "cg_quantize", "cg_decode_symbols", "cg_dequantize", "cg_stream_decode",
-            "cg_decode_paged"]
+            "cg_decode_paged", "cg_tables_serialize", "cg_tables_check", "cg_tables_import",
+            "cg_container_check", "cg_blob_import"]
 
 _lib = None
 
@@ -97,6 +106,11 @@ def load() -> ctypes.CDLL:
         "cg_dequantize": [vp, vp, vp, vp, vp, vp],
         "cg_stream_decode": [ctypes.POINTER(StreamItem), u32, vp, u64, u32, vp, vp, vp,
                              ctypes.POINTER(StreamStats)],
+        "cg_tables_serialize": [vp, vp, u64, ctypes.POINTER(ctypes.c_uint64)],
+        "cg_tables_check": [vp, u64, ctypes.POINTER(TablesHeader)],
+        "cg_tables_import": [vp, u64, pp],
+        "cg_container_check": [vp, u64, ctypes.POINTER(ContainerHeader)],
+        "cg_blob_import": [vp, vp, u64, vp, pp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -131,10 +145,11 @@ class Tables:
     """Per-(layer, K/V, channel) ranges and frequency tables, owned by libcg."""
 
     def __init__(self, handle: ctypes.c_void_p, L, H_kv, d, S, group, chunk, bins, device,
-                 bins_v=None, n_sink=0, anchor_bits=16):
+                 bins_v=None, n_sink=0, anchor_bits=16, outlier_ppm=0):
         self.handle = handle
         self.n_sink = min(int(n_sink), S)
         self.anchor_bits = int(anchor_bits)
+        self.outlier_ppm = int(outlier_ppm)
         self.L, self.H_kv, self.d, self.S = L, H_kv, d, S
         self.group, self.chunk = group, chunk
         self.bins = tuple(int(b) for b in bins)             # K rows (and V rows without bins_v)
@@ -175,6 +190,14 @@ class Tables:
         _check(load().cg_tables_export(self.handle, lo.ctypes.data, w.ctypes.data,
                                        r.ctypes.data, fr.ctypes.data))
         return {"lo": lo, "w": w, "r": r, "freqs": fr}
+
+    def serialize(self) -> bytes:
+        """The stored tables (include/cg.h layout)."""
+        n = ctypes.c_uint64()
+        _check(load().cg_tables_serialize(self.handle, None, 0, ctypes.byref(n)))
+        buf = ctypes.create_string_buffer(max(n.value, 1))
+        _check(load().cg_tables_serialize(self.handle, buf, n.value, ctypes.byref(n)))
+        return buf.raw[:n.value]
 
     def __del__(self):
         if getattr(self, "handle", None) and _lib is not None:
@@ -229,7 +252,19 @@ class Blob:
         """fp16 bits [rows, C], or uint8 grid codes [rows, C] with 8-bit anchors."""
         h = self.header
         raw = self.read(h["anchors_offset"], h["anchors_bytes"])
-        return (raw if h["reserved"] == 8 else raw.view(np.uint16)).reshape(-1, self.tables.C)
+        return (raw if h["anchor_bits"] == 8 else raw.view(np.uint16)).reshape(-1, self.tables.C)
+
+    def outliers(self):
+        """(offsets uint64 [n_groups + 1], keys uint32, values uint16), or None without
+        the outlier table."""
+        h = self.header
+        if not h["outlier_ppm"]:
+            return None
+        n = h["n_outliers"]
+        offs = self.read(h["outliers_offset"], (h["n_groups"] + 1) * 8).view(np.uint64)
+        keys = self.read(h["outlier_keys_offset"], n * 4).view(np.uint32)
+        vals = self.read(h["outlier_values_offset"], n * 2).view(np.uint16)
+        return offs, keys, vals
 
     def payload(self) -> np.ndarray:
         h = self.header
@@ -249,11 +284,14 @@ class Blob:
 
 def build_cdf(kv: torch.Tensor, group: int, chunk: int, bins: Sequence[int],
               H_kv: Optional[int] = None, bins_v: Optional[Sequence[int]] = None,
-              n_sink: int = 0, anchor_bits: int = 16) -> Tables:
+              n_sink: int = 0, anchor_bits: int = 16, outlier_ppm: int = 0) -> Tables:
     """kv: fp16 CUDA [L, 2, S, C].  H_kv only labels the channel split (C = H_kv * d).
     bins: bin count per layer; with bins_v, those of the K rows, and bins_v those of the
-    V rows.  n_sink: the first n_sink tokens are kept as an fp16 copy (attention sinks).
-    anchor_bits: 16 (fp16 anchors) or 8 (anchors as codes on a per-channel grid)."""
+    V rows.  n_sink: the first n_sink tokens are kept in fp16 (attention sinks), in every
+    container that holds them.
+    anchor_bits: 16 (fp16 anchors) or 8 (anchors as codes on a per-channel grid).
+    outlier_ppm: 0, or the clip budget (parts per million at each end) of the sparse
+    outlier table."""
     _kv_check(kv)
     if n_sink < 0:
         raise ValueError("n_sink must be >= 0")
@@ -272,13 +310,13 @@ def build_cdf(kv: torch.Tensor, group: int, chunk: int, bins: Sequence[int],
     u8p = ctypes.POINTER(ctypes.c_uint8)
     p = Params(L, H, C // H, S, group, chunk, b.ctypes.data_as(u8p),
                bv.ctypes.data_as(u8p) if bv is not None else None, int(n_sink),
-               int(anchor_bits))
+               int(anchor_bits), int(outlier_ppm))
     h = ctypes.c_void_p()
     with torch.cuda.device(kv.device):
         _check(load().cg_build_cdf(ctypes.byref(p), kv.data_ptr(), _stream(kv.device),
                                    ctypes.byref(h)))
     return Tables(h, L, H, C // H, S, group, chunk, b, kv.device, bins_v=bv, n_sink=n_sink,
-                  anchor_bits=anchor_bits)
+                  anchor_bits=anchor_bits, outlier_ppm=outlier_ppm)
 
 
 def encode(tables: Tables, kv: torch.Tensor, chunk_begin: int = 0,
@@ -409,3 +447,50 @@ def stream_decode(items: Sequence[tuple], staging: torch.Tensor, n_slots: int,
         return None
     return {"total_ms": st.total_ms, "copy_ms": st.copy_ms, "decode_ms": st.decode_ms,
             "copied_bytes": int(st.copied_bytes)}
+
+
+# ------------------------------------------------------------------ stored form
+def _bytes_arg(data) -> tuple:
+    buf = np.frombuffer(bytes(data) if not isinstance(data, (bytes, bytearray)) else data, np.uint8)
+    return buf, buf.ctypes.data if buf.size else None
+
+
+def tables_check(data) -> dict:
+    """Checks stored tables on the host (no device); returns the header fields."""
+    buf, ptr = _bytes_arg(data)
+    h = TablesHeader()
+    _check(load().cg_tables_check(ptr, buf.size, ctypes.byref(h)))
+    return {f: getattr(h, f) for f, _ in TablesHeader._fields_}
+
+
+def container_check(data) -> dict:
+    """Checks a container on the host (no device); returns the header fields."""
+    buf, ptr = _bytes_arg(data)
+    h = ContainerHeader()
+    _check(load().cg_container_check(ptr, buf.size, ctypes.byref(h)))
+    return {f: getattr(h, f) for f, _ in ContainerHeader._fields_}
+
+
+def tables_import(data, device=None) -> Tables:
+    """Tables handle on `device` (default: the current CUDA device) from stored tables."""
+    hdr = tables_check(data)
+    buf, ptr = _bytes_arg(data)
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    h = ctypes.c_void_p()
+    with torch.cuda.device(dev):
+        _check(load().cg_tables_import(ptr, buf.size, ctypes.byref(h)))
+    L = hdr["L"]
+    bins = np.frombuffer(buf[56:56 + 2 * L].tobytes(), np.uint8).reshape(L, 2)
+    return Tables(h, L, hdr["H_kv"], hdr["d"], hdr["S"], hdr["group"], hdr["chunk"],
+                  bins[:, 0].copy(), dev, bins_v=bins[:, 1].copy(), n_sink=hdr["n_sink"],
+                  anchor_bits=hdr["anchor_bits"], outlier_ppm=hdr["outlier_ppm"])
+
+
+def blob_import(tables: Tables, data) -> Blob:
+    """Blob on the tables' device from container bytes (checked first)."""
+    buf, ptr = _bytes_arg(data)
+    h = ctypes.c_void_p()
+    with torch.cuda.device(tables.device):
+        _check(load().cg_blob_import(tables.handle, ptr, buf.size, _stream(tables.device),
+                                     ctypes.byref(h)))
+    return Blob(h, tables)

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -17,8 +18,12 @@ using namespace cgk;
 
 namespace {
 
-constexpr uint32_t kTablesMagic = 0x54424743u;  // "CGBT"
-constexpr uint32_t kBlobMagic = 0x42424743u;    // "CGBB"
+constexpr uint32_t kTablesMagic = 0x54424743u;  // "CGBT" (live handle)
+constexpr uint32_t kBlobMagic = 0x42424743u;    // "CGBB" (live handle)
+constexpr uint64_t kHeaderBytes = sizeof(cg_container_header);
+constexpr uint32_t kMaxOutlierPpm = 250000;
+static_assert(sizeof(cg_container_header) == 160, "container header is 160 bytes");
+static_assert(sizeof(cg_tables_header) == 56, "tables header is 56 bytes");
 
 thread_local std::string g_error;
 
@@ -88,6 +93,21 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 uint32_t ceil_div(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
 
+// The shape limits of include/cg.h; returns an error text or nullptr.
+const char *shape_error(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc)
+{
+    if (!L || !H || !d || !S || !G || !Tc) return "zero dimension";
+    if (Tc > CG_MAX_CHUNK) return "chunk > 16384";
+    const uint64_t C = (uint64_t)H * d;
+    if (C % 8 != 0) return "H_kv * d must be a multiple of 8";
+    // 32-bit offsets inside one (layer, K/V) row of symbols and inside one chunk's rows
+    if (C >= (1u << 24) || S >= (1u << 31) || (uint64_t)L * 2 * C >= (1ull << 31) ||
+        (uint64_t)L * 2 * S * C >= (1ull << 40) || (uint64_t)S * C >= (1ull << 32) ||
+        (uint64_t)Tc * C * 2 >= (1ull << 32))
+        return "cache too large";
+    return nullptr;
+}
+
 }  // namespace
 
 struct cg_tables {
@@ -101,7 +121,8 @@ struct cg_tables {
     uint16_t *d_freqs;
     uint32_t *d_dtab;
     uint32_t n_sink;              // min(params n_sink, S)
-    uint16_t *d_sinks;            // fp16 [L][2][n_sink][C], or null
+    uint32_t anchor_bits;         // 16 or 8
+    uint32_t outlier_ppm;
     float *d_alo, *d_aw, *d_ar;   // 8-bit anchor grid [L][2][C], or null (fp16 anchors)
 };
 
@@ -133,17 +154,6 @@ Geom make_geom(const cg_tables *t, uint32_t kb, uint32_t ke)
     return g;
 }
 
-// Writes the sink rows among the tokens of chunks [kb, ke) into a contiguous output or,
-// when pg.pages is set, into pages.
-hipError_t put_sinks(const cg_tables *t, uint32_t kb, uint32_t ke, uint16_t *out, const Paged &pg,
-                     hipStream_t st)
-{
-    if (!t->n_sink) return hipSuccess;
-    const uint64_t a = (uint64_t)kb * t->Tc, b = std::min<uint64_t>((uint64_t)ke * t->Tc, t->n_sink);
-    if (a >= b) return hipSuccess;
-    return launch_sinks(make_geom(t, kb, ke), t->d_sinks, t->n_sink, (uint32_t)a, (uint32_t)b, out, pg, st);
-}
-
 // Tokens per thread for the streaming kernels: about two million threads in flight.
 uint32_t pick_tpt(const cg_tables *t, uint64_t tokens)
 {
@@ -152,6 +162,50 @@ uint32_t pick_tpt(const cg_tables *t, uint64_t tokens)
     if (tpt < 8) tpt = 8;
     if (tpt > 4096) tpt = 4096;
     return (uint32_t)tpt;
+}
+
+// Sink tokens stored in a container of chunks [kb, ke): tokens kb * Tc .. + count.
+uint32_t sinks_in(const cg_tables *t, uint32_t kb, uint32_t ke)
+{
+    const uint64_t a = (uint64_t)kb * t->Tc;
+    const uint64_t b = std::min<uint64_t>(std::min<uint64_t>((uint64_t)ke * t->Tc, t->S), t->n_sink);
+    return b > a ? (uint32_t)(b - a) : 0u;
+}
+
+// Anchor rows of chunks [kb, ke) in closed form: only the cache's last chunk is short.
+uint64_t anchor_rows(uint32_t L, uint32_t S, uint32_t G, uint32_t Tc, uint32_t kb, uint32_t ke)
+{
+    const uint32_t nk = ceil_div(S, Tc);
+    const uint32_t last = S - (nk - 1) * Tc;
+    uint64_t per_chunk = ceil_div(Tc, G);
+    uint64_t rows = (uint64_t)(ke - kb) * per_chunk;
+    if (ke == nk && last != Tc) rows = rows - per_chunk + ceil_div(last, G);
+    return rows * L * 2;
+}
+
+// Every section offset of a container header from its shape, chunk range, anchor width,
+// sink count, outlier setting and entry count, and payload size (include/cg.h layout).
+void fill_layout(cg_container_header &h)
+{
+    const uint64_t C = (uint64_t)h.H_kv * h.d;
+    h.n_blocks = (uint32_t)((C + kLanes - 1) / kLanes);
+    h.n_groups = (uint64_t)(h.chunk_end - h.chunk_begin) * h.L * 2 * h.n_blocks;
+    h.offsets_offset = align256(kHeaderBytes);
+    h.anchors_offset = align256(h.offsets_offset + (h.n_groups + 1) * 8);
+    h.anchors_bytes = anchor_rows(h.L, h.S, h.group, h.chunk, h.chunk_begin, h.chunk_end) * C *
+                      (h.anchor_bits == 8 ? 1u : 2u);
+    h.sinks_offset = align256(h.anchors_offset + h.anchors_bytes);
+    uint64_t end = h.sinks_offset + (uint64_t)2 * h.L * h.n_sink * C * 2;
+    h.outliers_offset = align256(end);
+    if (h.outlier_ppm) {
+        h.outlier_keys_offset = align256(h.outliers_offset + (h.n_groups + 1) * 8);
+        h.outlier_values_offset = align256(h.outlier_keys_offset + h.n_outliers * 4);
+        end = h.outlier_values_offset + h.n_outliers * 2;
+    } else {
+        h.outlier_keys_offset = h.outlier_values_offset = h.outliers_offset;
+    }
+    h.payload_offset = align256(end);
+    h.total_bytes = h.payload_offset + h.payload_words * 2 + kPayloadPadBytes;
 }
 
 int check_tables(const cg_tables *t)
@@ -165,8 +219,9 @@ int check_blob(const cg_tables *t, const cg_blob *b)
     if (!b || b->magic != kBlobMagic) return fail(CG_E_INVAL, "invalid cg_blob handle");
     const cg_container_header &h = b->hdr;
     if (h.L != t->L || h.H_kv != t->H || h.d != t->d || h.S != t->S || h.group != t->G ||
-        h.chunk != t->Tc || h.reserved != (t->d_alo ? 8u : 0u))
-        return fail(CG_E_CORRUPT, "container and tables describe different caches");
+        h.chunk != t->Tc || h.anchor_bits != t->anchor_bits || h.outlier_ppm != t->outlier_ppm ||
+        h.n_sink != sinks_in(t, h.chunk_begin, h.chunk_end))
+        return fail(CG_E_CORRUPT, "container and tables describe different caches or settings");
     return CG_OK;
 }
 
@@ -178,18 +233,100 @@ ContainerView view_of(const cg_blob *b)
     v.anchors_bytes = b->hdr.anchors_bytes;
     v.payload_off = b->hdr.payload_offset;
     v.payload_words = b->hdr.payload_words;
+    v.sinks_off = b->hdr.sinks_offset;
+    v.n_sink = b->hdr.n_sink;
+    v.out_off = b->hdr.outliers_offset;
+    v.keys_off = b->hdr.outlier_keys_offset;
+    v.vals_off = b->hdr.outlier_values_offset;
+    v.n_out = b->hdr.n_outliers;
+    v.outliers = b->hdr.outlier_ppm != 0;
     return v;
 }
 
-uint64_t anchor_rows(const cg_tables *t, uint32_t kb, uint32_t ke)
+// After the decoded rows: the container's sink rows, then its outlier entries.
+hipError_t put_extras(const cg_tables *t, const cg_blob *b, const uint8_t *cont, uint16_t *out,
+                      const Paged &pg, hipStream_t st)
 {
-    uint64_t rows = 0;
-    for (uint32_t k = kb; k < ke; ++k) {
-        uint32_t t0 = k * t->Tc;
-        uint32_t len = (t->S - t0 < t->Tc) ? t->S - t0 : t->Tc;
-        rows += (uint64_t)t->L * 2 * ceil_div(len, t->G);
+    const Geom g = make_geom(t, b->hdr.chunk_begin, b->hdr.chunk_end);
+    const ContainerView cv = view_of(b);
+    hipError_t e = launch_sinks(g, reinterpret_cast<const uint16_t *>(cont + cv.sinks_off), cv.n_sink,
+                                b->hdr.chunk_begin * t->Tc, out, pg, st);
+    if (e != hipSuccess) return e;
+    return launch_apply_outliers(g, cont, cv, out, pg, st);
+}
+
+// Frees a half-built handle on every error path.
+struct TablesOwner {
+    cg_tables *t;
+    ~TablesOwner();
+};
+
+// A tables handle with its shape set and its device arrays allocated (decode tables
+// zeroed), or an error.  `bins` holds the level count of every (layer, K/V) row.
+int new_tables(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,
+               const std::vector<uint8_t> &bins, uint32_t n_sink, uint32_t anchor_bits,
+               uint32_t ppm, hipStream_t st, cg_tables **out)
+{
+    cg_tables *t = new (std::nothrow) cg_tables();
+    if (!t) return fail(CG_E_NOMEM, "host allocation");
+    t->magic = kTablesMagic;  // cg_free may release it from here on
+    TablesOwner owner{t};
+    CG_HIP(hipGetDevice(&t->device), "hipGetDevice");
+    t->L = L;
+    t->H = H;
+    t->d = d;
+    t->S = S;
+    t->G = G;
+    t->Tc = Tc;
+    t->C = H * d;
+    t->NB = ceil_div(t->C, kLanes);
+    t->bins = bins;
+    t->max_bins = 0;
+    for (uint8_t n : bins) t->max_bins = std::max<uint32_t>(t->max_bins, n);
+    t->n_sink = std::min(n_sink, S);
+    t->anchor_bits = anchor_bits == 8 ? 8u : 16u;
+    t->outlier_ppm = ppm;
+    const uint64_t rows = (uint64_t)t->L * 2 * t->C;
+    DevBuf bins_d, lo_d, w_d, r_d, fr_d, dt_d;
+    CG_HIP(bins_d.alloc((uint64_t)2 * t->L), "hipMalloc");
+    CG_HIP(lo_d.alloc(rows * 4), "hipMalloc");
+    CG_HIP(w_d.alloc(rows * 4), "hipMalloc");
+    CG_HIP(r_d.alloc(rows * 4), "hipMalloc");
+    CG_HIP(fr_d.alloc(rows * kMaxBins * 2), "hipMalloc");
+    const uint64_t dtab_bytes = (uint64_t)t->L * 2 * t->NB * kTabBlock * sizeof(uint32_t);
+    CG_HIP(dt_d.alloc(dtab_bytes), "hipMalloc");
+    if (t->anchor_bits == 8) {
+        DevBuf alo_d, aw_d, ar_d;
+        CG_HIP(alo_d.alloc(rows * 4), "hipMalloc");
+        CG_HIP(aw_d.alloc(rows * 4), "hipMalloc");
+        CG_HIP(ar_d.alloc(rows * 4), "hipMalloc");
+        t->d_alo = static_cast<float *>(alo_d.detach());
+        t->d_aw = static_cast<float *>(aw_d.detach());
+        t->d_ar = static_cast<float *>(ar_d.detach());
     }
-    return rows;
+    t->d_bins = static_cast<uint8_t *>(bins_d.detach());
+    t->d_lo = static_cast<float *>(lo_d.detach());
+    t->d_w = static_cast<float *>(w_d.detach());
+    t->d_r = static_cast<float *>(r_d.detach());
+    t->d_freqs = static_cast<uint16_t *>(fr_d.detach());
+    t->d_dtab = static_cast<uint32_t *>(dt_d.detach());
+    CG_HIP(hipMemcpyAsync(t->d_bins, t->bins.data(), (size_t)2 * t->L, hipMemcpyHostToDevice, st),
+           "copy bins");
+    CG_HIP(hipMemsetAsync(t->d_freqs, 0, rows * kMaxBins * 2, st), "memset");
+    CG_HIP(hipMemsetAsync(t->d_dtab, 0, dtab_bytes, st), "memset");
+    owner.t = nullptr;
+    *out = t;
+    return CG_OK;
+}
+
+// Size of the stored tables.
+uint64_t tables_stored_bytes(const cg_tables *t)
+{
+    const uint64_t rows = (uint64_t)t->L * 2 * t->C;
+    uint64_t bytes = sizeof(cg_tables_header) + (((uint64_t)2 * t->L + 3) & ~uint64_t(3));
+    bytes += rows * 8 * (t->anchor_bits == 8 ? 2 : 1);
+    for (uint32_t r = 0; r < 2 * t->L; ++r) bytes += (uint64_t)t->C * t->bins[r] * 2;
+    return bytes;
 }
 
 }  // namespace
@@ -204,133 +341,57 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     if (!params || !kv_dev || !out || !params->bins)
         return fail(CG_E_INVAL, "null argument");
     const cg_params &p = *params;
-    if (!p.L || !p.H_kv || !p.d || !p.S || !p.group || !p.chunk)
-        return fail(CG_E_INVAL, "zero dimension");
-    if (p.chunk > CG_MAX_CHUNK) return fail(CG_E_INVAL, "chunk > 16384");
+    if (const char *err = shape_error(p.L, p.H_kv, p.d, p.S, p.group, p.chunk))
+        return fail(CG_E_INVAL, err);
     if (p.anchor_bits != 0 && p.anchor_bits != 8 && p.anchor_bits != 16)
         return fail(CG_E_INVAL, "anchor_bits must be 0, 8 or 16");
-    uint64_t C = (uint64_t)p.H_kv * p.d;
-    if (C % 8 != 0) return fail(CG_E_INVAL, "H_kv * d must be a multiple of 8");
-    // 32-bit offsets inside one (layer, K/V) row of symbols and inside one chunk's rows
-    if (C >= (1u << 24) || p.S >= (1u << 31) || (uint64_t)p.L * 2 * C >= (1ull << 31) ||
-        (uint64_t)p.L * 2 * p.S * C >= (1ull << 40) || (uint64_t)p.S * C >= (1ull << 32) ||
-        (uint64_t)p.chunk * C * 2 >= (1ull << 32))
-        return fail(CG_E_INVAL, "cache too large");
-    uint32_t max_bins = 0;
+    if (p.outlier_ppm > kMaxOutlierPpm) return fail(CG_E_INVAL, "outlier_ppm > 250000");
+    std::vector<uint8_t> bins((size_t)2 * p.L);  // per (layer, K/V) row: l * 2 + kv
     for (uint32_t l = 0; l < p.L; ++l)
         for (uint32_t kv = 0; kv < 2; ++kv) {
             const uint8_t n = (kv && p.bins_v) ? p.bins_v[l] : p.bins[l];
             if (n < 2 || n > CG_MAX_BINS) return fail(CG_E_INVAL, "bins outside [2, 32]");
-            if (n > max_bins) max_bins = n;
+            bins[2 * l + kv] = n;
         }
     hipStream_t st = (hipStream_t)hip_stream;
-
-    cg_tables *t = new (std::nothrow) cg_tables();
-    if (!t) return fail(CG_E_NOMEM, "host allocation");
-    t->magic = 0;
-    CG_HIP(hipGetDevice(&t->device), "hipGetDevice");
-    t->L = p.L;
-    t->H = p.H_kv;
-    t->d = p.d;
-    t->S = p.S;
-    t->G = p.group;
-    t->Tc = p.chunk;
-    t->C = (uint32_t)C;
-    t->NB = ceil_div(t->C, kLanes);
-    t->max_bins = max_bins;
-    t->n_sink = std::min(p.n_sink, p.S);
-    t->d_sinks = nullptr;
-    t->d_alo = t->d_aw = t->d_ar = nullptr;
-    t->bins.resize((size_t)2 * p.L);  // per (layer, K/V) row: l * 2 + kv
-    for (uint32_t l = 0; l < p.L; ++l) {
-        t->bins[2 * l] = p.bins[l];
-        t->bins[2 * l + 1] = p.bins_v ? p.bins_v[l] : p.bins[l];
-    }
-
-    struct Owner {  // frees the half-built handle on every error path
-        cg_tables *t;
-        ~Owner()
-        {
-            if (t) cg_free(t);
-        }
-    } owner{t};
-    t->magic = kTablesMagic;  // cg_free may now release it
+    cg_tables *t = nullptr;
+    if (int rc = new_tables(p.L, p.H_kv, p.d, p.S, p.group, p.chunk, bins, p.n_sink,
+                            p.anchor_bits, p.outlier_ppm, st, &t))
+        return rc;
+    TablesOwner owner{t};
 
     const uint64_t rows = (uint64_t)t->L * 2 * t->C;
-    DevBuf bins_d, lo_d, w_d, r_d, fr_d, dt_d;
-    CG_HIP(bins_d.alloc((uint64_t)2 * t->L), "hipMalloc");
-    CG_HIP(lo_d.alloc(rows * 4), "hipMalloc");
-    CG_HIP(w_d.alloc(rows * 4), "hipMalloc");
-    CG_HIP(r_d.alloc(rows * 4), "hipMalloc");
-    CG_HIP(fr_d.alloc(rows * kMaxBins * 2), "hipMalloc");
-    const uint64_t dtab_bytes = (uint64_t)t->L * 2 * t->NB * kTabBlock * sizeof(uint32_t);
-    CG_HIP(dt_d.alloc(dtab_bytes), "hipMalloc");
-    t->d_bins = bins_d.as<uint8_t>();
-    t->d_lo = lo_d.as<float>();
-    t->d_w = w_d.as<float>();
-    t->d_r = r_d.as<float>();
-    t->d_freqs = fr_d.as<uint16_t>();
-    t->d_dtab = dt_d.as<uint32_t>();
-    if (p.anchor_bits == 8) {
-        DevBuf alo_d, aw_d, ar_d;
-        CG_HIP(alo_d.alloc(rows * 4), "hipMalloc");
-        CG_HIP(aw_d.alloc(rows * 4), "hipMalloc");
-        CG_HIP(ar_d.alloc(rows * 4), "hipMalloc");
-        t->d_alo = alo_d.as<float>();
-        t->d_aw = aw_d.as<float>();
-        t->d_ar = ar_d.as<float>();
-        alo_d.detach();
-        aw_d.detach();
-        ar_d.detach();
-    }
-    const uint64_t sink_row = (uint64_t)t->n_sink * t->C * 2;  // bytes per (layer, K/V)
-    if (sink_row) {
-        DevBuf sk_d;
-        CG_HIP(sk_d.alloc(2 * t->L * sink_row), "hipMalloc");
-        t->d_sinks = sk_d.as<uint16_t>();
-        sk_d.detach();
-        CG_HIP(hipMemcpy2DAsync(t->d_sinks, sink_row, kv_dev, (uint64_t)t->S * t->C * 2, sink_row,
-                                2 * t->L, hipMemcpyDeviceToDevice, st),
-               "copy sink rows");
-    }
-    bins_d.detach();
-    lo_d.detach();
-    w_d.detach();
-    r_d.detach();
-    fr_d.detach();
-    dt_d.detach();
-
-    DevBuf ordlo, ordhi, counts, flag;
+    DevBuf ordlo, ordhi, hi, counts, flag, fine;
     CG_HIP(ordlo.alloc(rows * 4), "hipMalloc");
     CG_HIP(ordhi.alloc(rows * 4), "hipMalloc");
+    CG_HIP(hi.alloc(rows * 4), "hipMalloc");
     CG_HIP(counts.alloc(rows * kMaxBins * 4), "hipMalloc");
     CG_HIP(flag.alloc(4), "hipMalloc");
-
-    CG_HIP(hipMemcpyAsync(t->d_bins, t->bins.data(), (size_t)2 * t->L, hipMemcpyHostToDevice, st),
-           "copy bins");
     CG_HIP(hipMemsetAsync(ordlo.p, 0xFF, rows * 4, st), "memset");
     CG_HIP(hipMemsetAsync(ordhi.p, 0x00, rows * 4, st), "memset");
     CG_HIP(hipMemsetAsync(counts.p, 0, rows * kMaxBins * 4, st), "memset");
     CG_HIP(hipMemsetAsync(flag.p, 0, 4, st), "memset");
-    CG_HIP(hipMemsetAsync(t->d_dtab, 0, dtab_bytes, st), "memset");
 
+    const uint16_t *X = static_cast<const uint16_t *>(kv_dev);
     Geom g = make_geom(t, 0, ceil_div(t->S, t->Tc));
     if (t->d_alo)
-        CG_HIP(launch_anchor_grid(static_cast<const uint16_t *>(kv_dev), g, t->d_alo, t->d_aw,
-                                  t->d_ar, st),
-               "k_anchor_grid");
-    CG_HIP(launch_k0(static_cast<const uint16_t *>(kv_dev), g, pick_tpt(t, t->S),
-                     ordlo.as<uint32_t>(), ordhi.as<uint32_t>(), flag.as<uint32_t>(), st),
+        CG_HIP(launch_anchor_grid(X, g, t->d_alo, t->d_aw, t->d_ar, st), "k_anchor_grid");
+    CG_HIP(launch_k0(X, g, pick_tpt(t, t->S), ordlo.as<uint32_t>(), ordhi.as<uint32_t>(),
+                     flag.as<uint32_t>(), st),
            "k0_minmax");
-    CG_HIP(launch_k0_finalize(g, t->d_bins, ordlo.as<uint32_t>(), ordhi.as<uint32_t>(), t->d_lo,
-                              t->d_w, t->d_r, st),
+    CG_HIP(launch_k0_finalize(g, ordlo.as<uint32_t>(), ordhi.as<uint32_t>(), t->d_lo, hi.as<float>(), st),
            "k0_finalize");
-    CG_HIP(launch_k1(static_cast<const uint16_t *>(kv_dev), g, t->d_bins, max_bins, t->d_lo,
-                     t->d_r, counts.as<uint32_t>(), st),
+    if (t->outlier_ppm) {
+        CG_HIP(fine.alloc(rows * kFineBins * 4), "hipMalloc");
+        CG_HIP(hipMemsetAsync(fine.p, 0, rows * kFineBins * 4, st), "memset");
+        CG_HIP(launch_fine_hist(X, g, t->d_lo, hi.as<float>(), fine.as<uint32_t>(), st), "k_fine_hist");
+        CG_HIP(launch_clip(g, fine.as<uint32_t>(), t->outlier_ppm, t->d_lo, hi.as<float>(), st), "k_clip");
+    }
+    CG_HIP(launch_width(g, t->d_bins, t->d_lo, hi.as<float>(), t->d_w, t->d_r, st), "k_width");
+    CG_HIP(launch_k1(X, g, t->d_bins, t->max_bins, t->d_lo, t->d_r, counts.as<uint32_t>(), st),
            "k1_hist");
-    CG_HIP(launch_k1_freqs(g, t->d_bins, counts.as<uint32_t>(), t->d_lo, t->d_w, t->d_freqs,
-                           t->d_dtab, st),
-           "k1_freqs");
+    CG_HIP(launch_k1_freqs(g, t->d_bins, counts.as<uint32_t>(), t->d_freqs, st), "k1_freqs");
+    CG_HIP(launch_dtab(g, t->d_bins, t->d_freqs, t->d_lo, t->d_w, t->d_dtab, st), "k_dtab");
     uint32_t h_flag = 0;
     CG_HIP(hipMemcpyAsync(&h_flag, flag.p, 4, hipMemcpyDeviceToHost, st), "copy flag");
     CG_HIP(hipStreamSynchronize(st), "hipStreamSynchronize");
@@ -351,43 +412,60 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     DeviceScope ds;
     CG_HIP(ds.enter(t->device), "hipSetDevice");
     hipStream_t st = (hipStream_t)hip_stream;
+    const uint16_t *X = static_cast<const uint16_t *>(kv_dev);
     Geom g = make_geom(t, kb, ke);
     const uint32_t t_lo = kb * t->Tc;
     const uint32_t t_hi = (ke * (uint64_t)t->Tc < t->S) ? ke * t->Tc : t->S;
     const uint32_t T_r = t_hi - t_lo;
     const uint64_t n_groups = (uint64_t)(ke - kb) * t->L * 2 * t->NB;
-    const uint64_t arows = anchor_rows(t, kb, ke);
+    const uint64_t arows = anchor_rows(t->L, t->S, t->G, t->Tc, kb, ke);
 
     // word-read ballots of every step of every group, 64 steps per row chunk
     const uint32_t full = t->Tc < t->S ? t->Tc : t->S;
     const uint32_t mstride = (full - ceil_div(full, t->G) + 63) / 64 * 64;
-    DevBuf sym, anc, lane_words, group_words, group_off, masks;
+    DevBuf sym, anc, lane_words, group_words, group_off, masks, counters, ocount, ooff;
     CG_HIP(sym.alloc((uint64_t)t->L * 2 * T_r * t->C), "hipMalloc symbols");
     CG_HIP(anc.alloc(arows * t->C * 2), "hipMalloc anchors");
     CG_HIP(lane_words.alloc(n_groups * kLanes * 4), "hipMalloc");
     CG_HIP(group_words.alloc(n_groups * 8), "hipMalloc");
     CG_HIP(group_off.alloc((n_groups + 1) * 8), "hipMalloc");
     CG_HIP(masks.alloc(n_groups * (mstride ? mstride : 1) * 8), "hipMalloc ballots");
+    CG_HIP(counters.alloc(8), "hipMalloc");
+    CG_HIP(hipMemsetAsync(counters.p, 0, 8, st), "memset");
+    if (t->outlier_ppm) {
+        CG_HIP(ocount.alloc(n_groups * 8), "hipMalloc");
+        CG_HIP(ooff.alloc((n_groups + 1) * 8), "hipMalloc");
+    }
 
-    CG_HIP(launch_k2(static_cast<const uint16_t *>(kv_dev), g, t->d_bins, t->d_lo, t->d_r, t_lo,
-                     t_hi, pick_tpt(t, T_r), sym.as<uint8_t>(), t_lo, T_r, anc.as<uint16_t>(), st),
+    CG_HIP(launch_k2(X, g, t->d_bins, t->d_lo, t->d_r, t_lo, t_hi, pick_tpt(t, T_r), sym.as<uint8_t>(),
+                     t_lo, T_r, anc.as<uint16_t>(), counters.as<unsigned long long>(), st),
            "k2_delta_quant");
     CG_HIP(launch_k5_plan(sym.as<uint8_t>(), t_lo, T_r, g, t->d_bins, t->d_dtab,
                           lane_words.as<uint32_t>(), group_words.as<uint64_t>(),
                           masks.as<uint64_t>(), mstride, st),
            "k5_plan");
-    CG_HIP(launch_scan(group_words.as<uint64_t>(), group_off.as<uint64_t>(), n_groups, st),
-           "scan");
-    uint64_t total_words = 0;
-    CG_HIP(hipMemcpyAsync(&total_words, group_off.as<uint64_t>() + n_groups, 8,
-                          hipMemcpyDeviceToHost, st),
+    CG_HIP(launch_scan(group_words.as<uint64_t>(), group_off.as<uint64_t>(), n_groups, st), "scan");
+    if (t->outlier_ppm) {
+        CG_HIP(launch_outliers(X, g, t->d_bins, t->d_lo, t->d_r, ocount.as<uint64_t>(), nullptr,
+                               nullptr, nullptr, st),
+               "k_outliers (count)");
+        CG_HIP(launch_scan(ocount.as<uint64_t>(), ooff.as<uint64_t>(), n_groups, st), "scan");
+    }
+    uint64_t sizes[3] = {0, 0, 0};  // payload words, elements off their grid, outlier entries
+    CG_HIP(hipMemcpyAsync(&sizes[0], group_off.as<uint64_t>() + n_groups, 8, hipMemcpyDeviceToHost, st),
            "copy size");
+    CG_HIP(hipMemcpyAsync(&sizes[1], counters.p, 8, hipMemcpyDeviceToHost, st), "copy count");
+    if (t->outlier_ppm)
+        CG_HIP(hipMemcpyAsync(&sizes[2], ooff.as<uint64_t>() + n_groups, 8, hipMemcpyDeviceToHost, st),
+               "copy count");
     CG_HIP(hipStreamSynchronize(st), "hipStreamSynchronize");
+    if (t->outlier_ppm && sizes[2] != sizes[1])
+        return fail(CG_E_HIP, "internal: the outlier passes disagree on the entry count");
 
     cg_container_header h;
     std::memset(&h, 0, sizeof h);
     h.magic = CG_CONTAINER_MAGIC;
-    h.version = 2;  // rANS with 8-bit frequencies
+    h.version = CG_CONTAINER_VERSION;
     h.L = t->L;
     h.H_kv = t->H;
     h.d = t->d;
@@ -396,15 +474,13 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     h.chunk = t->Tc;
     h.chunk_begin = kb;
     h.chunk_end = ke;
-    h.n_blocks = t->NB;
-    h.n_groups = n_groups;
-    h.offsets_offset = align256(sizeof(cg_container_header));
-    h.anchors_offset = align256(h.offsets_offset + (n_groups + 1) * 8);
-    h.anchors_bytes = arows * t->C * (t->d_alo ? 1 : 2);
-    h.reserved = t->d_alo ? 8u : 0u;  // bits per stored anchor element (0: fp16)
-    h.payload_offset = align256(h.anchors_offset + h.anchors_bytes);
-    h.payload_words = total_words;
-    h.total_bytes = h.payload_offset + total_words * 2 + kPayloadPadBytes;
+    h.anchor_bits = t->anchor_bits;
+    h.n_sink = sinks_in(t, kb, ke);
+    h.outlier_ppm = t->outlier_ppm;
+    h.n_outliers = t->outlier_ppm ? sizes[2] : 0;
+    h.clamped = t->outlier_ppm ? 0 : sizes[1];
+    h.payload_words = sizes[0];
+    fill_layout(h);
 
     cg_blob *b = new (std::nothrow) cg_blob();
     if (!b) return fail(CG_E_NOMEM, "host allocation");
@@ -417,7 +493,7 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
         delete b;
         return hip_fail(e, "hipMalloc container");
     }
-    e = scratch.alloc(total_words * 2);
+    e = scratch.alloc(sizes[0] * 2);
     if (e != hipSuccess) {
         delete b;
         return hip_fail(e, "hipMalloc scratch");
@@ -431,15 +507,42 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
             return hip_fail(e2_, what);      \
         }                                    \
     } while (0)
+    // zero bytes between sections and after the payload
+    const uint64_t C = t->C;
+    const uint64_t ends[][2] = {
+        {kHeaderBytes, h.offsets_offset},
+        {h.offsets_offset + (n_groups + 1) * 8, h.anchors_offset},
+        {h.anchors_offset + h.anchors_bytes, h.sinks_offset},
+        {h.sinks_offset + (uint64_t)2 * t->L * h.n_sink * C * 2, h.outliers_offset},
+        {h.outlier_ppm ? h.outliers_offset + (n_groups + 1) * 8 : h.outliers_offset, h.outlier_keys_offset},
+        {h.outlier_keys_offset + h.n_outliers * 4, h.outlier_values_offset},
+        {h.outlier_values_offset + (h.outlier_ppm ? h.n_outliers * 2 : 0), h.payload_offset},
+        {h.payload_offset + sizes[0] * 2, h.total_bytes}};
+    for (const auto &z : ends)
+        if (z[1] > z[0]) CG_HIP_B(hipMemsetAsync(base + z[0], 0, z[1] - z[0], st), "clear padding");
     CG_HIP_B(hipMemcpyAsync(base, &h, sizeof h, hipMemcpyHostToDevice, st), "copy header");
-    CG_HIP_B(hipMemsetAsync(base + h.payload_offset + total_words * 2, 0, kPayloadPadBytes, st),
-             "clear padding");
     CG_HIP_B(hipMemcpyAsync(base + h.offsets_offset, group_off.p, (n_groups + 1) * 8,
                             hipMemcpyDeviceToDevice, st),
              "copy offsets");
-    CG_HIP_B(hipMemcpyAsync(base + h.anchors_offset, anc.p, h.anchors_bytes,
-                            hipMemcpyDeviceToDevice, st),
+    CG_HIP_B(hipMemcpyAsync(base + h.anchors_offset, anc.p, h.anchors_bytes, hipMemcpyDeviceToDevice, st),
              "copy anchors");
+    if (h.n_sink) {
+        // the sink rows of the encoded cache: 2L rows of n_sink tokens from token t_lo
+        const uint64_t w = (uint64_t)h.n_sink * C * 2;
+        CG_HIP_B(hipMemcpy2DAsync(base + h.sinks_offset, w, X + (uint64_t)t_lo * C,
+                                  (uint64_t)t->S * C * 2, w, 2 * t->L, hipMemcpyDeviceToDevice, st),
+                 "copy sink rows");
+    }
+    if (t->outlier_ppm) {
+        CG_HIP_B(hipMemcpyAsync(base + h.outliers_offset, ooff.p, (n_groups + 1) * 8,
+                                hipMemcpyDeviceToDevice, st),
+                 "copy outlier offsets");
+        if (h.n_outliers)
+            CG_HIP_B(launch_outliers(X, g, t->d_bins, t->d_lo, t->d_r, nullptr, ooff.as<uint64_t>(),
+                                     reinterpret_cast<uint32_t *>(base + h.outlier_keys_offset),
+                                     reinterpret_cast<uint16_t *>(base + h.outlier_values_offset), st),
+                     "k_outliers");
+    }
     CG_HIP_B(launch_k5_encode(sym.as<uint8_t>(), t_lo, T_r, g, t->d_bins, t->d_dtab,
                               lane_words.as<uint32_t>(), group_off.as<uint64_t>(),
                               scratch.as<uint16_t>(), st),
@@ -483,7 +586,7 @@ int cg_decode_paged(const cg_tables *t, const cg_blob *b, const void *container_
     CG_HIP(launch_k3_paged(g, t->d_bins, t->d_dtab, t->d_lo, t->d_w, cont, view_of(b), pg,
                            (hipStream_t)hip_stream),
            "k3_decode (paged)");
-    CG_HIP(put_sinks(t, g.kb, g.ke, nullptr, pg, (hipStream_t)hip_stream), "k_sinks (paged)");
+    CG_HIP(put_extras(t, b, cont, nullptr, pg, (hipStream_t)hip_stream), "sinks / outliers (paged)");
     return CG_OK;
 }
 
@@ -498,11 +601,11 @@ int cg_decode(const cg_tables *t, const cg_blob *b, const void *container_dev, v
     CG_HIP(ds.enter(t->device), "hipSetDevice");
     const uint8_t *cont = container_dev ? static_cast<const uint8_t *>(container_dev) : b->d_data;
     Geom g = make_geom(t, b->hdr.chunk_begin, b->hdr.chunk_end);
-    CG_HIP(launch_k3(g, t->d_bins, t->d_dtab, t->d_lo, t->d_w, cont, view_of(b), static_cast<uint16_t *>(kv_out_dev),
-                     nullptr, (hipStream_t)hip_stream),
+    uint16_t *out = static_cast<uint16_t *>(kv_out_dev);
+    CG_HIP(launch_k3(g, t->d_bins, t->d_dtab, t->d_lo, t->d_w, cont, view_of(b), out, nullptr,
+                     (hipStream_t)hip_stream),
            "k3_decode");
-    CG_HIP(put_sinks(t, g.kb, g.ke, static_cast<uint16_t *>(kv_out_dev), Paged{}, (hipStream_t)hip_stream),
-           "k_sinks");
+    CG_HIP(put_extras(t, b, cont, out, Paged{}, (hipStream_t)hip_stream), "sinks / outliers");
     return CG_OK;
 }
 
@@ -617,9 +720,9 @@ int cg_stream_decode(const cg_stream_item *items, uint32_t n_items, void *stagin
             what = "k3_decode";
             break;
         }
-        if ((err = put_sinks(it.tables, g.kb, g.ke, static_cast<uint16_t *>(kv_out_dev), Paged{}, dec)) !=
+        if ((err = put_extras(it.tables, b, slot, static_cast<uint16_t *>(kv_out_dev), Paged{}, dec)) !=
             hipSuccess) {
-            what = "k_sinks";
+            what = "sinks / outliers";
             break;
         }
         if (ie && (err = hipEventRecord(ie[3], dec)) != hipSuccess) { what = "hipEventRecord"; break; }
@@ -681,12 +784,11 @@ int cg_dequantize(const cg_tables *t, const cg_blob *b, const void *container_de
     Geom g = make_geom(t, b->hdr.chunk_begin, b->hdr.chunk_end);
     const uint32_t t_lo = g.kb * t->Tc;
     const uint32_t t_hi = (g.ke * (uint64_t)t->Tc < t->S) ? g.ke * t->Tc : t->S;
+    uint16_t *out = static_cast<uint16_t *>(kv_out_dev);
     CG_HIP(launch_k4(g, t->d_lo, t->d_w, static_cast<const uint8_t *>(sym_dev), cont, view_of(b),
-                     t_lo, t_hi, pick_tpt(t, t_hi - t_lo), static_cast<uint16_t *>(kv_out_dev),
-                     (hipStream_t)hip_stream),
+                     t_lo, t_hi, pick_tpt(t, t_hi - t_lo), out, (hipStream_t)hip_stream),
            "k4_dequant");
-    CG_HIP(put_sinks(t, g.kb, g.ke, static_cast<uint16_t *>(kv_out_dev), Paged{}, (hipStream_t)hip_stream),
-           "k_sinks");
+    CG_HIP(put_extras(t, b, cont, out, Paged{}, (hipStream_t)hip_stream), "sinks / outliers");
     return CG_OK;
 }
 
@@ -705,7 +807,7 @@ int cg_quantize(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke
     const uint32_t t_hi = (ke * (uint64_t)t->Tc < t->S) ? ke * t->Tc : t->S;
     CG_HIP(launch_k2(static_cast<const uint16_t *>(kv_dev), g, t->d_bins, t->d_lo, t->d_r, t_lo,
                      t_hi, pick_tpt(t, t_hi - t_lo), static_cast<uint8_t *>(sym_dev), 0, t->S,
-                     nullptr, (hipStream_t)hip_stream),
+                     nullptr, nullptr, (hipStream_t)hip_stream),
            "k2_delta_quant");
     return CG_OK;
 }
@@ -737,11 +839,7 @@ int cg_tables_get_info(const cg_tables *t, cg_tables_info *info)
     info->S = t->S;
     info->group = t->G;
     info->chunk = t->Tc;
-    uint64_t bytes = (uint64_t)t->L * 2 * t->C * 8 + (uint64_t)2 * t->L;
-    for (uint32_t r = 0; r < 2 * t->L; ++r) bytes += (uint64_t)t->C * t->bins[r] * 2;
-    bytes += (uint64_t)2 * t->L * t->n_sink * t->C * 2;
-    if (t->d_alo) bytes += (uint64_t)t->L * 2 * t->C * 8;
-    info->stored_bytes = bytes;
+    info->stored_bytes = tables_stored_bytes(t);
     return CG_OK;
 }
 
@@ -769,6 +867,276 @@ int cg_blob_read(const cg_blob *b, uint64_t offset, uint64_t nbytes, void *host_
     return CG_OK;
 }
 
+// ------------------------------------------------------------------------------ stored form
+int cg_tables_serialize(const cg_tables *t, void *host_dst, uint64_t capacity, uint64_t *size_out)
+{
+    g_error.clear();
+    if (int rc = check_tables(t)) return rc;
+    const uint64_t size = tables_stored_bytes(t);
+    if (size_out) *size_out = size;
+    if (!host_dst) return size_out ? CG_OK : fail(CG_E_INVAL, "null destination");
+    if (capacity < size) return fail(CG_E_INVAL, "destination smaller than the stored tables");
+    DeviceScope ds;
+    CG_HIP(ds.enter(t->device), "hipSetDevice");
+    const uint64_t rows = (uint64_t)t->L * 2 * t->C;
+    std::vector<float> lo(rows), w(rows), alo, aw;
+    std::vector<uint16_t> fr(rows * kMaxBins);
+    CG_HIP(hipMemcpy(lo.data(), t->d_lo, rows * 4, hipMemcpyDeviceToHost), "copy lo");
+    CG_HIP(hipMemcpy(w.data(), t->d_w, rows * 4, hipMemcpyDeviceToHost), "copy w");
+    CG_HIP(hipMemcpy(fr.data(), t->d_freqs, rows * kMaxBins * 2, hipMemcpyDeviceToHost), "copy freqs");
+    if (t->anchor_bits == 8) {
+        alo.resize(rows);
+        aw.resize(rows);
+        CG_HIP(hipMemcpy(alo.data(), t->d_alo, rows * 4, hipMemcpyDeviceToHost), "copy alo");
+        CG_HIP(hipMemcpy(aw.data(), t->d_aw, rows * 4, hipMemcpyDeviceToHost), "copy aw");
+    }
+    uint8_t *p = static_cast<uint8_t *>(host_dst);
+    cg_tables_header h;
+    std::memset(&h, 0, sizeof h);
+    h.magic = CG_TABLES_MAGIC;
+    h.version = CG_TABLES_VERSION;
+    h.L = t->L;
+    h.H_kv = t->H;
+    h.d = t->d;
+    h.S = t->S;
+    h.group = t->G;
+    h.chunk = t->Tc;
+    h.n_sink = t->n_sink;
+    h.anchor_bits = t->anchor_bits;
+    h.outlier_ppm = t->outlier_ppm;
+    h.total_bytes = size;
+    std::memcpy(p, &h, sizeof h);
+    p += sizeof h;
+    const uint64_t bins_pad = ((uint64_t)2 * t->L + 3) & ~uint64_t(3);
+    std::memset(p, 0, bins_pad);
+    std::memcpy(p, t->bins.data(), (size_t)2 * t->L);
+    p += bins_pad;
+    std::memcpy(p, lo.data(), rows * 4);
+    p += rows * 4;
+    std::memcpy(p, w.data(), rows * 4);
+    p += rows * 4;
+    if (t->anchor_bits == 8) {
+        std::memcpy(p, alo.data(), rows * 4);
+        p += rows * 4;
+        std::memcpy(p, aw.data(), rows * 4);
+        p += rows * 4;
+    }
+    for (uint64_t i = 0; i < rows; ++i) {
+        const uint32_t n = t->bins[i / t->C];
+        std::memcpy(p, fr.data() + i * kMaxBins, (size_t)n * 2);
+        p += (size_t)n * 2;
+    }
+    return CG_OK;
+}
+
+int cg_tables_check(const void *host_bytes, uint64_t nbytes, cg_tables_header *header_out)
+{
+    g_error.clear();
+    if (!host_bytes) return fail(CG_E_INVAL, "null bytes");
+    if (nbytes < sizeof(cg_tables_header)) return fail(CG_E_CORRUPT, "shorter than a tables header");
+    cg_tables_header h;
+    std::memcpy(&h, host_bytes, sizeof h);
+    if (h.magic != CG_TABLES_MAGIC) return fail(CG_E_CORRUPT, "not stored tables (magic)");
+    if (h.version != CG_TABLES_VERSION) return fail(CG_E_CORRUPT, "unknown tables version");
+    if (const char *err = shape_error(h.L, h.H_kv, h.d, h.S, h.group, h.chunk))
+        return fail(CG_E_CORRUPT, std::string("tables shape: ") + err);
+    if (h.anchor_bits != 8 && h.anchor_bits != 16) return fail(CG_E_CORRUPT, "anchor_bits");
+    if (h.outlier_ppm > kMaxOutlierPpm) return fail(CG_E_CORRUPT, "outlier_ppm");
+    if (h.n_sink > h.S) return fail(CG_E_CORRUPT, "n_sink above S");
+    const uint64_t C = (uint64_t)h.H_kv * h.d, rows = (uint64_t)h.L * 2 * C;
+    const uint64_t bins_pad = ((uint64_t)2 * h.L + 3) & ~uint64_t(3);
+    const uint64_t fixed = sizeof h + bins_pad + rows * 8 * (h.anchor_bits == 8 ? 2 : 1);
+    if (nbytes < fixed) return fail(CG_E_CORRUPT, "truncated tables");
+    const uint8_t *p = static_cast<const uint8_t *>(host_bytes);
+    const uint8_t *bins = p + sizeof h;
+    uint64_t size = fixed;
+    for (uint32_t r = 0; r < 2 * h.L; ++r) {
+        if (bins[r] < 2 || bins[r] > CG_MAX_BINS) return fail(CG_E_CORRUPT, "bins outside [2, 32]");
+        size += C * bins[r] * 2;
+    }
+    for (uint64_t j = 2 * h.L; j < bins_pad; ++j)
+        if (bins[j]) return fail(CG_E_CORRUPT, "padding after bins is not zero");
+    if (h.total_bytes != size || nbytes < size) return fail(CG_E_CORRUPT, "tables size");
+    const uint8_t *q = p + sizeof h + bins_pad;
+    const uint64_t n_grid = rows * (h.anchor_bits == 8 ? 4 : 2);  // lo, w (, alo, aw)
+    for (uint64_t i = 0; i < n_grid; ++i) {
+        float v;
+        std::memcpy(&v, q + 4 * i, 4);
+        const uint64_t which = i / rows;  // 0 lo, 1 w, 2 alo, 3 aw
+        if (!std::isfinite(v) || ((which == 1 || which == 3) && !(v >= 0.0f)))
+            return fail(CG_E_CORRUPT, "grid values must be finite, widths >= 0");
+    }
+    const uint8_t *f = q + 4 * n_grid;
+    for (uint64_t i = 0; i < rows; ++i) {
+        const uint32_t n = bins[i / C];
+        uint32_t sum = 0;
+        for (uint32_t s = 0; s < n; ++s) {
+            uint16_t v;
+            std::memcpy(&v, f, 2);
+            f += 2;
+            if (v == 0) return fail(CG_E_CORRUPT, "a frequency of 0");
+            sum += v;
+        }
+        if (sum != kProbTotal) return fail(CG_E_CORRUPT, "frequencies do not sum to 256");
+    }
+    if (header_out) *header_out = h;
+    return CG_OK;
+}
+
+int cg_tables_import(const void *host_bytes, uint64_t nbytes, cg_tables **out)
+{
+    g_error.clear();
+    if (!out) return fail(CG_E_INVAL, "null argument");
+    cg_tables_header h;
+    if (int rc = cg_tables_check(host_bytes, nbytes, &h)) return rc;
+    const uint8_t *p = static_cast<const uint8_t *>(host_bytes);
+    std::vector<uint8_t> bins(p + sizeof h, p + sizeof h + (size_t)2 * h.L);
+    cg_tables *t = nullptr;
+    if (int rc = new_tables(h.L, h.H_kv, h.d, h.S, h.group, h.chunk, bins, h.n_sink, h.anchor_bits,
+                            h.outlier_ppm, nullptr, &t))
+        return rc;
+    TablesOwner owner{t};
+    const uint64_t rows = (uint64_t)t->L * 2 * t->C;
+    const uint8_t *q = p + sizeof h + ((((uint64_t)2 * h.L) + 3) & ~uint64_t(3));
+    std::vector<float> lo(rows), w(rows), r(rows);
+    std::memcpy(lo.data(), q, rows * 4);
+    std::memcpy(w.data(), q + rows * 4, rows * 4);
+    q += rows * 8;
+    for (uint64_t i = 0; i < rows; ++i) r[i] = w[i] > 0.0f ? 1.0f / w[i] : 0.0f;
+    CG_HIP(hipMemcpy(t->d_lo, lo.data(), rows * 4, hipMemcpyHostToDevice), "copy lo");
+    CG_HIP(hipMemcpy(t->d_w, w.data(), rows * 4, hipMemcpyHostToDevice), "copy w");
+    CG_HIP(hipMemcpy(t->d_r, r.data(), rows * 4, hipMemcpyHostToDevice), "copy r");
+    if (t->anchor_bits == 8) {
+        std::vector<float> alo(rows), aw(rows), ar(rows);
+        std::memcpy(alo.data(), q, rows * 4);
+        std::memcpy(aw.data(), q + rows * 4, rows * 4);
+        q += rows * 8;
+        for (uint64_t i = 0; i < rows; ++i) ar[i] = aw[i] > 0.0f ? 1.0f / aw[i] : 0.0f;
+        CG_HIP(hipMemcpy(t->d_alo, alo.data(), rows * 4, hipMemcpyHostToDevice), "copy alo");
+        CG_HIP(hipMemcpy(t->d_aw, aw.data(), rows * 4, hipMemcpyHostToDevice), "copy aw");
+        CG_HIP(hipMemcpy(t->d_ar, ar.data(), rows * 4, hipMemcpyHostToDevice), "copy ar");
+    }
+    std::vector<uint16_t> fr(rows * kMaxBins, 0);
+    for (uint64_t i = 0; i < rows; ++i) {
+        const uint32_t n = t->bins[i / t->C];
+        std::memcpy(fr.data() + i * kMaxBins, q, (size_t)n * 2);
+        q += (size_t)n * 2;
+    }
+    CG_HIP(hipMemcpy(t->d_freqs, fr.data(), rows * kMaxBins * 2, hipMemcpyHostToDevice), "copy freqs");
+    CG_HIP(launch_dtab(make_geom(t, 0, 1), t->d_bins, t->d_freqs, t->d_lo, t->d_w, t->d_dtab, nullptr),
+           "k_dtab");
+    CG_HIP(hipStreamSynchronize(nullptr), "hipStreamSynchronize");
+    owner.t = nullptr;
+    *out = t;
+    return CG_OK;
+}
+
+int cg_container_check(const void *host_bytes, uint64_t nbytes, cg_container_header *header_out)
+{
+    g_error.clear();
+    if (!host_bytes) return fail(CG_E_INVAL, "null bytes");
+    if (nbytes < kHeaderBytes) return fail(CG_E_CORRUPT, "shorter than a container header");
+    cg_container_header h;
+    std::memcpy(&h, host_bytes, sizeof h);
+    if (h.magic != CG_CONTAINER_MAGIC) return fail(CG_E_CORRUPT, "not a container (magic)");
+    if (h.version != CG_CONTAINER_VERSION) return fail(CG_E_CORRUPT, "unknown container version");
+    if (const char *err = shape_error(h.L, h.H_kv, h.d, h.S, h.group, h.chunk))
+        return fail(CG_E_CORRUPT, std::string("container shape: ") + err);
+    const uint32_t nk = ceil_div(h.S, h.chunk);
+    if (h.chunk_begin >= h.chunk_end || h.chunk_end > nk) return fail(CG_E_CORRUPT, "chunk range");
+    if (h.anchor_bits != 8 && h.anchor_bits != 16) return fail(CG_E_CORRUPT, "anchor_bits");
+    if (h.outlier_ppm > kMaxOutlierPpm) return fail(CG_E_CORRUPT, "outlier_ppm");
+    if (!h.outlier_ppm && h.n_outliers) return fail(CG_E_CORRUPT, "outlier entries without the table");
+    const uint64_t t_lo = (uint64_t)h.chunk_begin * h.chunk;
+    const uint64_t t_hi = std::min<uint64_t>((uint64_t)h.chunk_end * h.chunk, h.S);
+    if (h.n_sink > t_hi - t_lo) return fail(CG_E_CORRUPT, "more sink tokens than tokens");
+    const uint64_t C = (uint64_t)h.H_kv * h.d;
+    const uint64_t elems = (uint64_t)h.L * 2 * (t_hi - t_lo) * C;
+    if (h.n_outliers > elems || h.clamped > elems || h.payload_words > (1ull << 46))
+        return fail(CG_E_CORRUPT, "counts larger than the container's elements");
+    cg_container_header e = h;
+    fill_layout(e);
+    if (std::memcmp(&e, &h, sizeof h) != 0)
+        return fail(CG_E_CORRUPT, "section offsets do not follow the layout");
+    if (h.total_bytes > nbytes) return fail(CG_E_CORRUPT, "container truncated");
+    const uint8_t *p = static_cast<const uint8_t *>(host_bytes);
+    // group word offsets: 0 first, non-decreasing, the payload size last
+    const uint64_t ng = h.n_groups;
+    uint64_t prev = 0;
+    for (uint64_t g = 0; g <= ng; ++g) {
+        uint64_t v;
+        std::memcpy(&v, p + h.offsets_offset + 8 * g, 8);
+        if ((g == 0 && v != 0) || v < prev || v > h.payload_words)
+            return fail(CG_E_CORRUPT, "group offsets out of order or past the payload");
+        prev = v;
+    }
+    if (prev != h.payload_words) return fail(CG_E_CORRUPT, "group offsets do not end at the payload size");
+    if (h.outlier_ppm) {
+        const uint32_t NB = h.n_blocks, last_len = h.S - (nk - 1) * h.chunk;
+        prev = 0;
+        for (uint64_t g = 0; g <= ng; ++g) {
+            uint64_t v;
+            std::memcpy(&v, p + h.outliers_offset + 8 * g, 8);
+            if ((g == 0 && v != 0) || v < prev || v > h.n_outliers)
+                return fail(CG_E_CORRUPT, "outlier offsets out of order or past the entries");
+            if (g > 0) {
+                const uint64_t gi = g - 1;
+                const uint32_t b = (uint32_t)(gi % NB);
+                const uint32_t k = h.chunk_begin + (uint32_t)(gi / NB / (2 * (uint64_t)h.L));
+                const uint32_t len = (k == nk - 1) ? last_len : h.chunk;
+                const uint64_t lanes = std::min<uint64_t>(kLanes, C - (uint64_t)b * kLanes);
+                for (uint64_t i = prev; i < v; ++i) {
+                    uint32_t key;
+                    std::memcpy(&key, p + h.outlier_keys_offset + 4 * i, 4);
+                    if ((key >> 6) >= len || (key & 63u) >= lanes)
+                        return fail(CG_E_CORRUPT, "an outlier key outside its group");
+                }
+            }
+            prev = v;
+        }
+        if (prev != h.n_outliers) return fail(CG_E_CORRUPT, "outlier offsets do not end at the entry count");
+    }
+    if (header_out) *header_out = h;
+    return CG_OK;
+}
+
+int cg_blob_import(const cg_tables *t, const void *host_bytes, uint64_t nbytes, void *hip_stream,
+                   cg_blob **out)
+{
+    g_error.clear();
+    if (int rc = check_tables(t)) return rc;
+    if (!out) return fail(CG_E_INVAL, "null argument");
+    cg_container_header h;
+    if (int rc = cg_container_check(host_bytes, nbytes, &h)) return rc;
+    if (h.L != t->L || h.H_kv != t->H || h.d != t->d || h.S != t->S || h.group != t->G ||
+        h.chunk != t->Tc || h.anchor_bits != t->anchor_bits || h.outlier_ppm != t->outlier_ppm ||
+        h.n_sink != sinks_in(t, h.chunk_begin, h.chunk_end))
+        return fail(CG_E_CORRUPT, "container and tables describe different caches or settings");
+    DeviceScope ds;
+    CG_HIP(ds.enter(t->device), "hipSetDevice");
+    hipStream_t st = (hipStream_t)hip_stream;
+    cg_blob *b = new (std::nothrow) cg_blob();
+    if (!b) return fail(CG_E_NOMEM, "host allocation");
+    b->magic = 0;
+    b->device = t->device;
+    b->hdr = h;
+    DevBuf data;
+    hipError_t e = data.alloc(align256(h.total_bytes));
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(data.p, host_bytes, h.total_bytes - kPayloadPadBytes, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess)
+        e = hipMemsetAsync(data.as<uint8_t>() + h.total_bytes - kPayloadPadBytes, 0, kPayloadPadBytes, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        delete b;
+        return hip_fail(e, "import container");
+    }
+    b->d_data = static_cast<uint8_t *>(data.detach());
+    b->magic = kBlobMagic;
+    *out = b;
+    return CG_OK;
+}
+
 void cg_free(void *handle)
 {
     if (!handle) return;
@@ -777,7 +1145,7 @@ void cg_free(void *handle)
     if (magic == kTablesMagic) {
         cg_tables *t = static_cast<cg_tables *>(handle);
         t->magic = 0;
-        void *ptrs[] = {t->d_bins, t->d_lo, t->d_w, t->d_r, t->d_freqs, t->d_dtab, t->d_sinks,
+        void *ptrs[] = {t->d_bins, t->d_lo, t->d_w, t->d_r, t->d_freqs, t->d_dtab,
                         t->d_alo, t->d_aw, t->d_ar};
         for (void *p : ptrs)
             if (p) (void)hipFree(p);
@@ -791,3 +1159,10 @@ void cg_free(void *handle)
 }
 
 }  // extern "C"
+
+namespace {
+TablesOwner::~TablesOwner()
+{
+    if (t) cg_free(t);
+}
+}  // namespace

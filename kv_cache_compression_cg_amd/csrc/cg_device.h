@@ -8,10 +8,10 @@
 //     all lanes step through the same token at the same time, so every output row
 //     is written as one contiguous 128-byte store and the interleaved words of the
 //     group are read from a contiguous, advancing window.
-//   * Decode table entry (8 bytes) of symbol s for a lane: {f[s] | cdf[s] << 16,
-//     dequantized delta lo + s * w as fp32 bits}, two planes [32][64 lanes] per
-//     (row, block), so that all 64 lanes reading entry s of their own channel hit
-//     64 different LDS banks whatever s each lane holds.
+//   * Coder tables of one (row, block) (kTabBlock words, see cg_internal.h): a plane
+//     [32 symbols][64 lanes] of {f | cdf << 24}, a plane of the dequantized deltas
+//     lo + s * w (fp32 bits), then the 256-slot symbol table; a lane's entries sit in
+//     its own 4-byte column, so 64 lanes reading any entries hit 64 different LDS banks.
 //
 // Float rules (bit-exact with the CPU oracle): -ffp-contract=off, fp32 division and
 // reciprocal correctly rounded (HIP default), fmaf only where written, fp16 output
@@ -72,6 +72,16 @@ __device__ __forceinline__ uint32_t quantize1(float delta, float lo, float r, ui
     if (!(v > 0.0f)) return 0;
     if (v > (float)(N - 1u)) return N - 1u;
     return (uint32_t)v;
+}
+
+// Whether quantize1 had to clamp: the nearest grid point is more than half a step away
+// (floor(fma(delta - lo, r, 0.5)) outside [0, N - 1]), or the grid has zero width (r = 0,
+// the single point lo) and delta is not on it.
+__device__ __forceinline__ bool off_grid(float delta, float lo, float r, uint32_t N)
+{
+    if (r == 0.0f) return delta != lo;
+    const float v = floorf(fmaf(delta - lo, r, 0.5f));
+    return v < 0.0f || v > (float)(N - 1u);
 }
 
 // fp16_rne of fp32 fma(a, b, c), the fma rounded to fp32 first.  (The empty asm keeps

@@ -43,24 +43,52 @@ struct Paged {
     uint32_t lp, num_pages, n_blocks;
 };
 
-// Byte offsets of the container sections.
+// Byte offsets of the container sections (and the counts the sections hold).
 struct ContainerView {
     uint64_t offsets_off, anchors_off, anchors_bytes, payload_off, payload_words;
+    uint64_t sinks_off;            // fp16 [L][2][n_sink][C] from token kb * Tc
+    uint32_t n_sink;
+    uint64_t out_off, keys_off, vals_off, n_out;  // outlier sections (n_out = 0: none)
+    bool outliers;
 };
+
+constexpr uint32_t kFineBins = 256;               // fine grid of the outlier clip
 
 hipError_t launch_k0(const uint16_t *X, const Geom &g, uint32_t tpt, uint32_t *ord_lo,
                      uint32_t *ord_hi, uint32_t *flag, hipStream_t st);
-hipError_t launch_k0_finalize(const Geom &g, const uint8_t *bins, const uint32_t *ord_lo,
-                              const uint32_t *ord_hi, float *lo, float *w, float *r,
-                              hipStream_t st);
+// lo and hi (zero bounds as +0) from the ordered min / max
+hipError_t launch_k0_finalize(const Geom &g, const uint32_t *ord_lo, const uint32_t *ord_hi,
+                              float *lo, float *hi, hipStream_t st);
+// outlier table: counts of the deltas in the 256 fine intervals over [lo, hi] of every
+// channel row, then the central range (lo, hi narrowed in place)
+hipError_t launch_fine_hist(const uint16_t *X, const Geom &g, const float *lo, const float *hi,
+                            uint32_t *fine_counts, hipStream_t st);
+hipError_t launch_clip(const Geom &g, const uint32_t *fine_counts, uint32_t ppm, float *lo,
+                       float *hi, hipStream_t st);
+// w = (hi - lo) / (N - 1), r = 1 / w (0 when w = 0)
+hipError_t launch_width(const Geom &g, const uint8_t *bins, const float *lo, const float *hi,
+                        float *w, float *r, hipStream_t st);
 hipError_t launch_k1(const uint16_t *X, const Geom &g, const uint8_t *bins, uint32_t max_bins,
                      const float *lo, const float *r, uint32_t *counts, hipStream_t st);
 hipError_t launch_k1_freqs(const Geom &g, const uint8_t *bins, const uint32_t *counts,
-                           const float *lo, const float *w, uint16_t *freqs, uint32_t *dtab,
-                           hipStream_t st);
+                           uint16_t *freqs, hipStream_t st);
+// the coder tables of every (row, 64-channel block) from the frequencies and grids
+hipError_t launch_dtab(const Geom &g, const uint8_t *bins, const uint16_t *freqs,
+                       const float *lo, const float *w, uint32_t *dtab, hipStream_t st);
+// clamped (if not null) accumulates the number of elements off their grid (tokens from
+// n_sink on; with 8-bit anchors, anchors off the anchor grid too)
 hipError_t launch_k2(const uint16_t *X, const Geom &g, const uint8_t *bins, const float *lo,
                      const float *r, uint32_t t_lo, uint32_t t_hi, uint32_t tpt, uint8_t *sym,
-                     uint32_t sym_t0, uint32_t sym_T, uint16_t *anchors, hipStream_t st);
+                     uint32_t sym_t0, uint32_t sym_T, uint16_t *anchors,
+                     unsigned long long *clamped, hipStream_t st);
+// Outlier entries of the groups of chunks [g.kb, g.ke): with counts set, the number of
+// entries of every group; otherwise the entries themselves, group g from offs[g].
+hipError_t launch_outliers(const uint16_t *X, const Geom &g, const uint8_t *bins, const float *lo,
+                           const float *r, uint64_t *counts, const uint64_t *offs, uint32_t *keys,
+                           uint16_t *vals, hipStream_t st);
+// Writes a container's outlier entries into the output (contiguous, or pages of pg).
+hipError_t launch_apply_outliers(const Geom &g, const uint8_t *container, const ContainerView &cv,
+                                 uint16_t *out, const Paged &pg, hipStream_t st);
 hipError_t launch_k5_plan(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
                           const uint8_t *bins, const uint32_t *dtab, uint32_t *lane_words,
                           uint64_t *group_words, uint64_t *masks, uint32_t mstride,
@@ -80,14 +108,14 @@ hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, c
 hipError_t launch_k3_paged(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
                            const float *lo, const float *w, const uint8_t *container,
                            const ContainerView &cv, const Paged &pg, hipStream_t st);
-// Writes the stored fp16 sink rows of tokens [t_a, t_b) into the output: the contiguous
-// [L][2][S][C] out, or the pages of pg when pg.pages is set.
 // The 8-bit anchor grid of every (layer, K/V, channel) row over its anchor tokens.
 hipError_t launch_anchor_grid(const uint16_t *X, const Geom &g, float *alo, float *aw, float *ar,
                               hipStream_t st);
+// Writes the fp16 sink rows sinks [L][2][n_tok][C] (tokens t0 .. t0 + n_tok) into the
+// output: the contiguous [L][2][S][C] out, or the pages of pg when pg.pages is set.
 
-hipError_t launch_sinks(const Geom &g, const uint16_t *sinks, uint32_t n_sink, uint32_t t_a,
-                        uint32_t t_b, uint16_t *out, const Paged &pg, hipStream_t st);
+hipError_t launch_sinks(const Geom &g, const uint16_t *sinks, uint32_t n_tok, uint32_t t0,
+                        uint16_t *out, const Paged &pg, hipStream_t st);
 hipError_t launch_k4(const Geom &g, const float *lo, const float *w, const uint8_t *sym,
                      const uint8_t *container, const ContainerView &cv, uint32_t t_lo,
                      uint32_t t_hi, uint32_t tpt, uint16_t *out, hipStream_t st);

@@ -789,21 +789,22 @@ hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, c
     return hipGetLastError();
 }
 
-// Attention sinks ("Guide to CacheGen", Best Practices): the first n_sink tokens of the
-// sequence are written from their fp16 copy, [L][2][n_sink][C], one thread per 8 channels
-// of one token of one (layer, K/V) row.
+// Attention sinks ("Guide to CacheGen", Best Practices): the container's fp16 rows of
+// the sink tokens among its chunks, [L][2][n_tok][C] for tokens t0 .., written into the
+// output, one thread per 8 channels of one token of one (layer, K/V) row.
 __global__ __launch_bounds__(256) void k_sinks(Geom g, const uint16_t *__restrict__ sinks,
-                                               uint32_t n_sink, uint32_t t_a, uint32_t nt,
+                                               uint32_t n_tok, uint32_t t0,
                                                uint16_t *__restrict__ out, Paged pg)
 {
     const uint32_t O = g.C / 8;
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (uint64_t)g.L * 2 * nt * O) return;
+    if (i >= (uint64_t)g.L * 2 * n_tok * O) return;
     const uint32_t o = (uint32_t)(i % O);
     const uint64_t tmp = i / O;
-    const uint32_t t = t_a + (uint32_t)(tmp % nt);
-    const uint32_t row = (uint32_t)(tmp / nt);
-    const uint4 v = *reinterpret_cast<const uint4 *>(sinks + ((uint64_t)row * n_sink + t) * g.C + o * 8);
+    const uint32_t ti = (uint32_t)(tmp % n_tok);
+    const uint32_t row = (uint32_t)(tmp / n_tok);
+    const uint32_t t = t0 + ti;
+    const uint4 v = *reinterpret_cast<const uint4 *>(sinks + ((uint64_t)row * n_tok + ti) * g.C + o * 8);
     uint16_t *dst;
     if (pg.pages) {
         const uint32_t blk = t >> pg.lp;
@@ -818,13 +819,72 @@ __global__ __launch_bounds__(256) void k_sinks(Geom g, const uint16_t *__restric
     *reinterpret_cast<uint4 *>(dst + o * 8) = v;
 }
 
-hipError_t launch_sinks(const Geom &g, const uint16_t *sinks, uint32_t n_sink, uint32_t t_a,
-                        uint32_t t_b, uint16_t *out, const Paged &pg, hipStream_t st)
+hipError_t launch_sinks(const Geom &g, const uint16_t *sinks, uint32_t n_tok, uint32_t t0,
+                        uint16_t *out, const Paged &pg, hipStream_t st)
 {
-    if (t_b <= t_a) return hipSuccess;
-    const uint64_t n = (uint64_t)g.L * 2 * (t_b - t_a) * (g.C / 8);
+    if (!n_tok) return hipSuccess;
+    const uint64_t n = (uint64_t)g.L * 2 * n_tok * (g.C / 8);
     hipLaunchKernelGGL(k_sinks, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, g, sinks,
-                       n_sink, t_a, t_b - t_a, out, pg);
+                       n_tok, t0, out, pg);
+    return hipGetLastError();
+}
+
+// Sparse outlier table ("Guide to CacheGen", Solution pillar 3): the entries of one group
+// (chunk, row, channel block b) per wavefront, written over the decoded rows.  The
+// container is not trusted: offsets are clamped to the entry count and an entry whose
+// token or channel lies outside its group is skipped.
+template <bool PAGED>
+__global__ __launch_bounds__(256) void k_apply_outliers(Geom g, const uint8_t *__restrict__ container,
+                                                         ContainerView cv, uint64_t n_groups,
+                                                         uint16_t *__restrict__ out, Paged pg)
+{
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const uint64_t gidx = (uint64_t)blockIdx.x * (blockDim.x / kLanes) + wave;
+    if (gidx >= n_groups) return;
+    const uint32_t lane = threadIdx.x % kLanes;
+    const uint64_t *offs = reinterpret_cast<const uint64_t *>(container + cv.out_off);
+    const uint64_t beg = min(offs[gidx], cv.n_out);
+    const uint64_t end = max(beg, min(offs[gidx + 1], cv.n_out));
+    if (beg == end) return;
+    const uint32_t b = (uint32_t)(gidx % g.NB);
+    const uint64_t tmp = gidx / g.NB;
+    const uint32_t row = (uint32_t)(tmp % (2 * g.L));
+    const uint32_t k = g.kb + (uint32_t)(tmp / (2 * g.L));
+    const uint32_t t0 = k * g.Tc, len = chunk_len(g, k);
+    const uint32_t *keys = reinterpret_cast<const uint32_t *>(container + cv.keys_off);
+    const uint16_t *vals = reinterpret_cast<const uint16_t *>(container + cv.vals_off);
+    for (uint64_t e = beg + lane; e < end; e += kLanes) {
+        const uint32_t key = keys[e];
+        const uint32_t u = key >> 6, c = b * kLanes + (key & 63u);
+        if (u >= len || c >= g.C) continue;
+        const uint32_t t = t0 + u;
+        uint16_t *dst;
+        if constexpr (PAGED) {
+            const uint32_t blk = t >> pg.lp;
+            if (blk >= pg.n_blocks) continue;
+            const uint32_t id = (uint32_t)pg.bt[blk];
+            if (id >= pg.num_pages) continue;  // negative ids too
+            const uint64_t pool = ((uint64_t)pg.num_pages << pg.lp) * g.C;
+            dst = pg.pages + row * pool + (((uint64_t)id << pg.lp) + (t & ((1u << pg.lp) - 1u))) * g.C + c;
+        } else {
+            dst = out + ((uint64_t)row * g.S + t) * g.C + c;
+        }
+        *dst = vals[e];
+    }
+}
+
+hipError_t launch_apply_outliers(const Geom &g, const uint8_t *container, const ContainerView &cv,
+                                 uint16_t *out, const Paged &pg, hipStream_t st)
+{
+    if (!cv.outliers || !cv.n_out) return hipSuccess;
+    const uint64_t n_groups = (uint64_t)(g.ke - g.kb) * g.L * 2 * g.NB;
+    const uint32_t blocks = (uint32_t)((n_groups + 3) / 4);
+    if (pg.pages)
+        hipLaunchKernelGGL(k_apply_outliers<true>, dim3(blocks), dim3(256), 0, st, g, container, cv,
+                           n_groups, out, pg);
+    else
+        hipLaunchKernelGGL(k_apply_outliers<false>, dim3(blocks), dim3(256), 0, st, g, container, cv,
+                           n_groups, out, pg);
     return hipGetLastError();
 }
 

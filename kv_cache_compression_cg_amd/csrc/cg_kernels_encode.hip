@@ -93,27 +93,157 @@ __global__ __launch_bounds__(256) void k0_minmax(const uint16_t *__restrict__ X,
     if (bad) atomicOr(flag, 1u);
 }
 
-// lo, w = (hi - lo) / (N - 1), r = 1 / w per (row, channel).
-__global__ __launch_bounds__(256) void k0_finalize(Geom g, const uint8_t *__restrict__ bins,
-                                                    const uint32_t *__restrict__ ord_lo,
+// lo and hi per (row, channel) from the ordered min / max; a row with no coded token
+// gets lo = hi = 0, and a zero bound is stored as +0.
+__global__ __launch_bounds__(256) void k0_finalize(Geom g, const uint32_t *__restrict__ ord_lo,
                                                     const uint32_t *__restrict__ ord_hi,
-                                                    float *__restrict__ lo, float *__restrict__ w,
-                                                    float *__restrict__ r)
+                                                    float *__restrict__ lo, float *__restrict__ hi)
 {
     uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= g.L * 2 * g.C) return;
-    uint32_t row = i / g.C;   // (layer, K/V) row
     float a = 0.0f, b = 0.0f;
     if (ord_lo[i] != 0xFFFFFFFFu) {
         a = ord2f(ord_lo[i]);
         b = ord2f(ord_hi[i]);
     }
-    a = a + 0.0f;  // a zero bound is +0
-    b = b + 0.0f;
-    float ww = (b - a) / (float)(bins[row] - 1u);
-    lo[i] = a;
+    lo[i] = a + 0.0f;  // a zero bound is +0
+    hi[i] = b + 0.0f;
+}
+
+// w = (hi - lo) / (N - 1), r = 1 / w per (row, channel).
+__global__ __launch_bounds__(256) void k_width(Geom g, const uint8_t *__restrict__ bins,
+                                                const float *__restrict__ lo,
+                                                const float *__restrict__ hi,
+                                                float *__restrict__ w, float *__restrict__ r)
+{
+    uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= g.L * 2 * g.C) return;
+    const uint32_t row = i / g.C;   // (layer, K/V) row
+    const float ww = (hi[i] - lo[i]) / (float)(bins[row] - 1u);
     w[i] = ww;
     r[i] = (ww > 0.0f) ? 1.0f / ww : 0.0f;
+}
+
+// ------------------------------------------------------------------------------ outlier clip
+// Sparse outlier table ("Guide to CacheGen", Solution pillar 3): each channel row's grid
+// spans a central range chosen on the fine grid p_j = fma(j, wf, lo), wf = (hi - lo) / 256.
+// The fine interval of a delta is the largest j in [0, 255] with p_j <= delta (0 if
+// none): estimated from (delta - lo) / wf, then moved until exact (the points do not
+// decrease with j).
+__device__ __forceinline__ uint32_t fine_index(float dl, float lo, float wf, float rf)
+{
+    float e = floorf((dl - lo) * rf);
+    e = fminf(fmaxf(e, 0.0f), (float)(kFineBins - 1u));
+    uint32_t j = (uint32_t)e;
+    while (j < kFineBins - 1u && fmaf((float)(j + 1u), wf, lo) <= dl) ++j;
+    while (j > 0u && fmaf((float)j, wf, lo) > dl) --j;
+    return j;
+}
+
+// Counts of the coded deltas in the fine intervals, [rows][C][256].  Block = (row, tile
+// of 8 * OCT channels, token block), as in k1_hist, with an LDS histogram [256][8][OCT].
+__global__ __launch_bounds__(256) void k_fine_hist(const uint16_t *__restrict__ X, Geom g,
+                                                    const float *__restrict__ lo,
+                                                    const float *__restrict__ hi, uint32_t OCT,
+                                                    uint32_t SUB, uint32_t tpt, uint32_t ntiles,
+                                                    uint32_t ntb, uint32_t *__restrict__ counts)
+{
+    extern __shared__ uint32_t hist[];
+    const uint32_t tbb = blockIdx.x % ntb;
+    const uint32_t tmp = blockIdx.x / ntb;
+    const uint32_t ct = tmp % ntiles;
+    const uint32_t row = tmp / ntiles;
+    const uint32_t nh = kFineBins * 8 * OCT;
+    for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) hist[j] = 0;
+    __syncthreads();
+
+    const uint32_t O = g.C / 8;
+    const uint32_t ol = threadIdx.x % OCT, sub = threadIdx.x / OCT;
+    const uint32_t o = ct * OCT + ol;
+    const uint32_t t_begin = (tbb * SUB + sub) * tpt;
+    if (sub < SUB && o < O && t_begin < g.S) {
+        const uint32_t t_end = min(g.S, t_begin + tpt);
+        const uint16_t *base = X + (uint64_t)row * g.S * g.C + o * 8;
+        const uint64_t r0 = (uint64_t)row * g.C + o * 8;
+        float lo8[8], wf8[8], rf8[8], af[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            lo8[j] = lo[r0 + j];
+            wf8[j] = (hi[r0 + j] - lo8[j]) / (float)kFineBins;
+            rf8[j] = wf8[j] > 0.0f ? 1.0f / wf8[j] : 0.0f;
+        }
+        TokenWalk w;
+        w.init(g, t_begin);
+        if (w.gp != 0) {
+            uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
+            unpack8(a, af);
+            snap8(g, r0, af);
+        }
+        for (; w.t < t_end; w.next(g)) {
+            uint4 v = ntload16(base + (uint64_t)w.t * g.C);
+            float xf[8];
+            unpack8(v, xf);
+            if (w.gp == 0) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) af[j] = xf[j];
+                snap8(g, r0, af);
+            } else if (w.t >= g.n_sink) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (!(wf8[j] > 0.0f)) continue;  // nothing to narrow
+                    const uint32_t q = fine_index(xf[j] - af[j], lo8[j], wf8[j], rf8[j]);
+                    atomicAdd(&hist[(q * 8 + j) * OCT + ol], 1u);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) {
+        const uint32_t v = hist[j];
+        if (!v) continue;
+        const uint32_t s = j / (8 * OCT), rem = j - s * 8 * OCT;
+        const uint32_t jj = rem / OCT, oo = ct * OCT + rem % OCT;
+        if (oo >= O) continue;
+        atomicAdd(&counts[((uint64_t)row * g.C + oo * 8 + jj) * kFineBins + s], v);
+    }
+}
+
+// The central range of one channel row: with n coded deltas and the budget
+// b = floor(n * ppm / 10^6), whole fine intervals are dropped from the bottom while the
+// dropped count stays <= b, and from the top likewise; lo' = p_{j_lo},
+// hi' = p_{j_hi + 1} (hi when j_hi = 255), at most hi.  lo and hi are narrowed in place.
+__global__ __launch_bounds__(256) void k_clip(Geom g, const uint32_t *__restrict__ counts,
+                                               uint32_t ppm, float *__restrict__ lo,
+                                               float *__restrict__ hi)
+{
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= g.L * 2 * g.C) return;
+    const float l0 = lo[i], h0 = hi[i];
+    const float wf = (h0 - l0) / (float)kFineBins;
+    if (!(wf > 0.0f) || ppm == 0) return;
+    const uint32_t *cnt = counts + (uint64_t)i * kFineBins;
+    uint64_t n = 0;
+    for (uint32_t j = 0; j < kFineBins; ++j) n += cnt[j];
+    if (n == 0) return;
+    const uint64_t budget = (n * ppm) / 1000000u;
+    uint32_t j_lo = 0, j_hi = kFineBins - 1u;
+    uint64_t below = 0;
+    for (uint32_t j = 1; j < kFineBins; ++j) {
+        below += cnt[j - 1];
+        if (below > budget) break;
+        j_lo = j;
+    }
+    uint64_t above = 0;
+    for (uint32_t j = kFineBins - 1u; j > 0; --j) {
+        above += cnt[j];
+        if (above > budget) break;
+        j_hi = j - 1u;
+    }
+    const float lo_c = fmaf((float)j_lo, wf, l0);
+    float hi_c = (j_hi == kFineBins - 1u) ? h0 : fmaf((float)(j_hi + 1u), wf, l0);
+    if (hi_c > h0) hi_c = h0;
+    lo[i] = lo_c + 0.0f;
+    hi[i] = hi_c + 0.0f;
 }
 
 // ------------------------------------------------------------------------------ K1
@@ -187,18 +317,15 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
     }
 }
 
-// Frequencies (T = 4096, f >= 1, remainder to the most frequent symbol) and the decode
-// table of one (row, channel).
+// Frequencies of one (row, channel): T = 256, f[s] = 1 + floor(count[s] * (T - N) / n),
+// the remainder to the most frequent symbol (lowest index among equals).
 __global__ __launch_bounds__(256) void k1_freqs(Geom g, const uint8_t *__restrict__ bins,
                                                  const uint32_t *__restrict__ counts,
-                                                 const float *__restrict__ lo,
-                                                 const float *__restrict__ w,
-                                                 uint16_t *__restrict__ freqs,
-                                                 uint32_t *__restrict__ dtab)
+                                                 uint16_t *__restrict__ freqs)
 {
     uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= g.L * 2 * g.C) return;
-    uint32_t row = i / g.C, c = i - row * g.C;
+    uint32_t row = i / g.C;
     uint32_t N = bins[row];
     const uint32_t *cnt = counts + (uint64_t)i * kMaxBins;
     uint64_t n = 0;
@@ -212,17 +339,34 @@ __global__ __launch_bounds__(256) void k1_freqs(Geom g, const uint8_t *__restric
         if (cnt[s] > cnt[best]) best = s;
     }
     f[best] += kProbTotal - sum;
+    for (uint32_t s = 0; s < kMaxBins; ++s)
+        freqs[(uint64_t)i * kMaxBins + s] = (uint16_t)((s < N) ? f[s] : 0u);
+}
+
+// The coder tables of one (row, channel) from its frequencies (each >= 1, sum 256) and
+// grid: the {f | cdf << 24} plane, the dequantized deltas fma(s, w, lo), and the slot
+// table.
+__global__ __launch_bounds__(256) void k_dtab(Geom g, const uint8_t *__restrict__ bins,
+                                               const uint16_t *__restrict__ freqs,
+                                               const float *__restrict__ lo,
+                                               const float *__restrict__ w,
+                                               uint32_t *__restrict__ dtab)
+{
+    uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= g.L * 2 * g.C) return;
+    uint32_t row = i / g.C, c = i - row * g.C;
+    uint32_t N = bins[row];
+    uint32_t f[kMaxBins];
+    for (uint32_t s = 0; s < kMaxBins; ++s) f[s] = (s < N) ? freqs[(uint64_t)i * kMaxBins + s] : 0u;
     float lo1 = lo[i], w1 = w[i];
     uint32_t *tb = dtab + (uint64_t)(row * g.NB + c / kLanes) * kTabBlock + (c % kLanes);
     uint32_t cdf = 0;
     for (uint32_t s = 0; s < kMaxBins; ++s) {
-        uint32_t fs = (s < N) ? f[s] : 0;
-        freqs[(uint64_t)i * kMaxBins + s] = (uint16_t)fs;
         // (f <= 255 and cdf <= 255 since N >= 2; symbols >= N are never looked up)
-        tb[(uint64_t)s * kLanes] = (s < N) ? fs | (cdf << 24) : 0u;
+        tb[(uint64_t)s * kLanes] = (s < N) ? f[s] | (cdf << 24) : 0u;
         tb[kTabPlane + (uint64_t)s * kLanes] =
             __float_as_uint(fmaf((float)min(s, N - 1u), w1, lo1));
-        cdf += fs;
+        cdf += f[s];
     }
     // slot table: every slot in [cdf[s], cdf[s] + f[s]) names s; the byte of (slot, lane)
     // is at 256 (slot / 4) + 4 lane + slot mod 4, so each lane's slots share its own
@@ -232,7 +376,7 @@ __global__ __launch_bounds__(256) void k1_freqs(Geom g, const uint8_t *__restric
                                                kTabLut) + 4 * (c % kLanes);
     uint32_t s = 0, end = f[0];
     for (uint32_t slot = 0; slot < kProbTotal; ++slot) {
-        while (slot >= end) end += f[++s];
+        while (slot >= end && s + 1 < kMaxBins) end += f[++s];
         lut[(slot >> 2) * (4 * kLanes) + (slot & 3u)] = (uint8_t)s;
     }
 }
@@ -249,7 +393,8 @@ __global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict
                                                        uint32_t tpt, uint32_t ntb,
                                                        uint8_t *__restrict__ sym,
                                                        uint32_t sym_t0, uint32_t sym_T,
-                                                       uint16_t *__restrict__ anchors)
+                                                       uint16_t *__restrict__ anchors,
+                                                       unsigned long long *__restrict__ clamped)
 {
     const uint32_t O = g.C / 8;
     uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -278,11 +423,13 @@ __global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict
         unpack8(a, af);
         snap8(g, (uint64_t)row * g.C + o * 8, af);
     }
+    uint32_t n_off = 0;  // elements off their grid (counted from token n_sink on)
     for (; w.t < t_end; w.next(g)) {
         uint4 v = ntload16(base + (uint64_t)w.t * g.C);
         uint2 packed = make_uint2(0, 0);
         float xf[8];
         unpack8(v, xf);
+        const bool coded = w.t >= g.n_sink;
         if (w.gp == 0) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) af[j] = xf[j];
@@ -293,6 +440,7 @@ __global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict
                 uint32_t cd[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
+                    n_off += (coded && off_grid(af[j], g.alo[r0 + j], g.ar[r0 + j], 256u)) ? 1u : 0u;
                     cd[j] = quantize1(af[j], g.alo[r0 + j], g.ar[r0 + j], 256u);
                     af[j] = h2f(f2h_fma((float)cd[j], g.aw[r0 + j], g.alo[r0 + j]));
                 }
@@ -309,12 +457,81 @@ __global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict
         } else {
             uint32_t q[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) q[j] = quantize1(xf[j] - af[j], lo8[j], r8[j], N);
+            for (int j = 0; j < 8; ++j) {
+                q[j] = quantize1(xf[j] - af[j], lo8[j], r8[j], N);
+                n_off += (coded && off_grid(xf[j] - af[j], lo8[j], r8[j], N)) ? 1u : 0u;
+            }
             packed.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
             packed.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
         }
         ntstore8(sbase + (uint64_t)(w.t - sym_t0) * g.C, packed);
     }
+    if (clamped && n_off) atomicAdd(clamped, (unsigned long long)n_off);
+}
+
+// ------------------------------------------------------------------------------ outliers
+// The outlier entries of one group (chunk, row, channel block b) per wavefront, lane =
+// channel: tokens in ascending order, from n_sink on, each element tested against its
+// grid as the quantizer sees it (the delta against the anchor's decoded value; with
+// 8-bit anchors the anchor's own code against the anchor grid).  Counting pass: the
+// group's number of entries.  Writing pass: entry e of the group at offs[gidx] + e,
+// key (token within the chunk) << 6 | lane, value the element's fp16 bits; a token's
+// entries are placed in lane order by a ballot.
+template <bool WRITE>
+__global__ __launch_bounds__(256) void k_outliers(const uint16_t *__restrict__ X, Geom g,
+                                                   const uint8_t *__restrict__ bins,
+                                                   const float *__restrict__ lo,
+                                                   const float *__restrict__ r,
+                                                   uint64_t n_groups, uint64_t *__restrict__ counts,
+                                                   const uint64_t *__restrict__ offs,
+                                                   uint32_t *__restrict__ keys,
+                                                   uint16_t *__restrict__ vals)
+{
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const uint64_t gidx = (uint64_t)blockIdx.x * (blockDim.x / kLanes) + wave;
+    if (gidx >= n_groups) return;
+    const uint32_t lane = threadIdx.x % kLanes;
+    const uint32_t b = (uint32_t)(gidx % g.NB);
+    const uint64_t tmp = gidx / g.NB;
+    const uint32_t row = (uint32_t)(tmp % (2 * g.L));
+    const uint32_t k = g.kb + (uint32_t)(tmp / (2 * g.L));
+    const uint32_t c = b * kLanes + lane;
+    const bool present = c < g.C;
+    const uint32_t t0 = k * g.Tc, len = chunk_len(g, k);
+    const uint32_t N = bins[row];
+    const uint64_t ri = (uint64_t)row * g.C + (present ? c : 0u);
+    const float lo1 = lo[ri], r1 = r[ri];
+    float alo = 0.0f, aw = 0.0f, ar = 0.0f;
+    if (g.alo) {
+        alo = g.alo[ri];
+        aw = g.aw[ri];
+        ar = g.ar[ri];
+    }
+    const uint16_t *col = X + (uint64_t)row * g.S * g.C + (present ? c : 0u);
+    uint64_t run = WRITE ? offs[gidx] : 0;
+    float af = 0.0f;
+    uint32_t gp = 0;
+    for (uint32_t u = 0; u < len; ++u, gp = (gp + 1 == g.G) ? 0u : gp + 1) {
+        const uint32_t t = t0 + u;
+        const uint32_t x = col[(uint64_t)t * g.C];
+        const float xf = h2f(x);
+        bool off;
+        if (gp == 0) {
+            off = g.alo && t >= g.n_sink && off_grid(xf, alo, ar, 256u);
+            af = g.alo ? anchor_snap(xf, alo, aw, ar) : xf;
+        } else {
+            off = t >= g.n_sink && off_grid(xf - af, lo1, r1, N);
+        }
+        off = off && present;
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(off);
+        if (WRITE && off) {
+            const uint64_t e = run + mbcnt64(mask);
+            keys[e] = (u << 6) | lane;
+            vals[e] = (uint16_t)x;
+        }
+        run += (uint64_t)__builtin_popcountll(mask);
+    }
+    if (!WRITE && lane == 0) counts[gidx] = run;
 }
 
 // 8-bit anchor grid ("Guide to CacheGen", Solution pillar 2: the anchor is quantized with
@@ -693,12 +910,45 @@ hipError_t launch_k0(const uint16_t *X, const Geom &g, uint32_t tpt, uint32_t *o
     return hipGetLastError();
 }
 
-hipError_t launch_k0_finalize(const Geom &g, const uint8_t *bins, const uint32_t *ord_lo,
-                              const uint32_t *ord_hi, float *lo, float *w, float *r, hipStream_t st)
+hipError_t launch_k0_finalize(const Geom &g, const uint32_t *ord_lo, const uint32_t *ord_hi,
+                              float *lo, float *hi, hipStream_t st)
 {
     uint32_t n = g.L * 2 * g.C;
-    hipLaunchKernelGGL(k0_finalize, dim3((n + 255) / 256), dim3(256), 0, st, g, bins, ord_lo,
-                       ord_hi, lo, w, r);
+    hipLaunchKernelGGL(k0_finalize, dim3((n + 255) / 256), dim3(256), 0, st, g, ord_lo, ord_hi, lo, hi);
+    return hipGetLastError();
+}
+
+hipError_t launch_width(const Geom &g, const uint8_t *bins, const float *lo, const float *hi,
+                        float *w, float *r, hipStream_t st)
+{
+    uint32_t n = g.L * 2 * g.C;
+    hipLaunchKernelGGL(k_width, dim3((n + 255) / 256), dim3(256), 0, st, g, bins, lo, hi, w, r);
+    return hipGetLastError();
+}
+
+hipError_t launch_fine_hist(const uint16_t *X, const Geom &g, const float *lo, const float *hi,
+                            uint32_t *fine_counts, hipStream_t st)
+{
+    const uint32_t O = g.C / 8;
+    const uint32_t OCT = O < 4 ? O : 4;           // LDS: 256 bins x 8 x OCT counters
+    const uint32_t SUB = 256 / OCT;
+    const uint32_t ntiles = (O + OCT - 1) / OCT;
+    const uint64_t rows = (uint64_t)g.L * 2;
+    uint64_t ntb_target = (8192 + rows * ntiles - 1) / (rows * ntiles);
+    uint64_t tpt = (g.S + ntb_target * SUB - 1) / (ntb_target * SUB);
+    if (tpt < 16) tpt = 16;
+    uint32_t ntb = (uint32_t)((g.S + tpt * SUB - 1) / (tpt * SUB));
+    size_t lds = (size_t)kFineBins * 8 * OCT * sizeof(uint32_t);
+    hipLaunchKernelGGL(k_fine_hist, dim3((uint32_t)(rows * ntiles * ntb)), dim3(256), lds, st, X,
+                       g, lo, hi, OCT, SUB, (uint32_t)tpt, ntiles, ntb, fine_counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_clip(const Geom &g, const uint32_t *fine_counts, uint32_t ppm, float *lo,
+                       float *hi, hipStream_t st)
+{
+    uint32_t n = g.L * 2 * g.C;
+    hipLaunchKernelGGL(k_clip, dim3((n + 255) / 256), dim3(256), 0, st, g, fine_counts, ppm, lo, hi);
     return hipGetLastError();
 }
 
@@ -721,23 +971,46 @@ hipError_t launch_k1(const uint16_t *X, const Geom &g, const uint8_t *bins, uint
 }
 
 hipError_t launch_k1_freqs(const Geom &g, const uint8_t *bins, const uint32_t *counts,
-                           const float *lo, const float *w, uint16_t *freqs, uint32_t *dtab,
-                           hipStream_t st)
+                           uint16_t *freqs, hipStream_t st)
 {
     uint32_t n = g.L * 2 * g.C;
-    hipLaunchKernelGGL(k1_freqs, dim3((n + 255) / 256), dim3(256), 0, st, g, bins, counts, lo, w,
-                       freqs, dtab);
+    hipLaunchKernelGGL(k1_freqs, dim3((n + 255) / 256), dim3(256), 0, st, g, bins, counts, freqs);
+    return hipGetLastError();
+}
+
+hipError_t launch_dtab(const Geom &g, const uint8_t *bins, const uint16_t *freqs,
+                       const float *lo, const float *w, uint32_t *dtab, hipStream_t st)
+{
+    uint32_t n = g.L * 2 * g.C;
+    hipLaunchKernelGGL(k_dtab, dim3((n + 255) / 256), dim3(256), 0, st, g, bins, freqs, lo, w, dtab);
     return hipGetLastError();
 }
 
 hipError_t launch_k2(const uint16_t *X, const Geom &g, const uint8_t *bins, const float *lo,
                      const float *r, uint32_t t_lo, uint32_t t_hi, uint32_t tpt, uint8_t *sym,
-                     uint32_t sym_t0, uint32_t sym_T, uint16_t *anchors, hipStream_t st)
+                     uint32_t sym_t0, uint32_t sym_T, uint16_t *anchors,
+                     unsigned long long *clamped, hipStream_t st)
 {
     uint32_t ntb = (t_hi - t_lo + tpt - 1) / tpt;
     uint64_t threads = (uint64_t)g.L * 2 * ntb * (g.C / 8);
     hipLaunchKernelGGL(k2_delta_quant, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st,
-                       X, g, bins, lo, r, t_lo, t_hi, tpt, ntb, sym, sym_t0, sym_T, anchors);
+                       X, g, bins, lo, r, t_lo, t_hi, tpt, ntb, sym, sym_t0, sym_T, anchors,
+                       clamped);
+    return hipGetLastError();
+}
+
+hipError_t launch_outliers(const uint16_t *X, const Geom &g, const uint8_t *bins, const float *lo,
+                           const float *r, uint64_t *counts, const uint64_t *offs, uint32_t *keys,
+                           uint16_t *vals, hipStream_t st)
+{
+    const uint64_t n_groups = (uint64_t)(g.ke - g.kb) * g.L * 2 * g.NB;
+    const uint32_t blocks = (uint32_t)((n_groups + 3) / 4);
+    if (counts)
+        hipLaunchKernelGGL(k_outliers<false>, dim3(blocks), dim3(256), 0, st, X, g, bins, lo, r,
+                           n_groups, counts, offs, keys, vals);
+    else
+        hipLaunchKernelGGL(k_outliers<true>, dim3(blocks), dim3(256), 0, st, X, g, bins, lo, r,
+                           n_groups, counts, offs, keys, vals);
     return hipGetLastError();
 }
 

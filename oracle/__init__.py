@@ -463,8 +463,10 @@ def table_bytes(shp: Shape) -> int:
 
 
 def tables_bytes(shp: Shape, tab: Tables) -> bytes:
+    # a sink count above S acts as S and is stored as such
     head = np.array([TABLES_MAGIC, TABLES_VERSION, shp.L, shp.H, shp.d, shp.S, shp.G, shp.Tc,
-                     shp.n_sink, shp.anchor_bits, shp.outlier_ppm, 0], np.uint32).tobytes()
+                     min(shp.n_sink, shp.S), shp.anchor_bits, shp.outlier_ppm, 0],
+                    np.uint32).tobytes()
     parts = [head, np.array([table_bytes(shp)], np.uint64).tobytes()]
     bins = np.zeros((2 * shp.L + 3) & ~3, np.uint8)
     bins[:2 * shp.L] = shp.bins

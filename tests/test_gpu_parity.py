@@ -44,37 +44,49 @@ HEAVY = configs.GenSpec(rho=0.85, heavy_tail=True, outlier_frac=0.05, outlier_mu
 
 
 def full_parity(cg, X, H, G, Tc, bins, chunk_range=None, label="", bins_v=None, n_sink=0,
-                anchor_bits=16):
-    """Runs both sides on the same cache and compares every product of the path."""
+                anchor_bits=16, outlier_ppm=0, X_enc=None):
+    """Runs both sides on the same cache and compares every product of the path: the
+    stored tables and the whole container byte for byte, symbols, the fused and the
+    unfused decode; then a decode from the oracle's stored bytes imported into the
+    library.  X_enc: another cache of the same shape to encode with X's tables."""
     L, _, S, C = X.shape
-    _say("[parity] %s L=%d S=%d C=%d G=%d Tc=%d bins=%s bins_v=%s"
-         % (label, L, S, C, G, Tc, list(bins), None if bins_v is None else list(bins_v)))
+    _say("[parity] %s L=%d S=%d C=%d G=%d Tc=%d bins=%s bins_v=%s sinks=%d anchors=%d ppm=%d"
+         % (label, L, S, C, G, Tc, list(bins), None if bins_v is None else list(bins_v), n_sink,
+            anchor_bits, outlier_ppm))
     Xh = _u16(X)
+    Xe = X if X_enc is None else X_enc
+    Xeh = Xh if X_enc is None else _u16(X_enc)
     shp = O.Shape.make(L, H, C // H, S, G, Tc, bins, bins_v=bins_v, n_sink=n_sink,
-                       anchor_bits=anchor_bits)
+                       anchor_bits=anchor_bits, outlier_ppm=outlier_ppm)
     tab_o = O.build_tables(shp, Xh)
     kb, ke = chunk_range if chunk_range else (0, shp.n_chunks)
-    enc_o = O.encode(shp, Xh, tab_o, kb, ke)
+    enc_o = O.encode(shp, Xeh, tab_o, kb, ke)
 
     tab = cg.build_cdf(X, G, Tc, bins, H_kv=H, bins_v=bins_v, n_sink=n_sink,
-                       anchor_bits=anchor_bits)
+                       anchor_bits=anchor_bits, outlier_ppm=outlier_ppm)
     assert tab.stored_bytes == O.table_bytes(shp)
     ex = tab.export()
     for name in ("lo", "w", "r"):
         assert np.array_equal(ex[name].view(np.uint32), getattr(tab_o, name).view(np.uint32)), name
     assert np.array_equal(ex["freqs"], tab_o.freqs)
+    tb = tab.serialize()
+    assert tb == O.tables_bytes(shp, tab_o)
 
-    sym = cg.quantize(tab, X, kb, ke)
+    sym = cg.quantize(tab, Xe, kb, ke)
     t0, t1 = kb * Tc, min(ke * Tc, S)
-    sym_o = O.quantize(shp, O.snap_anchors(shp, Xh, tab_o), tab_o.lo, tab_o.r, t0, t1)
+    sym_o = O.quantize(shp, O.snap_anchors(shp, Xeh, tab_o), tab_o.lo, tab_o.r, t0, t1)
     assert np.array_equal(sym.cpu().numpy()[:, :, t0:t1], sym_o[:, :, t0:t1])
 
-    blob = cg.encode(tab, X, kb, ke)
+    blob = cg.encode(tab, Xe, kb, ke)
     assert np.array_equal(blob.offsets(), enc_o.offsets)
     assert np.array_equal(blob.anchors(), enc_o.anchors)
     assert np.array_equal(blob.payload(), enc_o.payload)
+    assert blob.header["n_outliers"] == enc_o.n_outliers and blob.header["clamped"] == enc_o.clamped
+    cb = O.container_bytes(shp, enc_o)
+    assert blob.read().tobytes() == cb
 
-    out = torch.full_like(X, float("nan"))
+    nan = float("nan")
+    out = torch.full_like(X, nan)
     cg.decode(tab, blob, out)
     ref = O.decode(shp, tab_o, enc_o, out=_u16(out))
     torch.cuda.synchronize()
@@ -82,9 +94,17 @@ def full_parity(cg, X, H, G, Tc, bins, chunk_range=None, label="", bins_v=None, 
 
     dsym = cg.decode_symbols(tab, blob)
     assert np.array_equal(dsym.cpu().numpy()[:, :, t0:t1], sym_o[:, :, t0:t1])
-    out2 = torch.full_like(X, float("nan"))
+    out2 = torch.full_like(X, nan)
     cg.dequantize(tab, blob, dsym, out2)
     assert np.array_equal(_u16(out2), _u16(out))
+
+    # a receiver that holds only the stored bytes (written by the oracle)
+    tab_i = cg.tables_import(O.tables_bytes(shp, tab_o), device=X.device)
+    blob_i = cg.blob_import(tab_i, cb)
+    out3 = torch.full_like(X, nan)
+    cg.decode(tab_i, blob_i, out3)
+    torch.cuda.synchronize()
+    assert np.array_equal(_u16(out3), _u16(out))
     return tab, blob, tab_o, enc_o
 
 
@@ -359,3 +379,113 @@ def test_format_variants_together(cg):
     X[:, :, 1:4] = 1500.0
     full_parity(cg, X, 17, 10, 100, (32, 16, 8), bins_v=(16, 8, 4), n_sink=4,
                 anchor_bits=8, label="bins_v + sinks + 8-bit anchors")
+
+
+@pytest.mark.parametrize("S,C,G,Tc,rng,ppm,n_sink,anchor_bits",
+                         [(1000, 192, 10, 300, None, 2000, 0, 16),
+                          (1000, 72, 7, 256, (1, 3), 20000, 0, 16),
+                          (2000, 136, 10, 90, None, 5000, 4, 16),
+                          (2000, 136, 10, 60, (2, 30), 1000, 0, 8),
+                          (700, 64, 10, 700, None, 250000, 9, 8),
+                          (300, 64, 1, 100, None, 50000, 0, 16)])
+def test_outlier_table(cg, S, C, G, Tc, rng, ppm, n_sink, anchor_bits):
+    """Sparse outlier table ("Guide to CacheGen", Solution pillar 3): clipped ranges,
+    tables, every byte of the container (entries included) and the decode (fused,
+    unfused, imported, paged) equal the oracle's; several tiles, partial lane blocks,
+    paired chunks, chunk ranges, sinks, 8-bit anchors, G = 1 (no coded token)."""
+    L, bins = 2, (32, 8)
+    H = {192: 3, 72: 9, 136: 17, 64: 1}[C]
+    X = _gen(L, S, C, HEAVY)
+    tab, blob, tab_o, enc_o = full_parity(cg, X, H, G, Tc, bins, chunk_range=rng, label="outliers",
+                                          n_sink=n_sink, anchor_bits=anchor_bits, outlier_ppm=ppm)
+    if G > 1:
+        assert enc_o.n_outliers > 0
+    P = 16
+    nb = -(-S // P)
+    bt = torch.randperm(nb, generator=torch.Generator().manual_seed(S + ppm)).to(torch.int32).cuda()
+    pages = torch.full((L, 2, nb, P, C), float("nan"), dtype=torch.float16, device="cuda")
+    cg.decode_paged(tab, blob, pages, bt)
+    torch.cuda.synchronize()
+    shp = O.Shape.make(L, H, C // H, S, G, Tc, bins, n_sink=n_sink, anchor_bits=anchor_bits,
+                       outlier_ppm=ppm)
+    nan16 = _u16(torch.full((1,), float("nan"), dtype=torch.float16))[0]
+    ref = O.decode(shp, tab_o, enc_o, out=np.full((L, 2, S, C), nan16, np.uint16))
+    assert np.array_equal(_u16(_gather_pages(pages, bt, S)), ref)
+
+
+@pytest.mark.parametrize("ppm,anchor_bits,n_sink", [(0, 16, 4), (3000, 16, 4), (0, 8, 4),
+                                                    (3000, 8, 12)])
+def test_another_cache_with_calibration_tables(cg, ppm, anchor_bits, n_sink):
+    """Tables built from one cache code another of the same shape: the container holds
+    the new cache's own sink rows, and the elements the tables' grids cannot hold are
+    counted as clamped or, with the outlier table, stored exactly; container and decode
+    equal the oracle's."""
+    L, S, C, G, Tc = 2, 900, 72, 10, 300
+    X = _gen(L, S, C, HEAVY)
+    Y = _gen(L, S, C, configs.GenSpec(rho=0.8, heavy_tail=True, outlier_frac=0.05,
+                                      outlier_mult=40.0, seed=9))
+    Y[:, :, 1:n_sink] = 2500.0
+    Y[0, 0, 300, 5] = 3000.0          # an anchor far outside its grid
+    tab, blob, tab_o, enc_o = full_parity(cg, X, 9, G, Tc, (16, 4), label="other cache",
+                                          n_sink=n_sink, anchor_bits=anchor_bits,
+                                          outlier_ppm=ppm, X_enc=Y)
+    out = cg.decode(tab, blob)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :, :n_sink].view(torch.int16), Y[:, :, :n_sink].view(torch.int16))
+    if ppm:
+        assert enc_o.n_outliers > 0 and blob.header["clamped"] == 0
+        assert out[0, 0, 300, 5].item() == 3000.0
+    else:
+        assert blob.header["clamped"] == enc_o.clamped > 0
+
+
+def test_import_after_the_encoder_is_gone(cg):
+    """Encode, copy the stored tables and container to host memory, free every handle of
+    the encoder, import into new handles and decode: equal to the oracle's decode.  Then
+    a streamed decode of per-chunk containers imported from bytes."""
+    L, S, C, G, Tc, H, bins = 2, 1200, 136, 10, 300, 17, (16, 8)
+    X = _gen(L, S, C, HEAVY)
+    tab = cg.build_cdf(X, G, Tc, bins, H_kv=H, n_sink=4, outlier_ppm=3000)
+    blob = cg.encode(tab, X)
+    tb, cb = tab.serialize(), blob.read().tobytes()
+    per_chunk = [cg.encode(tab, X, k, k + 1).read().tobytes() for k in range(4)]
+    del blob, tab
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    tab2 = cg.tables_import(tb)
+    blob2 = cg.blob_import(tab2, cb)
+    out = cg.decode(tab2, blob2)
+    Xh = _u16(X)
+    shp = O.Shape.make(L, H, C // H, S, G, Tc, bins, n_sink=4, outlier_ppm=3000)
+    tab_o = O.build_tables(shp, Xh)
+    enc_o = O.encode(shp, Xh, tab_o)
+    ref = O.decode(shp, tab_o, enc_o)
+    torch.cuda.synchronize()
+    assert np.array_equal(_u16(out), ref)
+    assert cb == O.container_bytes(shp, enc_o) and tb == O.tables_bytes(shp, tab_o)
+    # streamed decode from imported per-chunk containers
+    blobs = [cg.blob_import(tab2, b) for b in per_chunk]
+    hosts = [torch.from_numpy(np.frombuffer(b, np.uint8).copy()).pin_memory() for b in per_chunk]
+    slot = (max(b.nbytes for b in blobs) + 255) // 256 * 256
+    staging = torch.empty(2 * slot, dtype=torch.uint8, device="cuda")
+    out2 = torch.full_like(X, float("nan"))
+    cs, ds = torch.cuda.Stream(), torch.cuda.Stream()
+    cg.stream_decode([(tab2, b, h) for b, h in zip(blobs, hosts)], staging, 2, out2, cs, ds)
+    torch.cuda.synchronize()
+    assert np.array_equal(_u16(out2), ref)
+
+
+def test_imported_blob_must_match_its_tables(cg):
+    X = _gen(1, 300, 64, GAUSS)
+    t1 = cg.build_cdf(X, 10, 100, (8,), H_kv=1)
+    t2 = cg.build_cdf(X, 10, 100, (8,), H_kv=1, outlier_ppm=1000)
+    t3 = cg.build_cdf(X, 10, 100, (8,), H_kv=1, n_sink=4)
+    cb = cg.encode(t1, X).read().tobytes()
+    for t in (t2, t3):
+        with pytest.raises(cg.CgError) as e:
+            cg.blob_import(t, cb)
+        assert e.value.code == -5
+    with pytest.raises(cg.CgError) as e:
+        cg.blob_import(t1, cb[:-2000])
+    assert e.value.code == -5

@@ -867,7 +867,8 @@ def _parse_header(buf):
 
 
 @pytest.mark.parametrize("ppm,anchor_bits,n_sink,rng", [(0, 16, 0, None), (30000, 16, 5, None),
-                                                         (30000, 8, 5, (1, 3)), (0, 8, 200, (0, 2))])
+                                                         (30000, 8, 5, (1, 3)), (0, 8, 200, (0, 2)),
+                                                         (0, 16, 900, None)])
 def test_container_and_table_bytes_follow_their_layout(ppm, anchor_bits, n_sink, rng):
     """The stored bytes: every section 256-byte aligned after a 160-byte header, in the
     order offsets, anchors, sinks, outlier offsets / keys / values, payload, with the
@@ -913,7 +914,8 @@ def test_container_and_table_bytes_follow_their_layout(ppm, anchor_bits, n_sink,
     assert len(tb) == O.table_bytes(shp)
     import struct
     t32 = struct.unpack_from("<12I", tb, 0)
-    assert t32[:2] == (0x31544743, 1) and t32[2:11] == (L, 1, C, S, G, Tc, n_sink, anchor_bits, ppm)
+    assert t32[:2] == (0x31544743, 1)
+    assert t32[2:11] == (L, 1, C, S, G, Tc, min(n_sink, S), anchor_bits, ppm)
     assert struct.unpack_from("<Q", tb, 48)[0] == len(tb)
     off = 56 + 4
     assert list(tb[56:56 + 2 * L]) == list(shp.bins)
