@@ -13,10 +13,15 @@ metric), from HIP events around each decode on the stream it runs on, averaged o
 and two untimed decodes (the container resident in HBM).  `decode_ms_in_step` is the decode inside the steps,
 right after each step's encode.  `ms_per_step` is the wall time of a whole step.
 
+Beside it: the encode (cg_build_cdf + cg_encode) time and % of HBM, a measured device copy
+bandwidth, bits per symbol against the empirical entropy per bin tier, and the oracle's
+encode and decode throughput on the host CPUs (`cpu_baseline`).
+
 An object "paged" decodes the same container into a paged cache (16-token pages, a
-shuffled block table); "kv_asymmetric" covers the same cache with the V rows one step
-coarser than the K rows, "sinks" with the first four tokens kept in fp16, and "anchors8"
-with 8-bit anchors (decode throughput and ratio).  An object "streamed" covers the streamed
+shuffled block table); "outliers" codes the cache with the sparse outlier table (ratio,
+entries, error, decode throughput); "kv_asymmetric" covers the same cache with the V rows
+one step coarser than the K rows, "sinks" with the first four tokens kept in fp16, and
+"anchors8" with 8-bit anchors (decode throughput and ratio).  An object "streamed" covers the streamed
 decode of the 131K-token cache
 (L=80, S=131072, 42.95 GB): every chunk encoded at three levels, one level per chunk
 chosen from a seeded bandwidth trace, the chosen containers copied from pinned host
@@ -76,42 +81,154 @@ def measured_traffic(alg_bytes: float):
     return d.get("bytes_per_launch")
 
 
+def host_info() -> dict:
+    """Host CPU facts for the oracle leg: logical CPUs, the ones this process may use,
+    the cgroup CPU quota if any, and the CPU model."""
+    info = {"nproc": os.cpu_count()}
+    try:
+        info["affinity"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    try:
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        info["cgroup_cpu_quota"] = None if q == "max" else round(int(q) / int(per), 2)
+    except (OSError, ValueError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(w, X, max_threads: int) -> dict:
-    """The oracle (as it stands) decoding a bounded sample of the same workload."""
+    """The oracle (as it stands) encoding and decoding a bounded sample of the same
+    workload: 16 of the 80 layers (every fifth, the bin tiers in the workload's 2:2:4
+    ratio), all chunks, K and V.  Encode = tables (range, quantize, histogram,
+    frequencies) + coding of every chunk; decode = every chunk back to fp16.  Layers and
+    chunk ranges are spread over a thread pool of the host CPUs this GPU's share allows."""
     import numpy as np
     import torch
 
     import oracle as O
 
-    cores = max(1, min(max_threads, os.cpu_count() or 1))
+    hinfo = host_info()
+    avail = hinfo.get("affinity") or os.cpu_count() or 1
+    if hinfo.get("cgroup_cpu_quota"):
+        avail = min(avail, max(1, int(hinfo["cgroup_cpu_quota"])))
+    cores = max(1, min(max_threads, avail))
     layers = CPU_SAMPLE_LAYERS
     host = {l: np.ascontiguousarray(X[l:l + 1].cpu().view(torch.int16).numpy().view(np.uint16))
             for l in layers}
     shapes = {l: O.Shape.make(1, w.H_kv, w.d, w.S, w.group, w.chunk, [w.bins[l]]) for l in layers}
-    t = time.time()
     with cf.ThreadPoolExecutor(cores) as ex:
+        t0 = time.perf_counter()
         tabs = dict(zip(layers, ex.map(lambda l: O.build_tables(shapes[l], host[l]), layers)))
-        # split each layer into chunk ranges so the decode spreads over every thread
+        t_tab = time.perf_counter() - t0
+        # split each layer into chunk ranges so the work spreads over every thread
         per = max(1, -(-w.n_chunks * len(layers) // (2 * cores)))
         items = [(l, k0, min(k0 + per, w.n_chunks)) for l in layers
                  for k0 in range(0, w.n_chunks, per)]
+        t0 = time.perf_counter()
         encs = list(ex.map(lambda it: O.encode(shapes[it[0]], host[it[0]], tabs[it[0]],
                                                it[1], it[2]), items))
-        log("[cpu] oracle prep (tables + encode of %d layers) %.1fs" % (len(layers),
-                                                                       time.time() - t))
+        t_enc = time.perf_counter() - t0
         outs = {l: np.zeros((1, 2, w.S, w.C), np.uint16) for l in layers}
         t0 = time.perf_counter()
         list(ex.map(lambda ie: O.decode(shapes[ie[0][0]], tabs[ie[0][0]], ie[1],
                                         out=outs[ie[0][0]]), zip(items, encs)))
-        dt = time.perf_counter() - t0
+        t_dec = time.perf_counter() - t0
     for l in layers:
         assert np.array_equal(outs[l][:, :, ::w.group][:, :, :w.chunk // w.group],
                               host[l][:, :, ::w.group][:, :, :w.chunk // w.group])
     raw = len(layers) * 2 * w.C * w.S * 2
-    return {"value": round(raw / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": "oracle decode of layers %s (all 22 chunks, K and V; %.2f GB raw), "
-                      "%d threads over (layer, chunk-range) items, %.2fs wall"
-                      % (list(layers), raw / 1e9, cores, dt)}
+    log("[cpu] oracle on %d threads: tables %.2fs, encode %.2fs, decode %.2fs (%.2f GB raw)"
+        % (cores, t_tab, t_enc, t_dec, raw / 1e9))
+    res = {"value": round(raw / t_dec / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": "oracle decode of layers %s (all %d chunks, K and V; %.2f GB raw), "
+                     "%d threads over (layer, chunk-range) items, %.2fs wall"
+                     % (list(layers), w.n_chunks, raw / 1e9, cores, t_dec),
+           "decode_GBps": round(raw / t_dec / 1e9, 4),
+           "encode_GBps": round(raw / (t_tab + t_enc) / 1e9, 4),
+           "encode_s": {"tables": round(t_tab, 3), "coding": round(t_enc, 3)},
+           "decode_s": round(t_dec, 3), "sample_raw_bytes": raw}
+    res.update(hinfo)
+    return res
+
+
+def copy_bandwidth(dev, reps: int = 5, nbytes: int = 4 << 30) -> dict:
+    """A plain device-to-device copy (torch, one kernel) of 4 GiB, timed with HIP events:
+    read + write bytes per second, the practical HBM ceiling on this machine."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    del src, dst
+    torch.cuda.empty_cache()
+    gbps = 2 * nbytes / (ms[len(ms) // 2] * 1e-3) / 1e9
+    return {"bytes": nbytes, "reps": reps, "median_ms": round(ms[len(ms) // 2], 4),
+            "GBps_read_plus_write": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
+
+
+def entropy_report(w, X, tab, blob) -> dict:
+    """Bits per coded symbol against the empirical entropy, per bin tier: the symbols
+    (cg_quantize) counted per channel row over the coded tokens, H_emp = sum n H(counts/n),
+    the tables' cross-entropy sum count * log2(256 / f), and the payload's 16 bits per word
+    (the groups' word counts from the container's offsets)."""
+    import numpy as np
+    import torch
+
+    from kv_cache_compression_cg_amd import cg
+    dev = X.device
+    tt = torch.arange(w.S, device=dev)
+    coded = ((tt % w.chunk) % w.group) != 0
+    freqs = torch.from_numpy(tab.export()["freqs"].astype(np.float64)).to(dev)  # [L,2,C,32]
+    offs = blob.offsets().astype(np.int64)
+    words = offs[1:] - offs[:-1]
+    NB = -(-w.C // 64)
+    per_layer = words.reshape(w.n_chunks, w.L, 2, NB).sum(axis=(0, 2, 3))
+    tiers = {}
+    sym = cg.quantize(tab, X)                          # uint8 [L, 2, S, C]
+    for l in range(w.L):
+        s = sym[l][:, coded].long()                     # [2, T, C]
+        idx = (torch.arange(2 * w.C, device=dev).view(2, 1, w.C) * 32 + s).reshape(-1)
+        cnt = torch.bincount(idx, minlength=2 * w.C * 32).double().view(2, w.C, 32)
+        n = cnt.sum(-1, keepdim=True)
+        p = cnt / n.clamp_min(1)
+        h_emp = float(-(cnt * torch.log2(p.clamp_min(1e-300))).sum())
+        f = freqs[l]
+        h_tab = float((cnt * torch.log2(256.0 / f.clamp_min(1))).sum())
+        b = w.bins[l]
+        t = tiers.setdefault(str(b), {"layers": 0, "symbols": 0, "H_emp_bits": 0.0,
+                                      "table_bits": 0.0, "payload_bits": 0})
+        t["layers"] += 1
+        t["symbols"] += int(n.sum())
+        t["H_emp_bits"] += h_emp
+        t["table_bits"] += h_tab
+        t["payload_bits"] += int(per_layer[l]) * 16
+    del sym
+    out = {}
+    for b, t in tiers.items():
+        m = t["symbols"]
+        out["bins_" + b] = {"layers": t["layers"], "symbols": m,
+                            "H_emp_bits_per_symbol": round(t["H_emp_bits"] / m, 4),
+                            "table_cross_entropy_bits_per_symbol": round(t["table_bits"] / m, 4),
+                            "payload_bits_per_symbol": round(t["payload_bits"] / m, 4),
+                            "payload_over_H_emp": round(t["payload_bits"] / t["H_emp_bits"], 4)}
+    torch.cuda.empty_cache()
+    return out
 
 
 def streamed_report(dev, n_slots: int = 8, reps: int = 3, seed: int = 0) -> dict:
@@ -317,6 +434,69 @@ def sinks_report(w, X, out, reps: int, n_sink: int = 4) -> dict:
     return res
 
 
+OUTLIER_PPM = 1000          # 0.1% of each channel row's deltas may fall out at each end
+ERROR_LAYERS = (0, 40, 79)  # one layer of each bin tier
+
+
+def outliers_report(w, X, out_plain, tab_plain, reps: int) -> dict:
+    """Sparse outlier table ("Guide to CacheGen", Solution pillar 3): each channel row's
+    grid spans the central range leaving at most 0.1% of its deltas out at each end, and
+    every element off the grid is stored exactly.  Reported: the ratio and the entries,
+    the decode throughput over back-to-back decodes, the narrowing of the bin widths, and
+    the reconstruction error against the plain codec on one layer of each bin tier."""
+    import numpy as np
+    import torch
+
+    from kv_cache_compression_cg_amd import cg
+    tab = cg.build_cdf(X, w.group, w.chunk, w.bins, H_kv=w.H_kv, outlier_ppm=OUTLIER_PPM)
+    blob = cg.encode(tab, X)
+    out = torch.empty_like(X)
+    stream = torch.cuda.current_stream(X.device)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps + 2)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        cg.decode(tab, blob, out)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev[2:]]
+    dec = sum(ms) / len(ms)
+    h = blob.header
+    w_full, w_clip = tab_plain.export()["w"], tab.export()["w"]
+    ok = w_full > 0
+    narrow = np.median(w_clip[ok] / w_full[ok])
+    errs = {}
+    for name, y in (("plain", out_plain), ("outliers", out)):
+        tot, n, mx = 0.0, 0, 0.0
+        for l in ERROR_LAYERS:
+            e = (X[l].float() - y[l].float()).abs()
+            wf = torch.from_numpy(w_full[l]).to(X.device)[:, None, :]
+            tot += float(e.double().sum())
+            n += e.numel()
+            mx = max(mx, float((e / (wf / 2).clamp_min(1e-30)).max()))
+        errs[name] = {"mean_abs_error": tot / n, "max_error_over_full_half_bin": round(mx, 4)}
+    comp = cg.compressed_bytes(tab, [blob])
+    res = {"outlier_ppm": OUTLIER_PPM, "workload": w.name,
+           "n_outliers": int(h["n_outliers"]),
+           "outlier_fraction": round(h["n_outliers"] / (w.raw_bytes / 2), 6),
+           "outlier_section_bytes": int(h["payload_offset"] - h["outliers_offset"]),
+           "compression_ratio": round(w.raw_bytes / comp, 4), "compressed_bytes": comp,
+           "median_bin_width_clipped_over_full": round(float(narrow), 4),
+           "error_layers": list(ERROR_LAYERS), "error": errs,
+           "mean_abs_error_ratio": round(errs["outliers"]["mean_abs_error"]
+                                         / errs["plain"]["mean_abs_error"], 4),
+           "decode_ms": round(dec, 4), "decode_reps": len(ms),
+           "value_GBps": round(w.raw_bytes / (dec * 1e-3) / 1e9, 2),
+           "pct_hbm_peak": round(100 * w.raw_bytes / (dec * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+    log("[outliers] %d entries (%.4f%%), ratio %.3f, bin width x%.3f, mean |error| x%.3f, "
+        "decode %.3f ms (%.1f GB/s)" % (res["n_outliers"], 100 * res["outlier_fraction"],
+                                       res["compression_ratio"], narrow,
+                                       res["mean_abs_error_ratio"], dec, res["value_GBps"]))
+    del blob, tab, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_loop(w, dev, n: int) -> dict:
     """One encode of the workload, then n decodes back to back on one stream, each timed
     with HIP events; the rest of the step is left out, so that a counter run or a power
@@ -357,7 +537,10 @@ def main() -> int:
                     help="skip the streamed decode of the 131K-token cache")
     ap.add_argument("--only-streamed", action="store_true",
                     help="run only the streamed decode of the 131K-token cache (profiling)")
-    ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--cpu-threads", type=int, default=16,
+                    help="oracle threads: the host CPUs one GPU's share of the box allows")
+    ap.add_argument("--no-entropy", action="store_true",
+                    help="skip the bits-per-symbol against empirical entropy report")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 4 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--no-kv-asymmetric", action="store_true",
@@ -408,18 +591,23 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     def step():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         ts = time.perf_counter()
+        ev[0].record(stream)
         tab = cg.build_cdf(X, w.group, w.chunk, w.bins, H_kv=w.H_kv)
         blob = cg.encode(tab, X)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        ev[1].record(stream)
+        tw = time.perf_counter()
+        ev[2].record(stream)
         cg.decode(tab, blob, out)
-        e1.record(stream)
+        ev[3].record(stream)
         torch.cuda.synchronize()
         te = time.perf_counter()
-        return e0.elapsed_time(e1), (te - ts) * 1e3, tab, blob
+        return (ev[2].elapsed_time(ev[3]), (te - ts) * 1e3, ev[0].elapsed_time(ev[1]),
+                (tw - ts) * 1e3, tab, blob)
 
+    copy = copy_bandwidth(dev)
+    log("[bench] device copy of 4 GiB: %.1f GB/s read + write" % copy["GBps_read_plus_write"])
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -427,8 +615,8 @@ def main() -> int:
     t0 = time.perf_counter()
     for _ in range(args.steps):
         last = None                      # the previous step's handles are released here
-        dms, sms, tab, blob = step()
-        recs.append((dms, sms))
+        dms, sms, ems, ewall, tab, blob = step()
+        recs.append((dms, sms, ems, ewall))
         last = (tab, blob)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -436,6 +624,8 @@ def main() -> int:
     tab, blob = last
     in_step_ms = [r[0] for r in recs]
     step_ms = [r[1] for r in recs]
+    enc_ev_ms = [r[2] for r in recs]
+    enc_wall_ms = [r[3] for r in recs]
     # Decode phase: cg_decode of the last step's container, back to back, each launch timed
     # with HIP events.  Inside a step the decode follows that step's encode directly and
     # runs while the encoder's freshly written container and scratch are still being
@@ -454,6 +644,7 @@ def main() -> int:
     torch.cuda.synchronize()
     dec_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     dec_mean = sum(dec_ms) / len(dec_ms)
+    dec_sorted = sorted(dec_ms)
     value = w.raw_bytes / (dec_mean * 1e-3) / 1e9
 
     # sanity: anchors bit-exact, first layer within half a bin
@@ -486,21 +677,40 @@ def main() -> int:
         "compression_ratio": round(w.raw_bytes / comp, 4),
         "compressed_bytes": {"total": comp, "payload": 2 * h["payload_words"],
                              "anchors": h["anchors_bytes"],
-                             "offsets_and_header": h["payload_offset"] - h["anchors_bytes"],
+                             "header_offsets_padding": comp - 2 * h["payload_words"]
+                             - h["anchors_bytes"] - tab.stored_bytes,
                              "tables": tab.stored_bytes},
-        "decode_ms": round(dec_mean, 4), "decode_ms_min": round(min(dec_ms), 4),
+        "value_loop": "decode phase: %d back-to-back cg_decode calls of the last step's "
+                      "resident container, each timed with HIP events on the library's "
+                      "stream, after %d untimed ones" % (len(dec_ms), DECODE_WARMUP),
+        "decode_ms": round(dec_mean, 4), "decode_ms_min": round(dec_sorted[0], 4),
+        "decode_ms_median": round(dec_sorted[len(dec_sorted) // 2], 4),
+        "decode_ms_max": round(dec_sorted[-1], 4),
         "decode_reps": len(dec_ms), "decode_warmup": DECODE_WARMUP,
         "decode_ms_in_step": round(sum(in_step_ms) / len(in_step_ms), 4),
-        "encode_ms": round(sum(step_ms) / len(step_ms) - sum(in_step_ms) / len(in_step_ms), 3),
+        "pct_hbm_peak_in_step": round(100 * w.raw_bytes / (sum(in_step_ms) / len(in_step_ms)
+                                                          * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "target_pct_hbm_peak": 40.0,
+        "encode_ms": round(sum(enc_ev_ms) / len(enc_ev_ms), 3),
+        "encode_ms_wall": round(sum(enc_wall_ms) / len(enc_wall_ms), 3),
+        "encode_timing": "cg_build_cdf + cg_encode, HIP events on the library's stream "
+                         "before the first and after the last call (host work between "
+                         "kernels included); wall: host clock around both calls",
+        "copy": copy,
         "roofline": roofline,
     }
     res["encode_GBps"] = round(w.raw_bytes / (res["encode_ms"] * 1e-3) / 1e9, 2)
+    res["encode_pct_hbm_peak"] = round(100 * res["encode_GBps"] / HBM_PEAK_GBPS, 2)
     log("[bench] decode %.3f ms (%.1f GB/s, %.1f%% of HBM peak; %.3f ms inside the steps), "
         "step %.1f ms, ratio %.3f" % (dec_mean, value, res["pct_hbm_peak"],
                                      res["decode_ms_in_step"], res["ms_per_step"],
                                      res["compression_ratio"]))
+    if not args.no_entropy:
+        res["entropy"] = entropy_report(w, X, tab, blob)
+        log("[entropy] %s" % json.dumps(res["entropy"]))
     if not args.no_kv_asymmetric:
         res["paged"] = paged_report(w, tab, blob, out, args.decode_reps)
+        res["outliers"] = outliers_report(w, X, out, tab, args.decode_reps)
         res["kv_asymmetric"] = kv_asymmetric_report(w, X, out, args.decode_reps)
         res["sinks"] = sinks_report(w, X, out, args.decode_reps)
         res["anchors8"] = anchors8_report(w, X, out, args.decode_reps)
