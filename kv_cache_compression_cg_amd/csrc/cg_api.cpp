@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -107,6 +108,57 @@ const char *shape_error(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t
         return "cache too large";
     return nullptr;
 }
+
+// Scratch kept between calls, one area per device (grown when a call needs more).
+// Calls that use it hold the lock from their first launch to their last wait, so a
+// kernel never runs on an area another call is about to replace.
+struct Arena {
+    int device;
+    void *p;
+    uint64_t bytes;
+};
+std::mutex g_arena_mu;
+std::vector<Arena> g_arenas;
+
+// Scratch of at least `bytes` on `device` (the caller holds g_arena_mu).
+hipError_t arena_get(int device, uint64_t bytes, uint8_t **out)
+{
+    Arena *a = nullptr;
+    for (Arena &x : g_arenas)
+        if (x.device == device) a = &x;
+    if (!a) {
+        g_arenas.push_back(Arena{device, nullptr, 0});
+        a = &g_arenas.back();
+    }
+    if (a->bytes < bytes) {
+        if (a->p) {
+            hipError_t e = hipFree(a->p);
+            a->p = nullptr;
+            a->bytes = 0;
+            if (e != hipSuccess) return e;
+        }
+        const uint64_t want = (bytes + (bytes >> 4) + 0xFFFFF) & ~uint64_t(0xFFFFF);  // +1/16
+        hipError_t e = hipMalloc(&a->p, want);
+        if (e != hipSuccess) {
+            a->p = nullptr;
+            return e;
+        }
+        a->bytes = want;
+    }
+    *out = static_cast<uint8_t *>(a->p);
+    return hipSuccess;
+}
+
+// Consecutive 256-byte aligned pieces of one scratch area.
+struct Carve {
+    uint64_t used = 0;
+    uint64_t take(uint64_t bytes)
+    {
+        const uint64_t at = used;
+        used += (bytes + 255) & ~uint64_t(255);
+        return at;
+    }
+};
 
 }  // namespace
 
@@ -361,39 +413,39 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     TablesOwner owner{t};
 
     const uint64_t rows = (uint64_t)t->L * 2 * t->C;
-    DevBuf ordlo, ordhi, hi, counts, flag, fine;
-    CG_HIP(ordlo.alloc(rows * 4), "hipMalloc");
-    CG_HIP(ordhi.alloc(rows * 4), "hipMalloc");
-    CG_HIP(hi.alloc(rows * 4), "hipMalloc");
-    CG_HIP(counts.alloc(rows * kMaxBins * 4), "hipMalloc");
-    CG_HIP(flag.alloc(4), "hipMalloc");
-    CG_HIP(hipMemsetAsync(ordlo.p, 0xFF, rows * 4, st), "memset");
-    CG_HIP(hipMemsetAsync(ordhi.p, 0x00, rows * 4, st), "memset");
-    CG_HIP(hipMemsetAsync(counts.p, 0, rows * kMaxBins * 4, st), "memset");
-    CG_HIP(hipMemsetAsync(flag.p, 0, 4, st), "memset");
+    Carve cv;
+    const uint64_t o_lo = cv.take(rows * 4), o_hi = cv.take(rows * 4), o_h = cv.take(rows * 4);
+    const uint64_t o_cnt = cv.take(rows * kMaxBins * 4), o_flag = cv.take(4);
+    const uint64_t o_fine = t->outlier_ppm ? cv.take(rows * kFineBins * 4) : 0;
+    std::lock_guard<std::mutex> lock(g_arena_mu);
+    uint8_t *sc = nullptr;
+    CG_HIP(arena_get(t->device, cv.used, &sc), "scratch");
+    uint32_t *ordlo = reinterpret_cast<uint32_t *>(sc + o_lo), *ordhi = reinterpret_cast<uint32_t *>(sc + o_hi);
+    float *hi = reinterpret_cast<float *>(sc + o_h);
+    uint32_t *counts = reinterpret_cast<uint32_t *>(sc + o_cnt), *flag = reinterpret_cast<uint32_t *>(sc + o_flag);
+    uint32_t *fine = reinterpret_cast<uint32_t *>(sc + o_fine);
+    CG_HIP(hipMemsetAsync(ordlo, 0xFF, rows * 4, st), "memset");
+    CG_HIP(hipMemsetAsync(ordhi, 0x00, rows * 4, st), "memset");
+    CG_HIP(hipMemsetAsync(counts, 0, rows * kMaxBins * 4, st), "memset");
+    CG_HIP(hipMemsetAsync(flag, 0, 4, st), "memset");
 
     const uint16_t *X = static_cast<const uint16_t *>(kv_dev);
     Geom g = make_geom(t, 0, ceil_div(t->S, t->Tc));
     if (t->d_alo)
         CG_HIP(launch_anchor_grid(X, g, t->d_alo, t->d_aw, t->d_ar, st), "k_anchor_grid");
-    CG_HIP(launch_k0(X, g, pick_tpt(t, t->S), ordlo.as<uint32_t>(), ordhi.as<uint32_t>(),
-                     flag.as<uint32_t>(), st),
-           "k0_minmax");
-    CG_HIP(launch_k0_finalize(g, ordlo.as<uint32_t>(), ordhi.as<uint32_t>(), t->d_lo, hi.as<float>(), st),
-           "k0_finalize");
+    CG_HIP(launch_k0(X, g, pick_tpt(t, t->S), ordlo, ordhi, flag, st), "k0_minmax");
+    CG_HIP(launch_k0_finalize(g, ordlo, ordhi, t->d_lo, hi, st), "k0_finalize");
     if (t->outlier_ppm) {
-        CG_HIP(fine.alloc(rows * kFineBins * 4), "hipMalloc");
-        CG_HIP(hipMemsetAsync(fine.p, 0, rows * kFineBins * 4, st), "memset");
-        CG_HIP(launch_fine_hist(X, g, t->d_lo, hi.as<float>(), fine.as<uint32_t>(), st), "k_fine_hist");
-        CG_HIP(launch_clip(g, fine.as<uint32_t>(), t->outlier_ppm, t->d_lo, hi.as<float>(), st), "k_clip");
+        CG_HIP(hipMemsetAsync(fine, 0, rows * kFineBins * 4, st), "memset");
+        CG_HIP(launch_fine_hist(X, g, t->d_lo, hi, fine, st), "k_fine_hist");
+        CG_HIP(launch_clip(g, fine, t->outlier_ppm, t->d_lo, hi, st), "k_clip");
     }
-    CG_HIP(launch_width(g, t->d_bins, t->d_lo, hi.as<float>(), t->d_w, t->d_r, st), "k_width");
-    CG_HIP(launch_k1(X, g, t->d_bins, t->max_bins, t->d_lo, t->d_r, counts.as<uint32_t>(), st),
-           "k1_hist");
-    CG_HIP(launch_k1_freqs(g, t->d_bins, counts.as<uint32_t>(), t->d_freqs, st), "k1_freqs");
+    CG_HIP(launch_width(g, t->d_bins, t->d_lo, hi, t->d_w, t->d_r, st), "k_width");
+    CG_HIP(launch_k1(X, g, t->d_bins, t->max_bins, t->d_lo, t->d_r, counts, st), "k1_hist");
+    CG_HIP(launch_k1_freqs(g, t->d_bins, counts, t->d_freqs, st), "k1_freqs");
     CG_HIP(launch_dtab(g, t->d_bins, t->d_freqs, t->d_lo, t->d_w, t->d_dtab, st), "k_dtab");
     uint32_t h_flag = 0;
-    CG_HIP(hipMemcpyAsync(&h_flag, flag.p, 4, hipMemcpyDeviceToHost, st), "copy flag");
+    CG_HIP(hipMemcpyAsync(&h_flag, flag, 4, hipMemcpyDeviceToHost, st), "copy flag");
     CG_HIP(hipStreamSynchronize(st), "hipStreamSynchronize");
     if (h_flag) return fail(CG_E_NONFINITE, "KV input holds Inf or NaN");
     owner.t = nullptr;
@@ -415,52 +467,33 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     const uint16_t *X = static_cast<const uint16_t *>(kv_dev);
     Geom g = make_geom(t, kb, ke);
     const uint32_t t_lo = kb * t->Tc;
-    const uint32_t t_hi = (ke * (uint64_t)t->Tc < t->S) ? ke * t->Tc : t->S;
-    const uint32_t T_r = t_hi - t_lo;
     const uint64_t n_groups = (uint64_t)(ke - kb) * t->L * 2 * t->NB;
-    const uint64_t arows = anchor_rows(t->L, t->S, t->G, t->Tc, kb, ke);
+    const uint64_t C = t->C;
+    const uint64_t anchor_bytes = anchor_rows(t->L, t->S, t->G, t->Tc, kb, ke) * C *
+                                  (t->anchor_bits == 8 ? 1u : 2u);
+    const uint64_t region_words = code_region_words(g);
 
-    // word-read ballots of every step of every group, 64 steps per row chunk
-    const uint32_t full = t->Tc < t->S ? t->Tc : t->S;
-    const uint32_t mstride = (full - ceil_div(full, t->G) + 63) / 64 * 64;
-    DevBuf sym, anc, lane_words, group_words, group_off, masks, counters, ocount, ooff;
-    CG_HIP(sym.alloc((uint64_t)t->L * 2 * T_r * t->C), "hipMalloc symbols");
-    CG_HIP(anc.alloc(arows * t->C * 2), "hipMalloc anchors");
-    CG_HIP(lane_words.alloc(n_groups * kLanes * 4), "hipMalloc");
-    CG_HIP(group_words.alloc(n_groups * 8), "hipMalloc");
-    CG_HIP(group_off.alloc((n_groups + 1) * 8), "hipMalloc");
-    CG_HIP(masks.alloc(n_groups * (mstride ? mstride : 1) * 8), "hipMalloc ballots");
-    CG_HIP(counters.alloc(8), "hipMalloc");
-    CG_HIP(hipMemsetAsync(counters.p, 0, 8, st), "memset");
-    if (t->outlier_ppm) {
-        CG_HIP(ocount.alloc(n_groups * 8), "hipMalloc");
-        CG_HIP(ooff.alloc((n_groups + 1) * 8), "hipMalloc");
-    }
+    // scratch: the groups' word regions, the anchors section, per-group counts and offsets
+    Carve cv;
+    const uint64_t o_reg = cv.take(n_groups * region_words * 2), o_anc = cv.take(anchor_bytes);
+    const uint64_t o_gw = cv.take(n_groups * 8), o_go = cv.take((n_groups + 1) * 8);
+    const uint64_t o_ow = cv.take(n_groups * 8), o_oo = cv.take((n_groups + 1) * 8);
+    std::lock_guard<std::mutex> lock(g_arena_mu);
+    uint8_t *sc = nullptr;
+    CG_HIP(arena_get(t->device, cv.used, &sc), "scratch");
+    uint16_t *regions = reinterpret_cast<uint16_t *>(sc + o_reg);
+    uint8_t *anc = sc + o_anc;
+    uint64_t *gwords = reinterpret_cast<uint64_t *>(sc + o_gw), *goff = reinterpret_cast<uint64_t *>(sc + o_go);
+    uint64_t *gout = reinterpret_cast<uint64_t *>(sc + o_ow), *ooff = reinterpret_cast<uint64_t *>(sc + o_oo);
 
-    CG_HIP(launch_k2(X, g, t->d_bins, t->d_lo, t->d_r, t_lo, t_hi, pick_tpt(t, T_r), sym.as<uint8_t>(),
-                     t_lo, T_r, anc.as<uint16_t>(), counters.as<unsigned long long>(), st),
-           "k2_delta_quant");
-    CG_HIP(launch_k5_plan(sym.as<uint8_t>(), t_lo, T_r, g, t->d_bins, t->d_dtab,
-                          lane_words.as<uint32_t>(), group_words.as<uint64_t>(),
-                          masks.as<uint64_t>(), mstride, st),
-           "k5_plan");
-    CG_HIP(launch_scan(group_words.as<uint64_t>(), group_off.as<uint64_t>(), n_groups, st), "scan");
-    if (t->outlier_ppm) {
-        CG_HIP(launch_outliers(X, g, t->d_bins, t->d_lo, t->d_r, ocount.as<uint64_t>(), nullptr,
-                               nullptr, nullptr, st),
-               "k_outliers (count)");
-        CG_HIP(launch_scan(ocount.as<uint64_t>(), ooff.as<uint64_t>(), n_groups, st), "scan");
-    }
-    uint64_t sizes[3] = {0, 0, 0};  // payload words, elements off their grid, outlier entries
-    CG_HIP(hipMemcpyAsync(&sizes[0], group_off.as<uint64_t>() + n_groups, 8, hipMemcpyDeviceToHost, st),
-           "copy size");
-    CG_HIP(hipMemcpyAsync(&sizes[1], counters.p, 8, hipMemcpyDeviceToHost, st), "copy count");
-    if (t->outlier_ppm)
-        CG_HIP(hipMemcpyAsync(&sizes[2], ooff.as<uint64_t>() + n_groups, 8, hipMemcpyDeviceToHost, st),
-               "copy count");
+    CG_HIP(launch_k5_code(X, g, t->d_bins, t->d_dtab, t->d_lo, t->d_r, regions, anc, gwords, gout, st),
+           "k5_code");
+    CG_HIP(launch_scan(gwords, goff, n_groups, st), "scan");
+    CG_HIP(launch_scan(gout, ooff, n_groups, st), "scan");
+    uint64_t sizes[2] = {0, 0};  // payload words, elements off their grid
+    CG_HIP(hipMemcpyAsync(&sizes[0], goff + n_groups, 8, hipMemcpyDeviceToHost, st), "copy size");
+    CG_HIP(hipMemcpyAsync(&sizes[1], ooff + n_groups, 8, hipMemcpyDeviceToHost, st), "copy count");
     CG_HIP(hipStreamSynchronize(st), "hipStreamSynchronize");
-    if (t->outlier_ppm && sizes[2] != sizes[1])
-        return fail(CG_E_HIP, "internal: the outlier passes disagree on the entry count");
 
     cg_container_header h;
     std::memset(&h, 0, sizeof h);
@@ -477,7 +510,7 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     h.anchor_bits = t->anchor_bits;
     h.n_sink = sinks_in(t, kb, ke);
     h.outlier_ppm = t->outlier_ppm;
-    h.n_outliers = t->outlier_ppm ? sizes[2] : 0;
+    h.n_outliers = t->outlier_ppm ? sizes[1] : 0;
     h.clamped = t->outlier_ppm ? 0 : sizes[1];
     h.payload_words = sizes[0];
     fill_layout(h);
@@ -487,16 +520,11 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     b->magic = 0;
     b->device = t->device;
     b->hdr = h;
-    DevBuf data, scratch;
+    DevBuf data;
     hipError_t e = data.alloc(align256(h.total_bytes));
     if (e != hipSuccess) {
         delete b;
         return hip_fail(e, "hipMalloc container");
-    }
-    e = scratch.alloc(sizes[0] * 2);
-    if (e != hipSuccess) {
-        delete b;
-        return hip_fail(e, "hipMalloc scratch");
     }
     uint8_t *base = data.as<uint8_t>();
 #define CG_HIP_B(call, what)                 \
@@ -508,7 +536,6 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
         }                                    \
     } while (0)
     // zero bytes between sections and after the payload
-    const uint64_t C = t->C;
     const uint64_t ends[][2] = {
         {kHeaderBytes, h.offsets_offset},
         {h.offsets_offset + (n_groups + 1) * 8, h.anchors_offset},
@@ -521,10 +548,9 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     for (const auto &z : ends)
         if (z[1] > z[0]) CG_HIP_B(hipMemsetAsync(base + z[0], 0, z[1] - z[0], st), "clear padding");
     CG_HIP_B(hipMemcpyAsync(base, &h, sizeof h, hipMemcpyHostToDevice, st), "copy header");
-    CG_HIP_B(hipMemcpyAsync(base + h.offsets_offset, group_off.p, (n_groups + 1) * 8,
-                            hipMemcpyDeviceToDevice, st),
+    CG_HIP_B(hipMemcpyAsync(base + h.offsets_offset, goff, (n_groups + 1) * 8, hipMemcpyDeviceToDevice, st),
              "copy offsets");
-    CG_HIP_B(hipMemcpyAsync(base + h.anchors_offset, anc.p, h.anchors_bytes, hipMemcpyDeviceToDevice, st),
+    CG_HIP_B(hipMemcpyAsync(base + h.anchors_offset, anc, h.anchors_bytes, hipMemcpyDeviceToDevice, st),
              "copy anchors");
     if (h.n_sink) {
         // the sink rows of the encoded cache: 2L rows of n_sink tokens from token t_lo
@@ -534,23 +560,18 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
                  "copy sink rows");
     }
     if (t->outlier_ppm) {
-        CG_HIP_B(hipMemcpyAsync(base + h.outliers_offset, ooff.p, (n_groups + 1) * 8,
+        CG_HIP_B(hipMemcpyAsync(base + h.outliers_offset, ooff, (n_groups + 1) * 8,
                                 hipMemcpyDeviceToDevice, st),
                  "copy outlier offsets");
         if (h.n_outliers)
-            CG_HIP_B(launch_outliers(X, g, t->d_bins, t->d_lo, t->d_r, nullptr, ooff.as<uint64_t>(),
+            CG_HIP_B(launch_outliers(X, g, t->d_bins, t->d_lo, t->d_r, nullptr, ooff,
                                      reinterpret_cast<uint32_t *>(base + h.outlier_keys_offset),
                                      reinterpret_cast<uint16_t *>(base + h.outlier_values_offset), st),
                      "k_outliers");
     }
-    CG_HIP_B(launch_k5_encode(sym.as<uint8_t>(), t_lo, T_r, g, t->d_bins, t->d_dtab,
-                              lane_words.as<uint32_t>(), group_off.as<uint64_t>(),
-                              scratch.as<uint16_t>(), st),
-             "k5_encode");
-    CG_HIP_B(launch_k5_interleave(g, lane_words.as<uint32_t>(), group_off.as<uint64_t>(),
-                                  masks.as<uint64_t>(), mstride, scratch.as<uint16_t>(),
-                                  reinterpret_cast<uint16_t *>(base + h.payload_offset), st),
-             "k5_interleave");
+    CG_HIP_B(launch_k5_compact(regions, region_words, gwords, goff, n_groups,
+                               reinterpret_cast<uint16_t *>(base + h.payload_offset), st),
+             "k5_compact");
     CG_HIP_B(hipStreamSynchronize(st), "hipStreamSynchronize");
 #undef CG_HIP_B
     b->d_data = static_cast<uint8_t *>(data.detach());

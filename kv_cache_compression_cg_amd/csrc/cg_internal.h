@@ -89,19 +89,23 @@ hipError_t launch_outliers(const uint16_t *X, const Geom &g, const uint8_t *bins
 // Writes a container's outlier entries into the output (contiguous, or pages of pg).
 hipError_t launch_apply_outliers(const Geom &g, const uint8_t *container, const ContainerView &cv,
                                  uint16_t *out, const Paged &pg, hipStream_t st);
-hipError_t launch_k5_plan(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
-                          const uint8_t *bins, const uint32_t *dtab, uint32_t *lane_words,
-                          uint64_t *group_words, uint64_t *masks, uint32_t mstride,
-                          hipStream_t st);
+// Words of one lane's stream for m symbols: at most 2 state words and floor(0.50036 m)
+// shifted words (each symbol multiplies the state by at most 256 (1 + 2^-8), each word
+// divides it by 2^16, and it starts and ends at or above 2^16).
+__host__ __device__ constexpr uint32_t lane_words_max(uint32_t m) { return (m >> 1) + (m >> 11) + 4; }
+// Words of the scratch region of one group (worst case over the chunks of g).
+uint64_t code_region_words(const Geom &g);
+// The fused encoder: for every group of chunks [g.kb, g.ke), its words placed at the end of
+// its region, its anchors into `anchors` (the container's anchors section layout), its
+// word count and its number of elements off their grid.
+hipError_t launch_k5_code(const uint16_t *X, const Geom &g, const uint8_t *bins,
+                          const uint32_t *dtab, const float *lo, const float *r,
+                          uint16_t *regions, uint8_t *anchors, uint64_t *group_words,
+                          uint64_t *group_off_grid, hipStream_t st);
 hipError_t launch_scan(const uint64_t *in, uint64_t *out, uint64_t n, hipStream_t st);
-hipError_t launch_k5_encode(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
-                            const uint8_t *bins, const uint32_t *dtab,
-                            const uint32_t *lane_words, const uint64_t *group_off,
-                            uint16_t *scratch, hipStream_t st);
-hipError_t launch_k5_interleave(const Geom &g, const uint32_t *lane_words,
-                                const uint64_t *group_off, const uint64_t *masks,
-                                uint32_t mstride, const uint16_t *scratch, uint16_t *payload,
-                                hipStream_t st);
+hipError_t launch_k5_compact(const uint16_t *regions, uint64_t region_words,
+                             const uint64_t *group_words, const uint64_t *group_off,
+                             uint64_t n_groups, uint16_t *payload, hipStream_t st);
 hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, const float *lo,
                      const float *w, const uint8_t *container, const ContainerView &cv,
                      uint16_t *out, uint8_t *sym_out, hipStream_t st);

@@ -5,6 +5,7 @@
 #include "cg_device.h"
 
 namespace cgk {
+constexpr int kNT16 = 2;  // aux bits of a buffer load: non-temporal (single-use stream)
 // Non-temporal (streaming) accesses for the encoder's single-use streams: the KV rows it
 // reads once per pass, the symbols and anchors it writes once.  (On the 70B-shaped cache
 // the encode went from 36.1 to 34.4 ms with them.)
@@ -576,197 +577,227 @@ hipError_t launch_anchor_grid(const uint16_t *X, const Geom &g, float *alo, floa
 }
 
 // ------------------------------------------------------------------------------ K5
-// rANS encoder, three passes over the groups (chunk, row, channel block b); a block
-// holds 4 wavefronts = 4 chunks of one (row, b), sharing that pair's {f | cdf << 24}
-// table plane in LDS, and lane i codes the stream of channel 64b + i.  The coder runs
-// from the chunk's last symbol to its first; symbols are loaded eight steps ahead.
-//   plan        replays the state evolution: counts each lane's words and records, for
-//               every step, the wavefront's ballot of lanes that shift a word out before
-//               coding that step's symbol -- the lanes whose decoders read a word after
-//               decoding it;
-//   encode      codes each lane's stream into a lane-major scratch of exact size, in
-//               decoder read order (state words first, then the shifted-out words from
-//               the first step to the last, i.e. filled from the end);
-//   interleave  moves every word to the position the lockstep decoders read it from,
-//               following the recorded ballots (no second replay of the coder).
-constexpr uint32_t kSymAhead = 8;
+// rANS encoder fused with anchor delta + quantize, one pass over the cache.  Block = 4
+// wavefronts = 4 chunks of one (row, channel block b) sharing the block's coding table in
+// LDS; wavefront = group (chunk, row, b), lane i codes the stream of channel 64b + i.
+//
+// The coder runs from a chunk's last symbol to its first, and the lockstep decoders read
+// the words in the order "state words, then after each symbol the words of the lanes that
+// renormalise, in lane order".  So the words of symbol i are the ones closest to the end
+// of the group's word sequence among those not yet placed: every word is placed at its
+// distance D from the end, D = (words of later symbols) + (words of symbol i) - rank of
+// the lane among the shifting lanes, and the state words last.  The words go to a
+// per-wavefront LDS ring indexed by -D and leave it 256 at a time (one 8-byte store per
+// lane) into a region of the group's worst-case size, counted back from the region's end;
+// a compaction copy then packs the regions into the container's payload.
+//
+// Coding step on symbol s with f = f[s], cdf = cdf[s] (state x in [2^16, 2^32)):
+//   if x >= f * 2^24, the low 16 bits of x leave as a word and x >>= 16 (now x < f * 2^24);
+//   q = floor(x / f); x = q * 256 + (x - q f) + cdf = x + q (256 - f) + cdf.
+// q is taken as trunc(double(x) * rcp) with rcp = (1/f)(1 + 2^-40) rounded to double:
+// the product exceeds x/f by a relative 2^-40 - 4 * 2^-53 > 0, so it is at least q, and by
+// less than x/f * 2^-39 < 1/f (x < 2^39), so it stays below q + 1 - 1/f + 1/f.
+//
+// The chunk's tokens are visited group by group from the last group to the first; in a
+// group the anchor first (it anchors the group's deltas, and goes to the anchors section),
+// then the other tokens from the last to the first.  Loads run kFeedAhead tokens ahead
+// through a buffer resource over the chunk's rows.
 constexpr uint32_t kEncWaves = 4;
+constexpr uint32_t kFeedAhead = 8;
+constexpr uint32_t kWordRing = 512;     // words per wavefront ring (power of two)
+constexpr uint32_t kFlushWords = 256;   // words per flush: 4 per lane
 
-struct GroupCtx {
-    uint32_t k, row, b, lane, c, nl, t0, len, ng, m;
-    bool present;
+typedef uint64_t __attribute__((may_alias)) ring_u64_t;
+
+struct EncEntry {
+    double rcp;        // (1/f)(1 + 2^-40)
+    uint32_t f24;      // f << 24: renormalisation threshold
+    uint32_t pk;       // (256 - f) | cdf << 24
 };
 
-__device__ __forceinline__ GroupCtx group_ctx(const Geom &g, uint64_t gidx, uint32_t lane)
-{
-    GroupCtx x;
-    x.b = (uint32_t)(gidx % g.NB);
-    uint64_t tmp = gidx / g.NB;
-    x.row = (uint32_t)(tmp % (2 * g.L));
-    x.k = g.kb + (uint32_t)(tmp / (2 * g.L));
-    x.lane = lane;
-    x.c = x.b * kLanes + lane;
-    x.nl = min(kLanes, g.C - x.b * kLanes);
-    x.present = x.c < g.C;
-    x.t0 = x.k * g.Tc;
-    x.len = chunk_len(g, x.k);
-    x.ng = (x.len + g.G - 1) / g.G;
-    x.m = x.len - x.ng;
-    return x;
-}
-
-__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t lane)
-{
-    uint32_t x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t y = __shfl_up(x, d, 64);
-        if (lane >= (uint32_t)d) x += y;
-    }
-    return x - v;
-}
-
-
-// Symbol i of a lane's stream sits at token t0 + 1 + i + i / (G - 1): anchors are
-// skipped.  The feed walks i = m - 1 down to 0.  Loads go through a buffer resource over
-// the symbol rows of one (layer, K/V), the lane's channel as vector offset and the token
-// row as scalar offset; reads outside the rows return 0 (the look-ahead past i = 0 reads
-// such rows, and is never used).
-struct SymFeed {
-    __amdgpu_buffer_rsrc_t rs;
-    uint32_t voff, C, G1, rel, pos;
-
-    // m >= 1 and G >= 2
-    __device__ __forceinline__ void init(const uint8_t *rows, uint32_t bytes, uint32_t c,
-                                         uint32_t C_, uint32_t G, uint32_t t_rel, uint32_t m)
+// Token order of a chunk for the encoder (see above): position (group gi, j), j = 0 the
+// anchor, then j = glen - 1 down to 1.  All fields are wave-uniform.
+struct EncWalk {
+    uint32_t gi, j, G, len;
+    __device__ __forceinline__ void init(uint32_t G_, uint32_t len_)
     {
-        rs = make_rsrc(rows, bytes);
-        voff = c;
-        C = C_;
-        G1 = G - 1;
-        pos = (m - 1) % G1;
-        rel = t_rel + 1 + (m - 1) + (m - 1) / G1;
+        G = G_;
+        len = len_;
+        gi = (len + G - 1) / G - 1;
+        j = 0;
     }
-    // issues the load of the next symbol (downwards)
-    __device__ __forceinline__ uint32_t next()
+    __device__ __forceinline__ uint32_t u() const { return gi * G + j; }
+    __device__ __forceinline__ void next()
     {
-        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b8(rs, voff, rel * C, 2 /* nt */);
-        if (pos == 0) {
-            pos = G1 - 1;
-            rel -= 2;
-        } else {
-            --pos;
-            rel -= 1;
+        if (j == 0) {
+            const uint32_t gl = min(G, len - gi * G);
+            if (gl > 1) {
+                j = gl - 1;
+                return;
+            }
+        } else if (j > 1) {
+            --j;
+            return;
         }
-        return v;
+        if (gi > 0) {  // the first group's last element stays put: later loads repeat it
+            --gi;
+            j = 0;
+        }
     }
 };
 
-// One rANS coding step on a table entry {f | cdf << 24}; returns whether the low 16
-// bits of the state were shifted out first (into *word).
-__device__ __forceinline__ bool rans_step(uint32_t &state, uint32_t e, uint32_t &word)
-{
-    const uint32_t f = max(e & 0xFFu, 1u);  // (absent lanes read an unset entry)
-    const bool shift = state >= (f << 24);
-    word = state & 0xFFFFu;
-    if (shift) state >>= 16;
-    const uint32_t q = state / f;
-    state = q * kProbTotal + (state - q * f) + (e >> 24);
-    return shift;
-}
-
-// Block set-up shared by the encoder passes: (row, b, set) from the block index, the
-// P = 2^logp used entries of the table plane staged into LDS.  Returns the chunk of
-// this wavefront.
-__device__ __forceinline__ uint32_t enc_block(const Geom &g, const uint8_t *__restrict__ bins,
-                                              const uint32_t *__restrict__ dtab,
-                                              uint32_t n_sets, uint32_t *tab, uint32_t &row,
-                                              uint32_t &b)
-{
-    // block order as in the decoder: channel block fastest, rotated by the row, so that
-    // the blocks each XCD holds at a time cover all columns of the token rows
-    const uint32_t tmp = blockIdx.x / g.NB;
-    const uint32_t set = tmp % n_sets;
-    row = tmp / n_sets;
-    b = (blockIdx.x % g.NB + row) % g.NB;
-    const uint32_t N = bins[row];
-    uint32_t P = 1;
-    while (P < N) P <<= 1;
-    const uint4 *src = reinterpret_cast<const uint4 *>(dtab + (uint64_t)(row * g.NB + b) * kTabBlock);
-    uint4 *dst = reinterpret_cast<uint4 *>(tab);
-    for (uint32_t j = threadIdx.x; j < P * kLanes / 4; j += blockDim.x) dst[j] = src[j];
-    __syncthreads();
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
-    return g.kb + set * kEncWaves + wave;
-}
-
-__global__ __launch_bounds__(256) void k5_plan(const uint8_t *__restrict__ sym, uint32_t sym_t0,
-                                                uint32_t sym_T, Geom g,
+__global__ __launch_bounds__(256) void k5_code(const uint16_t *__restrict__ X, Geom g,
                                                 const uint8_t *__restrict__ bins,
                                                 const uint32_t *__restrict__ dtab,
-                                                uint32_t n_sets, uint32_t *__restrict__ lane_words,
+                                                const float *__restrict__ lo,
+                                                const float *__restrict__ r, uint32_t n_sets,
+                                                uint64_t region_words,
+                                                uint16_t *__restrict__ regions,
+                                                uint8_t *__restrict__ anchors,
                                                 uint64_t *__restrict__ group_words,
-                                                uint64_t *__restrict__ masks, uint32_t mstride)
+                                                uint64_t *__restrict__ group_off_grid)
 {
-    __shared__ uint32_t tab[kTabPlane];
-    uint32_t row, b;
-    const uint32_t k = enc_block(g, bins, dtab, n_sets, tab, row, b);
+    __shared__ EncEntry tab[kMaxBins * kLanes];
+    __shared__ __attribute__((aligned(16))) uint16_t rings[kEncWaves * kWordRing];
+    // block order as in the decoder: channel block fastest, rotated by the row
+    const uint32_t tmp = blockIdx.x / g.NB;
+    const uint32_t set = tmp % n_sets;
+    const uint32_t row = tmp / n_sets;
+    const uint32_t b = (blockIdx.x % g.NB + row) % g.NB;
+    const uint32_t N = bins[row];
+    {
+        const uint32_t *src = dtab + (uint64_t)(row * g.NB + b) * kTabBlock;
+        for (uint32_t j = threadIdx.x; j < N * kLanes; j += blockDim.x) {
+            const uint32_t e = src[j];
+            const uint32_t f = max(e & 0xFFu, 1u), cdf = e >> 24;  // (absent lanes: f = 1)
+            EncEntry en;
+            en.rcp = (1.0 / (double)f) * (1.0 + 0x1p-40);
+            en.f24 = f << 24;
+            en.pk = (kProbTotal - f) | (cdf << 24);
+            tab[j] = en;
+        }
+    }
+    __syncthreads();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const uint32_t k = g.kb + set * kEncWaves + wave;
     if (k >= g.ke) return;
     const uint32_t lane = threadIdx.x % kLanes;
     const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
-    const GroupCtx x = group_ctx(g, gidx, lane);
-    uint32_t words = 0;
-    if (x.m > 0) {  // uniform
-        SymFeed sf;
-        sf.init(sym + (uint64_t)row * sym_T * g.C, sym_T * g.C, x.present ? x.c : 0, g.C, g.G,
-                x.t0 - sym_t0, x.m);
-        const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab) + lane * 4;
-        uint64_t *mrow = masks + gidx * mstride;
-        uint32_t state = kStateLow, ev = 0, mlo = 0, mhi = 0;
-        // one step: the ballot of step i is kept in lane i % 64 and written when i
-        // reaches a multiple of 64 (steps run downwards)
-        auto step = [&](uint32_t i, uint32_t s) __attribute__((always_inline)) {
-            const uint32_t e = *reinterpret_cast<const uint32_t *>(tb + s * kSymStride);
-            uint32_t word;
-            const bool need = rans_step(state, e, word) && x.present;
-            const uint64_t mask = __builtin_amdgcn_ballot_w64(need);
-            ev += need ? 1u : 0u;
-            const uint32_t j = i % kLanes;
-            if (lane == j) {
-                mlo = (uint32_t)mask;
-                mhi = (uint32_t)(mask >> 32);
-            }
-            if (j == 0) {
-                if (lane <= min(kLanes - 1, x.m - 1 - i)) {
-                    uint2 v;
-                    v.x = mlo;
-                    v.y = mhi;
-                    *reinterpret_cast<uint2 *>(mrow + i + lane) = v;
-                }
-            }
-        };
-        uint32_t sr[kSymAhead];
+    const uint32_t c = b * kLanes + lane;
+    const uint32_t nl = min(kLanes, g.C - b * kLanes);
+    const bool present = lane < nl;
+    const uint32_t t0 = k * g.Tc, len = chunk_len(g, k);
+    const uint32_t ng = (len + g.G - 1) / g.G, m = len - ng;
+    const uint64_t ri = (uint64_t)row * g.C + (present ? c : 0u);
+    const float lo1 = lo[ri], r1 = r[ri];
+    const bool a8 = g.alo != nullptr;
+    float alo = 0.0f, aw = 0.0f, ar = 0.0f;
+    if (a8) {
+        alo = g.alo[ri];
+        aw = g.aw[ri];
+        ar = g.ar[ri];
+    }
+    // the chunk's rows of this (layer, K/V): token u at byte u * 2C, channel at 2c
+    const __amdgpu_buffer_rsrc_t xs = make_rsrc(X + ((uint64_t)row * g.S + t0) * g.C,
+                                                (uint32_t)((uint64_t)len * g.C * 2));
+    const uint32_t voff = 2 * (present ? c : 0u);
+    const uint32_t rstride = 2 * g.C;
+    uint16_t *ring = rings + wave * kWordRing;
+    uint16_t *rend = regions + (gidx + 1) * region_words;   // the region's end
+    const uint64_t arow0 = anchor_row(g, k, row, 0);         // anchor rows gi: arow0 + gi
+
+    EncWalk lw, cw;  // load walker (kFeedAhead ahead) and consume walker
+    lw.init(g.G, len);
+    cw.init(g.G, len);
+    uint32_t sv[kFeedAhead];
 #pragma unroll
-        for (uint32_t r = 0; r < kSymAhead; ++r) sr[r] = sf.next();
-        uint32_t done = 0;
-        for (; done + kSymAhead <= x.m; done += kSymAhead) {
-#pragma unroll
-            for (uint32_t r = 0; r < kSymAhead; ++r) {
-                const uint32_t s_ = sr[r];
-                sr[r] = sf.next();
-                step(x.m - 1 - (done + r), s_);
+    for (uint32_t i = 0; i < kFeedAhead; ++i) {
+        sv[i] = __builtin_amdgcn_raw_buffer_load_b16(xs, voff, lw.u() * rstride, kNT16);
+        lw.next();
+    }
+    uint32_t x = kStateLow;
+    uint32_t E = 0, flushed = 0;   // words placed / words written out (wave-uniform)
+    uint32_t n_off = 0;            // elements off their grid (wave-uniform)
+    float af = 0.0f;
+
+    auto element = [&](uint32_t v) __attribute__((always_inline)) {
+        const uint32_t u = cw.u();
+        const bool coded_tok = t0 + u >= g.n_sink;
+        if (cw.j == 0) {
+            // an anchor: its decoded value anchors the group; fp16 bits or its grid code
+            // go to the anchors section
+            const float xa = h2f(v);
+            const uint64_t ai = (arow0 + cw.gi) * g.C + c;
+            if (a8) {
+                const uint32_t code = quantize1(xa, alo, ar, 256u);
+                const bool off = present && coded_tok && off_grid(xa, alo, ar, 256u);
+                n_off += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(off));
+                af = h2f(f2h_fma((float)code, aw, alo));
+                if (present) anchors[ai] = (uint8_t)code;
+            } else {
+                af = xa;
+                if (present) reinterpret_cast<uint16_t *>(anchors)[ai] = (uint16_t)v;
+            }
+        } else {
+            const float dl = h2f(v) - af;
+            const uint32_t q = quantize1(dl, lo1, r1, N);
+            const bool off = present && coded_tok && off_grid(dl, lo1, r1, N);
+            n_off += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(off));
+            const EncEntry en = tab[q * kLanes + lane];
+            const bool shift = present && x >= en.f24;
+            const uint64_t mask = __builtin_amdgcn_ballot_w64(shift);
+            const uint32_t cnt = (uint32_t)__builtin_popcountll(mask);
+            if (shift) {
+                const uint32_t D = E + cnt - mbcnt64(mask);
+                ring[(0u - D) & (kWordRing - 1)] = (uint16_t)x;
+                x >>= 16;
+            }
+            E += cnt;
+            const uint32_t qq = (uint32_t)((double)x * en.rcp);
+            x = __umul24(qq, en.pk & 0xFFFFFFu) + x + (en.pk >> 24);
+            if (E - flushed >= kFlushWords) {
+                // distances flushed + 1 .. flushed + 256: region words [end - flushed - 256,
+                // end - flushed), 4 per lane
+                const uint32_t s0 = (0u - (flushed + kFlushWords) + 4 * lane) & (kWordRing - 1);
+                const uint64_t w4 = *reinterpret_cast<const ring_u64_t *>(ring + s0);
+                *reinterpret_cast<uint64_t *>(rend - flushed - kFlushWords + 4 * lane) = w4;
+                flushed += kFlushWords;
             }
         }
+        cw.next();
+    };
+
+    uint32_t done = 0;
+    for (; done + kFeedAhead <= len; done += kFeedAhead) {
 #pragma unroll
-        for (uint32_t r = 0; r < kSymAhead; ++r)
-            if (done + r < x.m) step(x.m - 1 - (done + r), sr[r]);
-        if (x.present) words = 2 + ev;
+        for (uint32_t i = 0; i < kFeedAhead; ++i) {
+            const uint32_t v = sv[i];
+            sv[i] = __builtin_amdgcn_raw_buffer_load_b16(xs, voff, lw.u() * rstride, kNT16);
+            lw.next();
+            element(v);
+        }
     }
-    lane_words[gidx * kLanes + lane] = words;
-    uint32_t tot = words;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) tot += __shfl_xor(tot, d, 64);
-    if (lane == 0) group_words[gidx] = tot;
+    for (uint32_t i = 0; i < kFeedAhead; ++i)
+        if (done + i < len) element(sv[i]);
+
+    // the state words come first in read order: lane i's two words at positions 2i, 2i+1
+    uint32_t total = 0;
+    if (m > 0) {
+        total = E + 2 * nl;
+        if (present) {
+            ring[(0u - (total - 2 * lane)) & (kWordRing - 1)] = (uint16_t)(x >> 16);
+            ring[(0u - (total - 2 * lane - 1)) & (kWordRing - 1)] = (uint16_t)x;
+        }
+    }
+    for (uint32_t i = lane; i < total - flushed; i += kLanes) {
+        const uint32_t D = flushed + 1 + i;
+        *(rend - D) = ring[(0u - D) & (kWordRing - 1)];
+    }
+    if (lane == 0) {
+        group_words[gidx] = total;
+        group_off_grid[gidx] = n_off;
+    }
 }
 
 // Exclusive prefix sum of n values in one block; out[n] = total.
@@ -795,107 +826,23 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *__restrict__ in,
     if (tid == 1023) out[n] = part[1023];
 }
 
-__global__ __launch_bounds__(256) void k5_encode(const uint8_t *__restrict__ sym, uint32_t sym_t0,
-                                                  uint32_t sym_T, Geom g,
-                                                  const uint8_t *__restrict__ bins,
-                                                  const uint32_t *__restrict__ dtab,
-                                                  uint32_t n_sets,
-                                                  const uint32_t *__restrict__ lane_words,
-                                                  const uint64_t *__restrict__ group_off,
-                                                  uint16_t *__restrict__ scratch)
+// Packs the groups' words from the ends of their regions into the payload; wavefront =
+// group.
+__global__ __launch_bounds__(256) void k5_compact(const uint16_t *__restrict__ regions,
+                                                   uint64_t region_words,
+                                                   const uint64_t *__restrict__ group_words,
+                                                   const uint64_t *__restrict__ group_off,
+                                                   uint64_t n_groups,
+                                                   uint16_t *__restrict__ payload)
 {
-    __shared__ uint32_t tab[kTabPlane];
-    uint32_t row, b;
-    const uint32_t k = enc_block(g, bins, dtab, n_sets, tab, row, b);
-    if (k >= g.ke) return;
-    const uint32_t lane = threadIdx.x % kLanes;
-    const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
-    const GroupCtx x = group_ctx(g, gidx, lane);
-    const uint32_t nwords = lane_words[gidx * kLanes + lane];
-    const uint32_t lane_off = wave_excl_scan(nwords, lane);
-    if (x.m == 0) return;  // uniform
-    uint16_t *out = scratch + group_off[gidx] + lane_off;
-    if (!x.present) return;
-    SymFeed sf;
-    sf.init(sym + (uint64_t)row * sym_T * g.C, sym_T * g.C, x.c, g.C, g.G, x.t0 - sym_t0, x.m);
-    const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab) + lane * 4;
-    // words shifted out at steps m-1, m-2, ... fill the scratch from its end
-    uint32_t state = kStateLow, pos = nwords - 1;
-    auto step = [&](uint32_t s) __attribute__((always_inline)) {
-        const uint32_t e = *reinterpret_cast<const uint32_t *>(tb + s * kSymStride);
-        uint32_t word;
-        if (rans_step(state, e, word)) out[pos--] = (uint16_t)word;
-    };
-    uint32_t sr[kSymAhead];
-#pragma unroll
-    for (uint32_t r = 0; r < kSymAhead; ++r) sr[r] = sf.next();
-    uint32_t done = 0;
-    for (; done + kSymAhead <= x.m; done += kSymAhead) {
-#pragma unroll
-        for (uint32_t r = 0; r < kSymAhead; ++r) {
-            const uint32_t s_ = sr[r];
-            sr[r] = sf.next();
-            step(s_);
-        }
-    }
-#pragma unroll
-    for (uint32_t r = 0; r < kSymAhead; ++r)
-        if (done + r < x.m) step(sr[r]);
-    out[0] = (uint16_t)(state >> 16);
-    out[1] = (uint16_t)(state & 0xFFFFu);
-}
-
-__global__ __launch_bounds__(256) void k5_interleave(Geom g, uint32_t n_sets,
-                                                      const uint32_t *__restrict__ lane_words,
-                                                      const uint64_t *__restrict__ group_off,
-                                                      const uint64_t *__restrict__ masks,
-                                                      uint32_t mstride,
-                                                      const uint16_t *__restrict__ scratch,
-                                                      uint16_t *__restrict__ payload)
-{
-    const uint32_t tmp = blockIdx.x / g.NB;
-    const uint32_t set = tmp % n_sets;
-    const uint32_t row = tmp / n_sets;
-    const uint32_t b = (blockIdx.x % g.NB + row) % g.NB;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
-    const uint32_t k = g.kb + set * kEncWaves + wave;
-    if (k >= g.ke) return;
+    const uint64_t gidx = (uint64_t)blockIdx.x * (blockDim.x / kLanes) + wave;
+    if (gidx >= n_groups) return;
     const uint32_t lane = threadIdx.x % kLanes;
-    const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
-    const GroupCtx x = group_ctx(g, gidx, lane);
-    const uint32_t nwords = lane_words[gidx * kLanes + lane];
-    const uint32_t lane_off = wave_excl_scan(nwords, lane);
-    if (x.m == 0) return;  // uniform
-    const uint16_t *src = scratch + group_off[gidx] + lane_off;
+    const uint64_t n = group_words[gidx];
+    const uint16_t *src = regions + (gidx + 1) * region_words - n;
     uint16_t *dst = payload + group_off[gidx];
-    uint32_t e = 2, w_next = 0;
-    if (x.present) {
-        dst[2 * lane] = src[0];
-        dst[2 * lane + 1] = src[1];
-        if (nwords > 2) w_next = src[2];
-    }
-    const uint64_t *mrow = masks + gidx * mstride;
-    uint32_t cursor = 2 * x.nl;
-    for (uint32_t base = 0; base < x.m; base += kLanes) {
-        // the ballots of steps base .. base + 63, one per lane
-        uint2 mm = make_uint2(0, 0);
-        if (base + lane < x.m) mm = *reinterpret_cast<const uint2 *>(mrow + base + lane);
-        const uint32_t n = min(kLanes, x.m - base);
-        for (uint32_t j = 0; j < n; ++j) {
-            // (readlane returns a signed int: go through uint32_t, no sign extension)
-            const uint32_t mlo = (uint32_t)__builtin_amdgcn_readlane(mm.x, j);
-            const uint32_t mhi = (uint32_t)__builtin_amdgcn_readlane(mm.y, j);
-            const uint64_t mask = ((uint64_t)mhi << 32) | mlo;
-            if (mask) {
-                if ((mask >> lane) & 1u) {
-                    dst[cursor + mbcnt64(mask)] = (uint16_t)w_next;
-                    ++e;
-                    if (e < nwords) w_next = src[e];
-                }
-                cursor += (uint32_t)__builtin_popcountll(mask);
-            }
-        }
-    }
+    for (uint64_t i = lane; i < n; i += kLanes) dst[i] = src[i];
 }
 
 
@@ -1016,15 +963,22 @@ hipError_t launch_outliers(const uint16_t *X, const Geom &g, const uint8_t *bins
 
 static uint32_t enc_sets(const Geom &g) { return (g.ke - g.kb + kEncWaves - 1) / kEncWaves; }
 
-hipError_t launch_k5_plan(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
-                          const uint8_t *bins, const uint32_t *dtab, uint32_t *lane_words,
-                          uint64_t *group_words, uint64_t *masks, uint32_t mstride,
-                          hipStream_t st)
+uint64_t code_region_words(const Geom &g)
+{
+    const uint32_t full = g.Tc < g.S ? g.Tc : g.S;
+    const uint32_t m = full - (full + g.G - 1) / g.G;
+    return ((uint64_t)kLanes * lane_words_max(m) + 3) & ~uint64_t(3);
+}
+
+hipError_t launch_k5_code(const uint16_t *X, const Geom &g, const uint8_t *bins,
+                          const uint32_t *dtab, const float *lo, const float *r,
+                          uint16_t *regions, uint8_t *anchors, uint64_t *group_words,
+                          uint64_t *group_off_grid, hipStream_t st)
 {
     const uint32_t n_sets = enc_sets(g);
     const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
-    hipLaunchKernelGGL(k5_plan, dim3((uint32_t)blocks), dim3(256), 0, st, sym, sym_t0, sym_T, g,
-                       bins, dtab, n_sets, lane_words, group_words, masks, mstride);
+    hipLaunchKernelGGL(k5_code, dim3((uint32_t)blocks), dim3(256), 0, st, X, g, bins, dtab, lo, r,
+                       n_sets, code_region_words(g), regions, anchors, group_words, group_off_grid);
     return hipGetLastError();
 }
 
@@ -1034,27 +988,13 @@ hipError_t launch_scan(const uint64_t *in, uint64_t *out, uint64_t n, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_k5_encode(const uint8_t *sym, uint32_t sym_t0, uint32_t sym_T, const Geom &g,
-                            const uint8_t *bins, const uint32_t *dtab,
-                            const uint32_t *lane_words, const uint64_t *group_off,
-                            uint16_t *scratch, hipStream_t st)
+hipError_t launch_k5_compact(const uint16_t *regions, uint64_t region_words,
+                             const uint64_t *group_words, const uint64_t *group_off,
+                             uint64_t n_groups, uint16_t *payload, hipStream_t st)
 {
-    const uint32_t n_sets = enc_sets(g);
-    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
-    hipLaunchKernelGGL(k5_encode, dim3((uint32_t)blocks), dim3(256), 0, st, sym, sym_t0, sym_T, g,
-                       bins, dtab, n_sets, lane_words, group_off, scratch);
-    return hipGetLastError();
-}
-
-hipError_t launch_k5_interleave(const Geom &g, const uint32_t *lane_words,
-                                const uint64_t *group_off, const uint64_t *masks,
-                                uint32_t mstride, const uint16_t *scratch, uint16_t *payload,
-                                hipStream_t st)
-{
-    const uint32_t n_sets = enc_sets(g);
-    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
-    hipLaunchKernelGGL(k5_interleave, dim3((uint32_t)blocks), dim3(256), 0, st, g, n_sets,
-                       lane_words, group_off, masks, mstride, scratch, payload);
+    if (!n_groups) return hipSuccess;
+    hipLaunchKernelGGL(k5_compact, dim3((uint32_t)((n_groups + 3) / 4)), dim3(256), 0, st, regions,
+                       region_words, group_words, group_off, n_groups, payload);
     return hipGetLastError();
 }
 
