@@ -116,19 +116,27 @@ struct Arena {
     int device;
     void *p;
     uint64_t bytes;
+    uint64_t *host;   // 256 pinned host bytes: values a call reads back, a header it writes
 };
 std::mutex g_arena_mu;
 std::vector<Arena> g_arenas;
 
-// Scratch of at least `bytes` on `device` (the caller holds g_arena_mu).
-hipError_t arena_get(int device, uint64_t bytes, uint8_t **out)
+// Scratch of at least `bytes` on `device`, and the device's pinned read-back words (the
+// caller holds g_arena_mu).
+hipError_t arena_get(int device, uint64_t bytes, uint8_t **out, uint64_t **host = nullptr)
 {
     Arena *a = nullptr;
     for (Arena &x : g_arenas)
         if (x.device == device) a = &x;
     if (!a) {
-        g_arenas.push_back(Arena{device, nullptr, 0});
+        g_arenas.push_back(Arena{device, nullptr, 0, nullptr});
         a = &g_arenas.back();
+    }
+    if (!a->host) {
+        void *h = nullptr;
+        hipError_t e = hipHostMalloc(&h, 256, hipHostMallocDefault);
+        if (e != hipSuccess) return e;
+        a->host = static_cast<uint64_t *>(h);
     }
     if (a->bytes < bytes) {
         if (a->p) {
@@ -146,6 +154,7 @@ hipError_t arena_get(int device, uint64_t bytes, uint8_t **out)
         a->bytes = want;
     }
     *out = static_cast<uint8_t *>(a->p);
+    if (host) *host = a->host;
     return hipSuccess;
 }
 
@@ -419,7 +428,8 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     const uint64_t o_fine = t->outlier_ppm ? cv.take(rows * kFineBins * 4) : 0;
     std::lock_guard<std::mutex> lock(g_arena_mu);
     uint8_t *sc = nullptr;
-    CG_HIP(arena_get(t->device, cv.used, &sc), "scratch");
+    uint64_t *hw = nullptr;
+    CG_HIP(arena_get(t->device, cv.used, &sc, &hw), "scratch");
     uint32_t *ordlo = reinterpret_cast<uint32_t *>(sc + o_lo), *ordhi = reinterpret_cast<uint32_t *>(sc + o_hi);
     float *hi = reinterpret_cast<float *>(sc + o_h);
     uint32_t *counts = reinterpret_cast<uint32_t *>(sc + o_cnt), *flag = reinterpret_cast<uint32_t *>(sc + o_flag);
@@ -444,10 +454,9 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     CG_HIP(launch_k1(X, g, t->d_bins, t->max_bins, t->d_lo, t->d_r, counts, st), "k1_hist");
     CG_HIP(launch_k1_freqs(g, t->d_bins, counts, t->d_freqs, st), "k1_freqs");
     CG_HIP(launch_dtab(g, t->d_bins, t->d_freqs, t->d_lo, t->d_w, t->d_dtab, st), "k_dtab");
-    uint32_t h_flag = 0;
-    CG_HIP(hipMemcpyAsync(&h_flag, flag, 4, hipMemcpyDeviceToHost, st), "copy flag");
+    CG_HIP(hipMemcpyAsync(hw, flag, 4, hipMemcpyDeviceToHost, st), "copy flag");
     CG_HIP(hipStreamSynchronize(st), "hipStreamSynchronize");
-    if (h_flag) return fail(CG_E_NONFINITE, "KV input holds Inf or NaN");
+    if (*reinterpret_cast<volatile uint32_t *>(hw)) return fail(CG_E_NONFINITE, "KV input holds Inf or NaN");
     owner.t = nullptr;
     *out = t;
     return CG_OK;
@@ -480,7 +489,8 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     const uint64_t o_ow = cv.take(n_groups * 8), o_oo = cv.take((n_groups + 1) * 8);
     std::lock_guard<std::mutex> lock(g_arena_mu);
     uint8_t *sc = nullptr;
-    CG_HIP(arena_get(t->device, cv.used, &sc), "scratch");
+    uint64_t *hw = nullptr;
+    CG_HIP(arena_get(t->device, cv.used, &sc, &hw), "scratch");
     uint16_t *regions = reinterpret_cast<uint16_t *>(sc + o_reg);
     uint8_t *anc = sc + o_anc;
     uint64_t *gwords = reinterpret_cast<uint64_t *>(sc + o_gw), *goff = reinterpret_cast<uint64_t *>(sc + o_go);
@@ -490,10 +500,10 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
            "k5_code");
     CG_HIP(launch_scan(gwords, goff, n_groups, st), "scan");
     CG_HIP(launch_scan(gout, ooff, n_groups, st), "scan");
-    uint64_t sizes[2] = {0, 0};  // payload words, elements off their grid
-    CG_HIP(hipMemcpyAsync(&sizes[0], goff + n_groups, 8, hipMemcpyDeviceToHost, st), "copy size");
-    CG_HIP(hipMemcpyAsync(&sizes[1], ooff + n_groups, 8, hipMemcpyDeviceToHost, st), "copy count");
+    CG_HIP(hipMemcpyAsync(hw, goff + n_groups, 8, hipMemcpyDeviceToHost, st), "copy size");
+    CG_HIP(hipMemcpyAsync(hw + 1, ooff + n_groups, 8, hipMemcpyDeviceToHost, st), "copy count");
     CG_HIP(hipStreamSynchronize(st), "hipStreamSynchronize");
+    const uint64_t sizes[2] = {hw[0], hw[1]};  // payload words, elements off their grid
 
     cg_container_header h;
     std::memset(&h, 0, sizeof h);
@@ -545,9 +555,17 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
         {h.outlier_keys_offset + h.n_outliers * 4, h.outlier_values_offset},
         {h.outlier_values_offset + (h.outlier_ppm ? h.n_outliers * 2 : 0), h.payload_offset},
         {h.payload_offset + sizes[0] * 2, h.total_bytes}};
+    ZeroRanges zr;
+    zr.n = 0;
     for (const auto &z : ends)
-        if (z[1] > z[0]) CG_HIP_B(hipMemsetAsync(base + z[0], 0, z[1] - z[0], st), "clear padding");
-    CG_HIP_B(hipMemcpyAsync(base, &h, sizeof h, hipMemcpyHostToDevice, st), "copy header");
+        if (z[1] > z[0]) {
+            zr.r[zr.n][0] = z[0];
+            zr.r[zr.n][1] = z[1];
+            ++zr.n;
+        }
+    CG_HIP_B(launch_zero_ranges(base, zr, st), "clear padding");
+    std::memcpy(hw + 8, &h, sizeof h);  // staged in pinned memory (waited for below)
+    CG_HIP_B(hipMemcpyAsync(base, hw + 8, sizeof h, hipMemcpyHostToDevice, st), "copy header");
     CG_HIP_B(hipMemcpyAsync(base + h.offsets_offset, goff, (n_groups + 1) * 8, hipMemcpyDeviceToDevice, st),
              "copy offsets");
     CG_HIP_B(hipMemcpyAsync(base + h.anchors_offset, anc, h.anchors_bytes, hipMemcpyDeviceToDevice, st),

@@ -74,6 +74,14 @@ __device__ __forceinline__ uint32_t quantize1(float delta, float lo, float r, ui
     return (uint32_t)v;
 }
 
+// quantize1 without branches, for finite delta, lo and r: the clamp to [0, N - 1] as the
+// median of (v, 0, N - 1) gives the same integer (v <= 0, -0 included, -> 0;
+// v > N - 1 -> N - 1).  nm1 = (float)(N - 1).
+__device__ __forceinline__ uint32_t quantize_bf(float delta, float lo, float r, float nm1)
+{
+    return (uint32_t)__builtin_amdgcn_fmed3f(floorf(fmaf(delta - lo, r, 0.5f)), 0.0f, nm1);
+}
+
 // Whether quantize1 had to clamp: the nearest grid point is more than half a step away
 // (floor(fma(delta - lo, r, 0.5)) outside [0, N - 1]), or the grid has zero width (r = 0,
 // the single point lo) and delta is not on it.

@@ -103,6 +103,12 @@ hipError_t launch_k5_code(const uint16_t *X, const Geom &g, const uint8_t *bins,
                           uint16_t *regions, uint8_t *anchors, uint64_t *group_words,
                           uint64_t *group_off_grid, hipStream_t st);
 hipError_t launch_scan(const uint64_t *in, uint64_t *out, uint64_t n, hipStream_t st);
+// Byte ranges to clear, [r[i][0], r[i][1]) for i < n (each range small: one block).
+struct ZeroRanges {
+    uint64_t r[8][2];
+    uint32_t n;
+};
+hipError_t launch_zero_ranges(uint8_t *base, const ZeroRanges &zr, hipStream_t st);
 hipError_t launch_k5_compact(const uint16_t *regions, uint64_t region_words,
                              const uint64_t *group_words, const uint64_t *group_off,
                              uint64_t n_groups, uint16_t *payload, hipStream_t st);

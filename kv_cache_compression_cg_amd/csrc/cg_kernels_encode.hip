@@ -265,6 +265,7 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
     uint32_t ct = tmp % ntiles;
     uint32_t row = tmp / ntiles;
     uint32_t N = bins[row];
+    const float nm1 = (float)(N - 1u);
     uint32_t nh = N * 8 * OCT;
     for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) hist[j] = 0;
     __syncthreads();
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
             } else if (w.t >= g.n_sink) {  // and out of the histograms
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    uint32_t q = quantize1(xf[j] - af[j], lo8[j], r8[j], N);
+                    const uint32_t q = quantize_bf(xf[j] - af[j], lo8[j], r8[j], nm1);
                     atomicAdd(&hist[(q * 8 + j) * OCT + ol], 1u);
                 }
             }
@@ -589,7 +590,8 @@ hipError_t launch_anchor_grid(const uint16_t *X, const Geom &g, float *alo, floa
 // the lane among the shifting lanes, and the state words last.  The words go to a
 // per-wavefront LDS ring indexed by -D and leave it 256 at a time (one 8-byte store per
 // lane) into a region of the group's worst-case size, counted back from the region's end;
-// a compaction copy then packs the regions into the container's payload.
+// a compaction copy then packs the regions into the container's payload.  Lanes that do
+// not shift write a parking slot of their own, so the step has no branch.
 //
 // Coding step on symbol s with f = f[s], cdf = cdf[s] (state x in [2^16, 2^32)):
 //   if x >= f * 2^24, the low 16 bits of x leave as a word and x >>= 16 (now x < f * 2^24);
@@ -600,12 +602,15 @@ hipError_t launch_anchor_grid(const uint16_t *X, const Geom &g, float *alo, floa
 //
 // The chunk's tokens are visited group by group from the last group to the first; in a
 // group the anchor first (it anchors the group's deltas, and goes to the anchors section),
-// then the other tokens from the last to the first.  Loads run kFeedAhead tokens ahead
-// through a buffer resource over the chunk's rows.
-constexpr uint32_t kEncWaves = 4;
-constexpr uint32_t kFeedAhead = 8;
-constexpr uint32_t kWordRing = 512;     // words per wavefront ring (power of two)
+// then the other tokens from the last to the first.  Groups of 10 tokens (the usual
+// anchor interval) are unrolled: their 9 symbols and table reads are independent of the
+// state and come first, the state chain follows, and the next group's rows are loaded
+// meanwhile; other lengths go one token at a time.
+constexpr uint32_t kEncWaves = 8;
+constexpr uint32_t kWordRing = 1024;    // words per wavefront ring (power of two)
+constexpr uint32_t kRingAlloc = kWordRing + kLanes;  // + one parking slot per lane
 constexpr uint32_t kFlushWords = 256;   // words per flush: 4 per lane
+constexpr uint32_t kUG = 10;            // group length of the unrolled path
 
 typedef uint64_t __attribute__((may_alias)) ring_u64_t;
 
@@ -615,50 +620,76 @@ struct EncEntry {
     uint32_t pk;       // (256 - f) | cdf << 24
 };
 
-// Token order of a chunk for the encoder (see above): position (group gi, j), j = 0 the
-// anchor, then j = glen - 1 down to 1.  All fields are wave-uniform.
-struct EncWalk {
-    uint32_t gi, j, G, len;
-    __device__ __forceinline__ void init(uint32_t G_, uint32_t len_)
+// State of one wavefront's coder: the lane's channel parameters, the rANS state, and the
+// placement of words (all counts wave-uniform).
+struct Coder {
+    const EncEntry *tab;
+    uint16_t *ring;
+    uint16_t *rend;         // end of the group's region
+    float lo, r, nm1, af;   // grid, N - 1 as a float, the current anchor value
+    bool zero_w;            // the grid is the single point lo
+    bool present;           // this lane has a channel
+    uint64_t pmask;         // lanes with a channel
+    uint32_t lane, x, E, flushed, n_off;
+
+    // q = clamp(floor(fma(delta - lo, r, 0.5)), 0, N - 1) without branches (v is finite,
+    // so the median of (v, 0, N - 1) gives quantize1's result); off: the clamp changed v,
+    // or a zero-width grid misses delta.  `coded`: the token is from n_sink on.
+    __device__ __forceinline__ uint32_t symbol(float dl, bool coded)
     {
-        G = G_;
-        len = len_;
-        gi = (len + G - 1) / G - 1;
-        j = 0;
+        const float v = floorf(fmaf(dl - lo, r, 0.5f));
+        const float vc = __builtin_amdgcn_fmed3f(v, 0.0f, nm1);
+        const bool off = (v != vc) | (zero_w & (dl != lo));
+        const uint64_t om = __builtin_amdgcn_ballot_w64(off) & pmask;
+        n_off += coded ? (uint32_t)__builtin_popcountll(om) : 0u;
+        return (uint32_t)vc;
     }
-    __device__ __forceinline__ uint32_t u() const { return gi * G + j; }
-    __device__ __forceinline__ void next()
+
+    __device__ __forceinline__ EncEntry entry(uint32_t q) const { return tab[q * kLanes + lane]; }
+
+    // One coding step with the table entry of the symbol; the shifted-out word (if any)
+    // goes to the ring at its distance from the end, other lanes write their parking slot.
+    __device__ __forceinline__ void step(const EncEntry &en)
     {
-        if (j == 0) {
-            const uint32_t gl = min(G, len - gi * G);
-            if (gl > 1) {
-                j = gl - 1;
-                return;
-            }
-        } else if (j > 1) {
-            --j;
-            return;
-        }
-        if (gi > 0) {  // the first group's last element stays put: later loads repeat it
-            --gi;
-            j = 0;
+        const bool mine = (x >= en.f24) & present;
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(mine);
+        const uint32_t cnt = (uint32_t)__builtin_popcountll(mask);
+        const uint32_t D = E + cnt - mbcnt64(mask);
+        const uint32_t slot = mine ? ((0u - D) & (kWordRing - 1)) : kWordRing + lane;
+        ring[slot] = (uint16_t)x;
+        x = mine ? x >> 16 : x;
+        E += cnt;
+        const uint32_t qq = (uint32_t)((double)x * en.rcp);
+        x = __umul24(qq, en.pk) + x + (en.pk >> 24);
+    }
+
+    // writes out whole 256-word blocks of placed words (distances flushed + 1 ..): region
+    // words [end - flushed - 256, end - flushed), 4 per lane
+    __device__ __forceinline__ void flush()
+    {
+        while (E - flushed >= kFlushWords) {
+            const uint32_t s0 = (0u - (flushed + kFlushWords) + 4 * lane) & (kWordRing - 1);
+            const uint64_t w4 = *reinterpret_cast<const ring_u64_t *>(ring + s0);
+            *reinterpret_cast<uint64_t *>(rend - flushed - kFlushWords + 4 * lane) = w4;
+            flushed += kFlushWords;
         }
     }
 };
 
-__global__ __launch_bounds__(256) void k5_code(const uint16_t *__restrict__ X, Geom g,
-                                                const uint8_t *__restrict__ bins,
-                                                const uint32_t *__restrict__ dtab,
-                                                const float *__restrict__ lo,
-                                                const float *__restrict__ r, uint32_t n_sets,
-                                                uint64_t region_words,
-                                                uint16_t *__restrict__ regions,
-                                                uint8_t *__restrict__ anchors,
-                                                uint64_t *__restrict__ group_words,
-                                                uint64_t *__restrict__ group_off_grid)
+template <uint32_t GU>
+__global__ __launch_bounds__(kEncWaves * 64) void k5_code(const uint16_t *__restrict__ X, Geom g,
+                                                         const uint8_t *__restrict__ bins,
+                                                         const uint32_t *__restrict__ dtab,
+                                                         const float *__restrict__ lo,
+                                                         const float *__restrict__ r,
+                                                         uint32_t n_sets, uint64_t region_words,
+                                                         uint16_t *__restrict__ regions,
+                                                         uint8_t *__restrict__ anchors,
+                                                         uint64_t *__restrict__ group_words,
+                                                         uint64_t *__restrict__ group_off_grid)
 {
     __shared__ EncEntry tab[kMaxBins * kLanes];
-    __shared__ __attribute__((aligned(16))) uint16_t rings[kEncWaves * kWordRing];
+    __shared__ __attribute__((aligned(16))) uint16_t rings[kEncWaves * kRingAlloc];
     // block order as in the decoder: channel block fastest, rotated by the row
     const uint32_t tmp = blockIdx.x / g.NB;
     const uint32_t set = tmp % n_sets;
@@ -687,9 +718,9 @@ __global__ __launch_bounds__(256) void k5_code(const uint16_t *__restrict__ X, G
     const uint32_t nl = min(kLanes, g.C - b * kLanes);
     const bool present = lane < nl;
     const uint32_t t0 = k * g.Tc, len = chunk_len(g, k);
-    const uint32_t ng = (len + g.G - 1) / g.G, m = len - ng;
+    const uint32_t G = GU ? GU : g.G;
+    const uint32_t ng = (len + G - 1) / G, m = len - ng;
     const uint64_t ri = (uint64_t)row * g.C + (present ? c : 0u);
-    const float lo1 = lo[ri], r1 = r[ri];
     const bool a8 = g.alo != nullptr;
     float alo = 0.0f, aw = 0.0f, ar = 0.0f;
     if (a8) {
@@ -697,137 +728,186 @@ __global__ __launch_bounds__(256) void k5_code(const uint16_t *__restrict__ X, G
         aw = g.aw[ri];
         ar = g.ar[ri];
     }
+    Coder cd;
+    cd.tab = tab;
+    cd.ring = rings + wave * kRingAlloc;
+    cd.rend = regions + (gidx + 1) * region_words;
+    cd.lo = lo[ri];
+    cd.r = r[ri];
+    cd.nm1 = (float)(N - 1u);
+    cd.zero_w = cd.r == 0.0f;
+    cd.af = 0.0f;
+    cd.present = present;
+    cd.pmask = __builtin_amdgcn_ballot_w64(present);
+    cd.lane = lane;
+    cd.x = kStateLow;
+    cd.E = cd.flushed = cd.n_off = 0;
+
     // the chunk's rows of this (layer, K/V): token u at byte u * 2C, channel at 2c
     const __amdgpu_buffer_rsrc_t xs = make_rsrc(X + ((uint64_t)row * g.S + t0) * g.C,
                                                 (uint32_t)((uint64_t)len * g.C * 2));
     const uint32_t voff = 2 * (present ? c : 0u);
     const uint32_t rstride = 2 * g.C;
-    uint16_t *ring = rings + wave * kWordRing;
-    uint16_t *rend = regions + (gidx + 1) * region_words;   // the region's end
-    const uint64_t arow0 = anchor_row(g, k, row, 0);         // anchor rows gi: arow0 + gi
-
-    EncWalk lw, cw;  // load walker (kFeedAhead ahead) and consume walker
-    lw.init(g.G, len);
-    cw.init(g.G, len);
-    uint32_t sv[kFeedAhead];
-#pragma unroll
-    for (uint32_t i = 0; i < kFeedAhead; ++i) {
-        sv[i] = __builtin_amdgcn_raw_buffer_load_b16(xs, voff, lw.u() * rstride, kNT16);
-        lw.next();
-    }
-    uint32_t x = kStateLow;
-    uint32_t E = 0, flushed = 0;   // words placed / words written out (wave-uniform)
-    uint32_t n_off = 0;            // elements off their grid (wave-uniform)
-    float af = 0.0f;
-
-    auto element = [&](uint32_t v) __attribute__((always_inline)) {
-        const uint32_t u = cw.u();
-        const bool coded_tok = t0 + u >= g.n_sink;
-        if (cw.j == 0) {
-            // an anchor: its decoded value anchors the group; fp16 bits or its grid code
-            // go to the anchors section
-            const float xa = h2f(v);
-            const uint64_t ai = (arow0 + cw.gi) * g.C + c;
-            if (a8) {
-                const uint32_t code = quantize1(xa, alo, ar, 256u);
-                const bool off = present && coded_tok && off_grid(xa, alo, ar, 256u);
-                n_off += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(off));
-                af = h2f(f2h_fma((float)code, aw, alo));
-                if (present) anchors[ai] = (uint8_t)code;
-            } else {
-                af = xa;
-                if (present) reinterpret_cast<uint16_t *>(anchors)[ai] = (uint16_t)v;
-            }
+    const uint64_t arow0 = anchor_row(g, k, row, 0);   // anchor row of group gi: arow0 + gi
+    auto load = [&](uint32_t u) __attribute__((always_inline)) {
+        return __builtin_amdgcn_raw_buffer_load_b16(xs, voff, u * rstride, kNT16);
+    };
+    // an anchor: its decoded value anchors the group; its fp16 bits or grid code go to
+    // the anchors section
+    auto anchor = [&](uint32_t v, uint32_t gi) __attribute__((always_inline)) {
+        const float xa = h2f(v);
+        const uint64_t ai = (arow0 + gi) * g.C + c;
+        if (a8) {
+            const uint32_t code = quantize1(xa, alo, ar, 256u);
+            const bool off = off_grid(xa, alo, ar, 256u);
+            const uint64_t om = __builtin_amdgcn_ballot_w64(off) & cd.pmask;
+            cd.n_off += (t0 + gi * G >= g.n_sink) ? (uint32_t)__builtin_popcountll(om) : 0u;
+            cd.af = h2f(f2h_fma((float)code, aw, alo));
+            if (present) anchors[ai] = (uint8_t)code;
         } else {
-            const float dl = h2f(v) - af;
-            const uint32_t q = quantize1(dl, lo1, r1, N);
-            const bool off = present && coded_tok && off_grid(dl, lo1, r1, N);
-            n_off += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(off));
-            const EncEntry en = tab[q * kLanes + lane];
-            const bool shift = present && x >= en.f24;
-            const uint64_t mask = __builtin_amdgcn_ballot_w64(shift);
-            const uint32_t cnt = (uint32_t)__builtin_popcountll(mask);
-            if (shift) {
-                const uint32_t D = E + cnt - mbcnt64(mask);
-                ring[(0u - D) & (kWordRing - 1)] = (uint16_t)x;
-                x >>= 16;
-            }
-            E += cnt;
-            const uint32_t qq = (uint32_t)((double)x * en.rcp);
-            x = __umul24(qq, en.pk & 0xFFFFFFu) + x + (en.pk >> 24);
-            if (E - flushed >= kFlushWords) {
-                // distances flushed + 1 .. flushed + 256: region words [end - flushed - 256,
-                // end - flushed), 4 per lane
-                const uint32_t s0 = (0u - (flushed + kFlushWords) + 4 * lane) & (kWordRing - 1);
-                const uint64_t w4 = *reinterpret_cast<const ring_u64_t *>(ring + s0);
-                *reinterpret_cast<uint64_t *>(rend - flushed - kFlushWords + 4 * lane) = w4;
-                flushed += kFlushWords;
-            }
+            cd.af = xa;
+            if (present) reinterpret_cast<uint16_t *>(anchors)[ai] = (uint16_t)v;
         }
-        cw.next();
+    };
+    // any group, one token at a time (its last token first)
+    auto group_generic = [&](uint32_t gi) __attribute__((always_inline)) {
+        const uint32_t u0 = gi * G, gl = min(G, len - u0);
+        anchor(load(u0), gi);
+        for (uint32_t j = gl - 1; j >= 1; --j) {
+            const uint32_t q = cd.symbol(h2f(load(u0 + j)) - cd.af, t0 + u0 + j >= g.n_sink);
+            cd.step(cd.entry(q));
+            cd.flush();
+        }
     };
 
-    uint32_t done = 0;
-    for (; done + kFeedAhead <= len; done += kFeedAhead) {
+    uint32_t gi = ng;  // groups left, processed from the last to the first
+    if constexpr (GU > 0) {
+        // the chunk's last group may be short: one token at a time; then full groups,
+        // unrolled, the next group's rows loaded while this one is coded
+        const uint32_t last = len - (ng - 1) * G;
+        if (last != G) group_generic(--gi);
+        if (gi > 0) {
+            uint32_t cur[GU], nxt[GU];
+            --gi;
 #pragma unroll
-        for (uint32_t i = 0; i < kFeedAhead; ++i) {
-            const uint32_t v = sv[i];
-            sv[i] = __builtin_amdgcn_raw_buffer_load_b16(xs, voff, lw.u() * rstride, kNT16);
-            lw.next();
-            element(v);
+            for (uint32_t j = 0; j < GU; ++j) cur[j] = load(gi * G + j);
+            while (true) {
+                const uint32_t ugi = gi;
+                const bool more = ugi > 0;
+                const uint32_t nb = more ? (ugi - 1) * G : ugi * G;  // in bounds either way
+#pragma unroll
+                for (uint32_t j = 0; j < GU; ++j) nxt[j] = load(nb + j);
+                anchor(cur[0], ugi);
+                const bool coded = t0 + ugi * G + 1 >= g.n_sink;
+                uint32_t q[GU];
+#pragma unroll
+                for (uint32_t j = GU - 1; j >= 1; --j)
+                    q[j] = cd.symbol(h2f(cur[j]) - cd.af, coded || t0 + ugi * G + j >= g.n_sink);
+                EncEntry en[GU];
+#pragma unroll
+                for (uint32_t j = GU - 1; j >= 1; --j) en[j] = cd.entry(q[j]);
+#pragma unroll
+                for (uint32_t j = GU - 1; j >= 1; --j) cd.step(en[j]);
+                cd.flush();
+                if (!more) break;
+                --gi;
+#pragma unroll
+                for (uint32_t j = 0; j < GU; ++j) cur[j] = nxt[j];
+            }
         }
+    } else {
+        while (gi > 0) group_generic(--gi);
     }
-#pragma unroll
-    for (uint32_t i = 0; i < kFeedAhead; ++i)
-        if (done + i < len) element(sv[i]);
 
     // the state words come first in read order: lane i's two words at positions 2i, 2i+1
     uint32_t total = 0;
     if (m > 0) {
-        total = E + 2 * nl;
+        total = cd.E + 2 * nl;
         if (present) {
-            ring[(0u - (total - 2 * lane)) & (kWordRing - 1)] = (uint16_t)(x >> 16);
-            ring[(0u - (total - 2 * lane - 1)) & (kWordRing - 1)] = (uint16_t)x;
+            cd.ring[(0u - (total - 2 * lane)) & (kWordRing - 1)] = (uint16_t)(cd.x >> 16);
+            cd.ring[(0u - (total - 2 * lane - 1)) & (kWordRing - 1)] = (uint16_t)cd.x;
         }
     }
-    for (uint32_t i = lane; i < total - flushed; i += kLanes) {
-        const uint32_t D = flushed + 1 + i;
-        *(rend - D) = ring[(0u - D) & (kWordRing - 1)];
+    for (uint32_t i = lane; i < total - cd.flushed; i += kLanes) {
+        const uint32_t D = cd.flushed + 1 + i;
+        *(cd.rend - D) = cd.ring[(0u - D) & (kWordRing - 1)];
     }
     if (lane == 0) {
         group_words[gidx] = total;
-        group_off_grid[gidx] = n_off;
+        group_off_grid[gidx] = cd.n_off;
     }
 }
 
-// Exclusive prefix sum of n values in one block; out[n] = total.
+// Exclusive prefix sum of n values in one block of 1024 threads; out[n] = total.  Tiles
+// of 4096 values: each thread loads 4 consecutive ones, the 1024 sums are scanned in the
+// wavefronts (shuffles) and across them (LDS), and a carry runs over the tiles.
 __global__ __launch_bounds__(1024) void k_scan(const uint64_t *__restrict__ in,
                                                 uint64_t *__restrict__ out, uint64_t n)
 {
-    __shared__ uint64_t part[1024];
-    uint32_t tid = threadIdx.x;
-    uint64_t per = (n + 1023) / 1024;
-    uint64_t beg = min(n, (uint64_t)tid * per), end = min(n, beg + per);
-    uint64_t s = 0;
-    for (uint64_t j = beg; j < end; ++j) s += in[j];
-    part[tid] = s;
-    __syncthreads();
-    for (uint32_t d = 1; d < 1024; d <<= 1) {
-        uint64_t y = (tid >= d) ? part[tid - d] : 0;
+    __shared__ uint64_t wsum[16];
+    const uint32_t tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    uint64_t carry = 0;
+    for (uint64_t base = 0; base < n; base += 4096) {
+        const uint64_t i0 = base + 4 * (uint64_t)tid;
+        uint64_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = (i0 + k < n) ? in[i0 + k] : 0;
+        const uint64_t tsum = v[0] + v[1] + v[2] + v[3];
+        uint64_t incl = tsum;  // inclusive scan of the thread sums in the wavefront
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint64_t y = __shfl_up(incl, d, 64);
+            if (lane >= (uint32_t)d) incl += y;
+        }
+        if (lane == 63) wsum[wave] = incl;
         __syncthreads();
-        part[tid] += y;
+        uint64_t before = carry;
+        for (uint32_t w = 0; w < wave; ++w) before += wsum[w];
+        uint64_t tile = 0;
+        for (uint32_t w = 0; w < 16; ++w) tile += wsum[w];
+        uint64_t run = before + incl - tsum;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (i0 + k < n) out[i0 + k] = run;
+            run += v[k];
+        }
+        carry += tile;
         __syncthreads();
     }
-    uint64_t run = part[tid] - s;
-    for (uint64_t j = beg; j < end; ++j) {
-        out[j] = run;
-        run += in[j];
-    }
-    if (tid == 1023) out[n] = part[1023];
+    if (tid == 0) out[n] = carry;
 }
 
 // Packs the groups' words from the ends of their regions into the payload; wavefront =
-// group.
+// group.  The payload side is written in 16-byte pieces: the words before the first
+// 16-byte boundary and after the last one go one per lane, the rest 8 per lane, each
+// piece cut out of the two aligned 16-byte source pieces it straddles (the source is off
+// by the same number of words m for the whole group).
+__device__ __forceinline__ uint4 words_at(uint4 A, uint4 B, uint32_t m)
+{
+    const uint32_t w[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
+    const uint32_t sh = (m & 1u) * 16u;
+    uint32_t o[4];
+    switch (m >> 1) {  // wave-uniform
+    case 0:
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], sh);
+        break;
+    case 1:
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_alignbit(w[i + 2], w[i + 1], sh);
+        break;
+    case 2:
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_alignbit(w[i + 3], w[i + 2], sh);
+        break;
+    default:
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_alignbit(i + 4 < 8 ? w[i + 4] : 0u, w[i + 3], sh);
+        break;
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __global__ __launch_bounds__(256) void k5_compact(const uint16_t *__restrict__ regions,
                                                    uint64_t region_words,
                                                    const uint64_t *__restrict__ group_words,
@@ -840,9 +920,21 @@ __global__ __launch_bounds__(256) void k5_compact(const uint16_t *__restrict__ r
     if (gidx >= n_groups) return;
     const uint32_t lane = threadIdx.x % kLanes;
     const uint64_t n = group_words[gidx];
-    const uint16_t *src = regions + (gidx + 1) * region_words - n;
-    uint16_t *dst = payload + group_off[gidx];
-    for (uint64_t i = lane; i < n; i += kLanes) dst[i] = src[i];
+    const uint64_t s0 = (gidx + 1) * region_words - n;   // first source word
+    const uint64_t d0 = group_off[gidx];                  // first payload word
+    const uint64_t head = min(n, (8 - (d0 & 7)) & 7);
+    for (uint64_t i = lane; i < head; i += kLanes) payload[d0 + i] = regions[s0 + i];
+    const uint64_t body = (n - head) & ~uint64_t(7);
+    const uint64_t sa = s0 + head, da = d0 + head;       // da is a multiple of 8
+    const uint32_t m = (uint32_t)(sa & 7);
+    const uint4 *src = reinterpret_cast<const uint4 *>(regions + (sa - m));
+    uint4 *dst = reinterpret_cast<uint4 *>(payload + da);
+    for (uint64_t p = lane; p < body / 8; p += kLanes) {
+        const uint4 A = src[p];
+        const uint4 B = m ? src[p + 1] : A;
+        dst[p] = m ? words_at(A, B, m) : A;
+    }
+    for (uint64_t i = head + body + lane; i < n; i += kLanes) payload[d0 + i] = regions[s0 + i];
 }
 
 
@@ -977,8 +1069,28 @@ hipError_t launch_k5_code(const uint16_t *X, const Geom &g, const uint8_t *bins,
 {
     const uint32_t n_sets = enc_sets(g);
     const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
-    hipLaunchKernelGGL(k5_code, dim3((uint32_t)blocks), dim3(256), 0, st, X, g, bins, dtab, lo, r,
-                       n_sets, code_region_words(g), regions, anchors, group_words, group_off_grid);
+    if (g.G == kUG)
+        hipLaunchKernelGGL(k5_code<kUG>, dim3((uint32_t)blocks), dim3(kEncWaves * 64), 0, st, X, g,
+                           bins, dtab, lo, r, n_sets, code_region_words(g), regions, anchors,
+                           group_words, group_off_grid);
+    else
+        hipLaunchKernelGGL(k5_code<0>, dim3((uint32_t)blocks), dim3(kEncWaves * 64), 0, st, X, g,
+                           bins, dtab, lo, r, n_sets, code_region_words(g), regions, anchors,
+                           group_words, group_off_grid);
+    return hipGetLastError();
+}
+
+// Clears the byte ranges [r[i][0], r[i][1]) of a buffer (the padding between container
+// sections): one launch instead of a fill per range.
+__global__ __launch_bounds__(256) void k_zero_ranges(uint8_t *__restrict__ base, ZeroRanges zr)
+{
+    for (uint32_t i = 0; i < zr.n; ++i)
+        for (uint64_t a = zr.r[i][0] + threadIdx.x; a < zr.r[i][1]; a += blockDim.x) base[a] = 0;
+}
+
+hipError_t launch_zero_ranges(uint8_t *base, const ZeroRanges &zr, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_zero_ranges, dim3(1), dim3(256), 0, st, base, zr);
     return hipGetLastError();
 }
 
