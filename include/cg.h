@@ -238,6 +238,26 @@ int cg_decode_paged(const cg_tables *tables, const cg_blob *blob, const void *co
  * no-op; any other pointer must be a live handle of this library. */
 void cg_free(void *handle);
 
+/*
+ * cg_encode for callers that cannot allocate memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same kernels and the same container
+ * bytes, written into a caller-owned buffer, with the scratch taken from a fixed 64 MiB
+ * array in the library's device memory (one per device, held until the process ends).
+ * No hipMalloc, hipFree or other allocating call is made.
+ *   container_dev: device buffer of `capacity` bytes, 256-byte aligned.
+ *   header_out:    receives the container's header (host), also when the capacity is too
+ *                  small (then its total_bytes is the size needed and nothing is written).
+ * Encodes whose scratch (about (2 + m / 2 + m / 2048 + 2) * 128 bytes per 64-channel
+ * group of a chunk with m coded tokens, plus the anchors section) exceeds 64 MiB are
+ * refused with CG_E_INVAL before any device work.  All calls on one device share the
+ * array: the library serialises them (a call holds it from its first launch to its last
+ * wait); the array keeps the last call's contents and needs no clearing.  Synchronises
+ * hip_stream twice.  Errors: CG_E_INVAL, CG_E_HIP.
+ */
+int cg_encode_noalloc(const cg_tables *tables, const void *kv_dev, uint32_t chunk_begin,
+                      uint32_t chunk_end, void *container_dev, uint64_t capacity,
+                      void *hip_stream, cg_container_header *header_out);
+
 /* ----------------------------------------------------------------------------------
  * Stored form.  Tables and containers are written to host memory, kept or sent
  * elsewhere, and imported by a receiver that decodes them ("Guide to CacheGen", Problem:

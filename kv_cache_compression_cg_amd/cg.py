@@ -76,7 +76,7 @@ EXPORTED = ["cg_build_cdf", "cg_encode", "cg_decode", "cg_free", "cg_last_error"
             "cg_tables_export", "cg_tables_get_info", "cg_blob_get_info", "cg_blob_read",
             "cg_quantize", "cg_decode_symbols", "cg_dequantize", "cg_stream_decode",
             "cg_decode_paged", "cg_tables_serialize", "cg_tables_check", "cg_tables_import",
-            "cg_container_check", "cg_blob_import"]
+            "cg_container_check", "cg_blob_import", "cg_encode_noalloc"]
 
 _lib = None
 
@@ -111,6 +111,7 @@ def load() -> ctypes.CDLL:
         "cg_tables_import": [vp, u64, pp],
         "cg_container_check": [vp, u64, ctypes.POINTER(ContainerHeader)],
         "cg_blob_import": [vp, vp, u64, vp, pp],
+        "cg_encode_noalloc": [vp, vp, u32, u32, vp, u64, vp, ctypes.POINTER(ContainerHeader)],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -494,3 +495,19 @@ def blob_import(tables: Tables, data) -> Blob:
         _check(load().cg_blob_import(tables.handle, ptr, buf.size, _stream(tables.device),
                                      ctypes.byref(h)))
     return Blob(h, tables)
+
+
+def encode_noalloc(tables: Tables, kv: torch.Tensor, container: torch.Tensor,
+                   chunk_begin: int = 0, chunk_end: Optional[int] = None) -> dict:
+    """cg_encode_noalloc: the container of chunks [chunk_begin, chunk_end) written into
+    `container` (a CUDA uint8 tensor, 256-byte aligned); returns the header fields."""
+    _kv_check(kv, tables.shape)
+    chunk_end = tables.n_chunks if chunk_end is None else chunk_end
+    if not container.is_cuda or container.dtype != torch.uint8 or not container.is_contiguous():
+        raise ValueError("container must be a contiguous uint8 CUDA tensor")
+    h = ContainerHeader()
+    with torch.cuda.device(kv.device):
+        _check(load().cg_encode_noalloc(tables.handle, kv.data_ptr(), chunk_begin, chunk_end,
+                                        container.data_ptr(), container.numel(),
+                                        _stream(kv.device), ctypes.byref(h)))
+    return {f: getattr(h, f) for f, _ in ContainerHeader._fields_}

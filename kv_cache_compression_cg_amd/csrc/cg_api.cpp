@@ -462,49 +462,59 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     return CG_OK;
 }
 
-int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, void *hip_stream,
-              cg_blob **out)
+}  // extern "C"
+
+namespace {
+
+// Scratch of an encode of chunks [kb, ke): the groups' word regions, the anchors section,
+// per-group word and off-grid counts and their scans.
+struct EncPlan {
+    uint64_t n_groups, region_words, anchor_bytes;
+    uint64_t o_reg, o_anc, o_gw, o_go, o_ow, o_oo, bytes;
+};
+
+EncPlan enc_plan(const cg_tables *t, uint32_t kb, uint32_t ke)
 {
-    g_error.clear();
-    if (int rc = check_tables(t)) return rc;
-    if (!kv_dev || !out) return fail(CG_E_INVAL, "null argument");
-    const uint32_t nchunks = ceil_div(t->S, t->Tc);
-    if (kb >= ke || ke > nchunks) return fail(CG_E_INVAL, "chunk range out of bounds");
-    DeviceScope ds;
-    CG_HIP(ds.enter(t->device), "hipSetDevice");
-    hipStream_t st = (hipStream_t)hip_stream;
-    const uint16_t *X = static_cast<const uint16_t *>(kv_dev);
-    Geom g = make_geom(t, kb, ke);
-    const uint32_t t_lo = kb * t->Tc;
-    const uint64_t n_groups = (uint64_t)(ke - kb) * t->L * 2 * t->NB;
-    const uint64_t C = t->C;
-    const uint64_t anchor_bytes = anchor_rows(t->L, t->S, t->G, t->Tc, kb, ke) * C *
-                                  (t->anchor_bits == 8 ? 1u : 2u);
-    const uint64_t region_words = code_region_words(g);
-
-    // scratch: the groups' word regions, the anchors section, per-group counts and offsets
+    EncPlan p;
+    const Geom g = make_geom(t, kb, ke);
+    p.n_groups = (uint64_t)(ke - kb) * t->L * 2 * t->NB;
+    p.region_words = code_region_words(g);
+    p.anchor_bytes = anchor_rows(t->L, t->S, t->G, t->Tc, kb, ke) * t->C * (t->anchor_bits == 8 ? 1u : 2u);
     Carve cv;
-    const uint64_t o_reg = cv.take(n_groups * region_words * 2), o_anc = cv.take(anchor_bytes);
-    const uint64_t o_gw = cv.take(n_groups * 8), o_go = cv.take((n_groups + 1) * 8);
-    const uint64_t o_ow = cv.take(n_groups * 8), o_oo = cv.take((n_groups + 1) * 8);
-    std::lock_guard<std::mutex> lock(g_arena_mu);
-    uint8_t *sc = nullptr;
-    uint64_t *hw = nullptr;
-    CG_HIP(arena_get(t->device, cv.used, &sc, &hw), "scratch");
-    uint16_t *regions = reinterpret_cast<uint16_t *>(sc + o_reg);
-    uint8_t *anc = sc + o_anc;
-    uint64_t *gwords = reinterpret_cast<uint64_t *>(sc + o_gw), *goff = reinterpret_cast<uint64_t *>(sc + o_go);
-    uint64_t *gout = reinterpret_cast<uint64_t *>(sc + o_ow), *ooff = reinterpret_cast<uint64_t *>(sc + o_oo);
+    p.o_reg = cv.take(p.n_groups * p.region_words * 2);
+    p.o_anc = cv.take(p.anchor_bytes);
+    p.o_gw = cv.take(p.n_groups * 8);
+    p.o_go = cv.take((p.n_groups + 1) * 8);
+    p.o_ow = cv.take(p.n_groups * 8);
+    p.o_oo = cv.take((p.n_groups + 1) * 8);
+    p.bytes = cv.used;
+    return p;
+}
 
-    CG_HIP(launch_k5_code(X, g, t->d_bins, t->d_dtab, t->d_lo, t->d_r, regions, anc, gwords, gout, st),
-           "k5_code");
-    CG_HIP(launch_scan(gwords, goff, n_groups, st), "scan");
-    CG_HIP(launch_scan(gout, ooff, n_groups, st), "scan");
-    CG_HIP(hipMemcpyAsync(hw, goff + n_groups, 8, hipMemcpyDeviceToHost, st), "copy size");
-    CG_HIP(hipMemcpyAsync(hw + 1, ooff + n_groups, 8, hipMemcpyDeviceToHost, st), "copy count");
-    CG_HIP(hipStreamSynchronize(st), "hipStreamSynchronize");
-    const uint64_t sizes[2] = {hw[0], hw[1]};  // payload words, elements off their grid
+// The coding pass and the scans; back on the host (after a wait): the payload words and
+// the elements off their grid.  `rb` receives them (pinned memory, or a host variable).
+hipError_t enc_code(const cg_tables *t, const uint16_t *X, uint32_t kb, uint32_t ke, uint8_t *sc,
+                    const EncPlan &p, hipStream_t st, uint64_t *rb, const char **what)
+{
+    const Geom g = make_geom(t, kb, ke);
+    uint64_t *gw = reinterpret_cast<uint64_t *>(sc + p.o_gw), *go = reinterpret_cast<uint64_t *>(sc + p.o_go);
+    uint64_t *ow = reinterpret_cast<uint64_t *>(sc + p.o_ow), *oo = reinterpret_cast<uint64_t *>(sc + p.o_oo);
+    hipError_t e;
+    *what = "k5_code";
+    if ((e = launch_k5_code(X, g, t->d_bins, t->d_dtab, t->d_lo, t->d_r,
+                            reinterpret_cast<uint16_t *>(sc + p.o_reg), sc + p.o_anc, gw, ow, st)) != hipSuccess)
+        return e;
+    *what = "scan";
+    if ((e = launch_scan(gw, go, p.n_groups, st)) != hipSuccess) return e;
+    if ((e = launch_scan(ow, oo, p.n_groups, st)) != hipSuccess) return e;
+    *what = "read back sizes";
+    if ((e = hipMemcpyAsync(rb, go + p.n_groups, 8, hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
+    if ((e = hipMemcpyAsync(rb + 1, oo + p.n_groups, 8, hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
+    return hipStreamSynchronize(st);
+}
 
+cg_container_header enc_header(const cg_tables *t, uint32_t kb, uint32_t ke, uint64_t words, uint64_t n_off)
+{
     cg_container_header h;
     std::memset(&h, 0, sizeof h);
     h.magic = CG_CONTAINER_MAGIC;
@@ -520,41 +530,34 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
     h.anchor_bits = t->anchor_bits;
     h.n_sink = sinks_in(t, kb, ke);
     h.outlier_ppm = t->outlier_ppm;
-    h.n_outliers = t->outlier_ppm ? sizes[1] : 0;
-    h.clamped = t->outlier_ppm ? 0 : sizes[1];
-    h.payload_words = sizes[0];
+    h.n_outliers = t->outlier_ppm ? n_off : 0;
+    h.clamped = t->outlier_ppm ? 0 : n_off;
+    h.payload_words = words;
     fill_layout(h);
+    return h;
+}
 
-    cg_blob *b = new (std::nothrow) cg_blob();
-    if (!b) return fail(CG_E_NOMEM, "host allocation");
-    b->magic = 0;
-    b->device = t->device;
-    b->hdr = h;
-    DevBuf data;
-    hipError_t e = data.alloc(align256(h.total_bytes));
-    if (e != hipSuccess) {
-        delete b;
-        return hip_fail(e, "hipMalloc container");
-    }
-    uint8_t *base = data.as<uint8_t>();
-#define CG_HIP_B(call, what)                 \
-    do {                                     \
-        hipError_t e2_ = (call);             \
-        if (e2_ != hipSuccess) {             \
-            delete b;                        \
-            return hip_fail(e2_, what);      \
-        }                                    \
-    } while (0)
+// Writes the container described by h at `base` (device, h.total_bytes): padding, the
+// header (copied from `hsrc`, which must stay valid until the stream has run), offsets,
+// anchors, sink rows, outlier sections and the packed payload.  Asynchronous.
+hipError_t enc_write(const cg_tables *t, const uint16_t *X, uint32_t kb, uint32_t ke, uint8_t *sc,
+                     const EncPlan &p, const cg_container_header &h, const void *hsrc, uint8_t *base,
+                     hipStream_t st, const char **what)
+{
+    const Geom g = make_geom(t, kb, ke);
+    const uint64_t C = t->C, ng = p.n_groups;
+    uint64_t *gw = reinterpret_cast<uint64_t *>(sc + p.o_gw), *go = reinterpret_cast<uint64_t *>(sc + p.o_go);
+    uint64_t *oo = reinterpret_cast<uint64_t *>(sc + p.o_oo);
     // zero bytes between sections and after the payload
     const uint64_t ends[][2] = {
         {kHeaderBytes, h.offsets_offset},
-        {h.offsets_offset + (n_groups + 1) * 8, h.anchors_offset},
+        {h.offsets_offset + (ng + 1) * 8, h.anchors_offset},
         {h.anchors_offset + h.anchors_bytes, h.sinks_offset},
         {h.sinks_offset + (uint64_t)2 * t->L * h.n_sink * C * 2, h.outliers_offset},
-        {h.outlier_ppm ? h.outliers_offset + (n_groups + 1) * 8 : h.outliers_offset, h.outlier_keys_offset},
+        {h.outlier_ppm ? h.outliers_offset + (ng + 1) * 8 : h.outliers_offset, h.outlier_keys_offset},
         {h.outlier_keys_offset + h.n_outliers * 4, h.outlier_values_offset},
         {h.outlier_values_offset + (h.outlier_ppm ? h.n_outliers * 2 : 0), h.payload_offset},
-        {h.payload_offset + sizes[0] * 2, h.total_bytes}};
+        {h.payload_offset + h.payload_words * 2, h.total_bytes}};
     ZeroRanges zr;
     zr.n = 0;
     for (const auto &z : ends)
@@ -563,38 +566,158 @@ int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, 
             zr.r[zr.n][1] = z[1];
             ++zr.n;
         }
-    CG_HIP_B(launch_zero_ranges(base, zr, st), "clear padding");
-    std::memcpy(hw + 8, &h, sizeof h);  // staged in pinned memory (waited for below)
-    CG_HIP_B(hipMemcpyAsync(base, hw + 8, sizeof h, hipMemcpyHostToDevice, st), "copy header");
-    CG_HIP_B(hipMemcpyAsync(base + h.offsets_offset, goff, (n_groups + 1) * 8, hipMemcpyDeviceToDevice, st),
-             "copy offsets");
-    CG_HIP_B(hipMemcpyAsync(base + h.anchors_offset, anc, h.anchors_bytes, hipMemcpyDeviceToDevice, st),
-             "copy anchors");
+    hipError_t e;
+    *what = "clear padding";
+    if ((e = launch_zero_ranges(base, zr, st)) != hipSuccess) return e;
+    *what = "copy header";
+    if ((e = hipMemcpyAsync(base, hsrc, sizeof h, hipMemcpyHostToDevice, st)) != hipSuccess) return e;
+    *what = "copy offsets";
+    if ((e = hipMemcpyAsync(base + h.offsets_offset, go, (ng + 1) * 8, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+        return e;
+    *what = "copy anchors";
+    if ((e = hipMemcpyAsync(base + h.anchors_offset, sc + p.o_anc, h.anchors_bytes, hipMemcpyDeviceToDevice,
+                            st)) != hipSuccess)
+        return e;
     if (h.n_sink) {
-        // the sink rows of the encoded cache: 2L rows of n_sink tokens from token t_lo
+        // the sink rows of the encoded cache: 2L rows of n_sink tokens from the first token
         const uint64_t w = (uint64_t)h.n_sink * C * 2;
-        CG_HIP_B(hipMemcpy2DAsync(base + h.sinks_offset, w, X + (uint64_t)t_lo * C,
-                                  (uint64_t)t->S * C * 2, w, 2 * t->L, hipMemcpyDeviceToDevice, st),
-                 "copy sink rows");
+        *what = "copy sink rows";
+        if ((e = hipMemcpy2DAsync(base + h.sinks_offset, w, X + (uint64_t)kb * t->Tc * C,
+                                  (uint64_t)t->S * C * 2, w, 2 * t->L, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+            return e;
     }
     if (t->outlier_ppm) {
-        CG_HIP_B(hipMemcpyAsync(base + h.outliers_offset, ooff, (n_groups + 1) * 8,
-                                hipMemcpyDeviceToDevice, st),
-                 "copy outlier offsets");
-        if (h.n_outliers)
-            CG_HIP_B(launch_outliers(X, g, t->d_bins, t->d_lo, t->d_r, nullptr, ooff,
-                                     reinterpret_cast<uint32_t *>(base + h.outlier_keys_offset),
-                                     reinterpret_cast<uint16_t *>(base + h.outlier_values_offset), st),
-                     "k_outliers");
+        *what = "copy outlier offsets";
+        if ((e = hipMemcpyAsync(base + h.outliers_offset, oo, (ng + 1) * 8, hipMemcpyDeviceToDevice, st)) !=
+            hipSuccess)
+            return e;
+        *what = "k_outliers";
+        if (h.n_outliers &&
+            (e = launch_outliers(X, g, t->d_bins, t->d_lo, t->d_r, nullptr, oo,
+                                 reinterpret_cast<uint32_t *>(base + h.outlier_keys_offset),
+                                 reinterpret_cast<uint16_t *>(base + h.outlier_values_offset), st)) != hipSuccess)
+            return e;
     }
-    CG_HIP_B(launch_k5_compact(regions, region_words, gwords, goff, n_groups,
-                               reinterpret_cast<uint16_t *>(base + h.payload_offset), st),
-             "k5_compact");
-    CG_HIP_B(hipStreamSynchronize(st), "hipStreamSynchronize");
-#undef CG_HIP_B
+    *what = "k5_compact";
+    return launch_k5_compact(reinterpret_cast<const uint16_t *>(sc + p.o_reg), p.region_words, gw, go, ng,
+                             reinterpret_cast<uint16_t *>(base + h.payload_offset), st);
+}
+
+// Scratch for cg_encode_noalloc: a fixed array in each device's memory, its address
+// looked up once per device.  Calls hold g_static_mu from the first launch to the last
+// wait, so calls do not overlap on it.
+constexpr uint64_t kStaticScratch = 64ull << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+uint8_t *g_static_ptr[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratch];
+
+namespace {
+hipError_t static_scratch(int device, uint8_t **out)
+{
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    if (!g_static_ptr[device]) {
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_static_ptr[device] = static_cast<uint8_t *>(p);
+    }
+    *out = g_static_ptr[device];
+    return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+int cg_encode(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke, void *hip_stream,
+              cg_blob **out)
+{
+    g_error.clear();
+    if (int rc = check_tables(t)) return rc;
+    if (!kv_dev || !out) return fail(CG_E_INVAL, "null argument");
+    const uint32_t nchunks = ceil_div(t->S, t->Tc);
+    if (kb >= ke || ke > nchunks) return fail(CG_E_INVAL, "chunk range out of bounds");
+    DeviceScope ds;
+    CG_HIP(ds.enter(t->device), "hipSetDevice");
+    hipStream_t st = (hipStream_t)hip_stream;
+    const uint16_t *X = static_cast<const uint16_t *>(kv_dev);
+    const EncPlan p = enc_plan(t, kb, ke);
+    std::lock_guard<std::mutex> lock(g_arena_mu);
+    uint8_t *sc = nullptr;
+    uint64_t *hw = nullptr;
+    CG_HIP(arena_get(t->device, p.bytes, &sc, &hw), "scratch");
+    const char *what = "";
+    hipError_t e = enc_code(t, X, kb, ke, sc, p, st, hw, &what);
+    if (e != hipSuccess) return hip_fail(e, what);
+    const cg_container_header h = enc_header(t, kb, ke, hw[0], hw[1]);
+
+    cg_blob *b = new (std::nothrow) cg_blob();
+    if (!b) return fail(CG_E_NOMEM, "host allocation");
+    b->magic = 0;
+    b->device = t->device;
+    b->hdr = h;
+    DevBuf data;
+    e = data.alloc(align256(h.total_bytes));
+    if (e != hipSuccess) {
+        delete b;
+        return hip_fail(e, "hipMalloc container");
+    }
+    std::memcpy(hw + 8, &h, sizeof h);  // staged in pinned memory (waited for below)
+    e = enc_write(t, X, kb, ke, sc, p, h, hw + 8, data.as<uint8_t>(), st, &what);
+    if (e == hipSuccess) {
+        what = "hipStreamSynchronize";
+        e = hipStreamSynchronize(st);
+    }
+    if (e != hipSuccess) {
+        delete b;
+        return hip_fail(e, what);
+    }
     b->d_data = static_cast<uint8_t *>(data.detach());
     b->magic = kBlobMagic;
     *out = b;
+    return CG_OK;
+}
+
+int cg_encode_noalloc(const cg_tables *t, const void *kv_dev, uint32_t kb, uint32_t ke,
+                      void *container_dev, uint64_t capacity, void *hip_stream,
+                      cg_container_header *header_out)
+{
+    g_error.clear();
+    if (int rc = check_tables(t)) return rc;
+    if (!kv_dev || !container_dev || !header_out) return fail(CG_E_INVAL, "null argument");
+    if (reinterpret_cast<uintptr_t>(container_dev) % 256 != 0)
+        return fail(CG_E_INVAL, "container buffer must be 256-byte aligned");
+    const uint32_t nchunks = ceil_div(t->S, t->Tc);
+    if (kb >= ke || ke > nchunks) return fail(CG_E_INVAL, "chunk range out of bounds");
+    const EncPlan p = enc_plan(t, kb, ke);
+    if (p.bytes > kStaticScratch)
+        return fail(CG_E_INVAL, "encode needs " + std::to_string(p.bytes) +
+                                    " bytes of scratch, more than the 64 MiB of cg_encode_noalloc");
+    DeviceScope ds;
+    CG_HIP(ds.enter(t->device), "hipSetDevice");
+    hipStream_t st = (hipStream_t)hip_stream;
+    const uint16_t *X = static_cast<const uint16_t *>(kv_dev);
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    uint8_t *sc = nullptr;
+    CG_HIP(static_scratch(t->device, &sc), "hipGetSymbolAddress");
+    uint64_t rb[2] = {0, 0};
+    const char *what = "";
+    hipError_t e = enc_code(t, X, kb, ke, sc, p, st, rb, &what);
+    if (e != hipSuccess) return hip_fail(e, what);
+    const cg_container_header h = enc_header(t, kb, ke, rb[0], rb[1]);
+    *header_out = h;
+    if (h.total_bytes > capacity)
+        return fail(CG_E_INVAL, "container needs " + std::to_string(h.total_bytes) +
+                                    " bytes, more than the capacity given (header_out holds its size)");
+    e = enc_write(t, X, kb, ke, sc, p, h, &h, static_cast<uint8_t *>(container_dev), st, &what);
+    if (e == hipSuccess) {
+        what = "hipStreamSynchronize";
+        e = hipStreamSynchronize(st);  // (the header is copied from this frame)
+    }
+    if (e != hipSuccess) return hip_fail(e, what);
     return CG_OK;
 }
 
