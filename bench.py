@@ -542,7 +542,8 @@ def main() -> int:
     ap.add_argument("--no-entropy", action="store_true",
                     help="skip the bits-per-symbol against empirical entropy report")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain 4 GiB device-to-device copy (counter calibration)")
+                    help="only run 4 GiB through a plain copy and through the decoder's access "
+                         "forms (memory-counter calibration)")
     ap.add_argument("--no-kv-asymmetric", action="store_true",
                     help="skip the paged-output, keys-finer-than-values and sink objects")
     ap.add_argument("--decode-reps", type=int, default=20,
@@ -559,13 +560,30 @@ def main() -> int:
     import torch
 
     if args.calibrate_copy:
+        # known byte counts for the memory counters: a plain 4 GiB device copy (torch),
+        # then 4 GiB through each of the decoder's access forms (libcg_calib.so):
+        # 4-byte non-temporal loads, 2-byte non-temporal loads, 2-byte non-temporal stores
+        import ctypes
+        from kv_cache_compression_cg_amd import build as _b
+        if not os.path.exists(_b.CALIB_LIB):
+            _b.build()
+        calib = ctypes.CDLL(_b.CALIB_LIB)
+        calib.cg_calib_run.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64,
+                                       ctypes.c_void_p, ctypes.c_void_p]
         n = 4 << 30
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
+        sink = torch.zeros(2048, dtype=torch.int32, device="cuda:0")
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         for _ in range(3):
             dst.copy_(src)
+        for kind in (0, 1, 2):
+            for _ in range(3):
+                assert calib.cg_calib_run(kind, src.data_ptr(), n, sink.data_ptr(), stream) == 0
         torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n, "reps": 3}), flush=True)
+        print(json.dumps({"calibrate_bytes": n, "reps": 3,
+                          "kernels": ["copy (torch)", "read4_nt", "read2_nt", "write2_nt"]}),
+              flush=True)
         return 0
 
     from kv_cache_compression_cg_amd import build, configs, synth

@@ -18,6 +18,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIB_DIR, "libcg.so")
+# counter-calibration kernels used by the benchmark only (not part of the codec's ABI)
+CALIB_LIB = os.path.join(LIB_DIR, "libcg_calib.so")
+CALIB_SOURCES = [os.path.join(CSRC, "cg_calib.hip")]
 SOURCES = [os.path.join(CSRC, "cg_kernels_encode.hip"), os.path.join(CSRC, "cg_kernels_decode.hip"),
            os.path.join(CSRC, "cg_api.cpp")]
 ARCH = os.environ.get("CG_OFFLOAD_ARCH", "gfx950")
@@ -36,14 +39,19 @@ def flags() -> list:
             "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + flags() + ["-shared", "-x", "hip"] + SOURCES + ["-o", tmp]
+def _link(sources, lib, verbose):
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + flags() + ["-shared", "-x", "hip"] + sources + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(LIB_DIR, exist_ok=True)
+    _link(SOURCES, LIB, verbose)
+    _link(CALIB_SOURCES, CALIB_LIB, verbose)
     return LIB
 
 

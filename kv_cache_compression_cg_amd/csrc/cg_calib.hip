@@ -1,0 +1,83 @@
+// cg_calib.hip -- memory-counter calibration kernels for the benchmark (not part of the
+// codec's ABI): reads and writes of a known number of bytes with the decoder's own access
+// forms, so that the hardware byte counters (FETCH_SIZE, WRITE_SIZE) can be scaled to
+// bytes for each form.
+//   read4_nt:   4-byte non-temporal buffer loads, 64 lanes reading 256 contiguous bytes
+//               (the decoder's payload-word fetches);
+//   read2_nt:   2-byte non-temporal buffer loads, 128 contiguous bytes per wavefront (its
+//               anchor-row loads);
+//   write2_nt:  2-byte non-temporal buffer stores, 128 contiguous bytes per wavefront (its
+//               output-row stores).
+// Each kernel walks the buffer in 256-thread blocks, grid-stride.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+constexpr int kNT = 2;
+constexpr int kFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kFlags);
+}
+
+// buffers are processed in windows of 1 GiB so that offsets fit a resource
+constexpr uint64_t kWin = 1ull << 30;
+
+__global__ __launch_bounds__(256) void read4_nt(const uint8_t *src, uint64_t bytes, uint32_t *sink)
+{
+    uint32_t acc = 0;
+    for (uint64_t w0 = 0; w0 < bytes; w0 += kWin) {
+        const uint32_t wb = (uint32_t)(bytes - w0 < kWin ? bytes - w0 : kWin);
+        const __amdgpu_buffer_rsrc_t rs = rsrc(src + w0, wb);
+        for (uint64_t i = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < wb;
+             i += (uint64_t)gridDim.x * blockDim.x * 4)
+            acc ^= __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)i, 0, kNT);
+    }
+    if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // keeps the loads; almost never stores
+}
+
+__global__ __launch_bounds__(256) void read2_nt(const uint8_t *src, uint64_t bytes, uint32_t *sink)
+{
+    uint32_t acc = 0;
+    for (uint64_t w0 = 0; w0 < bytes; w0 += kWin) {
+        const uint32_t wb = (uint32_t)(bytes - w0 < kWin ? bytes - w0 : kWin);
+        const __amdgpu_buffer_rsrc_t rs = rsrc(src + w0, wb);
+        for (uint64_t i = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 2; i < wb;
+             i += (uint64_t)gridDim.x * blockDim.x * 2)
+            acc ^= __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)i, 0, kNT);
+    }
+    if (acc == 0x79B9u) sink[blockIdx.x] = acc;  // (16-bit values: a 16-bit test)
+}
+
+__global__ __launch_bounds__(256) void write2_nt(uint8_t *dst, uint64_t bytes)
+{
+    for (uint64_t w0 = 0; w0 < bytes; w0 += kWin) {
+        const uint32_t wb = (uint32_t)(bytes - w0 < kWin ? bytes - w0 : kWin);
+        const __amdgpu_buffer_rsrc_t rs = rsrc(dst + w0, wb);
+        for (uint64_t i = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 2; i < wb;
+             i += (uint64_t)gridDim.x * blockDim.x * 2)
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)i, rs, (uint32_t)i, 0, kNT);
+    }
+}
+
+}  // namespace
+
+// kind 0: read4_nt, 1: read2_nt, 2: write2_nt over `bytes` (a multiple of 4) at buf.
+// sink: 4 * 2048 bytes of device memory.  Returns a hipError_t.
+extern "C" int cg_calib_run(int kind, void *buf, uint64_t bytes, void *sink, void *stream)
+{
+    const dim3 grid(2048), block(256);
+    hipStream_t st = (hipStream_t)stream;
+    if (kind == 0)
+        hipLaunchKernelGGL(read4_nt, grid, block, 0, st, (const uint8_t *)buf, bytes, (uint32_t *)sink);
+    else if (kind == 1)
+        hipLaunchKernelGGL(read2_nt, grid, block, 0, st, (const uint8_t *)buf, bytes, (uint32_t *)sink);
+    else if (kind == 2)
+        hipLaunchKernelGGL(write2_nt, grid, block, 0, st, (uint8_t *)buf, bytes);
+    else
+        return (int)hipErrorInvalidValue;
+    return (int)hipGetLastError();
+}
