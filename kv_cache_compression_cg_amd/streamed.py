@@ -35,6 +35,23 @@ def bandwidth_trace(n_chunks: int, seed: int = 0) -> np.ndarray:
     return rng.uniform(TRACE_LO_GBPS, TRACE_HI_GBPS, size=n_chunks)
 
 
+def correlated_trace(n_chunks: int, seed: int = 0, rho: float = 0.97) -> np.ndarray:
+    """Per-chunk link rate in Gbit/s that drifts rather than jumps: the log-rate follows a
+    seeded AR(1) process around the geometric middle of [1, 25] with lag-one correlation
+    rho, spread so that the stationary range covers [1, 25] at about two standard
+    deviations, and is clipped to [1, 25].  A link whose rate persists from one chunk to
+    the next is what a rate estimated from the chunks already sent can follow."""
+    rng = np.random.default_rng([seed, 6])
+    lo, hi = np.log(TRACE_LO_GBPS), np.log(TRACE_HI_GBPS)
+    mu, sigma = 0.5 * (lo + hi), 0.25 * (hi - lo)
+    z = np.empty(n_chunks)
+    prev = rng.standard_normal()
+    for k in range(n_chunks):
+        prev = rho * prev + np.sqrt(1.0 - rho * rho) * rng.standard_normal() if k else prev
+        z[k] = prev
+    return np.clip(np.exp(mu + sigma * z), TRACE_LO_GBPS, TRACE_HI_GBPS)
+
+
 def choose_levels(sizes: np.ndarray, bw_gbps: np.ndarray, ref_level: int = REFERENCE_LEVEL,
                   ref_gbps: Optional[float] = None) -> np.ndarray:
     """sizes: bytes [levels][chunks], level 0 the finest.  Returns the level per chunk."""
@@ -79,6 +96,11 @@ class ControllerConfig:
     prior_gbps: float = 10.0
     prefill_tok_per_s: float = 0.0
     text_bytes_per_token: int = 4
+    # the share of its slack a chunk may spend (1: all of it), and whether the remaining
+    # chunks are budgeted at the lower of the estimate and the last measured rate (a
+    # rate that has just fallen is then planned for before the estimate has caught up)
+    slack_share: float = 1.0
+    cautious: bool = False
 
 
 def control_levels(sizes: np.ndarray, bw_gbps: np.ndarray, chunk_tokens: Sequence[int],
@@ -93,14 +115,16 @@ def control_levels(sizes: np.ndarray, bw_gbps: np.ndarray, chunk_tokens: Sequenc
     if bw.shape != (n,) or len(chunk_tokens) != n:
         raise ValueError("one rate and one token count per chunk expected")
     est = float(cfg.prior_gbps)
+    last = est
     elapsed = 0.0
     levels = np.zeros(n, dtype=np.int64)
     estimates = np.zeros(n, dtype=np.float64)
     for k in range(n):
         estimates[k] = est
         pred = sizes[:, k] * 8.0 / (est * 1e9)
-        slack = cfg.slo_s - elapsed - float(np.sum(sizes[-1, k:])) * 8.0 / (est * 1e9)
-        allowed = pred[-1] + max(slack, 0.0) / (n - k)
+        plan = min(est, last) if cfg.cautious else est
+        slack = cfg.slo_s - elapsed - float(np.sum(sizes[-1, k:])) * 8.0 / (plan * 1e9)
+        allowed = pred[-1] + cfg.slack_share * max(slack, 0.0) / (n - k)
         choice = int(np.nonzero(pred <= allowed)[0][0])   # the coarsest level always fits
         text_bytes = float(chunk_tokens[k]) * cfg.text_bytes_per_token
         recompute = (float(chunk_tokens[k]) / cfg.prefill_tok_per_s
@@ -111,6 +135,7 @@ def control_levels(sizes: np.ndarray, bw_gbps: np.ndarray, chunk_tokens: Sequenc
         elapsed += sent * 8.0 / (bw[k] * 1e9) + (recompute if choice == TEXT else 0.0)
         # the transfer just made measures the link rate of this chunk
         est = cfg.alpha * bw[k] + (1.0 - cfg.alpha) * est
+        last = bw[k]
         levels[k] = choice
     return levels, estimates, elapsed
 
@@ -143,15 +168,17 @@ class Prepared:
 
 def prepare(kv: torch.Tensor, group: int, chunk: int, level_bins: Sequence[Sequence[int]],
             H_kv: int, seed: int = 0, force_levels: Optional[Sequence[int]] = None,
-            controller: Optional[ControllerConfig] = None) -> Prepared:
+            controller: Optional[ControllerConfig] = None,
+            trace: Optional[np.ndarray] = None) -> Prepared:
     """Builds the tables of every level, encodes every chunk at every level, picks one
     level per chunk and keeps that container in pinned host memory.  A chunk at level
     TEXT (recomputed from text) is not kept.  With `controller`, the levels come from
     control_levels over the trace: the container sizes of every chunk at every level are
-    taken first (a sender has them: the containers are encoded ahead of time)."""
+    taken first (a sender has them: the containers are encoded ahead of time).  `trace`:
+    the per-chunk link rates (default: the uniform trace of `seed`)."""
     tables = [cg.build_cdf(kv, group, chunk, bins, H_kv=H_kv) for bins in level_bins]
     n = tables[0].n_chunks
-    bw = bandwidth_trace(n, seed)
+    bw = bandwidth_trace(n, seed) if trace is None else np.asarray(trace, dtype=np.float64)
     if controller is not None:
         all_sizes = np.array([[cg.encode(t, kv, k, k + 1).nbytes for k in range(n)]
                               for t in tables], dtype=np.int64)

@@ -107,3 +107,40 @@ def test_controller_without_fallback_never_sends_text():
     cfg.prefill_tok_per_s = 1e6
     lv, _, _ = streamed.control_levels(sizes, rng.uniform(0.1, 1.0, size=30), [1536] * 30, cfg)
     assert (lv == streamed.TEXT).all()
+
+
+def test_correlated_trace_is_seeded_in_range_and_persistent():
+    a = streamed.correlated_trace(86, 0)
+    assert np.array_equal(a, streamed.correlated_trace(86, 0))
+    assert a.shape == (86,) and a.min() >= 1.0 and a.max() <= 25.0
+    assert not np.array_equal(a, streamed.correlated_trace(86, 1))
+    la = np.log(streamed.correlated_trace(4000, 3))
+    r1 = np.corrcoef(la[:-1], la[1:])[0, 1]
+    assert 0.9 < r1 < 0.99                           # lag-one correlation near rho = 0.97
+    u = np.log(streamed.bandwidth_trace(4000, 3))
+    assert abs(np.corrcoef(u[:-1], u[1:])[0, 1]) < 0.1   # the uniform trace has none
+
+
+def test_cautious_controller_tracks_a_persistent_rate():
+    """With the rate persisting from chunk to chunk the estimate from the chunks already
+    sent stays close to each chunk's rate (far closer than on the uniform trace), and the
+    cautious controller (a quarter of the slack spent, the remaining chunks budgeted at
+    the lower of the estimate and the last rate) meets an SLO of the open-loop choice's
+    fetch time plus 2% on the correlated trace, over several seeds."""
+    n = 86
+    tokens = [1536] * n
+    errs = {}
+    for seed in range(4):
+        rng = np.random.default_rng(seed)
+        base = rng.uniform(0.8, 1.2, size=n) * 4e7
+        sizes = np.stack([base, base * 0.6, base * 0.35])
+        for name, bw in (("corr", streamed.correlated_trace(n, seed)),
+                         ("unif", streamed.bandwidth_trace(n, seed))):
+            slo = streamed.network_seconds(sizes, streamed.choose_levels(sizes, bw), bw)
+            cfg = streamed.ControllerConfig(slo_s=slo * 1.02, prior_gbps=13.0, alpha=0.8,
+                                            slack_share=0.25, cautious=True)
+            lv, est, fetch = streamed.control_levels(sizes, bw, tokens, cfg)
+            errs.setdefault(name, []).append(np.median(np.abs(est[1:] - bw[1:]) / bw[1:]))
+            if name == "corr":
+                assert fetch <= cfg.slo_s, seed
+    assert max(errs["corr"]) < 0.2 and min(errs["unif"]) > 2 * max(errs["corr"])
