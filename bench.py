@@ -231,7 +231,7 @@ def entropy_report(w, X, tab, blob) -> dict:
     return out
 
 
-def streamed_report(dev, n_slots: int = 8, reps: int = 3, seed: int = 0) -> dict:
+def streamed_report(dev, n_slots: int = 32, reps: int = 3, seed: int = 0) -> dict:
     """The 131K-token cache streamed chunk by chunk from pinned host memory, each chunk
     at the level its bandwidth-trace entry allows, decoded while later chunks copy."""
     import numpy as np

@@ -318,15 +318,19 @@ typedef struct cg_stream_item {
 typedef struct cg_stream_stats {
     float total_ms;        /* first copy started -> last decode finished */
     float copy_ms;         /* sum over items of the host-to-device copy */
-    float decode_ms;       /* sum over items of the decode */
+    float decode_ms;       /* sum over windows of the decode (see cg_stream_decode) */
     uint64_t copied_bytes; /* sum over items of the container size */
 } cg_stream_stats;
 
 /*
  * Decodes items[0 .. n_items) in order into kv_out_dev (fp16 [L][2][S][C]).  Item i is
  * copied into staging slot i % n_slots (slot j starts at staging_dev + j * slot_bytes)
- * on copy_stream and decoded from there on decode_stream (sink tokens as in cg_decode);
- * a slot is refilled only after the decode that read it has finished.
+ * on copy_stream and decoded from there on decode_stream (sink tokens and outliers as in
+ * cg_decode); a slot is refilled only after the decode that read it has finished.  The
+ * items are decoded in windows of min(32, max(1, n_slots / 2)) consecutive items: once a
+ * window's copies have landed, one launch decodes every chunk of the window (more than
+ * one if the window holds over 32 chunks or 4 sets of tables, or fp16 and 8-bit anchors),
+ * while the next window is copied into other slots.
  *   staging_dev:   caller-owned device memory, n_slots * slot_bytes bytes; the address
  *                  and slot_bytes are multiples of 256.
  *   copy_stream, decode_stream: two different streams of the tables' device.

@@ -800,6 +800,65 @@ bool same_shape(const cg_tables *a, const cg_tables *b)
            a->Tc == b->Tc;
 }
 
+// Decodes every chunk of items[0 .. n) (container i staged at slot[i]) with as few
+// multi-container launches as the launch limits allow: the chunks are grouped by their
+// tables (first appearance order), each group cut into sets of up to 8 chunks, and the
+// sets packed into launches of up to kMaxBatch chunks and kMaxBatchTables tables, with
+// fp16 and 8-bit anchors in launches of their own.
+hipError_t decode_window(const cg_stream_item *items, uint32_t n, uint8_t *const *slot,
+                         uint16_t *out, hipStream_t st)
+{
+    const Geom g = make_geom(items[0].tables, 0, 1);
+    std::vector<const cg_tables *> order;
+    for (uint32_t i = 0; i < n; ++i)
+        if (std::find(order.begin(), order.end(), items[i].tables) == order.end())
+            order.push_back(items[i].tables);
+    for (int a8 = 0; a8 < 2; ++a8) {
+        ChunkSrcs srcs{};
+        uint32_t n_ch = 0, n_tab = 0;
+        auto flush = [&]() -> hipError_t {
+            hipError_t e = launch_k3_multi(g, srcs, out, st);
+            srcs = ChunkSrcs{};
+            n_ch = n_tab = 0;
+            return e;
+        };
+        for (const cg_tables *t : order) {
+            if ((t->d_alo != nullptr) != (a8 == 1)) continue;
+            // this group's chunks in item order
+            std::vector<BatchChunk> chunks;
+            for (uint32_t i = 0; i < n; ++i) {
+                if (items[i].tables != t) continue;
+                const cg_blob *b = items[i].blob;
+                const ContainerView cv = view_of(b);
+                for (uint32_t k = b->hdr.chunk_begin; k < b->hdr.chunk_end; ++k)
+                    chunks.push_back(BatchChunk{slot[i], cv.offsets_off, cv.anchors_off,
+                                                cv.anchors_bytes, cv.payload_off,
+                                                cv.payload_words, k, b->hdr.chunk_begin});
+            }
+            for (size_t c0 = 0; c0 < chunks.size();) {
+                const uint32_t m =
+                    (uint32_t)std::min<size_t>(kBatchSetChunks, chunks.size() - c0);
+                if (n_ch + m > kMaxBatch || srcs.n_sets == kMaxBatch ||
+                    (n_tab == kMaxBatchTables && !(srcs.tab[n_tab - 1].dtab == t->d_dtab))) {
+                    if (hipError_t e = flush()) return e;
+                }
+                if (n_tab == 0 || srcs.tab[n_tab - 1].dtab != t->d_dtab)
+                    srcs.tab[n_tab++] = BatchTables{t->d_bins, t->d_dtab, t->d_lo, t->d_w,
+                                                    t->d_alo, t->d_aw};
+                const uint32_t j = srcs.n_sets++;
+                srcs.set_first[j] = (uint8_t)n_ch;
+                srcs.set_n[j] = (uint8_t)m;
+                srcs.set_tab[j] = (uint8_t)(n_tab - 1);
+                for (uint32_t q = 0; q < m; ++q) srcs.ch[n_ch++] = chunks[c0 + q];
+                c0 += m;
+            }
+        }
+        if (srcs.n_sets)
+            if (hipError_t e = flush()) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace
 
 int cg_stream_decode(const cg_stream_item *items, uint32_t n_items, void *staging_dev,
@@ -835,61 +894,99 @@ int cg_stream_decode(const cg_stream_item *items, uint32_t n_items, void *stagin
     CG_HIP(ds.enter(t0->device), "hipSetDevice");
     hipStream_t cs = (hipStream_t)copy_stream, dec = (hipStream_t)decode_stream;
 
-    // per slot: copied (decode may start) and freed (the slot may be refilled); with
-    // stats, per item: copy start/end and decode start/end
-    EventSet slot_ev, item_ev;
-    CG_HIP(slot_ev.make(2 * (size_t)n_slots, false), "hipEventCreate");
-    if (stats) CG_HIP(item_ev.make(4 * (size_t)n_items, true), "hipEventCreate");
-    hipEvent_t *copied = slot_ev.ev.data(), *freed = copied + n_slots;
+    // Items are decoded in windows of up to `batch` (half the slots, at most 32): the
+    // window's copies go out back to back, and once the last has landed a multi-container
+    // decode takes every chunk of the window, whatever its tables (a lone chunk per launch
+    // fills too little of the GPU, and a launch per level leaves it idle between
+    // launches).  Meanwhile the next window copies into other slots.  The last windows
+    // shrink (batch / 2, batch / 4, batch / 8 items, at least 1) so that little decoding
+    // is left once the last copy has landed; the first window takes what does not divide.
+    // Per window: copied (its decode may start) and decoded (its slots may be refilled);
+    // with stats, per item: copy start/end, and per window: decode start/end.
+    const uint32_t batch = std::min(kMaxBatch, n_slots > 1 ? n_slots / 2 : 1u);
+    std::vector<uint32_t> wbeg;   // window starts, then n_items
+    {
+        std::vector<uint32_t> sizes;   // from the last window back
+        uint32_t left = n_items, m = std::max(1u, batch / 8);
+        while (left) {
+            sizes.push_back(std::min(left, m));
+            left -= sizes.back();
+            m = std::min(batch, 2 * m);
+        }
+        wbeg.push_back(0);
+        for (size_t j = sizes.size(); j-- > 0;) wbeg.push_back(wbeg.back() + sizes[j]);
+    }
+    const uint32_t n_windows = (uint32_t)wbeg.size() - 1;
+    std::vector<uint32_t> win_of(n_items);
+    for (uint32_t wi = 0; wi < n_windows; ++wi)
+        for (uint32_t i = wbeg[wi]; i < wbeg[wi + 1]; ++i) win_of[i] = wi;
+    EventSet slot_ev, item_ev, win_ev;
+    CG_HIP(slot_ev.make(2 * (size_t)n_windows, false), "hipEventCreate");
+    if (stats) {
+        CG_HIP(item_ev.make(2 * (size_t)n_items, true), "hipEventCreate");
+        CG_HIP(win_ev.make(2 * (size_t)n_windows, true), "hipEventCreate");
+    }
+    hipEvent_t *copied = slot_ev.ev.data(), *decoded = copied + n_windows;
 
     hipError_t err = hipSuccess;
     const char *what = "";
     uint64_t bytes = 0;
-    const uint32_t batch = n_slots > 1 ? n_slots / 2 : 1;
-    for (uint32_t i = 0; i < n_items && err == hipSuccess; ++i) {
-        const cg_stream_item &it = items[i];
-        const uint32_t j = i % n_slots;
-        uint8_t *slot = static_cast<uint8_t *>(staging_dev) + (uint64_t)j * slot_bytes;
-        const uint64_t nb = it.blob->hdr.total_bytes;
-        hipEvent_t *ie = stats ? item_ev.ev.data() + 4 * (size_t)i : nullptr;
-        // slot reuse: one wait per `batch` items, on the decode of the last item whose
-        // slot the next `batch` items take (decodes finish in order, so that event covers
-        // the earlier ones).  A wait per copy leaves the copy engine idle between copies.
-        if (i >= n_slots && (i - n_slots) % batch == 0) {
-            const uint32_t last = i - n_slots + batch - 1;
-            if ((err = hipStreamWaitEvent(cs, freed[last % n_slots], 0)) != hipSuccess) {
-                what = "hipStreamWaitEvent";
+    uint16_t *out = static_cast<uint16_t *>(kv_out_dev);
+    auto slot_of = [&](uint32_t i) {
+        return static_cast<uint8_t *>(staging_dev) + (uint64_t)(i % n_slots) * slot_bytes;
+    };
+    uint32_t waited = 0;   // windows [0, waited) known decoded on the copy stream
+    for (uint32_t wi = 0; wi < n_windows && err == hipSuccess; ++wi) {
+        const uint32_t ib = wbeg[wi], ie_ = wbeg[wi + 1];
+        for (uint32_t i = ib; i < ie_; ++i) {
+            const cg_stream_item &it = items[i];
+            hipEvent_t *ie = stats ? item_ev.ev.data() + 2 * (size_t)i : nullptr;
+            // slot reuse: item i - n_slots, which held this slot, must have been decoded.
+            // Its window is an earlier one (windows hold at most n_slots / 2 items),
+            // already queued; one wait per window, as a wait per copy leaves the copy
+            // engine idle between copies.
+            if (i >= n_slots && win_of[i - n_slots] >= waited) {
+                const uint32_t w = win_of[i - n_slots];
+                if ((err = hipStreamWaitEvent(cs, decoded[w], 0)) != hipSuccess) {
+                    what = "hipStreamWaitEvent";
+                    break;
+                }
+                waited = w + 1;
+            }
+            if (ie && (err = hipEventRecord(ie[0], cs)) != hipSuccess) { what = "hipEventRecord"; break; }
+            if ((err = hipMemcpyAsync(slot_of(i), it.host_container, it.blob->hdr.total_bytes,
+                                      hipMemcpyHostToDevice, cs)) != hipSuccess) {
+                what = "hipMemcpyAsync";
                 break;
             }
+            if (ie && (err = hipEventRecord(ie[1], cs)) != hipSuccess) { what = "hipEventRecord"; break; }
+            bytes += it.blob->hdr.total_bytes;
         }
-        if (ie && (err = hipEventRecord(ie[0], cs)) != hipSuccess) { what = "hipEventRecord"; break; }
-        if ((err = hipMemcpyAsync(slot, it.host_container, nb, hipMemcpyHostToDevice, cs)) !=
-            hipSuccess) {
-            what = "hipMemcpyAsync";
-            break;
-        }
-        if (ie && (err = hipEventRecord(ie[1], cs)) != hipSuccess) { what = "hipEventRecord"; break; }
-        if ((err = hipEventRecord(copied[j], cs)) != hipSuccess ||
-            (err = hipStreamWaitEvent(dec, copied[j], 0)) != hipSuccess) {
+        if (err != hipSuccess) break;
+        if ((err = hipEventRecord(copied[wi], cs)) != hipSuccess ||
+            (err = hipStreamWaitEvent(dec, copied[wi], 0)) != hipSuccess) {
             what = "copy -> decode event";
             break;
         }
-        if (ie && (err = hipEventRecord(ie[2], dec)) != hipSuccess) { what = "hipEventRecord"; break; }
-        const cg_blob *b = it.blob;
-        Geom g = make_geom(it.tables, b->hdr.chunk_begin, b->hdr.chunk_end);
-        if ((err = launch_k3(g, it.tables->d_bins, it.tables->d_dtab, it.tables->d_lo, it.tables->d_w, slot, view_of(b),
-                             static_cast<uint16_t *>(kv_out_dev), nullptr, dec)) != hipSuccess) {
-            what = "k3_decode";
+        hipEvent_t *we = stats ? win_ev.ev.data() + 2 * (size_t)wi : nullptr;
+        if (we && (err = hipEventRecord(we[0], dec)) != hipSuccess) { what = "hipEventRecord"; break; }
+        std::vector<uint8_t *> slots(ie_ - ib);
+        for (uint32_t i = ib; i < ie_; ++i) slots[i - ib] = slot_of(i);
+        if ((err = decode_window(items + ib, ie_ - ib, slots.data(), out, dec)) != hipSuccess) {
+            what = "k3_decode_multi";
             break;
         }
-        if ((err = put_extras(it.tables, b, slot, static_cast<uint16_t *>(kv_out_dev), Paged{}, dec)) !=
-            hipSuccess) {
-            what = "sinks / outliers";
+        // sinks and outliers after the decodes that wrote those rows
+        for (uint32_t i = ib; i < ie_ && err == hipSuccess; ++i)
+            if ((err = put_extras(items[i].tables, items[i].blob, slot_of(i), out, Paged{}, dec)) !=
+                hipSuccess)
+                what = "sinks / outliers";
+        if (err != hipSuccess) break;
+        if (we && (err = hipEventRecord(we[1], dec)) != hipSuccess) { what = "hipEventRecord"; break; }
+        if ((err = hipEventRecord(decoded[wi], dec)) != hipSuccess) {
+            what = "hipEventRecord";
             break;
         }
-        if (ie && (err = hipEventRecord(ie[3], dec)) != hipSuccess) { what = "hipEventRecord"; break; }
-        if ((err = hipEventRecord(freed[j], dec)) != hipSuccess) { what = "hipEventRecord"; break; }
-        bytes += nb;
     }
     if (err != hipSuccess) {
         (void)hipStreamSynchronize(cs);
@@ -901,15 +998,18 @@ int cg_stream_decode(const cg_stream_item *items, uint32_t n_items, void *stagin
     CG_HIP(hipStreamSynchronize(cs), "hipStreamSynchronize");
     CG_HIP(hipStreamSynchronize(dec), "hipStreamSynchronize");
     cg_stream_stats st{};
-    const hipEvent_t *ie = item_ev.ev.data();
+    const hipEvent_t *ie = item_ev.ev.data(), *we = win_ev.ev.data();
     for (uint32_t i = 0; i < n_items; ++i) {
-        float c = 0.f, d = 0.f;
-        CG_HIP(hipEventElapsedTime(&c, ie[4 * i], ie[4 * i + 1]), "hipEventElapsedTime");
-        CG_HIP(hipEventElapsedTime(&d, ie[4 * i + 2], ie[4 * i + 3]), "hipEventElapsedTime");
+        float c = 0.f;
+        CG_HIP(hipEventElapsedTime(&c, ie[2 * i], ie[2 * i + 1]), "hipEventElapsedTime");
         st.copy_ms += c;
+    }
+    for (uint32_t wi = 0; wi < n_windows; ++wi) {
+        float d = 0.f;
+        CG_HIP(hipEventElapsedTime(&d, we[2 * wi], we[2 * wi + 1]), "hipEventElapsedTime");
         st.decode_ms += d;
     }
-    CG_HIP(hipEventElapsedTime(&st.total_ms, ie[0], ie[4 * ((size_t)n_items - 1) + 3]),
+    CG_HIP(hipEventElapsedTime(&st.total_ms, ie[0], we[2 * ((size_t)n_windows - 1) + 1]),
            "hipEventElapsedTime");
     st.copied_bytes = bytes;
     *stats = st;

@@ -54,6 +54,32 @@ struct ContainerView {
 
 constexpr uint32_t kFineBins = 256;               // fine grid of the outlier clip
 
+// Chunks decoded by one launch from containers of their own (the streamed decode).  The
+// chunks form sets, each of up to 8 chunks that share one set of tables; set j is chunks
+// [set_first[j], set_first[j] + set_n[j]) with tables tab[set_tab[j]].  Chunk i is chunk
+// k of the cache, read from the container at c (whose first chunk is kb) with the
+// payload / offsets / anchors sections at the given byte offsets.
+constexpr uint32_t kMaxBatch = 32;        // chunks (and sets) one launch takes
+constexpr uint32_t kMaxBatchTables = 4;   // sets of tables one launch takes
+constexpr uint32_t kBatchSetChunks = 8;   // chunks of a set: 4 wavefronts x 2 streams
+struct BatchTables {
+    const uint8_t *bins;
+    const uint32_t *dtab;
+    const float *lo, *w;
+    const float *alo, *aw;   // 8-bit anchor grid, null for fp16 anchors
+};
+struct BatchChunk {
+    const uint8_t *c;
+    uint64_t offsets_off, anchors_off, anchors_bytes, payload_off, payload_words;
+    uint32_t k, kb;
+};
+struct ChunkSrcs {
+    uint32_t n_sets;
+    uint8_t set_first[kMaxBatch], set_n[kMaxBatch], set_tab[kMaxBatch];
+    BatchTables tab[kMaxBatchTables];
+    BatchChunk ch[kMaxBatch];
+};
+
 hipError_t launch_k0(const uint16_t *X, const Geom &g, uint32_t tpt, uint32_t *ord_lo,
                      uint32_t *ord_hi, uint32_t *flag, hipStream_t st);
 // lo and hi (zero bounds as +0) from the ordered min / max
@@ -115,6 +141,9 @@ hipError_t launch_k5_compact(const uint16_t *regions, uint64_t region_words,
 hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, const float *lo,
                      const float *w, const uint8_t *container, const ContainerView &cv,
                      uint16_t *out, uint8_t *sym_out, hipStream_t st);
+// Decodes the chunk sets of srcs (g gives the cache shape; its tables fields are unused).
+// Every set's tables have 8-bit anchors, or none has.
+hipError_t launch_k3_multi(const Geom &g, const ChunkSrcs &srcs, uint16_t *out, hipStream_t st);
 hipError_t launch_k3_paged(const Geom &g, const uint8_t *bins, const uint32_t *dtab,
                            const float *lo, const float *w, const uint8_t *container,
                            const ContainerView &cv, const Paged &pg, hipStream_t st);

@@ -539,7 +539,8 @@ __device__ __forceinline__ void paired_steps(Stream<SYMBOLS, PAGED, A8> (&st)[NS
 // One wavefront decodes NS chunks of the same (row, channel block) in lockstep, sharing
 // the block's LDS table.  With two, the symbol decodes of both streams sit in one
 // basic block, so the dependent LDS reads of one overlap the arithmetic of the other.
-template <bool SYMBOLS, bool FULL, int NS, bool PAGED, bool A8>
+// With MULTI, k0 and k1 index srcs->ch: the chunk and the container it is read from.
+template <bool SYMBOLS, bool FULL, int NS, bool PAGED, bool A8, bool MULTI = false>
 __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__restrict__ tab,
                                               uint16_t *__restrict__ ring,
                                               const float *__restrict__ lo,
@@ -548,14 +549,32 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
                                               const ContainerView &cv, uint32_t k0, uint32_t k1,
                                               uint32_t row, uint32_t b, uint32_t lane,
                                               uint16_t *__restrict__ out,
-                                              uint8_t *__restrict__ sym_out, const Paged &pg)
+                                              uint8_t *__restrict__ sym_out, const Paged &pg,
+                                              const ChunkSrcs *srcs = nullptr)
 {
     const bool present = FULL || lane < min(kLanes, g.C - b * kLanes);
     Stream<SYMBOLS, PAGED, A8> st[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-        st[s].init(g, ring + s * kRingAlloc, lo, w, container, cv, s == 0 ? k0 : k1, row, b, lane,
-                   present, out, sym_out, pg);
+    for (int s = 0; s < NS; ++s) {
+        const uint32_t i = s == 0 ? k0 : k1;
+        if constexpr (MULTI) {
+            const BatchChunk &ch = srcs->ch[i];
+            Geom gk = g;
+            gk.kb = ch.kb;
+            gk.ke = ch.k + 1;
+            ContainerView cvk{};
+            cvk.offsets_off = ch.offsets_off;
+            cvk.anchors_off = ch.anchors_off;
+            cvk.anchors_bytes = ch.anchors_bytes;
+            cvk.payload_off = ch.payload_off;
+            cvk.payload_words = ch.payload_words;
+            st[s].init(gk, ring + s * kRingAlloc, lo, w, ch.c, cvk, ch.k, row, b, lane, present,
+                       out, sym_out, pg);
+        } else {
+            st[s].init(g, ring + s * kRingAlloc, lo, w, container, cv, i, row, b, lane, present,
+                       out, sym_out, pg);
+        }
+    }
 #pragma unroll
     for (int s = 0; s < NS; ++s) st[s].first_anchor(lane);
     uint32_t ngmax = st[0].ng;
@@ -628,15 +647,16 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
 // row: otherwise an XCD would hold only the columns b with one residue mod 8, and its
 // writes and anchor reads would queue on the few L2 / memory channels those addresses
 // map to.
-template <bool SYMBOLS, uint32_t WPB, bool PAGED = false, bool A8 = false>
-__global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
-                                                  const uint32_t *__restrict__ dtab,
-                                                  const float *__restrict__ lo,
-                                                  const float *__restrict__ w,
-                                                  const uint8_t *__restrict__ container,
-                                                  ContainerView cv, uint32_t n_sets,
-                                                  uint16_t *__restrict__ out,
-                                                  uint8_t *__restrict__ sym_out, Paged pg)
+template <bool SYMBOLS, uint32_t WPB, bool PAGED, bool A8, bool MULTI>
+__device__ __forceinline__ void decode_block(Geom g, const uint8_t *__restrict__ bins,
+                                             const uint32_t *__restrict__ dtab,
+                                             const float *__restrict__ lo,
+                                             const float *__restrict__ w,
+                                             const uint8_t *__restrict__ container,
+                                             const ContainerView &cv, uint32_t n_sets,
+                                             uint16_t *__restrict__ out,
+                                             uint8_t *__restrict__ sym_out, const Paged &pg,
+                                             const ChunkSrcs *srcs)
 {
     __shared__ uint32_t tab[kLdsWords];
     __shared__ uint16_t rings[WPB * kStreamsPerWave * kRingAlloc];
@@ -644,6 +664,19 @@ __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__r
     const uint32_t set = tmp % n_sets;
     const uint32_t row = tmp / n_sets;
     const uint32_t b = (blockIdx.x % g.NB + row) % g.NB;
+    // chunks (indices into srcs->ch with MULTI) of this wavefront: k0, and k1 if below ke
+    uint32_t k0 = g.kb + set * WPB * kStreamsPerWave;
+    if constexpr (MULTI) {
+        const BatchTables &t = srcs->tab[srcs->set_tab[set]];
+        bins = t.bins;
+        dtab = t.dtab;
+        lo = t.lo;
+        w = t.w;
+        g.alo = t.alo;
+        g.aw = t.aw;
+        k0 = srcs->set_first[set];
+        g.ke = k0 + srcs->set_n[set];
+    }
     const uint32_t N = bins[row];
     // stage f and cdf of the N used entries as bytes, and the slot table
     const uint32_t *src = dtab + (uint64_t)(row * g.NB + b) * kTabBlock;
@@ -660,7 +693,7 @@ __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__r
     __syncthreads();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     const uint32_t lane = threadIdx.x % kLanes;
-    const uint32_t k0 = g.kb + set * WPB * kStreamsPerWave + wave;
+    k0 += wave;
     const uint32_t k1 = k0 + WPB;
     if (k0 >= g.ke) return;
     const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab);
@@ -668,15 +701,41 @@ __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__r
     const bool pair = k1 < g.ke;
     if (g.C - b * kLanes >= kLanes) {
         if (pair)
-            decode_chunks<SYMBOLS, true, 2, PAGED, A8>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
+            decode_chunks<SYMBOLS, true, 2, PAGED, A8, MULTI>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
         else
-            decode_chunks<SYMBOLS, true, 1, PAGED, A8>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
+            decode_chunks<SYMBOLS, true, 1, PAGED, A8, MULTI>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
     } else {
         if (pair)
-            decode_chunks<SYMBOLS, false, 2, PAGED, A8>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
+            decode_chunks<SYMBOLS, false, 2, PAGED, A8, MULTI>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
         else
-            decode_chunks<SYMBOLS, false, 1, PAGED, A8>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg);
+            decode_chunks<SYMBOLS, false, 1, PAGED, A8, MULTI>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
     }
+}
+
+template <bool SYMBOLS, uint32_t WPB, bool PAGED = false, bool A8 = false>
+__global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
+                                                  const uint32_t *__restrict__ dtab,
+                                                  const float *__restrict__ lo,
+                                                  const float *__restrict__ w,
+                                                  const uint8_t *__restrict__ container,
+                                                  ContainerView cv, uint32_t n_sets,
+                                                  uint16_t *__restrict__ out,
+                                                  uint8_t *__restrict__ sym_out, Paged pg)
+{
+    decode_block<SYMBOLS, WPB, PAGED, A8, false>(g, bins, dtab, lo, w, container, cv, n_sets, out,
+                                                 sym_out, pg, nullptr);
+}
+
+// The streamed decode's form: chunks from containers of their own, in sets that share
+// tables (see ChunkSrcs); blocks and wavefronts as above, a block per (row, channel
+// block, set).
+template <uint32_t WPB, bool A8>
+__global__ __launch_bounds__(WPB * 64) void k3_decode_multi(Geom g, uint16_t *__restrict__ out,
+                                                        ChunkSrcs srcs)
+{
+    decode_block<false, WPB, false, A8, true>(g, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                              ContainerView{}, srcs.n_sets, out, nullptr,
+                                              Paged{}, &srcs);
 }
 
 // ------------------------------------------------------------------------------ K4
@@ -885,6 +944,33 @@ hipError_t launch_apply_outliers(const Geom &g, const uint8_t *container, const 
     else
         hipLaunchKernelGGL(k_apply_outliers<false>, dim3(blocks), dim3(256), 0, st, g, container, cv,
                            n_groups, out, pg);
+    return hipGetLastError();
+}
+
+hipError_t launch_k3_multi(const Geom &g, const ChunkSrcs &srcs, uint16_t *out, hipStream_t st)
+{
+    if (srcs.n_sets == 0) return hipSuccess;
+    if (srcs.n_sets > kMaxBatch) return hipErrorInvalidValue;
+    uint32_t most = 0;
+    for (uint32_t j = 0; j < srcs.n_sets; ++j) {
+        if (srcs.set_n[j] == 0 || srcs.set_n[j] > kBatchSetChunks ||
+            srcs.set_first[j] + srcs.set_n[j] > kMaxBatch || srcs.set_tab[j] >= kMaxBatchTables)
+            return hipErrorInvalidValue;
+        most = std::max<uint32_t>(most, srcs.set_n[j]);
+    }
+    const bool a8 = srcs.tab[srcs.set_tab[0]].alo != nullptr;
+    // sets of at most 2 chunks: one wavefront per block (see k3_decode)
+    const bool wide = most > kStreamsPerWave;
+    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * srcs.n_sets;
+    const dim3 grid((uint32_t)blocks), block((wide ? kWavesPerBlock : 1u) * kLanes);
+    if (a8 && wide)
+        hipLaunchKernelGGL((k3_decode_multi<kWavesPerBlock, true>), grid, block, 0, st, g, out, srcs);
+    else if (a8)
+        hipLaunchKernelGGL((k3_decode_multi<1, true>), grid, block, 0, st, g, out, srcs);
+    else if (wide)
+        hipLaunchKernelGGL((k3_decode_multi<kWavesPerBlock, false>), grid, block, 0, st, g, out, srcs);
+    else
+        hipLaunchKernelGGL((k3_decode_multi<1, false>), grid, block, 0, st, g, out, srcs);
     return hipGetLastError();
 }
 

@@ -10,9 +10,12 @@ the reference level would take at the trace's mean rate, and takes the finest le
 container meets that deadline at the chunk's own rate, else the coarsest level.
 
 Host logic only: the copies and decodes run in libcg (cg_stream_decode), on two HIP
-streams.  Eight staging slots by default: with only two or three, a copy that must wait
-for the decode freeing its slot leaves the copy engine idle for a while after that
-decode has finished, and the copies no longer run back to back.
+streams.  32 staging slots by default: the chunks are decoded in windows of half the
+slots, one launch per window.  The decoder stages one chunk's tables per block and a
+block decodes only chunks that share them, so a window of 16 chunks over three levels
+gives each block about five chunks; with one chunk a launch it fills too little of the
+GPU.  With only two or three slots a copy that must wait for the decode freeing its slot
+also leaves the copy engine idle for a while.
 """
 from __future__ import annotations
 
@@ -212,14 +215,14 @@ class Pipeline:
     """Staging slots and the copy / decode streams, made once and reused: a stream's
     first use and a fresh allocation would otherwise fall inside the timed run."""
 
-    def __init__(self, prep: Prepared, device, n_slots: int = 8):
+    def __init__(self, prep: Prepared, device, n_slots: int = 32):
         self.n_slots = n_slots
         self.staging = torch.empty(n_slots * prep.slot_bytes, dtype=torch.uint8, device=device)
         self.copy_stream = torch.cuda.Stream(device=device)
         self.decode_stream = torch.cuda.Stream(device=device)
 
 
-def run(prep: Prepared, out: torch.Tensor, n_slots: int = 8,
+def run(prep: Prepared, out: torch.Tensor, n_slots: int = 32,
         pipe: Optional[Pipeline] = None) -> dict:
     """Streams every chunk into `out` and returns the event timings."""
     if pipe is None or pipe.staging.numel() < n_slots * prep.slot_bytes:

@@ -57,7 +57,9 @@ def _oracle_stream(Xh, H, G, Tc, level_bins, levels):
     return ref, encs
 
 
-@pytest.mark.parametrize("n_slots", [1, 2, 3])
+# 1 to 3 slots: windows of one chunk; 5, 8, 16: windows of 2, 4 and 8 chunks decoded by
+# one launch per level
+@pytest.mark.parametrize("n_slots", [1, 2, 3, 5, 8, 16])
 def test_streamed_forced_levels(cg, n_slots):
     L, S, H, d, G, Tc = 3, 4000, 2, 64, 10, 300
     _say("[streamed] L=%d S=%d C=%d G=%d Tc=%d slots=%d" % (L, S, H * d, G, Tc, n_slots))
@@ -238,3 +240,43 @@ def test_stream_decode_writes_sink_tokens(cg, anchor_bits):
     torch.cuda.synchronize()
     assert torch.equal(got[:, :, :24].view(torch.int16), ref[:, :, :24].view(torch.int16))
     assert torch.equal(got[:, :, :12].view(torch.int16), X[:, :, :12].view(torch.int16))
+
+
+@pytest.mark.parametrize("n_slots", [2, 7, 16, 64])
+def test_stream_decode_multi_chunk_items(cg, n_slots):
+    """Items whose containers hold one to 25 chunks, under three sets of tables (one with
+    sinks and an outlier table, one with 8-bit anchors), in windows of one to 32 items:
+    a window can hold more chunks than one launch takes and tables of both anchor widths.
+    The result equals cg_decode of every container, which the parity tests hold to the
+    oracle."""
+    L, S, C, G, Tc = 2, 5000, 128, 10, 100
+    _say("[streamed] multi-chunk items L=%d S=%d C=%d Tc=%d slots=%d" % (L, S, C, Tc, n_slots))
+    X = synth.gen_custom(L, S, C, HEAVY, device="cuda")
+    ta = cg.build_cdf(X, G, Tc, (16, 8), H_kv=2, n_sink=30, outlier_ppm=2000)
+    tb = cg.build_cdf(X, G, Tc, (8, 4), H_kv=2, n_sink=30)
+    tc = cg.build_cdf(X, G, Tc, (8, 4), H_kv=2, anchor_bits=8)
+    n = -(-S // Tc)
+    bounds, k = [], 0
+    for step in (3, 1, 2, 3, 3, 1, 2, 3, 3, 2, 2):
+        bounds.append((k, k + step))
+        k += step
+    bounds.append((k, n))
+    tabs = [(tb, ta, tc)[i % 3] for i in range(len(bounds))]
+    blobs = [cg.encode(t, X, a, b) for t, (a, b) in zip(tabs, bounds)]
+    hosts = [torch.empty(b.nbytes, dtype=torch.uint8, pin_memory=True) for b in blobs]
+    for b, h in zip(blobs, hosts):
+        b.read_into(h)
+    slot = (max(b.nbytes for b in blobs) + 255) // 256 * 256
+    staging = torch.empty(n_slots * slot, dtype=torch.uint8, device="cuda")
+    got = torch.full_like(X, float("nan"))
+    cs, ds = torch.cuda.Stream(), torch.cuda.Stream()
+    stats = cg.stream_decode(list(zip(tabs, blobs, hosts)), staging, n_slots, got, cs, ds,
+                             wait=True)
+    torch.cuda.synchronize()
+    ref = torch.full_like(X, float("nan"))
+    for t, b in zip(tabs, blobs):
+        cg.decode(t, b, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    assert stats["copied_bytes"] == sum(b.nbytes for b in blobs)
+    assert stats["decode_ms"] > 0
