@@ -280,13 +280,15 @@ def streamed_report(dev, n_slots: int = 32, reps: int = 3, seed: int = 0) -> dic
         "%.1f GB/s, overlap %.2f), ratio %.3f"
         % (res["end_to_end_GBps"], res["h2d_GBps"], res["decode_only_GBps"], res["overlap"],
            res["compression_ratio"]))
+    sizes = prep.sizes
     del prep, pipe
-    res["controller"] = controller_report(w, X, out, n_slots, seed, res["network_s_trace"])
+    res["controller"] = controller_report(w, X, out, n_slots, sizes,
+                                          streamed.bandwidth_trace(w.n_chunks, seed),
+                                          "uniform 1-25 Gbit/s per chunk")
     # a link whose rate drifts: the estimator has something to follow
-    from kv_cache_compression_cg_amd import streamed as _st
-    ctrace = _st.correlated_trace(w.n_chunks, seed)
-    res["controller_correlated"] = controller_report(w, X, out, n_slots, seed, None,
-                                                     trace=ctrace)
+    res["controller_correlated"] = controller_report(
+        w, X, out, n_slots, sizes, streamed.correlated_trace(w.n_chunks, seed),
+        "log-rate AR(1), lag-one correlation 0.97, clipped to 1-25 Gbit/s")
     del out, X
     torch.cuda.empty_cache()
     return res
@@ -295,60 +297,52 @@ def streamed_report(dev, n_slots: int = 32, reps: int = 3, seed: int = 0) -> dic
 CONTROLLER_PREFILL_TOK_S = 4000.0  # modelled recompute rate of the text fallback
 
 
-def controller_report(w, X, out, n_slots: int, seed: int, slo_s, trace=None) -> dict:
-    """The closed-loop controller choosing the levels: the rate is estimated from the
-    chunks already sent, and the SLO is the fetch time of the open-loop choice (which
-    knows every chunk's rate in advance).
-    - uniform trace (trace=None): the controller as configured for it, with the text
-      fallback at a modelled 4000 tokens/s;
-    - a given (correlated) trace: the SLO is the open-loop choice's fetch time on that
-      trace, and the controller is the cautious one (a quarter of the slack spent, the
-      remaining chunks planned at the lower of the estimate and the last rate, newest
-      rate weighted 0.8).
-    The chosen containers are streamed and decoded once; text chunks are not."""
+def controller_report(w, X, out, n_slots: int, sizes, bw, kind: str) -> dict:
+    """The closed-loop controller choosing the levels over one bandwidth trace.  The SLO
+    is the time the reference level (level 1 for every chunk) takes over the trace; the
+    open-loop rule's time (which knows every chunk's rate in advance) is given beside it.
+    The controller estimates the link from the chunks already sent (an average of the time
+    per bit, newest chunk weighted 0.8), plans the remaining chunks at the lower of that
+    estimate and the last rate, spends a quarter of its slack, and falls back to text
+    where recomputing (at a modelled 4000 tokens/s) is predicted to be faster than the
+    coarsest container of a late chunk.  The chosen containers are streamed and decoded
+    once; text chunks are not.  `sizes`: container bytes [levels][chunks]."""
     import numpy as np
     import torch
 
     from kv_cache_compression_cg_amd import streamed
-    tokens = [min(w.chunk, w.S - k * w.chunk) for k in range(w.n_chunks)]
-    if trace is None:
-        ctl = streamed.ControllerConfig(slo_s=slo_s, prior_gbps=13.0,
-                                        prefill_tok_per_s=CONTROLLER_PREFILL_TOK_S)
-        bw = streamed.bandwidth_trace(w.n_chunks, seed)
-        kind = "uniform 1-25 Gbit/s per chunk"
-    else:
-        bw = np.asarray(trace, dtype=np.float64)
-        ctl = streamed.ControllerConfig(slo_s=0.0, prior_gbps=13.0, alpha=0.8, slack_share=0.25,
-                                        cautious=True, prefill_tok_per_s=CONTROLLER_PREFILL_TOK_S)
-        kind = "log-rate AR(1), lag-one correlation 0.97, clipped to 1-25 Gbit/s"
-    # the open-loop choice over this trace sets the SLO when none is given
-    prep = streamed.prepare(X, w.group, w.chunk, w.levels, H_kv=w.H_kv, seed=seed, trace=bw,
-                            controller=None if slo_s is None else ctl)
-    if slo_s is None:
-        slo_s = streamed.network_seconds(prep.sizes, prep.levels, bw)
-        ctl.slo_s = slo_s
-        del prep
-        prep = streamed.prepare(X, w.group, w.chunk, w.levels, H_kv=w.H_kv, seed=seed, trace=bw,
-                                controller=ctl)
+    n = w.n_chunks
+    tokens = [min(w.chunk, w.S - k * w.chunk) for k in range(n)]
+    ref = np.full(n, streamed.REFERENCE_LEVEL)
+    slo_s = streamed.network_seconds(sizes, ref, bw)
+    open_loop_s = streamed.network_seconds(sizes, streamed.choose_levels(sizes, bw), bw)
+    ctl = streamed.ControllerConfig(slo_s=slo_s, prior_gbps=13.0, alpha=0.8, slack_share=0.25,
+                                    cautious=True, harmonic=True,
+                                    prefill_tok_per_s=CONTROLLER_PREFILL_TOK_S)
+    prep = streamed.prepare(X, w.group, w.chunk, w.levels, H_kv=w.H_kv, trace=bw,
+                            controller=ctl, sizes=sizes)
     levels, est, fetch_s = streamed.control_levels(prep.sizes, bw, tokens, ctl)
     stats = streamed.run(prep, out, n_slots=n_slots)
     torch.cuda.synchronize()
     lv, cnt = np.unique(levels, return_counts=True)
     names = {streamed.TEXT: "text"}
-    res = {"trace": kind, "slo_s": round(slo_s, 4),
+    ref_bytes = int(np.asarray(sizes)[streamed.REFERENCE_LEVEL].sum())
+    res = {"trace": kind, "slo": "reference level (1) for every chunk over the trace",
+           "slo_s": round(slo_s, 4), "open_loop_fetch_s": round(open_loop_s, 4),
            "prefill_tok_per_s_model": CONTROLLER_PREFILL_TOK_S,
            "alpha": ctl.alpha, "prior_gbps": ctl.prior_gbps, "slack_share": ctl.slack_share,
-           "cautious": ctl.cautious,
+           "cautious": ctl.cautious, "harmonic": ctl.harmonic,
            "chunks_per_level": {names.get(int(a), str(int(a))): int(b) for a, b in zip(lv, cnt)},
            "fetch_s_trace": round(fetch_s, 4), "slo_met": bool(fetch_s <= slo_s),
            "rate_estimate_median_rel_error": round(float(np.median(np.abs(est[1:] - bw[1:])
                                                                      / bw[1:])), 4),
-           "streamed_bytes": prep.streamed_bytes,
+           "streamed_bytes": prep.streamed_bytes, "reference_level_bytes": ref_bytes,
            "total_ms": round(stats["total_ms"], 3), "decode_ms": round(stats["decode_ms"], 3)}
-    log("[controller] %s: levels %s, fetch %.2f s over the trace (SLO %.2f s), estimate off by "
-        "%.0f%% (median), streamed %.2f GB" % (kind, res["chunks_per_level"], fetch_s, slo_s,
-                                             100 * res["rate_estimate_median_rel_error"],
-                                             prep.streamed_bytes / 1e9))
+    log("[controller] %s: levels %s, fetch %.2f s over the trace (SLO %.2f s, open loop %.2f s), "
+        "estimate off by %.0f%% (median), streamed %.2f GB (reference level %.2f GB)"
+        % (kind, res["chunks_per_level"], fetch_s, slo_s, open_loop_s,
+           100 * res["rate_estimate_median_rel_error"], prep.streamed_bytes / 1e9,
+           ref_bytes / 1e9))
     del prep
     return res
 

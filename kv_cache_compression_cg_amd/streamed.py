@@ -86,7 +86,7 @@ class ControllerConfig:
     model to recompute when the bandwidth is too low (gptget summary of arXiv 2310.07240,
     Methodology and abstract; phantomic12 notes).  They give no estimator or rule; the
     ones here: the rate is estimated from the chunks already sent (an exponentially
-    weighted mean, `alpha` on the newest).  The time left in the SLO first covers every
+    weighted mean of the rate, or with `harmonic` of its inverse, `alpha` on the newest).  The time left in the SLO first covers every
     remaining chunk at its coarsest level (at the estimate); what is left over, the
     slack, is shared equally, so chunk k may spend its coarsest time plus slack / (chunks
     left) and takes the finest level predicted to fit.  With a right estimate a feasible
@@ -104,6 +104,10 @@ class ControllerConfig:
     # rate that has just fallen is then planned for before the estimate has caught up)
     slack_share: float = 1.0
     cautious: bool = False
+    # average the time per bit (1 / rate) instead of the rate: a chunk's transfer time is
+    # proportional to 1 / rate, and where the rate varies from chunk to chunk the mean of
+    # 1 / rate exceeds 1 / (mean rate), so an average of the rate under-predicts times
+    harmonic: bool = False
 
 
 def control_levels(sizes: np.ndarray, bw_gbps: np.ndarray, chunk_tokens: Sequence[int],
@@ -137,7 +141,10 @@ def control_levels(sizes: np.ndarray, bw_gbps: np.ndarray, chunk_tokens: Sequenc
         sent = text_bytes if choice == TEXT else sizes[choice, k]
         elapsed += sent * 8.0 / (bw[k] * 1e9) + (recompute if choice == TEXT else 0.0)
         # the transfer just made measures the link rate of this chunk
-        est = cfg.alpha * bw[k] + (1.0 - cfg.alpha) * est
+        if cfg.harmonic:
+            est = 1.0 / (cfg.alpha / bw[k] + (1.0 - cfg.alpha) / est)
+        else:
+            est = cfg.alpha * bw[k] + (1.0 - cfg.alpha) * est
         last = bw[k]
         levels[k] = choice
     return levels, estimates, elapsed
@@ -172,19 +179,26 @@ class Prepared:
 def prepare(kv: torch.Tensor, group: int, chunk: int, level_bins: Sequence[Sequence[int]],
             H_kv: int, seed: int = 0, force_levels: Optional[Sequence[int]] = None,
             controller: Optional[ControllerConfig] = None,
-            trace: Optional[np.ndarray] = None) -> Prepared:
+            trace: Optional[np.ndarray] = None,
+            sizes: Optional[np.ndarray] = None) -> Prepared:
     """Builds the tables of every level, encodes every chunk at every level, picks one
     level per chunk and keeps that container in pinned host memory.  A chunk at level
     TEXT (recomputed from text) is not kept.  With `controller`, the levels come from
     control_levels over the trace: the container sizes of every chunk at every level are
-    taken first (a sender has them: the containers are encoded ahead of time).  `trace`:
-    the per-chunk link rates (default: the uniform trace of `seed`)."""
+    taken first (a sender has them: the containers are encoded ahead of time), or from
+    `sizes` ([levels][chunks] bytes of an earlier prepare of the same cache and levels).
+    `trace`: the per-chunk link rates (default: the uniform trace of `seed`)."""
     tables = [cg.build_cdf(kv, group, chunk, bins, H_kv=H_kv) for bins in level_bins]
     n = tables[0].n_chunks
     bw = bandwidth_trace(n, seed) if trace is None else np.asarray(trace, dtype=np.float64)
     if controller is not None:
-        all_sizes = np.array([[cg.encode(t, kv, k, k + 1).nbytes for k in range(n)]
-                              for t in tables], dtype=np.int64)
+        if sizes is not None:
+            all_sizes = np.asarray(sizes, dtype=np.int64)
+            if all_sizes.shape != (len(tables), n):
+                raise ValueError("sizes: one row per level, one column per chunk expected")
+        else:
+            all_sizes = np.array([[cg.encode(t, kv, k, k + 1).nbytes for k in range(n)]
+                                  for t in tables], dtype=np.int64)
         tokens = [min(chunk, kv.shape[2] - k * chunk) for k in range(n)]
         force_levels = list(control_levels(all_sizes, bw, tokens, controller)[0])
     sizes = np.zeros((len(tables), n), dtype=np.int64)
