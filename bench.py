@@ -104,12 +104,15 @@ def host_info() -> dict:
     return info
 
 
-def cpu_baseline(w, X, max_threads: int) -> dict:
+def cpu_baseline(w, X, max_threads: int, gpu_out=None) -> dict:
     """The oracle (as it stands) encoding and decoding a bounded sample of the same
     workload: 16 of the 80 layers (every fifth, the bin tiers in the workload's 2:2:4
     ratio), all chunks, K and V.  Encode = tables (range, quantize, histogram,
     frequencies) + coding of every chunk; decode = every chunk back to fp16.  Layers and
-    chunk ranges are spread over a thread pool of the host CPUs this GPU's share allows."""
+    chunk ranges are spread over a thread pool of the host CPUs this GPU's share allows.
+    With gpu_out (the GPU's decode of the whole cache), the sampled layers of both decodes
+    must be equal bit for bit (a layer's tables and decoded values do not depend on the
+    other layers)."""
     import numpy as np
     import torch
 
@@ -141,9 +144,13 @@ def cpu_baseline(w, X, max_threads: int) -> dict:
         list(ex.map(lambda ie: O.decode(shapes[ie[0][0]], tabs[ie[0][0]], ie[1],
                                         out=outs[ie[0][0]]), zip(items, encs)))
         t_dec = time.perf_counter() - t0
+    tt = np.arange(w.S)
+    anchor = ((tt % w.chunk) % w.group) == 0
     for l in layers:
-        assert np.array_equal(outs[l][:, :, ::w.group][:, :, :w.chunk // w.group],
-                              host[l][:, :, ::w.group][:, :, :w.chunk // w.group])
+        assert np.array_equal(outs[l][:, :, anchor], host[l][:, :, anchor])
+        if gpu_out is not None:
+            g = gpu_out[l:l + 1].cpu().view(torch.int16).numpy().view(np.uint16)
+            assert np.array_equal(outs[l], g), "oracle and GPU decodes differ on layer %d" % l
     raw = len(layers) * 2 * w.C * w.S * 2
     log("[cpu] oracle on %d threads: tables %.2fs, encode %.2fs, decode %.2fs (%.2f GB raw)"
         % (cores, t_tab, t_enc, t_dec, raw / 1e9))
@@ -154,7 +161,8 @@ def cpu_baseline(w, X, max_threads: int) -> dict:
            "decode_GBps": round(raw / t_dec / 1e9, 4),
            "encode_GBps": round(raw / (t_tab + t_enc) / 1e9, 4),
            "encode_s": {"tables": round(t_tab, 3), "coding": round(t_enc, 3)},
-           "decode_s": round(t_dec, 3), "sample_raw_bytes": raw}
+           "decode_s": round(t_dec, 3), "sample_raw_bytes": raw,
+           "equals_gpu_decode": gpu_out is not None}
     res.update(hinfo)
     return res
 
@@ -180,6 +188,41 @@ def copy_bandwidth(dev, reps: int = 5, nbytes: int = 4 << 30) -> dict:
     gbps = 2 * nbytes / (ms[len(ms) // 2] * 1e-3) / 1e9
     return {"bytes": nbytes, "reps": reps, "median_ms": round(ms[len(ms) // 2], 4),
             "GBps_read_plus_write": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
+
+
+def access_form_bandwidth(dev, reps: int = 5, nbytes: int = 4 << 30) -> dict:
+    """HBM rate of the decoder's own access forms alone, 4 GiB each (libcg_calib.so,
+    grid-stride kernels of 2048 x 256 threads), timed with HIP events: 2-byte
+    non-temporal stores, 128 contiguous bytes per wavefront (the output rows), and 4- and
+    2-byte non-temporal loads (payload words, anchor rows).  The store rate bounds how fast
+    the decoder can write its rows however little it computes."""
+    import ctypes
+
+    import torch
+
+    from kv_cache_compression_cg_amd import build as _b
+    calib = ctypes.CDLL(_b.CALIB_LIB)
+    calib.cg_calib_run.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_uint64,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(2048, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    res = {"bytes": nbytes, "reps": reps}
+    for kind, name in ((2, "write2_nt"), (0, "read4_nt"), (1, "read2_nt")):
+        assert calib.cg_calib_run(kind, buf.data_ptr(), nbytes, sink.data_ptr(), sp) == 0
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            assert calib.cg_calib_run(kind, buf.data_ptr(), nbytes, sink.data_ptr(), sp) == 0
+            e1.record(stream)
+        torch.cuda.synchronize(dev)
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+        res[name + "_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return res
 
 
 def entropy_report(w, X, tab, blob) -> dict:
@@ -650,6 +693,10 @@ def main() -> int:
 
     copy = copy_bandwidth(dev)
     log("[bench] device copy of 4 GiB: %.1f GB/s read + write" % copy["GBps_read_plus_write"])
+    forms = access_form_bandwidth(dev)
+    forms["rows_of_the_decode_ms_at_write2_nt"] = round(w.raw_bytes / forms["write2_nt_GBps"]
+                                                        / 1e6, 4)
+    log("[bench] decoder access forms alone: %s" % json.dumps(forms))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -739,6 +786,7 @@ def main() -> int:
                          "before the first and after the last call (host work between "
                          "kernels included); wall: host clock around both calls",
         "copy": copy,
+        "access_forms": forms,
         "roofline": roofline,
     }
     res["encode_GBps"] = round(w.raw_bytes / (res["encode_ms"] * 1e-3) / 1e9, 2)
@@ -757,7 +805,9 @@ def main() -> int:
         res["sinks"] = sinks_report(w, X, out, args.decode_reps)
         res["anchors8"] = anchors8_report(w, X, out, args.decode_reps)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, X, args.cpu_threads)
+        cg.decode(tab, blob, out)   # the main container again (the objects above reused `out`)
+        torch.cuda.synchronize()
+        res["cpu_baseline"] = cpu_baseline(w, X, args.cpu_threads, gpu_out=out)
     if not args.no_streamed:
         del X, out, tab, blob, last
         torch.cuda.empty_cache()
