@@ -630,18 +630,21 @@ struct Coder {
     bool zero_w;            // the grid is the single point lo
     bool present;           // this lane has a channel
     uint64_t pmask;         // lanes with a channel
+    uint64_t zmask;         // lanes whose grid is the single point lo
     uint32_t lane, x, E, flushed, n_off;
 
     // q = clamp(floor(fma(delta - lo, r, 0.5)), 0, N - 1) without branches (v is finite,
     // so the median of (v, 0, N - 1) gives quantize1's result); off: the clamp changed v,
-    // or a zero-width grid misses delta.  `coded`: the token is from n_sink on.
+    // or a zero-width grid misses delta.  `coded`: the token is from n_sink on.  The
+    // off-grid lanes come straight from the compares' lane masks (a ballot of a combined
+    // bool would first be materialised as 0 / 1 and compared again).
     __device__ __forceinline__ uint32_t symbol(float dl, bool coded)
     {
         const float v = floorf(fmaf(dl - lo, r, 0.5f));
         const float vc = __builtin_amdgcn_fmed3f(v, 0.0f, nm1);
-        const bool off = (v != vc) | (zero_w & (dl != lo));
-        const uint64_t om = __builtin_amdgcn_ballot_w64(off) & pmask;
-        n_off += coded ? (uint32_t)__builtin_popcountll(om) : 0u;
+        uint64_t om = __builtin_amdgcn_fcmpf(v, vc, 14 /* unordered or not equal */);
+        if (zmask) om |= zmask & __builtin_amdgcn_fcmpf(dl, lo, 14);   // (rare: uniform test)
+        n_off += coded ? (uint32_t)__builtin_popcountll(om & pmask) : 0u;
         return (uint32_t)vc;
     }
 
@@ -649,18 +652,25 @@ struct Coder {
 
     // One coding step with the table entry of the symbol; the shifted-out word (if any)
     // goes to the ring at its distance from the end, other lanes write their parking slot.
+    // The ring index is computed for every lane and then selected (kept opaque so that the
+    // select is not turned into a branch around the lane-count arithmetic).
     __device__ __forceinline__ void step(const EncEntry &en)
     {
+        const uint64_t mask = __builtin_amdgcn_uicmp(x, en.f24, 35 /* unsigned >= */) & pmask;
+        E += (uint32_t)__builtin_popcountll(mask);
+        // distance from the end D = E - rank; the ring is indexed by -D
+        uint32_t at = (mbcnt64(mask) - E) & (kWordRing - 1);
+        asm volatile("" : "+v"(at));
         const bool mine = (x >= en.f24) & present;
-        const uint64_t mask = __builtin_amdgcn_ballot_w64(mine);
-        const uint32_t cnt = (uint32_t)__builtin_popcountll(mask);
-        const uint32_t D = E + cnt - mbcnt64(mask);
-        const uint32_t slot = mine ? ((0u - D) & (kWordRing - 1)) : kWordRing + lane;
-        ring[slot] = (uint16_t)x;
+        ring[mine ? at : kWordRing + lane] = (uint16_t)x;
         x = mine ? x >> 16 : x;
-        E += cnt;
         const uint32_t qq = (uint32_t)((double)x * en.rcp);
-        x = __umul24(qq, en.pk) + x + (en.pk >> 24);
+        // x + q (256 - f) in one 24-bit multiply-add, then + cdf taken as byte 3 of pk
+        const uint32_t t = __umul24(qq, en.pk) + x;
+        asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
+            "src1_sel:BYTE_3"
+            : "=v"(x)
+            : "v"(t), "v"(en.pk));
     }
 
     // writes out whole 256-word blocks of placed words (distances flushed + 1 ..): region
@@ -739,6 +749,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void k5_code(const uint16_t *__rest
     cd.af = 0.0f;
     cd.present = present;
     cd.pmask = __builtin_amdgcn_ballot_w64(present);
+    cd.zmask = __builtin_amdgcn_ballot_w64(cd.zero_w);
     cd.lane = lane;
     cd.x = kStateLow;
     cd.E = cd.flushed = cd.n_off = 0;
