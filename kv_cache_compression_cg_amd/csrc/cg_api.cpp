@@ -425,7 +425,9 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     Carve cv;
     const uint64_t o_lo = cv.take(rows * 4), o_hi = cv.take(rows * 4), o_h = cv.take(rows * 4);
     const uint64_t o_cnt = cv.take(rows * kMaxBins * 4), o_flag = cv.take(4);
-    const uint64_t o_fine = t->outlier_ppm ? cv.take(rows * kFineBins * 4) : 0;
+    const uint64_t o_fine = t->outlier_ppm
+                                ? cv.take((uint64_t)fine_parts(make_geom(t, 0, 1)) * rows * kFineBins * 2)
+                                : 0;
     std::lock_guard<std::mutex> lock(g_arena_mu);
     uint8_t *sc = nullptr;
     uint64_t *hw = nullptr;
@@ -433,7 +435,7 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     uint32_t *ordlo = reinterpret_cast<uint32_t *>(sc + o_lo), *ordhi = reinterpret_cast<uint32_t *>(sc + o_hi);
     float *hi = reinterpret_cast<float *>(sc + o_h);
     uint32_t *counts = reinterpret_cast<uint32_t *>(sc + o_cnt), *flag = reinterpret_cast<uint32_t *>(sc + o_flag);
-    uint32_t *fine = reinterpret_cast<uint32_t *>(sc + o_fine);
+    uint16_t *fine = reinterpret_cast<uint16_t *>(sc + o_fine);
     CG_HIP(hipMemsetAsync(ordlo, 0xFF, rows * 4, st), "memset");
     CG_HIP(hipMemsetAsync(ordhi, 0x00, rows * 4, st), "memset");
     CG_HIP(hipMemsetAsync(counts, 0, rows * kMaxBins * 4, st), "memset");
@@ -446,7 +448,6 @@ int cg_build_cdf(const cg_params *params, const void *kv_dev, void *hip_stream, 
     CG_HIP(launch_k0(X, g, pick_tpt(t, t->S), ordlo, ordhi, flag, st), "k0_minmax");
     CG_HIP(launch_k0_finalize(g, ordlo, ordhi, t->d_lo, hi, st), "k0_finalize");
     if (t->outlier_ppm) {
-        CG_HIP(hipMemsetAsync(fine, 0, rows * kFineBins * 4, st), "memset");
         CG_HIP(launch_fine_hist(X, g, t->d_lo, hi, fine, st), "k_fine_hist");
         CG_HIP(launch_clip(g, fine, t->outlier_ppm, t->d_lo, hi, st), "k_clip");
     }

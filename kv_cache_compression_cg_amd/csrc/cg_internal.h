@@ -87,9 +87,11 @@ hipError_t launch_k0_finalize(const Geom &g, const uint32_t *ord_lo, const uint3
                               float *lo, float *hi, hipStream_t st);
 // outlier table: counts of the deltas in the 256 fine intervals over [lo, hi] of every
 // channel row, then the central range (lo, hi narrowed in place)
+// (partial: fine_parts(g) x [rows][C][256] uint16 counts, every entry written)
+uint32_t fine_parts(const Geom &g);
 hipError_t launch_fine_hist(const uint16_t *X, const Geom &g, const float *lo, const float *hi,
-                            uint32_t *fine_counts, hipStream_t st);
-hipError_t launch_clip(const Geom &g, const uint32_t *fine_counts, uint32_t ppm, float *lo,
+                            uint16_t *partial, hipStream_t st);
+hipError_t launch_clip(const Geom &g, const uint16_t *partial, uint32_t ppm, float *lo,
                        float *hi, hipStream_t st);
 // w = (hi - lo) / (N - 1), r = 1 / w (0 when w = 0)
 hipError_t launch_width(const Geom &g, const uint8_t *bins, const float *lo, const float *hi,

@@ -28,6 +28,31 @@ __device__ __forceinline__ void ntstore8(void *p, uint2 v)
 }
 
 
+// Calls body(row, walk) for the token rows [w.t, t_end) of one thread (16 bytes each at
+// base + t * C), with the loads of the next A rows in flight: the row loop of the
+// histogram passes would otherwise wait for one load at a time.  Loads past t_end read
+// the last row again (in bounds, unused).
+template <int A, class F>
+__device__ __forceinline__ void rows_ahead(const Geom &g, const uint16_t *base, TokenWalk &w,
+                                           uint32_t t_end, F body)
+{
+    if (w.t >= t_end) return;
+    uint4 buf[A];
+#pragma unroll
+    for (int u = 0; u < A; ++u) buf[u] = ntload16(base + (uint64_t)min(w.t + u, t_end - 1) * g.C);
+    while (w.t < t_end) {
+#pragma unroll
+        for (int u = 0; u < A; ++u) {
+            if (w.t < t_end) {
+                const uint4 v = buf[u];
+                buf[u] = ntload16(base + (uint64_t)min(w.t + A, t_end - 1) * g.C);
+                body(v, w);
+                w.next(g);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------------------ K0
 // Per-channel min / max of the anchor deltas, and the non-finite flag.
 // Thread = (row, token block, 8 channels); 16-byte loads, one row of C channels is
@@ -141,105 +166,184 @@ __device__ __forceinline__ uint32_t fine_index(float dl, float lo, float wf, flo
     return j;
 }
 
-// Counts of the coded deltas in the fine intervals, [rows][C][256].  Block = (row, tile
-// of 8 * OCT channels, token block), as in k1_hist, with an LDS histogram [256][8][OCT].
-__global__ __launch_bounds__(256) void k_fine_hist(const uint16_t *__restrict__ X, Geom g,
-                                                    const float *__restrict__ lo,
-                                                    const float *__restrict__ hi, uint32_t OCT,
-                                                    uint32_t SUB, uint32_t tpt, uint32_t ntiles,
-                                                    uint32_t ntb, uint32_t *__restrict__ counts)
+// Counts of the coded deltas in the fine intervals.  Block = 8 wavefronts over one
+// (row, 64-channel block b, token part p); lane = channel; each wavefront takes an eighth
+// of the part's tokens with 2-byte loads of its channel, kFineAhead rows in flight.  The
+// LDS histogram holds two 16-bit counters per word, word (bin / 2, lane) at
+// (bin / 2) * 65 + lane: one column per lane, so no two lanes of a wavefront update the
+// same word, and a padding column puts a lane's word in bank (bin / 2 + lane) mod 64.
+// 33 KiB per block lets 4 blocks (32 wavefronts) share a CU, enough 128-byte loads in
+// flight to stream the cache.  A part holds at most 65535 tokens, so no counter
+// overflows.  The block writes its counts to partial[p][row][c][256] (uint16, every bin);
+// k_clip sums the parts.
+constexpr uint32_t kFineCols = kLanes + 1;
+constexpr uint32_t kFineWaves = 8;
+constexpr int kFineAhead = 8;
+
+template <bool A8>
+__global__ __launch_bounds__(kFineWaves * 64) void k_fine_hist(const uint16_t *__restrict__ X, Geom g,
+                                                                const float *__restrict__ lo,
+                                                                const float *__restrict__ hi,
+                                                                uint32_t parts,
+                                                                uint16_t *__restrict__ partial)
 {
-    extern __shared__ uint32_t hist[];
-    const uint32_t tbb = blockIdx.x % ntb;
-    const uint32_t tmp = blockIdx.x / ntb;
-    const uint32_t ct = tmp % ntiles;
-    const uint32_t row = tmp / ntiles;
-    const uint32_t nh = kFineBins * 8 * OCT;
-    for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) hist[j] = 0;
+    __shared__ uint32_t hist[kFineBins / 2 * kFineCols];
+    const uint32_t p = blockIdx.x % parts;
+    const uint32_t tmp = blockIdx.x / parts;
+    const uint32_t b = tmp % g.NB;
+    const uint32_t row = tmp / g.NB;
+    for (uint32_t j = threadIdx.x; j < kFineBins / 2 * kFineCols; j += blockDim.x) hist[j] = 0;
     __syncthreads();
 
-    const uint32_t O = g.C / 8;
-    const uint32_t ol = threadIdx.x % OCT, sub = threadIdx.x / OCT;
-    const uint32_t o = ct * OCT + ol;
-    const uint32_t t_begin = (tbb * SUB + sub) * tpt;
-    if (sub < SUB && o < O && t_begin < g.S) {
-        const uint32_t t_end = min(g.S, t_begin + tpt);
-        const uint16_t *base = X + (uint64_t)row * g.S * g.C + o * 8;
-        const uint64_t r0 = (uint64_t)row * g.C + o * 8;
-        float lo8[8], wf8[8], rf8[8], af[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            lo8[j] = lo[r0 + j];
-            wf8[j] = (hi[r0 + j] - lo8[j]) / (float)kFineBins;
-            rf8[j] = wf8[j] > 0.0f ? 1.0f / wf8[j] : 0.0f;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const uint32_t lane = threadIdx.x % kLanes;
+    const uint32_t c = b * kLanes + lane;
+    const bool present = c < g.C;
+    const uint32_t per_part = (g.S + parts - 1) / parts;
+    const uint32_t p0 = min(g.S, p * per_part), p1 = min(g.S, p0 + per_part);
+    const uint32_t per_wave = (p1 - p0 + kFineWaves - 1) / kFineWaves;
+    const uint32_t t_begin = min(p1, p0 + wave * per_wave), t_end = min(p1, t_begin + per_wave);
+    const uint64_t ri = (uint64_t)row * g.C + (present ? c : 0u);
+    if (t_begin < t_end) {
+        const float l0 = lo[ri];
+        const float wf = (hi[ri] - l0) / (float)kFineBins;
+        const float rf = wf > 0.0f ? 1.0f / wf : 0.0f;
+        // lanes without a channel or with a zero-width row count nothing (and take no
+        // step in fine_index: a delta of -inf stays at interval 0)
+        const bool counts = present && wf > 0.0f;
+        float alo = 0.0f, aw = 0.0f, ar = 0.0f;
+        if constexpr (A8) {
+            alo = g.alo[ri];
+            aw = g.aw[ri];
+            ar = g.ar[ri];
         }
-        TokenWalk w;
-        w.init(g, t_begin);
-        if (w.gp != 0) {
-            uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
-            unpack8(a, af);
-            snap8(g, r0, af);
+        const uint16_t *col = X + (uint64_t)row * g.S * g.C + (present ? c : 0u);
+        auto load = [&](uint32_t t) __attribute__((always_inline)) {
+            return __builtin_nontemporal_load(col + (uint64_t)t * g.C);
+        };
+        // position of token t: u in its chunk, gp in its group (wave-uniform), advanced
+        // with selects rather than branches
+        uint32_t t = t_begin, u = t_begin % g.Tc, gp = u % g.G;
+        float af = 0.0f;
+        if (gp != 0) {
+            const float x = h2f(load(t_begin - gp));
+            af = A8 ? anchor_snap(x, alo, aw, ar) : x;
         }
-        for (; w.t < t_end; w.next(g)) {
-            uint4 v = ntload16(base + (uint64_t)w.t * g.C);
-            float xf[8];
-            unpack8(v, xf);
-            if (w.gp == 0) {
+        uint16_t buf[kFineAhead];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) af[j] = xf[j];
-                snap8(g, r0, af);
-            } else if (w.t >= g.n_sink) {
+        for (int k = 0; k < kFineAhead; ++k) buf[k] = load(min(t_begin + k, t_end - 1));
+        // A batch of kFineAhead rows (all below t_end when `full`): the fine interval of
+        // each delta from the estimate floor((delta - lo) / wf), which is exact when
+        // p_e <= delta < p_(e+1) (at the ends: e = 0 or e = 255); otherwise, rarely, the
+        // batch takes the stepping search.  Lanes that count nothing carry -inf.
+        auto batch = [&](bool full) __attribute__((always_inline)) {
+            float dl[kFineAhead];
+            bool cnt[kFineAhead];
+            uint32_t q[kFineAhead];
+            uint64_t bad = 0;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    if (!(wf8[j] > 0.0f)) continue;  // nothing to narrow
-                    const uint32_t q = fine_index(xf[j] - af[j], lo8[j], wf8[j], rf8[j]);
-                    atomicAdd(&hist[(q * 8 + j) * OCT + ol], 1u);
+            for (int k = 0; k < kFineAhead; ++k) {
+                const bool in = full || t < t_end;
+                const uint16_t v = buf[k];
+                if (full) buf[k] = load(min(t + kFineAhead, t_end - 1));
+                const float x = h2f(v);
+                const bool anc = in && gp == 0;
+                if constexpr (A8) {
+                    if (anc) af = anchor_snap(x, alo, aw, ar);
+                } else {
+                    af = anc ? x : af;
+                }
+                cnt[k] = counts & in & !anc & (t >= g.n_sink);   // (no short circuit: no branch)
+                float d = x - af;
+                asm volatile("" : "+v"(d));
+                dl[k] = cnt[k] ? d : -__builtin_inff();
+                const float e = fminf(fmaxf(floorf((dl[k] - l0) * rf), 0.0f), (float)(kFineBins - 1u));
+                const float p_e = fmaf(e, wf, l0), p_n = fmaf(e + 1.0f, wf, l0);
+                const bool ok = ((e == 0.0f) | (p_e <= dl[k])) &
+                                ((e == (float)(kFineBins - 1u)) | (p_n > dl[k]));
+                bad |= __builtin_amdgcn_ballot_w64(!ok);
+                q[k] = (uint32_t)e;
+                if (in) {
+                    ++t;
+                    const bool wrap = ++u == g.Tc;
+                    u = wrap ? 0u : u;
+                    gp = (wrap || gp + 1u == g.G) ? 0u : gp + 1u;
                 }
             }
-        }
+            if (bad) {
+#pragma unroll
+                for (int k = 0; k < kFineAhead; ++k) q[k] = fine_index(dl[k], l0, wf, rf);
+            }
+#pragma unroll
+            for (int k = 0; k < kFineAhead; ++k)
+                atomicAdd(&hist[(q[k] >> 1) * kFineCols + lane], cnt[k] ? 1u << ((q[k] & 1u) * 16u) : 0u);
+        };
+        for (uint32_t n = (t_end - t_begin) / kFineAhead; n > 0; --n) batch(true);
+        if (t < t_end) batch(false);
     }
     __syncthreads();
-    for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) {
-        const uint32_t v = hist[j];
-        if (!v) continue;
-        const uint32_t s = j / (8 * OCT), rem = j - s * 8 * OCT;
-        const uint32_t jj = rem / OCT, oo = ct * OCT + rem % OCT;
-        if (oo >= O) continue;
-        atomicAdd(&counts[((uint64_t)row * g.C + oo * 8 + jj) * kFineBins + s], v);
-    }
+    // thread -> (one of two channels, bin): consecutive threads write consecutive bins
+    const uint32_t nl = min(kLanes, g.C - b * kLanes);
+    uint16_t *dst = partial + (((uint64_t)p * g.L * 2 + row) * g.C + b * kLanes) * kFineBins;
+    const uint32_t bin = threadIdx.x % kFineBins;
+    for (uint32_t ch = threadIdx.x / kFineBins; ch < nl; ch += blockDim.x / kFineBins)
+        dst[(uint64_t)ch * kFineBins + bin] =
+            (uint16_t)(hist[(bin >> 1) * kFineCols + ch] >> ((bin & 1u) * 16u));
 }
 
 // The central range of one channel row: with n coded deltas and the budget
 // b = floor(n * ppm / 10^6), whole fine intervals are dropped from the bottom while the
 // dropped count stays <= b, and from the top likewise; lo' = p_{j_lo},
 // hi' = p_{j_hi + 1} (hi when j_hi = 255), at most hi.  lo and hi are narrowed in place.
-__global__ __launch_bounds__(256) void k_clip(Geom g, const uint32_t *__restrict__ counts,
-                                               uint32_t ppm, float *__restrict__ lo,
-                                               float *__restrict__ hi)
+// One wavefront per row element, lane i holding bins 4i .. 4i + 3 summed over the parts:
+// with pre(j) = the count below interval j (non-decreasing in j), j_lo is the number of
+// j in [1, 255] with pre(j) <= b, and 255 - j_hi the number with n - pre(j) <= b.
+__global__ __launch_bounds__(256) void k_clip(Geom g, const uint16_t *__restrict__ partial,
+                                               uint32_t parts, uint32_t ppm,
+                                               float *__restrict__ lo, float *__restrict__ hi)
 {
-    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= g.L * 2 * g.C) return;
+    const uint64_t rows = (uint64_t)g.L * 2 * g.C;
+    const uint64_t i = (uint64_t)blockIdx.x * (blockDim.x / kLanes) + threadIdx.x / kLanes;
+    const uint32_t lane = threadIdx.x % kLanes;
+    if (i >= rows) return;
     const float l0 = lo[i], h0 = hi[i];
     const float wf = (h0 - l0) / (float)kFineBins;
     if (!(wf > 0.0f) || ppm == 0) return;
-    const uint32_t *cnt = counts + (uint64_t)i * kFineBins;
-    uint64_t n = 0;
-    for (uint32_t j = 0; j < kFineBins; ++j) n += cnt[j];
+    uint32_t cnt[4] = {0u, 0u, 0u, 0u};
+    for (uint32_t p = 0; p < parts; ++p) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(partial + ((uint64_t)p * rows + i) * kFineBins + 4 * lane);
+        cnt[0] += v.x & 0xFFFFu;
+        cnt[1] += v.x >> 16;
+        cnt[2] += v.y & 0xFFFFu;
+        cnt[3] += v.y >> 16;
+    }
+    const uint32_t mine = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    // inclusive scan of the lane sums
+    uint32_t incl = mine;
+#pragma unroll
+    for (uint32_t d = 1; d < kLanes; d <<= 1) {
+        const uint32_t y = __shfl_up(incl, d, kLanes);
+        if (lane >= d) incl += y;
+    }
+    const uint32_t n = __shfl(incl, kLanes - 1, kLanes);
     if (n == 0) return;
-    const uint64_t budget = (n * ppm) / 1000000u;
-    uint32_t j_lo = 0, j_hi = kFineBins - 1u;
-    uint64_t below = 0;
-    for (uint32_t j = 1; j < kFineBins; ++j) {
-        below += cnt[j - 1];
-        if (below > budget) break;
-        j_lo = j;
+    const uint64_t budget = ((uint64_t)n * ppm) / 1000000u;
+    uint32_t pre = incl - mine, n_lo = 0, n_hi = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) {
+        if (4 * lane + k >= 1) {
+            n_lo += pre <= budget ? 1u : 0u;
+            n_hi += (uint64_t)(n - pre) <= budget ? 1u : 0u;
+        }
+        pre += cnt[k];
     }
-    uint64_t above = 0;
-    for (uint32_t j = kFineBins - 1u; j > 0; --j) {
-        above += cnt[j];
-        if (above > budget) break;
-        j_hi = j - 1u;
+#pragma unroll
+    for (uint32_t d = kLanes / 2; d >= 1; d >>= 1) {
+        n_lo += __shfl_xor(n_lo, d, kLanes);
+        n_hi += __shfl_xor(n_hi, d, kLanes);
     }
+    if (lane != 0) return;
+    const uint32_t j_lo = n_lo, j_hi = kFineBins - 1u - n_hi;
     const float lo_c = fmaf((float)j_lo, wf, l0);
     float hi_c = (j_hi == kFineBins - 1u) ? h0 : fmaf((float)(j_hi + 1u), wf, l0);
     if (hi_c > h0) hi_c = h0;
@@ -291,8 +395,7 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
             unpack8(a, af);
             snap8(g, (uint64_t)row * g.C + o * 8, af);
         }
-        for (; w.t < t_end; w.next(g)) {
-            uint4 v = ntload16(base + (uint64_t)w.t * g.C);
+        rows_ahead<4>(g, base, w, t_end, [&](uint4 v, const TokenWalk &w) {
             float xf[8];
             unpack8(v, xf);
             if (w.gp == 0) {
@@ -306,7 +409,7 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
                     atomicAdd(&hist[(q * 8 + j) * OCT + ol], 1u);
                 }
             }
-        }
+        });
     }
     __syncthreads();
     for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) {
@@ -976,29 +1079,33 @@ hipError_t launch_width(const Geom &g, const uint8_t *bins, const float *lo, con
     return hipGetLastError();
 }
 
-hipError_t launch_fine_hist(const uint16_t *X, const Geom &g, const float *lo, const float *hi,
-                            uint32_t *fine_counts, hipStream_t st)
+uint32_t fine_parts(const Geom &g)
 {
-    const uint32_t O = g.C / 8;
-    const uint32_t OCT = O < 4 ? O : 4;           // LDS: 256 bins x 8 x OCT counters
-    const uint32_t SUB = 256 / OCT;
-    const uint32_t ntiles = (O + OCT - 1) / OCT;
-    const uint64_t rows = (uint64_t)g.L * 2;
-    uint64_t ntb_target = (8192 + rows * ntiles - 1) / (rows * ntiles);
-    uint64_t tpt = (g.S + ntb_target * SUB - 1) / (ntb_target * SUB);
-    if (tpt < 16) tpt = 16;
-    uint32_t ntb = (uint32_t)((g.S + tpt * SUB - 1) / (tpt * SUB));
-    size_t lds = (size_t)kFineBins * 8 * OCT * sizeof(uint32_t);
-    hipLaunchKernelGGL(k_fine_hist, dim3((uint32_t)(rows * ntiles * ntb)), dim3(256), lds, st, X,
-                       g, lo, hi, OCT, SUB, (uint32_t)tpt, ntiles, ntb, fine_counts);
+    // token parts per (row, channel block): at most 65535 tokens each (16-bit counters),
+    // and up to 4 of about 16K tokens for enough blocks
+    return std::max((g.S + 65534u) / 65535u, std::min(4u, (g.S + 16383u) / 16384u));
+}
+
+hipError_t launch_fine_hist(const uint16_t *X, const Geom &g, const float *lo, const float *hi,
+                            uint16_t *partial, hipStream_t st)
+{
+    const uint32_t parts = fine_parts(g);
+    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * parts;
+    if (g.alo)
+        hipLaunchKernelGGL(k_fine_hist<true>, dim3((uint32_t)blocks), dim3(kFineWaves * 64), 0, st, X,
+                           g, lo, hi, parts, partial);
+    else
+        hipLaunchKernelGGL(k_fine_hist<false>, dim3((uint32_t)blocks), dim3(kFineWaves * 64), 0, st, X,
+                           g, lo, hi, parts, partial);
     return hipGetLastError();
 }
 
-hipError_t launch_clip(const Geom &g, const uint32_t *fine_counts, uint32_t ppm, float *lo,
+hipError_t launch_clip(const Geom &g, const uint16_t *partial, uint32_t ppm, float *lo,
                        float *hi, hipStream_t st)
 {
-    uint32_t n = g.L * 2 * g.C;
-    hipLaunchKernelGGL(k_clip, dim3((n + 255) / 256), dim3(256), 0, st, g, fine_counts, ppm, lo, hi);
+    const uint64_t n = (uint64_t)g.L * 2 * g.C;
+    hipLaunchKernelGGL(k_clip, dim3((uint32_t)((n + 3) / 4)), dim3(256), 0, st, g, partial,
+                       fine_parts(g), ppm, lo, hi);
     return hipGetLastError();
 }
 
