@@ -581,8 +581,15 @@ __global__ __launch_bounds__(256) void k2_delta_quant(const uint16_t *__restrict
 // 8-bit anchors the anchor's own code against the anchor grid).  Counting pass: the
 // group's number of entries.  Writing pass: entry e of the group at offs[gidx] + e,
 // key (token within the chunk) << 6 | lane, value the element's fp16 bits; a token's
-// entries are placed in lane order by a ballot.
-template <bool WRITE>
+// entries are placed in lane order by a ballot.  Rows are loaded kOutAhead ahead and
+// tested without branches (the quantizer's clamp changed floor(fma(delta - lo, r, 0.5)),
+// or a zero-width grid misses delta); only a row with an entry takes the writing branch.
+constexpr int kOutAhead = 8;
+template <bool B> struct BoolTag {
+    static constexpr bool value = B;
+};
+
+template <bool WRITE, bool A8>
 __global__ __launch_bounds__(256) void k_outliers(const uint16_t *__restrict__ X, Geom g,
                                                    const uint8_t *__restrict__ bins,
                                                    const float *__restrict__ lo,
@@ -603,39 +610,107 @@ __global__ __launch_bounds__(256) void k_outliers(const uint16_t *__restrict__ X
     const uint32_t c = b * kLanes + lane;
     const bool present = c < g.C;
     const uint32_t t0 = k * g.Tc, len = chunk_len(g, k);
-    const uint32_t N = bins[row];
+    const float nm1 = (float)(bins[row] - 1u);
     const uint64_t ri = (uint64_t)row * g.C + (present ? c : 0u);
     const float lo1 = lo[ri], r1 = r[ri];
     float alo = 0.0f, aw = 0.0f, ar = 0.0f;
-    if (g.alo) {
+    if constexpr (A8) {
         alo = g.alo[ri];
         aw = g.aw[ri];
         ar = g.ar[ri];
     }
-    const uint16_t *col = X + (uint64_t)row * g.S * g.C + (present ? c : 0u);
+    // the row parameters are waited for here: a wait at their first use inside the row
+    // loop would also drain the rows loaded ahead, every iteration
+    asm volatile("" ::"v"(lo1), "v"(r1), "v"(alo), "v"(aw), "v"(ar));
+    const uint64_t pmask = __builtin_amdgcn_ballot_w64(present);
+    const uint64_t zmask = __builtin_amdgcn_ballot_w64(r1 == 0.0f);   // zero-width grids
+    const uint64_t azmask = __builtin_amdgcn_ballot_w64(ar == 0.0f);  // (8-bit anchors)
+    // Each lane loads the aligned 4 bytes holding its channel (channel pairs share them)
+    // and shifts its half down: 16-bit values would be packed or masked at the end of
+    // every batch, which waits for the rows loaded ahead.  The rows come through a
+    // buffer resource over the chunk: the row offset advances in a scalar register and
+    // rows past the chunk read 0.
+    const __amdgpu_buffer_rsrc_t xs =
+        make_rsrc(X + ((uint64_t)row * g.S + t0) * g.C, (uint32_t)((uint64_t)len * g.C * 2));
+    const uint32_t voff = 2 * ((present ? c : 0u) & ~1u);
+    const uint32_t rstride = 2 * g.C;
+    const uint32_t half = 16u * (lane & 1u);
+    auto load = [&](uint32_t soff) __attribute__((always_inline)) {
+        return __builtin_amdgcn_raw_buffer_load_b32(xs, voff, soff, kNT16);
+    };
+    // lanes off the grid l + q / rr (q in [0, n]) for x
+    auto off_mask = [&](float x, float l, float rr, float n, uint64_t zm) __attribute__((always_inline)) {
+        const float v = floorf(fmaf(x - l, rr, 0.5f));
+        const float vc = __builtin_amdgcn_fmed3f(v, 0.0f, n);
+        return __builtin_amdgcn_fcmpf(v, vc, 14 /* unordered or not equal */) |
+               (zm & __builtin_amdgcn_fcmpf(x, l, 14));
+    };
+    // rows from u_sink on are coded (the sinks before it are not)
+    const uint32_t u_sink = g.n_sink > t0 ? min(g.n_sink - t0, len) : 0u;
     uint64_t run = WRITE ? offs[gidx] : 0;
     float af = 0.0f;
-    uint32_t gp = 0;
-    for (uint32_t u = 0; u < len; ++u, gp = (gp + 1 == g.G) ? 0u : gp + 1) {
-        const uint32_t t = t0 + u;
-        const uint32_t x = col[(uint64_t)t * g.C];
-        const float xf = h2f(x);
-        bool off;
-        if (gp == 0) {
-            off = g.alo && t >= g.n_sink && off_grid(xf, alo, ar, 256u);
-            af = g.alo ? anchor_snap(xf, alo, aw, ar) : xf;
-        } else {
-            off = t >= g.n_sink && off_grid(xf - af, lo1, r1, N);
+    uint32_t u = 0, gp = 0, soff = 0;
+    uint32_t buf[kOutAhead];
+#pragma unroll
+    for (int j = 0; j < kOutAhead; ++j) buf[j] = load(j * rstride);
+    // a batch of kOutAhead rows (all inside the chunk when FULL); ZW: some lane's grid has
+    // zero width
+    auto batch = [&](auto full_tag, auto zw_tag) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_tag)::value, ZW = decltype(zw_tag)::value;
+        uint64_t m[kOutAhead];
+        uint32_t x[kOutAhead];
+        uint32_t uu[kOutAhead];
+        uint64_t any = 0;
+#pragma unroll
+        for (int j = 0; j < kOutAhead; ++j) {
+            const bool in = FULL || u < len;
+            x[j] = buf[j] >> half;
+            if (FULL) buf[j] = load(soff + kOutAhead * rstride);
+            const float xf = h2f(x[j] & 0xFFFFu);
+            const bool anc = gp == 0;
+            uint64_t ma = 0;   // an anchor: off its own grid (8-bit anchors only)
+            if constexpr (A8) {
+                ma = off_mask(xf, alo, ar, 255.0f, azmask);
+                if (anc) af = anchor_snap(xf, alo, aw, ar);
+            } else {
+                af = anc ? xf : af;
+            }
+            float d = xf - af;
+            asm volatile("" : "+v"(d));
+            const float v = floorf(fmaf(d - lo1, r1, 0.5f));
+            const float vc = __builtin_amdgcn_fmed3f(v, 0.0f, nm1);
+            uint64_t mn = __builtin_amdgcn_fcmpf(v, vc, 14 /* unordered or not equal */);
+            if constexpr (ZW) mn |= zmask & __builtin_amdgcn_fcmpf(d, lo1, 14);
+            m[j] = (in & (u >= u_sink)) ? (anc ? ma : mn) & pmask : 0;
+            uu[j] = u;
+            any |= m[j];
+            if (in) {
+                ++u;
+                soff += rstride;
+                gp = gp + 1u == g.G ? 0u : gp + 1u;
+            }
         }
-        off = off && present;
-        const uint64_t mask = __builtin_amdgcn_ballot_w64(off);
-        if (WRITE && off) {
-            const uint64_t e = run + mbcnt64(mask);
-            keys[e] = (u << 6) | lane;
-            vals[e] = (uint16_t)x;
+        // only a batch with an entry moves the group's entry count
+        if (any) {
+#pragma unroll
+            for (int j = 0; j < kOutAhead; ++j) {
+                if (WRITE && ((m[j] >> lane) & 1u)) {
+                    const uint64_t e = run + mbcnt64(m[j]);
+                    keys[e] = (uu[j] << 6) | lane;
+                    vals[e] = (uint16_t)x[j];
+                }
+                run += (uint64_t)__builtin_popcountll(m[j]);
+            }
         }
-        run += (uint64_t)__builtin_popcountll(mask);
-    }
+    };
+    auto rows = [&](auto zw_tag) __attribute__((always_inline)) {
+        for (uint32_t n = len / kOutAhead; n > 0; --n) batch(BoolTag<true>{}, zw_tag);
+        if (u < len) batch(BoolTag<false>{}, zw_tag);
+    };
+    if (zmask)
+        rows(BoolTag<true>{});
+    else
+        rows(BoolTag<false>{});
     if (!WRITE && lane == 0) counts[gidx] = run;
 }
 
@@ -1162,12 +1237,18 @@ hipError_t launch_outliers(const uint16_t *X, const Geom &g, const uint8_t *bins
 {
     const uint64_t n_groups = (uint64_t)(g.ke - g.kb) * g.L * 2 * g.NB;
     const uint32_t blocks = (uint32_t)((n_groups + 3) / 4);
-    if (counts)
-        hipLaunchKernelGGL(k_outliers<false>, dim3(blocks), dim3(256), 0, st, X, g, bins, lo, r,
-                           n_groups, counts, offs, keys, vals);
+    if (counts && g.alo)
+        hipLaunchKernelGGL((k_outliers<false, true>), dim3(blocks), dim3(256), 0, st, X, g, bins, lo,
+                           r, n_groups, counts, offs, keys, vals);
+    else if (counts)
+        hipLaunchKernelGGL((k_outliers<false, false>), dim3(blocks), dim3(256), 0, st, X, g, bins, lo,
+                           r, n_groups, counts, offs, keys, vals);
+    else if (g.alo)
+        hipLaunchKernelGGL((k_outliers<true, true>), dim3(blocks), dim3(256), 0, st, X, g, bins, lo,
+                           r, n_groups, counts, offs, keys, vals);
     else
-        hipLaunchKernelGGL(k_outliers<true>, dim3(blocks), dim3(256), 0, st, X, g, bins, lo, r,
-                           n_groups, counts, offs, keys, vals);
+        hipLaunchKernelGGL((k_outliers<true, false>), dim3(blocks), dim3(256), 0, st, X, g, bins, lo,
+                           r, n_groups, counts, offs, keys, vals);
     return hipGetLastError();
 }
 
