@@ -756,8 +756,8 @@ hipError_t launch_anchor_grid(const uint16_t *X, const Geom &g, float *alo, floa
 }
 
 // ------------------------------------------------------------------------------ K5
-// rANS encoder fused with anchor delta + quantize, one pass over the cache.  Block = 4
-// wavefronts = 4 chunks of one (row, channel block b) sharing the block's coding table in
+// rANS encoder fused with anchor delta + quantize, one pass over the cache.  Block = 8
+// wavefronts = 8 chunks of one (row, channel block b) sharing the block's coding table in
 // LDS; wavefront = group (chunk, row, b), lane i codes the stream of channel 64b + i.
 //
 // The coder runs from a chunk's last symbol to its first, and the lockstep decoders read
