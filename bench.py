@@ -346,7 +346,8 @@ def controller_report(w, X, out, n_slots: int, sizes, bw, kind: str) -> dict:
     open-loop rule's time (which knows every chunk's rate in advance) is given beside it.
     The controller estimates the link from the chunks already sent (an average of the time
     per bit, newest chunk weighted 0.8), plans the remaining chunks at the lower of that
-    estimate and the last rate, spends a quarter of its slack, and falls back to text
+    estimate and the last rate against 95% of the SLO, spends a quarter of its slack, and
+    falls back to text
     where recomputing (at a modelled 4000 tokens/s) is predicted to be faster than the
     coarsest container of a late chunk.  The chosen containers are streamed and decoded
     once; text chunks are not.  `sizes`: container bytes [levels][chunks]."""
@@ -360,7 +361,7 @@ def controller_report(w, X, out, n_slots: int, sizes, bw, kind: str) -> dict:
     slo_s = streamed.network_seconds(sizes, ref, bw)
     open_loop_s = streamed.network_seconds(sizes, streamed.choose_levels(sizes, bw), bw)
     ctl = streamed.ControllerConfig(slo_s=slo_s, prior_gbps=13.0, alpha=0.8, slack_share=0.25,
-                                    cautious=True, harmonic=True,
+                                    cautious=True, harmonic=True, margin=0.05,
                                     prefill_tok_per_s=CONTROLLER_PREFILL_TOK_S)
     prep = streamed.prepare(X, w.group, w.chunk, w.levels, H_kv=w.H_kv, trace=bw,
                             controller=ctl, sizes=sizes)
@@ -374,7 +375,7 @@ def controller_report(w, X, out, n_slots: int, sizes, bw, kind: str) -> dict:
            "slo_s": round(slo_s, 4), "open_loop_fetch_s": round(open_loop_s, 4),
            "prefill_tok_per_s_model": CONTROLLER_PREFILL_TOK_S,
            "alpha": ctl.alpha, "prior_gbps": ctl.prior_gbps, "slack_share": ctl.slack_share,
-           "cautious": ctl.cautious, "harmonic": ctl.harmonic,
+           "cautious": ctl.cautious, "harmonic": ctl.harmonic, "margin": ctl.margin,
            "chunks_per_level": {names.get(int(a), str(int(a))): int(b) for a, b in zip(lv, cnt)},
            "fetch_s_trace": round(fetch_s, 4), "slo_met": bool(fetch_s <= slo_s),
            "rate_estimate_median_rel_error": round(float(np.median(np.abs(est[1:] - bw[1:])

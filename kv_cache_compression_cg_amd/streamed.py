@@ -108,6 +108,9 @@ class ControllerConfig:
     # proportional to 1 / rate, and where the rate varies from chunk to chunk the mean of
     # 1 / rate exceeds 1 / (mean rate), so an average of the rate under-predicts times
     harmonic: bool = False
+    # the share of the SLO held back: the controller plans against (1 - margin) x SLO, a
+    # reserve for the chunks whose rates the estimate misses
+    margin: float = 0.0
 
 
 def control_levels(sizes: np.ndarray, bw_gbps: np.ndarray, chunk_tokens: Sequence[int],
@@ -130,7 +133,8 @@ def control_levels(sizes: np.ndarray, bw_gbps: np.ndarray, chunk_tokens: Sequenc
         estimates[k] = est
         pred = sizes[:, k] * 8.0 / (est * 1e9)
         plan = min(est, last) if cfg.cautious else est
-        slack = cfg.slo_s - elapsed - float(np.sum(sizes[-1, k:])) * 8.0 / (plan * 1e9)
+        slack = (cfg.slo_s * (1.0 - cfg.margin) - elapsed
+                 - float(np.sum(sizes[-1, k:])) * 8.0 / (plan * 1e9))
         allowed = pred[-1] + cfg.slack_share * max(slack, 0.0) / (n - k)
         choice = int(np.nonzero(pred <= allowed)[0][0])   # the coarsest level always fits
         text_bytes = float(chunk_tokens[k]) * cfg.text_bytes_per_token
