@@ -716,31 +716,61 @@ __global__ __launch_bounds__(256) void k_outliers(const uint16_t *__restrict__ X
 
 // 8-bit anchor grid ("Guide to CacheGen", Solution pillar 2: the anchor is quantized with
 // high precision): per (layer, K/V, channel) row, min / max of its anchor tokens over all
-// chunks, width (max - min) / 255, zero bounds as +0.  One thread per row element; a
-// wavefront reads 64 consecutive channels of one anchor token.
-__global__ __launch_bounds__(256) void k_anchor_grid(const uint16_t *__restrict__ X, Geom g,
-                                                      float *__restrict__ alo,
-                                                      float *__restrict__ aw,
-                                                      float *__restrict__ ar)
+// chunks, width (max - min) / 255, zero bounds as +0.  Block = 16 wavefronts over one
+// (row, 64-channel block), lane = channel; wavefront p takes anchors p, p + 16, ... (anchor
+// a is token (a / ngF) Tc + (a % ngF) G: every chunk but the last is full), 8 loads in
+// flight; the 16 partial ranges meet in LDS.
+constexpr uint32_t kGridWaves = 16;
+
+__global__ __launch_bounds__(kGridWaves * 64) void k_anchor_grid(const uint16_t *__restrict__ X, Geom g,
+                                                                  float *__restrict__ alo,
+                                                                  float *__restrict__ aw,
+                                                                  float *__restrict__ ar)
 {
-    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (uint64_t)g.L * 2 * g.C) return;
-    const uint32_t c = (uint32_t)(i % g.C), row = (uint32_t)(i / g.C);
-    const uint16_t *base = X + (uint64_t)row * g.S * g.C + c;
-    float lo = 0.0f, hi = 0.0f;
-    bool any = false;
-    for (uint32_t t0 = 0; t0 < g.S; t0 += g.Tc) {
-        const uint32_t t1 = min(g.S, t0 + g.Tc);
-        for (uint32_t t = t0; t < t1; t += g.G) {
-            const float x = h2f(base[(uint64_t)t * g.C]);
-            if (!any || x < lo) lo = x;
-            if (!any || x > hi) hi = x;
-            any = true;
+    __shared__ float plo[kGridWaves][kLanes], phi[kGridWaves][kLanes];
+    const uint32_t b = blockIdx.x % g.NB, row = blockIdx.x / g.NB;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
+    const uint32_t lane = threadIdx.x % kLanes;
+    const uint32_t c = b * kLanes + lane;
+    const bool present = c < g.C;
+    const uint16_t *base = X + (uint64_t)row * g.S * g.C + (present ? c : 0u);
+    const uint32_t nk = (g.S + g.Tc - 1) / g.Tc;
+    const uint32_t n_anchor = (nk - 1) * g.ngF + (g.S - (nk - 1) * g.Tc + g.G - 1) / g.G;
+    auto token = [&](uint32_t a) __attribute__((always_inline)) {
+        return (a / g.ngF) * g.Tc + (a % g.ngF) * g.G;
+    };
+    float lo = __builtin_inff(), hi = -__builtin_inff();
+    constexpr uint32_t A = 8;
+    uint32_t a = wave;
+    for (; a + (A - 1) * kGridWaves < n_anchor; a += A * kGridWaves) {
+        uint16_t v[A];
+#pragma unroll
+        for (uint32_t j = 0; j < A; ++j) v[j] = base[(uint64_t)token(a + j * kGridWaves) * g.C];
+#pragma unroll
+        for (uint32_t j = 0; j < A; ++j) {
+            const float x = h2f(v[j]);
+            lo = x < lo ? x : lo;
+            hi = x > hi ? x : hi;
         }
+    }
+    for (; a < n_anchor; a += kGridWaves) {
+        const float x = h2f(base[(uint64_t)token(a) * g.C]);
+        lo = x < lo ? x : lo;
+        hi = x > hi ? x : hi;
+    }
+    plo[wave][lane] = lo;
+    phi[wave][lane] = hi;
+    __syncthreads();
+    if (wave != 0 || !present) return;
+#pragma unroll
+    for (uint32_t p = 1; p < kGridWaves; ++p) {
+        lo = plo[p][lane] < lo ? plo[p][lane] : lo;
+        hi = phi[p][lane] > hi ? phi[p][lane] : hi;
     }
     lo = lo + 0.0f;
     hi = hi + 0.0f;
     const float w = (hi - lo) / 255.0f;
+    const uint64_t i = (uint64_t)row * g.C + c;
     alo[i] = lo;
     aw[i] = w;
     ar[i] = (w > 0.0f) ? 1.0f / w : 0.0f;
@@ -749,8 +779,8 @@ __global__ __launch_bounds__(256) void k_anchor_grid(const uint16_t *__restrict_
 hipError_t launch_anchor_grid(const uint16_t *X, const Geom &g, float *alo, float *aw, float *ar,
                               hipStream_t st)
 {
-    const uint64_t n = (uint64_t)g.L * 2 * g.C;
-    hipLaunchKernelGGL(k_anchor_grid, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, X, g,
+    const uint64_t blocks = (uint64_t)g.L * 2 * g.NB;
+    hipLaunchKernelGGL(k_anchor_grid, dim3((uint32_t)blocks), dim3(kGridWaves * 64), 0, st, X, g,
                        alo, aw, ar);
     return hipGetLastError();
 }
