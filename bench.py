@@ -289,7 +289,9 @@ def streamed_report(dev, n_slots: int = 32, reps: int = 3, seed: int = 0) -> dic
     log("[streamed] %s: %d chunks encoded at %d levels, chosen containers in pinned memory "
         "(%.1fs)" % (w.name, w.n_chunks, len(w.levels), time.time() - t))
     out = torch.empty_like(X)
-    pipe = streamed.Pipeline(prep, dev, n_slots)
+    # one pipeline (staging slots and streams) for every run below: slots fit any chunk's
+    # container at any level
+    pipe = streamed.Pipeline(prep, dev, n_slots, slot_bytes=int(prep.sizes.max()))
     runs = [streamed.run(prep, out, n_slots=n_slots, pipe=pipe) for _ in range(reps + 1)][1:]
     tt = torch.arange(w.S, device=dev)
     anchor = ((tt % w.chunk) % w.group) == 0
@@ -324,14 +326,15 @@ def streamed_report(dev, n_slots: int = 32, reps: int = 3, seed: int = 0) -> dic
         % (res["end_to_end_GBps"], res["h2d_GBps"], res["decode_only_GBps"], res["overlap"],
            res["compression_ratio"]))
     sizes = prep.sizes
-    del prep, pipe
+    del prep
     res["controller"] = controller_report(w, X, out, n_slots, sizes,
                                           streamed.bandwidth_trace(w.n_chunks, seed),
-                                          "uniform 1-25 Gbit/s per chunk")
+                                          "uniform 1-25 Gbit/s per chunk", pipe)
     # a link whose rate drifts: the estimator has something to follow
     res["controller_correlated"] = controller_report(
         w, X, out, n_slots, sizes, streamed.correlated_trace(w.n_chunks, seed),
-        "log-rate AR(1), lag-one correlation 0.97, clipped to 1-25 Gbit/s")
+        "log-rate AR(1), lag-one correlation 0.97, clipped to 1-25 Gbit/s", pipe)
+    del pipe
     del out, X
     torch.cuda.empty_cache()
     return res
@@ -340,7 +343,7 @@ def streamed_report(dev, n_slots: int = 32, reps: int = 3, seed: int = 0) -> dic
 CONTROLLER_PREFILL_TOK_S = 4000.0  # modelled recompute rate of the text fallback
 
 
-def controller_report(w, X, out, n_slots: int, sizes, bw, kind: str) -> dict:
+def controller_report(w, X, out, n_slots: int, sizes, bw, kind: str, pipe=None) -> dict:
     """The closed-loop controller choosing the levels over one bandwidth trace.  The SLO
     is the time the reference level (level 1 for every chunk) takes over the trace; the
     open-loop rule's time (which knows every chunk's rate in advance) is given beside it.
@@ -366,7 +369,7 @@ def controller_report(w, X, out, n_slots: int, sizes, bw, kind: str) -> dict:
     prep = streamed.prepare(X, w.group, w.chunk, w.levels, H_kv=w.H_kv, trace=bw,
                             controller=ctl, sizes=sizes)
     levels, est, fetch_s = streamed.control_levels(prep.sizes, bw, tokens, ctl)
-    stats = streamed.run(prep, out, n_slots=n_slots)
+    stats = streamed.run(prep, out, n_slots=n_slots, pipe=pipe)
     torch.cuda.synchronize()
     lv, cnt = np.unique(levels, return_counts=True)
     names = {streamed.TEXT: "text"}

@@ -233,9 +233,12 @@ class Pipeline:
     """Staging slots and the copy / decode streams, made once and reused: a stream's
     first use and a fresh allocation would otherwise fall inside the timed run."""
 
-    def __init__(self, prep: Prepared, device, n_slots: int = 32):
+    def __init__(self, prep: Prepared, device, n_slots: int = 32, slot_bytes: int = 0):
+        """slot_bytes: at least prep's (a larger slot lets later preparations of the same
+        cache at other levels reuse the pipeline)."""
         self.n_slots = n_slots
-        self.staging = torch.empty(n_slots * prep.slot_bytes, dtype=torch.uint8, device=device)
+        slot = max(prep.slot_bytes, (int(slot_bytes) + 255) // 256 * 256)
+        self.staging = torch.empty(n_slots * slot, dtype=torch.uint8, device=device)
         self.copy_stream = torch.cuda.Stream(device=device)
         self.decode_stream = torch.cuda.Stream(device=device)
 
