@@ -489,3 +489,41 @@ def test_imported_blob_must_match_its_tables(cg):
     with pytest.raises(cg.CgError) as e:
         cg.blob_import(t1, cb[:-2000])
     assert e.value.code == -5
+
+
+def _sweep_cases(n=40, seed=2024):
+    """Seeded random shapes and settings for the sweep below (small enough for the oracle
+    to finish each in seconds): ragged chunk and group lengths, partial lane blocks, every
+    bin count from 2 to 32, the format variants in every combination, chunk ranges."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        L = int(rng.integers(1, 4))
+        H = int(rng.choice([1, 2, 3]))
+        d = int(rng.choice([8, 24, 64, 72]))
+        S = int(rng.integers(1, 1400))
+        G = int(rng.integers(1, 17))
+        Tc = int(rng.integers(1, 700))
+        bins = tuple(int(b) for b in rng.integers(2, 33, size=L))
+        bins_v = tuple(int(b) for b in rng.integers(2, 33, size=L)) if rng.random() < 0.3 else None
+        n_sink = int(rng.choice([0, 0, 1, 4, 37]))
+        anchor_bits = int(rng.choice([16, 16, 8]))
+        ppm = int(rng.choice([0, 0, 300, 20000, 250000]))
+        nk = -(-S // Tc)
+        kb = int(rng.integers(0, nk))
+        ke = int(rng.integers(kb + 1, nk + 1))
+        rngc = (kb, ke) if rng.random() < 0.4 else None
+        gen = HEAVY if rng.random() < 0.6 else GAUSS
+        cases.append((i, L, H, d, S, G, Tc, bins, bins_v, n_sink, anchor_bits, ppm, rngc, gen))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: "case%d" % c[0])
+def test_seeded_sweep_of_shapes_and_settings(cg, case):
+    """Every product of the path (tables, stored bytes, symbols, the whole container,
+    fused / unfused / imported decodes) bit for bit against the oracle over seeded random
+    shapes and settings."""
+    i, L, H, d, S, G, Tc, bins, bins_v, n_sink, anchor_bits, ppm, rngc, gen = case
+    X = _gen(L, S, H * d, gen)
+    full_parity(cg, X, H, G, Tc, bins, chunk_range=rngc, label="sweep %d" % i, bins_v=bins_v,
+                n_sink=n_sink, anchor_bits=anchor_bits, outlier_ppm=ppm)
