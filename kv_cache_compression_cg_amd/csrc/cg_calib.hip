@@ -7,7 +7,9 @@
 //   read2_nt:   2-byte non-temporal buffer loads, 128 contiguous bytes per wavefront (its
 //               anchor-row loads);
 //   write2_nt:  2-byte non-temporal buffer stores, 128 contiguous bytes per wavefront (its
-//               output-row stores).
+//               output-row stores);
+//   write4_nt:  4-byte non-temporal buffer stores, 256 contiguous bytes per wavefront (a
+//               wider store form, for comparison).
 // Each kernel walks the buffer in 256-thread blocks, grid-stride.
 #include <hip/hip_runtime.h>
 
@@ -63,9 +65,21 @@ __global__ __launch_bounds__(256) void write2_nt(uint8_t *dst, uint64_t bytes)
     }
 }
 
+__global__ __launch_bounds__(256) void write4_nt(uint8_t *dst, uint64_t bytes)
+{
+    for (uint64_t w0 = 0; w0 < bytes; w0 += kWin) {
+        const uint32_t wb = (uint32_t)(bytes - w0 < kWin ? bytes - w0 : kWin);
+        const __amdgpu_buffer_rsrc_t rs = rsrc(dst + w0, wb);
+        for (uint64_t i = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < wb;
+             i += (uint64_t)gridDim.x * blockDim.x * 4)
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)i, rs, (uint32_t)i, 0, kNT);
+    }
+}
+
 }  // namespace
 
-// kind 0: read4_nt, 1: read2_nt, 2: write2_nt over `bytes` (a multiple of 4) at buf.
+// kind 0: read4_nt, 1: read2_nt, 2: write2_nt, 3: write4_nt (4-byte non-temporal stores,
+// 256 contiguous bytes per wavefront) over `bytes` (a multiple of 4) at buf.
 // sink: 4 * 2048 bytes of device memory.  Returns a hipError_t.
 extern "C" int cg_calib_run(int kind, void *buf, uint64_t bytes, void *sink, void *stream)
 {
@@ -77,6 +91,8 @@ extern "C" int cg_calib_run(int kind, void *buf, uint64_t bytes, void *sink, voi
         hipLaunchKernelGGL(read2_nt, grid, block, 0, st, (const uint8_t *)buf, bytes, (uint32_t *)sink);
     else if (kind == 2)
         hipLaunchKernelGGL(write2_nt, grid, block, 0, st, (uint8_t *)buf, bytes);
+    else if (kind == 3)
+        hipLaunchKernelGGL(write4_nt, grid, block, 0, st, (uint8_t *)buf, bytes);
     else
         return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
