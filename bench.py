@@ -766,7 +766,7 @@ def main() -> int:
         "config": {"workload": w.name, "L": w.L, "H_kv": w.H_kv, "d": w.d, "S": w.S,
                    "group": w.group, "chunk": w.chunk,
                    "bins": "32 (layers 0-19) / 16 (20-39) / 8 (40-79)",
-                   "raw_bytes": w.raw_bytes, "parallelism": "single GPU"},
+                   "raw_bytes": w.raw_bytes, "seed": w.gen.seed, "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "compression_ratio": round(w.raw_bytes / comp, 4),
         "compressed_bytes": {"total": comp, "payload": 2 * h["payload_words"],

@@ -527,3 +527,30 @@ def test_seeded_sweep_of_shapes_and_settings(cg, case):
     X = _gen(L, S, H * d, gen)
     full_parity(cg, X, H, G, Tc, bins, chunk_range=rngc, label="sweep %d" % i, bins_v=bins_v,
                 n_sink=n_sink, anchor_bits=anchor_bits, outlier_ppm=ppm)
+
+
+def test_stored_form_through_files_and_repeat_runs_are_identical(cg, tmp_path):
+    """A cache kept as files (the stored tables and the container written out, read back
+    by a fresh import) decodes to what the encoder's own handles decode; and every run of
+    the path gives the same bytes: two table builds, two encodes, two decodes (the
+    histogram and range passes use atomics; their results do not depend on order)."""
+    L, S, C, G, Tc, H, bins = 3, 1500, 192, 10, 400, 3, (32, 16, 8)
+    X = _gen(L, S, C, HEAVY)
+    for kw in ({}, {"n_sink": 4, "outlier_ppm": 2000}, {"anchor_bits": 8}):
+        tabs = [cg.build_cdf(X, G, Tc, bins, H_kv=H, **kw) for _ in range(2)]
+        tbs = [t.serialize() for t in tabs]
+        assert tbs[0] == tbs[1], kw
+        blobs = [cg.encode(tabs[0], X), cg.encode(tabs[1], X)]
+        cbs = [b.read().tobytes() for b in blobs]
+        assert cbs[0] == cbs[1], kw
+        outs = [cg.decode(tabs[0], blobs[0]), cg.decode(tabs[0], blobs[0])]
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), kw
+        ft, fc = tmp_path / "tables.bin", tmp_path / "container.bin"
+        ft.write_bytes(tbs[0])
+        fc.write_bytes(cbs[0])
+        tab_f = cg.tables_import(np.fromfile(ft, dtype=np.uint8).tobytes())
+        blob_f = cg.blob_import(tab_f, np.fromfile(fc, dtype=np.uint8).tobytes())
+        out_f = cg.decode(tab_f, blob_f)
+        torch.cuda.synchronize()
+        assert torch.equal(out_f.view(torch.int16), outs[0].view(torch.int16)), kw
