@@ -222,7 +222,7 @@ int cg_decode(const cg_tables *tables, const cg_blob *blob, const void *containe
  *                    one pool of num_pages pages per (layer, K/V).
  *   block_table_dev: int32 [ceil(S / page_tokens)], device: token t of every (layer, K/V)
  *                    goes to page block_table[t / page_tokens], row t % page_tokens.
- *   page_tokens:     a power of two; num_pages * page_tokens * H_kv * d * 2 < 2^32.
+ *   page_tokens:     a power of two; (num_pages + 1) * page_tokens * H_kv * d * 2 <= 2^32.
  * Writes the tokens of the blob's chunks (sink rows and outlier entries as in
  * cg_decode); a block whose page id is negative or >= num_pages is skipped (none of its
  * rows is written), other pages are untouched.

@@ -733,7 +733,8 @@ int cg_decode_paged(const cg_tables *t, const cg_blob *b, const void *container_
     if (!page_tokens || (page_tokens & (page_tokens - 1)))
         return fail(CG_E_INVAL, "page_tokens must be a power of two");
     if (!num_pages) return fail(CG_E_INVAL, "no pages");
-    if ((uint64_t)num_pages * page_tokens * t->C * 2 >= (1ull << 32))
+    // (the decoder sends the rows of a skipped block to the page after the pool)
+    if ((uint64_t)(num_pages + 1ull) * page_tokens * t->C * 2 > (1ull << 32))
         return fail(CG_E_INVAL, "page pool too large for 32-bit offsets");
     DeviceScope ds;
     CG_HIP(ds.enter(t->device), "hipSetDevice");

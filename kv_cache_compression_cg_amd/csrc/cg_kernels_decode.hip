@@ -176,6 +176,27 @@ __device__ __forceinline__ void flush_rows(const __amdgpu_buffer_rsrc_t &ors, ui
     }
 }
 
+// The page pool of one (row, channel block) of a paged output, shared by the streams of
+// a wavefront: pool is the row's pool from channel b * 64 on; page p starts p << lp token
+// rows into it.  (Every decoded token is below S, so its block is below the table's
+// ceil(S / 2^lp) entries.)
+struct PageMap {
+    __amdgpu_buffer_rsrc_t pool;
+    const int32_t *bt;
+    uint32_t lp, num_pages;
+};
+
+// The page map of (row, b) for a paged decode (an unused one otherwise).
+template <bool PAGED>
+__device__ __forceinline__ PageMap page_map(const Geom &g, const Paged &pg, uint32_t row, uint32_t b)
+{
+    if constexpr (!PAGED) return PageMap{make_rsrc(nullptr, 0u), nullptr, 0u, 0u};
+    const uint64_t elems = ((uint64_t)pg.num_pages << pg.lp) * g.C;
+    return PageMap{make_rsrc(pg.pages + (uint64_t)row * elems + b * kLanes,
+                             (uint32_t)(2 * elems - 2 * (uint64_t)b * kLanes)),
+                   pg.bt, pg.lp, pg.num_pages};
+}
+
 // One decoder stream: chunk k of (row, channel block b), one channel per lane, with its
 // anchor rows, output rows and payload words.  Vector memory is only touched at anchor
 // boundaries: at a group's start the next anchor row and the next chunk of words are
@@ -198,46 +219,38 @@ struct Stream {
     bool fetch;
     float yf[kUnrolledSteps];
     uint32_t ys[kUnrolledSteps];
-    // paged output only (ors is then the row's page pool): the block whose page is
-    // cached, that page's byte offset in the pool and the resource its rows are stored
-    // through (a zero-size one for an invalid page id)
-    uint32_t pblk, poff;
-    const int32_t *bt;
-    uint32_t lp, n_blocks, num_pages;
-    __amdgpu_buffer_rsrc_t prs;
+    // paged output only: the block whose page is current, and the lane's byte offset of
+    // that page in the pool (for an invalid page id, the pool's end)
+    uint32_t pblk, pvo;
 
     static constexpr uint32_t kNoBlock = 0xFFFFFFFFu;
 
-    // Byte offset of token t in the row's page pool, and the resource to store it
-    // through.  A page id that is not a page of the pool selects a resource of zero size
-    // and address: the store is still issued (so every row store of a group stays
-    // unconditional) and the buffer range check discards it.
-    __device__ __forceinline__ uint32_t page_row(uint32_t t)
+    // Byte offset of token t in its page, after making pvo that page's offset.  A page id
+    // that is not a page of the pool selects the pool's end: the store is still issued
+    // (so every row store of a group stays unconditional) and the buffer range check
+    // discards it.  (The pool and one page more fit 32 bits, so no offset wraps.)
+    __device__ __forceinline__ uint32_t page_row(const PageMap &pm, uint32_t t)
     {
-        const uint32_t blk = t >> lp;
+        const uint32_t blk = t >> pm.lp;
         if (blk != pblk) {
             pblk = blk;
             // a scalar load (the table is read-only and the same for the whole wavefront),
             // waited for in the same block
-            uint32_t pg = kNoBlock;
-            if (blk < n_blocks) {
-                const int32_t *p = bt + blk;
-                asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)"
-                             : "=s"(pg) : "s"(p) : "memory");
-            }
-            const bool ok = pg < num_pages;
-            poff = ok ? (pg << lp) * ostride : 0u;
-            prs = ok ? ors : make_rsrc(nullptr, 0u);
+            uint32_t pg;
+            const int32_t *p = pm.bt + blk;
+            asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                         : "=s"(pg) : "s"(p) : "memory");
+            pvo = olane + ((pg < pm.num_pages ? pg : pm.num_pages) << pm.lp) * ostride;
         }
-        return poff + (t & ((1u << lp) - 1u)) * ostride;
+        return (t & ((1u << pm.lp) - 1u)) * ostride;
     }
 
     // stores value v as the row at orow value r (paged: token r)
-    __device__ __forceinline__ void store_row(uint32_t r, uint32_t v)
+    __device__ __forceinline__ void store_row(const PageMap &pm, uint32_t r, uint32_t v)
     {
         if constexpr (PAGED) {
-            const uint32_t o = page_row(r);
-            put_out<SYMBOLS>(prs, olane, o, v);
+            const uint32_t o = page_row(pm, r);
+            put_out<SYMBOLS>(pm.pool, pvo, o, v);
         } else {
             put_out<SYMBOLS>(ors, olane, r, v);
         }
@@ -247,31 +260,31 @@ struct Stream {
     __device__ __forceinline__ uint32_t rstep() const { return PAGED ? 1u : ostride; }
 
     // the rows held for one unrolled group
-    __device__ __forceinline__ void flush()
+    __device__ __forceinline__ void flush(const PageMap &pm)
     {
         if constexpr (!PAGED) {
             flush_rows<SYMBOLS>(ors, olane, orow_held, ostride, yf, ys);
-        } else if ((1u << lp) - (orow_held & ((1u << lp) - 1u)) >= (uint32_t)kUnrolledSteps) {
+        } else if ((1u << pm.lp) - (orow_held & ((1u << pm.lp) - 1u)) >= (uint32_t)kUnrolledSteps) {
             // the group's rows lie in one page: stored as the linear output stores them
-            const uint32_t o = page_row(orow_held);
-            flush_rows<SYMBOLS>(prs, olane, o, ostride, yf, ys);
+            const uint32_t o = page_row(pm, orow_held);
+            flush_rows<SYMBOLS>(pm.pool, pvo, o, ostride, yf, ys);
         } else {
-            flush_paged_rows();
+            flush_paged_rows(pm);
         }
     }
 
     // the held rows one by one, each through its own page
-    __device__ __forceinline__ void flush_paged_rows()
+    __device__ __forceinline__ void flush_paged_rows(const PageMap &pm)
     {
 #pragma unroll
         for (int u = 0; u < kUnrolledSteps; u += 2) {
             if (u + 1 < kUnrolledSteps) {
                 const f32x2 v = {yf[u], yf[u + 1]};
                 const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-                store_row(orow_held + u, h & 0xFFFFu);
-                store_row(orow_held + u + 1, h >> 16);
+                store_row(pm, orow_held + u, h & 0xFFFFu);
+                store_row(pm, orow_held + u + 1, h >> 16);
             } else {
-                store_row(orow_held + u, f2h(yf[u]));
+                store_row(pm, orow_held + u, f2h(yf[u]));
             }
         }
     }
@@ -282,8 +295,7 @@ struct Stream {
                                          const uint8_t *__restrict__ container,
                                          const ContainerView &cv, uint32_t k, uint32_t row,
                                          uint32_t b, uint32_t lane, bool present,
-                                         uint16_t *__restrict__ out, uint8_t *__restrict__ sym_out,
-                                         const Paged &pg)
+                                         uint16_t *__restrict__ out, uint8_t *__restrict__ sym_out)
     {
         const uint32_t nl = min(kLanes, g.C - b * kLanes);
         const uint32_t t0_chunk = k * g.Tc;
@@ -321,17 +333,8 @@ struct Stream {
         ostride = g.C * (SYMBOLS ? 1u : 2u);  // bytes between token rows
         olane = lane * (SYMBOLS ? 1u : 2u);
         if constexpr (PAGED) {
-            // this row's page pool: num_pages pages of 2^lp token rows
-            const uint64_t pool = ((uint64_t)pg.num_pages << pg.lp) * g.C;
-            ors = make_rsrc(pg.pages + (uint64_t)row * pool + b * kLanes,
-                            (uint32_t)(2 * pool - 2 * (uint64_t)b * kLanes));
-            prs = make_rsrc(nullptr, 0u);
-            bt = pg.bt;
-            lp = pg.lp;
-            n_blocks = pg.n_blocks;
-            num_pages = pg.num_pages;
             pblk = kNoBlock;
-            poff = 0;
+            pvo = olane;
         }
 
         dec.x = kStateLow;
@@ -392,22 +395,22 @@ struct Stream {
     }
 
     // write_rows for a stream holding rows with every lane present
-    __device__ __forceinline__ void write_held_rows()
+    __device__ __forceinline__ void write_held_rows(const PageMap &pm)
     {
-        flush();
+        flush(pm);
         held = false;
-        store_row(orow, SYMBOLS ? 0u : a16);
+        store_row(pm, orow, SYMBOLS ? 0u : a16);
         orow += rstep();
     }
 
     // the previous group's outputs, then this group's anchor row
-    __device__ __forceinline__ void write_rows()
+    __device__ __forceinline__ void write_rows(const PageMap &pm)
     {
         if (held) {
-            if (dec.present) flush();
+            if (dec.present) flush(pm);
             held = false;
         }
-        if (dec.present) store_row(orow, SYMBOLS ? 0u : a16);
+        if (dec.present) store_row(pm, orow, SYMBOLS ? 0u : a16);
         orow += rstep();
     }
 
@@ -462,21 +465,22 @@ struct Stream {
     }
 
     // any other group: one store per step
-    __device__ __forceinline__ void generic(const uint8_t *tab, uint32_t lane, uint32_t nsteps)
+    __device__ __forceinline__ void generic(const PageMap &pm, const uint8_t *tab, uint32_t lane,
+                                            uint32_t nsteps)
     {
         for (uint32_t u = nsteps; u != 0; --u) {
             float dq;
             const uint32_t sym = dec.symbol(tab, lane, dq);
             if (dec.present)
-                store_row(orow, SYMBOLS ? sym : f2h(af + dq));
+                store_row(pm, orow, SYMBOLS ? sym : f2h(af + dq));
             orow += rstep();
             if (++dec.i < dec.m) dec.renorm(lane);
         }
     }
 
-    __device__ __forceinline__ void final_flush()
+    __device__ __forceinline__ void final_flush(const PageMap &pm)
     {
-        if (held && dec.present) flush();
+        if (held && dec.present) flush(pm);
     }
 };
 
@@ -553,6 +557,7 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
                                               const ChunkSrcs *srcs = nullptr)
 {
     const bool present = FULL || lane < min(kLanes, g.C - b * kLanes);
+    const PageMap pm = page_map<PAGED>(g, pg, row, b);
     Stream<SYMBOLS, PAGED, A8> st[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -569,10 +574,10 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
             cvk.payload_off = ch.payload_off;
             cvk.payload_words = ch.payload_words;
             st[s].init(gk, ring + s * kRingAlloc, lo, w, ch.c, cvk, ch.k, row, b, lane, present,
-                       out, sym_out, pg);
+                       out, sym_out);
         } else {
             st[s].init(g, ring + s * kRingAlloc, lo, w, container, cv, i, row, b, lane, present,
-                       out, sym_out, pg);
+                       out, sym_out);
         }
     }
 #pragma unroll
@@ -598,7 +603,7 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
 #pragma unroll
             for (int s = 0; s < NS; ++s) st[s].request(gi, lane);
 #pragma unroll
-            for (int s = 0; s < NS; ++s) st[s].write_held_rows();
+            for (int s = 0; s < NS; ++s) st[s].write_held_rows(pm);
             __builtin_amdgcn_sched_barrier(0);
             paired_steps(st, tab, lane);
             __builtin_amdgcn_sched_barrier(0);
@@ -612,7 +617,7 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
             if (act[s]) st[s].request(gi, lane);
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-            if (act[s]) st[s].write_rows();
+            if (act[s]) st[s].write_rows(pm);
         __builtin_amdgcn_sched_barrier(0);
         if (NS == 2 && unr[0] && unr[NS - 1]) {
             paired_steps(st, tab, lane);
@@ -622,7 +627,7 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
                 if (unr[s])
                     st[s].unrolled(tab, lane);
                 else if (act[s])
-                    st[s].generic(tab, lane, nsteps[s]);
+                    st[s].generic(pm, tab, lane, nsteps[s]);
             }
         }
 
@@ -632,7 +637,7 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
             if (act[s]) st[s].consume(lane);
     }
 #pragma unroll
-    for (int s = 0; s < NS; ++s) st[s].final_flush();
+    for (int s = 0; s < NS; ++s) st[s].final_flush(pm);
 }
 
 // Block = WPB wavefronts over the chunks [kb + 2 WPB set, kb + 2 WPB (set + 1)) of one

@@ -305,6 +305,12 @@ def test_paged_output_skips_invalid_page_ids(cg):
     bt12 = torch.zeros(-(-S // 12), dtype=torch.int32, device="cuda")
     with pytest.raises(cg.CgError):        # 12 tokens per page: not a power of two
         cg.decode_paged(tab, blob, pages[:, :, :, :12].contiguous(), bt12)
+    # a pool that fits 32-bit offsets only without the page past its end is refused before
+    # any memory is touched (2^21 pages of 16 rows of 64 channels: 2^32 bytes)
+    lib = cg.load()
+    rc = lib.cg_decode_paged(tab.handle, blob.handle, None, pages.data_ptr(), bt.data_ptr(),
+                             P, 1 << 21, None)
+    assert rc != 0 and b"too large" in lib.cg_last_error()
 
 
 @pytest.mark.parametrize("n_sink,G,Tc,rng", [(4, 10, 300, None), (40, 5, 32, None),
