@@ -304,15 +304,16 @@ ContainerView view_of(const cg_blob *b)
     return v;
 }
 
-// After the decoded rows: the container's sink rows, then its outlier entries.
+// After the decoded rows: the container's sink rows, then its outlier entries (unless the
+// value decode wrote them: values_decode).
 hipError_t put_extras(const cg_tables *t, const cg_blob *b, const uint8_t *cont, uint16_t *out,
-                      const Paged &pg, hipStream_t st)
+                      const Paged &pg, hipStream_t st, bool values_decode = false)
 {
     const Geom g = make_geom(t, b->hdr.chunk_begin, b->hdr.chunk_end);
     const ContainerView cv = view_of(b);
     hipError_t e = launch_sinks(g, reinterpret_cast<const uint16_t *>(cont + cv.sinks_off), cv.n_sink,
                                 b->hdr.chunk_begin * t->Tc, out, pg, st);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || (values_decode && outliers_with_rows(cv))) return e;
     return launch_apply_outliers(g, cont, cv, out, pg, st);
 }
 
@@ -750,7 +751,8 @@ int cg_decode_paged(const cg_tables *t, const cg_blob *b, const void *container_
     CG_HIP(launch_k3_paged(g, t->d_bins, t->d_dtab, t->d_lo, t->d_w, cont, view_of(b), pg,
                            (hipStream_t)hip_stream),
            "k3_decode (paged)");
-    CG_HIP(put_extras(t, b, cont, nullptr, pg, (hipStream_t)hip_stream), "sinks / outliers (paged)");
+    CG_HIP(put_extras(t, b, cont, nullptr, pg, (hipStream_t)hip_stream, true),
+           "sinks / outliers (paged)");
     return CG_OK;
 }
 
@@ -769,7 +771,7 @@ int cg_decode(const cg_tables *t, const cg_blob *b, const void *container_dev, v
     CG_HIP(launch_k3(g, t->d_bins, t->d_dtab, t->d_lo, t->d_w, cont, view_of(b), out, nullptr,
                      (hipStream_t)hip_stream),
            "k3_decode");
-    CG_HIP(put_extras(t, b, cont, out, Paged{}, (hipStream_t)hip_stream), "sinks / outliers");
+    CG_HIP(put_extras(t, b, cont, out, Paged{}, (hipStream_t)hip_stream, true), "sinks / outliers");
     return CG_OK;
 }
 

@@ -54,6 +54,11 @@ struct ContainerView {
 
 constexpr uint32_t kFineBins = 256;               // fine grid of the outlier clip
 
+// The contiguous and paged value decodes (launch_k3 without symbols, launch_k3_paged)
+// write a container's outlier entries themselves, each wavefront those of its chunks;
+// for every other decode launch_apply_outliers writes them afterwards.
+inline bool outliers_with_rows(const ContainerView &cv) { return cv.outliers && cv.n_out > 0; }
+
 // Chunks decoded by one launch from containers of their own (the streamed decode).  The
 // chunks form sets, each of up to 8 chunks that share one set of tables; set j is chunks
 // [set_first[j], set_first[j] + set_n[j]) with tables tab[set_tab[j]].  Chunk i is chunk

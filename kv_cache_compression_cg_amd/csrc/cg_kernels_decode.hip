@@ -197,6 +197,41 @@ __device__ __forceinline__ PageMap page_map(const Geom &g, const Paged &pg, uint
                    pg.bt, pg.lp, pg.num_pages};
 }
 
+// The outlier entries of group gidx = (chunk k, row, channel block b), one per lane, over
+// the decoded rows.  The container is not trusted: offsets are clamped to the entry count
+// and an entry whose token or channel lies outside its group is skipped.
+template <bool PAGED>
+__device__ __forceinline__ void apply_group_outliers(const Geom &g, const uint8_t *container,
+                                                     const ContainerView &cv, uint64_t gidx,
+                                                     uint32_t k, uint32_t row, uint32_t b,
+                                                     uint32_t lane, uint16_t *out, const Paged &pg)
+{
+    const uint64_t *offs = reinterpret_cast<const uint64_t *>(container + cv.out_off);
+    const uint64_t beg = min(offs[gidx], cv.n_out);
+    const uint64_t end = max(beg, min(offs[gidx + 1], cv.n_out));
+    const uint32_t t0 = k * g.Tc, len = chunk_len(g, k);
+    const uint32_t *keys = reinterpret_cast<const uint32_t *>(container + cv.keys_off);
+    const uint16_t *vals = reinterpret_cast<const uint16_t *>(container + cv.vals_off);
+    for (uint64_t e = beg + lane; e < end; e += kLanes) {
+        const uint32_t key = keys[e];
+        const uint32_t u = key >> 6, c = b * kLanes + (key & 63u);
+        if (u >= len || c >= g.C) continue;
+        const uint32_t t = t0 + u;
+        uint16_t *dst;
+        if constexpr (PAGED) {
+            const uint32_t blk = t >> pg.lp;
+            if (blk >= pg.n_blocks) continue;
+            const uint32_t id = (uint32_t)pg.bt[blk];
+            if (id >= pg.num_pages) continue;  // negative ids too
+            const uint64_t pool = ((uint64_t)pg.num_pages << pg.lp) * g.C;
+            dst = pg.pages + row * pool + (((uint64_t)id << pg.lp) + (t & ((1u << pg.lp) - 1u))) * g.C + c;
+        } else {
+            dst = out + ((uint64_t)row * g.S + t) * g.C + c;
+        }
+        *dst = vals[e];
+    }
+}
+
 // One decoder stream: chunk k of (row, channel block b), one channel per lane, with its
 // anchor rows, output rows and payload words.  Vector memory is only touched at anchor
 // boundaries: at a group's start the next anchor row and the next chunk of words are
@@ -544,7 +579,7 @@ __device__ __forceinline__ void paired_steps(Stream<SYMBOLS, PAGED, A8> (&st)[NS
 // the block's LDS table.  With two, the symbol decodes of both streams sit in one
 // basic block, so the dependent LDS reads of one overlap the arithmetic of the other.
 // With MULTI, k0 and k1 index srcs->ch: the chunk and the container it is read from.
-template <bool SYMBOLS, bool FULL, int NS, bool PAGED, bool A8, bool MULTI = false>
+template <bool SYMBOLS, bool FULL, int NS, bool PAGED, bool A8, bool MULTI = false, bool OUTL = false>
 __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__restrict__ tab,
                                               uint16_t *__restrict__ ring,
                                               const float *__restrict__ lo,
@@ -638,6 +673,18 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) st[s].final_flush(pm);
+    if constexpr (OUTL) {
+        // The chunks' outlier entries over their rows.  An entry's element was stored by
+        // another lane of this wavefront: the release fence orders those row stores
+        // before the entries' stores.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint32_t k = s == 0 ? k0 : k1;
+            const uint64_t gidx = ((uint64_t)(k - g.kb) * 2 * g.L + row) * g.NB + b;
+            apply_group_outliers<PAGED>(g, container, cv, gidx, k, row, b, lane, out, pg);
+        }
+    }
 }
 
 // Block = WPB wavefronts over the chunks [kb + 2 WPB set, kb + 2 WPB (set + 1)) of one
@@ -652,7 +699,7 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
 // row: otherwise an XCD would hold only the columns b with one residue mod 8, and its
 // writes and anchor reads would queue on the few L2 / memory channels those addresses
 // map to.
-template <bool SYMBOLS, uint32_t WPB, bool PAGED, bool A8, bool MULTI>
+template <bool SYMBOLS, uint32_t WPB, bool PAGED, bool A8, bool MULTI, bool OUTL = false>
 __device__ __forceinline__ void decode_block(Geom g, const uint8_t *__restrict__ bins,
                                              const uint32_t *__restrict__ dtab,
                                              const float *__restrict__ lo,
@@ -706,18 +753,18 @@ __device__ __forceinline__ void decode_block(Geom g, const uint8_t *__restrict__
     const bool pair = k1 < g.ke;
     if (g.C - b * kLanes >= kLanes) {
         if (pair)
-            decode_chunks<SYMBOLS, true, 2, PAGED, A8, MULTI>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
+            decode_chunks<SYMBOLS, true, 2, PAGED, A8, MULTI, OUTL>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
         else
-            decode_chunks<SYMBOLS, true, 1, PAGED, A8, MULTI>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
+            decode_chunks<SYMBOLS, true, 1, PAGED, A8, MULTI, OUTL>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
     } else {
         if (pair)
-            decode_chunks<SYMBOLS, false, 2, PAGED, A8, MULTI>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
+            decode_chunks<SYMBOLS, false, 2, PAGED, A8, MULTI, OUTL>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
         else
-            decode_chunks<SYMBOLS, false, 1, PAGED, A8, MULTI>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
+            decode_chunks<SYMBOLS, false, 1, PAGED, A8, MULTI, OUTL>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
     }
 }
 
-template <bool SYMBOLS, uint32_t WPB, bool PAGED = false, bool A8 = false>
+template <bool SYMBOLS, uint32_t WPB, bool PAGED = false, bool A8 = false, bool OUTL = false>
 __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__restrict__ bins,
                                                   const uint32_t *__restrict__ dtab,
                                                   const float *__restrict__ lo,
@@ -727,8 +774,8 @@ __global__ __launch_bounds__(WPB * 64) void k3_decode(Geom g, const uint8_t *__r
                                                   uint16_t *__restrict__ out,
                                                   uint8_t *__restrict__ sym_out, Paged pg)
 {
-    decode_block<SYMBOLS, WPB, PAGED, A8, false>(g, bins, dtab, lo, w, container, cv, n_sets, out,
-                                                 sym_out, pg, nullptr);
+    decode_block<SYMBOLS, WPB, PAGED, A8, false, OUTL>(g, bins, dtab, lo, w, container, cv, n_sets,
+                                                       out, sym_out, pg, nullptr);
 }
 
 // The streamed decode's form: chunks from containers of their own, in sets that share
@@ -813,6 +860,28 @@ __global__ __launch_bounds__(256) void k4_dequant(Geom g, const float *__restric
 }
 
 // ------------------------------------------------------------------------------ launchers
+// The value decode (fp16 or 8-bit anchors, contiguous or paged, the outlier entries
+// written by the decoding wavefronts or not).
+template <bool PAGED, bool OUTL>
+void launch_values(const Geom &g, bool wide, dim3 grid, dim3 block, const uint8_t *bins,
+                   const uint32_t *dtab, const float *lo, const float *w, const uint8_t *container,
+                   const ContainerView &cv, uint32_t n_sets, uint16_t *out, const Paged &pg,
+                   hipStream_t st)
+{
+    if (g.alo && wide)
+        hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock, PAGED, true, OUTL>), grid, block, 0, st,
+                           g, bins, dtab, lo, w, container, cv, n_sets, out, nullptr, pg);
+    else if (g.alo)
+        hipLaunchKernelGGL((k3_decode<false, 1, PAGED, true, OUTL>), grid, block, 0, st, g, bins,
+                           dtab, lo, w, container, cv, n_sets, out, nullptr, pg);
+    else if (wide)
+        hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock, PAGED, false, OUTL>), grid, block, 0, st,
+                           g, bins, dtab, lo, w, container, cv, n_sets, out, nullptr, pg);
+    else
+        hipLaunchKernelGGL((k3_decode<false, 1, PAGED, false, OUTL>), grid, block, 0, st, g, bins,
+                           dtab, lo, w, container, cv, n_sets, out, nullptr, pg);
+}
+
 hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, const float *lo,
                      const float *w, const uint8_t *container, const ContainerView &cv,
                      uint16_t *out, uint8_t *sym_out, hipStream_t st)
@@ -835,20 +904,12 @@ hipError_t launch_k3(const Geom &g, const uint8_t *bins, const uint32_t *dtab, c
         else
             hipLaunchKernelGGL((k3_decode<true, 1>), grid, block, 0, st, g, bins, dtab,
                                lo, w, container, cv, n_sets, out, sym_out, none);
-    } else if (g.alo) {
-        if (wide)
-            hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock, false, true>), grid, block, 0, st, g,
-                               bins, dtab, lo, w, container, cv, n_sets, out, sym_out, none);
-        else
-            hipLaunchKernelGGL((k3_decode<false, 1, false, true>), grid, block, 0, st, g, bins, dtab,
-                               lo, w, container, cv, n_sets, out, sym_out, none);
+    } else if (outliers_with_rows(cv)) {
+        launch_values<false, true>(g, wide, grid, block, bins, dtab, lo, w, container, cv, n_sets,
+                                   out, none, st);
     } else {
-        if (wide)
-            hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock>), grid, block, 0, st, g, bins,
-                               dtab, lo, w, container, cv, n_sets, out, sym_out, none);
-        else
-            hipLaunchKernelGGL((k3_decode<false, 1>), grid, block, 0, st, g, bins, dtab,
-                               lo, w, container, cv, n_sets, out, sym_out, none);
+        launch_values<false, false>(g, wide, grid, block, bins, dtab, lo, w, container, cv, n_sets,
+                                    out, none, st);
     }
     return hipGetLastError();
 }
@@ -905,36 +966,11 @@ __global__ __launch_bounds__(256) void k_apply_outliers(Geom g, const uint8_t *_
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kLanes);
     const uint64_t gidx = (uint64_t)blockIdx.x * (blockDim.x / kLanes) + wave;
     if (gidx >= n_groups) return;
-    const uint32_t lane = threadIdx.x % kLanes;
-    const uint64_t *offs = reinterpret_cast<const uint64_t *>(container + cv.out_off);
-    const uint64_t beg = min(offs[gidx], cv.n_out);
-    const uint64_t end = max(beg, min(offs[gidx + 1], cv.n_out));
-    if (beg == end) return;
     const uint32_t b = (uint32_t)(gidx % g.NB);
     const uint64_t tmp = gidx / g.NB;
     const uint32_t row = (uint32_t)(tmp % (2 * g.L));
     const uint32_t k = g.kb + (uint32_t)(tmp / (2 * g.L));
-    const uint32_t t0 = k * g.Tc, len = chunk_len(g, k);
-    const uint32_t *keys = reinterpret_cast<const uint32_t *>(container + cv.keys_off);
-    const uint16_t *vals = reinterpret_cast<const uint16_t *>(container + cv.vals_off);
-    for (uint64_t e = beg + lane; e < end; e += kLanes) {
-        const uint32_t key = keys[e];
-        const uint32_t u = key >> 6, c = b * kLanes + (key & 63u);
-        if (u >= len || c >= g.C) continue;
-        const uint32_t t = t0 + u;
-        uint16_t *dst;
-        if constexpr (PAGED) {
-            const uint32_t blk = t >> pg.lp;
-            if (blk >= pg.n_blocks) continue;
-            const uint32_t id = (uint32_t)pg.bt[blk];
-            if (id >= pg.num_pages) continue;  // negative ids too
-            const uint64_t pool = ((uint64_t)pg.num_pages << pg.lp) * g.C;
-            dst = pg.pages + row * pool + (((uint64_t)id << pg.lp) + (t & ((1u << pg.lp) - 1u))) * g.C + c;
-        } else {
-            dst = out + ((uint64_t)row * g.S + t) * g.C + c;
-        }
-        *dst = vals[e];
-    }
+    apply_group_outliers<PAGED>(g, container, cv, gidx, k, row, b, threadIdx.x % kLanes, out, pg);
 }
 
 hipError_t launch_apply_outliers(const Geom &g, const uint8_t *container, const ContainerView &cv,
@@ -990,18 +1026,12 @@ hipError_t launch_k3_paged(const Geom &g, const uint8_t *bins, const uint32_t *d
     const uint32_t n_sets = (g.ke - g.kb + per_block - 1) / per_block;
     const uint64_t blocks = (uint64_t)g.L * 2 * g.NB * n_sets;
     const dim3 grid((uint32_t)blocks), block(wpb * kLanes);
-    if (g.alo && wide)
-        hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock, true, true>), grid, block, 0, st, g,
-                           bins, dtab, lo, w, container, cv, n_sets, nullptr, nullptr, pg);
-    else if (g.alo)
-        hipLaunchKernelGGL((k3_decode<false, 1, true, true>), grid, block, 0, st, g, bins, dtab, lo,
-                           w, container, cv, n_sets, nullptr, nullptr, pg);
-    else if (wide)
-        hipLaunchKernelGGL((k3_decode<false, kWavesPerBlock, true>), grid, block, 0, st, g, bins,
-                           dtab, lo, w, container, cv, n_sets, nullptr, nullptr, pg);
+    if (outliers_with_rows(cv))
+        launch_values<true, true>(g, wide, grid, block, bins, dtab, lo, w, container, cv, n_sets,
+                                  nullptr, pg, st);
     else
-        hipLaunchKernelGGL((k3_decode<false, 1, true>), grid, block, 0, st, g, bins, dtab, lo, w,
-                           container, cv, n_sets, nullptr, nullptr, pg);
+        launch_values<true, false>(g, wide, grid, block, bins, dtab, lo, w, container, cv, n_sets,
+                                   nullptr, pg, st);
     return hipGetLastError();
 }
 
