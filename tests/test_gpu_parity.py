@@ -419,6 +419,39 @@ def test_outlier_table(cg, S, C, G, Tc, rng, ppm, n_sink, anchor_bits):
     assert np.array_equal(_u16(_gather_pages(pages, bt, S)), ref)
 
 
+@pytest.mark.parametrize("P,anchor_bits", [(1, 16), (64, 8), (256, 16)])
+def test_outlier_entries_into_pages(cg, P, anchor_bits):
+    """A container with outlier entries decoded into pages of 1, 64 and 256 tokens (the
+    decoding wavefronts write the entries through the block table) equals its contiguous
+    decode; the block mapped to an invalid page id writes nothing."""
+    L, S, C, G, Tc = 2, 900, 136, 10, 120
+    X = _gen(L, S, C, HEAVY)
+    tab = cg.build_cdf(X, G, Tc, (32, 8), H_kv=17, anchor_bits=anchor_bits, outlier_ppm=20000)
+    blob = cg.encode(tab, X)
+    assert blob.header["n_outliers"] > 0
+    ref = cg.decode(tab, blob)
+    nb = -(-S // P)
+    bt = torch.randperm(nb, generator=torch.Generator().manual_seed(P)).to(torch.int32)
+    bad = nb // 2
+    bt[bad] = -1
+    bt = bt.cuda()
+    pages = torch.full((L, 2, nb, P, C), float("nan"), dtype=torch.float16, device="cuda")
+    _say("[paged outliers] P=%d anchor_bits=%d entries=%d" % (P, anchor_bits, blob.header["n_outliers"]))
+    cg.decode_paged(tab, blob, pages, bt)
+    torch.cuda.synchronize()
+    got = _u16(pages)
+    want = _u16(ref)
+    btc = bt.cpu().tolist()
+    nan16 = _u16(torch.full((1,), float("nan"), dtype=torch.float16))[0]
+    for j in range(nb):
+        n = min(P, S - j * P)
+        if j == bad:
+            continue
+        assert np.array_equal(got[:, :, btc[j], :n], want[:, :, j * P:j * P + n]), j
+    unused = sorted(set(range(nb)) - set(x for x in btc if x >= 0))
+    assert (got[:, :, unused] == nan16).all()
+
+
 @pytest.mark.parametrize("ppm,anchor_bits,n_sink", [(0, 16, 4), (3000, 16, 4), (0, 8, 4),
                                                     (3000, 8, 12)])
 def test_another_cache_with_calibration_tables(cg, ppm, anchor_bits, n_sink):
