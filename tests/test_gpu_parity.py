@@ -215,6 +215,56 @@ def test_damaged_container_decodes_without_fault(cg, S, Tc):
     assert torch.equal(a.view(torch.int16), X[:, :, ::10][:, :, :13].view(torch.int16))
 
 
+def test_damaged_outlier_sections_decode_without_fault(cg):
+    """A container's outlier sections damaged: changed values land only on their entries'
+    elements; garbage offsets and keys still decode (contiguous and paged) with every
+    write inside the output."""
+    L, S, C, G, Tc = 2, 900, 136, 10, 120
+    X = _gen(L, S, C, HEAVY)
+    tab = cg.build_cdf(X, G, Tc, (32, 8), H_kv=17, outlier_ppm=20000)
+    blob = cg.encode(tab, X)
+    h = blob.header
+    n = h["n_outliers"]
+    assert n > 1000
+    ref = cg.decode(tab, blob)
+    raw0 = blob.read().copy()
+    # values changed: the decode differs from the reference exactly at the entries
+    raw = torch.from_numpy(raw0.copy()).cuda()
+    vals = raw[h["outlier_values_offset"]:h["outlier_values_offset"] + 2 * n].view(torch.int16)
+    vals ^= 0x0101
+    out = cg.decode(tab, blob, container=raw)
+    torch.cuda.synchronize()
+    offs = raw0[h["outliers_offset"]:h["outliers_offset"] + 8 * (h["n_groups"] + 1)].view(np.uint64)
+    keys = raw0[h["outlier_keys_offset"]:h["outlier_keys_offset"] + 4 * n].view(np.uint32)
+    NB = -(-C // 64)
+    mask = np.zeros((L, 2, S, C), bool)
+    for gidx in range(h["n_groups"]):
+        b, tmp = gidx % NB, gidx // NB
+        row, k = tmp % (2 * L), tmp // (2 * L)
+        for e in range(int(offs[gidx]), int(offs[gidx + 1])):
+            u, c = int(keys[e]) >> 6, b * 64 + (int(keys[e]) & 63)
+            mask[row // 2, row % 2, k * Tc + u, c] = True
+    diff = _u16(out) != _u16(ref)
+    assert np.array_equal(diff, mask)
+    # offsets and keys garbage: no fault, and the output keeps its shape
+    g = torch.Generator().manual_seed(1)
+    raw = torch.from_numpy(raw0.copy()).cuda()
+    o = raw[h["outliers_offset"]:h["outliers_offset"] + 8 * (h["n_groups"] + 1)].view(torch.int64)
+    o[3], o[4], o[7] = 1 << 40, 0, n + 5
+    kk = raw[h["outlier_keys_offset"]:h["outlier_keys_offset"] + 4 * n].view(torch.int32)
+    sel = torch.randint(0, n, (300,), generator=g).cuda()
+    kk[sel] = torch.randint(-2 ** 31, 2 ** 31 - 1, (300,), generator=g, dtype=torch.int64).to(torch.int32).cuda()
+    _say("[damaged outliers] n=%d" % n)
+    out = cg.decode(tab, blob, container=raw)
+    P = 16
+    nb = -(-S // P)
+    pages = torch.zeros((L, 2, nb, P, C), dtype=torch.float16, device="cuda")
+    cg.decode_paged(tab, blob, pages, torch.arange(nb, dtype=torch.int32, device="cuda"),
+                    container=raw)
+    torch.cuda.synchronize()
+    assert out.shape == X.shape
+
+
 def test_reconstruction_bound_at_scale(cg):
     """8B-shaped slice, GPU only: anchors exact, every other element within half a bin
     plus fp16 rounding (a property that holds at any size)."""
