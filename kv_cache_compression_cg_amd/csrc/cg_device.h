@@ -84,12 +84,12 @@ __device__ __forceinline__ uint32_t quantize_bf(float delta, float lo, float r, 
 
 // Whether quantize1 had to clamp: the nearest grid point is more than half a step away
 // (floor(fma(delta - lo, r, 0.5)) outside [0, N - 1]), or the grid has zero width (r = 0,
-// the single point lo) and delta is not on it.
+// the single point lo) and delta is not on it, or delta is NaN (no grid point holds it).
 __device__ __forceinline__ bool off_grid(float delta, float lo, float r, uint32_t N)
 {
     if (r == 0.0f) return delta != lo;
     const float v = floorf(fmaf(delta - lo, r, 0.5f));
-    return v < 0.0f || v > (float)(N - 1u);
+    return !(v >= 0.0f && v <= (float)(N - 1u));
 }
 
 // fp16_rne of fp32 fma(a, b, c), the fma rounded to fp32 first.  (The empty asm keeps

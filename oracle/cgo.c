@@ -273,7 +273,8 @@ static uint8_t quantize_one(float delta, float lo, float r, uint32_t N)
 
 /* An element is off its grid when the clamp above changes its code: its nearest grid
  * point is more than half a step away (floor(fma(Delta - lo, r, 0.5)) outside [0, N-1]),
- * or the grid has zero width (r = 0: the single point lo) and does not hold it.  The
+ * or the grid has zero width (r = 0: the single point lo) and does not hold it, or
+ * Delta is NaN (no grid point holds it; quantize_one codes it 0).  The
  * tables' own cache has no off-grid element except outside a clipped central range; a
  * cache coded with another cache's tables may have more. */
 static int off_grid(float delta, float lo, float r, uint32_t N)
@@ -281,7 +282,7 @@ static int off_grid(float delta, float lo, float r, uint32_t N)
     if (r == 0.0f)
         return delta != lo;
     float v = floorf(fmaf(delta - lo, r, 0.5f));
-    return v < 0.0f || v > (float)(N - 1u);
+    return !(v >= 0.0f && v <= (float)(N - 1u));   /* a NaN Delta: off every grid */
 }
 
 void cgo_quantize(uint32_t L, uint32_t H, uint32_t d, uint32_t S, uint32_t G, uint32_t Tc,

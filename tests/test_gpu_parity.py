@@ -502,6 +502,26 @@ def test_outlier_entries_into_pages(cg, P, anchor_bits):
     assert (got[:, :, unused] == nan16).all()
 
 
+@pytest.mark.parametrize("ppm,anchor_bits", [(0, 16), (3000, 16), (0, 8), (3000, 8)])
+def test_calibration_tables_on_a_cache_with_inf_and_nan(cg, ppm, anchor_bits):
+    """Tables built from a finite cache code another that holds Inf and NaN (the tables'
+    build rejects such a cache, the encode with calibration tables takes it): inside a
+    group's deltas, as an anchor, and in a sink row; container and decode equal the
+    oracle's bit for bit."""
+    L, S, C, G, Tc = 2, 600, 72, 10, 200
+    X = _gen(L, S, C, HEAVY)
+    Y = X.clone()
+    inf, nan = float("inf"), float("nan")
+    Y[0, 0, 13, 3] = inf
+    Y[0, 1, 27, 70] = -inf
+    Y[1, 0, 45, 10] = nan
+    Y[1, 1, 100, 40] = nan      # an anchor
+    Y[0, 0, 210, 5] = inf       # an anchor
+    Y[1, 0, 1, 7] = nan         # a sink row
+    full_parity(cg, X, 9, G, Tc, (16, 8), label="inf / nan", n_sink=2,
+                anchor_bits=anchor_bits, outlier_ppm=ppm, X_enc=Y)
+
+
 @pytest.mark.parametrize("ppm,anchor_bits,n_sink", [(0, 16, 4), (3000, 16, 4), (0, 8, 4),
                                                     (3000, 8, 12)])
 def test_another_cache_with_calibration_tables(cg, ppm, anchor_bits, n_sink):

@@ -823,6 +823,64 @@ def test_another_cache_is_coded_within_the_bound_with_the_table(anchor_bits):
     assert (np.abs(xs - ys) <= tol + 1e-30).all()
 
 
+@pytest.mark.parametrize("anchor_bits", [16, 8])
+def test_non_finite_elements_of_another_cache_are_stored_exactly(anchor_bits):
+    """Calibration tables coding a cache that holds NaN and Inf (reading: no grid point
+    holds a NaN delta, so such an element is off its grid like one beyond the range):
+    with the outlier table the entries are those of the finite cache plus exactly the
+    non-finite elements (and, with fp16 anchors, the rest of a group whose anchor is
+    NaN, all of whose deltas are NaN; with 8-bit anchors the NaN anchor itself), each
+    holding its fp16 bits, which the decode returns; without the table they are the
+    clamped count."""
+    L, S, C, G, Tc = 1, 200, 9, 5, 100
+    _, X = _small_data(L=L, S=S, C=C, G=G, Tc=Tc, bins=(8,), seed=1)
+    on = O.Shape.make(L, 1, C, S, G, Tc, (8,), anchor_bits=anchor_bits, outlier_ppm=5000)
+    off = O.Shape.make(L, 1, C, S, G, Tc, (8,), anchor_bits=anchor_bits)
+    tab = O.build_tables(on, X)
+
+    def entries(enc):
+        NB = -(-C // O.LANES)
+        got, g = set(), 0
+        for k in range(on.n_chunks):
+            for kv in range(2):
+                for b in range(NB):
+                    for e in range(int(enc.out_offsets[g]), int(enc.out_offsets[g + 1])):
+                        key = int(enc.out_keys[e])
+                        got.add((kv, k * Tc + (key >> 6), b * O.LANES + (key & 63)))
+                    g += 1
+        return got
+
+    base = entries(O.encode(on, X, tab))
+    nan16 = np.float16(np.nan).view(np.uint16)
+    nanp = np.uint16(nan16 | 0x0123)                   # a NaN with a payload
+    inf16, ninf16 = np.float16(np.inf).view(np.uint16), np.float16(-np.inf).view(np.uint16)
+    plain = {(0, 7, 2): nan16, (1, 13, 5): inf16, (0, 33, 8): ninf16, (1, 118, 0): nanp}
+    anchor = (1, 60, 1)                                # t = 60 anchors tokens 61..64
+    group = {(1, t, 1) for t in range(61, 65)}
+    new = set(plain) | (group if anchor_bits == 16 else {anchor})
+    assert not (new | group | {anchor}) & base         # all on their grids in X
+    Y = X.copy()
+    for (kv, t, c), v in plain.items():
+        Y[0, kv, t, c] = v
+    Y[0, anchor[0], anchor[1], anchor[2]] = nan16
+    enc = O.encode(on, Y, tab)
+    got = entries(enc)
+    if anchor_bits == 16:
+        assert got == base | new
+    else:
+        # the NaN anchor is coded 0, so the group's deltas are taken against the lowest
+        # point of the anchor grid and some of them may leave the delta grid
+        assert base | new <= got <= base | new | group
+    out = O.decode(on, tab, enc)
+    for (kv, t, c) in got:
+        assert out[0, kv, t, c] == Y[0, kv, t, c]
+    if anchor_bits == 16:                              # the anchor row itself is exact
+        assert out[0, anchor[0], anchor[1], anchor[2]] == nan16
+    tab_off = O.Tables(tab.lo, tab.w, tab.r, tab.counts, tab.freqs, tab.alo, tab.aw, tab.ar)
+    e_off = O.encode(off, Y, tab_off)
+    assert e_off.clamped == len(got) and e_off.n_outliers == 0
+
+
 def test_outlier_brute_force_tiny():
     """L=1, S=30, C=2, G=3, N=4, 10% budget: the clipped range, the entries and the
     decode worked out from exact rationals and a sort."""
