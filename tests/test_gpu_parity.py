@@ -502,6 +502,25 @@ def test_outlier_entries_into_pages(cg, P, anchor_bits):
     assert (got[:, :, unused] == nan16).all()
 
 
+@pytest.mark.parametrize("ppm,anchor_bits", [(0, 16), (20000, 16), (0, 8), (20000, 8)])
+def test_extreme_finite_values(cg, ppm, anchor_bits):
+    """Channels that span the whole fp16 range (+-65504, whose deltas reach 131008 and
+    whose decoded values can round to +-Inf), subnormals and signed zeros next to
+    ordinary channels: tables, container and decodes equal the oracle's bit for bit."""
+    L, S, C, G, Tc = 2, 500, 80, 10, 170
+    X = _gen(L, S, C, HEAVY)
+    g = torch.Generator().manual_seed(5)
+    big = torch.tensor([65504.0, -65504.0, 0.0, -0.0], dtype=torch.float16)
+    X[0, 0, :, 3] = big[torch.randint(0, 4, (S,), generator=g)].cuda()
+    X[1, 1, :, 70] = big[torch.randint(0, 2, (S,), generator=g)].cuda()
+    sub = torch.tensor([1, 2, 1023, 0x8001 - 0x10000, 0x83FF - 0x10000, 0], dtype=torch.int16)  # subnormals
+    X[0, 1, :, 9] = sub[torch.randint(0, 6, (S,), generator=g)].cuda().view(torch.float16)
+    X[1, 0, ::7, 40] = 65504.0
+    X[1, 0, 3::11, 41] = -65504.0
+    full_parity(cg, X, 8, G, Tc, (32, 4), label="extreme finite", anchor_bits=anchor_bits,
+                outlier_ppm=ppm)
+
+
 @pytest.mark.parametrize("ppm,anchor_bits", [(0, 16), (3000, 16), (0, 8), (3000, 8)])
 def test_calibration_tables_on_a_cache_with_inf_and_nan(cg, ppm, anchor_bits):
     """Tables built from a finite cache code another that holds Inf and NaN (the tables'
