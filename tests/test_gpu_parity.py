@@ -657,6 +657,39 @@ def test_seeded_sweep_of_shapes_and_settings(cg, case):
                 n_sink=n_sink, anchor_bits=anchor_bits, outlier_ppm=ppm)
 
 
+def _calibration_cases(n=60, seed=12):
+    """Sweep cases whose cache is coded with tables built on another one: its own seeded
+    generator, and in some cases a few Inf, NaN, +-65504 or zero elements."""
+    rng = np.random.default_rng(seed + 1000)
+    out = []
+    for case in _sweep_cases(n=n, seed=seed):
+        spec = configs.GenSpec(rho=float(rng.uniform(0.3, 0.95)), heavy_tail=bool(rng.random() < 0.5),
+                               outlier_frac=float(rng.uniform(0, 0.1)),
+                               outlier_mult=float(rng.uniform(5, 60)), seed=int(rng.integers(0, 10 ** 6)))
+        pokes = []
+        if rng.random() < 0.4:
+            for _ in range(int(rng.integers(1, 6))):
+                pokes.append((rng.random(), rng.random(), rng.random(), rng.random(), int(rng.integers(0, 6))))
+        out.append((case, spec, pokes))
+    return out
+
+
+@pytest.mark.parametrize("cc", _calibration_cases(), ids=lambda c: "case%d" % c[0][0])
+def test_seeded_sweep_with_calibration_tables(cg, cc):
+    """As the sweep above, each cache coded with the tables of another (R28), some with
+    non-finite or extreme elements (R31): every product bit for bit against the oracle."""
+    case, spec, pokes = cc
+    i, L, H, d, S, G, Tc, bins, bins_v, n_sink, anchor_bits, ppm, rngc, gen = case
+    C = H * d
+    X = _gen(L, S, C, gen)
+    Y = _gen(L, S, C, spec)
+    vals = [float("inf"), float("-inf"), float("nan"), 65504.0, -65504.0, 0.0]
+    for a, b, c, e, v in pokes:
+        Y[int(a * L), int(b * 2), int(c * S), int(e * C)] = vals[v]
+    full_parity(cg, X, H, G, Tc, bins, chunk_range=rngc, label="calibration sweep %d" % i,
+                bins_v=bins_v, n_sink=n_sink, anchor_bits=anchor_bits, outlier_ppm=ppm, X_enc=Y)
+
+
 def test_stored_form_through_files_and_repeat_runs_are_identical(cg, tmp_path):
     """A cache kept as files (the stored tables and the container written out, read back
     by a fresh import) decodes to what the encoder's own handles decode; and every run of
