@@ -354,8 +354,9 @@ __global__ __launch_bounds__(256) void k_clip(Geom g, const uint16_t *__restrict
 // ------------------------------------------------------------------------------ K1
 // Fused delta -> quantize -> histogram.  Block = (row, tile of 8*OCT channels, token
 // block); its SUB x OCT threads each own 8 channels of a token sub-range.  Counts go
-// to an LDS histogram [N][8][OCT] (consecutive lanes -> consecutive banks), then the
-// non-zero bins are added to the global u32 counts.
+// to an LDS histogram [N/2][8][OCT] of 16-bit counter pairs (bins 2m and 2m + 1 in one
+// word; consecutive lanes -> consecutive banks; half the LDS of 32-bit counters, so more
+// blocks are resident), then the non-zero bins are added to the global u32 counts.
 __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, Geom g,
                                                 const uint8_t *__restrict__ bins,
                                                 const float *__restrict__ lo,
@@ -370,7 +371,9 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
     uint32_t row = tmp / ntiles;
     uint32_t N = bins[row];
     const float nm1 = (float)(N - 1u);
-    uint32_t nh = N * 8 * OCT;
+    // counters of bins 2m and 2m + 1 share a word (16 bits each: a block counts fewer
+    // than 2^16 tokens per channel)
+    uint32_t nh = (N + 1) / 2 * 8 * OCT;
     for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) hist[j] = 0;
     __syncthreads();
 
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const uint32_t q = quantize_bf(xf[j] - af[j], lo8[j], r8[j], nm1);
-                    atomicAdd(&hist[(q * 8 + j) * OCT + ol], 1u);
+                    atomicAdd(&hist[((q >> 1) * 8 + j) * OCT + ol], 1u << (16 * (q & 1u)));
                 }
             }
         });
@@ -415,10 +418,12 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
     for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) {
         uint32_t v = hist[j];
         if (!v) continue;
-        uint32_t s = j / (8 * OCT), rem = j - s * 8 * OCT;
+        uint32_t m = j / (8 * OCT), rem = j - m * 8 * OCT;
         uint32_t jj = rem / OCT, oo = ct * OCT + rem % OCT;
         if (oo >= O) continue;
-        atomicAdd(&counts[((uint64_t)row * g.C + oo * 8 + jj) * kMaxBins + s], v);
+        uint32_t *cnt = &counts[((uint64_t)row * g.C + oo * 8 + jj) * kMaxBins + 2 * m];
+        if (v & 0xFFFFu) atomicAdd(cnt, v & 0xFFFFu);
+        if (v >> 16) atomicAdd(cnt + 1, v >> 16);
     }
 }
 
@@ -1225,8 +1230,9 @@ hipError_t launch_k1(const uint16_t *X, const Geom &g, const uint8_t *bins, uint
     uint64_t ntb_target = (8192 + rows * ntiles - 1) / (rows * ntiles);
     uint64_t tpt = (g.S + ntb_target * SUB - 1) / (ntb_target * SUB);
     if (tpt < 16) tpt = 16;
+    if (tpt * SUB > 0xFFFFu) tpt = 0xFFFFu / SUB;   // 16-bit counters per block
     uint32_t ntb = (uint32_t)((g.S + tpt * SUB - 1) / (tpt * SUB));
-    size_t lds = (size_t)max_bins * 8 * OCT * sizeof(uint32_t);
+    size_t lds = (size_t)(max_bins + 1) / 2 * 8 * OCT * sizeof(uint32_t);
     hipLaunchKernelGGL(k1_hist, dim3((uint32_t)(rows * ntiles * ntb)), dim3(256), lds, st, X, g,
                        bins, lo, r, OCT, SUB, (uint32_t)tpt, ntiles, ntb, counts);
     return hipGetLastError();
