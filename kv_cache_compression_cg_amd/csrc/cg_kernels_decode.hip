@@ -42,10 +42,13 @@ __device__ __forceinline__ void ring_put(uint16_t *ring, uint32_t pos, uint32_t 
     if (slot < 64) *reinterpret_cast<ring_pair_t *>(ring + slot + kRingWords) = v;
 }
 
-// The block's table in LDS, all bytes: f of symbol s for this lane at 64 s + lane, cdf of
-// s 2 KiB further, then the slot table at 64 slot + lane (20 KiB in all).  The
-// dequantized delta lo + s * w is recomputed (one conversion and one fma, as the table
-// builder does) rather than staged.
+// The block's table in LDS.  Tables of more than 16 symbols: f of symbol s for this lane
+// at byte 64 s + lane, cdf of s 2 KiB further.  Tables of at most 16: the entry
+// {f | cdf << 24} of s for this lane as the dword 64 s + lane (one read per symbol, and
+// the 64 lanes of a read hit 64 banks), in the same 4 KiB.  Then the slot table at byte
+// 256 (slot / 4) + 4 lane + slot mod 4 (20 KiB in all).  The dequantized delta lo + s * w
+// is recomputed (one conversion and one fma, as the table builder does) rather than
+// staged.
 constexpr uint32_t kLdsCdf = kMaxBins * kLanes;
 constexpr uint32_t kLdsLut = 2 * kMaxBins * kLanes;
 constexpr uint32_t kLdsWords = (kLdsLut + kProbTotal * kLanes) / 4;
@@ -74,20 +77,32 @@ struct WaveDecoder {
         return tab[kLdsLut + a];
     }
 
+    template <bool DW = false>
     __device__ __forceinline__ void update(const uint8_t *tab, uint32_t lane, uint32_t slot,
                                            uint32_t s, float &dq)
     {
         const uint32_t p = s * kLanes + lane;
-        const uint32_t f = tab[p], cdf = tab[kLdsCdf + p];
         // fma(s, w, lo) with s taken as the fp16 subnormal s * 2^-24 and w pre-scaled by
         // 2^24: both scalings are exact and the fma's product is the same real number,
         // so the result is bit-identical, and the hardware reads s straight from the
         // byte without a conversion instruction
         dq = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)s), dw24, dlo);
-        x = __umul24(f, x >> kProbBits) + slot - cdf;
+        if constexpr (DW) {
+            // the entry {f | cdf << 24} as one dword (tables of at most 16 symbols): f is
+            // its low 24 bits, slot - cdf one subtraction of byte 0 of x and byte 3
+            const uint32_t e = reinterpret_cast<const uint32_t *>(tab)[p];
+            uint32_t d;
+            asm("v_sub_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:BYTE_3"
+                : "=v"(d) : "v"(x), "v"(e));
+            x = __umul24(e, x >> kProbBits) + d;
+        } else {
+            const uint32_t f = tab[p], cdf = tab[kLdsCdf + p];
+            x = __umul24(f, x >> kProbBits) + slot - cdf;
+        }
     }
 
     // Returns the symbol.
+    template <bool DW = false>
     __device__ __forceinline__ uint32_t symbol(const uint8_t *tab, uint32_t lane, float &dq)
     {
         uint32_t slot;
@@ -95,7 +110,7 @@ struct WaveDecoder {
         // (an opaque 32-bit value from here: the byte read already zero-extends, and
         // without this the compiler masks it again)
         asm volatile("" : "+v"(s));
-        update(tab, lane, slot, s, dq);
+        update<DW>(tab, lane, slot, s, dq);
         return s;
     }
 
@@ -238,7 +253,7 @@ __device__ __forceinline__ void apply_group_outliers(const Geom &g, const uint8_
 // requested and the previous group's outputs (held in registers) are written; the
 // requested data is consumed at the group's end.  Waits for it therefore never wait for
 // a store issued during the group.
-template <bool SYMBOLS, bool PAGED = false, bool A8 = false>
+template <bool SYMBOLS, bool PAGED = false, bool A8 = false, bool DW = false>
 struct Stream {
     WaveDecoder dec;
     __amdgpu_buffer_rsrc_t ars, ors;
@@ -475,7 +490,7 @@ struct Stream {
     __device__ __forceinline__ void step_held(const uint8_t *tab, uint32_t lane, int u)
     {
         float dq;
-        const uint32_t s = dec.symbol(tab, lane, dq);
+        const uint32_t s = dec.symbol<DW>(tab, lane, dq);
         hold(u, s, dq);
     }
 
@@ -505,7 +520,7 @@ struct Stream {
     {
         for (uint32_t u = nsteps; u != 0; --u) {
             float dq;
-            const uint32_t sym = dec.symbol(tab, lane, dq);
+            const uint32_t sym = dec.symbol<DW>(tab, lane, dq);
             if (dec.present)
                 store_row(pm, orow, SYMBOLS ? sym : f2h(af + dq));
             orow += rstep();
@@ -520,8 +535,8 @@ struct Stream {
 };
 
 // An unrolled group of both streams of a wavefront in lockstep.
-template <bool SYMBOLS, bool PAGED, bool A8, int NS>
-__device__ __forceinline__ void paired_steps(Stream<SYMBOLS, PAGED, A8> (&st)[NS], const uint8_t *tab,
+template <bool SYMBOLS, bool PAGED, bool A8, bool DW, int NS>
+__device__ __forceinline__ void paired_steps(Stream<SYMBOLS, PAGED, A8, DW> (&st)[NS], const uint8_t *tab,
                                              uint32_t lane)
 {
 #pragma unroll
@@ -534,7 +549,7 @@ __device__ __forceinline__ void paired_steps(Stream<SYMBOLS, PAGED, A8> (&st)[NS
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             float dq;
-            st[s].dec.update(tab, lane, slot[s], sym[s], dq);
+            st[s].dec.template update<DW>(tab, lane, slot[s], sym[s], dq);
             st[s].hold(u, sym[s], dq);
         }
         // both state updates are computed here, next to their table reads
@@ -579,7 +594,8 @@ __device__ __forceinline__ void paired_steps(Stream<SYMBOLS, PAGED, A8> (&st)[NS
 // the block's LDS table.  With two, the symbol decodes of both streams sit in one
 // basic block, so the dependent LDS reads of one overlap the arithmetic of the other.
 // With MULTI, k0 and k1 index srcs->ch: the chunk and the container it is read from.
-template <bool SYMBOLS, bool FULL, int NS, bool PAGED, bool A8, bool MULTI = false, bool OUTL = false>
+template <bool SYMBOLS, bool FULL, int NS, bool PAGED, bool A8, bool MULTI = false, bool OUTL = false,
+          bool DW = false>
 __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__restrict__ tab,
                                               uint16_t *__restrict__ ring,
                                               const float *__restrict__ lo,
@@ -593,7 +609,7 @@ __device__ __forceinline__ void decode_chunks(const Geom &g, const uint8_t *__re
 {
     const bool present = FULL || lane < min(kLanes, g.C - b * kLanes);
     const PageMap pm = page_map<PAGED>(g, pg, row, b);
-    Stream<SYMBOLS, PAGED, A8> st[NS];
+    Stream<SYMBOLS, PAGED, A8, DW> st[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const uint32_t i = s == 0 ? k0 : k1;
@@ -733,10 +749,17 @@ __device__ __forceinline__ void decode_block(Geom g, const uint8_t *__restrict__
     // stage f and cdf of the N used entries as bytes, and the slot table
     const uint32_t *src = dtab + (uint64_t)(row * g.NB + b) * kTabBlock;
     uint8_t *tb8 = reinterpret_cast<uint8_t *>(tab);
-    for (uint32_t j = threadIdx.x; j < N * kLanes; j += blockDim.x) {
-        const uint32_t e = src[j];
-        tb8[j] = (uint8_t)e;
-        tb8[kLdsCdf + j] = (uint8_t)(e >> 24);
+    // tables of at most 16 symbols: their entries as dwords (one read per symbol and no
+    // bank conflicts, in the same 4 KiB); larger ones as the f and cdf byte planes
+    const bool dw = N <= 16;
+    if (dw) {
+        for (uint32_t j = threadIdx.x; j < N * kLanes; j += blockDim.x) tab[j] = src[j];
+    } else {
+        for (uint32_t j = threadIdx.x; j < N * kLanes; j += blockDim.x) {
+            const uint32_t e = src[j];
+            tb8[j] = (uint8_t)e;
+            tb8[kLdsCdf + j] = (uint8_t)(e >> 24);
+        }
     }
     const uint4 *lsrc = reinterpret_cast<const uint4 *>(src + kTabLut);
     uint4 *ldst = reinterpret_cast<uint4 *>(tb8 + kLdsLut);
@@ -751,13 +774,22 @@ __device__ __forceinline__ void decode_block(Geom g, const uint8_t *__restrict__
     const uint8_t *tb = reinterpret_cast<const uint8_t *>(tab);
     uint16_t *ring = rings + wave * kStreamsPerWave * kRingAlloc;
     const bool pair = k1 < g.ke;
-    if (g.C - b * kLanes >= kLanes) {
-        if (pair)
-            decode_chunks<SYMBOLS, true, 2, PAGED, A8, MULTI, OUTL>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
+    const bool full = g.C - b * kLanes >= kLanes;
+    if (dw) {
+        if (full && pair)
+            decode_chunks<SYMBOLS, true, 2, PAGED, A8, MULTI, OUTL, true>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
+        else if (full)
+            decode_chunks<SYMBOLS, true, 1, PAGED, A8, MULTI, OUTL, true>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
+        else if (pair)
+            decode_chunks<SYMBOLS, false, 2, PAGED, A8, MULTI, OUTL, true>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
         else
-            decode_chunks<SYMBOLS, true, 1, PAGED, A8, MULTI, OUTL>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
+            decode_chunks<SYMBOLS, false, 1, PAGED, A8, MULTI, OUTL, true>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
     } else {
-        if (pair)
+        if (full && pair)
+            decode_chunks<SYMBOLS, true, 2, PAGED, A8, MULTI, OUTL>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
+        else if (full)
+            decode_chunks<SYMBOLS, true, 1, PAGED, A8, MULTI, OUTL>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
+        else if (pair)
             decode_chunks<SYMBOLS, false, 2, PAGED, A8, MULTI, OUTL>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
         else
             decode_chunks<SYMBOLS, false, 1, PAGED, A8, MULTI, OUTL>(g, tb, ring, lo, w, container, cv, k0, k1, row, b, lane, out, sym_out, pg, srcs);
