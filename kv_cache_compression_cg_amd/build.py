@@ -12,6 +12,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -39,13 +40,29 @@ def flags() -> list:
             "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _link(sources, lib, verbose):
-    tmp = lib + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + flags() + ["-shared", "-x", "hip"] + sources + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, lib)
+
+
+def _link(sources, lib, verbose):
+    """Each source compiled to its own object in parallel (the kernels of one file call no
+    device code of another), then one shared library linked from them."""
+    tmp = lib + ".tmp%d" % os.getpid()
+    objs = [tmp + ".%d.o" % i for i in range(len(sources))]
+    cmds = [[hipcc()] + flags() + ["-c", "-x", "hip", src, "-o", obj]
+            for src, obj in zip(sources, objs)]
+    try:
+        with ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        _run([hipcc()] + flags() + ["-shared"] + objs + ["-o", tmp], verbose)
+        os.replace(tmp, lib)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
 
 
 def build(verbose: bool = False) -> str:

@@ -43,18 +43,6 @@ __device__ __forceinline__ float ord2f(uint32_t o)
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-__device__ __forceinline__ bool any_nonfinite(uint4 v)
-{
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    bool bad = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        bad |= (w[i] & 0x7C00u) == 0x7C00u;
-        bad |= (w[i] & 0x7C000000u) == 0x7C000000u;
-    }
-    return bad;
-}
-
 __device__ __forceinline__ void unpack8(uint4 v, float f[8])
 {
     uint32_t w[4] = {v.x, v.y, v.z, v.w};

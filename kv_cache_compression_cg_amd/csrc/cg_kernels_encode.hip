@@ -28,6 +28,22 @@ __device__ __forceinline__ void ntstore8(void *p, uint2 v)
 }
 
 
+// x - a for the fp16 bits h of x, as one mixed-precision fma x * one + (-a) that reads h
+// directly (one = 1.0 held in a register the compiler cannot see through, so the fma is
+// not folded back into a conversion and a subtraction).  The product is exact, so the
+// single rounding gives the fp32 difference bit for bit, signed zeros included.
+__device__ __forceinline__ float delta_mix(uint32_t h, float one, float a)
+{
+    return fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)h), one, -a);
+}
+// 1.0f, opaque to the compiler
+__device__ __forceinline__ float opaque_one()
+{
+    float one = 1.0f;
+    asm volatile("" : "+v"(one));
+    return one;
+}
+
 // Calls body(row, walk) for the token rows [w.t, t_end) of one thread (16 bytes each at
 // base + t * C), with the loads of the next A rows in flight: the row loop of the
 // histogram passes would otherwise wait for one load at a time.  Loads past t_end read
@@ -57,6 +73,35 @@ __device__ __forceinline__ void rows_ahead(const Geom &g, const uint16_t *base, 
 // Per-channel min / max of the anchor deltas, and the non-finite flag.
 // Thread = (row, token block, 8 channels); 16-byte loads, one row of C channels is
 // read by C/8 consecutive threads.
+//
+// A delta is the fp32 difference x - a of a token and its group's anchor, and rounding is
+// monotone, so over the tokens of one group min(x - a) = min(x) - a (likewise max): the
+// group's tokens are reduced as fp16 pairs (one packed min and one packed max per two
+// channels) and only the group's extremes are converted and differenced.  That is exact
+// for finite inputs; an input with an Inf or NaN is rejected through the flag, which
+// collects x * 0 + acc per half (0 for every finite x, NaN from the first Inf or NaN on).
+// Signed zeros may come out in another order than element by element; a zero bound is
+// stored as +0 in any case.
+__device__ __forceinline__ uint32_t pk_min_f16(uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ uint32_t pk_max_f16(uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+// acc + x * 0 per half: stays 0 while x is finite, NaN from the first Inf or NaN on
+__device__ __forceinline__ uint32_t pk_nonfinite_acc(uint32_t acc, uint32_t x)
+{
+    uint32_t r;
+    asm("v_pk_fma_f16 %0, %1, 0, %2" : "=v"(r) : "v"(x), "v"(acc));
+    return r;
+}
+
 __global__ __launch_bounds__(256) void k0_minmax(const uint16_t *__restrict__ X, Geom g,
                                                   uint32_t tpt, uint32_t ntb,
                                                   uint32_t *__restrict__ ord_lo,
@@ -74,49 +119,71 @@ __global__ __launch_bounds__(256) void k0_minmax(const uint16_t *__restrict__ X,
     if (t_begin >= g.S) return;
     uint32_t t_end = min(g.S, t_begin + tpt);
     const uint16_t *base = X + (uint64_t)row * g.S * g.C + o * 8;
+    const uint64_t r0 = (uint64_t)row * g.C + o * 8;
 
+    constexpr uint32_t kPosInf2 = 0x7C007C00u, kNegInf2 = 0xFC00FC00u;
     TokenWalk w;
     w.init(g, t_begin);
     float af[8], mn[8], mx[8];
-    bool any = false, bad = false;
+    uint32_t gmn[4], gmx[4], nf[4];  // the group's fp16 min / max pairs; the non-finite sums
+    bool any = false, gany = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        gmn[j] = kPosInf2;
+        gmx[j] = kNegInf2;
+        nf[j] = 0;
+    }
     if (w.gp != 0) {
         uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
         unpack8(a, af);
-        snap8(g, (uint64_t)row * g.C + o * 8, af);
+        snap8(g, r0, af);
     }
-    for (; w.t < t_end; w.next(g)) {
-        uint4 v = ntload16(base + (uint64_t)w.t * g.C);
-        bad |= any_nonfinite(v);
-        float xf[8];
-        unpack8(v, xf);
-        if (w.gp == 0) {
+    // the current group's extremes into the fp32 range of deltas
+    auto fold = [&]() __attribute__((always_inline)) {
+        if (!gany) return;
+        float hmn[8], hmx[8];
+        unpack8(make_uint4(gmn[0], gmn[1], gmn[2], gmn[3]), hmn);
+        unpack8(make_uint4(gmx[0], gmx[1], gmx[2], gmx[3]), hmx);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) af[j] = xf[j];
-            snap8(g, (uint64_t)row * g.C + o * 8, af);
+        for (int j = 0; j < 8; ++j) {
+            const float dmn = hmn[j] - af[j], dmx = hmx[j] - af[j];
+            mn[j] = (!any || dmn < mn[j]) ? dmn : mn[j];
+            mx[j] = (!any || dmx > mx[j]) ? dmx : mx[j];
+        }
+        any = true;
+        gany = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gmn[j] = kPosInf2;
+            gmx[j] = kNegInf2;
+        }
+    };
+    rows_ahead<4>(g, base, w, t_end, [&](uint4 v, const TokenWalk &w) {
+        const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nf[j] = pk_nonfinite_acc(nf[j], x[j]);
+        if (w.gp == 0) {
+            fold();
+            unpack8(v, af);
+            snap8(g, r0, af);
         } else if (w.t >= g.n_sink) {  // sink tokens stay out of the range
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float dl = xf[j] - af[j];
-                if (!any) {
-                    mn[j] = dl;
-                    mx[j] = dl;
-                } else {
-                    mn[j] = (dl < mn[j]) ? dl : mn[j];
-                    mx[j] = (dl > mx[j]) ? dl : mx[j];
-                }
+            for (int j = 0; j < 4; ++j) {
+                gmn[j] = pk_min_f16(gmn[j], x[j]);
+                gmx[j] = pk_max_f16(gmx[j], x[j]);
             }
-            any = true;
+            gany = true;
         }
-    }
+    });
+    fold();
     if (any) {
-        uint64_t r0 = (uint64_t)row * g.C + o * 8;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             atomicMin(&ord_lo[r0 + j], f2ord(mn[j]));
             atomicMax(&ord_hi[r0 + j], f2ord(mx[j]));
         }
     }
-    if (bad) atomicOr(flag, 1u);
+    if (((nf[0] | nf[1] | nf[2] | nf[3]) & 0x7FFF7FFFu) != 0) atomicOr(flag, 1u);
 }
 
 // lo and hi per (row, channel) from the ordered min / max; a row with no coded token
@@ -391,6 +458,13 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
             lo8[j] = lo[r0 + j];
             r8[j] = r[r0 + j];
         }
+        // byte offset of the counter word of (bin pair m, channel j):
+        // 4 (m * 8 OCT + j OCT + ol), with 4 m * 8 OCT = (q & ~1) * 16 OCT for q = 2m or 2m + 1
+        const uint32_t pair_bytes = 16 * OCT;
+        uint32_t hb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hb[j] = 4 * (j * OCT + ol);
+        const float one = opaque_one();
         TokenWalk w;
         w.init(g, t_begin);
         if (w.gp != 0) {
@@ -399,17 +473,18 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
             snap8(g, (uint64_t)row * g.C + o * 8, af);
         }
         rows_ahead<4>(g, base, w, t_end, [&](uint4 v, const TokenWalk &w) {
-            float xf[8];
-            unpack8(v, xf);
             if (w.gp == 0) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) af[j] = xf[j];
+                unpack8(v, af);
                 snap8(g, (uint64_t)row * g.C + o * 8, af);
             } else if (w.t >= g.n_sink) {  // and out of the histograms
+                const uint32_t x[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const uint32_t q = quantize_bf(xf[j] - af[j], lo8[j], r8[j], nm1);
-                    atomicAdd(&hist[((q >> 1) * 8 + j) * OCT + ol], 1u << (16 * (q & 1u)));
+                    const uint32_t h = (j & 1) ? x[j / 2] >> 16 : x[j / 2] & 0xFFFFu;
+                    const uint32_t q = quantize_bf(delta_mix(h, one, af[j]), lo8[j], r8[j], nm1);
+                    uint32_t *cw = reinterpret_cast<uint32_t *>(
+                        reinterpret_cast<char *>(hist) + __umul24(q & ~1u, pair_bytes) + hb[j]);
+                    atomicAdd(cw, 1u << (16 * (q & 1u)));
                 }
             }
         });
@@ -970,6 +1045,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void k5_code(const uint16_t *__rest
     // the chunk's rows of this (layer, K/V): token u at byte u * 2C, channel at 2c
     const __amdgpu_buffer_rsrc_t xs = make_rsrc(X + ((uint64_t)row * g.S + t0) * g.C,
                                                 (uint32_t)((uint64_t)len * g.C * 2));
+    const float one = opaque_one();
     const uint32_t voff = 2 * (present ? c : 0u);
     const uint32_t rstride = 2 * g.C;
     const uint64_t arow0 = anchor_row(g, k, row, 0);   // anchor row of group gi: arow0 + gi
@@ -998,7 +1074,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void k5_code(const uint16_t *__rest
         const uint32_t u0 = gi * G, gl = min(G, len - u0);
         anchor(load(u0), gi);
         for (uint32_t j = gl - 1; j >= 1; --j) {
-            const uint32_t q = cd.symbol(h2f(load(u0 + j)) - cd.af, t0 + u0 + j >= g.n_sink);
+            const uint32_t q = cd.symbol(delta_mix(load(u0 + j), one, cd.af), t0 + u0 + j >= g.n_sink);
             cd.step(cd.entry(q));
             cd.flush();
         }
@@ -1026,7 +1102,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void k5_code(const uint16_t *__rest
                 uint32_t q[GU];
 #pragma unroll
                 for (uint32_t j = GU - 1; j >= 1; --j)
-                    q[j] = cd.symbol(h2f(cur[j]) - cd.af, coded || t0 + ugi * G + j >= g.n_sink);
+                    q[j] = cd.symbol(delta_mix(cur[j], one, cd.af), coded || t0 + ugi * G + j >= g.n_sink);
                 EncEntry en[GU];
 #pragma unroll
                 for (uint32_t j = GU - 1; j >= 1; --j) en[j] = cd.entry(q[j]);
