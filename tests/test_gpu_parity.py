@@ -180,6 +180,19 @@ def test_nonfinite_input_is_rejected(cg):
     assert e.value.code == -4
 
 
+# fp16 bits of +Inf, -Inf, a quiet NaN, a signalling NaN and a negative NaN, each placed
+# at an anchor, a coded token, a sink token and the last token, in even and odd channels
+# (the low and high half of a 32-bit word)
+@pytest.mark.parametrize("bits", [0x7C00, 0xFC00, 0x7E00, 0x7C01, 0xFFFF])
+@pytest.mark.parametrize("t,c", [(0, 0), (20, 5), (33, 7), (2, 64), (299, 127), (151, 130)])
+def test_every_nonfinite_form_is_rejected(cg, bits, t, c):
+    X = _gen(1, 300, 136, GAUSS)
+    X.view(torch.int16)[0, 1, t, c] = bits - 0x10000 if bits >= 0x8000 else bits
+    with pytest.raises(cg.CgError) as e:
+        cg.build_cdf(X, 10, 128, (8,), H_kv=1, n_sink=4)
+    assert e.value.code == -4
+
+
 def test_mismatched_container_is_rejected(cg):
     X = _gen(1, 64, 64, GAUSS)
     t1 = cg.build_cdf(X, 10, 64, (8,), H_kv=1)
