@@ -4,6 +4,8 @@
 
 #include "cg_device.h"
 
+#include <type_traits>
+
 namespace cgk {
 constexpr int kNT16 = 2;  // aux bits of a buffer load: non-temporal (single-use stream)
 // Non-temporal (streaming) accesses for the encoder's single-use streams: the KV rows it
@@ -923,15 +925,17 @@ struct Coder {
 
     // q = clamp(floor(fma(delta - lo, r, 0.5)), 0, N - 1) without branches (v is finite,
     // so the median of (v, 0, N - 1) gives quantize1's result); off: the clamp changed v,
-    // or a zero-width grid misses delta.  `coded`: the token is from n_sink on.  The
-    // off-grid lanes come straight from the compares' lane masks (a ballot of a combined
-    // bool would first be materialised as 0 / 1 and compared again).
+    // or a zero-width grid misses delta (tested only with ZW: some lane of the wavefront
+    // has a zero-width grid).  `coded`: the token is from n_sink on.  The off-grid lanes
+    // come straight from the compares' lane masks (a ballot of a combined bool would
+    // first be materialised as 0 / 1 and compared again).
+    template <bool ZW>
     __device__ __forceinline__ uint32_t symbol(float dl, bool coded)
     {
         const float v = floorf(fmaf(dl - lo, r, 0.5f));
         const float vc = __builtin_amdgcn_fmed3f(v, 0.0f, nm1);
         uint64_t om = __builtin_amdgcn_fcmpf(v, vc, 14 /* unordered or not equal */);
-        if (zmask) om |= zmask & __builtin_amdgcn_fcmpf(dl, lo, 14);   // (rare: uniform test)
+        if constexpr (ZW) om |= zmask & __builtin_amdgcn_fcmpf(dl, lo, 14);
         n_off += coded ? (uint32_t)__builtin_popcountll(om & pmask) : 0u;
         return (uint32_t)vc;
     }
@@ -1069,55 +1073,66 @@ __global__ __launch_bounds__(kEncWaves * 64) void k5_code(const uint16_t *__rest
             if (present) reinterpret_cast<uint16_t *>(anchors)[ai] = (uint16_t)v;
         }
     };
-    // any group, one token at a time (its last token first)
-    auto group_generic = [&](uint32_t gi) __attribute__((always_inline)) {
-        const uint32_t u0 = gi * G, gl = min(G, len - u0);
-        anchor(load(u0), gi);
-        for (uint32_t j = gl - 1; j >= 1; --j) {
-            const uint32_t q = cd.symbol(delta_mix(load(u0 + j), one, cd.af), t0 + u0 + j >= g.n_sink);
-            cd.step(cd.entry(q));
-            cd.flush();
-        }
-    };
-
-    uint32_t gi = ng;  // groups left, processed from the last to the first
-    if constexpr (GU > 0) {
-        // the chunk's last group may be short: one token at a time; then full groups,
-        // unrolled, the next group's rows loaded while this one is coded
-        const uint32_t last = len - (ng - 1) * G;
-        if (last != G) group_generic(--gi);
-        if (gi > 0) {
-            uint32_t cur[GU], nxt[GU];
-            --gi;
-#pragma unroll
-            for (uint32_t j = 0; j < GU; ++j) cur[j] = load(gi * G + j);
-            while (true) {
-                const uint32_t ugi = gi;
-                const bool more = ugi > 0;
-                const uint32_t nb = more ? (ugi - 1) * G : ugi * G;  // in bounds either way
-#pragma unroll
-                for (uint32_t j = 0; j < GU; ++j) nxt[j] = load(nb + j);
-                anchor(cur[0], ugi);
-                const bool coded = t0 + ugi * G + 1 >= g.n_sink;
-                uint32_t q[GU];
-#pragma unroll
-                for (uint32_t j = GU - 1; j >= 1; --j)
-                    q[j] = cd.symbol(delta_mix(cur[j], one, cd.af), coded || t0 + ugi * G + j >= g.n_sink);
-                EncEntry en[GU];
-#pragma unroll
-                for (uint32_t j = GU - 1; j >= 1; --j) en[j] = cd.entry(q[j]);
-#pragma unroll
-                for (uint32_t j = GU - 1; j >= 1; --j) cd.step(en[j]);
+    // The coding loop, compiled twice: with the zero-width grid test (some lane's grid is
+    // the single point lo) and without it, so the usual case takes no per-symbol branch.
+    auto code_chunk = [&](auto zw) __attribute__((always_inline)) {
+        constexpr bool ZW = decltype(zw)::value;
+        // any group, one token at a time (its last token first)
+        auto group_generic = [&](uint32_t gi) __attribute__((always_inline)) {
+            const uint32_t u0 = gi * G, gl = min(G, len - u0);
+            anchor(load(u0), gi);
+            for (uint32_t j = gl - 1; j >= 1; --j) {
+                const uint32_t q = cd.template symbol<ZW>(delta_mix(load(u0 + j), one, cd.af),
+                                                          t0 + u0 + j >= g.n_sink);
+                cd.step(cd.entry(q));
                 cd.flush();
-                if (!more) break;
+            }
+        };
+
+        uint32_t gi = ng;  // groups left, processed from the last to the first
+        if constexpr (GU > 0) {
+            // the chunk's last group may be short: one token at a time; then full groups,
+            // unrolled, the next group's rows loaded while this one is coded
+            const uint32_t last = len - (ng - 1) * G;
+            if (last != G) group_generic(--gi);
+            if (gi > 0) {
+                uint32_t cur[GU], nxt[GU];
                 --gi;
 #pragma unroll
-                for (uint32_t j = 0; j < GU; ++j) cur[j] = nxt[j];
+                for (uint32_t j = 0; j < GU; ++j) cur[j] = load(gi * G + j);
+                while (true) {
+                    const uint32_t ugi = gi;
+                    const bool more = ugi > 0;
+                    const uint32_t nb = more ? (ugi - 1) * G : ugi * G;  // in bounds either way
+#pragma unroll
+                    for (uint32_t j = 0; j < GU; ++j) nxt[j] = load(nb + j);
+                    anchor(cur[0], ugi);
+                    const bool coded = t0 + ugi * G + 1 >= g.n_sink;
+                    uint32_t q[GU];
+#pragma unroll
+                    for (uint32_t j = GU - 1; j >= 1; --j)
+                        q[j] = cd.template symbol<ZW>(delta_mix(cur[j], one, cd.af),
+                                                      coded || t0 + ugi * G + j >= g.n_sink);
+                    EncEntry en[GU];
+#pragma unroll
+                    for (uint32_t j = GU - 1; j >= 1; --j) en[j] = cd.entry(q[j]);
+#pragma unroll
+                    for (uint32_t j = GU - 1; j >= 1; --j) cd.step(en[j]);
+                    cd.flush();
+                    if (!more) break;
+                    --gi;
+#pragma unroll
+                    for (uint32_t j = 0; j < GU; ++j) cur[j] = nxt[j];
+                }
             }
+        } else {
+            while (gi > 0) group_generic(--gi);
         }
-    } else {
-        while (gi > 0) group_generic(--gi);
-    }
+    };
+    if (cd.zmask)
+        code_chunk(std::true_type{});
+    else
+        code_chunk(std::false_type{});
 
     // the state words come first in read order: lane i's two words at positions 2i, 2i+1
     uint32_t total = 0;
