@@ -932,11 +932,20 @@ struct Coder {
     template <bool ZW>
     __device__ __forceinline__ uint32_t symbol(float dl, bool coded)
     {
+        uint64_t om;
+        const uint32_t q = symbol_mask<ZW>(dl, om);
+        n_off += coded ? (uint32_t)__builtin_popcountll(om & pmask) : 0u;
+        return q;
+    }
+
+    // The same, with the off-grid lanes returned in om rather than counted.
+    template <bool ZW>
+    __device__ __forceinline__ uint32_t symbol_mask(float dl, uint64_t &om) const
+    {
         const float v = floorf(fmaf(dl - lo, r, 0.5f));
         const float vc = __builtin_amdgcn_fmed3f(v, 0.0f, nm1);
-        uint64_t om = __builtin_amdgcn_fcmpf(v, vc, 14 /* unordered or not equal */);
+        om = __builtin_amdgcn_fcmpf(v, vc, 14 /* unordered or not equal */);
         if constexpr (ZW) om |= zmask & __builtin_amdgcn_fcmpf(dl, lo, 14);
-        n_off += coded ? (uint32_t)__builtin_popcountll(om & pmask) : 0u;
         return (uint32_t)vc;
     }
 
@@ -1108,11 +1117,22 @@ __global__ __launch_bounds__(kEncWaves * 64) void k5_code(const uint16_t *__rest
                     for (uint32_t j = 0; j < GU; ++j) nxt[j] = load(nb + j);
                     anchor(cur[0], ugi);
                     const bool coded = t0 + ugi * G + 1 >= g.n_sink;
+                    // The group's symbols; their off-grid lanes are only gathered, and
+                    // counted token by token when some lane is off its grid (rare).
                     uint32_t q[GU];
+                    uint64_t anyoff = 0;
 #pragma unroll
-                    for (uint32_t j = GU - 1; j >= 1; --j)
-                        q[j] = cd.template symbol<ZW>(delta_mix(cur[j], one, cd.af),
-                                                      coded || t0 + ugi * G + j >= g.n_sink);
+                    for (uint32_t j = GU - 1; j >= 1; --j) {
+                        uint64_t om;
+                        q[j] = cd.template symbol_mask<ZW>(delta_mix(cur[j], one, cd.af), om);
+                        anyoff |= om;
+                    }
+                    if (anyoff & cd.pmask) {
+#pragma unroll
+                        for (uint32_t j = GU - 1; j >= 1; --j)
+                            cd.template symbol<ZW>(delta_mix(cur[j], one, cd.af),
+                                                   coded || t0 + ugi * G + j >= g.n_sink);
+                    }
                     EncEntry en[GU];
 #pragma unroll
                     for (uint32_t j = GU - 1; j >= 1; --j) en[j] = cd.entry(q[j]);
