@@ -172,6 +172,22 @@ def test_constant_and_signed_zero_channels(cg):
     assert ex["w"][0, 0, 0] == 0 and ex["lo"][0, 1, 2].view(np.uint32) == 0
 
 
+@pytest.mark.parametrize("ppm,ab", [(0, 16), (1000, 16), (1000, 8)])
+def test_zero_width_grids_with_off_grid_elements(cg, ppm, ab):
+    """Tables from a cache with constant channels (zero-width grids: only lo is on them)
+    coding a cache where those channels vary: every such delta is off its grid, counted in
+    the header or stored as an outlier entry, in full and partial groups."""
+    X = _gen(2, 700, 128, GAUSS)
+    X[0, 0, :, 3] = 1.5                  # constant: zero-width grid
+    X[1, 1, :, 64] = -0.25               # another, in the second channel block
+    Xe = X.clone()
+    Xe[0, 0, 100:110, 3] = 2.0           # off the grid in the encoded cache
+    Xe[1, 1, 5::7, 64] = 0.5
+    Xe[1, 1, 690:, 64] = -1.0            # in the short last group of the last chunk
+    full_parity(cg, X, 2, 10, 256, (8, 16), label="zero-width off-grid", X_enc=Xe,
+                outlier_ppm=ppm, anchor_bits=ab)
+
+
 def test_nonfinite_input_is_rejected(cg):
     X = _gen(1, 64, 64, GAUSS)
     X[0, 1, 33, 7] = float("inf")
