@@ -72,9 +72,8 @@ __device__ __forceinline__ void rows_ahead(const Geom &g, const uint16_t *base, 
 }
 
 // ------------------------------------------------------------------------------ K0
-// Per-channel min / max of the anchor deltas, and the non-finite flag.
-// Thread = (row, token block, 8 channels); 16-byte loads, one row of C channels is
-// read by C/8 consecutive threads.
+// Per-channel min / max of the anchor deltas, and the non-finite flag; 16-byte loads,
+// one row of C channels read by C/8 consecutive threads.
 //
 // A delta is the fp32 difference x - a of a token and its group's anchor, and rounding is
 // monotone, so over the tokens of one group min(x - a) = min(x) - a (likewise max): the
@@ -104,85 +103,93 @@ __device__ __forceinline__ uint32_t pk_nonfinite_acc(uint32_t acc, uint32_t x)
     return r;
 }
 
+// Thread = (row, token stream tb, 8 channels): the thread takes the row's groups tb,
+// tb + ntb, tb + 2 ntb, ... (group slots in chunk order, ngF per chunk), so the threads of a
+// row read neighbouring groups at the same time (a window of ntb groups moving through the
+// row) rather than each its own distant token range.
 __global__ __launch_bounds__(256) void k0_minmax(const uint16_t *__restrict__ X, Geom g,
-                                                  uint32_t tpt, uint32_t ntb,
-                                                  uint32_t *__restrict__ ord_lo,
+                                                  uint32_t ntb, uint32_t *__restrict__ ord_lo,
                                                   uint32_t *__restrict__ ord_hi,
                                                   uint32_t *__restrict__ flag)
 {
     const uint32_t O = g.C / 8;
-    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (uint64_t)g.L * 2 * ntb * O) return;
-    uint32_t o = (uint32_t)(i % O);
-    uint64_t tmp = i / O;
-    uint32_t tb = (uint32_t)(tmp % ntb);
-    uint32_t row = (uint32_t)(tmp / ntb);
-    uint32_t t_begin = tb * tpt;
-    if (t_begin >= g.S) return;
-    uint32_t t_end = min(g.S, t_begin + tpt);
+    const uint32_t o = (uint32_t)(i % O);
+    const uint64_t tmp = i / O;
+    const uint32_t tb = (uint32_t)(tmp % ntb);
+    const uint32_t row = (uint32_t)(tmp / ntb);
     const uint16_t *base = X + (uint64_t)row * g.S * g.C + o * 8;
     const uint64_t r0 = (uint64_t)row * g.C + o * 8;
+    const uint32_t slots = (g.S + g.Tc - 1) / g.Tc * g.ngF;
 
     constexpr uint32_t kPosInf2 = 0x7C007C00u, kNegInf2 = 0xFC00FC00u;
-    TokenWalk w;
-    w.init(g, t_begin);
-    float af[8], mn[8], mx[8];
-    uint32_t gmn[4], gmx[4], nf[4];  // the group's fp16 min / max pairs; the non-finite sums
-    bool any = false, gany = false;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        gmn[j] = kPosInf2;
-        gmx[j] = kNegInf2;
-        nf[j] = 0;
-    }
-    if (w.gp != 0) {
-        uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
+    constexpr uint32_t kBatch = 9;   // tokens loaded together after a group's anchor
+    float mn[8], mx[8];
+    uint32_t nf[4] = {0u, 0u, 0u, 0u};  // the non-finite sums
+    bool any = false;
+    for (uint32_t j = tb; j < slots; j += ntb) {
+        const uint32_t k = j / g.ngF, gi = j - k * g.ngF;
+        const uint32_t cl = chunk_len(g, k);
+        if (gi * g.G >= cl) continue;  // past the last group of a short last chunk
+        const uint32_t t0 = k * g.Tc + gi * g.G, gl = min(g.G, cl - gi * g.G);
+        const uint4 a = ntload16(base + (uint64_t)t0 * g.C);
+        nf[0] = pk_nonfinite_acc(nf[0], a.x);
+        nf[1] = pk_nonfinite_acc(nf[1], a.y);
+        nf[2] = pk_nonfinite_acc(nf[2], a.z);
+        nf[3] = pk_nonfinite_acc(nf[3], a.w);
+        float af[8];
         unpack8(a, af);
         snap8(g, r0, af);
-    }
-    // the current group's extremes into the fp32 range of deltas
-    auto fold = [&]() __attribute__((always_inline)) {
-        if (!gany) return;
-        float hmn[8], hmx[8];
-        unpack8(make_uint4(gmn[0], gmn[1], gmn[2], gmn[3]), hmn);
-        unpack8(make_uint4(gmx[0], gmx[1], gmx[2], gmx[3]), hmx);
+        uint32_t gmn[4], gmx[4];  // the group's fp16 min / max pairs
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float dmn = hmn[j] - af[j], dmx = hmx[j] - af[j];
-            mn[j] = (!any || dmn < mn[j]) ? dmn : mn[j];
-            mx[j] = (!any || dmx > mx[j]) ? dmx : mx[j];
+        for (int q = 0; q < 4; ++q) {
+            gmn[q] = kPosInf2;
+            gmx[q] = kNegInf2;
         }
-        any = true;
-        gany = false;
+        bool gany = false;
+        // the other tokens, kBatch at a time; loads past the group's end repeat its last
+        // token, which changes neither the min / max nor the non-finite sums
+        for (uint32_t u0 = 1; u0 < gl; u0 += kBatch) {
+            uint4 v[kBatch];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            gmn[j] = kPosInf2;
-            gmx[j] = kNegInf2;
-        }
-    };
-    rows_ahead<4>(g, base, w, t_end, [&](uint4 v, const TokenWalk &w) {
-        const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+            for (uint32_t b = 0; b < kBatch; ++b)
+                v[b] = ntload16(base + (uint64_t)(t0 + min(u0 + b, gl - 1)) * g.C);
+            const bool all_coded = t0 + u0 >= g.n_sink;  // else: sink tokens in the batch
 #pragma unroll
-        for (int j = 0; j < 4; ++j) nf[j] = pk_nonfinite_acc(nf[j], x[j]);
-        if (w.gp == 0) {
-            fold();
-            unpack8(v, af);
-            snap8(g, r0, af);
-        } else if (w.t >= g.n_sink) {  // sink tokens stay out of the range
+            for (uint32_t b = 0; b < kBatch; ++b) {
+                const uint32_t x[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                gmn[j] = pk_min_f16(gmn[j], x[j]);
-                gmx[j] = pk_max_f16(gmx[j], x[j]);
+                for (int q = 0; q < 4; ++q) nf[q] = pk_nonfinite_acc(nf[q], x[q]);
+                if (all_coded || t0 + min(u0 + b, gl - 1) >= g.n_sink) {  // sinks stay out
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        gmn[q] = pk_min_f16(gmn[q], x[q]);
+                        gmx[q] = pk_max_f16(gmx[q], x[q]);
+                    }
+                    gany = true;
+                }
             }
-            gany = true;
         }
-    });
-    fold();
+        if (gany) {
+            // the group's extremes into the fp32 range of deltas
+            float hmn[8], hmx[8];
+            unpack8(make_uint4(gmn[0], gmn[1], gmn[2], gmn[3]), hmn);
+            unpack8(make_uint4(gmx[0], gmx[1], gmx[2], gmx[3]), hmx);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float dmn = hmn[q] - af[q], dmx = hmx[q] - af[q];
+                mn[q] = (!any || dmn < mn[q]) ? dmn : mn[q];
+                mx[q] = (!any || dmx > mx[q]) ? dmx : mx[q];
+            }
+            any = true;
+        }
+    }
     if (any) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            atomicMin(&ord_lo[r0 + j], f2ord(mn[j]));
-            atomicMax(&ord_hi[r0 + j], f2ord(mx[j]));
+        for (int q = 0; q < 8; ++q) {
+            atomicMin(&ord_lo[r0 + q], f2ord(mn[q]));
+            atomicMax(&ord_hi[r0 + q], f2ord(mx[q]));
         }
     }
     if (((nf[0] | nf[1] | nf[2] | nf[3]) & 0x7FFF7FFFu) != 0) atomicOr(flag, 1u);
@@ -1277,10 +1284,14 @@ __global__ __launch_bounds__(256) void k5_compact(const uint16_t *__restrict__ r
 hipError_t launch_k0(const uint16_t *X, const Geom &g, uint32_t tpt, uint32_t *ord_lo,
                      uint32_t *ord_hi, uint32_t *flag, hipStream_t st)
 {
-    uint32_t ntb = (g.S + tpt - 1) / tpt;
+    // token streams per row: one per 2 tpt tokens, at most one per group slot (~52 on the
+    // 70B-shaped cache: fewer streams merge fewer partial results at the end, more read
+    // more in parallel; 26, 52, 104, 416 and 1664 took 1.83, 1.79, 1.89, 3.7 and 14.5 ms)
+    const uint32_t slots = (g.S + g.Tc - 1) / g.Tc * g.ngF;
+    const uint32_t ntb = std::max(1u, std::min((g.S + 2 * tpt - 1) / (2 * tpt), slots));
     uint64_t threads = (uint64_t)g.L * 2 * ntb * (g.C / 8);
     hipLaunchKernelGGL(k0_minmax, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st, X, g,
-                       tpt, ntb, ord_lo, ord_hi, flag);
+                       ntb, ord_lo, ord_hi, flag);
     return hipGetLastError();
 }
 
