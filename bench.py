@@ -194,9 +194,10 @@ def access_form_bandwidth(dev, reps: int = 5, nbytes: int = 4 << 30) -> dict:
     """HBM rate of the decoder's own access forms alone, 4 GiB each (libcg_calib.so,
     grid-stride kernels of 2048 x 256 threads), timed with HIP events: 2-byte
     non-temporal stores, 128 contiguous bytes per wavefront (the output rows), 4-byte ones
-    (256 bytes per wavefront, for comparison), and 4- and 2-byte non-temporal loads
-    (payload words, anchor rows).  The store rate bounds how fast the decoder can write its
-    rows however little it computes."""
+    (256 bytes per wavefront, for comparison), 4- and 2-byte non-temporal loads (payload
+    words, anchor rows), and a plain streaming read of 16-byte loads (the rate the
+    encoder's passes over the cache could reach).  The store rate bounds how fast the
+    decoder can write its rows however little it computes."""
     import ctypes
 
     import torch
@@ -210,7 +211,8 @@ def access_form_bandwidth(dev, reps: int = 5, nbytes: int = 4 << 30) -> dict:
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     res = {"bytes": nbytes, "reps": reps}
-    for kind, name in ((2, "write2_nt"), (3, "write4_nt"), (0, "read4_nt"), (1, "read2_nt")):
+    for kind, name in ((2, "write2_nt"), (3, "write4_nt"), (0, "read4_nt"), (1, "read2_nt"),
+                       (4, "read16_nt")):
         assert calib.cg_calib_run(kind, buf.data_ptr(), nbytes, sink.data_ptr(), sp) == 0
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]

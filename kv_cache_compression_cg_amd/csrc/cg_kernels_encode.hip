@@ -46,31 +46,6 @@ __device__ __forceinline__ float opaque_one()
     return one;
 }
 
-// Calls body(row, walk) for the token rows [w.t, t_end) of one thread (16 bytes each at
-// base + t * C), with the loads of the next A rows in flight: the row loop of the
-// histogram passes would otherwise wait for one load at a time.  Loads past t_end read
-// the last row again (in bounds, unused).
-template <int A, class F>
-__device__ __forceinline__ void rows_ahead(const Geom &g, const uint16_t *base, TokenWalk &w,
-                                           uint32_t t_end, F body)
-{
-    if (w.t >= t_end) return;
-    uint4 buf[A];
-#pragma unroll
-    for (int u = 0; u < A; ++u) buf[u] = ntload16(base + (uint64_t)min(w.t + u, t_end - 1) * g.C);
-    while (w.t < t_end) {
-#pragma unroll
-        for (int u = 0; u < A; ++u) {
-            if (w.t < t_end) {
-                const uint4 v = buf[u];
-                buf[u] = ntload16(base + (uint64_t)min(w.t + A, t_end - 1) * g.C);
-                body(v, w);
-                w.next(g);
-            }
-        }
-    }
-}
-
 // ------------------------------------------------------------------------------ K0
 // Per-channel min / max of the anchor deltas, and the non-finite flag; 16-byte loads,
 // one row of C channels read by C/8 consecutive threads.
@@ -428,16 +403,18 @@ __global__ __launch_bounds__(256) void k_clip(Geom g, const uint16_t *__restrict
 }
 
 // ------------------------------------------------------------------------------ K1
-// Fused delta -> quantize -> histogram.  Block = (row, tile of 8*OCT channels, token
-// block); its SUB x OCT threads each own 8 channels of a token sub-range.  Counts go
-// to an LDS histogram [N/2][8][OCT] of 16-bit counter pairs (bins 2m and 2m + 1 in one
-// word; consecutive lanes -> consecutive banks; half the LDS of 32-bit counters, so more
-// blocks are resident), then the non-zero bins are added to the global u32 counts.
+// Fused delta -> quantize -> histogram.  Block = (row, tile of 8*OCT channels, set of
+// SUB token streams); its SUB x OCT threads each own 8 channels of one stream, which takes
+// every NS-th group of the row (NS = streams per row), so that a row's blocks read
+// neighbouring groups at the same time.  Counts go to an LDS histogram [N/2][8][OCT] of
+// 16-bit counter pairs (bins 2m and 2m + 1 in one word; consecutive lanes -> consecutive
+// banks; half the LDS of 32-bit counters, so more blocks are resident), then the non-zero
+// bins are added to the global u32 counts.
 __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, Geom g,
                                                 const uint8_t *__restrict__ bins,
                                                 const float *__restrict__ lo,
                                                 const float *__restrict__ r, uint32_t OCT,
-                                                uint32_t SUB, uint32_t tpt, uint32_t ntiles,
+                                                uint32_t SUB, uint32_t ntiles,
                                                 uint32_t ntb, uint32_t *__restrict__ counts)
 {
     extern __shared__ uint32_t hist[];
@@ -456,9 +433,7 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
     const uint32_t O = g.C / 8;
     uint32_t ol = threadIdx.x % OCT, sub = threadIdx.x / OCT;
     uint32_t o = ct * OCT + ol;
-    uint32_t t_begin = (tbb * SUB + sub) * tpt;
-    if (sub < SUB && o < O && t_begin < g.S) {
-        uint32_t t_end = min(g.S, t_begin + tpt);
+    if (sub < SUB && o < O) {
         const uint16_t *base = X + (uint64_t)row * g.S * g.C + o * 8;
         float lo8[8], r8[8], af[8];
         uint64_t r0 = (uint64_t)row * g.C + o * 8;
@@ -474,29 +449,39 @@ __global__ __launch_bounds__(256) void k1_hist(const uint16_t *__restrict__ X, G
 #pragma unroll
         for (int j = 0; j < 8; ++j) hb[j] = 4 * (j * OCT + ol);
         const float one = opaque_one();
-        TokenWalk w;
-        w.init(g, t_begin);
-        if (w.gp != 0) {
-            uint4 a = *reinterpret_cast<const uint4 *>(base + (uint64_t)(t_begin - w.gp) * g.C);
-            unpack8(a, af);
-            snap8(g, (uint64_t)row * g.C + o * 8, af);
-        }
-        rows_ahead<4>(g, base, w, t_end, [&](uint4 v, const TokenWalk &w) {
-            if (w.gp == 0) {
-                unpack8(v, af);
-                snap8(g, (uint64_t)row * g.C + o * 8, af);
-            } else if (w.t >= g.n_sink) {  // and out of the histograms
-                const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+        // the stream's groups: slots st, st + NS, st + 2 NS, ... of the row (as in the range
+        // pass, so that the blocks of a row read neighbouring groups at the same time)
+        const uint32_t NS = ntb * SUB, st = tbb * SUB + sub;
+        const uint32_t slots = (g.S + g.Tc - 1) / g.Tc * g.ngF;
+        constexpr uint32_t kBatch = 9;   // tokens loaded together after a group's anchor
+        for (uint32_t j = st; j < slots; j += NS) {
+            const uint32_t k = j / g.ngF, gi = j - k * g.ngF;
+            const uint32_t cl = chunk_len(g, k);
+            if (gi * g.G >= cl) continue;  // past the last group of a short last chunk
+            const uint32_t t0 = k * g.Tc + gi * g.G, gl = min(g.G, cl - gi * g.G);
+            unpack8(ntload16(base + (uint64_t)t0 * g.C), af);
+            snap8(g, r0, af);
+            for (uint32_t u0 = 1; u0 < gl; u0 += kBatch) {
+                uint4 v[kBatch];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t h = (j & 1) ? x[j / 2] >> 16 : x[j / 2] & 0xFFFFu;
-                    const uint32_t q = quantize_bf(delta_mix(h, one, af[j]), lo8[j], r8[j], nm1);
-                    uint32_t *cw = reinterpret_cast<uint32_t *>(
-                        reinterpret_cast<char *>(hist) + __umul24(q & ~1u, pair_bytes) + hb[j]);
-                    atomicAdd(cw, 1u << (16 * (q & 1u)));
+                for (uint32_t b = 0; b < kBatch; ++b)
+                    v[b] = ntload16(base + (uint64_t)(t0 + min(u0 + b, gl - 1)) * g.C);
+#pragma unroll
+                for (uint32_t b = 0; b < kBatch; ++b) {
+                    // tokens of the group only, and from n_sink on (sinks stay out)
+                    if (u0 + b >= gl || t0 + u0 + b < g.n_sink) continue;
+                    const uint32_t x[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        const uint32_t h = (c & 1) ? x[c / 2] >> 16 : x[c / 2] & 0xFFFFu;
+                        const uint32_t q = quantize_bf(delta_mix(h, one, af[c]), lo8[c], r8[c], nm1);
+                        uint32_t *cw = reinterpret_cast<uint32_t *>(
+                            reinterpret_cast<char *>(hist) + __umul24(q & ~1u, pair_bytes) + hb[c]);
+                        atomicAdd(cw, 1u << (16 * (q & 1u)));
+                    }
                 }
             }
-        });
+        }
     }
     __syncthreads();
     for (uint32_t j = threadIdx.x; j < nh; j += blockDim.x) {
@@ -1352,11 +1337,14 @@ hipError_t launch_k1(const uint16_t *X, const Geom &g, const uint8_t *bins, uint
     uint64_t ntb_target = (8192 + rows * ntiles - 1) / (rows * ntiles);
     uint64_t tpt = (g.S + ntb_target * SUB - 1) / (ntb_target * SUB);
     if (tpt < 16) tpt = 16;
-    if (tpt * SUB > 0xFFFFu) tpt = 0xFFFFu / SUB;   // 16-bit counters per block
     uint32_t ntb = (uint32_t)((g.S + tpt * SUB - 1) / (tpt * SUB));
+    // 16-bit counters: a block's SUB streams take at most ceil(slots / (ntb SUB)) groups of
+    // at most G tokens each
+    const uint64_t slots = (uint64_t)((g.S + g.Tc - 1) / g.Tc) * g.ngF;
+    while ((uint64_t)SUB * ((slots + (uint64_t)ntb * SUB - 1) / ((uint64_t)ntb * SUB)) * g.G > 0xFFFFu) ++ntb;
     size_t lds = (size_t)(max_bins + 1) / 2 * 8 * OCT * sizeof(uint32_t);
     hipLaunchKernelGGL(k1_hist, dim3((uint32_t)(rows * ntiles * ntb)), dim3(256), lds, st, X, g,
-                       bins, lo, r, OCT, SUB, (uint32_t)tpt, ntiles, ntb, counts);
+                       bins, lo, r, OCT, SUB, ntiles, ntb, counts);
     return hipGetLastError();
 }
 
