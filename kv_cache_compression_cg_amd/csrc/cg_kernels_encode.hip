@@ -908,15 +908,15 @@ struct Coder {
     const EncEntry *tab;
     uint16_t *ring;
     uint16_t *rend;         // end of the group's region
-    float lo, r, nm1, af;   // grid, N - 1 as a float, the current anchor value
+    float lo, r, nmax, af;  // grid, the largest float below N, the current anchor value
     bool zero_w;            // the grid is the single point lo
     bool present;           // this lane has a channel
     uint64_t pmask;         // lanes with a channel
     uint64_t zmask;         // lanes whose grid is the single point lo
     uint32_t lane, x, E, flushed, n_off;
 
-    // q = clamp(floor(fma(delta - lo, r, 0.5)), 0, N - 1) without branches (v is finite,
-    // so the median of (v, 0, N - 1) gives quantize1's result); off: the clamp changed v,
+    // q = clamp(floor(fma(delta - lo, r, 0.5)), 0, N - 1) without branches (a median and a
+    // truncating conversion give quantize1's result); off: the clamp changed v,
     // or a zero-width grid misses delta (tested only with ZW: some lane of the wavefront
     // has a zero-width grid).  `coded`: the token is from n_sink on.  The off-grid lanes
     // come straight from the compares' lane masks (a ballot of a combined bool would
@@ -934,8 +934,11 @@ struct Coder {
     template <bool ZW>
     __device__ __forceinline__ uint32_t symbol_mask(float dl, uint64_t &om) const
     {
-        const float v = floorf(fmaf(dl - lo, r, 0.5f));
-        const float vc = __builtin_amdgcn_fmed3f(v, 0.0f, nm1);
+        // v before its floor: floor(v) lies in [0, N - 1] exactly when v lies in
+        // [0, nmax], so the clamp to [0, nmax] changes v exactly when floor(v) is off the
+        // grid, and the truncating conversion of the clamped value is floor(v) clamped
+        const float v = fmaf(dl - lo, r, 0.5f);
+        const float vc = __builtin_amdgcn_fmed3f(v, 0.0f, nmax);
         om = __builtin_amdgcn_fcmpf(v, vc, 14 /* unordered or not equal */);
         if constexpr (ZW) om |= zmask & __builtin_amdgcn_fcmpf(dl, lo, 14);
         return (uint32_t)vc;
@@ -1037,7 +1040,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void k5_code(const uint16_t *__rest
     cd.rend = regions + (gidx + 1) * region_words;
     cd.lo = lo[ri];
     cd.r = r[ri];
-    cd.nm1 = (float)(N - 1u);
+    cd.nmax = __uint_as_float(__float_as_uint((float)N) - 1u);
     cd.zero_w = cd.r == 0.0f;
     cd.af = 0.0f;
     cd.present = present;
